@@ -1,0 +1,149 @@
+"""fp64 numpy statement of the chunkwise (WY / UT) form of the mixers.
+
+Test infrastructure: the tests use it to show that the chunked algebra the
+GPU kernels implement is an exact rewrite of the sequential recurrence (it
+must equal the oracle to rounding), and to inspect per-chunk intermediates.
+It is not the oracle and the oracle does not use it.
+
+Derivation (state H = S^T, [d_k, d_v]; chunk rows i, j; Hn = state at the
+chunk start; g = within-chunk inclusive cumsum of log a):
+  u_i = b_i (v_i - a_i H_{i-1}^T k_i) unrolled inside the chunk gives
+  (I + A) U = diag(b) V - diag(b gamma) K Hn  with
+  A_ij = b_i (k_i . k_j) exp(g_i - g_j)  for j < i,   gamma_i = exp(g_i).
+  Hence U = U' - W Hn,  W = T diag(b gamma) K,  U' = T diag(b) V,  T = (I+A)^-1,
+  O = diag(gamma) Q Hn + ((Q K^T) o Gamma) U   (Gamma_ij = exp(g_i - g_j), j <= i),
+  H_next = gamma_C Hn + Ktil^T U,  Ktil_j = exp(g_C - g_j) k_j.
+KDA replaces the scalar g by a per-key-dimension G (C x d_k).
+"""
+import numpy as np
+
+
+def _chunks(T, C):
+    return [(s, min(T, s + C)) for s in range(0, T, C)]
+
+
+def fwd(variant, q, k, v, la, beta, h0, C):
+    q, k, v, la = (np.asarray(x, np.float64) for x in (q, k, v, la))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, T, H, dv))
+    ht = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            Hn = np.zeros((dk, dv)) if h0 is None else np.asarray(h0, np.float64)[b, h].copy()
+            for s, e in _chunks(T, C):
+                Q, K, V = q[b, s:e, h], k[b, s:e, h], v[b, s:e, h]
+                n = e - s
+                if variant == "kda":
+                    G = np.cumsum(la[b, s:e, h], axis=0)                 # [n, dk]
+                    E = np.exp(G[:, None, :] - G[None, :, :])            # [i, j, d]
+                    mask = np.tril(np.ones((n, n)))
+                    Aqk = np.einsum("id,jd,ijd->ij", Q, K, E) * mask
+                    bt = np.asarray(beta, np.float64)[b, s:e, h]
+                    A = bt[:, None] * np.einsum("id,jd,ijd->ij", K, K, E) * np.tril(np.ones((n, n)), -1)
+                    Tm = np.linalg.inv(np.eye(n) + A)
+                    W = Tm @ (bt[:, None] * K * np.exp(G))
+                    U = Tm @ (bt[:, None] * V) - W @ Hn
+                    o[b, s:e, h] = (Q * np.exp(G)) @ Hn + Aqk @ U
+                    Hn = np.exp(G[-1])[:, None] * Hn + (K * np.exp(G[-1][None, :] - G)).T @ U
+                    continue
+                g = np.cumsum(la[b, s:e, h])
+                gam = np.exp(g)
+                Gam = np.tril(np.exp(g[:, None] - g[None, :]))
+                if variant == "ssd":
+                    U = V
+                else:
+                    bt = np.asarray(beta, np.float64)[b, s:e, h]
+                    A = np.tril(bt[:, None] * (K @ K.T) * Gam, -1)
+                    Tm = np.linalg.inv(np.eye(n) + A)
+                    W = Tm @ ((bt * gam)[:, None] * K)
+                    U = Tm @ (bt[:, None] * V) - W @ Hn
+                o[b, s:e, h] = gam[:, None] * (Q @ Hn) + ((Q @ K.T) * Gam) @ U
+                Hn = gam[-1] * Hn + (np.exp(g[-1] - g)[:, None] * K).T @ U
+            ht[b, h] = Hn
+    return o, ht
+
+
+def gdn_bwd(q, k, v, la, beta, h0, do, dht, C):
+    """Chunked backward of GDN; returns (dq, dk, dv, dlog_a, dbeta, dh0)."""
+    q, k, v, la, beta, do = (np.asarray(x, np.float64) for x in (q, k, v, la, beta, do))
+    B, T, H, dk = q.shape
+    dv_ = v.shape[-1]
+    out = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros_like(la),
+           np.zeros_like(beta), np.zeros((B, H, dk, dv_))]
+    for b in range(B):
+        for h in range(H):
+            Hn = np.zeros((dk, dv_)) if h0 is None else np.asarray(h0, np.float64)[b, h].copy()
+            states = []
+            for s, e in _chunks(T, C):
+                states.append(Hn.copy())
+                _, Hn = _gdn_chunk(q[b, s:e, h], k[b, s:e, h], v[b, s:e, h], la[b, s:e, h],
+                                   beta[b, s:e, h], Hn)
+            dH = np.zeros((dk, dv_)) if dht is None else np.asarray(dht, np.float64)[b, h].copy()
+            for ci in reversed(range(len(states))):
+                s, e = _chunks(T, C)[ci]
+                Hn = states[ci]
+                Q, K, V, dO = q[b, s:e, h], k[b, s:e, h], v[b, s:e, h], do[b, s:e, h]
+                bt = beta[b, s:e, h]
+                g = np.cumsum(la[b, s:e, h])
+                n = e - s
+                gam = np.exp(g)
+                Gam = np.tril(np.exp(g[:, None] - g[None, :]))
+                KK = K @ K.T
+                A = np.tril(bt[:, None] * KK * Gam, -1)
+                Tm = np.linalg.inv(np.eye(n) + A)
+                X = (bt * gam)[:, None] * K
+                Y = bt[:, None] * V
+                W = Tm @ X
+                U = Tm @ Y - W @ Hn
+                P = (Q @ K.T) * Gam
+                kt = np.exp(g[-1] - g)
+                Kt = kt[:, None] * K
+                dU = P.T @ dO + Kt @ dH
+                dHn = gam[-1] * dH + Q.T @ (gam[:, None] * dO) - W.T @ dU
+                dS = (dO @ U.T) * Gam                         # gradient of Q K^T (masked)
+                dQ = gam[:, None] * (dO @ Hn.T) + dS @ K
+                dK = dS.T @ Q
+                dKt = U @ dH.T
+                dK += kt[:, None] * dKt
+                dW = -dU @ Hn.T
+                dT = dW @ X.T + dU @ Y.T
+                dX = Tm.T @ dW
+                dY = Tm.T @ dU
+                dV = bt[:, None] * dY
+                cx = np.sum(dX * K, 1)
+                dbt = np.sum(dY * V, 1) + gam * cx
+                dK += (bt * gam)[:, None] * dX
+                dA = np.tril(-(Tm.T @ dT @ Tm.T), -1)
+                M = dA * bt[:, None] * Gam
+                dbt += np.sum(dA * Gam * KK, 1)
+                dK += M @ K + M.T @ K
+                EP = dS * (Q @ K.T)                          # dGamma o Gamma from P
+                EA = dA * A
+                sj = np.sum(dKt * Kt, 1)
+                dg = gam * np.sum(dO * (Q @ Hn), 1)
+                dg += EP.sum(1) - EP.sum(0) + EA.sum(1) - EA.sum(0)
+                dg += bt * gam * cx
+                dg -= sj
+                dg[-1] += sj.sum() + gam[-1] * np.sum(dH * Hn)
+                out[0][b, s:e, h] = dQ
+                out[1][b, s:e, h] = dK
+                out[2][b, s:e, h] = dV
+                out[3][b, s:e, h] = np.cumsum(dg[::-1])[::-1]
+                out[4][b, s:e, h] = dbt
+                dH = dHn
+            out[5][b, h] = dH
+    return tuple(out)
+
+
+def _gdn_chunk(Q, K, V, la, bt, Hn):
+    g = np.cumsum(la)
+    n = len(g)
+    gam = np.exp(g)
+    Gam = np.tril(np.exp(g[:, None] - g[None, :]))
+    A = np.tril(bt[:, None] * (K @ K.T) * Gam, -1)
+    Tm = np.linalg.inv(np.eye(n) + A)
+    W = Tm @ ((bt * gam)[:, None] * K)
+    U = Tm @ (bt[:, None] * V) - W @ Hn
+    O = gam[:, None] * (Q @ Hn) + ((Q @ K.T) * Gam) @ U
+    return O, gam[-1] * Hn + (np.exp(g[-1] - g)[:, None] * K).T @ U
