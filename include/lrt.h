@@ -1,0 +1,127 @@
+/*
+ * lrt.h -- C ABI of liblrt.so: gated delta-rule token mixers on AMD MI355X (gfx950).
+ *
+ * The mixers are the linear-recurrent "M" layers of the hybrid stacks in the
+ * AMD ROCm blog "Pretraining hybrid LLMs with Primus" (section "How hybrid
+ * models are defined in Primus", mixer list under Table 2):
+ *   - Mamba2 (ssd_fwd): the state is decayed by one scalar gate per head and a
+ *     rank-one k v^T write is added each token;
+ *   - Gated DeltaNet (gdn_fwd, gdn_bwd): Mamba2 plus the delta rule, which
+ *     replaces the value stored under the current key instead of only adding;
+ *     one scalar forget gate per head;
+ *   - Kimi Delta Attention (kda_fwd): GDN with one gate value per key
+ *     dimension (the low-rank projection producing it is the caller's).
+ *
+ * With the state kept as H = S^T ([d_k, d_v], fp32), per batch b and head h:
+ *   GDN: H_t = a_t (I - b_t k_t k_t^T) H_{t-1} + b_t k_t v_t^T
+ *   SSD: H_t = a_t H_{t-1} + k_t v_t^T
+ *   KDA: H_t = (I - b_t k_t k_t^T) Diag(a_t) H_{t-1} + b_t k_t v_t^T
+ *   o_t = H_t^T q_t  (after token t's write),  a_t = exp(log_a_t),
+ *   H_0 = h0 (NULL = zeros),  ht = H_T.
+ * No query scaling is applied (pre-scale q if wanted).  The library evaluates
+ * the chunkwise form of these recurrences, an exact rewrite of them.
+ *
+ * Layouts (all dense, row-major, contiguous; element offsets are 64-bit):
+ *   q, k, do, dq, dk      [B, T, H, d_k]   dtype
+ *   v, o, dv              [B, T, H, d_v]   dtype
+ *   log_a, beta, dlog_a, dbeta   [B, T, H]  fp32   (KDA log_a: [B, T, H, d_k])
+ *   h0, ht, dht, dh0      [B, H, d_k, d_v] fp32
+ * dtype: LRT_F32 or LRT_BF16 (q, k, v, o and their gradients).  bf16 outputs
+ * are rounded to nearest even.  log_a must be finite (normally <= 0).
+ *
+ * Supported: B, H >= 1; T >= 0; d_k, d_v in {16, 32, 64, 128};
+ * chunk in {16, 32, 64}.  T need not be a multiple of chunk.
+ *
+ * Ownership and execution: the caller allocates and frees every buffer,
+ * including the workspace (size from lrt_workspace_bytes).  The library never
+ * allocates, frees or synchronises; it enqueues kernels on `stream`
+ * (a hipStream_t; NULL = the default stream) and returns.  Device faults
+ * surface at the caller's next synchronisation.  Calls on different streams
+ * with different workspaces may run concurrently.  All pointers are device
+ * pointers.  q, k, v, o, do, dq, dk, dv and the workspace must be 16-byte
+ * aligned; gates, beta, states and their gradients 4-byte aligned.
+ *
+ * Aliasing: ht may alias h0.  No other output may alias any input or output.
+ *
+ * Errors: every entry point validates all arguments before enqueuing
+ * anything; on a non-zero return nothing has been written.
+ */
+#ifndef LRT_H
+#define LRT_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define LRT_OK 0
+#define LRT_ERR_NULL (-1)      /* a required pointer is NULL */
+#define LRT_ERR_SHAPE (-2)     /* B, T, H, d_k or d_v out of the supported set */
+#define LRT_ERR_CHUNK (-3)     /* chunk not in {16, 32, 64} */
+#define LRT_ERR_DTYPE (-4)     /* dtype not LRT_F32 / LRT_BF16 */
+#define LRT_ERR_WORKSPACE (-5) /* workspace NULL or smaller than lrt_workspace_bytes */
+#define LRT_ERR_ALIGN (-6)     /* a pointer is under-aligned (see Ownership) */
+#define LRT_ERR_LAUNCH (-7)    /* the HIP runtime rejected a launch */
+#define LRT_ERR_OP (-8)        /* unknown op code */
+
+/* dtypes of q, k, v, o, do and the q/k/v gradients */
+#define LRT_F32 0
+#define LRT_BF16 1
+
+/* op codes for lrt_workspace_bytes */
+#define LRT_OP_GDN_FWD 0
+#define LRT_OP_GDN_BWD 1
+#define LRT_OP_KDA_FWD 2
+#define LRT_OP_SSD_FWD 3
+
+/*
+ * Gated DeltaNet forward.  Writes o and (if not NULL) ht.
+ * h0 may be NULL (zero initial state); ht may be NULL or equal to h0.
+ */
+int gdn_fwd(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+            const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk,
+            int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Gated DeltaNet backward: gradients of L = <do, o> + <dht, ht> with respect
+ * to q, k, v, log_a, beta and h0, for the forward of the same arguments.
+ * The forward is recomputed internally (no state is kept between calls).
+ * dht may be NULL (zero).  dh0 may be NULL (not written).  dq, dk, dv,
+ * dlog_a and dbeta are required.
+ */
+int gdn_bwd(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+            const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv,
+            float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v,
+            int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Kimi Delta Attention forward: as gdn_fwd, with log_a of shape [B, T, H, d_k]
+ * (one log-gate per key dimension).
+ */
+int kda_fwd(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+            const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk,
+            int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Mamba2 / SSD forward (scalar decay, no delta term): as gdn_fwd without beta.
+ */
+int ssd_fwd(const void* q, const void* k, const void* v, const float* log_a, const float* h0,
+            void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk, int dtype,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes needed by `op` (LRT_OP_*) at these sizes.  Returns
+ * (size_t)-1 for invalid arguments.  0 is never returned for valid ones.
+ */
+size_t lrt_workspace_bytes(int op, int B, int T, int H, int d_k, int d_v, int chunk, int dtype);
+
+/* Static, human-readable text for a status code. */
+const char* lrt_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRT_H */

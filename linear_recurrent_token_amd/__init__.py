@@ -1,0 +1,190 @@
+"""Python binding of liblrt.so: gated delta-rule token mixers on MI355X.
+
+Argument marshalling only.  Every step of every mixer runs in the library's
+gfx950 kernels; this module checks tensors, allocates outputs and the
+workspace with torch on the inputs' device, and passes raw pointers and the
+current HIP stream through ctypes.  There is no CPU fallback: if the library
+is missing, every call raises.
+
+Entry points (names as in include/lrt.h):
+  gdn_fwd(q, k, v, log_a, beta, h0=None, chunk=64)            -> (o, ht)
+  gdn_bwd(q, k, v, log_a, beta, h0, do, dht=None, chunk=64)   -> (dq, dk, dv, dlog_a, dbeta, dh0)
+  kda_fwd(q, k, v, log_a, beta, h0=None, chunk=64)            -> (o, ht)
+  ssd_fwd(q, k, v, log_a, h0=None, chunk=64)                   -> (o, ht)
+Layouts: q, k [B,T,H,d_k], v [B,T,H,d_v] (fp32 or bf16); log_a, beta fp32
+[B,T,H] (KDA log_a [B,T,H,d_k]); states fp32 [B,H,d_k,d_v].
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblrt.so")
+
+LRT_F32, LRT_BF16 = 0, 1
+OP_GDN_FWD, OP_GDN_BWD, OP_KDA_FWD, OP_SSD_FWD = 0, 1, 2, 3
+EXPORTS = ("gdn_fwd", "gdn_bwd", "kda_fwd", "ssd_fwd", "lrt_workspace_bytes", "lrt_status_string")
+
+_lib = None
+
+
+class LrtError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"liblrt.so not found at {LIB_PATH}; build it with "
+                               "`python -m linear_recurrent_token_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.gdn_fwd.argtypes = [vp] * 8 + [ci] * 7 + [vp, sz, vp]
+        L.kda_fwd.argtypes = [vp] * 8 + [ci] * 7 + [vp, sz, vp]
+        L.ssd_fwd.argtypes = [vp] * 7 + [ci] * 7 + [vp, sz, vp]
+        L.gdn_bwd.argtypes = [vp] * 14 + [ci] * 7 + [vp, sz, vp]
+        for f in ("gdn_fwd", "kda_fwd", "ssd_fwd", "gdn_bwd"):
+            getattr(L, f).restype = ci
+        L.lrt_workspace_bytes.argtypes = [ci] * 8
+        L.lrt_workspace_bytes.restype = sz
+        L.lrt_status_string.argtypes = [ci]
+        L.lrt_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().lrt_status_string(int(status)).decode()
+
+
+def workspace_bytes(op, B, T, H, dk, dv, chunk, dtype) -> int:
+    n = lib().lrt_workspace_bytes(op, B, T, H, dk, dv, chunk, dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes for lrt_workspace_bytes")
+    return int(n)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return LRT_BF16
+    if t.dtype == torch.float32:
+        return LRT_F32
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check(dev, dt, name, t, shape, dtype):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.device != dev:
+        raise ValueError(f"{name} must be a tensor on {dev}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _workspace(op, dev, B, T, H, dk, dv, chunk, dt, workspace):
+    need = workspace_bytes(op, B, T, H, dk, dv, chunk, dt)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+    return workspace, need
+
+
+def _fwd(fn, op, q, k, v, log_a, beta, h0, chunk, o, ht, workspace, kda=False):
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    _check(dev, dt, "k", k, (B, T, H, dk), dt)
+    _check(dev, dt, "v", v, (B, T, H, dv), dt)
+    _check(dev, dt, "q", q, (B, T, H, dk), dt)
+    _check(dev, dt, "log_a", log_a, (B, T, H, dk) if kda else (B, T, H), torch.float32)
+    if op != OP_SSD_FWD:
+        if beta is None:
+            raise ValueError("beta is required")
+        _check(dev, dt, "beta", beta, (B, T, H), torch.float32)
+    _check(dev, dt, "h0", h0, (B, H, dk, dv), torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check(dev, dt, "o", o, (B, T, H, dv), dt)
+    if ht is True:
+        ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif ht is False:
+        ht = None
+    _check(dev, dt, "ht", ht, (B, H, dk, dv), torch.float32)
+    code = _dtype_code(q)
+    ws, need = _workspace(op, dev, B, T, H, dk, dv, chunk, code, workspace)
+    with torch.cuda.device(dev):
+        if op == OP_SSD_FWD:
+            rc = fn(_p(q), _p(k), _p(v), _p(log_a), _p(h0), _p(o), _p(ht), B, T, H, dk, dv, chunk, code,
+                    _p(ws), need, _stream(dev))
+        else:
+            rc = fn(_p(q), _p(k), _p(v), _p(log_a), _p(beta), _p(h0), _p(o), _p(ht), B, T, H, dk, dv, chunk,
+                    code, _p(ws), need, _stream(dev))
+    if rc != 0:
+        raise LrtError(fn.__name__, rc)
+    return o, ht
+
+
+def gdn_fwd(q, k, v, log_a, beta, h0=None, chunk=64, o=None, ht=True, workspace=None):
+    """Gated DeltaNet forward -> (o, ht).  ht=False skips the final state."""
+    return _fwd(lib().gdn_fwd, OP_GDN_FWD, q, k, v, log_a, beta, h0, chunk, o, ht, workspace)
+
+
+def kda_fwd(q, k, v, log_a, beta, h0=None, chunk=64, o=None, ht=True, workspace=None):
+    """Kimi Delta Attention forward (log_a per key dim) -> (o, ht)."""
+    return _fwd(lib().kda_fwd, OP_KDA_FWD, q, k, v, log_a, beta, h0, chunk, o, ht, workspace, kda=True)
+
+
+def ssd_fwd(q, k, v, log_a, h0=None, chunk=64, o=None, ht=True, workspace=None):
+    """Mamba2 / SSD forward (no beta, no delta term) -> (o, ht)."""
+    return _fwd(lib().ssd_fwd, OP_SSD_FWD, q, k, v, log_a, None, h0, chunk, o, ht, workspace)
+
+
+def gdn_bwd(q, k, v, log_a, beta, h0, do, dht=None, chunk=64, want_dh0=True, workspace=None, out=None):
+    """Gated DeltaNet backward -> (dq, dk, dv, dlog_a, dbeta, dh0 or None)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    for name, t, shp, ty in (("k", k, (B, T, H, dk), dt), ("v", v, (B, T, H, dv), dt),
+                             ("log_a", log_a, (B, T, H), torch.float32),
+                             ("beta", beta, (B, T, H), torch.float32),
+                             ("h0", h0, (B, H, dk, dv), torch.float32),
+                             ("do", do, (B, T, H, dv), dt), ("dht", dht, (B, H, dk, dv), torch.float32)):
+        _check(dev, dt, name, t, shp, ty)
+    _check(dev, dt, "q", q, (B, T, H, dk), dt)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+               torch.empty((B, T, H), dtype=torch.float32, device=dev),
+               torch.empty((B, T, H), dtype=torch.float32, device=dev),
+               torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dh0 else None)
+    gq, gk, gv, gla, gb, gh0 = out
+    code = _dtype_code(q)
+    ws, need = _workspace(OP_GDN_BWD, dev, B, T, H, dk, dv, chunk, code, workspace)
+    with torch.cuda.device(dev):
+        rc = lib().gdn_bwd(_p(q), _p(k), _p(v), _p(log_a), _p(beta), _p(h0), _p(do), _p(dht), _p(gq), _p(gk),
+                           _p(gv), _p(gla), _p(gb), _p(gh0), B, T, H, dk, dv, chunk, code, _p(ws), need,
+                           _stream(dev))
+    if rc != 0:
+        raise LrtError("gdn_bwd", rc)
+    return gq, gk, gv, gla, gb, gh0

@@ -1,0 +1,141 @@
+// lrt_api.hip -- the C ABI of liblrt.so: argument validation, workspace
+// sizing and dispatch onto the caller's stream.  Nothing here allocates,
+// frees or synchronises.
+#include <stdint.h>
+
+#include "../../include/lrt.h"
+#include "lrt_common.hpp"
+#include "lrt_internal.hpp"
+
+namespace lrt {
+
+// ht = h0 (or zeros) for an empty sequence.
+__global__ void k_state_copy(const float* __restrict__ h0, float* ht, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) ht[i] = h0 ? h0[i] : 0.f;
+}
+
+static bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+static bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+static int check_common(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
+  if (dtype != LRT_F32 && dtype != LRT_BF16) return LRT_ERR_DTYPE;
+  if (B < 1 || H < 1 || T < 0 || !dim_ok(dk) || !dim_ok(dv)) return LRT_ERR_SHAPE;
+  // 64-bit offsets everywhere; keep token counts within int for the grid math
+  if ((long long)B * T > 0x7fffffffLL) return LRT_ERR_SHAPE;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return LRT_ERR_CHUNK;
+  return LRT_OK;
+}
+
+static size_t ws_bytes(int op, int B, int T, int H, int dk, int dv, int chunk, int dtype) {
+  const size_t esz = dtype == LRT_BF16 ? 2 : 4;
+  const bool kda = op == LRT_OP_KDA_FWD;
+  size_t b = fwd_ws_layout(B, T, H, dk, dv, chunk, esz, nullptr, kda).bytes;
+  if (op == LRT_OP_GDN_BWD) b += bwd_ws_extra(B, T, H, dk, dv, chunk, esz);
+  return b < 256 ? 256 : b;
+}
+
+static int launch_empty(const float* h0, float* ht, int B, int H, int dk, int dv, void* stream) {
+  if (ht == nullptr || ht == h0) return LRT_OK;
+  const size_t n = (size_t)B * H * dk * dv;
+  hipLaunchKernelGGL(k_state_copy, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, h0, ht,
+                     n);
+  return hipGetLastError() == hipSuccess ? LRT_OK : LRT_ERR_LAUNCH;
+}
+
+static int fwd_entry(int variant, const void* q, const void* k, const void* v, const float* log_a,
+                     const float* beta, const float* h0, void* o, float* ht, int B, int T, int H, int dk,
+                     int dv, int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(B, T, H, dk, dv, chunk, dtype);
+  if (rc) return rc;
+  // with T == 0 the token tensors are empty and may carry NULL pointers
+  if (T > 0 && (!q || !k || !v || !log_a || !o || (variant != kVarSSD && !beta))) return LRT_ERR_NULL;
+  // token tensors and the workspace are read with 16-byte vectors; gates and
+  // states with 4-byte scalars
+  const void* vec[] = {q, k, v, o, workspace};
+  for (const void* p : vec)
+    if (p && !aligned(p)) return LRT_ERR_ALIGN;
+  const void* sca[] = {log_a, beta, h0, ht};
+  for (const void* p : sca)
+    if (p && !aligned4(p)) return LRT_ERR_ALIGN;
+  const int op = variant == kVarGDN ? LRT_OP_GDN_FWD : variant == kVarSSD ? LRT_OP_SSD_FWD : LRT_OP_KDA_FWD;
+  if (!workspace || workspace_bytes < ws_bytes(op, B, T, H, dk, dv, chunk, dtype)) return LRT_ERR_WORKSPACE;
+  if (T == 0) return launch_empty(h0, ht, B, H, dk, dv, stream);
+  FwdArgs a{variant, q, k, v, log_a, beta, h0, o, ht, B, T, H, dk, dv, chunk, dtype, workspace, stream};
+  rc = variant == kVarKDA ? fwd_kda(a) : fwd_scalar_gate(a);
+  return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : LRT_ERR_SHAPE);
+}
+
+}  // namespace lrt
+
+using namespace lrt;
+
+extern "C" {
+
+int gdn_fwd(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+            const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk,
+            int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_entry(kVarGDN, q, k, v, log_a, beta, h0, o, ht, B, T, H, d_k, d_v, chunk, dtype, workspace,
+                   workspace_bytes, stream);
+}
+
+int kda_fwd(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+            const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk,
+            int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_entry(kVarKDA, q, k, v, log_a, beta, h0, o, ht, B, T, H, d_k, d_v, chunk, dtype, workspace,
+                   workspace_bytes, stream);
+}
+
+int ssd_fwd(const void* q, const void* k, const void* v, const float* log_a, const float* h0, void* o,
+            float* ht, int B, int T, int H, int d_k, int d_v, int chunk, int dtype, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  return fwd_entry(kVarSSD, q, k, v, log_a, nullptr, h0, o, ht, B, T, H, d_k, d_v, chunk, dtype, workspace,
+                   workspace_bytes, stream);
+}
+
+int gdn_bwd(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+            const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv,
+            float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v, int chunk,
+            int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(B, T, H, d_k, d_v, chunk, dtype);
+  if (rc) return rc;
+  if (T > 0 && (!q || !k || !v || !log_a || !beta || !d_o || !dq || !dk || !dv || !dlog_a || !dbeta))
+    return LRT_ERR_NULL;
+  const void* vec[] = {q, k, v, d_o, dq, dk, dv, workspace};
+  for (const void* p : vec)
+    if (p && !aligned(p)) return LRT_ERR_ALIGN;
+  const void* sca[] = {log_a, beta, h0, dht, dlog_a, dbeta, dh0};
+  for (const void* p : sca)
+    if (p && !aligned4(p)) return LRT_ERR_ALIGN;
+  if (!workspace || workspace_bytes < ws_bytes(LRT_OP_GDN_BWD, B, T, H, d_k, d_v, chunk, dtype))
+    return LRT_ERR_WORKSPACE;
+  if (T == 0) return launch_empty(dht, dh0, B, H, d_k, d_v, stream);
+  BwdArgs a{q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0,
+            B, T, H, d_k, d_v, chunk, dtype, workspace, stream};
+  rc = bwd_gdn(a);
+  return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : LRT_ERR_SHAPE);
+}
+
+size_t lrt_workspace_bytes(int op, int B, int T, int H, int d_k, int d_v, int chunk, int dtype) {
+  if (op < LRT_OP_GDN_FWD || op > LRT_OP_SSD_FWD) return (size_t)-1;
+  if (check_common(B, T, H, d_k, d_v, chunk, dtype) != LRT_OK) return (size_t)-1;
+  return ws_bytes(op, B, T, H, d_k, d_v, chunk, dtype);
+}
+
+const char* lrt_status_string(int status) {
+  switch (status) {
+    case LRT_OK: return "ok";
+    case LRT_ERR_NULL: return "a required pointer is NULL";
+    case LRT_ERR_SHAPE: return "unsupported shape (B, H >= 1, T >= 0, d_k and d_v in {16, 32, 64, 128})";
+    case LRT_ERR_CHUNK: return "unsupported chunk size (16, 32 or 64)";
+    case LRT_ERR_DTYPE: return "unsupported dtype (LRT_F32 or LRT_BF16)";
+    case LRT_ERR_WORKSPACE: return "workspace missing or smaller than lrt_workspace_bytes";
+    case LRT_ERR_ALIGN: return "a pointer is under-aligned (token tensors and workspace: 16 bytes; gates and states: 4)";
+    case LRT_ERR_LAUNCH: return "kernel launch failed";
+    case LRT_ERR_OP: return "unknown op";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// lrt_internal.hpp -- host-side argument bundles and workspace layout of liblrt.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lrt {
+
+enum { kVarGDN = 0, kVarSSD = 1, kVarKDA = 2 };
+
+struct FwdArgs {
+  int variant;
+  const void *q, *k, *v;
+  const float *log_a, *beta, *h0;
+  void* o;
+  float* ht;
+  int B, T, H, dk, dv, chunk, dtype;
+  void* workspace;
+  void* stream;
+};
+
+struct BwdArgs {
+  const void *q, *k, *v;
+  const float *log_a, *beta, *h0;
+  const void* d_o;
+  const float* dht;
+  void *dq, *dk_out, *dv_out;
+  float *dlog_a, *dbeta, *dh0;
+  int B, T, H, dk, dv, chunk, dtype;
+  void* workspace;
+  void* stream;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Per-chunk workspace tiles of the forward, chunk-major per (b, h):
+//   W   [C][dk]   E   W = Tinv diag(b gamma) K           (delta variants)
+//   Up  [dv][C]   E   U'^T = (Tinv diag(b) V)^T          (SSD: V^T)
+//   Kt  [dk][C]   E   Ktil^T, Ktil_j = e^(g_C - g_j) k_j
+//   U   [dv][C]   E   U^T = (U' - W Hn)^T
+//   S   [dv][dk]  E   S_n = Hn^T, the state at the chunk start
+//   G   [C]       f32 within-chunk inclusive cumsum of log a
+//   GC  [dk]      f32 per-key-dim chunk log-decay (KDA)
+//   Qg  [C][dk]   E   Q o e^G (KDA)
+//   P   [C][C]    E   intra-chunk attention matrix (KDA)
+struct FwdWs {
+  void *W, *Up, *Kt, *U, *S, *Qg, *P;
+  float *G, *GC;
+  size_t bytes;
+};
+
+inline FwdWs fwd_ws_layout(int B, int T, int H, int dk, int dv, int C, size_t esz, void* base, bool kda = false) {
+  const size_t N = (size_t)(T + C - 1) / C;
+  const size_t tiles = (size_t)B * H * N;
+  size_t off = 0;
+  FwdWs w;
+  char* p = (char*)base;
+  auto take = [&](size_t bytes) {
+    void* r = p ? (void*)(p + off) : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  w.W = take(tiles * C * dk * esz);
+  w.Up = take(tiles * dv * C * esz);
+  w.Kt = take(tiles * dk * C * esz);
+  w.U = take(tiles * dv * C * esz);
+  w.S = take(tiles * dv * dk * esz);
+  w.G = (float*)take(tiles * C * sizeof(float));
+  w.GC = kda ? (float*)take(tiles * dk * sizeof(float)) : nullptr;
+  w.Qg = kda ? take(tiles * C * dk * esz) : nullptr;
+  w.P = kda ? take(tiles * C * C * esz) : nullptr;
+  w.bytes = off;
+  return w;
+}
+
+int fwd_scalar_gate(const FwdArgs& a);
+int fwd_kda(const FwdArgs& a);
+int bwd_gdn(const BwdArgs& a);
+// workspace bytes the backward needs beyond the forward's tiles
+size_t bwd_ws_extra(int B, int T, int H, int dk, int dv, int C, size_t esz);
+
+}  // namespace lrt
