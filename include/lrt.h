@@ -30,7 +30,9 @@
  * are rounded to nearest even.  log_a must be finite (normally <= 0).
  *
  * Supported: B, H >= 1; T >= 0; d_k, d_v in {16, 32, 64, 128};
- * chunk in {16, 32, 64}.  T need not be a multiple of chunk.
+ * chunk in {16, 32, 64}.  T need not be a multiple of chunk.  The fp32
+ * backward (gdn_bwd with LRT_F32) is limited to d_k, d_v <= 64 and
+ * chunk <= 32 (LRT_ERR_SHAPE / LRT_ERR_CHUNK otherwise).
  *
  * Ownership and execution: the caller allocates and frees every buffer,
  * including the workspace (size from lrt_workspace_bytes).  The library never

@@ -114,7 +114,7 @@ int gdn_bwd(const void* q, const void* k, const void* v, const float* log_a, con
   BwdArgs a{q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0,
             B, T, H, d_k, d_v, chunk, dtype, workspace, stream};
   rc = bwd_gdn(a);
-  return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : LRT_ERR_SHAPE);
+  return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
 }
 
 size_t lrt_workspace_bytes(int op, int B, int T, int H, int d_k, int d_v, int chunk, int dtype) {

@@ -145,6 +145,44 @@ __device__ __forceinline__ void block_to_lds(E* lds, int ls, const E* g) {
   }
 }
 
+// Scatter the 16 bytes x (elements c0.. of row r of a row-major source) into
+// an LDS array stored transposed: lds[(c0 + e) * ld + r].
+template <typename E>
+__device__ __forceinline__ void vec_to_lds_T(E* lds, int ld, int r, int c0, uint4 x) {
+  constexpr int V = 16 / (int)sizeof(E);
+  E e[V];
+  __builtin_memcpy(e, &x, 16);
+#pragma unroll
+  for (int i = 0; i < V; ++i) lds[(c0 + i) * ld + r] = e[i];
+}
+
+// Elementwise scale of the 16 bytes x by s (in fp32, rounded back to E).
+template <typename E>
+__device__ __forceinline__ uint4 vec_scale(uint4 x, float s) {
+  constexpr int V = 16 / (int)sizeof(E);
+  E e[V];
+  __builtin_memcpy(e, &x, 16);
+#pragma unroll
+  for (int i = 0; i < V; ++i) e[i] = from_f<E>(to_f(e[i]) * s);
+  __builtin_memcpy(&x, e, 16);
+  return x;
+}
+
+// Sum over the 16 lanes of a row group (lanes with equal l / 16).
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 4, 64);
+  x += __shfl_xor(x, 8, 64);
+  return x;
+}
+// Sum over the 4 lanes sharing a column (lanes with equal l % 16).
+__device__ __forceinline__ float sum4(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ float wave_incl_scan(float x) {
   const int l = lane_id();
@@ -152,6 +190,17 @@ __device__ __forceinline__ float wave_incl_scan(float x) {
   for (int d = 1; d < 64; d <<= 1) {
     const float y = __shfl_up(x, d, 64);
     if (l >= d) x += y;
+  }
+  return x;
+}
+
+// Inclusive suffix sum across the 64 lanes of a wave.
+__device__ __forceinline__ float wave_incl_suffix(float x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float y = __shfl_down(x, d, 64);
+    if (l + d < 64) x += y;
   }
   return x;
 }

@@ -1,384 +1,8 @@
-// lrt_fwd.hip -- chunkwise forward of the gated delta-rule mixers on gfx950.
-//
-// The recurrences (state H = S^T, [d_k, d_v]) are those of the mixers on the
-// AMD ROCm blog "Pretraining hybrid LLMs with Primus", section "How hybrid
-// models are defined in Primus" (mixer list under Table 2).  Inside a chunk of
-// C tokens with start state Hn, g = inclusive cumsum of log a, gamma = e^g:
-//   A     = strict_lower(diag(b) (K K^T) o Gamma),   Gamma_ij = e^(g_i - g_j)
-//   Tinv  = (I + A)^-1
-//   W     = Tinv diag(b gamma) K,   U' = Tinv diag(b) V           (chunk prep)
-//   U     = U' - W Hn,   H_next = gamma_C Hn + Ktil^T U,  Ktil_j = e^(g_C - g_j) k_j
-//                                                              (state pass)
-//   O     = diag(gamma) Q Hn + ((Q K^T) o Gamma_incl) U           (output)
-// SSD has no beta and no delta term (U = V).  Every exponent is a difference
-// g_later - g_earlier <= 0, so nothing overflows however strong the decay.
-//
-// Three kernels, all 256 threads:
-//   k_prep  one workgroup per (b, h, chunk): gates, K K^T, (I + A)^-1, W, U', Ktil
-//   k_state one workgroup per (b, h, d_v block): serial over chunks, state in
-//           MFMA accumulators, writes each chunk's start state S_n and U
-//   k_out   one workgroup per (b, h, chunk): O = gamma Q Hn + P U
-// Workspace tiles are chunk-major per (b, h): tile = (b*H + h)*N + n.
-#include <type_traits>
-
-#include "lrt_common.hpp"
+// lrt_fwd.hip -- launchers of the chunkwise forward (gdn_fwd, ssd_fwd).
+#include "lrt_fwd_kernels.hpp"
 #include "lrt_internal.hpp"
 
 namespace lrt {
-
-// ------------------------------------------------------------------ k_prep
-template <typename E, int C, int DK, int DV, bool DELTA>
-__global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ k, const E* __restrict__ v,
-                                                   const float* __restrict__ log_a,
-                                                   const float* __restrict__ beta, int T, int H, int N,
-                                                   E* __restrict__ wW, E* __restrict__ wUp,
-                                                   E* __restrict__ wKt, float* __restrict__ wG) {
-  constexpr int P = lds_pad<E>();
-  constexpr int LK = DK + P;  // rows indexed by token, contiguous over d
-  constexpr int LC = C + P;   // rows indexed by d or v, contiguous over tokens
-  constexpr int NB = C / 16;
-  constexpr int LA = C + 1;
-  __shared__ float sg[C], sgam[C], sb[C];
-  __shared__ __attribute__((aligned(16))) E sK[C * LK];
-  __shared__ __attribute__((aligned(16))) E sYt[DV * LC];
-  __shared__ __attribute__((aligned(16))) E sXt[DELTA ? DK * LC : 8];
-  __shared__ __attribute__((aligned(16))) E sT[DELTA ? C * LC : 8];
-  __shared__ float sA[DELTA ? C * LA : 1];
-  __shared__ float sTf[DELTA ? C * LA : 1];
-  __shared__ float sR[DELTA ? 3 * 256 : 1];
-
-  const int tile = blockIdx.x;
-  const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
-  const int t0 = n * C, nv = min(C, T - t0);
-  const size_t tok0 = (size_t)b * T + t0;
-  const int w = wave_id(), l = lane_id();
-
-  if (threadIdx.x < 64) {
-    const int t = threadIdx.x;
-    float la = 0.f, bt = 0.f;
-    if (t < nv) {
-      la = log_a[(tok0 + t) * H + h];
-      if (DELTA) bt = beta[(tok0 + t) * H + h];
-    }
-    const float g = wave_incl_scan(la);
-    if (t < C) {
-      sg[t] = g;
-      sgam[t] = __expf(g);
-      sb[t] = bt;
-      wG[(size_t)tile * C + t] = g;
-    }
-  }
-  rows_to_lds<E, C, DK>(sK, LK, k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-  __syncthreads();
-
-  // Y^T = (diag(b) V)^T (SSD: V^T) -> sYt[v][t]
-  for (int idx = threadIdx.x; idx < C * DV; idx += kThreads) {
-    const int t = idx / DV, c = idx % DV;
-    float x = 0.f;
-    if (t < nv) x = to_f(v[((tok0 + t) * H + h) * DV + c]);
-    sYt[c * LC + t] = from_f<E>(DELTA ? sb[t] * x : x);
-  }
-  // Ktil^T[d][t] = e^(g_C - g_t) k_t[d] -> workspace
-  {
-    const float gC = sg[C - 1];
-    E* out = wKt + (size_t)tile * DK * C;
-    for (int idx = threadIdx.x; idx < DK * C; idx += kThreads) {
-      const int d = idx / C, t = idx % C;
-      out[idx] = from_f<E>(__expf(gC - sg[t]) * to_f(sK[t * LK + d]));
-    }
-  }
-  if constexpr (!DELTA) {
-    __syncthreads();
-    E* out = wUp + (size_t)tile * DV * C;
-    for (int idx = threadIdx.x; idx < DV * C; idx += kThreads) {
-      const int c = idx / C, t = idx % C;
-      out[idx] = sYt[c * LC + t];
-    }
-    return;
-  } else {
-    // X^T = (diag(b gamma) K)^T -> sXt[d][t]
-    for (int idx = threadIdx.x; idx < C * DK; idx += kThreads) {
-      const int t = idx / DK, d = idx % DK;
-      sXt[d * LC + t] = from_f<E>(sb[t] * sgam[t] * to_f(sK[t * LK + d]));
-    }
-    // A = strict_lower(b_i (k_i . k_j) e^(g_i - g_j))
-    for (int tt = w; tt < NB * NB; tt += kWaves) {
-      const int ti = tt / NB, tj = tt % NB;
-      f32x4 acc = zero4();
-      if (tj <= ti) mma<DK>(acc, sK + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
-      const int j = tj * 16 + (l & 15);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = ti * 16 + (l >> 4) * 4 + r;
-        sA[i * LA + j] = (j < i) ? sb[i] * acc[r] * __expf(sg[i] - sg[j]) : 0.f;
-      }
-    }
-    __syncthreads();
-    // (I + A)^-1, stage 1: the 16x16 diagonal blocks by forward substitution,
-    // one lane per column (lanes 16*bb .. 16*bb+15 own block bb).
-    if (threadIdx.x < 16 * NB) {
-      const int bb = threadIdx.x >> 4, j = threadIdx.x & 15;
-      const float* Ab = sA + (bb * 16) * LA + bb * 16;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = (r == j) ? 1.f : 0.f;
-#pragma unroll
-        for (int m = 0; m < r; ++m) s -= Ab[r * LA + m] * x[m];
-        x[r] = s;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sTf[(bb * 16 + r) * LA + bb * 16 + j] = x[r];
-    }
-    __syncthreads();
-    // stage 2: block row bi, T[bi][bj] = -T[bi][bi] sum_{m=bj}^{bi-1} A[bi][m] T[m][bj]
-    {
-      const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
-      for (int bi = 1; bi < NB; ++bi) {
-        for (int bj = 0; bj < bi; ++bj) {
-          float s = 0.f;
-          for (int m = bj * 16; m < bi * 16; ++m) s += sA[(bi * 16 + r) * LA + m] * sTf[m * LA + bj * 16 + c];
-          sR[bj * 256 + r * 16 + c] = s;
-        }
-        __syncthreads();
-        for (int bj = 0; bj < bi; ++bj) {
-          float s = 0.f;
-#pragma unroll
-          for (int m = 0; m < 16; ++m) s += sTf[(bi * 16 + r) * LA + bi * 16 + m] * sR[bj * 256 + m * 16 + c];
-          sTf[(bi * 16 + r) * LA + bj * 16 + c] = -s;
-        }
-        __syncthreads();
-      }
-    }
-    for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
-      const int i = idx / C, j = idx % C;
-      sT[i * LC + j] = from_f<E>(j <= i ? sTf[i * LA + j] : 0.f);
-    }
-    __syncthreads();
-    // W^T = X^T Tinv^T (rows d, cols t) -> W[t][d]
-    E* wout = wW + (size_t)tile * C * DK;
-    for (int tt = w; tt < (DK / 16) * NB; tt += kWaves) {
-      const int td = tt / NB, tc = tt % NB;
-      f32x4 acc = zero4();
-      mma<C>(acc, sXt + td * 16 * LC, LC, sT + tc * 16 * LC, LC);
-      store4<E>(wout + (size_t)(tc * 16 + (l & 15)) * DK + td * 16 + (l >> 4) * 4, acc);
-    }
-    // U' = Tinv Y (rows t, cols v) -> U'^T[v][t]
-    E* uout = wUp + (size_t)tile * DV * C;
-    for (int tt = w; tt < NB * (DV / 16); tt += kWaves) {
-      const int ti = tt / (DV / 16), tv = tt % (DV / 16);
-      f32x4 acc = zero4();
-      mma<C>(acc, sT + ti * 16 * LC, LC, sYt + tv * 16 * LC, LC);
-      store4<E>(uout + (size_t)(tv * 16 + (l & 15)) * C + ti * 16 + (l >> 4) * 4, acc);
-    }
-  }
-}
-
-// ----------------------------------------------------------------- k_state
-// One workgroup per (b, h, d_v block of BV columns); walks the N chunks.
-template <typename E, int C, int DK, int BV, bool DELTA>
-__global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, const E* __restrict__ wUp,
-                                                    const E* __restrict__ wKt, const float* __restrict__ wG,
-                                                    const float* h0, float* ht, E* __restrict__ wU,
-                                                    E* __restrict__ wS, int N, int DV) {
-  constexpr int P = lds_pad<E>();
-  constexpr int LK = DK + P, LC = C + P;
-  constexpr int NTV = BV / 16;
-  constexpr int NH = (DK / 16) * NTV;  // state tiles
-  constexpr int HPW = (NH + kWaves - 1) / kWaves;
-  constexpr int NU = (C / 16) * NTV;  // U tiles
-  constexpr int UPW = (NU + kWaves - 1) / kWaves;
-  constexpr int V16 = 16 / (int)sizeof(E);
-  constexpr int NW16 = DELTA ? C * DK / V16 : 0;
-  constexpr int NK16 = DK * C / V16;
-  constexpr int PW = (NW16 + kThreads - 1) / kThreads;
-  constexpr int PK = (NK16 + kThreads - 1) / kThreads;
-  __shared__ __attribute__((aligned(16))) E sW[DELTA ? C * LK : 8];
-  __shared__ __attribute__((aligned(16))) E sKt[DK * LC];
-  __shared__ __attribute__((aligned(16))) E sS[DELTA ? BV * LK : 8];
-  __shared__ __attribute__((aligned(16))) E sU[BV * LC];
-
-  const int nvb = DV / BV;
-  const int vb = blockIdx.x % nvb, bh = blockIdx.x / nvb;
-  const int v0 = vb * BV;
-  const int w = wave_id(), l = lane_id();
-
-  f32x4 hacc[HPW];
-#pragma unroll
-  for (int s = 0; s < HPW; ++s) {
-    const int tt = w + kWaves * s;
-    hacc[s] = zero4();
-    if (tt < NH && h0 != nullptr) {
-      const int td = tt / NTV, tv = tt % NTV;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        hacc[s][r] = h0[((size_t)bh * DK + td * 16 + (l >> 4) * 4 + r) * DV + v0 + tv * 16 + (l & 15)];
-    }
-  }
-
-  uint4 rW[PW > 0 ? PW : 1], rK[PK];
-  f32x4 rUp[UPW];
-  float rgc = 0.f;
-  auto fetch = [&](int n) {
-    const size_t tile = (size_t)bh * N + n;
-    const uint4* gw = (const uint4*)(wW + tile * C * DK);
-    const uint4* gk = (const uint4*)(wKt + tile * DK * C);
-#pragma unroll
-    for (int s = 0; s < PW; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (idx < NW16) rW[s] = gw[idx];
-    }
-#pragma unroll
-    for (int s = 0; s < PK; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (idx < NK16) rK[s] = gk[idx];
-    }
-#pragma unroll
-    for (int s = 0; s < UPW; ++s) {
-      const int tt = w + kWaves * s;
-      if (tt < NU) {
-        const int ti = tt / NTV, tv = tt % NTV;
-        rUp[s] = load4<E>(wUp + tile * DV * C + (size_t)(v0 + tv * 16 + (l & 15)) * C + ti * 16 + (l >> 4) * 4);
-      }
-    }
-    rgc = wG[tile * C + C - 1];
-  };
-
-  fetch(0);
-  for (int n = 0; n < N; ++n) {
-    const size_t tile = (size_t)bh * N + n;
-#pragma unroll
-    for (int s = 0; s < PW; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (idx < NW16) {
-        const int e = idx * V16;
-        *(uint4*)(sW + (e / DK) * LK + e % DK) = rW[s];
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < PK; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (idx < NK16) {
-        const int e = idx * V16;
-        *(uint4*)(sKt + (e / C) * LC + e % C) = rK[s];
-      }
-    }
-    f32x4 up[UPW];
-#pragma unroll
-    for (int s = 0; s < UPW; ++s) up[s] = rUp[s];
-    const float dec = __expf(rgc);
-    if (n + 1 < N) fetch(n + 1);
-
-    // chunk start state: S = H^T -> LDS (operand of W Hn) and workspace
-#pragma unroll
-    for (int s = 0; s < HPW; ++s) {
-      const int tt = w + kWaves * s;
-      if (tt < NH) {
-        const int td = tt / NTV, tv = tt % NTV;
-        const int vv = tv * 16 + (l & 15), d = td * 16 + (l >> 4) * 4;
-        if (DELTA) store4<E>(sS + vv * LK + d, hacc[s]);
-        store4<E>(wS + tile * DV * DK + (size_t)(v0 + vv) * DK + d, hacc[s]);
-      }
-    }
-    __syncthreads();
-    // U = U' - W Hn  (rows t, cols v)
-#pragma unroll
-    for (int s = 0; s < UPW; ++s) {
-      const int tt = w + kWaves * s;
-      if (tt < NU) {
-        const int ti = tt / NTV, tv = tt % NTV;
-        const int vv = tv * 16 + (l & 15), t = ti * 16 + (l >> 4) * 4;
-        f32x4 u = up[s];
-        if constexpr (DELTA) {
-          f32x4 acc = zero4();
-          mma<DK>(acc, sW + ti * 16 * LK, LK, sS + tv * 16 * LK, LK);
-          u -= acc;
-        }
-        store4<E>(sU + vv * LC + t, u);
-        store4<E>(wU + tile * DV * C + (size_t)(v0 + vv) * C + t, u);
-      }
-    }
-    __syncthreads();
-    // H <- e^(g_C) H + Ktil^T U
-#pragma unroll
-    for (int s = 0; s < HPW; ++s) {
-      const int tt = w + kWaves * s;
-      if (tt < NH) {
-        const int td = tt / NTV, tv = tt % NTV;
-        hacc[s] *= dec;
-        mma<C>(hacc[s], sKt + td * 16 * LC, LC, sU + tv * 16 * LC, LC);
-      }
-    }
-    __syncthreads();
-  }
-  if (ht != nullptr) {
-#pragma unroll
-    for (int s = 0; s < HPW; ++s) {
-      const int tt = w + kWaves * s;
-      if (tt < NH) {
-        const int td = tt / NTV, tv = tt % NTV;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          ht[((size_t)bh * DK + td * 16 + (l >> 4) * 4 + r) * DV + v0 + tv * 16 + (l & 15)] = hacc[s][r];
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------- k_out
-// O^T = S Q^T (scaled by gamma per token) + U^T P^T, one workgroup per
-// (chunk, block of BVO value columns).
-template <typename E, int C, int DK, int BVO>
-__global__ __launch_bounds__(kThreads) void k_out(const E* __restrict__ q, const E* __restrict__ k,
-                                                  const float* __restrict__ wG, const E* __restrict__ wS,
-                                                  const E* __restrict__ wU, E* __restrict__ o, int T, int H,
-                                                  int N, int DV) {
-  constexpr int P = lds_pad<E>();
-  constexpr int LK = DK + P, LC = C + P;
-  constexpr int NB = C / 16;
-  __shared__ float sg[C];
-  __shared__ __attribute__((aligned(16))) E sQ[C * LK];
-  __shared__ __attribute__((aligned(16))) E sK[C * LK];
-  __shared__ __attribute__((aligned(16))) E sS[BVO * LK];
-  __shared__ __attribute__((aligned(16))) E sU[BVO * LC];
-  __shared__ __attribute__((aligned(16))) E sP[C * LC];
-
-  const int nvb = DV / BVO;
-  const int tile = blockIdx.x / nvb, v0 = (blockIdx.x % nvb) * BVO;
-  const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
-  const int t0 = n * C, nv = min(C, T - t0);
-  const size_t tok0 = (size_t)b * T + t0;
-  const int w = wave_id(), l = lane_id();
-
-  rows_to_lds<E, C, DK>(sQ, LK, q + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-  rows_to_lds<E, C, DK>(sK, LK, k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-  block_to_lds<E, BVO, DK>(sS, LK, wS + ((size_t)tile * DV + v0) * DK);
-  block_to_lds<E, BVO, C>(sU, LC, wU + ((size_t)tile * DV + v0) * C);
-  if (threadIdx.x < C) sg[threadIdx.x] = wG[(size_t)tile * C + threadIdx.x];
-  __syncthreads();
-  // P = (Q K^T) o Gamma, inclusive lower triangle
-  for (int tt = w; tt < NB * NB; tt += kWaves) {
-    const int ti = tt / NB, tj = tt % NB;
-    f32x4 acc = zero4();
-    if (tj <= ti) mma<DK>(acc, sQ + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
-    const int j = tj * 16 + (l & 15);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = ti * 16 + (l >> 4) * 4 + r;
-      sP[i * LC + j] = from_f<E>(j <= i ? acc[r] * __expf(sg[i] - sg[j]) : 0.f);
-    }
-  }
-  __syncthreads();
-  for (int tt = w; tt < (BVO / 16) * NB; tt += kWaves) {
-    const int tv = tt / NB, ti = tt % NB;
-    f32x4 acc = zero4();
-    mma<DK>(acc, sS + tv * 16 * LK, LK, sQ + ti * 16 * LK, LK);
-    const int i = ti * 16 + (l & 15);
-    acc *= __expf(sg[i]);
-    mma<C>(acc, sU + tv * 16 * LC, LC, sP + ti * 16 * LC, LC);
-    if (i < nv) store4<E>(o + ((tok0 + i) * H + h) * DV + v0 + tv * 16 + (l >> 4) * 4, acc);
-  }
-}
 
 // --------------------------------------------------------------- launchers
 template <typename E, int C, int DK, int DV>
@@ -390,10 +14,10 @@ int fwd_impl(const FwdArgs& a) {
   const bool delta = a.variant == kVarGDN;
   if (delta)
     hipLaunchKernelGGL((k_prep<E, C, DK, DV, true>), dim3(tiles), dim3(kThreads), 0, st, (const E*)a.k,
-                       (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.G);
+                       (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.G, (E*)nullptr);
   else
     hipLaunchKernelGGL((k_prep<E, C, DK, DV, false>), dim3(tiles), dim3(kThreads), 0, st, (const E*)a.k,
-                       (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.G);
+                       (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.G, (E*)nullptr);
   constexpr int BV = DV < 32 ? DV : 32;
   const int sgrid = a.B * a.H * (DV / BV);
   if (delta)
