@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet training step on one MI355X.
+
+One step = gdn_fwd + gdn_bwd (all six gradients) over one batch of the
+pretraining-shaped workload: B=16 sequences of T=2048 tokens, H=8 heads,
+d_k = d_v = 128, chunk 64, bf16 tensors, fp32 gates and state (the shape of
+the 2048-token bf16 runs on the AMD ROCm blog "Pretraining hybrid LLMs with
+Primus", Table 4).  Inputs are synthetic (seeded), resident in HBM before the
+timed region, and rotated over three independent sets so that no step reads
+the previous step's inputs out of the 256 MB last-level cache.
+
+Prints one JSON line with the step throughput (tokens/s), a roofline entry
+for the kernel that takes most of the step's time (its algorithmic bytes or
+flops per launch over its average duration, timed with HIP events on its own
+stream) and a CPU baseline (the fp64 oracle on a bounded sample).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+MFMA_FP32_PEAK_TFLOPS = 157.3
+WORKLOAD = "gdn_train_bf16_2k"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--sets", type=int, default=3, help="independent input sets rotated over the steps")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (events), via ctypes."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            rc = self.lib.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            arr[i] = e.value
+        return arr
+
+    def elapsed_ms(self, a, b):
+        out = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(out.value)
+
+    def destroy(self, arr):
+        for e in arr:
+            self.lib.hipEventDestroy(e)
+
+
+def kernel_model(name, c, esz=2):
+    """Algorithmic (bytes, flops) of one launch of a library kernel on workload c.
+
+    Bytes: each tensor the kernel must read or write, counted once.  Flops:
+    the dense GEMM products the kernel's step of the method needs (2*M*N*K
+    each; the (I + A)^-1 solve and elementwise work excluded).
+    """
+    B, T, H, dk, dv, C = c["B"], c["T"], c["H"], c["dk"], c["dv"], c["chunk"]
+    ht = B * T * H
+    tiles = B * H * ((T + C - 1) // C)
+    per_ht = {
+        # reads k, v, log_a, beta; writes W, U'^T, Ktil^T, g, Tinv
+        "k_prep": ((dk + dv) * esz + 8 + (2 * dk + dv) * esz + 4 + C * esz,
+                   2 * C * dk + 2 * C * dk + 2 * C * dv),
+        # reads W, U'^T, Ktil^T, g; writes U^T and the chunk-start states
+        "k_state": ((2 * dk + dv) * esz + 4 + dv * esz + dk * dv * esz / C, 4 * dk * dv),
+        # reads q, k, states, U, g; writes o
+        "k_out": (2 * dk * esz + dk * dv * esz / C + dv * esz + 4 + dv * esz, 2 * C * dk + 2 * dk * dv + 2 * C * dv),
+        # reads q, k, do, g; writes dU_local
+        "k_bwd_local": (2 * dk * esz + 2 * dv * esz + 4, 2 * C * dk + 2 * C * dv),
+        # reads q, k, do, W, dU_local, g; writes dU and the end-state gradients
+        "k_dstate": (3 * dk * esz + 2 * dv * esz + 4 + dv * esz + dk * dv * esz / C, 6 * dk * dv),
+        # reads q, k, do, U, dU, states, state grads, g; writes dq, dW, dK part, dg part
+        "k_grad1": (2 * dk * esz + 3 * dv * esz + 2 * dk * dv * esz / C + 4 + dk * esz + dk * esz + dk * 4 + 4,
+                    2 * C * dk + 2 * C * dv + 2 * dk * dv + 2 * C * dk + 2 * dk * dv + 2 * dk * dv + 2 * C * dk),
+        # reads k, v, beta, g, Tinv, dW, dU, dK part, dg part; writes dk, dv, dlog_a, dbeta
+        "k_grad2": (dk * esz + dv * esz + 8 + C * esz + dk * esz + dv * esz + dk * 4 + 4 + dk * esz + dv * esz + 8,
+                    2 * C * dk + 2 * C * dv + 2 * C * dk + 2 * C * dv + 4 * C * C + 2 * C * dk + 4 * C * dk),
+    }
+    if name not in per_ht:
+        return None
+    b, f = per_ht[name]
+    return b * ht, f * ht
+
+
+def make_sets(L, synth, torch, c, nsets):
+    sets = []
+    for s in range(nsets):
+        inp = synth.config_inputs(WORKLOAD, device="cuda", seed=s)
+        sets.append(inp)
+    return sets
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the mixer's hot path is measured on one MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import linear_recurrent_token_amd as L
+    from linear_recurrent_token_amd import synth
+
+    L.lib()
+    c = dict(synth.CONFIGS[WORKLOAD])
+    B, T, H, dk, dv, C = c["B"], c["T"], c["H"], c["dk"], c["dv"], c["chunk"]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    sets = make_sets(L, synth, torch, c, args.sets)
+    code = L.LRT_BF16
+    ws_bytes = max(L.workspace_bytes(L.OP_GDN_FWD, B, T, H, dk, dv, C, code),
+                   L.workspace_bytes(L.OP_GDN_BWD, B, T, H, dk, dv, C, code))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    grads = (torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
+             torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
+             torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev),
+             torch.empty((B, T, H), dtype=torch.float32, device=dev),
+             torch.empty((B, T, H), dtype=torch.float32, device=dev),
+             torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev))
+
+    def step(i):
+        s = sets[i % len(sets)]
+        L.gdn_fwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s["h0"], chunk=C, o=o, ht=ht, workspace=ws)
+        L.gdn_bwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s["h0"], s["do"], s.get("dht"), chunk=C,
+                  workspace=ws, out=grads)
+
+    hip = Hip()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: throughput
+    ev = hip.events(2)
+    t0 = time.perf_counter()
+    hip.lib.hipEventRecord(ctypes.c_void_p(ev[0]), ctypes.c_void_p(stream))
+    for i in range(args.steps):
+        step(i)
+    hip.lib.hipEventRecord(ctypes.c_void_p(ev[1]), ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = hip.elapsed_ms(ev[0], ev[1])
+    hip.destroy(ev)
+    ms_per_step = ms / args.steps
+    tokens = B * T
+    value = tokens * args.steps / (ms / 1e3)
+
+    # timed region again, every library kernel bracketed by HIP events
+    per_step_kernels = 16
+    nk = per_step_kernels * args.steps
+    kev = hip.events(2 * nk)
+    kinds = (ctypes.c_int * nk)()
+    L.lib().lrt_profile_attach(ctypes.cast(kev, ctypes.c_void_p), ctypes.cast(kinds, ctypes.c_void_p), nk)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    n_rec = L.lib().lrt_profile_count()
+    L.lib().lrt_profile_attach(None, None, 0)
+    dur = {}
+    for i in range(n_rec):
+        name = L.lib().lrt_kernel_name(kinds[i]).decode()
+        dur.setdefault(name, []).append(hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]))
+    hip.destroy(kev)
+    kernels = {n: {"launches": len(d), "avg_us": 1e3 * sum(d) / len(d), "total_us_per_step": 1e3 * sum(d) / args.steps}
+               for n, d in dur.items()}
+    dom = max(kernels, key=lambda n: kernels[n]["total_us_per_step"])
+    model = kernel_model(dom, c)
+    roof = None
+    if model is not None:
+        nbytes, flops = model
+        # launches of the dominant kernel per step carry the same work
+        per_launch_bytes = nbytes
+        per_launch_flops = flops
+        avg_s = kernels[dom]["avg_us"] / 1e6
+        intensity = per_launch_flops / per_launch_bytes
+        ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if intensity < ridge:
+            ach = per_launch_bytes / avg_s / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                    "algorithmic_bytes": int(per_launch_bytes), "algorithmic_flops": int(per_launch_flops),
+                    "avg_us": round(kernels[dom]["avg_us"], 2)}
+        else:
+            ach = per_launch_flops / avg_s / 1e12
+            roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": dom, "algorithmic_bytes": int(per_launch_bytes),
+                    "algorithmic_flops": int(per_launch_flops), "avg_us": round(kernels[dom]["avg_us"], 2)}
+
+    # algorithmic step totals: GEMM flops of the method (forward + backward)
+    flops_fwd = (2 * C * (3 * dk + 2 * dv) + 6 * dk * dv) * B * T * H
+    flops_bwd = (12 * C * dk + 8 * C * dv + 12 * dk * dv + 4 * C * C) * B * T * H
+    step_tflops = (flops_fwd + flops_bwd) / (ms_per_step / 1e3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(sets[0], C, args.cpu_seconds)
+
+    line = {
+        "metric": "GDN chunked fwd+bwd tokens/s (B=16 T=2048 H=8 d=128, chunk 64)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal inputs; 3 rotating input sets resident in HBM)",
+        "config": {"workload": WORKLOAD, "B": B, "T": T, "H": H, "d_k": dk, "d_v": dv, "chunk": C,
+                   "op": "gdn_fwd + gdn_bwd"},
+        "step_tflops": round(step_tflops, 2),
+        "mfma_frac_of_bf16_peak": round(step_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roof,
+        "kernels": {n: {k: round(v, 2) if isinstance(v, float) else v for k, v in d.items()}
+                    for n, d in kernels.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(inp, C, target_s):
+    """The fp64 oracle (forward + backward) on whole sequences of the first
+    batch rows, adding rows until about target_s seconds of CPU work."""
+    import oracle
+
+    cpu = {k: (v.detach().cpu() if v is not None else None) for k, v in inp.items()}
+    B, T, H = cpu["q"].shape[:3]
+    cores = oracle.max_threads()
+    per = max(1, min(B, -(-cores // H)))  # rows per call: enough (b, h) tasks for every core
+    done_tokens, spent, rows = 0, 0.0, 0
+    while rows < B and spent < target_s:
+        sl = slice(rows, min(B, rows + per))
+        a = {k: (v[sl].contiguous() if v is not None else None) for k, v in cpu.items()}
+        t0 = time.perf_counter()
+        oracle.fwd("gdn", a["q"], a["k"], a["v"], a["log_a"], a["beta"], a["h0"])
+        oracle.bwd("gdn", a["q"], a["k"], a["v"], a["log_a"], a["beta"], a["h0"], a["do"], a.get("dht"))
+        spent += time.perf_counter() - t0
+        done_tokens += T * (sl.stop - sl.start)
+        rows = sl.stop
+    return {"value": round(done_tokens / spent, 1), "unit": "tokens/s", "cores": min(cores, per * H),
+            "kind": "oracle",
+            "sample": f"{rows} of {B} sequences x {T} tokens x {H} heads, fp64 forward + backward "
+                      f"({spent:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -122,6 +122,20 @@ size_t lrt_workspace_bytes(int op, int B, int T, int H, int d_k, int d_v, int ch
 /* Static, human-readable text for a status code. */
 const char* lrt_status_string(int status);
 
+/*
+ * Per-kernel timing hook for benchmarks (the only process-wide state of the
+ * library; not thread-safe).  After lrt_profile_attach(events, kinds, n),
+ * the next n kernels the library enqueues are each bracketed by
+ * hipEventRecord(events[2i]) and hipEventRecord(events[2i + 1]) on the
+ * kernel's own stream, and kinds[i] receives the kernel's id.  `events`
+ * holds 2n hipEvent_t created by the caller; `kinds` holds n ints.  Passing
+ * NULL detaches.  lrt_profile_count() returns the kernels recorded since the
+ * last attach; lrt_kernel_name(id) a static name for an id.
+ */
+int lrt_profile_attach(void** events, int* kinds, int n_kernels);
+int lrt_profile_count(void);
+const char* lrt_kernel_name(int kind);
+
 #ifdef __cplusplus
 }
 #endif

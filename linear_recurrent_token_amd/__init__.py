@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(HERE, "liblrt.so")
 
 LRT_F32, LRT_BF16 = 0, 1
 OP_GDN_FWD, OP_GDN_BWD, OP_KDA_FWD, OP_SSD_FWD = 0, 1, 2, 3
-EXPORTS = ("gdn_fwd", "gdn_bwd", "kda_fwd", "ssd_fwd", "lrt_workspace_bytes", "lrt_status_string")
+EXPORTS = ("gdn_fwd", "gdn_bwd", "kda_fwd", "ssd_fwd", "lrt_workspace_bytes", "lrt_status_string",
+           "lrt_profile_attach", "lrt_profile_count", "lrt_kernel_name")
 
 _lib = None
 
@@ -54,6 +55,11 @@ def lib():
         L.lrt_workspace_bytes.restype = sz
         L.lrt_status_string.argtypes = [ci]
         L.lrt_status_string.restype = ctypes.c_char_p
+        L.lrt_profile_attach.argtypes = [vp, vp, ci]
+        L.lrt_profile_attach.restype = ci
+        L.lrt_profile_count.restype = ci
+        L.lrt_kernel_name.argtypes = [ci]
+        L.lrt_kernel_name.restype = ctypes.c_char_p
         _lib = L
     return _lib
 

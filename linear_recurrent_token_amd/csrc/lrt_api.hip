@@ -9,6 +9,31 @@
 
 namespace lrt {
 
+// ---------------------------------------------------------------- timing hook
+// Process-wide; only the benchmark attaches it.
+static struct {
+  hipEvent_t* ev = nullptr;
+  int* kinds = nullptr;
+  int n = 0;     // kernels that fit
+  int next = 0;  // kernels recorded
+} g_prof;
+
+void prof_before(int kind, void* stream) {
+  if (g_prof.ev == nullptr || g_prof.next >= g_prof.n) return;
+  g_prof.kinds[g_prof.next] = kind;
+  hipEventRecord(g_prof.ev[2 * g_prof.next], (hipStream_t)stream);
+}
+
+void prof_after(void* stream) {
+  if (g_prof.ev == nullptr || g_prof.next >= g_prof.n) return;
+  hipEventRecord(g_prof.ev[2 * g_prof.next + 1], (hipStream_t)stream);
+  ++g_prof.next;
+}
+
+static const char* const kKernelNames[kKNumKinds] = {"k_prep",  "k_state", "k_out",     "k_bwd_local",
+                                                     "k_dstate", "k_grad1", "k_grad2",   "k_kda_prep",
+                                                     "k_state_copy"};
+
 // ht = h0 (or zeros) for an empty sequence.
 __global__ void k_state_copy(const float* __restrict__ h0, float* ht, size_t n) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -39,8 +64,7 @@ static size_t ws_bytes(int op, int B, int T, int H, int dk, int dv, int chunk, i
 static int launch_empty(const float* h0, float* ht, int B, int H, int dk, int dv, void* stream) {
   if (ht == nullptr || ht == h0) return LRT_OK;
   const size_t n = (size_t)B * H * dk * dv;
-  hipLaunchKernelGGL(k_state_copy, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, h0, ht,
-                     n);
+  LRT_LAUNCH(kKStateCopy, k_state_copy, dim3((unsigned)((n + 255) / 256)), dim3(256), stream, h0, ht, n);
   return hipGetLastError() == hipSuccess ? LRT_OK : LRT_ERR_LAUNCH;
 }
 
@@ -121,6 +145,26 @@ size_t lrt_workspace_bytes(int op, int B, int T, int H, int d_k, int d_v, int ch
   if (op < LRT_OP_GDN_FWD || op > LRT_OP_SSD_FWD) return (size_t)-1;
   if (check_common(B, T, H, d_k, d_v, chunk, dtype) != LRT_OK) return (size_t)-1;
   return ws_bytes(op, B, T, H, d_k, d_v, chunk, dtype);
+}
+
+int lrt_profile_attach(void** events, int* kinds, int n_kernels) {
+  if (events == nullptr || kinds == nullptr || n_kernels <= 0) {
+    g_prof.ev = nullptr;
+    g_prof.kinds = nullptr;
+    g_prof.n = g_prof.next = 0;
+    return LRT_OK;
+  }
+  g_prof.ev = (hipEvent_t*)events;
+  g_prof.kinds = kinds;
+  g_prof.n = n_kernels;
+  g_prof.next = 0;
+  return LRT_OK;
+}
+
+int lrt_profile_count(void) { return g_prof.next; }
+
+const char* lrt_kernel_name(int kind) {
+  return (kind >= 0 && kind < kKNumKinds) ? kKernelNames[kind] : "unknown";
 }
 
 const char* lrt_status_string(int status) {

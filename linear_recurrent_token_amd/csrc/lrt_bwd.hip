@@ -688,22 +688,22 @@ int bwd_impl(const BwdArgs& a) {
     hipStream_t st = (hipStream_t)a.stream;
     constexpr int BV = DV < 32 ? DV : 32;
     const int sgrid = a.B * a.H * (DV / BV);
-    hipLaunchKernelGGL((k_prep<E, C, DK, DV, true, true>), dim3(tiles), dim3(kThreads), 0, st, (const E*)a.k,
+    LRT_LAUNCH(kKPrep, (k_prep<E, C, DK, DV, true, true>), dim3(tiles), dim3(kThreads), st, (const E*)a.k,
                        (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, (E*)ws.f.W, (E*)ws.f.Up, (E*)ws.f.Kt,
                        ws.f.G, (E*)ws.T);
-    hipLaunchKernelGGL((k_state<E, C, DK, BV, true>), dim3(sgrid), dim3(kThreads), 0, st, (const E*)ws.f.W,
-                       (const E*)ws.f.Up, (const E*)ws.f.Kt, ws.f.G, a.h0, (float*)nullptr, (E*)ws.f.U,
+    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, true>), dim3(sgrid), dim3(kThreads), st, (const E*)ws.f.W,
+                       (const E*)ws.f.Up, (const E*)ws.f.Kt, ws.f.G, (const float*)nullptr, a.h0, (float*)nullptr, (E*)ws.f.U,
                        (E*)ws.f.S, N, DV);
     E* dUl = (E*)ws.f.Up;
-    hipLaunchKernelGGL((k_bwd_local<E, C, DK, DV>), dim3(tiles), dim3(kThreads), 0, st, (const E*)a.q,
+    LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV>), dim3(tiles), dim3(kThreads), st, (const E*)a.q,
                        (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N);
-    hipLaunchKernelGGL((k_dstate<E, C, DK, BV>), dim3(sgrid), dim3(kThreads), 0, st, (const E*)a.q,
+    LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV>), dim3(sgrid), dim3(kThreads), st, (const E*)a.q,
                        (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.W, (const E*)dUl, a.dht, a.dh0,
                        (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
-    hipLaunchKernelGGL((k_grad1<E, C, DK, DV>), dim3(tiles), dim3(kThreads), 0, st, (const E*)a.q,
+    LRT_LAUNCH(kKGrad1, (k_grad1<E, C, DK, DV>), dim3(tiles), dim3(kThreads), st, (const E*)a.q,
                        (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.S, (const E*)ws.dS,
                        (const E*)ws.f.U, (const E*)ws.dU, (E*)a.dq, (E*)ws.dW, ws.dK1, ws.dg1, a.T, a.H, N);
-    hipLaunchKernelGGL((k_grad2<E, C, DK, DV>), dim3(tiles), dim3(kThreads), 0, st, (const E*)a.k,
+    LRT_LAUNCH(kKGrad2, (k_grad2<E, C, DK, DV>), dim3(tiles), dim3(kThreads), st, (const E*)a.k,
                        (const E*)a.v, a.beta, ws.f.G, (const E*)ws.T, (const E*)ws.dW, (const E*)ws.dU, ws.dK1,
                        ws.dg1, (E*)a.dk_out, (E*)a.dv_out, a.dlog_a, a.dbeta, a.T, a.H, N);
     return hipGetLastError() == hipSuccess ? 0 : -7;

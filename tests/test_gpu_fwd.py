@@ -139,3 +139,38 @@ def test_fwd_deterministic():
     b = L.gdn_fwd(inp["q"], inp["k"], inp["v"], inp["log_a"], inp["beta"], inp["h0"])
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+KDA_CASES = [
+    # name, B, T, H, dk, dv, chunk, dtype, gate kind, gate_shift, h0_std
+    ("kda_fp32_perdim_C16", 1, 70, 2, 32, 32, 16, torch.float32, "perdim", 0.0, 0.1),
+    ("kda_fp32_slow_C64", 1, 150, 2, 64, 64, 64, torch.float32, "perdim", -6.0, 0.1),
+    ("kda_bf16_perdim_C64", 2, 200, 2, 128, 128, 64, torch.bfloat16, "perdim", 0.0, 0.1),
+    ("kda_bf16_perdim_fast_C32", 1, 130, 2, 128, 128, 32, torch.bfloat16, "perdim", 2.0, 0.1),
+    ("kda_bf16_slow_T61_C16", 2, 61, 2, 64, 32, 16, torch.bfloat16, "perdim", -6.0, 0.1),
+    ("kda_bf16_lowrank_C64", 1, 256, 4, 128, 128, 64, torch.bfloat16, "lowrank", 0.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", KDA_CASES, ids=[c[0] for c in KDA_CASES])
+def test_kda_fwd_small(case):
+    name, B, T, H, dk, dv, chunk, dt, gate, shift, h0s = case
+    say(f"[fwd] {name}")
+    inp = synth.make_inputs("kda_fwd", B, T, H, dk, dv, dtype=dt, seed=0, device="cuda", gate=gate,
+                            gate_shift=shift, h0_std=h0s)
+    eo, eh = run_fwd("kda", inp, chunk)
+    say(f"  rel err o={eo:.2e} ht={eh:.2e}")
+    assert eo <= TOL[dt] and eh <= TOL[dt], (eo, eh)
+
+
+def test_kda_uniform_gate_matches_gdn_kernel():
+    """A per-dimension gate that is equal over d_k must give the GDN result."""
+    L = lrt()
+    inp = synth.make_inputs("gdn_fwd", 1, 200, 2, 128, 128, dtype=torch.bfloat16, device="cuda",
+                            gate_shift=0.0, h0_std=0.1)
+    q, k, v, la, beta, h0 = (inp[n] for n in ("q", "k", "v", "log_a", "beta", "h0"))
+    og, hg = L.gdn_fwd(q, k, v, la, beta, h0)
+    ok, hk = L.kda_fwd(q, k, v, la[..., None].expand(1, 200, 2, 128).contiguous(), beta, h0)
+    torch.cuda.synchronize()
+    assert rel(ok.float().cpu(), og.float().cpu()) <= 1e-2
+    assert rel(hk.cpu(), hg.cpu()) <= 1e-2
