@@ -91,15 +91,17 @@ __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q,
   const size_t tok0 = (size_t)b * T + t0;
   const int w = wave_id(), l = lane_id();
 
-  rows_to_lds<E, C, DK>(sQ, LK, q + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-  rows_to_lds<E, C, DK>(sK, LK, k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-  for (int idx = threadIdx.x; idx < C * (DV / V); idx += kThreads) {
-    const int r = idx / (DV / V), c = (idx % (DV / V)) * V;
-    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    if (r < nv) x = *(const uint4*)(d_o + ((tok0 + r) * H + h) * DV + c);
-    vec_to_lds_T<E>(sdOt, LC, r, c, x);
+  {
+    Tile<E, C, DK> tq, tk;
+    Tile<E, C, DV> to;
+    tq.load_rows(q + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+    tk.load_rows(k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+    to.load_rows(d_o + (tok0 * H + h) * DV, (size_t)H * DV, nv);
+    if (threadIdx.x < C) sg[threadIdx.x] = wG[(size_t)tile * C + threadIdx.x];
+    tq.store(sQ, LK);
+    tk.store(sK, LK);
+    to.store_T(sdOt, LC);
   }
-  if (threadIdx.x < C) sg[threadIdx.x] = wG[(size_t)tile * C + threadIdx.x];
   __syncthreads();
   for (int tt = w; tt < NB * NB; tt += kWaves) {
     const int ti = tt / NB, tj = tt % NB;
@@ -141,6 +143,7 @@ __global__ __launch_bounds__(kThreads) void k_dstate(const E* __restrict__ q, co
   __shared__ __attribute__((aligned(16))) E sKt[C * LK];   // Ktil, row-major
   __shared__ __attribute__((aligned(16))) E sdS[BV * LK];  // dH'^T
   __shared__ float sg[C];
+  __shared__ float sgs[2 * C];
 
   const int nvb = DV / BV;
   const int vb = blockIdx.x % nvb, bh = blockIdx.x / nvb;
@@ -160,44 +163,29 @@ __global__ __launch_bounds__(kThreads) void k_dstate(const E* __restrict__ q, co
     }
   }
 
-  uint4 rQ[PQ], rK[PQ], rW[PQ], rO[PO];
+  Tile<E, C, DK> tQ, tK, tW;
+  Tile<E, C, BV> tO;
   f32x4 rU[UPW];
   float rg = 0.f;
-  auto fetch = [&](int n) {
-    const size_t tile = (size_t)bh * N + n;
-    const int t0 = n * C, nv = min(C, T - t0);
-    const size_t tok0 = (size_t)b * T + t0;
-#pragma unroll
-    for (int s = 0; s < PQ; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (idx < NQ) {
-        const int r = idx / PR, c = (idx % PR) * V;
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        rQ[s] = r < nv ? *(const uint4*)(q + ((tok0 + r) * H + h) * DK + c) : z;
-        rK[s] = r < nv ? *(const uint4*)(k + ((tok0 + r) * H + h) * DK + c) : z;
-        rW[s] = *(const uint4*)(wW + tile * C * DK + (size_t)idx * V);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < PO; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (idx < NO) {
-        const int r = idx / PRO, c = (idx % PRO) * V;
-        rO[s] = r < nv ? *(const uint4*)(d_o + ((tok0 + r) * H + h) * DV + v0 + c) : make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < UPW; ++s) {
-      const int tt = w + kWaves * s;
-      if (tt < NU) {
-        const int ti = tt / NTV, tv = tt % NTV;
-        rU[s] = load4<E>(wdUl + tile * DV * C + (size_t)(v0 + tv * 16 + (l & 15)) * C + ti * 16 + (l >> 4) * 4);
-      }
-    }
-    rg = threadIdx.x < C ? wG[tile * C + threadIdx.x] : 0.f;
-  };
+#define LRT_DSTATE_FETCH(n_)                                                                        \
+  {                                                                                                 \
+    const size_t ft = (size_t)bh * N + (n_);                                                        \
+    const int fnv = min(C, T - (n_) * C);                                                           \
+    const size_t ftok = (size_t)b * T + (size_t)(n_) * C;                                           \
+    tQ.load_rows(q + (ftok * H + h) * DK, (size_t)H * DK, fnv);                                     \
+    tK.load_rows(k + (ftok * H + h) * DK, (size_t)H * DK, fnv);                                     \
+    tW.load_block(wW + ft * C * DK);                                                                \
+    tO.load_rows(d_o + (ftok * H + h) * DV + v0, (size_t)H * DV, fnv);                              \
+    _Pragma("unroll") for (int s = 0; s < UPW; ++s) {                                               \
+      const int tt = w + kWaves * s;                                                                \
+      if (tt < NU)                                                                                  \
+        rU[s] = load4<E>(wdUl + ft * DV * C + (size_t)(v0 + (tt % NTV) * 16 + (l & 15)) * C +      \
+                         (tt / NTV) * 16 + (l >> 4) * 4);                                           \
+    }                                                                                               \
+    rg = threadIdx.x < C ? wG[ft * C + threadIdx.x] : 0.f;                                          \
+  }
 
-  fetch(N - 1);
+  LRT_DSTATE_FETCH(N - 1)
   for (int n = N - 1; n >= 0; --n) {
     const size_t tile = (size_t)bh * N + n;
     if (threadIdx.x < C) sg[threadIdx.x] = rg;
@@ -214,28 +202,24 @@ __global__ __launch_bounds__(kThreads) void k_dstate(const E* __restrict__ q, co
     }
     __syncthreads();
     const float gC = sg[C - 1];
-#pragma unroll
-    for (int s = 0; s < PQ; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (idx < NQ) {
-        const int r = idx / PR, c = (idx % PR) * V;
-        vec_to_lds_T<E>(sA2, L2, r, c, rQ[s]);
-        vec_to_lds_T<E>(sA2 + C, L2, r, c, rW[s]);
-        *(uint4*)(sKt + r * LK + c) = vec_scale<E>(rK[s], __expf(gC - sg[r]));
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < PO; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (idx < NO) {
-        const int r = idx / PRO, c = (idx % PRO) * V;
-        vec_to_lds_T<E>(sB2, L2, r, c, vec_scale<E>(rO[s], __expf(sg[r])));
+    tQ.store_T(sA2, L2);
+    tW.store_T(sA2 + C, L2);
+    {
+      float* sc = sgs;  // e^(g_C - g_t) and gamma_t, per token
+      if (threadIdx.x < C) {
+        sc[threadIdx.x] = __expf(gC - sg[threadIdx.x]);
+        sc[C + threadIdx.x] = __expf(sg[threadIdx.x]);
       }
     }
     f32x4 du[UPW];
 #pragma unroll
     for (int s = 0; s < UPW; ++s) du[s] = rU[s];
-    if (n > 0) fetch(n - 1);
+    __syncthreads();
+    tK.scale_rows(sgs);
+    tK.store(sKt, LK);
+    tO.scale_rows(sgs + C);
+    tO.store_T(sB2, L2);
+    if (n > 0) LRT_DSTATE_FETCH(n - 1)
     __syncthreads();
     // dU = dU_local + Ktil dH'  (rows t, cols v)
 #pragma unroll
@@ -264,6 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_dstate(const E* __restrict__ q, co
     }
     __syncthreads();
   }
+#undef LRT_DSTATE_FETCH
   if (dh0 != nullptr) {
 #pragma unroll
     for (int s = 0; s < HPW; ++s) {
@@ -332,19 +317,31 @@ __global__ __launch_bounds__(kThreads) void k_grad1(const E* __restrict__ q, con
   const size_t tok0 = (size_t)b * T + t0;
   const int w = wave_id(), l = lane_id();
 
-  rows_to_lds<E, C, DK>(sQ, LK, q + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-  rows_to_lds<E, C, DK>(sK, LK, k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-  rows_to_lds<E, C, DV>(sdO, LV, d_o + (tok0 * H + h) * DV, (size_t)H * DV, nv);
-  for (int idx = threadIdx.x; idx < DV * (C / V); idx += kThreads) {
-    const int vv = idx / (C / V), c = (idx % (C / V)) * V;
-    vec_to_lds_T<E>(sU, LV, vv, c, *(const uint4*)(wU + (size_t)tile * DV * C + (size_t)vv * C + c));
+  Tile<E, C, DK> tq, tk;
+  {
+    Tile<E, C, DV> to;
+    Tile<E, DV, C> tu;
+    tq.load_rows(q + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+    tk.load_rows(k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+    to.load_rows(d_o + (tok0 * H + h) * DV, (size_t)H * DV, nv);
+    tu.load_block(wU + (size_t)tile * DV * C);
+    if (threadIdx.x < C) {
+      sg[threadIdx.x] = wG[(size_t)tile * C + threadIdx.x];
+      sdg[threadIdx.x] = 0.f;
+    }
+    if (threadIdx.x == 0) sdot[0] = 0.f;
+    tq.store(sQ, LK);
+    tk.store(sK, LK);
+    to.store(sdO, LV);
+    tu.store_T(sU, LV);
   }
-  if (threadIdx.x < C) {
-    sg[threadIdx.x] = wG[(size_t)tile * C + threadIdx.x];
-    sdg[threadIdx.x] = 0.f;
-  }
-  if (threadIdx.x == 0) sdot[0] = 0.f;
   __syncthreads();
+  // states, state gradients and dU of this chunk: in flight during dS
+  Tile<E, DV, DK> tS, tdS;
+  Tile<E, DV, C> tdU;
+  tS.load_block(wS + (size_t)tile * DV * DK);
+  tdS.load_block(wdS + (size_t)tile * DV * DK);
+  tdU.load_block(wdU + (size_t)tile * DV * C);
 
   // dS = (dO U^T) o Gamma (inclusive); E = dS o (Q K^T) -> dg rows +, cols -
   for (int tt = w; tt < NB * NB; tt += kWaves) {
@@ -372,29 +369,27 @@ __global__ __launch_bounds__(kThreads) void k_grad1(const E* __restrict__ q, con
 #pragma unroll
     for (int r = 0; r < 4; ++r) sdSij[(i0 + r) * LC + j] = from_f<E>(ds[r]);
   }
-  // Q^T, K^T
-  for (int idx = threadIdx.x; idx < C * (DK / V); idx += kThreads) {
-    const int r = idx / (DK / V), c = (idx % (DK / V)) * V;
-    vec_to_lds_T<E>(sQt, LC, r, c, *(const uint4*)(sQ + r * LK + c));
-    vec_to_lds_T<E>(sKt, LC, r, c, *(const uint4*)(sK + r * LK + c));
-  }
+  // Q^T, K^T from the registers still holding q and k
+  tq.store_T(sQt, LC);
+  tk.store_T(sKt, LC);
   __syncthreads();
-  // Hn [d][v] into R23, dU [t][v] into R1; <dH', Hn> from the workspace
+  // Hn [d][v] into R23, dU [t][v] into R1; <dH', Hn> from the same registers
   E* sH = (E*)(smem + Lay::R23);
   E* sdU = (E*)(smem + Lay::R1);
-  for (int idx = threadIdx.x; idx < DV * (DK / V); idx += kThreads) {
-    const int vv = idx / (DK / V), c = (idx % (DK / V)) * V;
-    vec_to_lds_T<E>(sH, LV, vv, c, *(const uint4*)(wS + (size_t)tile * DV * DK + (size_t)vv * DK + c));
-  }
-  for (int idx = threadIdx.x; idx < DV * (C / V); idx += kThreads) {
-    const int vv = idx / (C / V), c = (idx % (C / V)) * V;
-    vec_to_lds_T<E>(sdU, LV, vv, c, *(const uint4*)(wdU + (size_t)tile * DV * C + (size_t)vv * C + c));
-  }
+  tS.store_T(sH, LV);
+  tdU.store_T(sdU, LV);
   {
     float part = 0.f;
-    const E* a = wS + (size_t)tile * DV * DK;
-    const E* d = wdS + (size_t)tile * DV * DK;
-    for (int idx = threadIdx.x; idx < DV * DK; idx += kThreads) part += to_f(a[idx]) * to_f(d[idx]);
+#pragma unroll
+    for (int s2 = 0; s2 < tS.PT; ++s2) {
+      if (threadIdx.x + kThreads * s2 < tS.NP) {
+        E a[V], d[V];
+        __builtin_memcpy(a, &tS.x[s2], 16);
+        __builtin_memcpy(d, &tdS.x[s2], 16);
+#pragma unroll
+        for (int e = 0; e < V; ++e) part += to_f(a[e]) * to_f(d[e]);
+      }
+    }
     part = sum16(part);
     part = sum4(part);
     if (l == 0) atomicAdd(sdot, part);
@@ -422,10 +417,7 @@ __global__ __launch_bounds__(kThreads) void k_grad1(const E* __restrict__ q, con
   __syncthreads();
   // dH' [d][v] into R23
   E* sdH = (E*)(smem + Lay::R23);
-  for (int idx = threadIdx.x; idx < DV * (DK / V); idx += kThreads) {
-    const int vv = idx / (DK / V), c = (idx % (DK / V)) * V;
-    vec_to_lds_T<E>(sdH, LV, vv, c, *(const uint4*)(wdS + (size_t)tile * DV * DK + (size_t)vv * DK + c));
-  }
+  tdS.store_T(sdH, LV);
   __syncthreads();
   // dK1^T = e^(g_C - g_j) (dH' U^T) + Q^T dS   (rows d, cols j)
   const float gC = sg[C - 1];
@@ -508,28 +500,25 @@ __global__ __launch_bounds__(kThreads) void k_grad2(const E* __restrict__ k, con
   const size_t tok0 = (size_t)b * T + t0;
   const int w = wave_id(), l = lane_id();
 
-  for (int idx = threadIdx.x; idx < C * (DK / V); idx += kThreads) {
-    const int r = idx / (DK / V), c = (idx % (DK / V)) * V;
-    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    if (r < nv) x = *(const uint4*)(k + ((tok0 + r) * H + h) * DK + c);
-    *(uint4*)(sK + r * LK + c) = x;
-    vec_to_lds_T<E>(sKt, LC, r, c, x);
-    const uint4 y = *(const uint4*)(wdW + (size_t)tile * C * DK + (size_t)r * DK + c);
-    *(uint4*)(sdW + r * LK + c) = y;
-    vec_to_lds_T<E>(sdWt, LC, r, c, y);
-  }
-  rows_to_lds<E, C, DV>(sV, LV, v + (tok0 * H + h) * DV, (size_t)H * DV, nv);
-  for (int idx = threadIdx.x; idx < C * (C / V); idx += kThreads) {
-    const int r = idx / (C / V), c = (idx % (C / V)) * V;
-    const uint4 x = *(const uint4*)(wT + (size_t)tile * C * C + (size_t)r * C + c);
-    *(uint4*)(sT + r * LC + c) = x;
-    vec_to_lds_T<E>(sTt, LC, r, c, x);
-  }
-  for (int idx = threadIdx.x; idx < DV * (C / V); idx += kThreads) {
-    const int vv = idx / (C / V), c = (idx % (C / V)) * V;
-    const uint4 x = *(const uint4*)(wdU + (size_t)tile * DV * C + (size_t)vv * C + c);
-    *(uint4*)(sdUt + vv * LC + c) = x;
-    vec_to_lds_T<E>(sdU, LV, vv, c, x);
+  {
+    Tile<E, C, DK> tk, tdw;
+    Tile<E, C, DV> tv;
+    Tile<E, C, C> tt;
+    Tile<E, DV, C> tdu;
+    tk.load_rows(k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+    tdw.load_block(wdW + (size_t)tile * C * DK);
+    tv.load_rows(v + (tok0 * H + h) * DV, (size_t)H * DV, nv);
+    tt.load_block(wT + (size_t)tile * C * C);
+    tdu.load_block(wdU + (size_t)tile * DV * C);
+    tk.store(sK, LK);
+    tk.store_T(sKt, LC);
+    tdw.store(sdW, LK);
+    tdw.store_T(sdWt, LC);
+    tv.store(sV, LV);
+    tt.store(sT, LC);
+    tt.store_T(sTt, LC);
+    tdu.store(sdUt, LC);
+    tdu.store_T(sdU, LV);
   }
   if (threadIdx.x < C) {
     const int t = threadIdx.x;

@@ -17,6 +17,9 @@ typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16 raw bytes in four VGPRs (a native vector, so register arrays of it stay in
+// registers; HIP's uint4 is a class type)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -120,35 +123,10 @@ __device__ __forceinline__ f32x4 load4(const E* p) {
   return Vec4<E>::unpack(*(const typename Vec4<E>::T*)p);
 }
 
-// Copy R rows of W elements from global (row stride gs elements) into LDS
-// (row stride ls), 16 bytes per access; rows >= nvalid become zero.
-template <typename E, int R, int W>
-__device__ __forceinline__ void rows_to_lds(E* lds, int ls, const E* g, size_t gs, int nvalid) {
-  constexpr int V = 16 / (int)sizeof(E);
-  constexpr int PR = W / V;
-  for (int idx = threadIdx.x; idx < R * PR; idx += kThreads) {
-    const int r = idx / PR, c = (idx % PR) * V;
-    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    if (r < nvalid) x = *(const uint4*)(g + (size_t)r * gs + c);
-    *(uint4*)(lds + r * ls + c) = x;
-  }
-}
-
-// Copy a dense block of R x W elements (contiguous in global) into LDS.
-template <typename E, int R, int W>
-__device__ __forceinline__ void block_to_lds(E* lds, int ls, const E* g) {
-  constexpr int V = 16 / (int)sizeof(E);
-  constexpr int PR = W / V;
-  for (int idx = threadIdx.x; idx < R * PR; idx += kThreads) {
-    const int r = idx / PR, c = (idx % PR) * V;
-    *(uint4*)(lds + r * ls + c) = *(const uint4*)(g + (size_t)r * W + c);
-  }
-}
-
 // Scatter the 16 bytes x (elements c0.. of row r of a row-major source) into
 // an LDS array stored transposed: lds[(c0 + e) * ld + r].
 template <typename E>
-__device__ __forceinline__ void vec_to_lds_T(E* lds, int ld, int r, int c0, uint4 x) {
+__device__ __forceinline__ void vec_to_lds_T(E* lds, int ld, int r, int c0, u32x4 x) {
   constexpr int V = 16 / (int)sizeof(E);
   E e[V];
   __builtin_memcpy(e, &x, 16);
@@ -158,7 +136,7 @@ __device__ __forceinline__ void vec_to_lds_T(E* lds, int ld, int r, int c0, uint
 
 // Elementwise scale of the 16 bytes x by s (in fp32, rounded back to E).
 template <typename E>
-__device__ __forceinline__ uint4 vec_scale(uint4 x, float s) {
+__device__ __forceinline__ u32x4 vec_scale(u32x4 x, float s) {
   constexpr int V = 16 / (int)sizeof(E);
   E e[V];
   __builtin_memcpy(e, &x, 16);
@@ -166,6 +144,85 @@ __device__ __forceinline__ uint4 vec_scale(uint4 x, float s) {
   for (int i = 0; i < V; ++i) e[i] = from_f<E>(to_f(e[i]) * s);
   __builtin_memcpy(&x, e, 16);
   return x;
+}
+
+// An R x W tile of E moved global -> registers -> LDS in 16-byte pieces.
+// Every load of a tile is issued before the first LDS store, so a thread
+// keeps all its loads in flight at once (the loops unroll completely).
+template <typename E, int R, int W>
+struct Tile {
+  static constexpr int V = 16 / (int)sizeof(E);
+  static constexpr int PR = W / V;  // pieces per row
+  static constexpr int NP = R * PR;
+  static constexpr int PT = (NP + kThreads - 1) / kThreads;
+  u32x4 x[PT];
+
+  // rows of a strided global array; rows >= nvalid read as zero
+  __device__ __forceinline__ void load_rows(const E* g, size_t gs, int nvalid) {
+#pragma unroll
+    for (int s = 0; s < PT; ++s) {
+      const int idx = threadIdx.x + kThreads * s;
+      x[s] = u32x4{0u, 0u, 0u, 0u};
+      if (idx < NP) {
+        const int r = idx / PR, c = (idx % PR) * V;
+        if (r < nvalid) x[s] = *(const u32x4*)(g + (size_t)r * gs + c);
+      }
+    }
+  }
+  // a dense, contiguous R x W block
+  __device__ __forceinline__ void load_block(const E* g) {
+#pragma unroll
+    for (int s = 0; s < PT; ++s) {
+      const int idx = threadIdx.x + kThreads * s;
+      if (idx < NP) x[s] = *(const u32x4*)(g + (size_t)idx * V);
+    }
+  }
+  __device__ __forceinline__ void scale_rows(const float* rs) {
+#pragma unroll
+    for (int s = 0; s < PT; ++s) {
+      const int idx = threadIdx.x + kThreads * s;
+      if (idx < NP) x[s] = vec_scale<E>(x[s], rs[idx / PR]);
+    }
+  }
+  // lds[r * ls + c]
+  __device__ __forceinline__ void store(E* lds, int ls) const {
+#pragma unroll
+    for (int s = 0; s < PT; ++s) {
+      const int idx = threadIdx.x + kThreads * s;
+      if (idx < NP) {
+        const int r = idx / PR, c = (idx % PR) * V;
+        *(u32x4*)(lds + r * ls + c) = x[s];
+      }
+    }
+  }
+  // transposed: lds[c * ld + r]
+  __device__ __forceinline__ void store_T(E* lds, int ld) const {
+#pragma unroll
+    for (int s = 0; s < PT; ++s) {
+      const int idx = threadIdx.x + kThreads * s;
+      if (idx < NP) {
+        const int r = idx / PR, c = (idx % PR) * V;
+        vec_to_lds_T<E>(lds, ld, r, c, x[s]);
+      }
+    }
+  }
+};
+
+// Copy R rows of W elements from global (row stride gs elements) into LDS
+// (row stride ls); rows >= nvalid become zero.
+template <typename E, int R, int W>
+__device__ __forceinline__ void rows_to_lds(E* lds, int ls, const E* g, size_t gs, int nvalid) {
+  Tile<E, R, W> t;
+  t.load_rows(g, gs, nvalid);
+  t.store(lds, ls);
+}
+
+// Copy a dense block of R x W elements (contiguous in global) into LDS.
+template <typename E, int R, int W>
+__device__ __forceinline__ void block_to_lds(E* lds, int ls, const E* g) {
+  Tile<E, R, W> t;
+  t.load_block(g);
+  t.store(lds, ls);
 }
 
 // Sum over the 16 lanes of a row group (lanes with equal l / 16).

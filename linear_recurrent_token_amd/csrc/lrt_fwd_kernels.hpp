@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ k, cons
   constexpr int LC = C + P;   // rows indexed by d or v, contiguous over tokens
   constexpr int NB = C / 16;
   constexpr int LA = C + 1;
-  __shared__ float sg[C], sgam[C], sb[C];
+  __shared__ float sg[C], sgam[C], sb[C], sbg[C];
   __shared__ __attribute__((aligned(16))) E sK[C * LK];
   __shared__ __attribute__((aligned(16))) E sYt[DV * LC];
   __shared__ __attribute__((aligned(16))) E sXt[DELTA ? DK * LC : 8];
@@ -102,6 +102,10 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ k, cons
   const size_t tok0 = (size_t)b * T + t0;
   const int w = wave_id(), l = lane_id();
 
+  Tile<E, C, DK> tk;
+  Tile<E, C, DV> tv;
+  tk.load_rows(k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+  tv.load_rows(v + (tok0 * H + h) * DV, (size_t)H * DV, nv);
   if (threadIdx.x < 64) {
     const int t = threadIdx.x;
     float la = 0.f, bt = 0.f;
@@ -114,42 +118,44 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ k, cons
       sg[t] = g;
       sgam[t] = __expf(g);
       sb[t] = bt;
+      sbg[t] = bt * __expf(g);
       wG[(size_t)tile * C + t] = g;
     }
   }
-  rows_to_lds<E, C, DK>(sK, LK, k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+  tk.store(sK, LK);
   __syncthreads();
 
   // Y^T = (diag(b) V)^T (SSD: V^T) -> sYt[v][t]
-  for (int idx = threadIdx.x; idx < C * DV; idx += kThreads) {
-    const int t = idx / DV, c = idx % DV;
-    float x = 0.f;
-    if (t < nv) x = to_f(v[((tok0 + t) * H + h) * DV + c]);
-    sYt[c * LC + t] = from_f<E>(DELTA ? sb[t] * x : x);
-  }
-  // Ktil^T[d][t] = e^(g_C - g_t) k_t[d] -> workspace
+  if (DELTA) tv.scale_rows(sb);
+  tv.store_T(sYt, LC);
+  // Ktil^T[d][t] = e^(g_C - g_t) k_t[d] -> workspace, 16 bytes per store
   {
+    constexpr int V = 16 / (int)sizeof(E);
     const float gC = sg[C - 1];
     E* out = wKt + (size_t)tile * DK * C;
-    for (int idx = threadIdx.x; idx < DK * C; idx += kThreads) {
-      const int d = idx / C, t = idx % C;
-      out[idx] = from_f<E>(__expf(gC - sg[t]) * to_f(sK[t * LK + d]));
+    for (int idx = threadIdx.x; idx < DK * (C / V); idx += kThreads) {
+      const int d = idx / (C / V), t = (idx % (C / V)) * V;
+      E e[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) e[i] = from_f<E>(__expf(gC - sg[t + i]) * to_f(sK[(t + i) * LK + d]));
+      u32x4 x;
+      __builtin_memcpy(&x, e, 16);
+      *(u32x4*)(out + (size_t)d * C + t) = x;
     }
   }
   if constexpr (!DELTA) {
     __syncthreads();
+    constexpr int V = 16 / (int)sizeof(E);
     E* out = wUp + (size_t)tile * DV * C;
-    for (int idx = threadIdx.x; idx < DV * C; idx += kThreads) {
-      const int c = idx / C, t = idx % C;
-      out[idx] = sYt[c * LC + t];
+    for (int idx = threadIdx.x; idx < DV * (C / V); idx += kThreads) {
+      const int c = idx / (C / V), t = (idx % (C / V)) * V;
+      *(u32x4*)(out + (size_t)c * C + t) = *(const u32x4*)(sYt + c * LC + t);
     }
     return;
   } else {
-    // X^T = (diag(b gamma) K)^T -> sXt[d][t]
-    for (int idx = threadIdx.x; idx < C * DK; idx += kThreads) {
-      const int t = idx / DK, d = idx % DK;
-      sXt[d * LC + t] = from_f<E>(sb[t] * sgam[t] * to_f(sK[t * LK + d]));
-    }
+    // X^T = (diag(b gamma) K)^T -> sXt[d][t], from the registers of K
+    tk.scale_rows(sbg);
+    tk.store_T(sXt, LC);
     // A = strict_lower(b_i (k_i . k_j) e^(g_i - g_j))
     for (int tt = w; tt < NB * NB; tt += kWaves) {
       const int ti = tt / NB, tj = tt % NB;
@@ -233,62 +239,37 @@ __global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, co
     }
   }
 
-  uint4 rW[PW > 0 ? PW : 1], rK[PK];
+  Tile<E, C, DK> tW;   // W of the next chunk (delta variants)
+  Tile<E, DK, C> tK;   // Ktil^T of the next chunk
   f32x4 rUp[UPW];
   f32x4 rgd[PERDIM ? HPW : 1];
   float rgc = 0.f;
-  auto fetch = [&](int n) {
-    const size_t tile = (size_t)bh * N + n;
-    const uint4* gw = (const uint4*)(wW + tile * C * DK);
-    const uint4* gk = (const uint4*)(wKt + tile * DK * C);
-#pragma unroll
-    for (int s = 0; s < PW; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (idx < NW16) rW[s] = gw[idx];
-    }
-#pragma unroll
-    for (int s = 0; s < PK; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (idx < NK16) rK[s] = gk[idx];
-    }
-#pragma unroll
-    for (int s = 0; s < UPW; ++s) {
-      const int tt = w + kWaves * s;
-      if (tt < NU) {
-        const int ti = tt / NTV, tv = tt % NTV;
-        rUp[s] = load4<E>(wUp + tile * DV * C + (size_t)(v0 + tv * 16 + (l & 15)) * C + ti * 16 + (l >> 4) * 4);
-      }
-    }
-    if constexpr (PERDIM) {
-#pragma unroll
-      for (int s = 0; s < HPW; ++s) {
-        const int tt = w + kWaves * s;
-        if (tt < NH) rgd[s] = *(const f32x4*)(wGC + tile * DK + (tt / NTV) * 16 + (l >> 4) * 4);
-      }
-    } else {
-      rgc = wG[tile * C + C - 1];
-    }
-  };
+#define LRT_STATE_FETCH(n_)                                                                         \
+  {                                                                                                 \
+    const size_t ft = (size_t)bh * N + (n_);                                                        \
+    if (DELTA) tW.load_block(wW + ft * C * DK);                                                     \
+    tK.load_block(wKt + ft * DK * C);                                                               \
+    _Pragma("unroll") for (int s = 0; s < UPW; ++s) {                                               \
+      const int tt = w + kWaves * s;                                                                \
+      if (tt < NU)                                                                                  \
+        rUp[s] = load4<E>(wUp + ft * DV * C + (size_t)(v0 + (tt % NTV) * 16 + (l & 15)) * C +      \
+                          (tt / NTV) * 16 + (l >> 4) * 4);                                          \
+    }                                                                                               \
+    if constexpr (PERDIM) {                                                                         \
+      _Pragma("unroll") for (int s = 0; s < HPW; ++s) {                                             \
+        const int tt = w + kWaves * s;                                                              \
+        if (tt < NH) rgd[s] = *(const f32x4*)(wGC + ft * DK + (tt / NTV) * 16 + (l >> 4) * 4);     \
+      }                                                                                             \
+    } else {                                                                                        \
+      rgc = wG[ft * C + C - 1];                                                                     \
+    }                                                                                               \
+  }
 
-  fetch(0);
+  LRT_STATE_FETCH(0)
   for (int n = 0; n < N; ++n) {
     const size_t tile = (size_t)bh * N + n;
-#pragma unroll
-    for (int s = 0; s < PW; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (idx < NW16) {
-        const int e = idx * V16;
-        *(uint4*)(sW + (e / DK) * LK + e % DK) = rW[s];
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < PK; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
-      if (idx < NK16) {
-        const int e = idx * V16;
-        *(uint4*)(sKt + (e / C) * LC + e % C) = rK[s];
-      }
-    }
+    if (DELTA) tW.store(sW, LK);
+    tK.store(sKt, LC);
     f32x4 up[UPW];
 #pragma unroll
     for (int s = 0; s < UPW; ++s) up[s] = rUp[s];
@@ -299,7 +280,8 @@ __global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, co
       for (int s = 0; s < HPW; ++s)
         decd[s] = f32x4{__expf(rgd[s][0]), __expf(rgd[s][1]), __expf(rgd[s][2]), __expf(rgd[s][3])};
     }
-    if (n + 1 < N) fetch(n + 1);
+    if (n + 1 < N) LRT_STATE_FETCH(n + 1)
+#undef LRT_STATE_FETCH
 
     // chunk start state: S = H^T -> LDS (operand of W Hn) and workspace
 #pragma unroll
@@ -388,16 +370,29 @@ __global__ __launch_bounds__(kThreads) void k_out(const E* __restrict__ q, const
   const size_t tok0 = (size_t)b * T + t0;
   const int w = wave_id(), l = lane_id();
 
-  if constexpr (FROM_WS) {
-    block_to_lds<E, C, DK>(sQ, LK, wQg + (size_t)tile * C * DK);
-    block_to_lds<E, C, C>(sP, LC, wP + (size_t)tile * C * C);
-  } else {
-    rows_to_lds<E, C, DK>(sQ, LK, q + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-    rows_to_lds<E, C, DK>(sK, LK, k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-    if (threadIdx.x < C) sg[threadIdx.x] = wG[(size_t)tile * C + threadIdx.x];
+  {
+    Tile<E, C, DK> tq;
+    Tile<E, FROM_WS ? C : C, FROM_WS ? C : DK> tk;  // K rows, or P (FROM_WS)
+    Tile<E, BVO, DK> ts;
+    Tile<E, BVO, C> tu;
+    if constexpr (FROM_WS) {
+      tq.load_block(wQg + (size_t)tile * C * DK);
+      tk.load_block(wP + (size_t)tile * C * C);
+    } else {
+      tq.load_rows(q + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+      tk.load_rows(k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+      if (threadIdx.x < C) sg[threadIdx.x] = wG[(size_t)tile * C + threadIdx.x];
+    }
+    ts.load_block(wS + ((size_t)tile * DV + v0) * DK);
+    tu.load_block(wU + ((size_t)tile * DV + v0) * C);
+    tq.store(sQ, LK);
+    if constexpr (FROM_WS)
+      tk.store(sP, LC);
+    else
+      tk.store(sK, LK);
+    ts.store(sS, LK);
+    tu.store(sU, LC);
   }
-  block_to_lds<E, BVO, DK>(sS, LK, wS + ((size_t)tile * DV + v0) * DK);
-  block_to_lds<E, BVO, C>(sU, LC, wU + ((size_t)tile * DV + v0) * C);
   __syncthreads();
   // P = (Q K^T) o Gamma, inclusive lower triangle
   if constexpr (!FROM_WS) {

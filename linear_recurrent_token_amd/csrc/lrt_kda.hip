@@ -71,13 +71,17 @@ __global__ __launch_bounds__(kThreads) void k_kda_prep(const E* __restrict__ q, 
   const size_t tok0 = (size_t)b * T + t0;
   const int w = wave_id(), l = lane_id();
 
-  rows_to_lds<E, C, DK>(sK, LK, k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-  rows_to_lds<E, C, DK>(sQ, LK, q + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-  for (int idx = threadIdx.x; idx < C * (DK / 4); idx += kThreads) {
-    const int t = idx / (DK / 4), d = (idx % (DK / 4)) * 4;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < nv) x = *(const float4*)(log_a + ((tok0 + t) * H + h) * DK + d);
-    *(float4*)(sG + t * LG + d) = x;
+  Tile<E, C, DV> tv;  // v, stored after the solve
+  {
+    Tile<E, C, DK> tk, tq;
+    Tile<float, C, DK> tg;
+    tk.load_rows(k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+    tq.load_rows(q + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+    tg.load_rows(log_a + (tok0 * H + h) * DK, (size_t)H * DK, nv);
+    tv.load_rows(v + (tok0 * H + h) * DV, (size_t)H * DV, nv);
+    tk.store(sK, LK);
+    tq.store(sQ, LK);
+    tg.store(sG, LG);
   }
   if (threadIdx.x < C) sb[threadIdx.x] = threadIdx.x < nv ? beta[(tok0 + threadIdx.x) * H + h] : 0.f;
   for (int idx = threadIdx.x; idx < C * LA; idx += kThreads) sA[idx] = 0.f;
@@ -177,12 +181,8 @@ __global__ __launch_bounds__(kThreads) void k_kda_prep(const E* __restrict__ q, 
     const int t = idx / DK, d = idx % DK;
     sXt[d * LC + t] = from_f<E>(sb[t] * to_f(sK[t * LK + d]) * __expf(sG[t * LG + d]));
   }
-  for (int idx = threadIdx.x; idx < C * (DV / V); idx += kThreads) {
-    const int t = idx / (DV / V), c = (idx % (DV / V)) * V;
-    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    if (t < nv) x = *(const uint4*)(v + ((tok0 + t) * H + h) * DV + c);
-    vec_to_lds_T<E>(sYt, LC, t, c, vec_scale<E>(x, sb[t]));
-  }
+  tv.scale_rows(sb);
+  tv.store_T(sYt, LC);
   unit_lower_inverse<C>(sA, sTf, sR);
   for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
     const int i = idx / C, j = idx % C;
