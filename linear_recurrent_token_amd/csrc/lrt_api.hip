@@ -32,7 +32,18 @@ void prof_after(void* stream) {
 
 static const char* const kKernelNames[kKNumKinds] = {"k_prep",  "k_state", "k_out",     "k_bwd_local",
                                                      "k_dstate", "k_grad1", "k_grad2",   "k_kda_prep",
-                                                     "k_state_copy"};
+                                                     "k_state_copy", "k_fwd"};
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
 
 // ht = h0 (or zeros) for an empty sequence.
 __global__ void k_state_copy(const float* __restrict__ h0, float* ht, size_t n) {

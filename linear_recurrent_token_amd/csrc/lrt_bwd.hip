@@ -34,13 +34,13 @@ namespace lrt {
 //   dS  [dv][dk] E    dH'^T, gradient of each chunk's end state
 //   dU  [dv][C]  E    dU^T
 //   dW  [C][dk]  E    dW
-//   dK1 [C][dk]  f32  the dS / state part of dK
+//   dK1 [C][dk]  E    the dS / state part of dK (accumulator-tile order, as dW)
 //   dg1 [C]      f32  part of dg
 // dU_local reuses the forward's U' tiles (dead once the state pass has run).
 struct BwdWs {
   FwdWs f;
-  void *T, *dS, *dU, *dW;
-  float *dK1, *dg1;
+  void *T, *dS, *dU, *dW, *dK1;
+  float* dg1;
   size_t bytes;
 };
 
@@ -59,7 +59,7 @@ static BwdWs bwd_ws_layout(int B, int T, int H, int dk, int dv, int C, size_t es
   w.dS = take(tiles * dv * dk * esz);
   w.dU = take(tiles * dv * C * esz);
   w.dW = take(tiles * C * dk * esz);
-  w.dK1 = (float*)take(tiles * C * dk * sizeof(float));
+  w.dK1 = take(tiles * C * dk * esz);
   w.dg1 = (float*)take(tiles * C * sizeof(float));
   w.bytes = off;
   return w;
@@ -72,88 +72,119 @@ size_t bwd_ws_extra(int B, int T, int H, int dk, int dv, int C, size_t esz) {
 
 // ------------------------------------------------------------- k_bwd_local
 // dU_local = P^T dO with P = (Q K^T) o Gamma (inclusive), stored as [v][t].
+// Workgroups walk the chunks persistently, prefetching the next one.
+template <typename E, int C, int DK, int DV>
+struct LocalLds {
+  static constexpr int P = lds_pad<E>();
+  static constexpr int LK = DK + P, LV = DV + P, LC = C + P;
+  static constexpr size_t es = sizeof(E);
+  static constexpr size_t QK = 0;  // q rows, k rows; later dU_local^T for the copy-out
+  static constexpr size_t QKS = (2 * (size_t)C * LK > (size_t)DV * LC ? 2 * (size_t)C * LK : (size_t)DV * LC) * es;
+  static constexpr size_t DO = QK + QKS;
+  static constexpr size_t PT = DO + (size_t)C * LV * es;
+  static constexpr size_t G = PT + (size_t)C * LC * es;
+  static constexpr size_t TOTAL = G + C * 4;
+};
+
 template <typename E, int C, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q, const E* __restrict__ k,
                                                         const E* __restrict__ d_o, const float* __restrict__ wG,
-                                                        E* __restrict__ wdUl, int T, int H, int N) {
-  constexpr int P = lds_pad<E>();
-  constexpr int LK = DK + P, LC = C + P, NB = C / 16;
-  constexpr int V = 16 / (int)sizeof(E);
-  __shared__ float sg[C];
-  __shared__ __attribute__((aligned(16))) E sQ[C * LK];
-  __shared__ __attribute__((aligned(16))) E sK[C * LK];
-  __shared__ __attribute__((aligned(16))) E sdOt[DV * LC];
-  __shared__ __attribute__((aligned(16))) E sPt[C * LC];
-
-  const int tile = blockIdx.x;
-  const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
-  const int t0 = n * C, nv = min(C, T - t0);
-  const size_t tok0 = (size_t)b * T + t0;
+                                                        E* __restrict__ wdUl, int T, int H, int N, int ntiles) {
+  typedef LocalLds<E, C, DK, DV> Lay;
+  constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, NB = C / 16;
+  __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
+  E* sQ = (E*)(smem + Lay::QK);
+  E* sK = sQ + C * LK;
+  E* sUl = (E*)(smem + Lay::QK);
+  E* sdO = (E*)(smem + Lay::DO);
+  E* sPt = (E*)(smem + Lay::PT);
+  float* sg = (float*)(smem + Lay::G);
   const int w = wave_id(), l = lane_id();
 
-  {
-    Tile<E, C, DK> tq, tk;
-    Tile<E, C, DV> to;
-    tq.load_rows(q + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-    tk.load_rows(k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-    to.load_rows(d_o + (tok0 * H + h) * DV, (size_t)H * DV, nv);
-    if (threadIdx.x < C) sg[threadIdx.x] = wG[(size_t)tile * C + threadIdx.x];
+  Tile<E, C, DK> tq, tk;
+  Tile<E, C, DV> to;
+  float rg = 0.f;
+#define LRT_LOCAL_LOAD(tile_)                                                             \
+  {                                                                                       \
+    const int ln = (tile_) % N, lbh = (tile_) / N;                                        \
+    const int lnv = min(C, T - ln * C);                                                   \
+    const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                           \
+    const int lh = lbh % H;                                                               \
+    tq.load_rows(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
+    tk.load_rows(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
+    to.load_rows(d_o + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                        \
+    if (threadIdx.x < C) rg = wG[(size_t)(tile_) * C + threadIdx.x];                      \
+  }
+
+  int tile = blockIdx.x;
+  if (tile < ntiles) LRT_LOCAL_LOAD(tile)
+  for (; tile < ntiles; tile += gridDim.x) {
     tq.store(sQ, LK);
     tk.store(sK, LK);
-    to.store_T(sdOt, LC);
-  }
-  __syncthreads();
-  for (int tt = w; tt < NB * NB; tt += kWaves) {
-    const int ti = tt / NB, tj = tt % NB;
-    f32x4 acc = zero4();
-    if (tj <= ti) mma<DK>(acc, sQ + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
-    const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
+    to.store(sdO, LV);
+    if (threadIdx.x < C) sg[threadIdx.x] = rg;
+    lds_barrier();
+    if (tile + (int)gridDim.x < ntiles) LRT_LOCAL_LOAD(tile + (int)gridDim.x)
+    for (int tt = w; tt < NB * NB; tt += kWaves) {
+      const int ti = tt / NB, tj = tt % NB;
+      f32x4 acc = zero4();
+      if (tj <= ti) mma<DK>(acc, sQ + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
+      const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = (j <= i0 + r) ? acc[r] * __expf(sg[i0 + r] - sg[j]) : 0.f;
-    store4<E>(sPt + j * LC + i0, acc);
+      for (int r = 0; r < 4; ++r) acc[r] = (j <= i0 + r) ? acc[r] * __expf(sg[i0 + r] - sg[j]) : 0.f;
+      store4<E>(sPt + j * LC + i0, acc);
+    }
+    lds_barrier();
+    // dU_local = P^T dO (rows j, cols v) -> [v][t] over the dead q, k rows
+    for (int tt = w; tt < NB * (DV / 16); tt += kWaves) {
+      const int tj = tt / (DV / 16), tv = tt % (DV / 16);
+      f32x4 acc = zero4();
+      mma<C, false, true>(acc, sPt + tj * 16 * LC, LC, sdO + tv * 16, LV);
+      store4<E>(sUl + (tv * 16 + (l & 15)) * LC + tj * 16 + (l >> 4) * 4, acc);
+    }
+    lds_barrier();
+    lds_to_block<E, DV, C>(wdUl + (size_t)tile * DV * C, sUl, LC);
+    lds_barrier();
   }
-  __syncthreads();
-  for (int tt = w; tt < NB * (DV / 16); tt += kWaves) {
-    const int tj = tt / (DV / 16), tv = tt % (DV / 16);
-    f32x4 acc = zero4();
-    mma<C>(acc, sPt + tj * 16 * LC, LC, sdOt + tv * 16 * LC, LC);
-    store4<E>(wdUl + (size_t)tile * DV * C + (size_t)(tv * 16 + (l & 15)) * C + tj * 16 + (l >> 4) * 4, acc);
-  }
+#undef LRT_LOCAL_LOAD
 }
 
 // ---------------------------------------------------------------- k_dstate
-// Reverse scan over chunks for one (b, h, block of BV value columns).
-template <typename E, int C, int DK, int BV>
-__global__ __launch_bounds__(kThreads) void k_dstate(const E* __restrict__ q, const E* __restrict__ k,
-                                                     const E* __restrict__ d_o, const float* __restrict__ wG,
-                                                     const E* __restrict__ wW, const E* __restrict__ wdUl,
-                                                     const float* dht, float* dh0, E* __restrict__ wdS,
-                                                     E* __restrict__ wdU, int T, int H, int N, int DV) {
+// Reverse scan over chunks for one (b, h, block of BV value columns), NW
+// waves.  q, W and Ktil stay row-major in LDS; the products contracting over
+// tokens read them with the LDS transpose read, so nothing is transposed by
+// hand.  dH' and dU leave through LDS as coalesced 16-byte rows.
+template <typename E, int C, int DK, int BV, int NW = 8>
+__global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, const E* __restrict__ k,
+                                                    const E* __restrict__ d_o, const float* __restrict__ wG,
+                                                    const E* __restrict__ wW, const E* __restrict__ wdUl,
+                                                    const float* dht, float* dh0, E* __restrict__ wdS,
+                                                    E* __restrict__ wdU, int T, int H, int N, int DV) {
+  constexpr int NT = 64 * NW;
   constexpr int P = lds_pad<E>();
-  constexpr int LK = DK + P, L2 = 2 * C + P;
-  constexpr int V = 16 / (int)sizeof(E);
+  constexpr int LK = DK + P, LC = C + P, LB = BV + P;
   constexpr int NTV = BV / 16;
-  constexpr int NH = (DK / 16) * NTV, HPW = (NH + kWaves - 1) / kWaves;
-  constexpr int NU = (C / 16) * NTV, UPW = (NU + kWaves - 1) / kWaves;
-  constexpr int PR = DK / V;                      // 16-byte pieces per row of q, k, W
-  constexpr int NQ = C * PR, PQ = (NQ + kThreads - 1) / kThreads;
-  constexpr int PRO = BV / V, NO = C * PRO, PO = (NO + kThreads - 1) / kThreads;
-  __shared__ __attribute__((aligned(16))) E sA2[DK * L2];  // [d][t] = Q^T | [d][C+t] = W^T
-  __shared__ __attribute__((aligned(16))) E sB2[BV * L2];  // [v][t] = (gamma dO)^T | [v][C+t] = -dU^T
-  __shared__ __attribute__((aligned(16))) E sKt[C * LK];   // Ktil, row-major
+  constexpr int NH = (DK / 16) * NTV, HPW = (NH + NW - 1) / NW;
+  constexpr int NU = (C / 16) * NTV, UPW = (NU + NW - 1) / NW;
+  __shared__ __attribute__((aligned(16))) E sQ[C * LK];    // q rows
+  __shared__ __attribute__((aligned(16))) E sW[C * LK];    // W rows
+  __shared__ __attribute__((aligned(16))) E sKt[C * LK];   // Ktil rows
+  __shared__ __attribute__((aligned(16))) E sOg[C * LB];   // gamma_t dO rows (this block's columns)
+  __shared__ __attribute__((aligned(16))) E sdU[BV * LC];  // dU^T
   __shared__ __attribute__((aligned(16))) E sdS[BV * LK];  // dH'^T
   __shared__ float sg[C];
   __shared__ float sgs[2 * C];
 
   const int nvb = DV / BV;
-  const int vb = blockIdx.x % nvb, bh = blockIdx.x / nvb;
+  const int wg = xcd_group(blockIdx.x, gridDim.x);  // the d_v blocks of one (b, h) share an L2
+  const int vb = wg % nvb, bh = wg / nvb;
   const int b = bh / H, h = bh % H, v0 = vb * BV;
   const int w = wave_id(), l = lane_id();
 
   f32x4 hacc[HPW];
 #pragma unroll
   for (int s = 0; s < HPW; ++s) {
-    const int tt = w + kWaves * s;
+    const int tt = w + NW * s;
     hacc[s] = zero4();
     if (tt < NH && dht != nullptr) {
       const int td = tt / NTV, tv = tt % NTV;
@@ -163,8 +194,8 @@ __global__ __launch_bounds__(kThreads) void k_dstate(const E* __restrict__ q, co
     }
   }
 
-  Tile<E, C, DK> tQ, tK, tW;
-  Tile<E, C, BV> tO;
+  Tile<E, C, DK, NT> tQ, tK, tW;
+  Tile<E, C, BV, NT> tO;
   f32x4 rU[UPW];
   float rg = 0.f;
 #define LRT_DSTATE_FETCH(n_)                                                                        \
@@ -177,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void k_dstate(const E* __restrict__ q, co
     tW.load_block(wW + ft * C * DK);                                                                \
     tO.load_rows(d_o + (ftok * H + h) * DV + v0, (size_t)H * DV, fnv);                              \
     _Pragma("unroll") for (int s = 0; s < UPW; ++s) {                                               \
-      const int tt = w + kWaves * s;                                                                \
+      const int tt = w + NW * s;                                                                    \
       if (tt < NU)                                                                                  \
         rU[s] = load4<E>(wdUl + ft * DV * C + (size_t)(v0 + (tt % NTV) * 16 + (l & 15)) * C +      \
                          (tt / NTV) * 16 + (l >> 4) * 4);                                           \
@@ -188,71 +219,71 @@ __global__ __launch_bounds__(kThreads) void k_dstate(const E* __restrict__ q, co
   LRT_DSTATE_FETCH(N - 1)
   for (int n = N - 1; n >= 0; --n) {
     const size_t tile = (size_t)bh * N + n;
-    if (threadIdx.x < C) sg[threadIdx.x] = rg;
-    // dH' (gradient of this chunk's end state) -> LDS and workspace, as [v][d]
+    // gates: g, e^(g_C - g_t), gamma_t (wave 0 holds g of this chunk, one token per lane)
+    if (threadIdx.x < 64) {
+      const float gC = __shfl(rg, C - 1, 64);
+      if (threadIdx.x < C) {
+        sg[threadIdx.x] = rg;
+        sgs[threadIdx.x] = __expf(gC - rg);
+        sgs[C + threadIdx.x] = __expf(rg);
+      }
+    }
+    // dH' (gradient of this chunk's end state) -> LDS as [v][d]
 #pragma unroll
     for (int s = 0; s < HPW; ++s) {
-      const int tt = w + kWaves * s;
+      const int tt = w + NW * s;
       if (tt < NH) {
         const int td = tt / NTV, tv = tt % NTV;
-        const int vv = tv * 16 + (l & 15), d = td * 16 + (l >> 4) * 4;
-        store4<E>(sdS + vv * LK + d, hacc[s]);
-        store4<E>(wdS + tile * DV * DK + (size_t)(v0 + vv) * DK + d, hacc[s]);
+        store4<E>(sdS + (tv * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, hacc[s]);
       }
     }
-    __syncthreads();
-    const float gC = sg[C - 1];
-    tQ.store_T(sA2, L2);
-    tW.store_T(sA2 + C, L2);
-    {
-      float* sc = sgs;  // e^(g_C - g_t) and gamma_t, per token
-      if (threadIdx.x < C) {
-        sc[threadIdx.x] = __expf(gC - sg[threadIdx.x]);
-        sc[C + threadIdx.x] = __expf(sg[threadIdx.x]);
-      }
-    }
+    tQ.store(sQ, LK);
+    tW.store(sW, LK);
     f32x4 du[UPW];
 #pragma unroll
     for (int s = 0; s < UPW; ++s) du[s] = rU[s];
-    __syncthreads();
+    lds_barrier();
+    lds_to_block<E, BV, DK, NT>(wdS + (tile * DV + v0) * DK, sdS, LK);
     tK.scale_rows(sgs);
     tK.store(sKt, LK);
     tO.scale_rows(sgs + C);
-    tO.store_T(sB2, L2);
+    tO.store(sOg, LB);
     if (n > 0) LRT_DSTATE_FETCH(n - 1)
-    __syncthreads();
-    // dU = dU_local + Ktil dH'  (rows t, cols v)
+    const float dec = __expf(sg[C - 1]);
+    lds_barrier();
+    // dU = dU_local + Ktil dH'  (rows t, cols v) -> dU^T
 #pragma unroll
     for (int s = 0; s < UPW; ++s) {
-      const int tt = w + kWaves * s;
+      const int tt = w + NW * s;
       if (tt < NU) {
         const int ti = tt / NTV, tv = tt % NTV;
-        const int vv = tv * 16 + (l & 15), t = ti * 16 + (l >> 4) * 4;
         f32x4 acc = du[s];
         mma<DK>(acc, sKt + ti * 16 * LK, LK, sdS + tv * 16 * LK, LK);
-        store4<E>(wdU + tile * DV * C + (size_t)(v0 + vv) * C + t, acc);
-        store4<E>(sB2 + vv * L2 + C + t, -acc);
+        store4<E>(sdU + (tv * 16 + (l & 15)) * LC + ti * 16 + (l >> 4) * 4, acc);
       }
     }
-    __syncthreads();
+    lds_barrier();
+    lds_to_block<E, BV, C, NT>(wdU + (tile * DV + v0) * C, sdU, LC);
     // dH <- gamma_C dH' + Q^T diag(gamma) dO - W^T dU
-    const float dec = __expf(gC);
 #pragma unroll
     for (int s = 0; s < HPW; ++s) {
-      const int tt = w + kWaves * s;
+      const int tt = w + NW * s;
       if (tt < NH) {
         const int td = tt / NTV, tv = tt % NTV;
+        f32x4 wdu = zero4();
         hacc[s] *= dec;
-        mma<2 * C>(hacc[s], sA2 + td * 16 * L2, L2, sB2 + tv * 16 * L2, L2);
+        mma<C, true, true>(hacc[s], sQ + td * 16, LK, sOg + tv * 16, LB);
+        mma<C, true, false>(wdu, sW + td * 16, LK, sdU + tv * 16 * LC, LC);
+        hacc[s] -= wdu;
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 #undef LRT_DSTATE_FETCH
   if (dh0 != nullptr) {
 #pragma unroll
     for (int s = 0; s < HPW; ++s) {
-      const int tt = w + kWaves * s;
+      const int tt = w + NW * s;
       if (tt < NH) {
         const int td = tt / NTV, tv = tt % NTV;
 #pragma unroll
@@ -264,26 +295,26 @@ __global__ __launch_bounds__(kThreads) void k_dstate(const E* __restrict__ q, co
 }
 
 // ----------------------------------------------------------------- k_grad1
-// Per chunk: dS, dQ (final), dW, the dS^T Q + Ktil-path part of dK (fp32),
-// and the Gamma / output / Ktil / gamma_C parts of dg.
+// Per chunk: dS, dQ (final), dW and the dS^T Q + Ktil-path part of dK (both
+// in accumulator-tile order), and the Gamma / output / Ktil / gamma_C parts
+// of dg.  Operands stay in their natural layouts; products contracting over
+// their rows use the LDS transpose read.
 template <typename E, int C, int DK, int DV>
 struct Grad1Lds {
   static constexpr int P = lds_pad<E>();
   static constexpr int LK = DK + P, LV = DV + P, LC = C + P;
-  static constexpr size_t sTK = (size_t)C * LK * sizeof(E), sTV = (size_t)C * LV * sizeof(E);
-  static constexpr size_t sDC = (size_t)DK * LC * sizeof(E), sCC = (size_t)C * LC * sizeof(E);
-  static constexpr size_t sDV = (size_t)DK * LV * sizeof(E);
-  static constexpr size_t R1 = 0;                                    // Q, later dU (rows t)
-  static constexpr size_t R23 = R1 + (sTK > sTV ? sTK : sTV);        // K, later Hn / dH' [d][v]
-  static constexpr size_t DO = R23 + (sTK > sDV ? sTK : sDV);
-  static constexpr size_t U = DO + sTV;
-  static constexpr size_t QT = U + sTV;
-  static constexpr size_t KT = QT + sDC;
-  static constexpr size_t DSIJ = KT + sDC;
-  static constexpr size_t DSJI = DSIJ + sCC;
-  static constexpr size_t G = DSJI + sCC;
-  static constexpr size_t DG = G + C * sizeof(float);
-  static constexpr size_t DOT = DG + C * sizeof(float);
+  static constexpr size_t es = sizeof(E);
+  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+  static constexpr size_t Q = 0;                                  // q rows [t][d]
+  static constexpr size_t K = Q + (size_t)C * LK * es;            // k rows [t][d]
+  static constexpr size_t DO = K + (size_t)C * LK * es;           // do rows [t][v]; later dq rows
+  static constexpr size_t UT = DO + mx((size_t)C * LV, (size_t)C * LK) * es;  // U^T [v][t]
+  static constexpr size_t ST = UT + (size_t)DV * LC * es;         // S_n = Hn^T [v][d]; later dH'^T
+  static constexpr size_t DUT = ST + (size_t)DV * LK * es;        // dU^T [v][t]
+  static constexpr size_t DSJ = DUT + (size_t)DV * LC * es;       // dS^T [j][i]
+  static constexpr size_t G = DSJ + (size_t)C * LC * es;
+  static constexpr size_t DG = G + C * 4;
+  static constexpr size_t DOT = DG + C * 4;
   static constexpr size_t TOTAL = DOT + 16;
 };
 
@@ -292,159 +323,184 @@ __global__ __launch_bounds__(kThreads) void k_grad1(const E* __restrict__ q, con
                                                     const E* __restrict__ d_o, const float* __restrict__ wG,
                                                     const E* __restrict__ wS, const E* __restrict__ wdS,
                                                     const E* __restrict__ wU, const E* __restrict__ wdU,
-                                                    E* __restrict__ dq, E* __restrict__ wdW,
-                                                    float* __restrict__ wdK1, float* __restrict__ wdg1, int T,
-                                                    int H, int N) {
+                                                    E* __restrict__ dq, E* __restrict__ wdW, E* __restrict__ wdK1,
+                                                    float* __restrict__ wdg1, int T, int H, int N, int ntiles) {
   typedef Grad1Lds<E, C, DK, DV> Lay;
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, NB = C / 16;
   constexpr int V = 16 / (int)sizeof(E);
+  constexpr int NKT = (DK / 16) * NB, KPW = (NKT + kWaves - 1) / kWaves;
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
-  E* sQ = (E*)(smem + Lay::R1);
-  E* sK = (E*)(smem + Lay::R23);
+  E* sQ = (E*)(smem + Lay::Q);
+  E* sK = (E*)(smem + Lay::K);
   E* sdO = (E*)(smem + Lay::DO);
-  E* sU = (E*)(smem + Lay::U);
-  E* sQt = (E*)(smem + Lay::QT);
-  E* sKt = (E*)(smem + Lay::KT);
-  E* sdSij = (E*)(smem + Lay::DSIJ);
-  E* sdSji = (E*)(smem + Lay::DSJI);
+  E* sdQ = (E*)(smem + Lay::DO);
+  E* sUt = (E*)(smem + Lay::UT);
+  E* sS = (E*)(smem + Lay::ST);
+  E* sdUt = (E*)(smem + Lay::DUT);
+  E* sdSj = (E*)(smem + Lay::DSJ);
   float* sg = (float*)(smem + Lay::G);
   float* sdg = (float*)(smem + Lay::DG);
   float* sdot = (float*)(smem + Lay::DOT);
-
-  const int tile = blockIdx.x;
-  const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
-  const int t0 = n * C, nv = min(C, T - t0);
-  const size_t tok0 = (size_t)b * T + t0;
   const int w = wave_id(), l = lane_id();
 
   Tile<E, C, DK> tq, tk;
-  {
-    Tile<E, C, DV> to;
-    Tile<E, DV, C> tu;
-    tq.load_rows(q + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-    tk.load_rows(k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-    to.load_rows(d_o + (tok0 * H + h) * DV, (size_t)H * DV, nv);
-    tu.load_block(wU + (size_t)tile * DV * C);
-    if (threadIdx.x < C) {
-      sg[threadIdx.x] = wG[(size_t)tile * C + threadIdx.x];
-      sdg[threadIdx.x] = 0.f;
-    }
-    if (threadIdx.x == 0) sdot[0] = 0.f;
+  Tile<E, C, DV> to;
+  Tile<E, DV, C> tu, tdu;
+  Tile<E, DV, DK> tS, tdS;
+  float rg = 0.f;
+#define LRT_G1_LOAD(tile_)                                                                \
+  {                                                                                       \
+    const int ln = (tile_) % N, lbh = (tile_) / N;                                        \
+    const int lnv = min(C, T - ln * C);                                                   \
+    const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                           \
+    const int lh = lbh % H;                                                               \
+    tq.load_rows(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
+    tk.load_rows(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
+    to.load_rows(d_o + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                        \
+    tu.load_block(wU + (size_t)(tile_) * DV * C);                                         \
+    tdu.load_block(wdU + (size_t)(tile_) * DV * C);                                       \
+    if (threadIdx.x < C) rg = wG[(size_t)(tile_) * C + threadIdx.x];                      \
+  }
+
+  int tile = blockIdx.x;
+  if (tile < ntiles) {
+    LRT_G1_LOAD(tile)
+    tS.load_block(wS + (size_t)tile * DV * DK);
+  }
+  for (; tile < ntiles; tile += gridDim.x) {
+    const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
+    const int t0 = n * C, nv = min(C, T - t0);
+    const size_t tok0 = (size_t)b * T + t0;
     tq.store(sQ, LK);
     tk.store(sK, LK);
     to.store(sdO, LV);
-    tu.store_T(sU, LV);
-  }
-  __syncthreads();
-  // states, state gradients and dU of this chunk: in flight during dS
-  Tile<E, DV, DK> tS, tdS;
-  Tile<E, DV, C> tdU;
-  tS.load_block(wS + (size_t)tile * DV * DK);
-  tdS.load_block(wdS + (size_t)tile * DV * DK);
-  tdU.load_block(wdU + (size_t)tile * DV * C);
+    tu.store(sUt, LC);
+    tdu.store(sdUt, LC);
+    tS.store(sS, LK);
+    if (threadIdx.x < C) {
+      sg[threadIdx.x] = rg;
+      sdg[threadIdx.x] = 0.f;
+    }
+    if (threadIdx.x == 0) sdot[0] = 0.f;
+    tdS.load_block(wdS + (size_t)tile * DV * DK);  // dH' of this chunk, needed after dQ
+    lds_barrier();
+    if (tile + (int)gridDim.x < ntiles) LRT_G1_LOAD(tile + (int)gridDim.x)
 
-  // dS = (dO U^T) o Gamma (inclusive); E = dS o (Q K^T) -> dg rows +, cols -
-  for (int tt = w; tt < NB * NB; tt += kWaves) {
-    const int ti = tt / NB, tj = tt % NB;
-    const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
-    f32x4 ds = zero4();
-    if (tj <= ti) {
-      f32x4 qk = zero4(), dp = zero4();
-      mma<DK>(qk, sQ + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
-      mma<DV>(dp, sdO + ti * 16 * LV, LV, sU + tj * 16 * LV, LV);
-      float ecol = 0.f;
+    // dS = (dO U^T) o Gamma (inclusive); E = dS o (Q K^T) -> dg rows +, cols -
+    for (int tt = w; tt < NB * NB; tt += kWaves) {
+      const int ti = tt / NB, tj = tt % NB;
+      const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
+      f32x4 ds = zero4();
+      if (tj <= ti) {
+        f32x4 qk = zero4(), dp = zero4();
+        mma<DK>(qk, sQ + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
+        mma<DV, false, true>(dp, sdO + ti * 16 * LV, LV, sUt + tj * 16, LC);
+        float ecol = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + r;
-        ds[r] = (j <= i) ? dp[r] * __expf(sg[i] - sg[j]) : 0.f;
-        const float e = ds[r] * qk[r];
-        ecol += e;
-        const float er = sum16(e);
-        if ((l & 15) == 0) atomicAdd(&sdg[i], er);
+        for (int r = 0; r < 4; ++r) {
+          const int i = i0 + r;
+          ds[r] = (j <= i) ? dp[r] * __expf(sg[i] - sg[j]) : 0.f;
+          const float e = ds[r] * qk[r];
+          ecol += e;
+          const float er = sum16(e);
+          if ((l & 15) == 0) atomicAdd(&sdg[i], er);
+        }
+        ecol = sum4(ecol);
+        if (l < 16) atomicAdd(&sdg[j], -ecol);
       }
-      ecol = sum4(ecol);
-      if (l < 16) atomicAdd(&sdg[j], -ecol);
+      store4<E>(sdSj + j * LC + i0, ds);
     }
-    store4<E>(sdSji + j * LC + i0, ds);
+    lds_barrier();
+    // dQ^T = gamma (Hn dO^T) + K^T dS^T (rows d, cols i), kept in registers;
+    // dW^T = -Hn dU^T -> workspace in accumulator-tile order
+    f32x4 dqa[KPW];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sdSij[(i0 + r) * LC + j] = from_f<E>(ds[r]);
-  }
-  // Q^T, K^T from the registers still holding q and k
-  tq.store_T(sQt, LC);
-  tk.store_T(sKt, LC);
-  __syncthreads();
-  // Hn [d][v] into R23, dU [t][v] into R1; <dH', Hn> from the same registers
-  E* sH = (E*)(smem + Lay::R23);
-  E* sdU = (E*)(smem + Lay::R1);
-  tS.store_T(sH, LV);
-  tdU.store_T(sdU, LV);
-  {
-    float part = 0.f;
+    for (int s = 0; s < KPW; ++s) {
+      const int tt = w + kWaves * s;
+      dqa[s] = zero4();
+      if (tt < NKT) {
+        const int td = tt / NB, ti = tt % NB;
+        const int i = ti * 16 + (l & 15), d0 = td * 16 + (l >> 4) * 4;
+        f32x4 acc = zero4();
+        mma<DV, true, false>(acc, sS + td * 16, LK, sdO + ti * 16 * LV, LV);
+        const float gam = __expf(sg[i]);
+        float e = 0.f;
 #pragma unroll
-    for (int s2 = 0; s2 < tS.PT; ++s2) {
-      if (threadIdx.x + kThreads * s2 < tS.NP) {
-        E a[V], d[V];
-        __builtin_memcpy(a, &tS.x[s2], 16);
-        __builtin_memcpy(d, &tdS.x[s2], 16);
-#pragma unroll
-        for (int e = 0; e < V; ++e) part += to_f(a[e]) * to_f(d[e]);
+        for (int r = 0; r < 4; ++r) e += to_f(sQ[i * LK + d0 + r]) * acc[r];
+        e = sum4(e * gam);
+        if (l < 16) atomicAdd(&sdg[i], e);
+        acc *= gam;
+        mma<C, true, true>(acc, sK + td * 16, LK, sdSj + ti * 16, LC);
+        dqa[s] = acc;
+        f32x4 dw = zero4();
+        mma<DV, true, true>(dw, sS + td * 16, LK, sdUt + ti * 16, LC);
+        acc_tile_store<E>(wdW + (size_t)tile * C * DK, tt, -dw);
       }
     }
-    part = sum16(part);
-    part = sum4(part);
-    if (l == 0) atomicAdd(sdot, part);
-  }
-  __syncthreads();
-  // dQ^T = gamma (Hn dO^T) + K^T dS^T  (rows d, cols i);  dW^T = -Hn dU^T
-  for (int tt = w; tt < (DK / 16) * NB; tt += kWaves) {
-    const int td = tt / NB, ti = tt % NB;
-    const int i = ti * 16 + (l & 15), d0 = td * 16 + (l >> 4) * 4;
-    f32x4 acc = zero4();
-    mma<DV>(acc, sH + td * 16 * LV, LV, sdO + ti * 16 * LV, LV);
-    const float gam = __expf(sg[i]);
-    float e = 0.f;
+    // <dH', Hn> from the registers of this chunk's S and dH'; then the next S
+    {
+      float part = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) e += to_f(sQt[(d0 + r) * LC + i]) * acc[r];
-    e = sum4(e * gam);
-    if (l < 16) atomicAdd(&sdg[i], e);
-    acc *= gam;
-    mma<C>(acc, sKt + td * 16 * LC, LC, sdSij + ti * 16 * LC, LC);
-    if (i < nv) store4<E>(dq + ((tok0 + i) * H + h) * DK + d0, acc);
-    f32x4 dw = zero4();
-    mma<DV>(dw, sH + td * 16 * LV, LV, sdU + ti * 16 * LV, LV);
-    store4<E>(wdW + (size_t)tile * C * DK + (size_t)i * DK + d0, -dw);
-  }
-  __syncthreads();
-  // dH' [d][v] into R23
-  E* sdH = (E*)(smem + Lay::R23);
-  tdS.store_T(sdH, LV);
-  __syncthreads();
-  // dK1^T = e^(g_C - g_j) (dH' U^T) + Q^T dS   (rows d, cols j)
-  const float gC = sg[C - 1];
-  for (int tt = w; tt < (DK / 16) * NB; tt += kWaves) {
-    const int td = tt / NB, tj = tt % NB;
-    const int j = tj * 16 + (l & 15), d0 = td * 16 + (l >> 4) * 4;
-    f32x4 acc = zero4();
-    mma<DV>(acc, sdH + td * 16 * LV, LV, sU + tj * 16 * LV, LV);
-    const float kt = __expf(gC - sg[j]);
-    float s = 0.f;
+      for (int s2 = 0; s2 < tS.PT; ++s2) {
+        if (threadIdx.x + kThreads * s2 < tS.NP) {
+          E a[V], d[V];
+          __builtin_memcpy(a, &tS.x[s2], 16);
+          __builtin_memcpy(d, &tdS.x[s2], 16);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s += acc[r] * to_f(sKt[(d0 + r) * LC + j]);
-    s = sum4(s * kt);
-    if (l < 16) {
-      atomicAdd(&sdg[j], -s);
-      atomicAdd(&sdg[C - 1], s);
+          for (int e = 0; e < V; ++e) part += to_f(a[e]) * to_f(d[e]);
+        }
+      }
+      part = sum16(part);
+      part = sum4(part);
+      if (l == 0) atomicAdd(sdot, part);
     }
-    acc *= kt;
-    mma<C>(acc, sQt + td * 16 * LC, LC, sdSji + tj * 16 * LC, LC);
-    *(float4*)(wdK1 + (size_t)tile * C * DK + (size_t)j * DK + d0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    if (tile + (int)gridDim.x < ntiles) tS.load_block(wS + (size_t)(tile + (int)gridDim.x) * DV * DK);
+    lds_barrier();
+    // dq rows over the dead dO; dH'^T over the dead S
+#pragma unroll
+    for (int s = 0; s < KPW; ++s) {
+      const int tt = w + kWaves * s;
+      if (tt < NKT) {
+        const int td = tt / NB, ti = tt % NB;
+        store4<E>(sdQ + (ti * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, dqa[s]);
+      }
+    }
+    tdS.store(sS, LK);
+    lds_barrier();
+    lds_to_rows<E, C, DK>(dq + (tok0 * H + h) * DK, (size_t)H * DK, sdQ, LK, nv);
+    // dK1^T = e^(g_C - g_j) (dH' U^T) + Q^T dS   (rows d, cols j)
+    const float gC = sg[C - 1];
+#pragma unroll
+    for (int s = 0; s < KPW; ++s) {
+      const int tt = w + kWaves * s;
+      if (tt < NKT) {
+        const int td = tt / NB, tj = tt % NB;
+        const int j = tj * 16 + (l & 15), d0 = td * 16 + (l >> 4) * 4;
+        f32x4 acc = zero4();
+        mma<DV, true, true>(acc, sS + td * 16, LK, sUt + tj * 16, LC);
+        const float kt = __expf(gC - sg[j]);
+        float sj = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sj += acc[r] * to_f(sK[j * LK + d0 + r]);
+        sj = sum4(sj * kt);
+        if (l < 16) {
+          atomicAdd(&sdg[j], -sj);
+          atomicAdd(&sdg[C - 1], sj);
+        }
+        acc *= kt;
+        mma<C, true, false>(acc, sQ + td * 16, LK, sdSj + tj * 16 * LC, LC);
+        acc_tile_store<E>(wdK1 + (size_t)tile * C * DK, tt, acc);
+      }
+    }
+    lds_barrier();
+    if (threadIdx.x < C) {
+      float x = sdg[threadIdx.x];
+      if (threadIdx.x == C - 1) x += __expf(gC) * sdot[0];
+      wdg1[(size_t)tile * C + threadIdx.x] = x;
+    }
+    lds_barrier();
   }
-  __syncthreads();
-  if (threadIdx.x < C) {
-    float x = sdg[threadIdx.x];
-    if (threadIdx.x == C - 1) x += __expf(gC) * sdot[0];
-    wdg1[(size_t)tile * C + threadIdx.x] = x;
-  }
+#undef LRT_G1_LOAD
 }
 
 // ----------------------------------------------------------------- k_grad2
@@ -454,13 +510,15 @@ template <typename E, int C, int DK, int DV>
 struct Grad2Lds {
   static constexpr int P = lds_pad<E>();
   static constexpr int LK = DK + P, LV = DV + P, LC = C + P;
-  static constexpr size_t sTK = (size_t)C * LK * sizeof(E), sTV = (size_t)C * LV * sizeof(E);
-  static constexpr size_t sDC = (size_t)DK * LC * sizeof(E), sVC = (size_t)DV * LC * sizeof(E);
-  static constexpr size_t sCC = (size_t)C * LC * sizeof(E);
-  static constexpr size_t K = 0, KT = K + sTK, VV = KT + sDC, TT = VV + sTV, TTT = TT + sCC, DW = TTT + sCC;
-  static constexpr size_t DU = DW + sTK;
-  static constexpr size_t F = DU + sTV;  // dW^T, dU^T; later dT, R^T, M, M^T
-  static constexpr size_t FS = (sDC + sVC) > 4 * sCC ? (sDC + sVC) : 4 * sCC;
+  static constexpr size_t es = sizeof(E);
+  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+  static constexpr size_t K = 0;                                   // k rows [t][d]
+  static constexpr size_t VV = K + (size_t)C * LK * es;            // v rows [t][v]
+  static constexpr size_t TT = VV + (size_t)C * LV * es;           // Tinv [i][j]
+  static constexpr size_t DW = TT + (size_t)C * LC * es;           // dW [i][d]; later dk rows
+  static constexpr size_t DUT = DW + (size_t)C * LK * es;          // dU^T [v][t]
+  static constexpr size_t F = DUT + (size_t)DV * LC * es;          // dv rows; later dT^T, R^T, M^T
+  static constexpr size_t FS = mx((size_t)C * LV * es, 3 * (size_t)C * LC * es);
   static constexpr size_t G = F + FS;
   static constexpr size_t BB = G + C * 4, DG = BB + C * 4, DB = DG + C * 4, CX = DB + C * 4;
   static constexpr size_t TOTAL = CX + C * 4;
@@ -470,195 +528,197 @@ template <typename E, int C, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void k_grad2(const E* __restrict__ k, const E* __restrict__ v,
                                                     const float* __restrict__ beta, const float* __restrict__ wG,
                                                     const E* __restrict__ wT, const E* __restrict__ wdW,
-                                                    const E* __restrict__ wdU, const float* __restrict__ wdK1,
+                                                    const E* __restrict__ wdU, const E* __restrict__ wdK1,
                                                     const float* __restrict__ wdg1, E* __restrict__ dk,
                                                     E* __restrict__ dv, float* __restrict__ dlog_a,
-                                                    float* __restrict__ dbeta, int T, int H, int N) {
+                                                    float* __restrict__ dbeta, int T, int H, int N, int ntiles) {
   typedef Grad2Lds<E, C, DK, DV> Lay;
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, NB = C / 16;
-  constexpr int V = 16 / (int)sizeof(E);
   constexpr int NKT = (DK / 16) * NB, KPW = (NKT + kWaves - 1) / kWaves;
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
   E* sK = (E*)(smem + Lay::K);
-  E* sKt = (E*)(smem + Lay::KT);
   E* sV = (E*)(smem + Lay::VV);
   E* sT = (E*)(smem + Lay::TT);
-  E* sTt = (E*)(smem + Lay::TTT);
   E* sdW = (E*)(smem + Lay::DW);
-  E* sdU = (E*)(smem + Lay::DU);
-  E* sdWt = (E*)(smem + Lay::F);
-  E* sdUt = (E*)(smem + Lay::F + Lay::sDC);
+  E* sdK = (E*)(smem + Lay::DW);
+  E* sdUt = (E*)(smem + Lay::DUT);
+  E* sdV = (E*)(smem + Lay::F);
+  E* sdTt = (E*)(smem + Lay::F);
+  E* sRt = sdTt + C * LC;
+  E* sMt = sRt + C * LC;
   float* sg = (float*)(smem + Lay::G);
   float* sb = (float*)(smem + Lay::BB);
   float* sdg = (float*)(smem + Lay::DG);
   float* sdb = (float*)(smem + Lay::DB);
   float* scx = (float*)(smem + Lay::CX);
-
-  const int tile = blockIdx.x;
-  const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
-  const int t0 = n * C, nv = min(C, T - t0);
-  const size_t tok0 = (size_t)b * T + t0;
   const int w = wave_id(), l = lane_id();
 
-  {
-    Tile<E, C, DK> tk, tdw;
-    Tile<E, C, DV> tv;
-    Tile<E, C, C> tt;
-    Tile<E, DV, C> tdu;
-    tk.load_rows(k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-    tdw.load_block(wdW + (size_t)tile * C * DK);
-    tv.load_rows(v + (tok0 * H + h) * DV, (size_t)H * DV, nv);
-    tt.load_block(wT + (size_t)tile * C * C);
-    tdu.load_block(wdU + (size_t)tile * DV * C);
+  Tile<E, C, DK> tk;
+  Tile<E, C, DV> tv;
+  Tile<E, C, C> tt;
+  Tile<E, DV, C> tdu;
+  f32x4 rk1[KPW];  // the first part of dK, accumulator layout (rows d, cols j)
+  float rg = 0.f, rb = 0.f, rd = 0.f;
+#define LRT_G2_LOAD(tile_)                                                                        \
+  {                                                                                               \
+    const int ln = (tile_) % N, lbh = (tile_) / N;                                                \
+    const int lnv = min(C, T - ln * C);                                                           \
+    const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                                   \
+    const int lh = lbh % H;                                                                       \
+    tk.load_rows(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                                  \
+    tv.load_rows(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                                  \
+    tt.load_block(wT + (size_t)(tile_) * C * C);                                                  \
+    tdu.load_block(wdU + (size_t)(tile_) * DV * C);                                               \
+    _Pragma("unroll") for (int s = 0; s < KPW; ++s) {                                             \
+      const int kt_ = w + kWaves * s;                                                             \
+      if (kt_ < NKT) rk1[s] = load4<E>(wdK1 + (size_t)(tile_) * C * DK + ((size_t)kt_ * 64 + l) * 4); \
+    }                                                                                             \
+    if (threadIdx.x < C) {                                                                        \
+      rg = wG[(size_t)(tile_) * C + threadIdx.x];                                                 \
+      rb = (int)threadIdx.x < lnv ? beta[(ltok + threadIdx.x) * H + lh] : 0.f;                    \
+      rd = wdg1[(size_t)(tile_) * C + threadIdx.x];                                               \
+    }                                                                                             \
+  }
+
+  int tile = blockIdx.x;
+  if (tile < ntiles) LRT_G2_LOAD(tile)
+  for (; tile < ntiles; tile += gridDim.x) {
+    const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
+    const int t0 = n * C, nv = min(C, T - t0);
+    const size_t tok0 = (size_t)b * T + t0;
     tk.store(sK, LK);
-    tk.store_T(sKt, LC);
-    tdw.store(sdW, LK);
-    tdw.store_T(sdWt, LC);
     tv.store(sV, LV);
     tt.store(sT, LC);
-    tt.store_T(sTt, LC);
     tdu.store(sdUt, LC);
-    tdu.store_T(sdU, LV);
-  }
-  if (threadIdx.x < C) {
-    const int t = threadIdx.x;
-    sg[t] = wG[(size_t)tile * C + t];
-    sb[t] = t < nv ? beta[(tok0 + t) * H + h] : 0.f;
-    sdg[t] = wdg1[(size_t)tile * C + t];
-    sdb[t] = 0.f;
-    scx[t] = 0.f;
-  }
-  // dK^T accumulators (rows d, cols j), seeded with the first part of dK
-  f32x4 dka[KPW];
-#pragma unroll
-  for (int s = 0; s < KPW; ++s) {
-    const int tt = w + kWaves * s;
-    dka[s] = zero4();
-    if (tt < NKT) {
-      const int td = tt / NB, tj = tt % NB;
-      const float4 x = *(const float4*)(wdK1 + (size_t)tile * C * DK + (size_t)(tj * 16 + (l & 15)) * DK +
-                                        td * 16 + (l >> 4) * 4);
-      dka[s] = f32x4{x.x, x.y, x.z, x.w};
+    acc_tiles_to_lds<E, DK / 16, NB>(sdW, LK, wdW + (size_t)tile * C * DK);
+    if (threadIdx.x < C) {
+      const int t = threadIdx.x;
+      sg[t] = rg;
+      sb[t] = rb;
+      sdg[t] = rd;
+      sdb[t] = 0.f;
+      scx[t] = 0.f;
     }
-  }
-  __syncthreads();
-  // dX^T = dW^T Tinv (rows d, cols j): dK += b gamma dX, cx_j = dX_j . k_j
+    f32x4 dka[KPW];
 #pragma unroll
-  for (int s = 0; s < KPW; ++s) {
-    const int tt = w + kWaves * s;
-    if (tt < NKT) {
-      const int td = tt / NB, tj = tt % NB;
-      const int j = tj * 16 + (l & 15), d0 = td * 16 + (l >> 4) * 4;
+    for (int s = 0; s < KPW; ++s) dka[s] = rk1[s];
+    lds_barrier();
+    if (tile + (int)gridDim.x < ntiles) LRT_G2_LOAD(tile + (int)gridDim.x)
+    // dX^T = dW^T Tinv (rows d, cols j): dK += b gamma dX, cx_j = dX_j . k_j
+#pragma unroll
+    for (int s = 0; s < KPW; ++s) {
+      const int kt = w + kWaves * s;
+      if (kt < NKT) {
+        const int td = kt / NB, tj = kt % NB;
+        const int j = tj * 16 + (l & 15), d0 = td * 16 + (l >> 4) * 4;
+        f32x4 acc = zero4();
+        mma<C, true, true>(acc, sdW + td * 16, LK, sT + tj * 16, LC);
+        dka[s] += (sb[j] * __expf(sg[j])) * acc;
+        float e = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sK[j * LK + d0 + r]);
+        e = sum4(e);
+        if (l < 16) atomicAdd(&scx[j], e);
+      }
+    }
+    // dY^T = dU^T Tinv (rows v, cols j): dV = b dY (rows staged), dbeta += dY_j . v_j
+    for (int tt2 = w; tt2 < (DV / 16) * NB; tt2 += kWaves) {
+      const int tvv = tt2 / NB, tj = tt2 % NB;
+      const int j = tj * 16 + (l & 15), v0 = tvv * 16 + (l >> 4) * 4;
       f32x4 acc = zero4();
-      mma<C>(acc, sdWt + td * 16 * LC, LC, sTt + tj * 16 * LC, LC);
-      dka[s] += (sb[j] * __expf(sg[j])) * acc;
+      mma<C, false, true>(acc, sdUt + tvv * 16 * LC, LC, sT + tj * 16, LC);
+      store4<E>(sdV + j * LV + v0, sb[j] * acc);
       float e = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sK[j * LK + d0 + r]);
+      for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sV[j * LV + v0 + r]);
       e = sum4(e);
-      if (l < 16) atomicAdd(&scx[j], e);
+      if (l < 16) atomicAdd(&sdb[j], e);
     }
-  }
-  // dY^T = dU^T Tinv (rows v, cols j): dV = b dY, dbeta += dY_j . v_j
-  for (int tt = w; tt < (DV / 16) * NB; tt += kWaves) {
-    const int tv = tt / NB, tj = tt % NB;
-    const int j = tj * 16 + (l & 15), v0 = tv * 16 + (l >> 4) * 4;
-    f32x4 acc = zero4();
-    mma<C>(acc, sdUt + tv * 16 * LC, LC, sTt + tj * 16 * LC, LC);
-    if (j < nv) store4<E>(dv + ((tok0 + j) * H + h) * DV + v0, sb[j] * acc);
-    float e = 0.f;
+    lds_barrier();
+    lds_to_rows<E, C, DV>(dv + (tok0 * H + h) * DV, (size_t)H * DV, sdV, LV, nv);
+    lds_barrier();
+    // dT = (dW K^T) diag(b gamma) + (dU V^T) diag(b)   (rows i, cols j) -> dT^T [j][i]
+    for (int t2 = w; t2 < NB * NB; t2 += kWaves) {
+      const int ti = t2 / NB, tj = t2 % NB;
+      const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
+      f32x4 z1 = zero4(), z2 = zero4();
+      mma<DK>(z1, sdW + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
+      mma<DV, true, false>(z2, sdUt + ti * 16, LC, sV + tj * 16 * LV, LV);
+      store4<E>(sdTt + j * LC + i0, sb[j] * (__expf(sg[j]) * z1 + z2));
+    }
+    lds_barrier();
+    // R = dT Tinv^T (rows i, cols k) -> R^T [k][i]
+    for (int t2 = w; t2 < NB * NB; t2 += kWaves) {
+      const int ti = t2 / NB, tk2 = t2 % NB;
+      f32x4 acc = zero4();
+      mma<C, true, false>(acc, sdTt + ti * 16, LC, sT + tk2 * 16 * LC, LC);
+      store4<E>(sRt + (tk2 * 16 + (l & 15)) * LC + ti * 16 + (l >> 4) * 4, acc);
+    }
+    lds_barrier();
+    // dA = -strict_lower(Tinv^T R); with A = b_i (K K^T) o Gamma:
+    //   M = dA o b_i Gamma -> M^T [k][i], dbeta_i += sum_k dA o Gamma o KK^T, E = dA o A -> dg
+    for (int t2 = w; t2 < NB * NB; t2 += kWaves) {
+      const int ti = t2 / NB, tk2 = t2 % NB;
+      const int kk = tk2 * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
+      f32x4 m = zero4();
+      if (tk2 <= ti) {
+        f32x4 acc = zero4(), kkt = zero4();
+        mma<C, true, false>(acc, sT + ti * 16, LC, sRt + tk2 * 16 * LC, LC);
+        mma<DK>(kkt, sK + ti * 16 * LK, LK, sK + tk2 * 16 * LK, LK);
+        float ecol = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sV[j * LV + v0 + r]);
-    e = sum4(e);
-    if (l < 16) atomicAdd(&sdb[j], e);
-  }
-  __syncthreads();
-  E* sdT = (E*)(smem + Lay::F);
-  E* sRt = sdT + C * LC;
-  E* sM = sRt + C * LC;
-  E* sMt = sM + C * LC;
-  // dT = dW X^T + dU Y^T = (dW K^T) diag(b gamma) + (dU V^T) diag(b)   (rows i, cols j)
-  for (int tt = w; tt < NB * NB; tt += kWaves) {
-    const int ti = tt / NB, tj = tt % NB;
-    const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
-    f32x4 z1 = zero4(), z2 = zero4();
-    mma<DK>(z1, sdW + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
-    mma<DV>(z2, sdU + ti * 16 * LV, LV, sV + tj * 16 * LV, LV);
-    const f32x4 d = sb[j] * (__expf(sg[j]) * z1 + z2);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sdT[(i0 + r) * LC + j] = from_f<E>(d[r]);
-  }
-  __syncthreads();
-  // R = dT Tinv^T (rows i, cols k) -> R^T [k][i]
-  for (int tt = w; tt < NB * NB; tt += kWaves) {
-    const int ti = tt / NB, tk = tt % NB;
-    f32x4 acc = zero4();
-    mma<C>(acc, sdT + ti * 16 * LC, LC, sT + tk * 16 * LC, LC);
-    store4<E>(sRt + (tk * 16 + (l & 15)) * LC + ti * 16 + (l >> 4) * 4, acc);
-  }
-  __syncthreads();
-  // dA = -strict_lower(Tinv^T R); with A = b_i (K K^T) o Gamma:
-  //   M = dA o b_i Gamma, dbeta_i += sum_k dA o Gamma o KK^T, E = dA o A -> dg
-  for (int tt = w; tt < NB * NB; tt += kWaves) {
-    const int ti = tt / NB, tk = tt % NB;
-    const int kk = tk * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
-    f32x4 m = zero4();
-    if (tk <= ti) {
-      f32x4 acc = zero4(), kkt = zero4();
-      mma<C>(acc, sTt + ti * 16 * LC, LC, sRt + tk * 16 * LC, LC);
-      mma<DK>(kkt, sK + ti * 16 * LK, LK, sK + tk * 16 * LK, LK);
-      float ecol = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + r;
-        const float gam = (kk < i) ? __expf(sg[i] - sg[kk]) : 0.f;
-        const float da = -acc[r];
-        const float a = sb[i] * kkt[r] * gam;
-        m[r] = da * sb[i] * gam;
-        const float e = da * a;
-        ecol += e;
-        const float er = sum16(e);
-        const float br = sum16(da * gam * kkt[r]);
-        if ((l & 15) == 0) {
-          atomicAdd(&sdg[i], er);
-          atomicAdd(&sdb[i], br);
+        for (int r = 0; r < 4; ++r) {
+          const int i = i0 + r;
+          const float gam = (kk < i) ? __expf(sg[i] - sg[kk]) : 0.f;
+          const float da = -acc[r];
+          const float a = sb[i] * kkt[r] * gam;
+          m[r] = da * sb[i] * gam;
+          const float e = da * a;
+          ecol += e;
+          const float er = sum16(e);
+          const float br = sum16(da * gam * kkt[r]);
+          if ((l & 15) == 0) {
+            atomicAdd(&sdg[i], er);
+            atomicAdd(&sdb[i], br);
+          }
         }
+        ecol = sum4(ecol);
+        if (l < 16) atomicAdd(&sdg[kk], -ecol);
       }
-      ecol = sum4(ecol);
-      if (l < 16) atomicAdd(&sdg[kk], -ecol);
+      store4<E>(sMt + kk * LC + i0, m);
     }
-    store4<E>(sMt + kk * LC + i0, m);
+    lds_barrier();
+    // dK^T += K^T M (cols j: sum_i k_i M_ij) + K^T M^T (cols i: sum_j k_j M_ij)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sM[(i0 + r) * LC + kk] = from_f<E>(m[r]);
-  }
-  __syncthreads();
-  // dK^T += K^T M (cols j: sum_i k_i M_ij) + K^T M^T (cols i: sum_j k_j M_ij)
-#pragma unroll
-  for (int s = 0; s < KPW; ++s) {
-    const int tt = w + kWaves * s;
-    if (tt < NKT) {
-      const int td = tt / NB, tj = tt % NB;
-      const int j = tj * 16 + (l & 15), d0 = td * 16 + (l >> 4) * 4;
-      mma<C>(dka[s], sKt + td * 16 * LC, LC, sMt + tj * 16 * LC, LC);
-      mma<C>(dka[s], sKt + td * 16 * LC, LC, sM + tj * 16 * LC, LC);
-      if (j < nv) store4<E>(dk + ((tok0 + j) * H + h) * DK + d0, dka[s]);
+    for (int s = 0; s < KPW; ++s) {
+      const int kt = w + kWaves * s;
+      if (kt < NKT) {
+        const int td = kt / NB, tj = kt % NB;
+        mma<C, true, false>(dka[s], sK + td * 16, LK, sMt + tj * 16 * LC, LC);
+        mma<C, true, true>(dka[s], sK + td * 16, LK, sMt + tj * 16, LC);
+        store4<E>(sdK + (tj * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, dka[s]);
+      }
     }
-  }
-  // dg (+ the X = diag(b gamma) K term), reverse cumsum -> dlog_a; dbeta
-  if (threadIdx.x < 64) {
-    const int t = threadIdx.x;
-    float dg = 0.f, db = 0.f;
-    if (t < C) {
-      const float gam = __expf(sg[t]);
-      dg = sdg[t] + sb[t] * gam * scx[t];
-      db = sdb[t] + gam * scx[t];
+    // dg (+ the X = diag(b gamma) K term), reverse cumsum -> dlog_a; dbeta
+    if (threadIdx.x < 64) {
+      const int t = threadIdx.x;
+      float dg = 0.f, db = 0.f;
+      if (t < C) {
+        const float gam = __expf(sg[t]);
+        dg = sdg[t] + sb[t] * gam * scx[t];
+        db = sdb[t] + gam * scx[t];
+      }
+      const float dla = wave_incl_suffix(dg);
+      if (t < nv) {
+        dlog_a[(tok0 + t) * H + h] = dla;
+        dbeta[(tok0 + t) * H + h] = db;
+      }
     }
-    const float dla = wave_incl_suffix(dg);
-    if (t < nv) {
-      dlog_a[(tok0 + t) * H + h] = dla;
-      dbeta[(tok0 + t) * H + h] = db;
-    }
+    lds_barrier();
+    lds_to_rows<E, C, DK>(dk + (tok0 * H + h) * DK, (size_t)H * DK, sdK, LK, nv);
+    lds_barrier();
   }
+#undef LRT_G2_LOAD
 }
 
 // --------------------------------------------------------------- launcher
@@ -675,26 +735,26 @@ int bwd_impl(const BwdArgs& a) {
     const int tiles = a.B * a.H * N;
     const BwdWs ws = bwd_ws_layout(a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
     hipStream_t st = (hipStream_t)a.stream;
-    constexpr int BV = DV < 32 ? DV : 32;
+    constexpr int BV = DV < 64 ? DV : 64;  // state columns per workgroup
     const int sgrid = a.B * a.H * (DV / BV);
-    LRT_LAUNCH(kKPrep, (k_prep<E, C, DK, DV, true, true>), dim3(tiles), dim3(kThreads), st, (const E*)a.k,
-                       (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, (E*)ws.f.W, (E*)ws.f.Up, (E*)ws.f.Kt,
+    LRT_LAUNCH(kKPrep, (k_prep<E, C, DK, DV, true, true>), dim3(persistent_grid(tiles, PrepLds<E, C, DK, DV, true>::TOTAL)), dim3(kThreads), st, (const E*)a.k,
+                       (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.f.W, (E*)ws.f.Up, (E*)ws.f.Kt,
                        ws.f.G, (E*)ws.T);
-    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, true>), dim3(sgrid), dim3(kThreads), st, (const E*)ws.f.W,
+    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, true, false, kStateWaves>), dim3(sgrid), dim3(64 * kStateWaves), st, (const E*)ws.f.W,
                        (const E*)ws.f.Up, (const E*)ws.f.Kt, ws.f.G, (const float*)nullptr, a.h0, (float*)nullptr, (E*)ws.f.U,
                        (E*)ws.f.S, N, DV);
     E* dUl = (E*)ws.f.Up;
-    LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV>), dim3(tiles), dim3(kThreads), st, (const E*)a.q,
-                       (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N);
-    LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV>), dim3(sgrid), dim3(kThreads), st, (const E*)a.q,
+    LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV>), dim3(persistent_grid(tiles, LocalLds<E, C, DK, DV>::TOTAL)), dim3(kThreads), st,
+               (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N, tiles);
+    LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves>), dim3(sgrid), dim3(64 * kStateWaves), st, (const E*)a.q,
                        (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.W, (const E*)dUl, a.dht, a.dh0,
                        (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
-    LRT_LAUNCH(kKGrad1, (k_grad1<E, C, DK, DV>), dim3(tiles), dim3(kThreads), st, (const E*)a.q,
+    LRT_LAUNCH(kKGrad1, (k_grad1<E, C, DK, DV>), dim3(persistent_grid(tiles, Grad1Lds<E, C, DK, DV>::TOTAL)), dim3(kThreads), st, (const E*)a.q,
                        (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.S, (const E*)ws.dS,
-                       (const E*)ws.f.U, (const E*)ws.dU, (E*)a.dq, (E*)ws.dW, ws.dK1, ws.dg1, a.T, a.H, N);
-    LRT_LAUNCH(kKGrad2, (k_grad2<E, C, DK, DV>), dim3(tiles), dim3(kThreads), st, (const E*)a.k,
-                       (const E*)a.v, a.beta, ws.f.G, (const E*)ws.T, (const E*)ws.dW, (const E*)ws.dU, ws.dK1,
-                       ws.dg1, (E*)a.dk_out, (E*)a.dv_out, a.dlog_a, a.dbeta, a.T, a.H, N);
+                       (const E*)ws.f.U, (const E*)ws.dU, (E*)a.dq, (E*)ws.dW, (E*)ws.dK1, ws.dg1, a.T, a.H, N, tiles);
+    LRT_LAUNCH(kKGrad2, (k_grad2<E, C, DK, DV>), dim3(persistent_grid(tiles, Grad2Lds<E, C, DK, DV>::TOTAL)), dim3(kThreads), st, (const E*)a.k,
+                       (const E*)a.v, a.beta, ws.f.G, (const E*)ws.T, (const E*)ws.dW, (const E*)ws.dU, (const E*)ws.dK1,
+                       ws.dg1, (E*)a.dk_out, (E*)a.dv_out, a.dlog_a, a.dbeta, a.T, a.H, N, tiles);
     return hipGetLastError() == hipSuccess ? 0 : -7;
   }
 }

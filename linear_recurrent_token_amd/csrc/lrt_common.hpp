@@ -34,6 +34,21 @@ constexpr int lds_pad() {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, then s_barrier.  Unlike __syncthreads() it does not drain the
+// wave's outstanding global loads and stores, so prefetched tiles stay in
+// flight across it.  Every kernel here exchanges data between waves through
+// LDS only.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2.  Renumber them so that consecutive logical ids run on one XCD (when
+// the grid divides evenly): work items that read the same data share a cache.
+__device__ __forceinline__ int xcd_group(int bid, int nblocks) {
+  if (nblocks % 8 != 0) return bid;
+  return (bid % 8) * (nblocks / 8) + bid / 8;
+}
+
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 
@@ -50,35 +65,91 @@ __device__ __forceinline__ bf16 from_f<bf16>(float x) {
 }
 
 // ---------------------------------------------------------------- MFMA tiles
-// acc(16x16) += A(16 x K) * B(K x 16), operands in LDS as described above.
-template <int K>
-__device__ __forceinline__ void mma(f32x4& acc, const bf16* a, int lda, const bf16* bt, int ldb) {
+// acc(16x16) += A(16 x K) * B(K x 16) from LDS.  Each operand is stored either
+//   "k-inner":  A(m, k) at a[m * lda + k],   B(k, n) at b[n * ldb + k]
+//   "k-outer":  A(m, k) at a[k * lda + m],   B(k, n) at b[k * ldb + n]
+// (template flags AK / BK select k-outer).  A k-inner fragment is one 16-byte
+// LDS read per lane.  A k-outer bf16 fragment uses the gfx950 LDS transpose
+// read (ds_read_b64_tr_b16): within each group of 16 lanes, lane j supplies
+// the address of 4 consecutive elements of row j/4, columns 4*(j%4).., and
+// lane r receives element r%4 of the rows supplied by lanes 4e + r/4
+// (e = 0..3), i.e. 4 consecutive k of column r -- so operands laid out
+// row-major by k feed the matrix cores without a transposed copy.
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ i16x4 lds_read_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const void*)p);
+}
+
+// 8 consecutive k (k0 + 8g .. k0 + 8g + 7, g = lane/16) of column n0 + lane%16
+// of a k-outer bf16 operand.
+__device__ __forceinline__ bf16x8 frag_k8_outer(const bf16* p, int ld, int k0, int n0) {
+  const int l = lane_id(), g = l >> 4, j = l & 15;
+  const bf16* src = p + (k0 + 8 * g + (j >> 2)) * ld + n0 + 4 * (j & 3);
+  const i16x4 lo = lds_read_tr(src);
+  const i16x4 hi = lds_read_tr(src + 4 * ld);
+  const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+// 4 consecutive k (k0 + 4g ..) of column n0 + lane%16, k-outer bf16 operand.
+__device__ __forceinline__ i16x4 frag_k4_outer(const bf16* p, int ld, int k0, int n0) {
+  const int l = lane_id(), g = l >> 4, j = l & 15;
+  return lds_read_tr(p + (k0 + 4 * g + (j >> 2)) * ld + n0 + 4 * (j & 3));
+}
+
+template <int K, bool AK = false, bool BK = false>
+__device__ __forceinline__ void mma(f32x4& acc, const bf16* a, int lda, const bf16* b, int ldb) {
   const int l = lane_id();
-  const bf16* pa = a + (l & 15) * lda + (l >> 4) * 8;
-  const bf16* pb = bt + (l & 15) * ldb + (l >> 4) * 8;
 #pragma unroll
-  for (int k = 0; k + 32 <= K; k += 32)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(pa + k), *(const bf16x8*)(pb + k),
-                                                  acc, 0, 0, 0);
+  for (int k = 0; k + 32 <= K; k += 32) {
+    bf16x8 fa, fb;
+    if constexpr (AK)
+      fa = frag_k8_outer(a, lda, k, 0);
+    else
+      fa = *(const bf16x8*)(a + (l & 15) * lda + k + (l >> 4) * 8);
+    if constexpr (BK)
+      fb = frag_k8_outer(b, ldb, k, 0);
+    else
+      fb = *(const bf16x8*)(b + (l & 15) * ldb + k + (l >> 4) * 8);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
+  }
   if constexpr (K % 32 == 16) {
-    const bf16* qa = a + (l & 15) * lda + (K - 16) + (l >> 4) * 4;
-    const bf16* qb = bt + (l & 15) * ldb + (K - 16) + (l >> 4) * 4;
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(*(const i16x4*)qa, *(const i16x4*)qb, acc, 0, 0, 0);
+    constexpr int k = K - 16;
+    i16x4 fa, fb;
+    if constexpr (AK)
+      fa = frag_k4_outer(a, lda, k, 0);
+    else
+      fa = *(const i16x4*)(a + (l & 15) * lda + k + (l >> 4) * 4);
+    if constexpr (BK)
+      fb = frag_k4_outer(b, ldb, k, 0);
+    else
+      fb = *(const i16x4*)(b + (l & 15) * ldb + k + (l >> 4) * 4);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa, fb, acc, 0, 0, 0);
   }
 }
 
 // fp32 operands: 16x16x4 MFMA.  Lane group g = l/16 feeds k = 4g + s at step
-// s, so each lane reads 4 consecutive k with one 16-byte load per 16 k.
-template <int K>
-__device__ __forceinline__ void mma(f32x4& acc, const float* a, int lda, const float* bt, int ldb) {
+// s, so a k-inner lane reads 4 consecutive k with one 16-byte load per 16 k;
+// a k-outer lane reads them one by one (consecutive lanes, consecutive m/n).
+template <int K, bool AK = false, bool BK = false>
+__device__ __forceinline__ void mma(f32x4& acc, const float* a, int lda, const float* b, int ldb) {
   static_assert(K % 16 == 0, "fp32 contraction length must be a multiple of 16");
-  const int l = lane_id();
-  const float* pa = a + (l & 15) * lda + (l >> 4) * 4;
-  const float* pb = bt + (l & 15) * ldb + (l >> 4) * 4;
+  const int l = lane_id(), g = l >> 4, j = l & 15;
 #pragma unroll
   for (int k = 0; k < K; k += 16) {
-    const f32x4 va = *(const f32x4*)(pa + k);
-    const f32x4 vb = *(const f32x4*)(pb + k);
+    f32x4 va, vb;
+    if constexpr (AK) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) va[s] = a[(k + 4 * g + s) * lda + j];
+    } else {
+      va = *(const f32x4*)(a + j * lda + k + 4 * g);
+    }
+    if constexpr (BK) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) vb[s] = b[(k + 4 * g + s) * ldb + j];
+    } else {
+      vb = *(const f32x4*)(b + j * ldb + k + 4 * g);
+    }
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(va[0], vb[0], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(va[1], vb[1], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(va[2], vb[2], acc, 0, 0, 0);
@@ -149,19 +220,19 @@ __device__ __forceinline__ u32x4 vec_scale(u32x4 x, float s) {
 // An R x W tile of E moved global -> registers -> LDS in 16-byte pieces.
 // Every load of a tile is issued before the first LDS store, so a thread
 // keeps all its loads in flight at once (the loops unroll completely).
-template <typename E, int R, int W>
+template <typename E, int R, int W, int NT = kThreads>
 struct Tile {
   static constexpr int V = 16 / (int)sizeof(E);
   static constexpr int PR = W / V;  // pieces per row
   static constexpr int NP = R * PR;
-  static constexpr int PT = (NP + kThreads - 1) / kThreads;
+  static constexpr int PT = (NP + NT - 1) / NT;
   u32x4 x[PT];
 
   // rows of a strided global array; rows >= nvalid read as zero
   __device__ __forceinline__ void load_rows(const E* g, size_t gs, int nvalid) {
 #pragma unroll
     for (int s = 0; s < PT; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
+      const int idx = threadIdx.x + NT * s;
       x[s] = u32x4{0u, 0u, 0u, 0u};
       if (idx < NP) {
         const int r = idx / PR, c = (idx % PR) * V;
@@ -173,14 +244,14 @@ struct Tile {
   __device__ __forceinline__ void load_block(const E* g) {
 #pragma unroll
     for (int s = 0; s < PT; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
+      const int idx = threadIdx.x + NT * s;
       if (idx < NP) x[s] = *(const u32x4*)(g + (size_t)idx * V);
     }
   }
   __device__ __forceinline__ void scale_rows(const float* rs) {
 #pragma unroll
     for (int s = 0; s < PT; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
+      const int idx = threadIdx.x + NT * s;
       if (idx < NP) x[s] = vec_scale<E>(x[s], rs[idx / PR]);
     }
   }
@@ -188,7 +259,7 @@ struct Tile {
   __device__ __forceinline__ void store(E* lds, int ls) const {
 #pragma unroll
     for (int s = 0; s < PT; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
+      const int idx = threadIdx.x + NT * s;
       if (idx < NP) {
         const int r = idx / PR, c = (idx % PR) * V;
         *(u32x4*)(lds + r * ls + c) = x[s];
@@ -199,7 +270,7 @@ struct Tile {
   __device__ __forceinline__ void store_T(E* lds, int ld) const {
 #pragma unroll
     for (int s = 0; s < PT; ++s) {
-      const int idx = threadIdx.x + kThreads * s;
+      const int idx = threadIdx.x + NT * s;
       if (idx < NP) {
         const int r = idx / PR, c = (idx % PR) * V;
         vec_to_lds_T<E>(lds, ld, r, c, x[s]);
@@ -207,6 +278,60 @@ struct Tile {
     }
   }
 };
+
+// Copy an R x W block from LDS (row stride ls) to a dense global block,
+// 16 bytes per access, threads [0, NT).
+template <typename E, int R, int W, int NT = kThreads>
+__device__ __forceinline__ void lds_to_block(E* g, const E* lds, int ls) {
+  constexpr int V = 16 / (int)sizeof(E), PR = W / V;
+#pragma unroll
+  for (int s = 0; s < (R * PR + NT - 1) / NT; ++s) {
+    const int idx = threadIdx.x + NT * s;
+    if (idx < R * PR) {
+      const int r = idx / PR, c = (idx % PR) * V;
+      *(u32x4*)(g + (size_t)r * W + c) = *(const u32x4*)(lds + r * ls + c);
+    }
+  }
+}
+
+// Accumulator-tile order: a matrix produced as 16x16 accumulator tiles of its
+// transpose (tile (ta, tb) holds X^T rows 16ta.., cols 16tb..) is written
+// lane-major -- each lane's 4 values at ((tile * 64 + lane) * 4) -- so one
+// wave writes 64 contiguous 4-element pieces.  acc_tiles_to_lds rebuilds X
+// row-major in LDS, X[16tb + l%16][16ta + 4(l/16) + r] = value r of lane l.
+template <typename E>
+__device__ __forceinline__ void acc_tile_store(E* base, int tile_id, f32x4 acc) {
+  store4<E>(base + ((size_t)tile_id * 64 + lane_id()) * 4, acc);
+}
+template <typename E, int NTA, int NTB, int NT = kThreads>
+__device__ __forceinline__ void acc_tiles_to_lds(E* lds, int ld, const E* g) {
+  constexpr int NS = NTA * NTB * 64;  // 4-element slots
+#pragma unroll
+  for (int s = 0; s < (NS + NT - 1) / NT; ++s) {
+    const int p = threadIdx.x + NT * s;
+    if (p < NS) {
+      const int tile = p >> 6, ln = p & 63;
+      const int ta = tile / NTB, tb = tile % NTB;
+      const f32x4 x = load4<E>(g + (size_t)p * 4);
+      store4<E>(lds + (tb * 16 + (ln & 15)) * ld + ta * 16 + (ln >> 4) * 4, x);
+    }
+  }
+}
+
+// Copy R rows of W elements from LDS (row stride ls) to global rows (row
+// stride gs), 16 bytes per access; rows >= nvalid are not written.
+template <typename E, int R, int W, int NT = kThreads>
+__device__ __forceinline__ void lds_to_rows(E* g, size_t gs, const E* lds, int ls, int nvalid) {
+  constexpr int V = 16 / (int)sizeof(E), PR = W / V;
+#pragma unroll
+  for (int s = 0; s < (R * PR + NT - 1) / NT; ++s) {
+    const int idx = threadIdx.x + NT * s;
+    if (idx < R * PR) {
+      const int r = idx / PR, c = (idx % PR) * V;
+      if (r < nvalid) *(u32x4*)(g + (size_t)r * gs + c) = *(const u32x4*)(lds + r * ls + c);
+    }
+  }
+}
 
 // Copy R rows of W elements from global (row stride gs elements) into LDS
 // (row stride ls); rows >= nvalid become zero.

@@ -1,4 +1,5 @@
 // lrt_fwd.hip -- launchers of the chunkwise forward (gdn_fwd, ssd_fwd).
+#include "lrt_fused_fwd.hpp"
 #include "lrt_fwd_kernels.hpp"
 #include "lrt_internal.hpp"
 
@@ -7,29 +8,43 @@ namespace lrt {
 // --------------------------------------------------------------- launchers
 template <typename E, int C, int DK, int DV>
 int fwd_impl(const FwdArgs& a) {
+  constexpr int BVF = DV < 64 ? DV : 64;
+  if constexpr (FusedLds<E, C, DK, BVF, true>::TOTAL <= 160 * 1024) {
+    // the whole forward in one kernel: state on chip, inputs read once
+    const int N = (a.T + C - 1) / C;
+    hipStream_t st = (hipStream_t)a.stream;
+    const int grid = a.B * a.H * (DV / BVF);
+    if (a.variant == kVarGDN)
+      LRT_LAUNCH(kKFwd, (k_fwd<E, C, DK, BVF, true, kStateWaves>), dim3(grid), dim3(64 * kStateWaves), st,
+                 (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.h0, a.ht, (E*)a.o, a.T, a.H, N, DV);
+    else
+      LRT_LAUNCH(kKFwd, (k_fwd<E, C, DK, BVF, false, kStateWaves>), dim3(grid), dim3(64 * kStateWaves), st,
+                 (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.h0, a.ht, (E*)a.o, a.T, a.H, N, DV);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+  }
   const int N = (a.T + C - 1) / C;
   const int tiles = a.B * a.H * N;
   const FwdWs ws = fwd_ws_layout(a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
   hipStream_t st = (hipStream_t)a.stream;
   const bool delta = a.variant == kVarGDN;
   if (delta)
-    LRT_LAUNCH(kKPrep, (k_prep<E, C, DK, DV, true>), dim3(tiles), dim3(kThreads), st, (const E*)a.k,
-                       (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.G, (E*)nullptr);
+    LRT_LAUNCH(kKPrep, (k_prep<E, C, DK, DV, true>), dim3(persistent_grid(tiles, PrepLds<E, C, DK, DV, true>::TOTAL)), dim3(kThreads), st, (const E*)a.k,
+                       (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.G, (E*)nullptr);
   else
-    LRT_LAUNCH(kKPrep, (k_prep<E, C, DK, DV, false>), dim3(tiles), dim3(kThreads), st, (const E*)a.k,
-                       (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.G, (E*)nullptr);
-  constexpr int BV = DV < 32 ? DV : 32;
+    LRT_LAUNCH(kKPrep, (k_prep<E, C, DK, DV, false>), dim3(persistent_grid(tiles, PrepLds<E, C, DK, DV, false>::TOTAL)), dim3(kThreads), st, (const E*)a.k,
+                       (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.G, (E*)nullptr);
+  constexpr int BV = DV < 64 ? DV : 64;  // state columns per workgroup
   const int sgrid = a.B * a.H * (DV / BV);
   if (delta)
-    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, true>), dim3(sgrid), dim3(kThreads), st, (const E*)ws.W,
+    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, true, false, kStateWaves>), dim3(sgrid), dim3(64 * kStateWaves), st, (const E*)ws.W,
                        (const E*)ws.Up, (const E*)ws.Kt, ws.G, (const float*)nullptr, a.h0, a.ht, (E*)ws.U, (E*)ws.S, N, DV);
   else
-    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, false>), dim3(sgrid), dim3(kThreads), st, (const E*)ws.W,
+    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, false, false, kStateWaves>), dim3(sgrid), dim3(64 * kStateWaves), st, (const E*)ws.W,
                        (const E*)ws.Up, (const E*)ws.Kt, ws.G, (const float*)nullptr, a.h0, a.ht, (E*)ws.U, (E*)ws.S, N, DV);
   // fp32 operands need twice the LDS: split the value columns in blocks of 64
   constexpr int BVO = (sizeof(E) == 4 && DV > 64) ? 64 : DV;
-  LRT_LAUNCH(kKOut, (k_out<E, C, DK, BVO>), dim3(tiles * (DV / BVO)), dim3(kThreads), st, (const E*)a.q,
-                     (const E*)a.k, ws.G, (const E*)ws.S, (const E*)ws.U, (const E*)nullptr, (const E*)nullptr, (E*)a.o, a.T, a.H, N, DV);
+  LRT_LAUNCH(kKOut, (k_out<E, C, DK, BVO>), dim3(persistent_grid(tiles * (DV / BVO), out_lds_bytes<E, C, DK, BVO, false>())), dim3(kThreads), st, (const E*)a.q,
+                     (const E*)a.k, ws.G, (const E*)ws.S, (const E*)ws.U, (const E*)nullptr, (const E*)nullptr, (E*)a.o, a.T, a.H, N, DV, tiles * (DV / BVO));
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

@@ -27,209 +27,249 @@ namespace lrt {
 // (I + A)^-1 for a strictly lower-triangular C x C matrix A in LDS (fp32,
 // row stride C + 1), written to Tf (same layout; only the lower triangle,
 // diagonal included, is defined).  Stage 1 inverts the 16 x 16 diagonal
-// blocks by forward substitution, one lane per column; stage 2 fills block
-// row bi from  T[bi][bj] = -T[bi][bi] sum_{m=bj}^{bi-1} A[bi][m] T[m][bj].
-// R is a 3 * 256-float scratch.  All 256 threads must call it after A is
-// visible to them; Tf is visible to all threads on return.
-template <int C>
+// blocks by forward substitution, one lane per column, right-looking (after
+// x_m is known every later row's partial sum takes its term at once, so the
+// dependent chain is 16 steps, not 120); stage 2 fills block row bi from
+// T[bi][bj] = -T[bi][bi] sum_{m=bj}^{bi-1} A[bi][m] T[m][bj].  R is a
+// 3 * 256-float scratch.  All NT threads must call it after A is visible to
+// them; Tf is visible to all threads on return.
+template <int C, int NT = kThreads>
 __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sTf, float* sR) {
   constexpr int NB = C / 16;
   constexpr int LA = C + 1;
-  // (I + A)^-1, stage 1: the 16x16 diagonal blocks by forward substitution,
-  // one lane per column (lanes 16*bb .. 16*bb+15 own block bb).
   if (threadIdx.x < 16 * NB) {
     const int bb = threadIdx.x >> 4, j = threadIdx.x & 15;
     const float* Ab = sA + (bb * 16) * LA + bb * 16;
     float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float s = (r == j) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
 #pragma unroll
-      for (int m = 0; m < r; ++m) s -= Ab[r * LA + m] * x[m];
-      x[r] = s;
-    }
+    for (int m = 0; m < 15; ++m)
+#pragma unroll
+      for (int r = m + 1; r < 16; ++r) x[r] -= Ab[r * LA + m] * x[m];
 #pragma unroll
     for (int r = 0; r < 16; ++r) sTf[(bb * 16 + r) * LA + bb * 16 + j] = x[r];
   }
-  __syncthreads();
+  lds_barrier();
   // stage 2: block row bi, T[bi][bj] = -T[bi][bi] sum_{m=bj}^{bi-1} A[bi][m] T[m][bj]
-  {
-    const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
-    for (int bi = 1; bi < NB; ++bi) {
+  const bool act = threadIdx.x < 256;
+  const int r = (threadIdx.x >> 4) & 15, c = threadIdx.x & 15;
+  for (int bi = 1; bi < NB; ++bi) {
+    if (act) {
       for (int bj = 0; bj < bi; ++bj) {
         float s = 0.f;
         for (int m = bj * 16; m < bi * 16; ++m) s += sA[(bi * 16 + r) * LA + m] * sTf[m * LA + bj * 16 + c];
         sR[bj * 256 + r * 16 + c] = s;
       }
-      __syncthreads();
+    }
+    lds_barrier();
+    if (act) {
       for (int bj = 0; bj < bi; ++bj) {
         float s = 0.f;
 #pragma unroll
         for (int m = 0; m < 16; ++m) s += sTf[(bi * 16 + r) * LA + bi * 16 + m] * sR[bj * 256 + m * 16 + c];
         sTf[(bi * 16 + r) * LA + bj * 16 + c] = -s;
       }
-      __syncthreads();
     }
+    lds_barrier();
   }
 }
 
-// ------------------------------------------------------------------ k_prep
+// LDS of k_prep, with the live ranges overlaid: K rows until K K^T is formed,
+// then the fp32 inverse; A until it is inverted, then Tinv in E.
+template <typename E, int C, int DK, int DV, bool DELTA>
+struct PrepLds {
+  static constexpr int P = lds_pad<E>();
+  static constexpr int LK = DK + P, LC = C + P, LA = C + 1;
+  static constexpr size_t es = sizeof(E);
+  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+  static constexpr size_t K = 0;
+  static constexpr size_t A = K + mx((size_t)C * LK * es, DELTA ? (size_t)C * LA * 4 : 0);
+  static constexpr size_t XT = A + (DELTA ? mx((size_t)C * LA * 4, (size_t)C * LC * es) : 0);
+  static constexpr size_t YT = XT + (DELTA ? (size_t)(DK > DV ? DK : DV) * LC * es : 0);
+  static constexpr size_t R = YT + (size_t)DV * LC * es;
+  static constexpr size_t G = R + (DELTA ? 3 * 256 * 4 : 0);
+  static constexpr size_t TOTAL = G + 4 * C * 4;
+};
+
+// Chunk-parallel: each workgroup walks tiles blockIdx.x, + gridDim.x, ...,
+// with the next tile's inputs loading into registers while this one computes.
 // WRITE_T (backward only) also stores Tinv [C][C] per chunk.
 template <typename E, int C, int DK, int DV, bool DELTA, bool WRITE_T = false>
 __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ k, const E* __restrict__ v,
                                                    const float* __restrict__ log_a,
                                                    const float* __restrict__ beta, int T, int H, int N,
-                                                   E* __restrict__ wW, E* __restrict__ wUp,
+                                                   int ntiles, E* __restrict__ wW, E* __restrict__ wUp,
                                                    E* __restrict__ wKt, float* __restrict__ wG,
                                                    E* __restrict__ wT) {
-  constexpr int P = lds_pad<E>();
-  constexpr int LK = DK + P;  // rows indexed by token, contiguous over d
-  constexpr int LC = C + P;   // rows indexed by d or v, contiguous over tokens
+  typedef PrepLds<E, C, DK, DV, DELTA> Lay;
+  constexpr int LK = Lay::LK, LC = Lay::LC, LA = Lay::LA;
   constexpr int NB = C / 16;
-  constexpr int LA = C + 1;
-  __shared__ float sg[C], sgam[C], sb[C], sbg[C];
-  __shared__ __attribute__((aligned(16))) E sK[C * LK];
-  __shared__ __attribute__((aligned(16))) E sYt[DV * LC];
-  __shared__ __attribute__((aligned(16))) E sXt[DELTA ? DK * LC : 8];
-  __shared__ __attribute__((aligned(16))) E sT[DELTA ? C * LC : 8];
-  __shared__ float sA[DELTA ? C * LA : 1];
-  __shared__ float sTf[DELTA ? C * LA : 1];
-  __shared__ float sR[DELTA ? 3 * 256 : 1];
-
-  const int tile = blockIdx.x;
-  const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
-  const int t0 = n * C, nv = min(C, T - t0);
-  const size_t tok0 = (size_t)b * T + t0;
+  constexpr int V = 16 / (int)sizeof(E);
+  __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
+  E* sK = (E*)(smem + Lay::K);
+  float* sTf = (float*)(smem + Lay::K);
+  float* sA = (float*)(smem + Lay::A);
+  E* sT = (E*)(smem + Lay::A);
+  E* sXt = (E*)(smem + Lay::XT);
+  E* sYt = (E*)(smem + Lay::YT);
+  float* sR = (float*)(smem + Lay::R);
+  float* sg = (float*)(smem + Lay::G);
+  float* sgam = sg + C;
+  float* sb = sg + 2 * C;
+  float* sbg = sg + 3 * C;
   const int w = wave_id(), l = lane_id();
 
   Tile<E, C, DK> tk;
   Tile<E, C, DV> tv;
-  tk.load_rows(k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-  tv.load_rows(v + (tok0 * H + h) * DV, (size_t)H * DV, nv);
-  if (threadIdx.x < 64) {
-    const int t = threadIdx.x;
-    float la = 0.f, bt = 0.f;
-    if (t < nv) {
-      la = log_a[(tok0 + t) * H + h];
-      if (DELTA) bt = beta[(tok0 + t) * H + h];
-    }
-    const float g = wave_incl_scan(la);
-    if (t < C) {
-      sg[t] = g;
-      sgam[t] = __expf(g);
-      sb[t] = bt;
-      sbg[t] = bt * __expf(g);
-      wG[(size_t)tile * C + t] = g;
-    }
+  float la = 0.f, bt = 0.f;
+#define LRT_PREP_LOAD(tile_)                                                              \
+  {                                                                                       \
+    const int ln = (tile_) % N, lbh = (tile_) / N;                                        \
+    const int lnv = min(C, T - ln * C);                                                   \
+    const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                           \
+    const int lh = lbh % H;                                                               \
+    tk.load_rows(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
+    tv.load_rows(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                          \
+    la = 0.f;                                                                             \
+    bt = 0.f;                                                                             \
+    if (threadIdx.x < lnv) {                                                              \
+      la = log_a[(ltok + threadIdx.x) * H + lh];                                          \
+      if (DELTA) bt = beta[(ltok + threadIdx.x) * H + lh];                                \
+    }                                                                                     \
   }
-  tk.store(sK, LK);
-  __syncthreads();
 
-  // Y^T = (diag(b) V)^T (SSD: V^T) -> sYt[v][t]
-  if (DELTA) tv.scale_rows(sb);
-  tv.store_T(sYt, LC);
-  // Ktil^T[d][t] = e^(g_C - g_t) k_t[d] -> workspace, 16 bytes per store
-  {
-    constexpr int V = 16 / (int)sizeof(E);
-    const float gC = sg[C - 1];
-    E* out = wKt + (size_t)tile * DK * C;
-    for (int idx = threadIdx.x; idx < DK * (C / V); idx += kThreads) {
-      const int d = idx / (C / V), t = (idx % (C / V)) * V;
-      E e[V];
-#pragma unroll
-      for (int i = 0; i < V; ++i) e[i] = from_f<E>(__expf(gC - sg[t + i]) * to_f(sK[(t + i) * LK + d]));
-      u32x4 x;
-      __builtin_memcpy(&x, e, 16);
-      *(u32x4*)(out + (size_t)d * C + t) = x;
-    }
-  }
-  if constexpr (!DELTA) {
-    __syncthreads();
-    constexpr int V = 16 / (int)sizeof(E);
-    E* out = wUp + (size_t)tile * DV * C;
-    for (int idx = threadIdx.x; idx < DV * (C / V); idx += kThreads) {
-      const int c = idx / (C / V), t = (idx % (C / V)) * V;
-      *(u32x4*)(out + (size_t)c * C + t) = *(const u32x4*)(sYt + c * LC + t);
-    }
-    return;
-  } else {
-    // X^T = (diag(b gamma) K)^T -> sXt[d][t], from the registers of K
-    tk.scale_rows(sbg);
-    tk.store_T(sXt, LC);
-    // A = strict_lower(b_i (k_i . k_j) e^(g_i - g_j))
-    for (int tt = w; tt < NB * NB; tt += kWaves) {
-      const int ti = tt / NB, tj = tt % NB;
-      f32x4 acc = zero4();
-      if (tj <= ti) mma<DK>(acc, sK + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
-      const int j = tj * 16 + (l & 15);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = ti * 16 + (l >> 4) * 4 + r;
-        sA[i * LA + j] = (j < i) ? sb[i] * acc[r] * __expf(sg[i] - sg[j]) : 0.f;
+  int tile = blockIdx.x;
+  if (tile < ntiles) LRT_PREP_LOAD(tile)
+  for (; tile < ntiles; tile += gridDim.x) {
+    if (threadIdx.x < 64) {
+      const int t = threadIdx.x;
+      const float g = wave_incl_scan(la);
+      if (t < C) {
+        const float gam = __expf(g);
+        sg[t] = g;
+        sgam[t] = gam;
+        sb[t] = bt;
+        sbg[t] = bt * gam;
+        wG[(size_t)tile * C + t] = g;
       }
     }
-    __syncthreads();
-    unit_lower_inverse<C>(sA, sTf, sR);
-    for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
-      const int i = idx / C, j = idx % C;
-      const E x = from_f<E>(j <= i ? sTf[i * LA + j] : 0.f);
-      sT[i * LC + j] = x;
-      if (WRITE_T) wT[(size_t)tile * C * C + idx] = x;
+    tk.store(sK, LK);
+    lds_barrier();
+    // Y^T = (diag(b) V)^T (SSD: V^T) -> sYt[v][t]
+    if (DELTA) tv.scale_rows(sb);
+    tv.store_T(sYt, LC);
+    if constexpr (DELTA) {
+      // X^T = (diag(b gamma) K)^T -> sXt[d][t], from the registers of K
+      tk.scale_rows(sbg);
+      tk.store_T(sXt, LC);
     }
-    __syncthreads();
-    // W^T = X^T Tinv^T (rows d, cols t) -> W[t][d]
-    E* wout = wW + (size_t)tile * C * DK;
-    for (int tt = w; tt < (DK / 16) * NB; tt += kWaves) {
-      const int td = tt / NB, tc = tt % NB;
-      f32x4 acc = zero4();
-      mma<C>(acc, sXt + td * 16 * LC, LC, sT + tc * 16 * LC, LC);
-      store4<E>(wout + (size_t)(tc * 16 + (l & 15)) * DK + td * 16 + (l >> 4) * 4, acc);
+    // Ktil^T[d][t] = e^(g_C - g_t) k_t[d] -> workspace, 16 bytes per store
+    {
+      const float gC = sg[C - 1];
+      E* out = wKt + (size_t)tile * DK * C;
+      for (int idx = threadIdx.x; idx < DK * (C / V); idx += kThreads) {
+        const int d = idx / (C / V), t = (idx % (C / V)) * V;
+        E e[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) e[i] = from_f<E>(__expf(gC - sg[t + i]) * to_f(sK[(t + i) * LK + d]));
+        u32x4 x;
+        __builtin_memcpy(&x, e, 16);
+        *(u32x4*)(out + (size_t)d * C + t) = x;
+      }
     }
-    // U' = Tinv Y (rows t, cols v) -> U'^T[v][t]
-    E* uout = wUp + (size_t)tile * DV * C;
-    for (int tt = w; tt < NB * (DV / 16); tt += kWaves) {
-      const int ti = tt / (DV / 16), tv = tt % (DV / 16);
-      f32x4 acc = zero4();
-      mma<C>(acc, sT + ti * 16 * LC, LC, sYt + tv * 16 * LC, LC);
-      store4<E>(uout + (size_t)(tv * 16 + (l & 15)) * C + ti * 16 + (l >> 4) * 4, acc);
+    // every register tile is consumed: start loading the next one
+    if (tile + (int)gridDim.x < ntiles) LRT_PREP_LOAD(tile + (int)gridDim.x)
+    if constexpr (!DELTA) {
+      lds_barrier();
+      E* out = wUp + (size_t)tile * DV * C;
+      for (int idx = threadIdx.x; idx < DV * (C / V); idx += kThreads) {
+        const int c = idx / (C / V), t = (idx % (C / V)) * V;
+        *(u32x4*)(out + (size_t)c * C + t) = *(const u32x4*)(sYt + c * LC + t);
+      }
+      lds_barrier();
+    } else {
+      // A = strict_lower(b_i (k_i . k_j) e^(g_i - g_j))
+      for (int tt = w; tt < NB * NB; tt += kWaves) {
+        const int ti = tt / NB, tj = tt % NB;
+        f32x4 acc = zero4();
+        if (tj <= ti) mma<DK>(acc, sK + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
+        const int j = tj * 16 + (l & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = ti * 16 + (l >> 4) * 4 + r;
+          sA[i * LA + j] = (j < i) ? sb[i] * acc[r] * __expf(sg[i] - sg[j]) : 0.f;
+        }
+      }
+      lds_barrier();
+      unit_lower_inverse<C>(sA, sTf, sR);  // writes over the dead K rows
+      for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
+        const int i = idx / C, j = idx % C;
+        const E x = from_f<E>(j <= i ? sTf[i * LA + j] : 0.f);
+        sT[i * LC + j] = x;  // over the dead A
+        if (WRITE_T) wT[(size_t)tile * C * C + idx] = x;
+      }
+      lds_barrier();
+      // W^T = X^T Tinv^T (rows d, cols t), staged as W[t][d] over the dead inverse
+      E* sWo = (E*)(smem + Lay::K);
+      for (int tt = w; tt < (DK / 16) * NB; tt += kWaves) {
+        const int td = tt / NB, tc = tt % NB;
+        f32x4 acc = zero4();
+        mma<C>(acc, sXt + td * 16 * LC, LC, sT + tc * 16 * LC, LC);
+        store4<E>(sWo + (tc * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, acc);
+      }
+      lds_barrier();
+      lds_to_block<E, C, DK>(wW + (size_t)tile * C * DK, sWo, LK);
+      // U' = Tinv Y (rows t, cols v), staged as U'^T[v][t] over the dead X^T
+      E* sUo = sXt;
+      for (int tt = w; tt < NB * (DV / 16); tt += kWaves) {
+        const int ti = tt / (DV / 16), tv = tt % (DV / 16);
+        f32x4 acc = zero4();
+        mma<C>(acc, sT + ti * 16 * LC, LC, sYt + tv * 16 * LC, LC);
+        store4<E>(sUo + (tv * 16 + (l & 15)) * LC + ti * 16 + (l >> 4) * 4, acc);
+      }
+      lds_barrier();
+      lds_to_block<E, DV, C>(wUp + (size_t)tile * DV * C, sUo, LC);
+      lds_barrier();
     }
   }
+#undef LRT_PREP_LOAD
 }
 
 // ----------------------------------------------------------------- k_state
-// One workgroup per (b, h, d_v block of BV columns); walks the N chunks.
+// One workgroup of NW waves per (b, h, d_v block of BV columns); walks the N
+// chunks.  The state block (d_k x BV, fp32) lives in MFMA accumulators; the
+// next chunk's W, Ktil^T and U' load into registers while this one computes;
+// chunk-start states and U leave through LDS as coalesced 16-byte rows.
 // PERDIM (KDA): the chunk decay is per key dimension, e^(GC[d]) from wGC.
-template <typename E, int C, int DK, int BV, bool DELTA, bool PERDIM = false>
-__global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, const E* __restrict__ wUp,
-                                                    const E* __restrict__ wKt, const float* __restrict__ wG,
-                                                    const float* __restrict__ wGC, const float* h0, float* ht,
-                                                    E* __restrict__ wU, E* __restrict__ wS, int N, int DV) {
+template <typename E, int C, int DK, int BV, bool DELTA, bool PERDIM = false, int NW = 8>
+__global__ __launch_bounds__(64 * NW) void k_state(const E* __restrict__ wW, const E* __restrict__ wUp,
+                                                   const E* __restrict__ wKt, const float* __restrict__ wG,
+                                                   const float* __restrict__ wGC, const float* h0, float* ht,
+                                                   E* __restrict__ wU, E* __restrict__ wS, int N, int DV) {
+  constexpr int NT = 64 * NW;
   constexpr int P = lds_pad<E>();
   constexpr int LK = DK + P, LC = C + P;
   constexpr int NTV = BV / 16;
   constexpr int NH = (DK / 16) * NTV;  // state tiles
-  constexpr int HPW = (NH + kWaves - 1) / kWaves;
+  constexpr int HPW = (NH + NW - 1) / NW;
   constexpr int NU = (C / 16) * NTV;  // U tiles
-  constexpr int UPW = (NU + kWaves - 1) / kWaves;
-  constexpr int V16 = 16 / (int)sizeof(E);
-  constexpr int NW16 = DELTA ? C * DK / V16 : 0;
-  constexpr int NK16 = DK * C / V16;
-  constexpr int PW = (NW16 + kThreads - 1) / kThreads;
-  constexpr int PK = (NK16 + kThreads - 1) / kThreads;
+  constexpr int UPW = (NU + NW - 1) / NW;
   __shared__ __attribute__((aligned(16))) E sW[DELTA ? C * LK : 8];
   __shared__ __attribute__((aligned(16))) E sKt[DK * LC];
-  __shared__ __attribute__((aligned(16))) E sS[DELTA ? BV * LK : 8];
+  __shared__ __attribute__((aligned(16))) E sS[BV * LK];
   __shared__ __attribute__((aligned(16))) E sU[BV * LC];
 
   const int nvb = DV / BV;
-  const int vb = blockIdx.x % nvb, bh = blockIdx.x / nvb;
+  const int wg = xcd_group(blockIdx.x, gridDim.x);  // the d_v blocks of one (b, h) share an L2
+  const int vb = wg % nvb, bh = wg / nvb;
   const int v0 = vb * BV;
   const int w = wave_id(), l = lane_id();
 
   f32x4 hacc[HPW];
 #pragma unroll
   for (int s = 0; s < HPW; ++s) {
-    const int tt = w + kWaves * s;
+    const int tt = w + NW * s;
     hacc[s] = zero4();
     if (tt < NH && h0 != nullptr) {
       const int td = tt / NTV, tv = tt % NTV;
@@ -239,8 +279,8 @@ __global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, co
     }
   }
 
-  Tile<E, C, DK> tW;   // W of the next chunk (delta variants)
-  Tile<E, DK, C> tK;   // Ktil^T of the next chunk
+  Tile<E, C, DK, NT> tW;   // W of the next chunk (delta variants)
+  Tile<E, DK, C, NT> tK;   // Ktil^T of the next chunk
   f32x4 rUp[UPW];
   f32x4 rgd[PERDIM ? HPW : 1];
   float rgc = 0.f;
@@ -250,14 +290,14 @@ __global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, co
     if (DELTA) tW.load_block(wW + ft * C * DK);                                                     \
     tK.load_block(wKt + ft * DK * C);                                                               \
     _Pragma("unroll") for (int s = 0; s < UPW; ++s) {                                               \
-      const int tt = w + kWaves * s;                                                                \
+      const int tt = w + NW * s;                                                                    \
       if (tt < NU)                                                                                  \
         rUp[s] = load4<E>(wUp + ft * DV * C + (size_t)(v0 + (tt % NTV) * 16 + (l & 15)) * C +      \
                           (tt / NTV) * 16 + (l >> 4) * 4);                                          \
     }                                                                                               \
     if constexpr (PERDIM) {                                                                         \
       _Pragma("unroll") for (int s = 0; s < HPW; ++s) {                                             \
-        const int tt = w + kWaves * s;                                                              \
+        const int tt = w + NW * s;                                                                  \
         if (tt < NH) rgd[s] = *(const f32x4*)(wGC + ft * DK + (tt / NTV) * 16 + (l >> 4) * 4);     \
       }                                                                                             \
     } else {                                                                                        \
@@ -280,43 +320,39 @@ __global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, co
       for (int s = 0; s < HPW; ++s)
         decd[s] = f32x4{__expf(rgd[s][0]), __expf(rgd[s][1]), __expf(rgd[s][2]), __expf(rgd[s][3])};
     }
-    if (n + 1 < N) LRT_STATE_FETCH(n + 1)
-#undef LRT_STATE_FETCH
-
-    // chunk start state: S = H^T -> LDS (operand of W Hn) and workspace
+    // chunk start state S = H^T -> LDS (operand of W Hn, then copied out)
 #pragma unroll
     for (int s = 0; s < HPW; ++s) {
-      const int tt = w + kWaves * s;
+      const int tt = w + NW * s;
       if (tt < NH) {
         const int td = tt / NTV, tv = tt % NTV;
-        const int vv = tv * 16 + (l & 15), d = td * 16 + (l >> 4) * 4;
-        if (DELTA) store4<E>(sS + vv * LK + d, hacc[s]);
-        store4<E>(wS + tile * DV * DK + (size_t)(v0 + vv) * DK + d, hacc[s]);
+        store4<E>(sS + (tv * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, hacc[s]);
       }
     }
-    __syncthreads();
+    if (n + 1 < N) LRT_STATE_FETCH(n + 1)
+    lds_barrier();
+    lds_to_block<E, BV, DK, NT>(wS + (tile * DV + v0) * DK, sS, LK);
     // U = U' - W Hn  (rows t, cols v)
 #pragma unroll
     for (int s = 0; s < UPW; ++s) {
-      const int tt = w + kWaves * s;
+      const int tt = w + NW * s;
       if (tt < NU) {
         const int ti = tt / NTV, tv = tt % NTV;
-        const int vv = tv * 16 + (l & 15), t = ti * 16 + (l >> 4) * 4;
         f32x4 u = up[s];
         if constexpr (DELTA) {
           f32x4 acc = zero4();
           mma<DK>(acc, sW + ti * 16 * LK, LK, sS + tv * 16 * LK, LK);
           u -= acc;
         }
-        store4<E>(sU + vv * LC + t, u);
-        store4<E>(wU + tile * DV * C + (size_t)(v0 + vv) * C + t, u);
+        store4<E>(sU + (tv * 16 + (l & 15)) * LC + ti * 16 + (l >> 4) * 4, u);
       }
     }
-    __syncthreads();
+    lds_barrier();
+    lds_to_block<E, BV, C, NT>(wU + (tile * DV + v0) * C, sU, LC);
     // H <- e^(g_C) H + Ktil^T U
 #pragma unroll
     for (int s = 0; s < HPW; ++s) {
-      const int tt = w + kWaves * s;
+      const int tt = w + NW * s;
       if (tt < NH) {
         const int td = tt / NTV, tv = tt % NTV;
         if constexpr (PERDIM)
@@ -326,12 +362,13 @@ __global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, co
         mma<C>(hacc[s], sKt + td * 16 * LC, LC, sU + tv * 16 * LC, LC);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
+#undef LRT_STATE_FETCH
   if (ht != nullptr) {
 #pragma unroll
     for (int s = 0; s < HPW; ++s) {
-      const int tt = w + kWaves * s;
+      const int tt = w + NW * s;
       if (tt < NH) {
         const int td = tt / NTV, tv = tt % NTV;
 #pragma unroll
@@ -343,48 +380,69 @@ __global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ wW, co
 }
 
 // ------------------------------------------------------------------- k_out
-// O^T = S Q^T (scaled by gamma per token) + U^T P^T, one workgroup per
-// (chunk, block of BVO value columns).
+// O^T = S Q^T (scaled by gamma per token) + U^T P^T per (chunk, block of BVO
+// value columns); workgroups walk these work items persistently, prefetching.
 // FROM_WS (KDA): Q o e^G and P are read from the workspace instead of being
 // formed from q, k and the scalar gates.
+template <typename E, int C, int DK, int BVO, bool FROM_WS>
+constexpr size_t out_lds_bytes() {
+  constexpr size_t P = lds_pad<E>(), es = sizeof(E);
+  constexpr size_t ko = C * ((DK > BVO ? DK : BVO) + P);
+  return C * 4 + (C * (DK + P) + ko + BVO * (DK + P) + BVO * (C + P) + C * (C + P)) * es;
+}
+
 template <typename E, int C, int DK, int BVO, bool FROM_WS = false>
 __global__ __launch_bounds__(kThreads) void k_out(const E* __restrict__ q, const E* __restrict__ k,
                                                   const float* __restrict__ wG, const E* __restrict__ wS,
                                                   const E* __restrict__ wU, const E* __restrict__ wQg,
                                                   const E* __restrict__ wP, E* __restrict__ o, int T, int H,
-                                                  int N, int DV) {
+                                                  int N, int DV, int nitems) {
   constexpr int P = lds_pad<E>();
   constexpr int LK = DK + P, LC = C + P;
   constexpr int NB = C / 16;
+  constexpr int LO = BVO + P;
   __shared__ float sg[C];
   __shared__ __attribute__((aligned(16))) E sQ[C * LK];
-  __shared__ __attribute__((aligned(16))) E sK[FROM_WS ? 8 : C * LK];
+  // K rows (dead once P is formed), then the output rows of this item
+  __shared__ __attribute__((aligned(16))) E sK[C * (DK > BVO ? LK : LO)];
   __shared__ __attribute__((aligned(16))) E sS[BVO * LK];
   __shared__ __attribute__((aligned(16))) E sU[BVO * LC];
   __shared__ __attribute__((aligned(16))) E sP[C * LC];
+  E* sO = sK;
 
   const int nvb = DV / BVO;
-  const int tile = blockIdx.x / nvb, v0 = (blockIdx.x % nvb) * BVO;
-  const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
-  const int t0 = n * C, nv = min(C, T - t0);
-  const size_t tok0 = (size_t)b * T + t0;
   const int w = wave_id(), l = lane_id();
+  Tile<E, C, DK> tq;
+  Tile<E, C, FROM_WS ? C : DK> tk;  // K rows, or P (FROM_WS)
+  Tile<E, BVO, DK> ts;
+  Tile<E, BVO, C> tu;
+  float rg = 0.f;
+#define LRT_OUT_LOAD(item_)                                                               \
+  {                                                                                       \
+    const int ltile = (item_) / nvb, lv0 = ((item_) % nvb) * BVO;                         \
+    const int ln = ltile % N, lbh = ltile / N;                                            \
+    const int lnv = min(C, T - ln * C);                                                   \
+    const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                           \
+    const int lh = lbh % H;                                                               \
+    if constexpr (FROM_WS) {                                                              \
+      tq.load_block(wQg + (size_t)ltile * C * DK);                                        \
+      tk.load_block(wP + (size_t)ltile * C * C);                                          \
+    } else {                                                                              \
+      tq.load_rows(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                        \
+      tk.load_rows(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                        \
+      if (threadIdx.x < C) rg = wG[(size_t)ltile * C + threadIdx.x];                      \
+    }                                                                                     \
+    ts.load_block(wS + ((size_t)ltile * DV + lv0) * DK);                                  \
+    tu.load_block(wU + ((size_t)ltile * DV + lv0) * C);                                   \
+  }
 
-  {
-    Tile<E, C, DK> tq;
-    Tile<E, FROM_WS ? C : C, FROM_WS ? C : DK> tk;  // K rows, or P (FROM_WS)
-    Tile<E, BVO, DK> ts;
-    Tile<E, BVO, C> tu;
-    if constexpr (FROM_WS) {
-      tq.load_block(wQg + (size_t)tile * C * DK);
-      tk.load_block(wP + (size_t)tile * C * C);
-    } else {
-      tq.load_rows(q + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-      tk.load_rows(k + (tok0 * H + h) * DK, (size_t)H * DK, nv);
-      if (threadIdx.x < C) sg[threadIdx.x] = wG[(size_t)tile * C + threadIdx.x];
-    }
-    ts.load_block(wS + ((size_t)tile * DV + v0) * DK);
-    tu.load_block(wU + ((size_t)tile * DV + v0) * C);
+  int item = blockIdx.x;
+  if (item < nitems) LRT_OUT_LOAD(item)
+  for (; item < nitems; item += gridDim.x) {
+    const int tile = item / nvb, v0 = (item % nvb) * BVO;
+    const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
+    const int t0 = n * C, nv = min(C, T - t0);
+    const size_t tok0 = (size_t)b * T + t0;
     tq.store(sQ, LK);
     if constexpr (FROM_WS)
       tk.store(sP, LC);
@@ -392,32 +450,38 @@ __global__ __launch_bounds__(kThreads) void k_out(const E* __restrict__ q, const
       tk.store(sK, LK);
     ts.store(sS, LK);
     tu.store(sU, LC);
-  }
-  __syncthreads();
-  // P = (Q K^T) o Gamma, inclusive lower triangle
-  if constexpr (!FROM_WS) {
-  for (int tt = w; tt < NB * NB; tt += kWaves) {
-    const int ti = tt / NB, tj = tt % NB;
-    f32x4 acc = zero4();
-    if (tj <= ti) mma<DK>(acc, sQ + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
-    const int j = tj * 16 + (l & 15);
+    if (!FROM_WS && threadIdx.x < C) sg[threadIdx.x] = rg;
+    lds_barrier();
+    if (item + (int)gridDim.x < nitems) LRT_OUT_LOAD(item + (int)gridDim.x)
+    // P = (Q K^T) o Gamma, inclusive lower triangle
+    if constexpr (!FROM_WS) {
+      for (int tt = w; tt < NB * NB; tt += kWaves) {
+        const int ti = tt / NB, tj = tt % NB;
+        f32x4 acc = zero4();
+        if (tj <= ti) mma<DK>(acc, sQ + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
+        const int j = tj * 16 + (l & 15);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = ti * 16 + (l >> 4) * 4 + r;
-      sP[i * LC + j] = from_f<E>(j <= i ? acc[r] * __expf(sg[i] - sg[j]) : 0.f);
+        for (int r = 0; r < 4; ++r) {
+          const int i = ti * 16 + (l >> 4) * 4 + r;
+          sP[i * LC + j] = from_f<E>(j <= i ? acc[r] * __expf(sg[i] - sg[j]) : 0.f);
+        }
+      }
+      lds_barrier();
     }
+    for (int tt = w; tt < (BVO / 16) * NB; tt += kWaves) {
+      const int tv = tt / NB, ti = tt % NB;
+      f32x4 acc = zero4();
+      mma<DK>(acc, sS + tv * 16 * LK, LK, sQ + ti * 16 * LK, LK);
+      const int i = ti * 16 + (l & 15);
+      if constexpr (!FROM_WS) acc *= __expf(sg[i]);
+      mma<C>(acc, sU + tv * 16 * LC, LC, sP + ti * 16 * LC, LC);
+      store4<E>(sO + i * LO + tv * 16 + (l >> 4) * 4, acc);
+    }
+    lds_barrier();
+    lds_to_rows<E, C, BVO>(o + (tok0 * H + h) * DV + v0, (size_t)H * DV, sO, LO, nv);
+    lds_barrier();
   }
-  __syncthreads();
-  }
-  for (int tt = w; tt < (BVO / 16) * NB; tt += kWaves) {
-    const int tv = tt / NB, ti = tt % NB;
-    f32x4 acc = zero4();
-    mma<DK>(acc, sS + tv * 16 * LK, LK, sQ + ti * 16 * LK, LK);
-    const int i = ti * 16 + (l & 15);
-    if constexpr (!FROM_WS) acc *= __expf(sg[i]);
-    mma<C>(acc, sU + tv * 16 * LC, LC, sP + ti * 16 * LC, LC);
-    if (i < nv) store4<E>(o + ((tok0 + i) * H + h) * DV + v0 + tv * 16 + (l >> 4) * 4, acc);
-  }
+#undef LRT_OUT_LOAD
 }
 
 }  // namespace lrt

@@ -83,6 +83,7 @@ enum KernelKind {
   kKGrad2,
   kKKdaPrep,
   kKStateCopy,
+  kKFwd,
   kKNumKinds
 };
 // Bracket one launch with the timing hook's events (no-ops unless attached).
@@ -95,6 +96,21 @@ void prof_after(void* stream);
     hipLaunchKernelGGL(kernel, grid, block, 0, (hipStream_t)(stream), __VA_ARGS__); \
     ::lrt::prof_after((void*)(stream));                                        \
   } while (0)
+
+// Waves per workgroup of the serial state passes.
+constexpr int kStateWaves = 8;
+
+// Compute units of the current device (cached per device id).
+int device_cu_count();
+// Grid of a chunk-parallel kernel that walks its tiles persistently: enough
+// workgroups to fill every CU at the occupancy its LDS allows, never more
+// than there are tiles.
+inline int persistent_grid(int tiles, size_t lds_bytes) {
+  int per_cu = lds_bytes ? (int)(160 * 1024 / lds_bytes) : 8;
+  per_cu = per_cu < 1 ? 1 : (per_cu > 8 ? 8 : per_cu);
+  const long g = (long)device_cu_count() * per_cu;
+  return (int)(tiles < g ? tiles : g);
+}
 
 int fwd_scalar_gate(const FwdArgs& a);
 int fwd_kda(const FwdArgs& a);

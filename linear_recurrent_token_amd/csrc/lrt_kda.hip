@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void k_kda_prep(const E* __restrict__ q, 
   }
   if (threadIdx.x < C) sb[threadIdx.x] = threadIdx.x < nv ? beta[(tok0 + threadIdx.x) * H + h] : 0.f;
   for (int idx = threadIdx.x; idx < C * LA; idx += kThreads) sA[idx] = 0.f;
-  __syncthreads();
+  lds_barrier();
   // G: inclusive cumsum over the chunk's tokens, per key dimension
   for (int d = threadIdx.x; d < DK; d += kThreads) {
     float s = 0.f;
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void k_kda_prep(const E* __restrict__ q, 
       sG[t * LG + d] = s;
     }
   }
-  __syncthreads();
+  lds_barrier();
   // Q o e^G [t][d], Ktil^T [d][t] = (k_t o e^(G_C - G_t))^T, chunk decay G_C
   {
     E* qg = wQg + (size_t)tile * C * DK;
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void k_kda_prep(const E* __restrict__ q, 
       }
       sS[row * LK + d] = from_f<E>(x);
     }
-    __syncthreads();
+    lds_barrier();
     // tiles: (kind, column block sj) for kind 0 = A (kk), 1 = P (qk)
     for (int tt = w; tt < 2 * s; tt += kWaves) {
       const int kind = tt / s, sj = tt % s;
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void k_kda_prep(const E* __restrict__ q, 
           pout[(size_t)i * C + j] = from_f<E>(acc[r]);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   // diagonal 16 x 16 blocks, element by element: pairs j <= i of one block
   for (int p = threadIdx.x; p < NB * 136; p += kThreads) {
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void k_kda_prep(const E* __restrict__ q, 
     const int i = idx / C, j = idx % C;
     if ((j >> 4) > (i >> 4) || ((j >> 4) == (i >> 4) && j > i)) pout[idx] = from_f<E>(0.f);
   }
-  __syncthreads();
+  lds_barrier();
   // (b K o e^G)^T -> sXt (over the staging area), (b V)^T -> sYt (over Q)
   E* sXt = sS;
   E* sYt = sQ;
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void k_kda_prep(const E* __restrict__ q, 
     const int i = idx / C, j = idx % C;
     sT[i * LC + j] = from_f<E>(j <= i ? sTf[i * LA + j] : 0.f);
   }
-  __syncthreads();
+  lds_barrier();
   // W^T = X^T Tinv^T (rows d, cols t) -> W[t][d]
   E* wout = wW + (size_t)tile * C * DK;
   for (int tt = w; tt < (DK / 16) * NB; tt += kWaves) {
@@ -219,14 +219,14 @@ int kda_impl(const FwdArgs& a) {
     LRT_LAUNCH(kKKdaPrep, (k_kda_prep<E, C, DK, DV>), dim3(tiles), dim3(kThreads), st, (const E*)a.q,
                (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt,
                ws.GC, (E*)ws.Qg, (E*)ws.P);
-    constexpr int BV = DV < 32 ? DV : 32;
-    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, true, true>), dim3(a.B * a.H * (DV / BV)), dim3(kThreads), st,
+    constexpr int BV = DV < 64 ? DV : 64;  // state columns per workgroup
+    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, true, true, kStateWaves>), dim3(a.B * a.H * (DV / BV)), dim3(64 * kStateWaves), st,
                (const E*)ws.W, (const E*)ws.Up, (const E*)ws.Kt, ws.G, (const float*)ws.GC, a.h0, a.ht,
                (E*)ws.U, (E*)ws.S, N, DV);
     constexpr int BVO = (sizeof(E) == 4 && DV > 64) ? 64 : DV;
-    LRT_LAUNCH(kKOut, (k_out<E, C, DK, BVO, true>), dim3(tiles * (DV / BVO)), dim3(kThreads), st,
+    LRT_LAUNCH(kKOut, (k_out<E, C, DK, BVO, true>), dim3(persistent_grid(tiles * (DV / BVO), out_lds_bytes<E, C, DK, BVO, true>())), dim3(kThreads), st,
                (const E*)a.q, (const E*)a.k, ws.G, (const E*)ws.S, (const E*)ws.U, (const E*)ws.Qg,
-               (const E*)ws.P, (E*)a.o, a.T, a.H, N, DV);
+               (const E*)ws.P, (E*)a.o, a.T, a.H, N, DV, tiles * (DV / BVO));
     return hipGetLastError() == hipSuccess ? 0 : -7;
   }
 }
