@@ -91,10 +91,25 @@ __device__ __forceinline__ bf16x8 frag_k8_outer(const bf16* p, int ld, int k0, i
   const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
 }
-// 4 consecutive k (k0 + 4g ..) of column n0 + lane%16, k-outer bf16 operand.
-__device__ __forceinline__ i16x4 frag_k4_outer(const bf16* p, int ld, int k0, int n0) {
+// A 16-long k range as the 16x16x32 operand: lane groups 0 and 1 carry
+// k0 .. k0 + 15, groups 2 and 3 read the same rows and are zeroed.
+__device__ __forceinline__ bf16x8 frag_k16_outer(const bf16* p, int ld, int k0) {
   const int l = lane_id(), g = l >> 4, j = l & 15;
-  return lds_read_tr(p + (k0 + 4 * g + (j >> 2)) * ld + n0 + 4 * (j & 3));
+  const bf16* src = p + (k0 + 8 * (g & 1) + (j >> 2)) * ld + 4 * (j & 3);
+  const i16x4 lo = lds_read_tr(src);
+  const i16x4 hi = lds_read_tr(src + 4 * ld);
+  const short z = g < 2 ? (short)-1 : (short)0;
+  const short __attribute__((ext_vector_type(8))) v = {(short)(lo[0] & z), (short)(lo[1] & z), (short)(lo[2] & z),
+                                                       (short)(lo[3] & z), (short)(hi[0] & z), (short)(hi[1] & z),
+                                                       (short)(hi[2] & z), (short)(hi[3] & z)};
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ bf16x8 frag_k16_inner(const bf16* p, int ld, int k0) {
+  const int l = lane_id(), g = l >> 4;
+  u32x4 x = *(const u32x4*)(p + (l & 15) * ld + k0 + 8 * (g & 1));
+  const unsigned z = g < 2 ? ~0u : 0u;
+  x &= u32x4{z, z, z, z};
+  return __builtin_bit_cast(bf16x8, x);
 }
 
 template <int K, bool AK = false, bool BK = false>
@@ -114,17 +129,13 @@ __device__ __forceinline__ void mma(f32x4& acc, const bf16* a, int lda, const bf
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
   }
   if constexpr (K % 32 == 16) {
+    // The 16-long tail also runs on the 16x16x32 instruction (half its lanes
+    // zero): a 16x16x16 MFMA accumulating directly onto a 16x16x32 result
+    // gave intermittently wrong sums on gfx950.
     constexpr int k = K - 16;
-    i16x4 fa, fb;
-    if constexpr (AK)
-      fa = frag_k4_outer(a, lda, k, 0);
-    else
-      fa = *(const i16x4*)(a + (l & 15) * lda + k + (l >> 4) * 4);
-    if constexpr (BK)
-      fb = frag_k4_outer(b, ldb, k, 0);
-    else
-      fb = *(const i16x4*)(b + (l & 15) * ldb + k + (l >> 4) * 4);
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa, fb, acc, 0, 0, 0);
+    const bf16x8 fa = AK ? frag_k16_outer(a, lda, k) : frag_k16_inner(a, lda, k);
+    const bf16x8 fb = BK ? frag_k16_outer(b, ldb, k) : frag_k16_inner(b, ldb, k);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
   }
 }
 

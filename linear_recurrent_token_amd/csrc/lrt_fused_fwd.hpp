@@ -39,8 +39,8 @@ struct FusedLds {
   static constexpr size_t TWSZ = DELTA ? mx((size_t)C * LA * 4, (size_t)C * LK * es) : 0;
   static constexpr size_t T = TW + TWSZ;                                // Tinv, Tinv diag(b gamma) (E)
   static constexpr size_t TSZ = DELTA ? 2 * (size_t)C * LC * es : 0;
-  static constexpr size_t O = T + TSZ;                                  // inverse scratch; then o rows
-  static constexpr size_t OSZ = mx(DELTA ? 3 * 256 * 4 : 0, (size_t)C * LB * es);
+  static constexpr size_t O = T + TSZ;                                  // o rows [t][v]
+  static constexpr size_t OSZ = (size_t)C * LB * es;
   static constexpr size_t G = O + OSZ;                                  // g, gamma, b, b gamma, e^(g_C - g)
   static constexpr size_t TOTAL = G + 5 * C * 4;
 };
@@ -70,7 +70,6 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const E* __restrict__ q, const 
   E* sW = (E*)(smem + Lay::TW);
   E* sT = (E*)(smem + Lay::T);
   E* sTw = sT + C * LC;
-  float* sR = (float*)(smem + Lay::O);
   E* sO = (E*)(smem + Lay::O);
   float* sg = (float*)(smem + Lay::G);
   float* sgam = sg + C;
@@ -179,7 +178,7 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const E* __restrict__ q, const 
     lds_barrier();
     if constexpr (DELTA) {
       // ---- S3: T = (I + A)^-1, in E twice: T and T diag(b gamma)
-      unit_lower_inverse<C, NT>(sA, sTf, sR);
+      unit_lower_inverse<C, NT>(sA, sTf);
       for (int idx = threadIdx.x; idx < C * C; idx += NT) {
         const int i = idx / C, j = idx % C;
         const float x = j <= i ? sTf[i * LA + j] : 0.f;

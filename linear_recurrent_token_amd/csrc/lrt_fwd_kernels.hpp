@@ -24,55 +24,101 @@
 
 namespace lrt {
 
+// LDS writes of one wave made visible to the rest of that wave: the wave's
+// LDS operations complete in order, the clobber keeps the compiler from
+// moving reads above the writes.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// One 16 x 16 x 16 fp32 product on the 16x16x4 MFMA, operands read from LDS
+// at any row stride (no alignment assumed): acc += X Y, X[m][k] at
+// x[m * ldx + k], Y[k][n] at y[k * ldy + n].  Step s feeds k = 4s + l/16.
+__device__ __forceinline__ void mma16_f32(f32x4& acc, const float* x, int ldx, const float* y, int ldy) {
+  const int l = lane_id(), g = l >> 4, j = l & 15;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[j * ldx + 4 * s + g], y[(4 * s + g) * ldy + j], acc, 0, 0, 0);
+}
+
+// Store a 16 x 16 accumulator tile (times sc) at d[m * ld + n].
+__device__ __forceinline__ void acc16_store(float* d, int ld, f32x4 acc, float sc) {
+  const int l = lane_id();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[((l >> 4) * 4 + i) * ld + (l & 15)] = sc * acc[i];
+}
+
 // (I + A)^-1 for a strictly lower-triangular C x C matrix A in LDS (fp32,
-// row stride C + 1), written to Tf (same layout; only the lower triangle,
-// diagonal included, is defined).  Stage 1 inverts the 16 x 16 diagonal
-// blocks by forward substitution, one lane per column, right-looking (after
-// x_m is known every later row's partial sum takes its term at once, so the
-// dependent chain is 16 steps, not 120); stage 2 fills block row bi from
-// T[bi][bj] = -T[bi][bi] sum_{m=bj}^{bi-1} A[bi][m] T[m][bj].  R is a
-// 3 * 256-float scratch.  All NT threads must call it after A is visible to
-// them; Tf is visible to all threads on return.
+// row stride C + 1, C in {16, 32, 64}), written to Tf (same layout).  Only
+// the lower triangle of Tf, diagonal included, is defined on return: its
+// strictly upper off-diagonal 16-blocks serve as scratch.
+//   stage 1  the 16 x 16 diagonal blocks by forward substitution, one lane
+//            per column, right-looking (after x_m is known every later row
+//            takes its term, so the dependent chain is 16 steps);
+//   stage 2  doubling to 32 x 32: [[X, 0], [Y, Z]]^-1 has lower-left block
+//            -Z^-1 Y X^-1, two fp32 MFMA products; one wave per 32-block
+//            does stages 1 and 2 without a workgroup barrier;
+//   stage 3  (C = 64) the same doubling to 64 x 64 with 32 x 32 blocks, the
+//            four 16-block outputs of each product on four waves.
+// All NT threads must call it after A is visible to them; Tf is visible to
+// all threads on return.
 template <int C, int NT = kThreads>
-__device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sTf, float* sR) {
+__device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sTf) {
+  static_assert(C == 16 || C == 32 || C == 64, "chunk must be 16, 32 or 64");
+  static_assert(NT >= 256, "the 64 x 64 doubling uses four waves");
   constexpr int NB = C / 16;
   constexpr int LA = C + 1;
-  if (threadIdx.x < 16 * NB) {
-    const int bb = threadIdx.x >> 4, j = threadIdx.x & 15;
-    const float* Ab = sA + (bb * 16) * LA + bb * 16;
-    float x[16];
+  constexpr int NP = NB > 1 ? NB / 2 : 1;  // 32-blocks (one wave each)
+  const int w = wave_id(), l = lane_id();
+  if (w < NP) {
+    // stage 1: diagonal blocks 2w (lanes 0..15) and 2w + 1 (lanes 16..31)
+    const int bb = 2 * w + (l >> 4);
+    if (l < 16 * (NB > 1 ? 2 : 1)) {
+      const int j = l & 15;
+      const float* Ab = sA + (bb * 16) * LA + bb * 16;
+      float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+      for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
 #pragma unroll
-    for (int m = 0; m < 15; ++m)
+      for (int m = 0; m < 15; ++m)
 #pragma unroll
-      for (int r = m + 1; r < 16; ++r) x[r] -= Ab[r * LA + m] * x[m];
+        for (int r = m + 1; r < 16; ++r) x[r] -= Ab[r * LA + m] * x[m];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sTf[(bb * 16 + r) * LA + bb * 16 + j] = x[r];
+      for (int r = 0; r < 16; ++r) sTf[(bb * 16 + r) * LA + bb * 16 + j] = x[r];
+    }
+    if constexpr (NB > 1) {
+      // stage 2: T[2w+1][2w] = -T[2w+1][2w+1] (A[2w+1][2w] T[2w][2w]); the
+      // intermediate sits in the upper block [2w][2w+1]
+      const int b0 = 2 * w * 16, b1 = b0 + 16;
+      wave_lds_sync();
+      f32x4 y = zero4();
+      mma16_f32(y, sA + b1 * LA + b0, LA, sTf + b0 * LA + b0, LA);
+      acc16_store(sTf + b0 * LA + b1, LA, y, 1.f);
+      wave_lds_sync();
+      f32x4 z = zero4();
+      mma16_f32(z, sTf + b1 * LA + b1, LA, sTf + b0 * LA + b1, LA);
+      acc16_store(sTf + b1 * LA + b0, LA, z, -1.f);
+    }
+  }
+  if constexpr (NB == 4) {
+    lds_barrier();
+    // stage 3a: X = A[hi][lo] T[lo] (32 x 32) into the upper rows 0..31,
+    // columns 32..63; wave w makes 16-block (a, b) = (2 + w/2, w%2)
+    if (w < 4) {
+      const int a = 2 + (w >> 1), b = w & 1;
+      f32x4 x = zero4();
+      for (int c = b; c < 2; ++c) mma16_f32(x, sA + a * 16 * LA + c * 16, LA, sTf + c * 16 * LA + b * 16, LA);
+      acc16_store(sTf + (a - 2) * 16 * LA + 32 + b * 16, LA, x, 1.f);
+    }
+    lds_barrier();
+    // stage 3b: T[a][b] = -sum_{c=2..a} T[a][c] X[c][b]
+    if (w < 4) {
+      const int a = 2 + (w >> 1), b = w & 1;
+      f32x4 t = zero4();
+      for (int c = 2; c <= a; ++c)
+        mma16_f32(t, sTf + a * 16 * LA + c * 16, LA, sTf + (c - 2) * 16 * LA + 32 + b * 16, LA);
+      acc16_store(sTf + a * 16 * LA + b * 16, LA, t, -1.f);
+    }
   }
   lds_barrier();
-  // stage 2: block row bi, T[bi][bj] = -T[bi][bi] sum_{m=bj}^{bi-1} A[bi][m] T[m][bj]
-  const bool act = threadIdx.x < 256;
-  const int r = (threadIdx.x >> 4) & 15, c = threadIdx.x & 15;
-  for (int bi = 1; bi < NB; ++bi) {
-    if (act) {
-      for (int bj = 0; bj < bi; ++bj) {
-        float s = 0.f;
-        for (int m = bj * 16; m < bi * 16; ++m) s += sA[(bi * 16 + r) * LA + m] * sTf[m * LA + bj * 16 + c];
-        sR[bj * 256 + r * 16 + c] = s;
-      }
-    }
-    lds_barrier();
-    if (act) {
-      for (int bj = 0; bj < bi; ++bj) {
-        float s = 0.f;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) s += sTf[(bi * 16 + r) * LA + bi * 16 + m] * sR[bj * 256 + m * 16 + c];
-        sTf[(bi * 16 + r) * LA + bj * 16 + c] = -s;
-      }
-    }
-    lds_barrier();
-  }
 }
 
 // LDS of k_prep, with the live ranges overlaid: K rows until K K^T is formed,
@@ -87,8 +133,7 @@ struct PrepLds {
   static constexpr size_t A = K + mx((size_t)C * LK * es, DELTA ? (size_t)C * LA * 4 : 0);
   static constexpr size_t XT = A + (DELTA ? mx((size_t)C * LA * 4, (size_t)C * LC * es) : 0);
   static constexpr size_t YT = XT + (DELTA ? (size_t)(DK > DV ? DK : DV) * LC * es : 0);
-  static constexpr size_t R = YT + (size_t)DV * LC * es;
-  static constexpr size_t G = R + (DELTA ? 3 * 256 * 4 : 0);
+  static constexpr size_t G = YT + (size_t)DV * LC * es;
   static constexpr size_t TOTAL = G + 4 * C * 4;
 };
 
@@ -113,7 +158,6 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ k, cons
   E* sT = (E*)(smem + Lay::A);
   E* sXt = (E*)(smem + Lay::XT);
   E* sYt = (E*)(smem + Lay::YT);
-  float* sR = (float*)(smem + Lay::R);
   float* sg = (float*)(smem + Lay::G);
   float* sgam = sg + C;
   float* sb = sg + 2 * C;
@@ -202,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ k, cons
         }
       }
       lds_barrier();
-      unit_lower_inverse<C>(sA, sTf, sR);  // writes over the dead K rows
+      unit_lower_inverse<C>(sA, sTf);  // writes over the dead K rows
       for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
         const int i = idx / C, j = idx % C;
         const E x = from_f<E>(j <= i ? sTf[i * LA + j] : 0.f);

@@ -39,8 +39,7 @@ struct KdaLds {
   static constexpr size_t A = S + mx((size_t)16 * (NB + 1) * LK * es, (size_t)DK * LC * es);
   static constexpr size_t TF = A + (size_t)C * LA * 4;
   static constexpr size_t T = TF + (size_t)C * LA * 4;
-  static constexpr size_t R = T + (size_t)C * LC * es;
-  static constexpr size_t BB = R + 3 * 256 * 4;
+  static constexpr size_t BB = T + (size_t)C * LC * es;
   static constexpr size_t TOTAL = BB + C * 4;
 };
 
@@ -62,7 +61,6 @@ __global__ __launch_bounds__(kThreads) void k_kda_prep(const E* __restrict__ q, 
   float* sA = (float*)(smem + Lay::A);
   float* sTf = (float*)(smem + Lay::TF);
   E* sT = (E*)(smem + Lay::T);
-  float* sR = (float*)(smem + Lay::R);
   float* sb = (float*)(smem + Lay::BB);
 
   const int tile = blockIdx.x;
@@ -183,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void k_kda_prep(const E* __restrict__ q, 
   }
   tv.scale_rows(sb);
   tv.store_T(sYt, LC);
-  unit_lower_inverse<C>(sA, sTf, sR);
+  unit_lower_inverse<C>(sA, sTf);
   for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
     const int i = idx / C, j = idx % C;
     sT[i * LC + j] = from_f<E>(j <= i ? sTf[i * LA + j] : 0.f);
