@@ -30,7 +30,8 @@
  * are rounded to nearest even.  log_a must be finite (normally <= 0).
  *
  * Supported: B, H >= 1; T >= 0; d_k, d_v in {16, 32, 64, 128};
- * chunk in {16, 32, 64}.  T need not be a multiple of chunk.  The fp32
+ * chunk in {16, 32, 64}; B * T and B * H * ceil(T / chunk) * d_v / 16 at
+ * most 2^31 - 1.  T need not be a multiple of chunk.  The fp32
  * backward (gdn_bwd with LRT_F32) is limited to d_k, d_v <= 64 and
  * chunk <= 32 (LRT_ERR_SHAPE / LRT_ERR_CHUNK otherwise).
  *

@@ -174,3 +174,28 @@ def test_kda_uniform_gate_matches_gdn_kernel():
     torch.cuda.synchronize()
     assert rel(ok.float().cpu(), og.float().cpu()) <= 1e-2
     assert rel(hk.cpu(), hg.cpu()) <= 1e-2
+
+
+def test_kda_long_context_workload():
+    """KDA at B=1, H=16, T=2^20, d=128, chunk 64 (16,384 chunks per head, the
+    state carried across all of them), rank-16 gate.  The whole forward runs on
+    the GPU; the oracle checks the last 8 value columns of o and ht (columns of
+    the state never mix, so the sample is exact for those columns)."""
+    L = lrt()
+    name = "kda_bf16_1m"
+    say(f"[fwd] workload {name}")
+    c = synth.CONFIGS[name]
+    inp = synth.config_inputs(name, device="cuda")
+    q, k, v, la, beta = (inp[n] for n in ("q", "k", "v", "log_a", "beta"))
+    o, ht = L.kda_fwd(q, k, v, la, beta, None, chunk=c["chunk"])
+    torch.cuda.synchronize()
+    c0, nc = c["dv"] - 8, 8
+    o_s = o[..., c0:c0 + nc].float().cpu().numpy()
+    ht_s = ht[..., c0:c0 + nc].cpu().numpy()
+    del o, ht
+    say("  gpu done; oracle on 8 columns")
+    ro, rh = oracle.fwd("kda", q.cpu(), k.cpu(), v.cpu(), la.cpu(), beta.cpu(), None, cols=(c0, nc))
+    assert np.all(np.isfinite(o_s)) and np.all(np.isfinite(ht_s))
+    eo, eh = rel(o_s, ro), rel(ht_s, rh)
+    say(f"  rel err o={eo:.2e} ht={eh:.2e}")
+    assert eo <= TOL[c["dtype"]] and eh <= TOL[c["dtype"]], (eo, eh)
