@@ -29,12 +29,21 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 MFMA_FP32_PEAK_TFLOPS = 157.3
-WORKLOAD = "gdn_train_bf16_2k"
+WORKLOAD = "gdn_train_bf16_2k"  # the headline workload (default)
+# other named workloads bench.py can time (forward passes; not the headline)
+WORKLOADS = {
+    "gdn_train_bf16_2k": ("GDN chunked fwd+bwd tokens/s and % bf16 MFMA peak, B=16 T=2048 H=8 d=128",
+                          "gdn_fwd + gdn_bwd"),
+    "gdn_bf16_2k": ("GDN chunked fwd tokens/s, B=16 T=2048 H=8 d=128", "gdn_fwd"),
+    "ssd_bf16_2k": ("SSD (Mamba2 case) chunked fwd tokens/s, B=16 T=2048 H=8 d=128", "ssd_fwd"),
+    "kda_bf16_1m": ("KDA chunked fwd tokens/s, B=1 T=2^20 H=16 d=128", "kda_fwd"),
+}
 
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--workload", default=WORKLOAD, choices=sorted(WORKLOADS))
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--sets", type=int, default=3, help="independent input sets rotated over the steps")
@@ -79,7 +88,7 @@ class Hip:
             self.lib.hipEventDestroy(e)
 
 
-def kernel_model(name, c, esz=2):
+def kernel_model(name, c, esz=2, op="gdn_fwd + gdn_bwd"):
     """Algorithmic (bytes, flops) of one launch of a library kernel on workload c.
 
     Bytes: each tensor the kernel must read or write, counted once per
@@ -111,6 +120,16 @@ def kernel_model(name, c, esz=2):
         "k_grad2": ((dk + dv) * e + 8 + C * e + dk * e + dv * e + dk * e + 4 + (dk + dv) * e + 8, 0,
                     2 * C * dk + 2 * C * dv + 2 * C * dk + 2 * C * dv + 4 * C * C + 2 * C * dk + 4 * C * dk),
     }
+    if op == "kda_fwd":
+        per.update({
+            # reads q, k, v, per-dim log_a, beta; writes W, U'^T, Ktil^T, chunk decay, Q o e^G, P
+            "k_kda_prep": ((2 * dk + dv) * e + dk * 4 + 4 + (2 * dk + dv) * e + dk * 4 / C + dk * e + C * e, 0,
+                           2 * C * dk + 2 * C * dk + 2 * C * dk + 2 * C * dv),
+            # reads W, U'^T, Ktil^T, chunk decay; writes U^T and the chunk-start states, ht
+            "k_state": ((2 * dk + dv) * e + dk * 4 / C + dv * e + dk * dv * e / C, st, 4 * dk * dv),
+            # reads Q o e^G, P, states, U; writes o
+            "k_out": (dk * e + C * e + dk * dv * e / C + dv * e + dv * e, 0, 2 * C * dv + 2 * dk * dv),
+        })
     if name not in per:
         return None
     b_th, b_bh, f_th = per[name]
@@ -158,10 +177,10 @@ def copy_probe(torch, dev, nbytes=1 << 30):
     del src, dst
 
 
-def make_sets(L, synth, torch, c, nsets):
+def make_sets(L, synth, torch, wl, nsets):
     sets = []
     for s in range(nsets):
-        inp = synth.config_inputs(WORKLOAD, device="cuda", seed=s)
+        inp = synth.config_inputs(wl, device="cuda", seed=s)
         sets.append(inp)
     return sets
 
@@ -178,29 +197,45 @@ def main():
     from linear_recurrent_token_amd import synth
 
     L.lib()
-    c = dict(synth.CONFIGS[WORKLOAD])
+    wl = args.workload
+    metric, op = WORKLOADS[wl]
+    c = dict(synth.CONFIGS[wl])
     B, T, H, dk, dv, C = c["B"], c["T"], c["H"], c["dk"], c["dv"], c["chunk"]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    sets = make_sets(L, synth, torch, c, args.sets)
+    # input sets larger than the last-level cache need no rotation
+    nsets = args.sets if B * T * H * (2 * dk + dv) * 2 < (1 << 30) else 1
+    sets = make_sets(L, synth, torch, wl, nsets)
     code = L.LRT_BF16
+    opc = {"gdn_fwd + gdn_bwd": L.OP_GDN_BWD, "gdn_fwd": L.OP_GDN_FWD, "ssd_fwd": L.OP_SSD_FWD,
+           "kda_fwd": L.OP_KDA_FWD}[op]
     ws_bytes = max(L.workspace_bytes(L.OP_GDN_FWD, B, T, H, dk, dv, C, code),
-                   L.workspace_bytes(L.OP_GDN_BWD, B, T, H, dk, dv, C, code))
+                   L.workspace_bytes(opc, B, T, H, dk, dv, C, code))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
     ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    grads = (torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
-             torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
-             torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev),
-             torch.empty((B, T, H), dtype=torch.float32, device=dev),
-             torch.empty((B, T, H), dtype=torch.float32, device=dev),
-             torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev))
+    grads = None
+    if op == "gdn_fwd + gdn_bwd":
+        grads = (torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
+                 torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
+                 torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev),
+                 torch.empty((B, T, H), dtype=torch.float32, device=dev),
+                 torch.empty((B, T, H), dtype=torch.float32, device=dev),
+                 torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev))
 
     def step(i):
         s = sets[i % len(sets)]
-        L.gdn_fwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s["h0"], chunk=C, o=o, ht=ht, workspace=ws)
-        L.gdn_bwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s["h0"], s["do"], s.get("dht"), chunk=C,
-                  workspace=ws, out=grads)
+        if op == "ssd_fwd":
+            L.ssd_fwd(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), chunk=C, o=o, ht=ht, workspace=ws)
+        elif op == "kda_fwd":
+            L.kda_fwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), chunk=C, o=o, ht=ht,
+                      workspace=ws)
+        else:
+            L.gdn_fwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), chunk=C, o=o, ht=ht,
+                      workspace=ws)
+        if grads is not None:
+            L.gdn_bwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), s["do"], s.get("dht"),
+                      chunk=C, workspace=ws, out=grads)
 
     hip = Hip()
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -242,7 +277,7 @@ def main():
     kernels = {n: {"launches": len(d), "avg_us": 1e3 * sum(d) / len(d), "total_us_per_step": 1e3 * sum(d) / args.steps}
                for n, d in dur.items()}
     dom = max(kernels, key=lambda n: kernels[n]["total_us_per_step"])
-    model = kernel_model(dom, c)
+    model = kernel_model(dom, c, op=op)
     roof = None
     if model is not None:
         # every launch of a kernel in a step carries the same work
@@ -251,7 +286,7 @@ def main():
         ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
         common = {"kernel": dom, "algorithmic_bytes": int(per_launch_bytes),
                   "algorithmic_flops": int(per_launch_flops), "avg_us": round(kernels[dom]["avg_us"], 2),
-                  "traffic": counted_traffic(dom)}
+                  "traffic": counted_traffic(dom) if wl == WORKLOAD else None}
         if per_launch_flops / per_launch_bytes < ridge:
             ach = per_launch_bytes / avg_s / 1e9
             roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -261,22 +296,23 @@ def main():
             roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), **common}
     for n, k in kernels.items():
-        m = kernel_model(n, c)
+        m = kernel_model(n, c, op=op)
         if m is not None:
             k["gbs_algorithmic"] = m[0] / (k["avg_us"] / 1e6) / 1e9
             k["tflops_algorithmic"] = m[1] / (k["avg_us"] / 1e6) / 1e12
 
-    # algorithmic step totals: GEMM flops of the method (forward + backward)
-    flops_fwd = (2 * C * (3 * dk + 2 * dv) + 6 * dk * dv) * B * T * H
-    flops_bwd = (12 * C * dk + 8 * C * dv + 12 * dk * dv + 4 * C * C) * B * T * H
-    step_tflops = (flops_fwd + flops_bwd) / (ms_per_step / 1e3) / 1e12
+    # algorithmic step totals: GEMM flops of the method (forward, + backward)
+    per_th = {"ssd_fwd": 2 * C * (dk + dv) + 4 * dk * dv}.get(op, 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv)
+    if grads is not None:
+        per_th += 12 * C * dk + 8 * C * dv + 12 * dk * dv + 4 * C * C
+    step_tflops = per_th * B * T * H / (ms_per_step / 1e3) / 1e12
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wl == WORKLOAD:
         cpu = cpu_baseline(sets[0], C, args.cpu_seconds)
 
     line = {
-        "metric": "GDN chunked fwd+bwd tokens/s and % bf16 MFMA peak, B=16 T=2048 H=8 d=128",
+        "metric": metric,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -287,9 +323,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded normal inputs; 3 rotating input sets resident in HBM)",
-        "config": {"workload": WORKLOAD, "B": B, "T": T, "H": H, "d_k": dk, "d_v": dv, "chunk": C,
-                   "op": "gdn_fwd + gdn_bwd"},
+        "data": f"synthetic (seeded normal inputs; {nsets} rotating input set(s) resident in HBM)",
+        "config": {"workload": wl, "B": B, "T": T, "H": H, "d_k": dk, "d_v": dv, "chunk": C, "op": op},
         "step_tflops": round(step_tflops, 2),
         "mfma_frac_of_bf16_peak": round(step_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "wall_s_timed": round(wall, 4),

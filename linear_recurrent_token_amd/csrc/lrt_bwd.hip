@@ -318,17 +318,18 @@ struct Grad1Lds {
   static constexpr size_t TOTAL = DOT + 16;
 };
 
-template <typename E, int C, int DK, int DV>
-__global__ __launch_bounds__(kThreads) void k_grad1(const E* __restrict__ q, const E* __restrict__ k,
+template <typename E, int C, int DK, int DV, int NW = 8>
+__global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, const E* __restrict__ k,
                                                     const E* __restrict__ d_o, const float* __restrict__ wG,
                                                     const E* __restrict__ wS, const E* __restrict__ wdS,
                                                     const E* __restrict__ wU, const E* __restrict__ wdU,
                                                     E* __restrict__ dq, E* __restrict__ wdW, E* __restrict__ wdK1,
                                                     float* __restrict__ wdg1, int T, int H, int N, int ntiles) {
   typedef Grad1Lds<E, C, DK, DV> Lay;
+  constexpr int NT = 64 * NW;
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, NB = C / 16;
   constexpr int V = 16 / (int)sizeof(E);
-  constexpr int NKT = (DK / 16) * NB, KPW = (NKT + kWaves - 1) / kWaves;
+  constexpr int NKT = (DK / 16) * NB, KPW = (NKT + NW - 1) / NW;
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
   E* sQ = (E*)(smem + Lay::Q);
   E* sK = (E*)(smem + Lay::K);
@@ -343,10 +344,10 @@ __global__ __launch_bounds__(kThreads) void k_grad1(const E* __restrict__ q, con
   float* sdot = (float*)(smem + Lay::DOT);
   const int w = wave_id(), l = lane_id();
 
-  Tile<E, C, DK> tq, tk;
-  Tile<E, C, DV> to;
-  Tile<E, DV, C> tu, tdu;
-  Tile<E, DV, DK> tS, tdS;
+  Tile<E, C, DK, NT> tq, tk;
+  Tile<E, C, DV, NT> to;
+  Tile<E, DV, C, NT> tu, tdu;
+  Tile<E, DV, DK, NT> tS, tdS;
   float rg = 0.f;
 #define LRT_G1_LOAD(tile_)                                                                \
   {                                                                                       \
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void k_grad1(const E* __restrict__ q, con
     if (tile + (int)gridDim.x < ntiles) LRT_G1_LOAD(tile + (int)gridDim.x)
 
     // dS = (dO U^T) o Gamma (inclusive); E = dS o (Q K^T) -> dg rows +, cols -
-    for (int tt = w; tt < NB * NB; tt += kWaves) {
+    for (int tt = w; tt < NB * NB; tt += NW) {
       const int ti = tt / NB, tj = tt % NB;
       const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
       f32x4 ds = zero4();
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void k_grad1(const E* __restrict__ q, con
     f32x4 dqa[KPW];
 #pragma unroll
     for (int s = 0; s < KPW; ++s) {
-      const int tt = w + kWaves * s;
+      const int tt = w + NW * s;
       dqa[s] = zero4();
       if (tt < NKT) {
         const int td = tt / NB, ti = tt % NB;
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void k_grad1(const E* __restrict__ q, con
       float part = 0.f;
 #pragma unroll
       for (int s2 = 0; s2 < tS.PT; ++s2) {
-        if (threadIdx.x + kThreads * s2 < tS.NP) {
+        if (threadIdx.x + NT * s2 < tS.NP) {
           E a[V], d[V];
           __builtin_memcpy(a, &tS.x[s2], 16);
           __builtin_memcpy(d, &tdS.x[s2], 16);
@@ -459,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void k_grad1(const E* __restrict__ q, con
     // dq rows over the dead dO; dH'^T over the dead S
 #pragma unroll
     for (int s = 0; s < KPW; ++s) {
-      const int tt = w + kWaves * s;
+      const int tt = w + NW * s;
       if (tt < NKT) {
         const int td = tt / NB, ti = tt % NB;
         store4<E>(sdQ + (ti * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, dqa[s]);
@@ -467,12 +468,12 @@ __global__ __launch_bounds__(kThreads) void k_grad1(const E* __restrict__ q, con
     }
     tdS.store(sS, LK);
     lds_barrier();
-    lds_to_rows<E, C, DK>(dq + (tok0 * H + h) * DK, (size_t)H * DK, sdQ, LK, nv);
+    lds_to_rows<E, C, DK, NT>(dq + (tok0 * H + h) * DK, (size_t)H * DK, sdQ, LK, nv);
     // dK1^T = e^(g_C - g_j) (dH' U^T) + Q^T dS   (rows d, cols j)
     const float gC = sg[C - 1];
 #pragma unroll
     for (int s = 0; s < KPW; ++s) {
-      const int tt = w + kWaves * s;
+      const int tt = w + NW * s;
       if (tt < NKT) {
         const int td = tt / NB, tj = tt % NB;
         const int j = tj * 16 + (l & 15), d0 = td * 16 + (l >> 4) * 4;
@@ -524,8 +525,8 @@ struct Grad2Lds {
   static constexpr size_t TOTAL = CX + C * 4;
 };
 
-template <typename E, int C, int DK, int DV>
-__global__ __launch_bounds__(kThreads) void k_grad2(const E* __restrict__ k, const E* __restrict__ v,
+template <typename E, int C, int DK, int DV, int NW = 8>
+__global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, const E* __restrict__ v,
                                                     const float* __restrict__ beta, const float* __restrict__ wG,
                                                     const E* __restrict__ wT, const E* __restrict__ wdW,
                                                     const E* __restrict__ wdU, const E* __restrict__ wdK1,
@@ -533,8 +534,9 @@ __global__ __launch_bounds__(kThreads) void k_grad2(const E* __restrict__ k, con
                                                     E* __restrict__ dv, float* __restrict__ dlog_a,
                                                     float* __restrict__ dbeta, int T, int H, int N, int ntiles) {
   typedef Grad2Lds<E, C, DK, DV> Lay;
+  constexpr int NT = 64 * NW;
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, NB = C / 16;
-  constexpr int NKT = (DK / 16) * NB, KPW = (NKT + kWaves - 1) / kWaves;
+  constexpr int NKT = (DK / 16) * NB, KPW = (NKT + NW - 1) / NW;
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
   E* sK = (E*)(smem + Lay::K);
   E* sV = (E*)(smem + Lay::VV);
@@ -553,10 +555,10 @@ __global__ __launch_bounds__(kThreads) void k_grad2(const E* __restrict__ k, con
   float* scx = (float*)(smem + Lay::CX);
   const int w = wave_id(), l = lane_id();
 
-  Tile<E, C, DK> tk;
-  Tile<E, C, DV> tv;
-  Tile<E, C, C> tt;
-  Tile<E, DV, C> tdu;
+  Tile<E, C, DK, NT> tk;
+  Tile<E, C, DV, NT> tv;
+  Tile<E, C, C, NT> tt;
+  Tile<E, DV, C, NT> tdu;
   f32x4 rk1[KPW];  // the first part of dK, accumulator layout (rows d, cols j)
   float rg = 0.f, rb = 0.f, rd = 0.f;
 #define LRT_G2_LOAD(tile_)                                                                        \
@@ -570,7 +572,7 @@ __global__ __launch_bounds__(kThreads) void k_grad2(const E* __restrict__ k, con
     tt.load_block(wT + (size_t)(tile_) * C * C);                                                  \
     tdu.load_block(wdU + (size_t)(tile_) * DV * C);                                               \
     _Pragma("unroll") for (int s = 0; s < KPW; ++s) {                                             \
-      const int kt_ = w + kWaves * s;                                                             \
+      const int kt_ = w + NW * s;                                                             \
       if (kt_ < NKT) rk1[s] = load4<E>(wdK1 + (size_t)(tile_) * C * DK + ((size_t)kt_ * 64 + l) * 4); \
     }                                                                                             \
     if (threadIdx.x < C) {                                                                        \
@@ -590,7 +592,7 @@ __global__ __launch_bounds__(kThreads) void k_grad2(const E* __restrict__ k, con
     tv.store(sV, LV);
     tt.store(sT, LC);
     tdu.store(sdUt, LC);
-    acc_tiles_to_lds<E, DK / 16, NB>(sdW, LK, wdW + (size_t)tile * C * DK);
+    acc_tiles_to_lds<E, DK / 16, NB, NT>(sdW, LK, wdW + (size_t)tile * C * DK);
     if (threadIdx.x < C) {
       const int t = threadIdx.x;
       sg[t] = rg;
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(kThreads) void k_grad2(const E* __restrict__ k, con
     // dX^T = dW^T Tinv (rows d, cols j): dK += b gamma dX, cx_j = dX_j . k_j
 #pragma unroll
     for (int s = 0; s < KPW; ++s) {
-      const int kt = w + kWaves * s;
+      const int kt = w + NW * s;
       if (kt < NKT) {
         const int td = kt / NB, tj = kt % NB;
         const int j = tj * 16 + (l & 15), d0 = td * 16 + (l >> 4) * 4;
@@ -622,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void k_grad2(const E* __restrict__ k, con
       }
     }
     // dY^T = dU^T Tinv (rows v, cols j): dV = b dY (rows staged), dbeta += dY_j . v_j
-    for (int tt2 = w; tt2 < (DV / 16) * NB; tt2 += kWaves) {
+    for (int tt2 = w; tt2 < (DV / 16) * NB; tt2 += NW) {
       const int tvv = tt2 / NB, tj = tt2 % NB;
       const int j = tj * 16 + (l & 15), v0 = tvv * 16 + (l >> 4) * 4;
       f32x4 acc = zero4();
@@ -635,10 +637,10 @@ __global__ __launch_bounds__(kThreads) void k_grad2(const E* __restrict__ k, con
       if (l < 16) atomicAdd(&sdb[j], e);
     }
     lds_barrier();
-    lds_to_rows<E, C, DV>(dv + (tok0 * H + h) * DV, (size_t)H * DV, sdV, LV, nv);
+    lds_to_rows<E, C, DV, NT>(dv + (tok0 * H + h) * DV, (size_t)H * DV, sdV, LV, nv);
     lds_barrier();
     // dT = (dW K^T) diag(b gamma) + (dU V^T) diag(b)   (rows i, cols j) -> dT^T [j][i]
-    for (int t2 = w; t2 < NB * NB; t2 += kWaves) {
+    for (int t2 = w; t2 < NB * NB; t2 += NW) {
       const int ti = t2 / NB, tj = t2 % NB;
       const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
       f32x4 z1 = zero4(), z2 = zero4();
@@ -648,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void k_grad2(const E* __restrict__ k, con
     }
     lds_barrier();
     // R = dT Tinv^T (rows i, cols k) -> R^T [k][i]
-    for (int t2 = w; t2 < NB * NB; t2 += kWaves) {
+    for (int t2 = w; t2 < NB * NB; t2 += NW) {
       const int ti = t2 / NB, tk2 = t2 % NB;
       f32x4 acc = zero4();
       mma<C, true, false>(acc, sdTt + ti * 16, LC, sT + tk2 * 16 * LC, LC);
@@ -657,7 +659,7 @@ __global__ __launch_bounds__(kThreads) void k_grad2(const E* __restrict__ k, con
     lds_barrier();
     // dA = -strict_lower(Tinv^T R); with A = b_i (K K^T) o Gamma:
     //   M = dA o b_i Gamma -> M^T [k][i], dbeta_i += sum_k dA o Gamma o KK^T, E = dA o A -> dg
-    for (int t2 = w; t2 < NB * NB; t2 += kWaves) {
+    for (int t2 = w; t2 < NB * NB; t2 += NW) {
       const int ti = t2 / NB, tk2 = t2 % NB;
       const int kk = tk2 * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
       f32x4 m = zero4();
@@ -691,7 +693,7 @@ __global__ __launch_bounds__(kThreads) void k_grad2(const E* __restrict__ k, con
     // dK^T += K^T M (cols j: sum_i k_i M_ij) + K^T M^T (cols i: sum_j k_j M_ij)
 #pragma unroll
     for (int s = 0; s < KPW; ++s) {
-      const int kt = w + kWaves * s;
+      const int kt = w + NW * s;
       if (kt < NKT) {
         const int td = kt / NB, tj = kt % NB;
         mma<C, true, false>(dka[s], sK + td * 16, LK, sMt + tj * 16 * LC, LC);
@@ -715,7 +717,7 @@ __global__ __launch_bounds__(kThreads) void k_grad2(const E* __restrict__ k, con
       }
     }
     lds_barrier();
-    lds_to_rows<E, C, DK>(dk + (tok0 * H + h) * DK, (size_t)H * DK, sdK, LK, nv);
+    lds_to_rows<E, C, DK, NT>(dk + (tok0 * H + h) * DK, (size_t)H * DK, sdK, LK, nv);
     lds_barrier();
   }
 #undef LRT_G2_LOAD
@@ -749,10 +751,10 @@ int bwd_impl(const BwdArgs& a) {
     LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves>), dim3(sgrid), dim3(64 * kStateWaves), st, (const E*)a.q,
                        (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.W, (const E*)dUl, a.dht, a.dh0,
                        (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
-    LRT_LAUNCH(kKGrad1, (k_grad1<E, C, DK, DV>), dim3(persistent_grid(tiles, Grad1Lds<E, C, DK, DV>::TOTAL)), dim3(kThreads), st, (const E*)a.q,
+    LRT_LAUNCH(kKGrad1, (k_grad1<E, C, DK, DV, kGradWaves>), dim3(persistent_grid(tiles, Grad1Lds<E, C, DK, DV>::TOTAL)), dim3(64 * kGradWaves), st, (const E*)a.q,
                        (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.S, (const E*)ws.dS,
                        (const E*)ws.f.U, (const E*)ws.dU, (E*)a.dq, (E*)ws.dW, (E*)ws.dK1, ws.dg1, a.T, a.H, N, tiles);
-    LRT_LAUNCH(kKGrad2, (k_grad2<E, C, DK, DV>), dim3(persistent_grid(tiles, Grad2Lds<E, C, DK, DV>::TOTAL)), dim3(kThreads), st, (const E*)a.k,
+    LRT_LAUNCH(kKGrad2, (k_grad2<E, C, DK, DV, kGradWaves>), dim3(persistent_grid(tiles, Grad2Lds<E, C, DK, DV>::TOTAL)), dim3(64 * kGradWaves), st, (const E*)a.k,
                        (const E*)a.v, a.beta, ws.f.G, (const E*)ws.T, (const E*)ws.dW, (const E*)ws.dU, (const E*)ws.dK1,
                        ws.dg1, (E*)a.dk_out, (E*)a.dv_out, a.dlog_a, a.dbeta, a.T, a.H, N, tiles);
     return hipGetLastError() == hipSuccess ? 0 : -7;

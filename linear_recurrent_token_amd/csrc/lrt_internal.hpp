@@ -99,6 +99,8 @@ void prof_after(void* stream);
 
 // Waves per workgroup of the serial state passes.
 constexpr int kStateWaves = 8;
+// Waves per workgroup of the chunk-parallel gradient kernels.
+constexpr int kGradWaves = 8;
 
 // Compute units of the current device (cached per device id).
 int device_cu_count();
