@@ -104,6 +104,15 @@ def kernel_model(name, c, esz=2, op="gdn_fwd + gdn_bwd"):
         # whole forward: reads q, k, v, log_a, beta, h0; writes o, ht
         "k_fwd": ((2 * dk + dv) * e + 8 + dv * e, 2 * st,
                   2 * C * (3 * dk + 2 * dv) + 6 * dk * dv),
+        # WY pass of the forward: reads q, k, v, log_a, beta; writes W, U'^T, g, P
+        "k_wy": ((2 * dk + dv) * e + 8 + (dk + dv) * e + 4 + C * e, 0,
+                 2 * C * dk + 2 * C * dk + 2 * C * dk + 2 * C * dv),
+        # serial scan of the forward: reads q, k, W, U'^T, g, P, h0; writes o, ht
+        "k_scan": (2 * dk * e + (dk + dv) * e + 4 + C * e + dv * e, 2 * st, 6 * dk * dv + 2 * C * dv),
+        # WY pass of the backward recompute: reads k, v, log_a, beta; writes W, U'^T, g, Tinv
+        "k_wy_bwd": ((dk + dv) * e + 8 + (dk + dv) * e + 4 + C * e, 0, 2 * C * dk + 2 * C * dk + 2 * C * dv),
+        # scan of the backward recompute: reads k, W, U'^T, g, h0; writes U^T and the chunk-start states
+        "k_scan_bwd": (2 * dk * e + dv * e + 4 + dv * e + dk * dv * e / C, st, 4 * dk * dv),
         # reads k, v, log_a, beta; writes W, U'^T, Ktil^T, g, Tinv
         "k_prep": ((dk + dv) * e + 8 + (2 * dk + dv) * e + 4 + C * e, 0,
                    2 * C * dk + 2 * C * dk + 2 * C * dv),

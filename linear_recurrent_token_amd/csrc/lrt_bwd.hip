@@ -26,6 +26,7 @@
 //   k_grad2      per chunk: the WY part of dK, dV, dbeta, dg -> dlog_a
 #include "lrt_fwd_kernels.hpp"
 #include "lrt_internal.hpp"
+#include "lrt_scan.hpp"
 
 namespace lrt {
 
@@ -739,12 +740,14 @@ int bwd_impl(const BwdArgs& a) {
     hipStream_t st = (hipStream_t)a.stream;
     constexpr int BV = DV < 64 ? DV : 64;  // state columns per workgroup
     const int sgrid = a.B * a.H * (DV / BV);
-    LRT_LAUNCH(kKPrep, (k_prep<E, C, DK, DV, true, true>), dim3(persistent_grid(tiles, PrepLds<E, C, DK, DV, true>::TOTAL)), dim3(kThreads), st, (const E*)a.k,
-                       (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.f.W, (E*)ws.f.Up, (E*)ws.f.Kt,
-                       ws.f.G, (E*)ws.T);
-    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, true, false, kStateWaves>), dim3(sgrid), dim3(64 * kStateWaves), st, (const E*)ws.f.W,
-                       (const E*)ws.f.Up, (const E*)ws.f.Kt, ws.f.G, (const float*)nullptr, a.h0, (float*)nullptr, (E*)ws.f.U,
-                       (E*)ws.f.S, N, DV);
+    // recompute: WY factors with T, then the chunk-start states and U
+    LRT_LAUNCH(kKWyBwd, (k_wy<E, C, DK, DV, false, true, kWyWaves>),
+               dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), st, (const E*)nullptr,
+               (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.f.W, (E*)ws.f.Up, ws.f.G,
+               (E*)nullptr, (E*)ws.T);
+    LRT_LAUNCH(kKScanBwd, (k_scan<E, C, DK, BV, false, kStateWaves>), dim3(sgrid), dim3(64 * kStateWaves), st,
+               (const E*)nullptr, (const E*)a.k, (const E*)ws.f.W, (const E*)ws.f.Up, (const float*)ws.f.G,
+               (const E*)nullptr, a.h0, (float*)nullptr, (E*)nullptr, (E*)ws.f.U, (E*)ws.f.S, a.T, a.H, N, DV);
     E* dUl = (E*)ws.f.Up;
     LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV>), dim3(persistent_grid(tiles, LocalLds<E, C, DK, DV>::TOTAL)), dim3(kThreads), st,
                (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N, tiles);

@@ -1,14 +1,37 @@
 // lrt_fwd.hip -- launchers of the chunkwise forward (gdn_fwd, ssd_fwd).
 #include "lrt_fused_fwd.hpp"
+#include "lrt_scan.hpp"
 #include "lrt_fwd_kernels.hpp"
 #include "lrt_internal.hpp"
 
 namespace lrt {
 
+// The GDN forward as the WY pass + serial scan (the backward's recompute
+// path) instead of the single fused kernel.
+constexpr bool kFwdSplit = false;
+
 // --------------------------------------------------------------- launchers
 template <typename E, int C, int DK, int DV>
 int fwd_impl(const FwdArgs& a) {
   constexpr int BVF = DV < 64 ? DV : 64;
+  if constexpr (WyLds<E, C, DK, DV>::TOTAL <= 160 * 1024 && ScanLds<E, C, DK, BVF, true>::TOTAL <= 160 * 1024) {
+    if (kFwdSplit && a.variant == kVarGDN) {
+      // chunk-parallel WY pass, then the serial scan
+      const int N = (a.T + C - 1) / C;
+      const int tiles = a.B * a.H * N;
+      const FwdWs ws = fwd_ws_layout(a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
+      hipStream_t st = (hipStream_t)a.stream;
+      LRT_LAUNCH(kKWy, (k_wy<E, C, DK, DV, true, false, kWyWaves>),
+                 dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), st,
+                 (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.W,
+                 (E*)ws.Up, ws.G, (E*)ws.P, (E*)nullptr);
+      LRT_LAUNCH(kKScan, (k_scan<E, C, DK, BVF, true, kStateWaves>), dim3(a.B * a.H * (DV / BVF)),
+                 dim3(64 * kStateWaves), st, (const E*)a.q, (const E*)a.k, (const E*)ws.W, (const E*)ws.Up,
+                 (const float*)ws.G, (const E*)ws.P, a.h0, a.ht, (E*)a.o, (E*)nullptr, (E*)nullptr, a.T, a.H, N,
+                 DV);
+      return hipGetLastError() == hipSuccess ? 0 : -7;
+    }
+  }
   if constexpr (FusedLds<E, C, DK, BVF, true>::TOTAL <= 160 * 1024) {
     // the whole forward in one kernel: state on chip, inputs read once
     const int N = (a.T + C - 1) / C;

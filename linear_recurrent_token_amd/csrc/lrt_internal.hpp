@@ -41,7 +41,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 //   G   [C]       f32 within-chunk inclusive cumsum of log a
 //   GC  [dk]      f32 per-key-dim chunk log-decay (KDA)
 //   Qg  [C][dk]   E   Q o e^G (KDA)
-//   P   [C][C]    E   intra-chunk attention matrix (KDA)
+//   P   [C][C]    E   intra-chunk attention matrix (Q K^T) o Gamma
 struct FwdWs {
   void *W, *Up, *Kt, *U, *S, *Qg, *P;
   float *G, *GC;
@@ -67,7 +67,7 @@ inline FwdWs fwd_ws_layout(int B, int T, int H, int dk, int dv, int C, size_t es
   w.G = (float*)take(tiles * C * sizeof(float));
   w.GC = kda ? (float*)take(tiles * dk * sizeof(float)) : nullptr;
   w.Qg = kda ? take(tiles * C * dk * esz) : nullptr;
-  w.P = kda ? take(tiles * C * C * esz) : nullptr;
+  w.P = take(tiles * C * C * esz);
   w.bytes = off;
   return w;
 }
@@ -84,6 +84,10 @@ enum KernelKind {
   kKKdaPrep,
   kKStateCopy,
   kKFwd,
+  kKWy,
+  kKScan,
+  kKWyBwd,
+  kKScanBwd,
   kKNumKinds
 };
 // Bracket one launch with the timing hook's events (no-ops unless attached).
@@ -101,6 +105,8 @@ void prof_after(void* stream);
 constexpr int kStateWaves = 8;
 // Waves per workgroup of the chunk-parallel gradient kernels.
 constexpr int kGradWaves = 8;
+// Waves per workgroup of the chunk-parallel WY pass.
+constexpr int kWyWaves = 8;
 
 // Compute units of the current device (cached per device id).
 int device_cu_count();
