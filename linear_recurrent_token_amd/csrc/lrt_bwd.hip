@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q,
     tq.load_rows(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
     tk.load_rows(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
     to.load_rows(d_o + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                        \
-    if (threadIdx.x < C) rg = wG[(size_t)(tile_) * C + threadIdx.x];                      \
+    rg = wG[(size_t)(tile_) * C + min((int)threadIdx.x, C - 1)];                          \
   }
 
   int tile = blockIdx.x;
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
 
   Tile<E, C, DK, NT> tQ, tK, tW;
   Tile<E, C, BV, NT> tO;
-  f32x4 rU[UPW];
+  typename Vec4<E>::T rU[UPW];  // packed: unpacked where used, so the fetch does not wait
   float rg = 0.f;
 #define LRT_DSTATE_FETCH(n_)                                                                        \
   {                                                                                                 \
@@ -209,12 +209,11 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
     tW.load_block(wW + ft * C * DK);                                                                \
     tO.load_rows(d_o + (ftok * H + h) * DV + v0, (size_t)H * DV, fnv);                              \
     _Pragma("unroll") for (int s = 0; s < UPW; ++s) {                                               \
-      const int tt = w + NW * s;                                                                    \
-      if (tt < NU)                                                                                  \
-        rU[s] = load4<E>(wdUl + ft * DV * C + (size_t)(v0 + (tt % NTV) * 16 + (l & 15)) * C +      \
-                         (tt / NTV) * 16 + (l >> 4) * 4);                                           \
+      const int tt = min(w + NW * s, NU - 1);                                                       \
+      rU[s] = load4_raw<E>(wdUl + ft * DV * C + (size_t)(v0 + (tt % NTV) * 16 + (l & 15)) * C +    \
+                           (tt / NTV) * 16 + (l >> 4) * 4);                                         \
     }                                                                                               \
-    rg = threadIdx.x < C ? wG[ft * C + threadIdx.x] : 0.f;                                          \
+    rg = wG[ft * C + min((int)threadIdx.x, C - 1)];                                                 \
   }
 
   LRT_DSTATE_FETCH(N - 1)
@@ -242,7 +241,7 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
     tW.store(sW, LK);
     f32x4 du[UPW];
 #pragma unroll
-    for (int s = 0; s < UPW; ++s) du[s] = rU[s];
+    for (int s = 0; s < UPW; ++s) du[s] = Vec4<E>::unpack(rU[s]);
     lds_barrier();
     lds_to_block<E, BV, DK, NT>(wdS + (tile * DV + v0) * DK, sdS, LK);
     tK.scale_rows(sgs);
@@ -361,7 +360,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
     to.load_rows(d_o + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                        \
     tu.load_block(wU + (size_t)(tile_) * DV * C);                                         \
     tdu.load_block(wdU + (size_t)(tile_) * DV * C);                                       \
-    if (threadIdx.x < C) rg = wG[(size_t)(tile_) * C + threadIdx.x];                      \
+    rg = wG[(size_t)(tile_) * C + min((int)threadIdx.x, C - 1)];                          \
   }
 
   int tile = blockIdx.x;
@@ -560,7 +559,8 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
   Tile<E, C, DV, NT> tv;
   Tile<E, C, C, NT> tt;
   Tile<E, DV, C, NT> tdu;
-  f32x4 rk1[KPW];  // the first part of dK, accumulator layout (rows d, cols j)
+  AccTiles<E, DK / 16, NB, NT> tdw;  // dW in accumulator-tile order
+  typename Vec4<E>::T rk1[KPW];  // the first part of dK, accumulator layout (rows d, cols j), packed
   float rg = 0.f, rb = 0.f, rd = 0.f;
 #define LRT_G2_LOAD(tile_)                                                                        \
   {                                                                                               \
@@ -572,14 +572,16 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
     tv.load_rows(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                                  \
     tt.load_block(wT + (size_t)(tile_) * C * C);                                                  \
     tdu.load_block(wdU + (size_t)(tile_) * DV * C);                                               \
+    tdw.load(wdW + (size_t)(tile_) * C * DK);                                                     \
     _Pragma("unroll") for (int s = 0; s < KPW; ++s) {                                             \
       const int kt_ = w + NW * s;                                                             \
-      if (kt_ < NKT) rk1[s] = load4<E>(wdK1 + (size_t)(tile_) * C * DK + ((size_t)kt_ * 64 + l) * 4); \
+      rk1[s] = load4_raw<E>(wdK1 + (size_t)(tile_) * C * DK + ((size_t)min(kt_, NKT - 1) * 64 + l) * 4); \
     }                                                                                             \
-    if (threadIdx.x < C) {                                                                        \
-      rg = wG[(size_t)(tile_) * C + threadIdx.x];                                                 \
-      rb = (int)threadIdx.x < lnv ? beta[(ltok + threadIdx.x) * H + lh] : 0.f;                    \
-      rd = wdg1[(size_t)(tile_) * C + threadIdx.x];                                               \
+    {                                                                                             \
+      const int tc = min((int)threadIdx.x, C - 1);                                                \
+      rg = wG[(size_t)(tile_) * C + tc];                                                          \
+      rb = beta[(ltok + min(tc, lnv - 1)) * H + lh];                                              \
+      rd = wdg1[(size_t)(tile_) * C + tc];                                                        \
     }                                                                                             \
   }
 
@@ -593,18 +595,18 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
     tv.store(sV, LV);
     tt.store(sT, LC);
     tdu.store(sdUt, LC);
-    acc_tiles_to_lds<E, DK / 16, NB, NT>(sdW, LK, wdW + (size_t)tile * C * DK);
+    tdw.store(sdW, LK);
     if (threadIdx.x < C) {
       const int t = threadIdx.x;
       sg[t] = rg;
-      sb[t] = rb;
+      sb[t] = t < nv ? rb : 0.f;
       sdg[t] = rd;
       sdb[t] = 0.f;
       scx[t] = 0.f;
     }
     f32x4 dka[KPW];
 #pragma unroll
-    for (int s = 0; s < KPW; ++s) dka[s] = rk1[s];
+    for (int s = 0; s < KPW; ++s) dka[s] = Vec4<E>::unpack(rk1[s]);
     lds_barrier();
     if (tile + (int)gridDim.x < ntiles) LRT_G2_LOAD(tile + (int)gridDim.x)
     // dX^T = dW^T Tinv (rows d, cols j): dK += b gamma dX, cx_j = dX_j . k_j

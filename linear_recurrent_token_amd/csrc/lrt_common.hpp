@@ -20,6 +20,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // 16 raw bytes in four VGPRs (a native vector, so register arrays of it stay in
 // registers; HIP's uint4 is a class type)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -176,16 +177,16 @@ template <typename E>
 struct Vec4;
 template <>
 struct Vec4<float> {
-  typedef float4 T;
-  static __device__ __forceinline__ T pack(f32x4 x) { return make_float4(x[0], x[1], x[2], x[3]); }
-  static __device__ __forceinline__ f32x4 unpack(T x) { return f32x4{x.x, x.y, x.z, x.w}; }
+  typedef f32x4 T;
+  static __device__ __forceinline__ T pack(f32x4 x) { return x; }
+  static __device__ __forceinline__ f32x4 unpack(T x) { return x; }
 };
 template <>
 struct Vec4<bf16> {
-  typedef uint2 T;
+  typedef u32x2 T;
   static __device__ __forceinline__ T pack(f32x4 x) {
     bf16 b0 = (bf16)x[0], b1 = (bf16)x[1], b2 = (bf16)x[2], b3 = (bf16)x[3];
-    uint2 r;
+    u32x2 r;
     r.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
     r.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
     return r;
@@ -203,6 +204,12 @@ __device__ __forceinline__ void store4(E* p, f32x4 x) {
 template <typename E>
 __device__ __forceinline__ f32x4 load4(const E* p) {
   return Vec4<E>::unpack(*(const typename Vec4<E>::T*)p);
+}
+// The packed bits only: a prefetch that is unpacked where it is used does not
+// make the load wait at the point of issue.
+template <typename E>
+__device__ __forceinline__ typename Vec4<E>::T load4_raw(const E* p) {
+  return *(const typename Vec4<E>::T*)p;
 }
 
 // Scatter the 16 bytes x (elements c0.. of row r of a row-major source) into
@@ -308,26 +315,38 @@ __device__ __forceinline__ void lds_to_block(E* g, const E* lds, int ls) {
 // Accumulator-tile order: a matrix produced as 16x16 accumulator tiles of its
 // transpose (tile (ta, tb) holds X^T rows 16ta.., cols 16tb..) is written
 // lane-major -- each lane's 4 values at ((tile * 64 + lane) * 4) -- so one
-// wave writes 64 contiguous 4-element pieces.  acc_tiles_to_lds rebuilds X
+// wave writes 64 contiguous 4-element pieces.  AccTiles rebuilds X
 // row-major in LDS, X[16tb + l%16][16ta + 4(l/16) + r] = value r of lane l.
 template <typename E>
 __device__ __forceinline__ void acc_tile_store(E* base, int tile_id, f32x4 acc) {
   store4<E>(base + ((size_t)tile_id * 64 + lane_id()) * 4, acc);
 }
+// load() issues the global loads into registers (packed, so nothing waits
+// for them), store() writes X into LDS.
 template <typename E, int NTA, int NTB, int NT = kThreads>
-__device__ __forceinline__ void acc_tiles_to_lds(E* lds, int ld, const E* g) {
-  constexpr int NS = NTA * NTB * 64;  // 4-element slots
+struct AccTiles {
+  static constexpr int NS = NTA * NTB * 64;
+  static constexpr int PT = (NS + NT - 1) / NT;
+  typename Vec4<E>::T x[PT];
+  __device__ __forceinline__ void load(const E* g) {
 #pragma unroll
-  for (int s = 0; s < (NS + NT - 1) / NT; ++s) {
-    const int p = threadIdx.x + NT * s;
-    if (p < NS) {
-      const int tile = p >> 6, ln = p & 63;
-      const int ta = tile / NTB, tb = tile % NTB;
-      const f32x4 x = load4<E>(g + (size_t)p * 4);
-      store4<E>(lds + (tb * 16 + (ln & 15)) * ld + ta * 16 + (ln >> 4) * 4, x);
+    for (int s = 0; s < PT; ++s) {
+      const int p = min((int)threadIdx.x + NT * s, NS - 1);
+      x[s] = load4_raw<E>(g + (size_t)p * 4);
     }
   }
-}
+  __device__ __forceinline__ void store(E* lds, int ld) const {
+#pragma unroll
+    for (int s = 0; s < PT; ++s) {
+      const int p = threadIdx.x + NT * s;
+      if (NS % NT == 0 || p < NS) {
+        const int tile = p >> 6, ln = p & 63;
+        const int ta = tile / NTB, tb = tile % NTB;
+        *(typename Vec4<E>::T*)(lds + (tb * 16 + (ln & 15)) * ld + ta * 16 + (ln >> 4) * 4) = x[s];
+      }
+    }
+  }
+};
 
 // Copy R rows of W elements from LDS (row stride ls) to global rows (row
 // stride gs), 16 bytes per access; rows >= nvalid are not written.

@@ -8,7 +8,7 @@ namespace lrt {
 
 // The GDN forward as the WY pass + serial scan (the backward's recompute
 // path) instead of the single fused kernel.
-constexpr bool kFwdSplit = false;
+constexpr bool kFwdSplit = true;
 
 // --------------------------------------------------------------- launchers
 template <typename E, int C, int DK, int DV>

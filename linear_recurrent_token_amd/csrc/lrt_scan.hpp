@@ -79,26 +79,28 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
     tk.load_rows(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
     if (WRITE_P) tq.load_rows(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);             \
     tv.load_rows(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                          \
-    la = 0.f;                                                                             \
-    bt = 0.f;                                                                             \
-    if ((int)threadIdx.x < lnv) {                                                         \
-      la = log_a[(ltok + threadIdx.x) * H + lh];                                          \
-      bt = beta[(ltok + threadIdx.x) * H + lh];                                           \
+    {                                                                                     \
+      const int tc = min((int)threadIdx.x, lnv - 1); /* masked where used */              \
+      la = log_a[(ltok + tc) * H + lh];                                                   \
+      bt = beta[(ltok + tc) * H + lh];                                                    \
     }                                                                                     \
   }
 
   int tile = blockIdx.x;
   if (tile < ntiles) LRT_WY_LOAD(tile)
   for (; tile < ntiles; tile += gridDim.x) {
+    const int nv = min(C, T - (tile % N) * C);
     if (threadIdx.x < 64) {
-      const float g = wave_incl_scan(la);
+      const bool valid = (int)threadIdx.x < nv;
+      const float g = wave_incl_scan(valid ? la : 0.f);
       if (threadIdx.x < C) {
         const int t = threadIdx.x;
         const float gam = __expf(g);
+        const float b_ = valid ? bt : 0.f;
         sg[t] = g;
         sgam[t] = gam;
-        sb[t] = bt;
-        sbg[t] = bt * gam;
+        sb[t] = b_;
+        sbg[t] = b_ * gam;
         wG[(size_t)tile * C + t] = g;
       }
     }
@@ -236,44 +238,46 @@ __global__ __launch_bounds__(64 * NW) void k_scan(const E* __restrict__ q, const
     }
   }
 
-  Tile<E, C, DK, NT> tW, tK, tQ;
-  Tile<E, C, C, NT> tP;
-  f32x4 rUp[UPW];
-  float rg = 0.f;
-#define LRT_SCAN_FETCH(n_)                                                                          \
-  {                                                                                                 \
-    const size_t ft = (size_t)bh * N + (n_);                                                        \
-    const int fnv = min(C, T - (n_) * C);                                                           \
-    const size_t ftok = (size_t)b * T + (size_t)(n_) * C;                                           \
-    tW.load_block(wW + ft * C * DK);                                                                \
-    tK.load_rows(k + (ftok * H + h) * DK, (size_t)H * DK, fnv);                                     \
-    if (FWD) {                                                                                      \
-      tQ.load_rows(q + (ftok * H + h) * DK, (size_t)H * DK, fnv);                                   \
-      tP.load_block(wP + ft * C * C);                                                               \
-    }                                                                                               \
-    _Pragma("unroll") for (int s = 0; s < UPW; ++s) {                                               \
-      const int tt = w + NW * s;                                                                    \
-      if (tt < NU)                                                                                  \
-        rUp[s] = load4<E>(wUp + (ft * DV + v0 + (tt % NTV) * 16 + (l & 15)) * C + (tt / NTV) * 16 + \
-                          (l >> 4) * 4);                                                            \
-    }                                                                                               \
-    if (threadIdx.x < C) rg = wG[ft * C + threadIdx.x];                                             \
-  }
+  // One chunk's operands in registers.  Two sets alternate, so the loads of
+  // chunk n + 2 are in flight while chunk n computes.
+  struct Ops {
+    Tile<E, C, DK, NT> W, K, Q;
+    Tile<E, C, C, NT> P;
+    typename Vec4<E>::T up[UPW];
+    float g;
+  };
+  auto fetch = [&](Ops& x, int n_) {
+    const size_t ft = (size_t)bh * N + n_;
+    const int fnv = min(C, T - n_ * C);
+    const size_t ftok = (size_t)b * T + (size_t)n_ * C;
+    x.W.load_block(wW + ft * C * DK);
+    x.K.load_rows(k + (ftok * H + h) * DK, (size_t)H * DK, fnv);
+    if constexpr (FWD) {
+      x.Q.load_rows(q + (ftok * H + h) * DK, (size_t)H * DK, fnv);
+      x.P.load_block(wP + ft * C * C);
+    }
+    // unconditional loads (clamped indices), so nothing waits for them here
+#pragma unroll
+    for (int s = 0; s < UPW; ++s) {
+      const int tt = min(w + NW * s, NU - 1);
+      x.up[s] = load4_raw<E>(wUp + (ft * DV + v0 + (tt % NTV) * 16 + (l & 15)) * C + (tt / NTV) * 16 + (l >> 4) * 4);
+    }
+    x.g = wG[ft * C + min((int)threadIdx.x, C - 1)];
+  };
 
-  LRT_SCAN_FETCH(0)
   size_t otok = 0;  // first token of the chunk whose o rows wait in sO
   int onv = 0;
-  for (int n = 0; n < N; ++n) {
+  auto step = [&](Ops& x, int n) {
     const size_t tile = (size_t)bh * N + n;
     const int nv = min(C, T - n * C);
     const size_t tok0 = (size_t)b * T + (size_t)n * C;
     // ---- this chunk's operands and start state into LDS
     if (threadIdx.x < 64) {
-      const float gC = __shfl(rg, C - 1, 64);
+      const float gC = __shfl(x.g, C - 1, 64);
       if (threadIdx.x < C) {
-        sg[threadIdx.x] = rg;
-        sgam[threadIdx.x] = __expf(rg);
-        skt[threadIdx.x] = __expf(gC - rg);
+        sg[threadIdx.x] = x.g;
+        sgam[threadIdx.x] = __expf(x.g);
+        skt[threadIdx.x] = __expf(gC - x.g);
       }
     }
 #pragma unroll
@@ -284,16 +288,16 @@ __global__ __launch_bounds__(64 * NW) void k_scan(const E* __restrict__ q, const
         store4<E>(sS + (tv * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, hacc[s]);
       }
     }
-    tW.store(sW, LK);
-    tK.store(sK, LK);
+    x.W.store(sW, LK);
+    x.K.store(sK, LK);
     if constexpr (FWD) {
-      tQ.store(sQ, LK);
-      tP.store(sP, LC);
+      x.Q.store(sQ, LK);
+      x.P.store(sP, LC);
     }
     f32x4 up[UPW];
 #pragma unroll
-    for (int s = 0; s < UPW; ++s) up[s] = rUp[s];
-    if (n + 1 < N) LRT_SCAN_FETCH(n + 1)
+    for (int s = 0; s < UPW; ++s) up[s] = Vec4<E>::unpack(x.up[s]);
+    if (n + 2 < N) fetch(x, n + 2);
     lds_barrier();
     if constexpr (FWD) {
       // o rows of the previous chunk (staged in sO by its last step)
@@ -342,8 +346,15 @@ __global__ __launch_bounds__(64 * NW) void k_scan(const E* __restrict__ q, const
       }
     }
     lds_barrier();
+  };
+
+  Ops x0, x1;
+  fetch(x0, 0);
+  if (N > 1) fetch(x1, 1);
+  for (int n = 0; n < N; n += 2) {
+    step(x0, n);
+    if (n + 1 < N) step(x1, n + 1);
   }
-#undef LRT_SCAN_FETCH
   if constexpr (FWD) {
     if (N > 0) lds_to_rows<E, C, BV, NT>(o + (otok * H + h) * DV + v0, (size_t)H * DV, sO, LB, onv);
   }
