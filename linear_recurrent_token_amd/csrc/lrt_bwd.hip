@@ -747,9 +747,25 @@ int bwd_impl(const BwdArgs& a) {
                dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), st, (const E*)nullptr,
                (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.f.W, (E*)ws.f.Up, ws.f.G,
                (E*)nullptr, (E*)ws.T);
-    LRT_LAUNCH(kKScanBwd, (k_scan<E, C, DK, BV, false, kStateWaves>), dim3(sgrid), dim3(64 * kStateWaves), st,
-               (const E*)nullptr, (const E*)a.k, (const E*)ws.f.W, (const E*)ws.f.Up, (const float*)ws.f.G,
-               (const E*)nullptr, a.h0, (float*)nullptr, (E*)nullptr, (E*)ws.f.U, (E*)ws.f.S, a.T, a.H, N, DV);
+    {
+      ScanArgs<E> sa{};
+      sa.k = (const E*)a.k;
+      sa.W = (const E*)ws.f.W;
+      sa.Up = (const E*)ws.f.Up;
+      sa.G = ws.f.G;
+      sa.hin = a.h0;
+      sa.hs_ld = DV;
+      sa.U = (E*)ws.f.U;
+      sa.S = (E*)ws.f.S;
+      sa.T = a.T;
+      sa.H = a.H;
+      sa.N = N;
+      sa.L = N;
+      sa.nseg = 1;
+      sa.DV = DV;
+      LRT_LAUNCH(kKScanBwd, (k_scan<E, C, DK, BV, kScanBwd, false, kStateWaves>), dim3(sgrid),
+                 dim3(64 * kStateWaves), st, sa);
+    }
     E* dUl = (E*)ws.f.Up;
     LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV>), dim3(persistent_grid(tiles, LocalLds<E, C, DK, DV>::TOTAL)), dim3(kThreads), st,
                (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N, tiles);

@@ -14,7 +14,7 @@ constexpr bool kFwdSplit = true;
 template <typename E, int C, int DK, int DV>
 int fwd_impl(const FwdArgs& a) {
   constexpr int BVF = DV < 64 ? DV : 64;
-  if constexpr (WyLds<E, C, DK, DV>::TOTAL <= 160 * 1024 && ScanLds<E, C, DK, BVF, true>::TOTAL <= 160 * 1024) {
+  if constexpr (WyLds<E, C, DK, DV>::TOTAL <= 160 * 1024 && ScanLds<E, C, DK, BVF, kScanFwd, false>::TOTAL <= 160 * 1024) {
     if (kFwdSplit && a.variant == kVarGDN) {
       // chunk-parallel WY pass, then the serial scan
       const int N = (a.T + C - 1) / C;
@@ -25,11 +25,8 @@ int fwd_impl(const FwdArgs& a) {
                  dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), st,
                  (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.W,
                  (E*)ws.Up, ws.G, (E*)ws.P, (E*)nullptr);
-      LRT_LAUNCH(kKScan, (k_scan<E, C, DK, BVF, true, kStateWaves>), dim3(a.B * a.H * (DV / BVF)),
-                 dim3(64 * kStateWaves), st, (const E*)a.q, (const E*)a.k, (const E*)ws.W, (const E*)ws.Up,
-                 (const float*)ws.G, (const E*)ws.P, a.h0, a.ht, (E*)a.o, (E*)nullptr, (E*)nullptr, a.T, a.H, N,
-                 DV);
-      return hipGetLastError() == hipSuccess ? 0 : -7;
+      if (hipGetLastError() != hipSuccess) return -7;
+      return launch_scan_fwd<E, C, DK, DV, false>(a, ws, N);
     }
   }
   if constexpr (FusedLds<E, C, DK, BVF, true>::TOTAL <= 160 * 1024) {

@@ -42,11 +42,27 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 //   GC  [dk]      f32 per-key-dim chunk log-decay (KDA)
 //   Qg  [C][dk]   E   Q o e^G (KDA)
 //   P   [C][C]    E   intra-chunk attention matrix (Q K^T) o Gamma
+//   SegLoc   [b*h][seg][dk][dv+dk] f32  end state of each segment from zero, and its map
+//   SegStart [b*h][seg][dk][dv]    f32  true start state of each segment
 struct FwdWs {
   void *W, *Up, *Kt, *U, *S, *Qg, *P;
-  float *G, *GC;
+  float *G, *GC, *SegLoc, *SegStart;
   size_t bytes;
 };
+
+// Segments per sequence of the forward scan: one unless the (b, h, column
+// block) workgroups alone would leave the device mostly idle; then enough for
+// about 512 workgroups, each segment at least 16 chunks long (and d_k a
+// multiple of the column block, for the identity columns of the local pass).  Depends on the
+// shape only, so the workspace size does not depend on the device.
+inline int scan_segments(int B, int H, int DK, int DV, int N) {
+  const int BV = DV < 64 ? DV : 64;
+  const long wgs = (long)B * H * (DV / BV);
+  if (wgs >= 256 || N < 32 || DK % BV != 0) return 1;
+  long ns = (512 + wgs - 1) / wgs;
+  if (ns > N / 16) ns = N / 16;
+  return ns < 1 ? 1 : (int)ns;
+}
 
 inline FwdWs fwd_ws_layout(int B, int T, int H, int dk, int dv, int C, size_t esz, void* base, bool kda = false) {
   const size_t N = (size_t)(T + C - 1) / C;
@@ -68,6 +84,9 @@ inline FwdWs fwd_ws_layout(int B, int T, int H, int dk, int dv, int C, size_t es
   w.GC = kda ? (float*)take(tiles * dk * sizeof(float)) : nullptr;
   w.Qg = kda ? take(tiles * C * dk * esz) : nullptr;
   w.P = take(tiles * C * C * esz);
+  const int nseg = scan_segments(B, H, dk, dv, (int)N);
+  w.SegLoc = nseg > 1 ? (float*)take((size_t)B * H * nseg * dk * (dv + dk) * sizeof(float)) : nullptr;
+  w.SegStart = nseg > 1 ? (float*)take((size_t)B * H * nseg * dk * dv * sizeof(float)) : nullptr;
   w.bytes = off;
   return w;
 }
@@ -88,6 +107,8 @@ enum KernelKind {
   kKScan,
   kKWyBwd,
   kKScanBwd,
+  kKScanLocal,
+  kKCarry,
   kKNumKinds
 };
 // Bracket one launch with the timing hook's events (no-ops unless attached).

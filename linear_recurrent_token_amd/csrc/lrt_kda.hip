@@ -23,6 +23,7 @@
 // and output kernel (operands from the workspace) then finish the chunk.
 #include "lrt_fwd_kernels.hpp"
 #include "lrt_internal.hpp"
+#include "lrt_scan.hpp"
 
 namespace lrt {
 
@@ -395,15 +396,8 @@ int kda_impl(const FwdArgs& a) {
                dim3(persistent_grid(tiles, KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL)), dim3(64 * kWyWaves), st,
                (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.W,
                (E*)ws.Up, (E*)ws.Kt, ws.GC, (E*)ws.Qg, (E*)ws.P);
-    constexpr int BV = DV < 64 ? DV : 64;  // state columns per workgroup
-    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, true, true, kStateWaves>), dim3(a.B * a.H * (DV / BV)), dim3(64 * kStateWaves), st,
-               (const E*)ws.W, (const E*)ws.Up, (const E*)ws.Kt, ws.G, (const float*)ws.GC, a.h0, a.ht,
-               (E*)ws.U, (E*)ws.S, N, DV);
-    constexpr int BVO = (sizeof(E) == 4 && DV > 64) ? 64 : DV;
-    LRT_LAUNCH(kKOut, (k_out<E, C, DK, BVO, true>), dim3(persistent_grid(tiles * (DV / BVO), out_lds_bytes<E, C, DK, BVO, true>())), dim3(kThreads), st,
-               (const E*)a.q, (const E*)a.k, ws.G, (const E*)ws.S, (const E*)ws.U, (const E*)ws.Qg,
-               (const E*)ws.P, (E*)a.o, a.T, a.H, N, DV, tiles * (DV / BVO));
-    return hipGetLastError() == hipSuccess ? 0 : -7;
+    if (hipGetLastError() != hipSuccess) return -7;
+    return launch_scan_fwd<E, C, DK, DV, true>(a, ws, N);
   }
 }
 

@@ -23,6 +23,7 @@
 //        registers while this one computes.
 #pragma once
 #include "lrt_fwd_kernels.hpp"
+#include "lrt_internal.hpp"
 
 namespace lrt {
 
@@ -173,32 +174,60 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
 }
 
 // ----------------------------------------------------------------- k_scan
-template <typename E, int C, int DK, int BV, bool FWD>
+// Modes: forward (writes o), backward recompute (writes the chunk-start
+// states S_n and U), or local (writes only the end state of its segment).
+enum ScanMode { kScanFwd = 0, kScanBwd = 1, kScanLocal = 2 };
+
+// Operands of k_scan.  Per-tile workspace arrays are chunk-major per (b, h).
+// States (hin / hout) are fp32 [b*h][segment][d_k][hs_ld].
+template <typename E>
+struct ScanArgs {
+  const E* q;       // q rows (GDN forward)
+  const E* k;       // k rows (GDN)
+  const E* W;       // W rows [C][d_k]
+  const E* Up;      // U'^T [d_v][C]
+  const E* P;       // P rows [C][C] (forward)
+  const E* Qg;      // (Q o e^G) rows [C][d_k] (KDA forward)
+  const E* Kt;      // Ktil^T [d_k][C] (KDA)
+  const float* G;   // g [C] (GDN)
+  const float* GC;  // per-dim chunk log-decay [d_k] (KDA)
+  const float* hin; // start state of each segment, or nullptr = zero
+  float* hout;      // end state of each segment, or nullptr
+  E* o;             // forward output
+  E* U;             // U^T [d_v][C] (backward recompute)
+  E* S;             // chunk-start states [d_v][d_k] (backward recompute)
+  int hs_ld;        // columns of a state row in hin / hout
+  int T, H, N;      // tokens, heads, chunks per sequence
+  int L, nseg;      // chunks per segment, segments per sequence
+  int DV;           // value columns (local mode appends d_k identity columns)
+};
+
+template <typename E, int C, int DK, int BV, int MODE, bool KDA>
 struct ScanLds {
   static constexpr int P = lds_pad<E>();
   static constexpr int LK = DK + P, LB = BV + P, LC = C + P;
   static constexpr size_t es = sizeof(E);
-  static constexpr size_t W = 0;                                     // W rows [t][d]
-  static constexpr size_t K = W + (size_t)C * LK * es;               // k rows [t][d]
-  static constexpr size_t S = K + (size_t)C * LK * es;               // Hn^T [v][d]
-  static constexpr size_t U = S + (size_t)BV * LK * es;              // U^T, (e^(g_C - g) U)^T [v][t]
-  static constexpr size_t Q = U + 2 * (size_t)BV * LC * es;          // q rows [t][d]
-  static constexpr size_t P_ = Q + (FWD ? (size_t)C * LK * es : 0);  // P [i][j]
-  static constexpr size_t O = P_ + (FWD ? (size_t)C * LC * es : 0);  // o rows [t][v]
-  static constexpr size_t G = O + (FWD ? (size_t)C * LB * es : 0);   // g, gamma, e^(g_C - g)
+  static constexpr bool FWD = MODE == kScanFwd;
+  static constexpr size_t W = 0;                                                  // W rows [t][d]
+  static constexpr size_t K = W + (size_t)C * LK * es;                            // k rows [t][d] / Ktil^T [d][t]
+  static constexpr size_t S = K + (KDA ? (size_t)DK * LC : (size_t)C * LK) * es;  // Hn^T [v][d]
+  static constexpr size_t U = S + (size_t)BV * LK * es;                           // U^T (, (e^(g_C - g) U)^T) [v][t]
+  static constexpr size_t Q = U + (KDA ? 1 : 2) * (size_t)BV * LC * es;           // q / Q o e^G rows [t][d]
+  static constexpr size_t P_ = Q + (FWD ? (size_t)C * LK * es : 0);               // P [i][j]
+  static constexpr size_t O = P_ + (FWD ? (size_t)C * LC * es : 0);               // o rows [t][v]
+  static constexpr size_t G = O + (FWD ? (size_t)C * LB * es : 0);                // g, gamma, e^(g_C - g)
   static constexpr size_t TOTAL = G + 3 * C * 4;
 };
 
-// FWD: writes o and ht.  Backward recompute (!FWD): writes S_n [d_v][d_k]
-// and U^T [d_v][C] per tile (chunk-major per (b, h)).
-template <typename E, int C, int DK, int BV, bool FWD, int NW = 8>
-__global__ __launch_bounds__(64 * NW) void k_scan(const E* __restrict__ q, const E* __restrict__ k,
-                                                  const E* __restrict__ wW, const E* __restrict__ wUp,
-                                                  const float* __restrict__ wG, const E* __restrict__ wP,
-                                                  const float* h0, float* ht, E* __restrict__ o,
-                                                  E* __restrict__ wU, E* __restrict__ wS, int T, int H, int N,
-                                                  int DV) {
-  typedef ScanLds<E, C, DK, BV, FWD> Lay;
+// One workgroup per (b, h, block of BV columns, segment) walks its chunks in
+// order, the state block in MFMA accumulators.  Local mode runs each segment
+// from a zero state and also carries d_k identity columns with U' = 0, so
+// its end state holds both the segment's own contribution E and its
+// transition M (the state map is affine: H_end = M H_start + E).
+template <typename E, int C, int DK, int BV, int MODE, bool KDA, int NW = 8>
+__global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
+  typedef ScanLds<E, C, DK, BV, MODE, KDA> Lay;
+  constexpr bool FWD = MODE == kScanFwd;
   constexpr int NT = 64 * NW;
   constexpr int LK = Lay::LK, LB = Lay::LB, LC = Lay::LC;
   constexpr int NB = C / 16, NTV = BV / 16;
@@ -207,7 +236,7 @@ __global__ __launch_bounds__(64 * NW) void k_scan(const E* __restrict__ q, const
   constexpr int NO = NTV * NB;                                   // O^T tiles (rows v, cols t)
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
   E* sW = (E*)(smem + Lay::W);
-  E* sK = (E*)(smem + Lay::K);
+  E* sK = (E*)(smem + Lay::K);  // GDN: k rows; KDA: Ktil^T
   E* sS = (E*)(smem + Lay::S);
   E* sU = (E*)(smem + Lay::U);
   E* sUk = sU + BV * LC;
@@ -218,12 +247,228 @@ __global__ __launch_bounds__(64 * NW) void k_scan(const E* __restrict__ q, const
   float* sgam = sg + C;
   float* skt = sg + 2 * C;
 
-  const int nvb = DV / BV;
-  const int wg = xcd_group(blockIdx.x, gridDim.x);  // the column blocks of one (b, h) share an L2
-  const int vb = wg % nvb, bh = wg / nvb;
+  const int DVX = MODE == kScanLocal ? a.DV + DK : a.DV;
+  const int nvb = DVX / BV;
+  const int wg = xcd_group(blockIdx.x, gridDim.x);  // column blocks of one (b, h) share an L2
+  const int seg = wg % a.nseg, vb = (wg / a.nseg) % nvb, bh = wg / a.nseg / nvb;
+  const int T = a.T, H = a.H, N = a.N, DV = a.DV;
   const int h = bh % H, b = bh / H;
   const int v0 = vb * BV;
+  const bool ident = MODE == kScanLocal && v0 >= DV;  // identity columns (U' = 0)
+  const int n0 = seg * a.L, n1 = min(N, n0 + a.L);
   const int w = wave_id(), l = lane_id();
+  const size_t st0 = ((size_t)bh * a.nseg + seg) * DK;  // first state row of this segment
+
+  f32x4 hacc[HPW];
+#pragma unroll
+  for (int s = 0; s < HPW; ++s) {
+    const int tt = w + NW * s;
+    hacc[s] = zero4();
+    if (tt < NH) {
+      const int td = tt / NTV, tv = tt % NTV;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = td * 16 + (l >> 4) * 4 + r, c = v0 + tv * 16 + (l & 15);
+        if (ident)
+          hacc[s][r] = (d == c - DV) ? 1.f : 0.f;
+        else if (a.hin != nullptr && MODE != kScanLocal)
+          hacc[s][r] = a.hin[(st0 + d) * a.hs_ld + c];
+      }
+    }
+  }
+
+  // One chunk's operands in registers; two sets alternate, so the loads of
+  // chunk n + 2 are in flight while chunk n computes.
+  struct Ops {
+    Tile<E, C, DK, NT> W, Q;
+    Tile<E, KDA ? DK : C, KDA ? C : DK, NT> K;
+    Tile<E, C, C, NT> P;
+    typename Vec4<E>::T up[UPW];
+    f32x4 gd[KDA ? HPW : 1];
+    float g;
+  };
+  auto fetch = [&](Ops& x, int n_) {
+    const size_t ft = (size_t)bh * N + n_;
+    const int fnv = min(C, T - n_ * C);
+    const size_t ftok = (size_t)b * T + (size_t)n_ * C;
+    x.W.load_block(a.W + ft * C * DK);
+    if constexpr (KDA) {
+      x.K.load_block(a.Kt + ft * DK * C);
+#pragma unroll
+      for (int s = 0; s < HPW; ++s) {
+        const int td = min(w + NW * s, NH - 1) / NTV;
+        x.gd[s] = *(const f32x4*)(a.GC + ft * DK + td * 16 + (l >> 4) * 4);
+      }
+    } else {
+      x.K.load_rows(a.k + (ftok * H + h) * DK, (size_t)H * DK, fnv);
+      x.g = a.G[ft * C + min((int)threadIdx.x, C - 1)];
+    }
+    if constexpr (FWD) {
+      if constexpr (KDA)
+        x.Q.load_block(a.Qg + ft * C * DK);
+      else
+        x.Q.load_rows(a.q + (ftok * H + h) * DK, (size_t)H * DK, fnv);
+      x.P.load_block(a.P + ft * C * C);
+    }
+    // unconditional loads (clamped indices), so nothing waits for them here
+    if (!ident) {
+#pragma unroll
+      for (int s = 0; s < UPW; ++s) {
+        const int tt = min(w + NW * s, NU - 1);
+        x.up[s] = load4_raw<E>(a.Up + (ft * DV + v0 + (tt % NTV) * 16 + (l & 15)) * C + (tt / NTV) * 16 + (l >> 4) * 4);
+      }
+    }
+  };
+
+  size_t otok = 0;  // first token of the chunk whose o rows wait in sO
+  int onv = 0;
+  auto step = [&](Ops& x, int n) {
+    const size_t tile = (size_t)bh * N + n;
+    const int nv = min(C, T - n * C);
+    const size_t tok0 = (size_t)b * T + (size_t)n * C;
+    // ---- this chunk's operands and start state into LDS
+    if constexpr (!KDA) {
+      if (threadIdx.x < 64) {
+        const float gC = __shfl(x.g, C - 1, 64);
+        if (threadIdx.x < C) {
+          sg[threadIdx.x] = x.g;
+          sgam[threadIdx.x] = __expf(x.g);
+          skt[threadIdx.x] = __expf(gC - x.g);
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < HPW; ++s) {
+      const int tt = w + NW * s;
+      if (tt < NH) {
+        const int td = tt / NTV, tv = tt % NTV;
+        store4<E>(sS + (tv * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, hacc[s]);
+      }
+    }
+    x.W.store(sW, LK);
+    x.K.store(sK, KDA ? LC : LK);
+    if constexpr (FWD) {
+      x.Q.store(sQ, LK);
+      x.P.store(sP, LC);
+    }
+    f32x4 up[UPW];
+#pragma unroll
+    for (int s = 0; s < UPW; ++s) up[s] = ident ? zero4() : Vec4<E>::unpack(x.up[s]);
+    f32x4 dec[HPW];
+    if constexpr (KDA) {
+#pragma unroll
+      for (int s = 0; s < HPW; ++s)
+        dec[s] = f32x4{__expf(x.gd[s][0]), __expf(x.gd[s][1]), __expf(x.gd[s][2]), __expf(x.gd[s][3])};
+    }
+    if (n + 2 < n1) fetch(x, n + 2);
+    lds_barrier();
+    if constexpr (FWD) {
+      // o rows of the previous chunk (staged in sO by its last step)
+      if (n > n0) lds_to_rows<E, C, BV, NT>(a.o + (otok * H + h) * DV + v0, (size_t)H * DV, sO, LB, onv);
+    } else if constexpr (MODE == kScanBwd) {
+      lds_to_block<E, BV, DK, NT>(a.S + (tile * DV + v0) * DK, sS, LK);
+    }
+    // ---- U = U' - W Hn -> U^T (GDN: and (e^(g_C - g) U)^T)
+#pragma unroll
+    for (int s = 0; s < UPW; ++s) {
+      const int tt = w + NW * s;
+      if (tt < NU) {
+        const int ti = tt / NTV, tv = tt % NTV;
+        f32x4 acc = zero4();
+        mma<DK>(acc, sW + ti * 16 * LK, LK, sS + tv * 16 * LK, LK);
+        const f32x4 u = up[s] - acc;
+        const int vv = tv * 16 + (l & 15), t = ti * 16 + (l >> 4) * 4;
+        store4<E>(sU + vv * LC + t, u);
+        if constexpr (!KDA)
+          store4<E>(sUk + vv * LC + t, f32x4{u[0] * skt[t], u[1] * skt[t + 1], u[2] * skt[t + 2], u[3] * skt[t + 3]});
+        if constexpr (MODE == kScanBwd) store4<E>(a.U + (tile * DV + v0 + vv) * C + t, u);
+      }
+    }
+    lds_barrier();
+    // ---- O^T = Hn^T (Q diag(gamma))^T + U^T P^T -> o rows; state update
+    if constexpr (FWD) {
+      for (int tt = w; tt < NO; tt += NW) {
+        const int tv = tt / NB, ti = tt % NB;
+        f32x4 acc = zero4();
+        mma<DK>(acc, sS + tv * 16 * LK, LK, sQ + ti * 16 * LK, LK);
+        const int i = ti * 16 + (l & 15);
+        if constexpr (!KDA) acc *= sgam[i];
+        mma<C>(acc, sU + tv * 16 * LC, LC, sP + ti * 16 * LC, LC);
+        store4<E>(sO + i * LB + tv * 16 + (l >> 4) * 4, acc);
+      }
+      otok = tok0;
+      onv = nv;
+    }
+    const float gdec = KDA ? 0.f : __expf(sg[C - 1]);
+#pragma unroll
+    for (int s = 0; s < HPW; ++s) {
+      const int tt = w + NW * s;
+      if (tt < NH) {
+        const int td = tt / NTV, tv = tt % NTV;
+        if constexpr (KDA) {
+          hacc[s] *= dec[s];
+          mma<C>(hacc[s], sK + td * 16 * LC, LC, sU + tv * 16 * LC, LC);
+        } else {
+          hacc[s] *= gdec;
+          mma<C, true, false>(hacc[s], sK + td * 16, LK, sUk + tv * 16 * LC, LC);
+        }
+      }
+    }
+    lds_barrier();
+  };
+
+  Ops x0, x1;
+  if (n0 < n1) fetch(x0, n0);
+  if (n0 + 1 < n1) fetch(x1, n0 + 1);
+  for (int n = n0; n < n1; n += 2) {
+    step(x0, n);
+    if (n + 1 < n1) step(x1, n + 1);
+  }
+  if constexpr (FWD) {
+    if (n1 > n0) lds_to_rows<E, C, BV, NT>(a.o + (otok * H + h) * DV + v0, (size_t)H * DV, sO, LB, onv);
+  }
+  if (a.hout != nullptr) {
+#pragma unroll
+    for (int s = 0; s < HPW; ++s) {
+      const int tt = w + NW * s;
+      if (tt < NH) {
+        const int td = tt / NTV, tv = tt % NTV;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          a.hout[(st0 + td * 16 + (l >> 4) * 4 + r) * a.hs_ld + v0 + tv * 16 + (l & 15)] = hacc[s][r];
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------- k_carry
+// The serial pass over segments, one workgroup per (b, h, block of BV
+// columns): from the local pass's end states [E | M] of each segment,
+//   Hstart(s) = H,  H <- M(s) H + E(s)
+// starting from h0 (or zero); writes every segment's start state and the
+// final state.  M and H enter the MFMA as bf16, with fp32 accumulation, as
+// the state does in the chunk scan.
+template <int DK, int BV>
+struct CarryLds {
+  static constexpr int LK = DK + 8;
+  static constexpr size_t M = 0;                                 // M rows [d][e] (bf16)
+  static constexpr size_t HT = M + (size_t)DK * LK * 2;          // H^T [c][e] (bf16)
+  static constexpr size_t TOTAL = HT + (size_t)BV * LK * 2;
+};
+
+template <int DK, int BV, int NW = 8>
+__global__ __launch_bounds__(64 * NW) void k_carry(const float* __restrict__ hloc, const float* h0,
+                                                   float* __restrict__ hstart, float* ht, int nseg, int DV) {
+  typedef CarryLds<DK, BV> Lay;
+  constexpr int NT = 64 * NW, LK = Lay::LK, NTV = BV / 16;
+  constexpr int NH = (DK / 16) * NTV, HPW = (NH + NW - 1) / NW;
+  __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
+  bf16* sM = (bf16*)(smem + Lay::M);
+  bf16* sH = (bf16*)(smem + Lay::HT);
+  const int nvb = DV / BV;
+  const int vb = blockIdx.x % nvb, bh = blockIdx.x / nvb, v0 = vb * BV;
+  const int w = wave_id(), l = lane_id();
+  const int LDX = DV + DK;  // columns of a local end state: E then M
 
   f32x4 hacc[HPW];
 #pragma unroll
@@ -237,126 +482,42 @@ __global__ __launch_bounds__(64 * NW) void k_scan(const E* __restrict__ q, const
         hacc[s][r] = h0[((size_t)bh * DK + td * 16 + (l >> 4) * 4 + r) * DV + v0 + tv * 16 + (l & 15)];
     }
   }
-
-  // One chunk's operands in registers.  Two sets alternate, so the loads of
-  // chunk n + 2 are in flight while chunk n computes.
-  struct Ops {
-    Tile<E, C, DK, NT> W, K, Q;
-    Tile<E, C, C, NT> P;
-    typename Vec4<E>::T up[UPW];
-    float g;
-  };
-  auto fetch = [&](Ops& x, int n_) {
-    const size_t ft = (size_t)bh * N + n_;
-    const int fnv = min(C, T - n_ * C);
-    const size_t ftok = (size_t)b * T + (size_t)n_ * C;
-    x.W.load_block(wW + ft * C * DK);
-    x.K.load_rows(k + (ftok * H + h) * DK, (size_t)H * DK, fnv);
-    if constexpr (FWD) {
-      x.Q.load_rows(q + (ftok * H + h) * DK, (size_t)H * DK, fnv);
-      x.P.load_block(wP + ft * C * C);
-    }
-    // unconditional loads (clamped indices), so nothing waits for them here
-#pragma unroll
-    for (int s = 0; s < UPW; ++s) {
-      const int tt = min(w + NW * s, NU - 1);
-      x.up[s] = load4_raw<E>(wUp + (ft * DV + v0 + (tt % NTV) * 16 + (l & 15)) * C + (tt / NTV) * 16 + (l >> 4) * 4);
-    }
-    x.g = wG[ft * C + min((int)threadIdx.x, C - 1)];
-  };
-
-  size_t otok = 0;  // first token of the chunk whose o rows wait in sO
-  int onv = 0;
-  auto step = [&](Ops& x, int n) {
-    const size_t tile = (size_t)bh * N + n;
-    const int nv = min(C, T - n * C);
-    const size_t tok0 = (size_t)b * T + (size_t)n * C;
-    // ---- this chunk's operands and start state into LDS
-    if (threadIdx.x < 64) {
-      const float gC = __shfl(x.g, C - 1, 64);
-      if (threadIdx.x < C) {
-        sg[threadIdx.x] = x.g;
-        sgam[threadIdx.x] = __expf(x.g);
-        skt[threadIdx.x] = __expf(gC - x.g);
-      }
-    }
+  for (int sg = 0; sg < nseg; ++sg) {
+    const float* base = hloc + ((size_t)bh * nseg + sg) * DK * LDX;
+    // this segment's start state; H^T -> LDS (bf16)
 #pragma unroll
     for (int s = 0; s < HPW; ++s) {
       const int tt = w + NW * s;
       if (tt < NH) {
         const int td = tt / NTV, tv = tt % NTV;
-        store4<E>(sS + (tv * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, hacc[s]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          hstart[(((size_t)bh * nseg + sg) * DK + td * 16 + (l >> 4) * 4 + r) * DV + v0 + tv * 16 + (l & 15)] =
+              hacc[s][r];
+        store4<bf16>(sH + (tv * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, hacc[s]);
       }
     }
-    x.W.store(sW, LK);
-    x.K.store(sK, LK);
-    if constexpr (FWD) {
-      x.Q.store(sQ, LK);
-      x.P.store(sP, LC);
-    }
-    f32x4 up[UPW];
-#pragma unroll
-    for (int s = 0; s < UPW; ++s) up[s] = Vec4<E>::unpack(x.up[s]);
-    if (n + 2 < N) fetch(x, n + 2);
-    lds_barrier();
-    if constexpr (FWD) {
-      // o rows of the previous chunk (staged in sO by its last step)
-      if (n > 0) lds_to_rows<E, C, BV, NT>(o + (otok * H + h) * DV + v0, (size_t)H * DV, sO, LB, onv);
-    } else {
-      lds_to_block<E, BV, DK, NT>(wS + (tile * DV + v0) * DK, sS, LK);
-    }
-    // ---- U = U' - W Hn -> U^T and (e^(g_C - g) U)^T
-#pragma unroll
-    for (int s = 0; s < UPW; ++s) {
-      const int tt = w + NW * s;
-      if (tt < NU) {
-        const int ti = tt / NTV, tv = tt % NTV;
-        f32x4 acc = zero4();
-        mma<DK>(acc, sW + ti * 16 * LK, LK, sS + tv * 16 * LK, LK);
-        const f32x4 u = up[s] - acc;
-        const int vv = tv * 16 + (l & 15), t = ti * 16 + (l >> 4) * 4;
-        store4<E>(sU + vv * LC + t, u);
-        store4<E>(sUk + vv * LC + t, f32x4{u[0] * skt[t], u[1] * skt[t + 1], u[2] * skt[t + 2], u[3] * skt[t + 3]});
-        if constexpr (!FWD) store4<E>(wU + (tile * DV + v0 + vv) * C + t, u);
-      }
+    // M rows -> LDS (bf16)
+    for (int p = threadIdx.x; p < DK * (DK / 4); p += NT) {
+      const int d = p / (DK / 4), e0 = (p % (DK / 4)) * 4;
+      store4<bf16>(sM + d * LK + e0, *(const f32x4*)(base + (size_t)d * LDX + DV + e0));
     }
     lds_barrier();
-    // ---- O^T = (Hn^T Q^T) diag(gamma) + U^T P^T -> o rows; state update
-    if constexpr (FWD) {
-      for (int tt = w; tt < NO; tt += NW) {
-        const int tv = tt / NB, ti = tt % NB;
-        f32x4 acc = zero4();
-        mma<DK>(acc, sS + tv * 16 * LK, LK, sQ + ti * 16 * LK, LK);
-        const int i = ti * 16 + (l & 15);
-        acc *= sgam[i];
-        mma<C>(acc, sU + tv * 16 * LC, LC, sP + ti * 16 * LC, LC);
-        store4<E>(sO + i * LB + tv * 16 + (l >> 4) * 4, acc);
-      }
-      otok = tok0;
-      onv = nv;
-    }
-    const float dec = __expf(sg[C - 1]);
+    // H <- M H + E
 #pragma unroll
     for (int s = 0; s < HPW; ++s) {
       const int tt = w + NW * s;
       if (tt < NH) {
         const int td = tt / NTV, tv = tt % NTV;
-        hacc[s] *= dec;
-        mma<C, true, false>(hacc[s], sK + td * 16, LK, sUk + tv * 16 * LC, LC);
+        f32x4 acc = zero4();
+        mma<DK>(acc, sM + td * 16 * LK, LK, sH + tv * 16 * LK, LK);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[r] += base[(size_t)(td * 16 + (l >> 4) * 4 + r) * LDX + v0 + tv * 16 + (l & 15)];
+        hacc[s] = acc;
       }
     }
     lds_barrier();
-  };
-
-  Ops x0, x1;
-  fetch(x0, 0);
-  if (N > 1) fetch(x1, 1);
-  for (int n = 0; n < N; n += 2) {
-    step(x0, n);
-    if (n + 1 < N) step(x1, n + 1);
-  }
-  if constexpr (FWD) {
-    if (N > 0) lds_to_rows<E, C, BV, NT>(o + (otok * H + h) * DV + v0, (size_t)H * DV, sO, LB, onv);
   }
   if (ht != nullptr) {
 #pragma unroll
@@ -370,6 +531,58 @@ __global__ __launch_bounds__(64 * NW) void k_scan(const E* __restrict__ q, const
       }
     }
   }
+}
+
+// ------------------------------------------------------------- launchers
+// The forward scan over (b, h, column block) workgroups; when those are too
+// few to occupy the device the sequence is cut into segments: a local pass
+// per segment, the carry over segments, and the scan from the true segment
+// start states.
+template <typename E, int C, int DK, int DV, bool KDA>
+int launch_scan_fwd(const FwdArgs& a, const FwdWs& ws, int N) {
+  constexpr int BV = DV < 64 ? DV : 64;
+  const int nseg = scan_segments(a.B, a.H, DK, DV, N);
+  hipStream_t st = (hipStream_t)a.stream;
+  ScanArgs<E> s{};
+  s.q = (const E*)a.q;
+  s.k = (const E*)a.k;
+  s.W = (const E*)ws.W;
+  s.Up = (const E*)ws.Up;
+  s.P = (const E*)ws.P;
+  s.Qg = (const E*)ws.Qg;
+  s.Kt = (const E*)ws.Kt;
+  s.G = ws.G;
+  s.GC = ws.GC;
+  s.o = (E*)a.o;
+  s.T = a.T;
+  s.H = a.H;
+  s.N = N;
+  s.DV = DV;
+  const int bhv = a.B * a.H * (DV / BV);
+  if (nseg == 1) {
+    s.hin = a.h0;
+    s.hout = a.ht;
+    s.hs_ld = DV;
+    s.L = N;
+    s.nseg = 1;
+    LRT_LAUNCH(kKScan, (k_scan<E, C, DK, BV, kScanFwd, KDA, kStateWaves>), dim3(bhv), dim3(64 * kStateWaves), st, s);
+  } else {
+    s.L = (N + nseg - 1) / nseg;
+    s.nseg = nseg;
+    s.hin = nullptr;
+    s.hout = ws.SegLoc;
+    s.hs_ld = DV + DK;
+    LRT_LAUNCH(kKScanLocal, (k_scan<E, C, DK, BV, kScanLocal, KDA, kStateWaves>),
+               dim3(a.B * a.H * ((DV + DK) / BV) * nseg), dim3(64 * kStateWaves), st, s);
+    LRT_LAUNCH(kKCarry, (k_carry<DK, BV, kStateWaves>), dim3(bhv), dim3(64 * kStateWaves), st,
+               (const float*)ws.SegLoc, a.h0, ws.SegStart, a.ht, nseg, DV);
+    s.hin = ws.SegStart;
+    s.hout = nullptr;
+    s.hs_ld = DV;
+    LRT_LAUNCH(kKScan, (k_scan<E, C, DK, BV, kScanFwd, KDA, kStateWaves>), dim3(bhv * nseg),
+               dim3(64 * kStateWaves), st, s);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
 }  // namespace lrt

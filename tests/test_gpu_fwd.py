@@ -199,3 +199,25 @@ def test_kda_long_context_workload():
     eo, eh = rel(o_s, ro), rel(ht_s, rh)
     say(f"  rel err o={eo:.2e} ht={eh:.2e}")
     assert eo <= TOL[c["dtype"]] and eh <= TOL[c["dtype"]], (eo, eh)
+
+
+SEG_CASES = [
+    # name, op, B, T, H, dk, dv, chunk, gate kind, gate_shift, h0_std -- few (b, h) pairs and
+    # long sequences: the forward scan runs segment-parallel (local pass, carry, scan)
+    ("gdn_seg10_slow_h0", "gdn", 1, 10240 - 13, 1, 128, 128, 64, "scalar", -6.0, 0.1),
+    ("gdn_seg2_fast", "gdn", 1, 2560, 2, 128, 128, 64, "scalar", 0.0, 0.1),
+    ("kda_seg8_slow_C32", "kda", 1, 4096 - 5, 2, 64, 64, 32, "perdim", -6.0, 0.1),
+    ("kda_seg4_perdim_C64", "kda", 1, 4096, 2, 128, 128, 64, "perdim", 0.0, 0.1),
+    ("kda_seg4_lowrank_C64", "kda", 1, 4096, 2, 128, 128, 64, "lowrank", 0.0, 0.1),
+]
+
+
+@pytest.mark.parametrize("case", SEG_CASES, ids=[c[0] for c in SEG_CASES])
+def test_fwd_segmented_scan(case):
+    name, op, B, T, H, dk, dv, chunk, gate, shift, h0s = case
+    say(f"[fwd] {name}")
+    inp = synth.make_inputs(f"{op}_fwd", B, T, H, dk, dv, dtype=torch.bfloat16, seed=1, device="cuda", gate=gate,
+                            gate_shift=shift, h0_std=h0s)
+    eo, eh = run_fwd(op, inp, chunk)
+    say(f"  rel err o={eo:.2e} ht={eh:.2e}")
+    assert eo <= 1e-2 and eh <= 1e-2, (eo, eh)
