@@ -50,18 +50,25 @@ struct FwdWs {
   size_t bytes;
 };
 
-// Segments per sequence of the forward scan: one unless the (b, h, column
-// block) workgroups alone would leave the device mostly idle; then enough for
-// about 512 workgroups, each segment at least 16 chunks long (and d_k a
-// multiple of the column block, for the identity columns of the local pass).  Depends on the
+// Column block and segments of the forward scan.  One segment of up to 64
+// columns per workgroup unless those (b, h, column block) workgroups alone
+// would leave the device mostly idle; then 128-column blocks (when d_k is a
+// multiple, for the identity columns of the local pass) and enough segments
+// for about 512 workgroups, each at least 16 chunks long.  Depends on the
 // shape only, so the workspace size does not depend on the device.
-inline int scan_segments(int B, int H, int DK, int DV, int N) {
-  const int BV = DV < 64 ? DV : 64;
-  const long wgs = (long)B * H * (DV / BV);
-  if (wgs >= 256 || N < 32 || DK % BV != 0) return 1;
+struct ScanPlan {
+  int bv, nseg;
+};
+inline ScanPlan scan_plan(int B, int H, int DK, int DV, int N) {
+  const int bv64 = DV < 64 ? DV : 64;
+  if ((long)B * H * (DV / bv64) >= 256 || N < 32) return {bv64, 1};
+  int bv = DV < 128 ? DV : 128;
+  if (DK % bv != 0) bv = bv64;
+  if (DK % bv != 0) return {bv64, 1};
+  const long wgs = (long)B * H * (DV / bv);
   long ns = (512 + wgs - 1) / wgs;
   if (ns > N / 16) ns = N / 16;
-  return ns < 1 ? 1 : (int)ns;
+  return {bv, ns < 1 ? 1 : (int)ns};
 }
 
 inline FwdWs fwd_ws_layout(int B, int T, int H, int dk, int dv, int C, size_t esz, void* base, bool kda = false) {
@@ -84,7 +91,7 @@ inline FwdWs fwd_ws_layout(int B, int T, int H, int dk, int dv, int C, size_t es
   w.GC = kda ? (float*)take(tiles * dk * sizeof(float)) : nullptr;
   w.Qg = kda ? take(tiles * C * dk * esz) : nullptr;
   w.P = take(tiles * C * C * esz);
-  const int nseg = scan_segments(B, H, dk, dv, (int)N);
+  const int nseg = scan_plan(B, H, dk, dv, (int)N).nseg;
   w.SegLoc = nseg > 1 ? (float*)take((size_t)B * H * nseg * dk * (dv + dk) * sizeof(float)) : nullptr;
   w.SegStart = nseg > 1 ? (float*)take((size_t)B * H * nseg * dk * dv * sizeof(float)) : nullptr;
   w.bytes = off;

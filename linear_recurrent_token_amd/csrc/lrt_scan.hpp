@@ -215,8 +215,8 @@ struct ScanLds {
   static constexpr size_t Q = U + (KDA ? 1 : 2) * (size_t)BV * LC * es;           // q / Q o e^G rows [t][d]
   static constexpr size_t P_ = Q + (FWD ? (size_t)C * LK * es : 0);               // P [i][j]
   static constexpr size_t O = P_ + (FWD ? (size_t)C * LC * es : 0);               // o rows [t][v]
-  static constexpr size_t G = O + (FWD ? (size_t)C * LB * es : 0);                // g, gamma, e^(g_C - g)
-  static constexpr size_t TOTAL = G + 3 * C * 4;
+  static constexpr size_t G = O + (FWD ? (size_t)C * LB * es : 0);                // g, gamma, e^(g_C - g) / KDA: G_C
+  static constexpr size_t TOTAL = G + (KDA ? DK : 3 * C) * 4;
 };
 
 // One workgroup per (b, h, block of BV columns, segment) walks its chunks in
@@ -249,8 +249,10 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
 
   const int DVX = MODE == kScanLocal ? a.DV + DK : a.DV;
   const int nvb = DVX / BV;
-  const int wg = xcd_group(blockIdx.x, gridDim.x);  // column blocks of one (b, h) share an L2
-  const int seg = wg % a.nseg, vb = (wg / a.nseg) % nvb, bh = wg / a.nseg / nvb;
+  // the column blocks of one (b, h, segment) are consecutive, so they share an
+  // XCD and its L2 (they read the same W, K, Q and P tiles)
+  const int wg = xcd_group(blockIdx.x, gridDim.x);
+  const int vb = wg % nvb, seg = (wg / nvb) % a.nseg, bh = wg / nvb / a.nseg;
   const int T = a.T, H = a.H, N = a.N, DV = a.DV;
   const int h = bh % H, b = bh / H;
   const int v0 = vb * BV;
@@ -284,8 +286,7 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
     Tile<E, KDA ? DK : C, KDA ? C : DK, NT> K;
     Tile<E, C, C, NT> P;
     typename Vec4<E>::T up[UPW];
-    f32x4 gd[KDA ? HPW : 1];
-    float g;
+    float g;  // GDN: g of token tid; KDA: G_C of key dimension tid
   };
   auto fetch = [&](Ops& x, int n_) {
     const size_t ft = (size_t)bh * N + n_;
@@ -294,11 +295,7 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
     x.W.load_block(a.W + ft * C * DK);
     if constexpr (KDA) {
       x.K.load_block(a.Kt + ft * DK * C);
-#pragma unroll
-      for (int s = 0; s < HPW; ++s) {
-        const int td = min(w + NW * s, NH - 1) / NTV;
-        x.gd[s] = *(const f32x4*)(a.GC + ft * DK + td * 16 + (l >> 4) * 4);
-      }
+      x.g = a.GC[ft * DK + min((int)threadIdx.x, DK - 1)];
     } else {
       x.K.load_rows(a.k + (ftok * H + h) * DK, (size_t)H * DK, fnv);
       x.g = a.G[ft * C + min((int)threadIdx.x, C - 1)];
@@ -327,7 +324,9 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
     const int nv = min(C, T - n * C);
     const size_t tok0 = (size_t)b * T + (size_t)n * C;
     // ---- this chunk's operands and start state into LDS
-    if constexpr (!KDA) {
+    if constexpr (KDA) {
+      if (threadIdx.x < DK) sg[threadIdx.x] = __expf(x.g);  // per-dim chunk decay
+    } else {
       if (threadIdx.x < 64) {
         const float gC = __shfl(x.g, C - 1, 64);
         if (threadIdx.x < C) {
@@ -354,12 +353,6 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
     f32x4 up[UPW];
 #pragma unroll
     for (int s = 0; s < UPW; ++s) up[s] = ident ? zero4() : Vec4<E>::unpack(x.up[s]);
-    f32x4 dec[HPW];
-    if constexpr (KDA) {
-#pragma unroll
-      for (int s = 0; s < HPW; ++s)
-        dec[s] = f32x4{__expf(x.gd[s][0]), __expf(x.gd[s][1]), __expf(x.gd[s][2]), __expf(x.gd[s][3])};
-    }
     if (n + 2 < n1) fetch(x, n + 2);
     lds_barrier();
     if constexpr (FWD) {
@@ -406,7 +399,7 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
       if (tt < NH) {
         const int td = tt / NTV, tv = tt % NTV;
         if constexpr (KDA) {
-          hacc[s] *= dec[s];
+          hacc[s] *= *(const f32x4*)(sg + td * 16 + (l >> 4) * 4);
           mma<C>(hacc[s], sK + td * 16 * LC, LC, sU + tv * 16 * LC, LC);
         } else {
           hacc[s] *= gdec;
@@ -538,10 +531,8 @@ __global__ __launch_bounds__(64 * NW) void k_carry(const float* __restrict__ hlo
 // few to occupy the device the sequence is cut into segments: a local pass
 // per segment, the carry over segments, and the scan from the true segment
 // start states.
-template <typename E, int C, int DK, int DV, bool KDA>
-int launch_scan_fwd(const FwdArgs& a, const FwdWs& ws, int N) {
-  constexpr int BV = DV < 64 ? DV : 64;
-  const int nseg = scan_segments(a.B, a.H, DK, DV, N);
+template <typename E, int C, int DK, int DV, int BV, bool KDA>
+int launch_scan_fwd_bv(const FwdArgs& a, const FwdWs& ws, int N, int nseg) {
   hipStream_t st = (hipStream_t)a.stream;
   ScanArgs<E> s{};
   s.q = (const E*)a.q;
@@ -583,6 +574,17 @@ int launch_scan_fwd(const FwdArgs& a, const FwdWs& ws, int N) {
                dim3(64 * kStateWaves), st, s);
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+template <typename E, int C, int DK, int DV, bool KDA>
+int launch_scan_fwd(const FwdArgs& a, const FwdWs& ws, int N) {
+  constexpr int BV64 = DV < 64 ? DV : 64;
+  constexpr int BV128 = DV < 128 ? DV : 128;
+  const ScanPlan pl = scan_plan(a.B, a.H, DK, DV, N);
+  if constexpr (BV128 != BV64 && DK % BV128 == 0 && ScanLds<E, C, DK, BV128, kScanFwd, KDA>::TOTAL <= 160 * 1024) {
+    if (pl.bv == BV128) return launch_scan_fwd_bv<E, C, DK, DV, BV128, KDA>(a, ws, N, pl.nseg);
+  }
+  return launch_scan_fwd_bv<E, C, DK, DV, BV64, KDA>(a, ws, N, pl.bv == BV64 ? pl.nseg : 1);
 }
 
 }  // namespace lrt
