@@ -25,7 +25,7 @@ namespace lrt {
 template <typename E, int C, int DK, int BV, bool DELTA>
 struct FusedLds {
   static constexpr int P = lds_pad<E>();
-  static constexpr int LK = DK + P, LB = BV + P, LC = C + P, LA = C + 1;
+  static constexpr int LK = DK + P, LB = BV + P, LC = C + P, LA = tri_ld<C>();
   static constexpr size_t es = sizeof(E);
   static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
   static constexpr size_t K = 0;                                        // k rows [t][d]
@@ -33,10 +33,10 @@ struct FusedLds {
   static constexpr size_t V = Q + (size_t)C * LK * es;                  // b v rows [t][v]
   static constexpr size_t S = V + (size_t)C * LB * es;                  // Hn^T [v][d]
   static constexpr size_t P_ = S + (size_t)BV * LK * es;                // (Q K^T) o Gamma [i][j]
-  static constexpr size_t U = P_ + (size_t)C * LC * es;                 // A (fp32); then U^T, (kt U)^T
+  static constexpr size_t U = P_ + (size_t)C * LC * es;                 // A, T (fp32, column-major); then U^T, (kt U)^T
   static constexpr size_t USZ = mx(DELTA ? (size_t)C * LA * 4 : 0, 2 * (size_t)BV * LC * es);
-  static constexpr size_t TW = U + USZ;                                 // Tinv (fp32); then W rows [t][d]
-  static constexpr size_t TWSZ = DELTA ? mx((size_t)C * LA * 4, (size_t)C * LK * es) : 0;
+  static constexpr size_t TW = U + USZ;                                 // W rows [t][d]
+  static constexpr size_t TWSZ = DELTA ? (size_t)C * LK * es : 0;
   static constexpr size_t T = TW + TWSZ;                                // Tinv, Tinv diag(b gamma) (E)
   static constexpr size_t TSZ = DELTA ? 2 * (size_t)C * LC * es : 0;
   static constexpr size_t O = T + TSZ;                                  // o rows [t][v]
@@ -66,7 +66,6 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const E* __restrict__ q, const 
   float* sA = (float*)(smem + Lay::U);
   E* sU = (E*)(smem + Lay::U);
   E* sUk = sU + BV * LC;
-  float* sTf = (float*)(smem + Lay::TW);
   E* sW = (E*)(smem + Lay::TW);
   E* sT = (E*)(smem + Lay::T);
   E* sTw = sT + C * LC;
@@ -149,10 +148,6 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const E* __restrict__ q, const 
     for (int tt = w; tt < NB * NB; tt += NW) {
       const int ti = tt / NB, tj = tt % NB;
       if (tj > ti) {
-        if constexpr (DELTA) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sA[(ti * 16 + (l >> 4) * 4 + r) * LA + tj * 16 + (l & 15)] = 0.f;
-        }
         store4<E>(sP + (ti * 16 + (l & 15)) * LC + tj * 16 + (l >> 4) * 4, zero4());
         continue;
       }
@@ -168,20 +163,19 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const E* __restrict__ q, const 
       if constexpr (DELTA) {
         f32x4 kk = zero4();
         mma<DK>(kk, sK + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
+        f32x4 av;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = i0 + r;
-          sA[i * LA + j] = (j < i) ? sb[i] * kk[r] * __expf(sg[i] - sg[j]) : 0.f;
-        }
+        for (int r = 0; r < 4; ++r) av[r] = (j < i0 + r) ? sb[i0 + r] * kk[r] * __expf(sg[i0 + r] - sg[j]) : 0.f;
+        *(f32x4*)(sA + j * LA + i0) = av;  // column-major
       }
     }
     lds_barrier();
     if constexpr (DELTA) {
       // ---- S3: T = (I + A)^-1, in E twice: T and T diag(b gamma)
-      unit_lower_inverse<C, NT>(sA, sTf);
+      unit_lower_inverse<C, NT>(sA);
       for (int idx = threadIdx.x; idx < C * C; idx += NT) {
-        const int i = idx / C, j = idx % C;
-        const float x = j <= i ? sTf[i * LA + j] : 0.f;
+        const int j = idx / C, i = idx % C;
+        const float x = j <= i ? sA[j * LA + i] : 0.f;
         sT[i * LC + j] = from_f<E>(x);
         sTw[i * LC + j] = from_f<E>(x * sbg[j]);
       }

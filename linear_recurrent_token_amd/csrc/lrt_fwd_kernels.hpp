@@ -29,73 +29,105 @@ namespace lrt {
 // moving reads above the writes.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// One 16 x 16 x 16 fp32 product on the 16x16x4 MFMA, operands read from LDS
-// at any row stride (no alignment assumed): acc += X Y, X[m][k] at
-// x[m * ldx + k], Y[k][n] at y[k * ldy + n].  Step s feeds k = 4s + l/16.
-__device__ __forceinline__ void mma16_f32(f32x4& acc, const float* x, int ldx, const float* y, int ldy) {
+// Triangular matrices of a chunk (A, then its inverse in place) live in LDS
+// column-major, element (r, c) at p[c * tri_ld<C>() + r]: a column of four
+// consecutive rows is one 16-byte access.
+template <int C>
+constexpr int tri_ld() {
+  return C + 4;
+}
+
+// One 16 x 16 x 16 fp32 product on the 16x16x4 MFMA from column-major LDS
+// blocks: acc += X Y with X(m, k) at x[k * ld + m], Y(k, n) at y[n * ld + k].
+// Lane group g feeds k = 4g + s at step s.
+__device__ __forceinline__ void mma16_cm(f32x4& acc, const float* x, const float* y, int ld) {
   const int l = lane_id(), g = l >> 4, j = l & 15;
+  const f32x4 yv = *(const f32x4*)(y + j * ld + 4 * g);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[j * ldx + 4 * s + g], y[(4 * s + g) * ldy + j], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[(4 * g + s) * ld + j], yv[s], acc, 0, 0, 0);
 }
 
-// Store a 16 x 16 accumulator tile (times sc) at d[m * ld + n].
-__device__ __forceinline__ void acc16_store(float* d, int ld, f32x4 acc, float sc) {
+// Store a 16 x 16 accumulator tile (times sc) column-major: D(m, n) at d[n * ld + m].
+__device__ __forceinline__ void acc16_store_cm(float* d, int ld, f32x4 acc, float sc) {
   const int l = lane_id();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) d[((l >> 4) * 4 + i) * ld + (l & 15)] = sc * acc[i];
+  *(f32x4*)(d + (l & 15) * ld + (l >> 4) * 4) = sc * acc;
 }
 
-// (I + A)^-1 for a strictly lower-triangular C x C matrix A in LDS (fp32,
-// row stride C + 1, C in {16, 32, 64}), written to Tf (same layout).  Only
-// the lower triangle of Tf, diagonal included, is defined on return: its
-// strictly upper off-diagonal 16-blocks serve as scratch.
-//   stage 1  the 16 x 16 diagonal blocks by forward substitution, one lane
-//            per column, right-looking (after x_m is known every later row
-//            takes its term, so the dependent chain is 16 steps);
+// Broadcast lane q of every group of four lanes to the whole group (DPP).
+template <int Q>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), Q * 0x55, 0xf, 0xf, false));
+}
+
+// (I + A)^-1 for a strictly lower-triangular C x C matrix A (fp32, C in
+// {16, 32, 64}), column-major in LDS with leading dimension tri_ld<C>(),
+// computed in place.  Only the lower triangle, diagonal included, is defined
+// on return: the strictly upper off-diagonal 16-blocks serve as scratch.
+//   stage 1  the 16 x 16 diagonal blocks by forward substitution, one wave per
+//            block, four lanes per column (each holding four rows): after
+//            x_m is known (a DPP broadcast inside the group of four) every
+//            later row takes its term, and the column of A that step m needs
+//            is one 16-byte read per lane, independent of x;
 //   stage 2  doubling to 32 x 32: [[X, 0], [Y, Z]]^-1 has lower-left block
-//            -Z^-1 Y X^-1, two fp32 MFMA products; one wave per 32-block
-//            does stages 1 and 2 without a workgroup barrier;
+//            -Z^-1 Y X^-1, two fp32 MFMA products in the wave that owns the
+//            upper diagonal block (so no workgroup barrier in between);
 //   stage 3  (C = 64) the same doubling to 64 x 64 with 32 x 32 blocks, the
 //            four 16-block outputs of each product on four waves.
-// All NT threads must call it after A is visible to them; Tf is visible to
-// all threads on return.
+// All NT threads must call it after A is visible to them; the result is
+// visible to all threads on return.
 template <int C, int NT = kThreads>
-__device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sTf) {
+__device__ __forceinline__ void unit_lower_inverse(float* p) {
   static_assert(C == 16 || C == 32 || C == 64, "chunk must be 16, 32 or 64");
   static_assert(NT >= 256, "the 64 x 64 doubling uses four waves");
   constexpr int NB = C / 16;
-  constexpr int LA = C + 1;
-  constexpr int NP = NB > 1 ? NB / 2 : 1;  // 32-blocks (one wave each)
+  constexpr int LD = tri_ld<C>();
   const int w = wave_id(), l = lane_id();
-  if (w < NP) {
-    // stage 1: diagonal blocks 2w (lanes 0..15) and 2w + 1 (lanes 16..31)
-    const int bb = 2 * w + (l >> 4);
-    if (l < 16 * (NB > 1 ? 2 : 1)) {
-      const int j = l & 15;
-      const float* Ab = sA + (bb * 16) * LA + bb * 16;
-      float x[16];
+  if (w < NB) {
+    // stage 1: block bb = w; lane (column j, row quarter rq) holds rows 4rq..4rq+3
+    const int bb = w, j = l >> 2, rq = l & 3;
+    float* blk = p + bb * 16 * LD + bb * 16;  // block (bb, bb)
+    float x[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+    for (int i = 0; i < 4; ++i) x[i] = (4 * rq + i == j) ? 1.f : 0.f;
+    // columns of A four steps at a time, the next four loading meanwhile
+    f32x4 cur[4], nxt[4];
 #pragma unroll
-      for (int m = 0; m < 15; ++m)
+    for (int i = 0; i < 4; ++i) cur[i] = *(const f32x4*)(blk + i * LD + 4 * rq);  // A(4rq.., m)
+#define LRT_INV_STEP(m_, a_)                                                                      \
+  {                                                                                               \
+    const float xm = quad_bcast<((m_) >> 2)>(x[(m_) & 3]);                                        \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) if (4 * rq + i > (m_)) x[i] -= (a_)[i] * xm;    \
+  }
 #pragma unroll
-        for (int r = m + 1; r < 16; ++r) x[r] -= Ab[r * LA + m] * x[m];
+    for (int g = 0; g < 4; ++g) {
+      if (g < 3) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sTf[(bb * 16 + r) * LA + bb * 16 + j] = x[r];
+        for (int i = 0; i < 4; ++i) nxt[i] = *(const f32x4*)(blk + min(4 * g + 4 + i, 14) * LD + 4 * rq);
+      }
+      if (g == 0) { LRT_INV_STEP(0, cur[0]) LRT_INV_STEP(1, cur[1]) LRT_INV_STEP(2, cur[2]) LRT_INV_STEP(3, cur[3]) }
+      if (g == 1) { LRT_INV_STEP(4, cur[0]) LRT_INV_STEP(5, cur[1]) LRT_INV_STEP(6, cur[2]) LRT_INV_STEP(7, cur[3]) }
+      if (g == 2) { LRT_INV_STEP(8, cur[0]) LRT_INV_STEP(9, cur[1]) LRT_INV_STEP(10, cur[2]) LRT_INV_STEP(11, cur[3]) }
+      if (g == 3) { LRT_INV_STEP(12, cur[0]) LRT_INV_STEP(13, cur[1]) LRT_INV_STEP(14, cur[2]) }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
     }
-    if constexpr (NB > 1) {
-      // stage 2: T[2w+1][2w] = -T[2w+1][2w+1] (A[2w+1][2w] T[2w][2w]); the
-      // intermediate sits in the upper block [2w][2w+1]
+#undef LRT_INV_STEP
+    *(f32x4*)(blk + j * LD + 4 * rq) = f32x4{x[0], x[1], x[2], x[3]};
+  }
+  if constexpr (NB > 1) {
+    lds_barrier();
+    // stage 2: wave w < NB/2 fills T[2w+1][2w] = -T[2w+1][2w+1] (A[2w+1][2w] T[2w][2w]),
+    // the intermediate in the upper block [2w][2w+1]
+    if (w < NB / 2) {
       const int b0 = 2 * w * 16, b1 = b0 + 16;
-      wave_lds_sync();
       f32x4 y = zero4();
-      mma16_f32(y, sA + b1 * LA + b0, LA, sTf + b0 * LA + b0, LA);
-      acc16_store(sTf + b0 * LA + b1, LA, y, 1.f);
+      mma16_cm(y, p + b0 * LD + b1, p + b0 * LD + b0, LD);
+      acc16_store_cm(p + b1 * LD + b0, LD, y, 1.f);
       wave_lds_sync();
       f32x4 z = zero4();
-      mma16_f32(z, sTf + b1 * LA + b1, LA, sTf + b0 * LA + b1, LA);
-      acc16_store(sTf + b1 * LA + b0, LA, z, -1.f);
+      mma16_cm(z, p + b1 * LD + b1, p + b1 * LD + b0, LD);
+      acc16_store_cm(p + b0 * LD + b1, LD, z, -1.f);
     }
   }
   if constexpr (NB == 4) {
@@ -105,8 +137,8 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sTf) 
     if (w < 4) {
       const int a = 2 + (w >> 1), b = w & 1;
       f32x4 x = zero4();
-      for (int c = b; c < 2; ++c) mma16_f32(x, sA + a * 16 * LA + c * 16, LA, sTf + c * 16 * LA + b * 16, LA);
-      acc16_store(sTf + (a - 2) * 16 * LA + 32 + b * 16, LA, x, 1.f);
+      for (int c = b; c < 2; ++c) mma16_cm(x, p + c * 16 * LD + a * 16, p + b * 16 * LD + c * 16, LD);
+      acc16_store_cm(p + (2 + b) * 16 * LD + (a - 2) * 16, LD, x, 1.f);
     }
     lds_barrier();
     // stage 3b: T[a][b] = -sum_{c=2..a} T[a][c] X[c][b]
@@ -114,8 +146,8 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sTf) 
       const int a = 2 + (w >> 1), b = w & 1;
       f32x4 t = zero4();
       for (int c = 2; c <= a; ++c)
-        mma16_f32(t, sTf + a * 16 * LA + c * 16, LA, sTf + (c - 2) * 16 * LA + 32 + b * 16, LA);
-      acc16_store(sTf + a * 16 * LA + b * 16, LA, t, -1.f);
+        mma16_cm(t, p + c * 16 * LD + a * 16, p + (2 + b) * 16 * LD + (c - 2) * 16, LD);
+      acc16_store_cm(p + b * 16 * LD + a * 16, LD, t, -1.f);
     }
   }
   lds_barrier();
@@ -126,12 +158,12 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sTf) 
 template <typename E, int C, int DK, int DV, bool DELTA>
 struct PrepLds {
   static constexpr int P = lds_pad<E>();
-  static constexpr int LK = DK + P, LC = C + P, LA = C + 1;
+  static constexpr int LK = DK + P, LC = C + P, LA = tri_ld<C>();
   static constexpr size_t es = sizeof(E);
   static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
   static constexpr size_t K = 0;
   static constexpr size_t A = K + mx((size_t)C * LK * es, DELTA ? (size_t)C * LA * 4 : 0);
-  static constexpr size_t XT = A + (DELTA ? mx((size_t)C * LA * 4, (size_t)C * LC * es) : 0);
+  static constexpr size_t XT = A + (DELTA ? mx((size_t)C * LA * 4, (size_t)C * LK * es) : 0);
   static constexpr size_t YT = XT + (DELTA ? (size_t)(DK > DV ? DK : DV) * LC * es : 0);
   static constexpr size_t G = YT + (size_t)DV * LC * es;
   static constexpr size_t TOTAL = G + 4 * C * 4;
@@ -153,9 +185,8 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ k, cons
   constexpr int V = 16 / (int)sizeof(E);
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
   E* sK = (E*)(smem + Lay::K);
-  float* sTf = (float*)(smem + Lay::K);
   float* sA = (float*)(smem + Lay::A);
-  E* sT = (E*)(smem + Lay::A);
+  E* sT = (E*)(smem + Lay::K);
   E* sXt = (E*)(smem + Lay::XT);
   E* sYt = (E*)(smem + Lay::YT);
   float* sg = (float*)(smem + Lay::G);
@@ -239,23 +270,23 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ k, cons
         f32x4 acc = zero4();
         if (tj <= ti) mma<DK>(acc, sK + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
         const int j = tj * 16 + (l & 15);
+        const int i0 = ti * 16 + (l >> 4) * 4;
+        f32x4 av;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = ti * 16 + (l >> 4) * 4 + r;
-          sA[i * LA + j] = (j < i) ? sb[i] * acc[r] * __expf(sg[i] - sg[j]) : 0.f;
-        }
+        for (int r = 0; r < 4; ++r) av[r] = (j < i0 + r) ? sb[i0 + r] * acc[r] * __expf(sg[i0 + r] - sg[j]) : 0.f;
+        *(f32x4*)(sA + j * LA + i0) = av;  // column-major
       }
       lds_barrier();
-      unit_lower_inverse<C>(sA, sTf);  // writes over the dead K rows
+      unit_lower_inverse<C>(sA);
       for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
-        const int i = idx / C, j = idx % C;
-        const E x = from_f<E>(j <= i ? sTf[i * LA + j] : 0.f);
-        sT[i * LC + j] = x;  // over the dead A
-        if (WRITE_T) wT[(size_t)tile * C * C + idx] = x;
+        const int j = idx / C, i = idx % C;
+        const E x = from_f<E>(j <= i ? sA[j * LA + i] : 0.f);
+        sT[i * LC + j] = x;  // over the dead K rows
+        if (WRITE_T) wT[(size_t)tile * C * C + i * C + j] = x;
       }
       lds_barrier();
       // W^T = X^T Tinv^T (rows d, cols t), staged as W[t][d] over the dead inverse
-      E* sWo = (E*)(smem + Lay::K);
+      E* sWo = (E*)(smem + Lay::A);
       for (int tt = w; tt < (DK / 16) * NB; tt += kWaves) {
         const int td = tt / NB, tc = tt % NB;
         f32x4 acc = zero4();

@@ -30,7 +30,7 @@ namespace lrt {
 template <typename E, int C, int DK, int DV, int NT>
 struct KdaLds {
   static constexpr int P = lds_pad<E>();
-  static constexpr int LK = DK + P, LV = DV + P, LC = C + P, LG = DK + 4, LA = C + 1, NB = C / 16;
+  static constexpr int LK = DK + P, LV = DV + P, LC = C + P, LG = DK + 4, LA = tri_ld<C>(), NB = C / 16;
   static constexpr int NQ = (NT / DK < C) ? NT / DK : C;  // row segments of the cumsum
   static constexpr size_t es = sizeof(E);
   static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
@@ -206,12 +206,11 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
           const int tj = r0;
           f32x4 acc = zero4();
           mma<DK>(acc, sKE + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
-          const int j = tj * 16 + (l & 15);
+          const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
+          f32x4 av;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = ti * 16 + (l >> 4) * 4 + r;
-            sA[i * LA + j] = (j < i) ? sb[i] * acc[r] : 0.f;
-          }
+          for (int r = 0; r < 4; ++r) av[r] = (j < i0 + r) ? sb[i0 + r] * acc[r] : 0.f;
+          *(f32x4*)(sA + j * LA + i0) = av;  // column-major
         } else {
           const int t2 = tt - NA, rj = t2 / NB, ci = t2 % NB;
           f32x4 acc = zero4();
@@ -295,7 +294,7 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
           const int i = r0 + (l & 15), j0 = sj * 16 + (l >> 4) * 4;
           if (kind == 0) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sA[i * LA + j0 + r] = sb[i] * acc[r];
+            for (int r = 0; r < 4; ++r) sA[(j0 + r) * LA + i] = sb[i] * acc[r];  // column-major
           } else {
             store4<E>(pout + (size_t)i * C + j0, acc);
           }
@@ -327,7 +326,7 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
             aqk += qi[e] * x;
           }
         }
-        if (j < i) sA[i * LA + j] = sb[i] * akk;
+        if (j < i) sA[j * LA + i] = sb[i] * akk;  // column-major
         pout[(size_t)i * C + j] = from_f<E>(aqk);
       }
       // P above the diagonal is zero: whole blocks (16-byte stores) and the
@@ -342,12 +341,12 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
       }
     }
     lds_barrier();
-    unit_lower_inverse<C, NT>(sA, sA);
+    unit_lower_inverse<C, NT>(sA);
     // T and T diag(b) in E; X = K o e^G rows (the fast path staged them already)
     E* sX = sS;
     for (int idx = tid; idx < C * C; idx += NT) {
-      const int i = idx / C, j = idx % C;
-      const float x = j <= i ? sA[i * LA + j] : 0.f;
+      const int j = idx / C, i = idx % C;
+      const float x = j <= i ? sA[j * LA + i] : 0.f;
       sT[i * LC + j] = from_f<E>(x);
       sTw[i * LC + j] = from_f<E>(x * sb[j]);
     }

@@ -31,13 +31,13 @@ namespace lrt {
 template <typename E, int C, int DK, int DV>
 struct WyLds {
   static constexpr int P = lds_pad<E>();
-  static constexpr int LK = DK + P, LV = DV + P, LC = C + P, LA = C + 1;
+  static constexpr int LK = DK + P, LV = DV + P, LC = C + P, LA = tri_ld<C>();
   static constexpr size_t es = sizeof(E);
   static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
   static constexpr size_t K = 0;                                                      // k rows [t][d]
   static constexpr size_t V = K + (size_t)C * LK * es;                                // b v rows [t][v]
   static constexpr size_t QT = V + (size_t)C * LV * es;                               // q rows; then T, T diag(b gamma)
-  static constexpr size_t A = QT + mx((size_t)C * LK * es, 2 * (size_t)C * LC * es);  // A (fp32), inverted in place
+  static constexpr size_t A = QT + mx((size_t)C * LK * es, 2 * (size_t)C * LC * es);  // A (fp32, column-major), inverted in place
   static constexpr size_t G = A + (size_t)C * LA * 4;                                 // g, gamma, b, b gamma
   static constexpr size_t TOTAL = G + 4 * C * 4;
 };
@@ -124,12 +124,11 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
         const int tj = r0;
         f32x4 acc = zero4();
         mma<DK>(acc, sK + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
-        const int j = tj * 16 + (l & 15);
+        const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
+        f32x4 av;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = ti * 16 + (l >> 4) * 4 + r;
-          sA[i * LA + j] = (j < i) ? sb[i] * acc[r] * __expf(sg[i] - sg[j]) : 0.f;
-        }
+        for (int r = 0; r < 4; ++r) av[r] = (j < i0 + r) ? sb[i0 + r] * acc[r] * __expf(sg[i0 + r] - sg[j]) : 0.f;
+        *(f32x4*)(sA + j * LA + i0) = av;  // column-major
       } else {
         const int t2 = tt - NA, rj = t2 / NB, ci = t2 % NB;
         f32x4 acc = zero4();
@@ -142,10 +141,10 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
       }
     }
     lds_barrier();
-    unit_lower_inverse<C, NT>(sA, sA);
+    unit_lower_inverse<C, NT>(sA);
     for (int idx = threadIdx.x; idx < C * C; idx += NT) {
-      const int i = idx / C, j = idx % C;
-      const float x = j <= i ? sA[i * LA + j] : 0.f;
+      const int j = idx / C, i = idx % C;
+      const float x = j <= i ? sA[j * LA + i] : 0.f;
       sT[i * LC + j] = from_f<E>(x);
       sTw[i * LC + j] = from_f<E>(x * sbg[j]);
     }
