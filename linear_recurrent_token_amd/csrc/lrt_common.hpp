@@ -25,11 +25,12 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 
-// LDS row padding (elements): 16 bytes keeps vector alignment and shifts
-// consecutive rows by four banks.
+// LDS row padding (elements): 32 bytes keeps vector alignment and shifts
+// consecutive rows by eight banks, so the four rows one transpose read
+// touches fall in different banks (measured slightly faster than 16 bytes).
 template <typename E>
 constexpr int lds_pad() {
-  return 16 / (int)sizeof(E);
+  return 32 / (int)sizeof(E);
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
