@@ -413,30 +413,35 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
     }
     lds_barrier();
     // dQ^T = gamma (Hn dO^T) + K^T dS^T (rows d, cols i), kept in registers;
-    // dW^T = -Hn dU^T -> workspace in accumulator-tile order
+    // dW^T = -Hn dU^T -> workspace in accumulator-tile order.  A wave's tiles
+    // share their column block, so its dO, dS and dU fragments are the same
+    // for every tile (loaded once) and its dg term is one sum.
+    static_assert(NW % NB == 0, "waves must cover whole column blocks");
     f32x4 dqa[KPW];
+    {
+      const int ti = w % NB, i = ti * 16 + (l & 15);
+      const float gam = __expf(sg[i]);
+      float esum = 0.f;
 #pragma unroll
-    for (int s = 0; s < KPW; ++s) {
-      const int tt = w + NW * s;
-      dqa[s] = zero4();
-      if (tt < NKT) {
-        const int td = tt / NB, ti = tt % NB;
-        const int i = ti * 16 + (l & 15), d0 = td * 16 + (l >> 4) * 4;
-        f32x4 acc = zero4();
-        mma<DV, true, false>(acc, sS + td * 16, LK, sdO + ti * 16 * LV, LV);
-        const float gam = __expf(sg[i]);
-        float e = 0.f;
+      for (int s = 0; s < KPW; ++s) {
+        const int td = w / NB + (NW / NB) * s;
+        dqa[s] = zero4();
+        if (td < DK / 16) {
+          const int d0 = td * 16 + (l >> 4) * 4;
+          f32x4 acc = zero4();
+          mma<DV, true, false>(acc, sS + td * 16, LK, sdO + ti * 16 * LV, LV);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) e += to_f(sQ[i * LK + d0 + r]) * acc[r];
-        e = sum4(e * gam);
-        if (l < 16) atomicAdd(&sdg[i], e);
-        acc *= gam;
-        mma<C, true, true>(acc, sK + td * 16, LK, sdSj + ti * 16, LC);
-        dqa[s] = acc;
-        f32x4 dw = zero4();
-        mma<DV, true, true>(dw, sS + td * 16, LK, sdUt + ti * 16, LC);
-        acc_tile_store<E>(wdW + (size_t)tile * C * DK, tt, -dw);
+          for (int r = 0; r < 4; ++r) esum += to_f(sQ[i * LK + d0 + r]) * acc[r];
+          acc *= gam;
+          mma<C, true, true>(acc, sK + td * 16, LK, sdSj + ti * 16, LC);
+          dqa[s] = acc;
+          f32x4 dw = zero4();
+          mma<DV, true, true>(dw, sS + td * 16, LK, sdUt + ti * 16, LC);
+          acc_tile_store<E>(wdW + (size_t)tile * C * DK, td * NB + ti, -dw);
+        }
       }
+      esum = sum4(esum * gam);
+      if (l < 16) atomicAdd(&sdg[i], esum);
     }
     // <dH', Hn> from the registers of this chunk's S and dH'; then the next S
     {
@@ -469,28 +474,31 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
     tdS.store(sS, LK);
     lds_barrier();
     lds_to_rows<E, C, DK, NT>(dq + (tok0 * H + h) * DK, (size_t)H * DK, sdQ, LK, nv);
-    // dK1^T = e^(g_C - g_j) (dH' U^T) + Q^T dS   (rows d, cols j)
+    // dK1^T = e^(g_C - g_j) (dH' U^T) + Q^T dS   (rows d, cols j); a wave's
+    // tiles share their column block j
     const float gC = sg[C - 1];
+    {
+      const int tj = w % NB, j = tj * 16 + (l & 15);
+      const float kt = __expf(gC - sg[j]);
+      float ssum = 0.f;
 #pragma unroll
-    for (int s = 0; s < KPW; ++s) {
-      const int tt = w + NW * s;
-      if (tt < NKT) {
-        const int td = tt / NB, tj = tt % NB;
-        const int j = tj * 16 + (l & 15), d0 = td * 16 + (l >> 4) * 4;
-        f32x4 acc = zero4();
-        mma<DV, true, true>(acc, sS + td * 16, LK, sUt + tj * 16, LC);
-        const float kt = __expf(gC - sg[j]);
-        float sj = 0.f;
+      for (int s = 0; s < KPW; ++s) {
+        const int td = w / NB + (NW / NB) * s;
+        if (td < DK / 16) {
+          const int d0 = td * 16 + (l >> 4) * 4;
+          f32x4 acc = zero4();
+          mma<DV, true, true>(acc, sS + td * 16, LK, sUt + tj * 16, LC);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sj += acc[r] * to_f(sK[j * LK + d0 + r]);
-        sj = sum4(sj * kt);
-        if (l < 16) {
-          atomicAdd(&sdg[j], -sj);
-          atomicAdd(&sdg[C - 1], sj);
+          for (int r = 0; r < 4; ++r) ssum += acc[r] * to_f(sK[j * LK + d0 + r]);
+          acc *= kt;
+          mma<C, true, false>(acc, sQ + td * 16, LK, sdSj + tj * 16 * LC, LC);
+          acc_tile_store<E>(wdK1 + (size_t)tile * C * DK, td * NB + tj, acc);
         }
-        acc *= kt;
-        mma<C, true, false>(acc, sQ + td * 16, LK, sdSj + tj * 16 * LC, LC);
-        acc_tile_store<E>(wdK1 + (size_t)tile * C * DK, tt, acc);
+      }
+      ssum = sum4(ssum * kt);
+      if (l < 16) {
+        atomicAdd(&sdg[j], -ssum);
+        atomicAdd(&sdg[C - 1], ssum);
       }
     }
     lds_barrier();

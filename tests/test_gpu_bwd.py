@@ -61,6 +61,8 @@ CASES = [
     ("bf16_fast_C64", 2, 256, 2, 128, 128, 64, torch.bfloat16, 2.0, 0.1, 0.0),
     ("bf16_d16_dv32", 1, 100, 2, 16, 32, 16, torch.bfloat16, -6.0, 0.1, 0.1),
     ("bf16_dk32_dv128", 1, 100, 2, 32, 128, 32, torch.bfloat16, -6.0, 0.1, 0.1),
+    # long sequence, slow gates: the state carry spans 64 chunks both ways
+    ("bf16_long_slow_C64", 1, 4096 - 7, 2, 128, 128, 64, torch.bfloat16, -6.0, 0.1, 0.1),
 ]
 
 
