@@ -330,6 +330,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, NB = C / 16;
   constexpr int V = 16 / (int)sizeof(E);
   constexpr int NKT = (DK / 16) * NB, KPW = (NKT + NW - 1) / NW;
+  static_assert(NW % NB == 0, "waves must cover whole column blocks");
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
   E* sQ = (E*)(smem + Lay::Q);
   E* sK = (E*)(smem + Lay::K);
@@ -388,6 +389,8 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
     if (tile + (int)gridDim.x < ntiles) LRT_G1_LOAD(tile + (int)gridDim.x)
 
     // dS = (dO U^T) o Gamma (inclusive); E = dS o (Q K^T) -> dg rows +, cols -
+    // (a wave's tiles share column block w % NB: one column sum per wave)
+    float ecol = 0.f;
     for (int tt = w; tt < NB * NB; tt += NW) {
       const int ti = tt / NB, tj = tt % NB;
       const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
@@ -396,7 +399,6 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
         f32x4 qk = zero4(), dp = zero4();
         mma<DK>(qk, sQ + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
         mma<DV, false, true>(dp, sdO + ti * 16 * LV, LV, sUt + tj * 16, LC);
-        float ecol = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = i0 + r;
@@ -406,17 +408,16 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
           const float er = sum16(e);
           if ((l & 15) == 0) atomicAdd(&sdg[i], er);
         }
-        ecol = sum4(ecol);
-        if (l < 16) atomicAdd(&sdg[j], -ecol);
       }
       store4<E>(sdSj + j * LC + i0, ds);
     }
+    ecol = sum4(ecol);
+    if (l < 16) atomicAdd(&sdg[(w % NB) * 16 + (l & 15)], -ecol);
     lds_barrier();
     // dQ^T = gamma (Hn dO^T) + K^T dS^T (rows d, cols i), kept in registers;
     // dW^T = -Hn dU^T -> workspace in accumulator-tile order.  A wave's tiles
     // share their column block, so its dO, dS and dU fragments are the same
     // for every tile (loaded once) and its dg term is one sum.
-    static_assert(NW % NB == 0, "waves must cover whole column blocks");
     f32x4 dqa[KPW];
     {
       const int ti = w % NB, i = ti * 16 + (l & 15);
@@ -545,6 +546,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
   constexpr int NT = 64 * NW;
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, NB = C / 16;
   constexpr int NKT = (DK / 16) * NB, KPW = (NKT + NW - 1) / NW;
+  static_assert(NW % NB == 0, "waves must cover whole column blocks");
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
   E* sK = (E*)(smem + Lay::K);
   E* sV = (E*)(smem + Lay::VV);
@@ -618,34 +620,44 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
     lds_barrier();
     if (tile + (int)gridDim.x < ntiles) LRT_G2_LOAD(tile + (int)gridDim.x)
     // dX^T = dW^T Tinv (rows d, cols j): dK += b gamma dX, cx_j = dX_j . k_j
-#pragma unroll
-    for (int s = 0; s < KPW; ++s) {
-      const int kt = w + NW * s;
-      if (kt < NKT) {
-        const int td = kt / NB, tj = kt % NB;
-        const int j = tj * 16 + (l & 15), d0 = td * 16 + (l >> 4) * 4;
-        f32x4 acc = zero4();
-        mma<C, true, true>(acc, sdW + td * 16, LK, sT + tj * 16, LC);
-        dka[s] += (sb[j] * __expf(sg[j])) * acc;
-        float e = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sK[j * LK + d0 + r]);
-        e = sum4(e);
-        if (l < 16) atomicAdd(&scx[j], e);
-      }
-    }
-    // dY^T = dU^T Tinv (rows v, cols j): dV = b dY (rows staged), dbeta += dY_j . v_j
-    for (int tt2 = w; tt2 < (DV / 16) * NB; tt2 += NW) {
-      const int tvv = tt2 / NB, tj = tt2 % NB;
-      const int j = tj * 16 + (l & 15), v0 = tvv * 16 + (l >> 4) * 4;
-      f32x4 acc = zero4();
-      mma<C, false, true>(acc, sdUt + tvv * 16 * LC, LC, sT + tj * 16, LC);
-      store4<E>(sdV + j * LV + v0, sb[j] * acc);
+    // (a wave's tiles all lie in column block w % NB, so each wave reduces
+    // its column sums once, after its tiles)
+    const int jw = (w % NB) * 16 + (l & 15);
+    {
+      const float bgj = sb[jw] * __expf(sg[jw]);
       float e = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sV[j * LV + v0 + r]);
+      for (int s = 0; s < KPW; ++s) {
+        const int kt = w + NW * s;
+        if (kt < NKT) {
+          const int td = kt / NB, tj = kt % NB;
+          const int d0 = td * 16 + (l >> 4) * 4;
+          f32x4 acc = zero4();
+          mma<C, true, true>(acc, sdW + td * 16, LK, sT + tj * 16, LC);
+          dka[s] += bgj * acc;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sK[jw * LK + d0 + r]);
+        }
+      }
       e = sum4(e);
-      if (l < 16) atomicAdd(&sdb[j], e);
+      if (l < 16) atomicAdd(&scx[jw], e);
+    }
+    // dY^T = dU^T Tinv (rows v, cols j): dV = b dY (rows staged), dbeta += dY_j . v_j
+    {
+      const float bj = sb[jw];
+      float e = 0.f;
+#pragma unroll
+      for (int tt2 = w; tt2 < (DV / 16) * NB; tt2 += NW) {
+        const int tvv = tt2 / NB, tj = tt2 % NB;
+        const int v0 = tvv * 16 + (l >> 4) * 4;
+        f32x4 acc = zero4();
+        mma<C, false, true>(acc, sdUt + tvv * 16 * LC, LC, sT + tj * 16, LC);
+        store4<E>(sdV + jw * LV + v0, bj * acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sV[jw * LV + v0 + r]);
+      }
+      e = sum4(e);
+      if (l < 16) atomicAdd(&sdb[jw], e);
     }
     lds_barrier();
     lds_to_rows<E, C, DV, NT>(dv + (tok0 * H + h) * DV, (size_t)H * DV, sdV, LV, nv);
@@ -670,6 +682,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
     lds_barrier();
     // dA = -strict_lower(Tinv^T R); with A = b_i (K K^T) o Gamma:
     //   M = dA o b_i Gamma -> M^T [k][i], dbeta_i += sum_k dA o Gamma o KK^T, E = dA o A -> dg
+    float ecol = 0.f;  // column kk = jw for every tile of this wave
     for (int t2 = w; t2 < NB * NB; t2 += NW) {
       const int ti = t2 / NB, tk2 = t2 % NB;
       const int kk = tk2 * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
@@ -678,7 +691,6 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
         f32x4 acc = zero4(), kkt = zero4();
         mma<C, true, false>(acc, sT + ti * 16, LC, sRt + tk2 * 16 * LC, LC);
         mma<DK>(kkt, sK + ti * 16 * LK, LK, sK + tk2 * 16 * LK, LK);
-        float ecol = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = i0 + r;
@@ -695,11 +707,11 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
             atomicAdd(&sdb[i], br);
           }
         }
-        ecol = sum4(ecol);
-        if (l < 16) atomicAdd(&sdg[kk], -ecol);
       }
       store4<E>(sMt + kk * LC + i0, m);
     }
+    ecol = sum4(ecol);
+    if (l < 16) atomicAdd(&sdg[jw], -ecol);
     lds_barrier();
     // dK^T += K^T M (cols j: sum_i k_i M_ij) + K^T M^T (cols i: sum_j k_j M_ij)
 #pragma unroll

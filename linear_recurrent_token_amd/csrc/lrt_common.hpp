@@ -381,12 +381,19 @@ __device__ __forceinline__ void block_to_lds(E* lds, int ls, const E* g) {
   t.store(lds, ls);
 }
 
-// Sum over the 16 lanes of a row group (lanes with equal l / 16).
+// x from another lane of the same 16-lane row, by a DPP control (VALU only).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+// Sum over the 16 lanes of a row group (lanes with equal l / 16), all in
+// DPP: pairs (quad_perm 1,0,3,2), quads (2,3,0,1), halves of the row
+// (mirror inside 8 lanes), then the two halves (mirror inside 16 lanes).
 __device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 1, 64);
-  x += __shfl_xor(x, 2, 64);
-  x += __shfl_xor(x, 4, 64);
-  x += __shfl_xor(x, 8, 64);
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  x += dpp_mov<0x140>(x);
   return x;
 }
 // Sum over the 4 lanes sharing a column (lanes with equal l % 16).
