@@ -572,6 +572,13 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
   AccTiles<E, DK / 16, NB, NT> tdw;  // dW in accumulator-tile order
   typename Vec4<E>::T rk1[KPW];  // the first part of dK, accumulator layout (rows d, cols j), packed
   float rg = 0.f, rb = 0.f, rd = 0.f;
+  // The previous chunk's dK rows, d log a and dbeta, written out while this
+  // chunk runs: stores left at the end of an iteration would be waited for
+  // by the next iteration's first wait on its prefetched loads.
+  Tile<E, C, DK, NT> pdk;
+  float pdla = 0.f, pdb = 0.f;
+  size_t ptok = 0;
+  int ph = 0, pnv = 0;
 #define LRT_G2_LOAD(tile_)                                                                        \
   {                                                                                               \
     const int ln = (tile_) % N, lbh = (tile_) / N;                                                \
@@ -606,6 +613,9 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
     tt.store(sT, LC);
     tdu.store(sdUt, LC);
     tdw.store(sdW, LK);
+    // every lane consumes the gate registers here, so no load into them is
+    // still pending (and waited for) when the next prefetch overwrites them
+    asm volatile("" ::"v"(rg), "v"(rb), "v"(rd));
     if (threadIdx.x < C) {
       const int t = threadIdx.x;
       sg[t] = rg;
@@ -617,6 +627,13 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
     f32x4 dka[KPW];
 #pragma unroll
     for (int s = 0; s < KPW; ++s) dka[s] = Vec4<E>::unpack(rk1[s]);
+    if (pnv > 0) {
+      pdk.store_rows(dk + (ptok * H + ph) * DK, (size_t)H * DK, pnv);
+      if ((int)threadIdx.x < pnv) {
+        dlog_a[(ptok + threadIdx.x) * H + ph] = pdla;
+        dbeta[(ptok + threadIdx.x) * H + ph] = pdb;
+      }
+    }
     lds_barrier();
     if (tile + (int)gridDim.x < ntiles) LRT_G2_LOAD(tile + (int)gridDim.x)
     // dX^T = dW^T Tinv (rows d, cols j): dK += b gamma dX, cx_j = dX_j . k_j
@@ -733,15 +750,22 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
         dg = sdg[t] + sb[t] * gam * scx[t];
         db = sdb[t] + gam * scx[t];
       }
-      const float dla = wave_incl_suffix(dg);
-      if (t < nv) {
-        dlog_a[(tok0 + t) * H + h] = dla;
-        dbeta[(tok0 + t) * H + h] = db;
-      }
+      pdla = wave_incl_suffix(dg);
+      pdb = db;
     }
     lds_barrier();
-    lds_to_rows<E, C, DK, NT>(dk + (tok0 * H + h) * DK, (size_t)H * DK, sdK, LK, nv);
+    pdk.load_lds(sdK, LK);
+    ptok = tok0;
+    ph = h;
+    pnv = nv;
     lds_barrier();
+  }
+  if (pnv > 0) {
+    pdk.store_rows(dk + (ptok * H + ph) * DK, (size_t)H * DK, pnv);
+    if ((int)threadIdx.x < pnv) {
+      dlog_a[(ptok + threadIdx.x) * H + ph] = pdla;
+      dbeta[(ptok + threadIdx.x) * H + ph] = pdb;
+    }
   }
 #undef LRT_G2_LOAD
 }

@@ -285,6 +285,28 @@ struct Tile {
       }
     }
   }
+  // the R x W block back from lds[r * ls + c]
+  __device__ __forceinline__ void load_lds(const E* lds, int ls) {
+#pragma unroll
+    for (int s = 0; s < PT; ++s) {
+      const int idx = threadIdx.x + NT * s;
+      if (idx < NP) {
+        const int r = idx / PR, c = (idx % PR) * V;
+        x[s] = *(const u32x4*)(lds + r * ls + c);
+      }
+    }
+  }
+  // rows [0, nvalid) to a strided global array
+  __device__ __forceinline__ void store_rows(E* g, size_t gs, int nvalid) const {
+#pragma unroll
+    for (int s = 0; s < PT; ++s) {
+      const int idx = threadIdx.x + NT * s;
+      if (idx < NP) {
+        const int r = idx / PR, c = (idx % PR) * V;
+        if (r < nvalid) *(u32x4*)(g + (size_t)r * gs + c) = x[s];
+      }
+    }
+  }
   // transposed: lds[c * ld + r]
   __device__ __forceinline__ void store_T(E* lds, int ld) const {
 #pragma unroll
