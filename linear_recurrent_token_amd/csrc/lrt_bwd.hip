@@ -396,18 +396,18 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
       const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
       f32x4 ds = zero4();
       if (tj <= ti) {
-        f32x4 qk = zero4(), dp = zero4();
+        f32x4 qk = zero4(), dp = zero4(), ev;
         mma<DK>(qk, sQ + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
         mma<DV, false, true>(dp, sdO + ti * 16 * LV, LV, sUt + tj * 16, LC);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = i0 + r;
           ds[r] = (j <= i) ? dp[r] * __expf(sg[i] - sg[j]) : 0.f;
-          const float e = ds[r] * qk[r];
-          ecol += e;
-          const float er = sum16(e);
-          if ((l & 15) == 0) atomicAdd(&sdg[i], er);
+          ev[r] = ds[r] * qk[r];
+          ecol += ev[r];
         }
+        const float er = rowsum4(ev);
+        if ((l & 3) == 0) atomicAdd(&sdg[i0 + ((l >> 2) & 3)], er);
       }
       store4<E>(sdSj + j * LC + i0, ds);
     }
@@ -579,35 +579,43 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
   float pdla = 0.f, pdb = 0.f;
   size_t ptok = 0;
   int ph = 0, pnv = 0;
-#define LRT_G2_LOAD(tile_)                                                                        \
+  // The next chunk's operands are fetched in parts (bit mask PART_), one
+  // part per phase of this chunk: a wave that issues all of them at once
+  // stalls on the full memory queue instead of computing.
+#define LRT_G2_LOAD(tile_, PART_)                                                                 \
   {                                                                                               \
     const int ln = (tile_) % N, lbh = (tile_) / N;                                                \
     const int lnv = min(C, T - ln * C);                                                           \
     const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                                   \
     const int lh = lbh % H;                                                                       \
-    tk.load_rows(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                                  \
-    tv.load_rows(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                                  \
-    tt.load_block(wT + (size_t)(tile_) * C * C);                                                  \
-    tdu.load_block(wdU + (size_t)(tile_) * DV * C);                                               \
-    tdw.load(wdW + (size_t)(tile_) * C * DK);                                                     \
-    _Pragma("unroll") for (int s = 0; s < KPW; ++s) {                                             \
-      const int kt_ = w + NW * s;                                                             \
-      rk1[s] = load4_raw<E>(wdK1 + (size_t)(tile_) * C * DK + ((size_t)min(kt_, NKT - 1) * 64 + l) * 4); \
-    }                                                                                             \
-    {                                                                                             \
+    if ((PART_) & 1) {                                                                            \
+      tk.load_rows(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                                \
       const int tc = min((int)threadIdx.x, C - 1);                                                \
       rg = wG[(size_t)(tile_) * C + tc];                                                          \
       rb = beta[(ltok + min(tc, lnv - 1)) * H + lh];                                              \
       rd = wdg1[(size_t)(tile_) * C + tc];                                                        \
     }                                                                                             \
+    if ((PART_) & 2) tv.load_rows(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                 \
+    if ((PART_) & 4) {                                                                            \
+      tt.load_block(wT + (size_t)(tile_) * C * C);                                                \
+      tdu.load_block(wdU + (size_t)(tile_) * DV * C);                                             \
+    }                                                                                             \
+    if ((PART_) & 8) tdw.load(wdW + (size_t)(tile_) * C * DK);                                    \
+    if ((PART_) & 16) {                                                                           \
+      _Pragma("unroll") for (int s = 0; s < KPW; ++s) {                                           \
+        const int kt_ = w + NW * s;                                                               \
+        rk1[s] = load4_raw<E>(wdK1 + (size_t)(tile_) * C * DK + ((size_t)min(kt_, NKT - 1) * 64 + l) * 4); \
+      }                                                                                           \
+    }                                                                                             \
   }
 
   int tile = blockIdx.x;
-  if (tile < ntiles) LRT_G2_LOAD(tile)
+  if (tile < ntiles) LRT_G2_LOAD(tile, 31)
   for (; tile < ntiles; tile += gridDim.x) {
     const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
     const int t0 = n * C, nv = min(C, T - t0);
     const size_t tok0 = (size_t)b * T + t0;
+    const int next = tile + (int)gridDim.x;
     tk.store(sK, LK);
     tv.store(sV, LV);
     tt.store(sT, LC);
@@ -635,7 +643,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
       }
     }
     lds_barrier();
-    if (tile + (int)gridDim.x < ntiles) LRT_G2_LOAD(tile + (int)gridDim.x)
+    if (next < ntiles) LRT_G2_LOAD(next, 1)
     // dX^T = dW^T Tinv (rows d, cols j): dK += b gamma dX, cx_j = dX_j . k_j
     // (a wave's tiles all lie in column block w % NB, so each wave reduces
     // its column sums once, after its tiles)
@@ -664,7 +672,9 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
       const float bj = sb[jw];
       float e = 0.f;
 #pragma unroll
-      for (int tt2 = w; tt2 < (DV / 16) * NB; tt2 += NW) {
+      for (int s2 = 0; s2 < ((DV / 16) * NB + NW - 1) / NW; ++s2) {
+        const int tt2 = w + NW * s2;
+        if (tt2 >= (DV / 16) * NB) break;
         const int tvv = tt2 / NB, tj = tt2 % NB;
         const int v0 = tvv * 16 + (l >> 4) * 4;
         f32x4 acc = zero4();
@@ -679,8 +689,12 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
     lds_barrier();
     lds_to_rows<E, C, DV, NT>(dv + (tok0 * H + h) * DV, (size_t)H * DV, sdV, LV, nv);
     lds_barrier();
+    if (next < ntiles) LRT_G2_LOAD(next, 2)
     // dT = (dW K^T) diag(b gamma) + (dU V^T) diag(b)   (rows i, cols j) -> dT^T [j][i]
-    for (int t2 = w; t2 < NB * NB; t2 += NW) {
+#pragma unroll
+    for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
+      const int t2 = w + NW * s2;
+      if (t2 >= NB * NB) break;
       const int ti = t2 / NB, tj = t2 % NB;
       const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
       f32x4 z1 = zero4(), z2 = zero4();
@@ -689,18 +703,26 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
       store4<E>(sdTt + j * LC + i0, sb[j] * (__expf(sg[j]) * z1 + z2));
     }
     lds_barrier();
+    if (next < ntiles) LRT_G2_LOAD(next, 4)
     // R = dT Tinv^T (rows i, cols k) -> R^T [k][i]
-    for (int t2 = w; t2 < NB * NB; t2 += NW) {
+#pragma unroll
+    for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
+      const int t2 = w + NW * s2;
+      if (t2 >= NB * NB) break;
       const int ti = t2 / NB, tk2 = t2 % NB;
       f32x4 acc = zero4();
       mma<C, true, false>(acc, sdTt + ti * 16, LC, sT + tk2 * 16 * LC, LC);
       store4<E>(sRt + (tk2 * 16 + (l & 15)) * LC + ti * 16 + (l >> 4) * 4, acc);
     }
     lds_barrier();
+    if (next < ntiles) LRT_G2_LOAD(next, 8)
     // dA = -strict_lower(Tinv^T R); with A = b_i (K K^T) o Gamma:
     //   M = dA o b_i Gamma -> M^T [k][i], dbeta_i += sum_k dA o Gamma o KK^T, E = dA o A -> dg
     float ecol = 0.f;  // column kk = jw for every tile of this wave
-    for (int t2 = w; t2 < NB * NB; t2 += NW) {
+#pragma unroll
+    for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
+      const int t2 = w + NW * s2;
+      if (t2 >= NB * NB) break;
       const int ti = t2 / NB, tk2 = t2 % NB;
       const int kk = tk2 * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
       f32x4 m = zero4();
@@ -708,6 +730,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
         f32x4 acc = zero4(), kkt = zero4();
         mma<C, true, false>(acc, sT + ti * 16, LC, sRt + tk2 * 16 * LC, LC);
         mma<DK>(kkt, sK + ti * 16 * LK, LK, sK + tk2 * 16 * LK, LK);
+        f32x4 ev, bv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = i0 + r;
@@ -715,14 +738,15 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
           const float da = -acc[r];
           const float a = sb[i] * kkt[r] * gam;
           m[r] = da * sb[i] * gam;
-          const float e = da * a;
-          ecol += e;
-          const float er = sum16(e);
-          const float br = sum16(da * gam * kkt[r]);
-          if ((l & 15) == 0) {
-            atomicAdd(&sdg[i], er);
-            atomicAdd(&sdb[i], br);
-          }
+          ev[r] = da * a;
+          bv[r] = da * gam * kkt[r];
+          ecol += ev[r];
+        }
+        const float er = rowsum4(ev), br = rowsum4(bv);
+        if ((l & 3) == 0) {
+          const int ir = i0 + ((l >> 2) & 3);
+          atomicAdd(&sdg[ir], er);
+          atomicAdd(&sdb[ir], br);
         }
       }
       store4<E>(sMt + kk * LC + i0, m);
@@ -730,6 +754,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
     ecol = sum4(ecol);
     if (l < 16) atomicAdd(&sdg[jw], -ecol);
     lds_barrier();
+    if (next < ntiles) LRT_G2_LOAD(next, 16)
     // dK^T += K^T M (cols j: sum_i k_i M_ij) + K^T M^T (cols i: sum_j k_j M_ij)
 #pragma unroll
     for (int s = 0; s < KPW; ++s) {

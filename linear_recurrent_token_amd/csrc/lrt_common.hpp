@@ -418,6 +418,20 @@ __device__ __forceinline__ float sum16(float x) {
   x += dpp_mov<0x140>(x);
   return x;
 }
+// Row sums of an accumulator tile: v[r] holds row 4 * (l / 16) + r of column
+// l % 16.  Returns, in every lane, the sum over the 16 columns of row
+// 4 * (l / 16) + ((l >> 2) & 3): halves of the row group trade rows (lane
+// l ^ 8), then quarters (lane 7 - l within eight), then the quad sums.
+__device__ __forceinline__ float rowsum4(f32x4 v) {
+  const int l = lane_id();
+  const bool hi = (l & 8) != 0, b2 = (l & 4) != 0;
+  const float p0 = (hi ? v[2] : v[0]) + dpp_mov<0x128>(hi ? v[0] : v[2]);
+  const float p1 = (hi ? v[3] : v[1]) + dpp_mov<0x128>(hi ? v[1] : v[3]);
+  float q = (b2 ? p1 : p0) + dpp_mov<0x141>(b2 ? p0 : p1);
+  q += dpp_mov<0xB1>(q);
+  q += dpp_mov<0x4E>(q);
+  return q;
+}
 // Sum over the 4 lanes sharing a column (lanes with equal l % 16).
 __device__ __forceinline__ float sum4(float x) {
   x += __shfl_xor(x, 16, 64);
