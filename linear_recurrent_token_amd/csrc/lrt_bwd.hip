@@ -350,48 +350,63 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
   Tile<E, DV, C, NT> tu, tdu;
   Tile<E, DV, DK, NT> tS, tdS;
   float rg = 0.f;
-#define LRT_G1_LOAD(tile_)                                                                \
+  // this chunk's dg partials, written out during the next chunk
+  float pdg = 0.f;
+  int ptile = -1;
+  // The next chunk's operands are fetched in parts (bit mask PART_) spread
+  // over this chunk's phases, so no wave stalls on a full memory queue.
+#define LRT_G1_LOAD(tile_, PART_)                                                         \
   {                                                                                       \
     const int ln = (tile_) % N, lbh = (tile_) / N;                                        \
     const int lnv = min(C, T - ln * C);                                                   \
     const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                           \
     const int lh = lbh % H;                                                               \
-    tq.load_rows(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
-    tk.load_rows(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
-    to.load_rows(d_o + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                        \
-    tu.load_block(wU + (size_t)(tile_) * DV * C);                                         \
-    tdu.load_block(wdU + (size_t)(tile_) * DV * C);                                       \
-    rg = wG[(size_t)(tile_) * C + min((int)threadIdx.x, C - 1)];                          \
+    if ((PART_) & 1) {                                                                    \
+      tq.load_rows_clamped(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                \
+      tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                \
+      rg = wG[(size_t)(tile_) * C + min((int)threadIdx.x, C - 1)];                        \
+    }                                                                                     \
+    if ((PART_) & 2) {                                                                    \
+      to.load_rows_clamped(d_o + (ltok * H + lh) * DV, (size_t)H * DV, lnv);              \
+      tu.load_block(wU + (size_t)(tile_) * DV * C);                                       \
+    }                                                                                     \
+    if ((PART_) & 4) tdu.load_block(wdU + (size_t)(tile_) * DV * C);                      \
+    if ((PART_) & 8) tS.load_block(wS + (size_t)(tile_) * DV * DK);                       \
   }
 
   int tile = blockIdx.x;
-  if (tile < ntiles) {
-    LRT_G1_LOAD(tile)
-    tS.load_block(wS + (size_t)tile * DV * DK);
-  }
+  if (tile < ntiles) LRT_G1_LOAD(tile, 15)
   for (; tile < ntiles; tile += gridDim.x) {
     const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
     const int t0 = n * C, nv = min(C, T - t0);
     const size_t tok0 = (size_t)b * T + t0;
-    tq.store(sQ, LK);
-    tk.store(sK, LK);
-    to.store(sdO, LV);
+    // the next chunk (the last one again on the final pass: its loads go
+    // unused, but unconditional loads keep the waits on older ones exact)
+    const int next = min(tile + (int)gridDim.x, ntiles - 1);
+    tq.store_masked(sQ, LK, nv);
+    tk.store_masked(sK, LK, nv);
+    to.store_masked(sdO, LV, nv);
     tu.store(sUt, LC);
     tdu.store(sdUt, LC);
     tS.store(sS, LK);
+    asm volatile("" ::"v"(rg));  // consumed by every lane (no load into it left pending)
     if (threadIdx.x < C) {
       sg[threadIdx.x] = rg;
       sdg[threadIdx.x] = 0.f;
     }
     if (threadIdx.x == 0) sdot[0] = 0.f;
-    tdS.load_block(wdS + (size_t)tile * DV * DK);  // dH' of this chunk, needed after dQ
+    if (ptile >= 0 && threadIdx.x < C) wdg1[(size_t)ptile * C + threadIdx.x] = pdg;
+    tdS.load_block(wdS + (size_t)tile * DV * DK);  // dH' of this chunk, needed after dS
     lds_barrier();
-    if (tile + (int)gridDim.x < ntiles) LRT_G1_LOAD(tile + (int)gridDim.x)
+    LRT_G1_LOAD(next, 1)
 
     // dS = (dO U^T) o Gamma (inclusive); E = dS o (Q K^T) -> dg rows +, cols -
     // (a wave's tiles share column block w % NB: one column sum per wave)
     float ecol = 0.f;
-    for (int tt = w; tt < NB * NB; tt += NW) {
+#pragma unroll
+    for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
+      const int tt = w + NW * s2;
+      if (tt >= NB * NB) break;
       const int ti = tt / NB, tj = tt % NB;
       const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
       f32x4 ds = zero4();
@@ -414,6 +429,26 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
     ecol = sum4(ecol);
     if (l < 16) atomicAdd(&sdg[(w % NB) * 16 + (l & 15)], -ecol);
     lds_barrier();
+    // <dH', Hn> from the registers of this chunk's S and dH' (before any
+    // store of this chunk, so the wait for dH' leaves the prefetch in flight);
+    // then the next S and more of the next chunk
+    {
+      float part = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < tS.PT; ++s2) {
+        if (threadIdx.x + NT * s2 < tS.NP) {
+          E a[V], d[V];
+          __builtin_memcpy(a, &tS.x[s2], 16);
+          __builtin_memcpy(d, &tdS.x[s2], 16);
+#pragma unroll
+          for (int e = 0; e < V; ++e) part += to_f(a[e]) * to_f(d[e]);
+        }
+      }
+      part = sum16(part);
+      part = sum4(part);
+      if (l == 0) atomicAdd(sdot, part);
+    }
+    LRT_G1_LOAD(next, 10)
     // dQ^T = gamma (Hn dO^T) + K^T dS^T (rows d, cols i), kept in registers;
     // dW^T = -Hn dU^T -> workspace in accumulator-tile order.  A wave's tiles
     // share their column block, so its dO, dS and dU fragments are the same
@@ -444,24 +479,6 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
       esum = sum4(esum * gam);
       if (l < 16) atomicAdd(&sdg[i], esum);
     }
-    // <dH', Hn> from the registers of this chunk's S and dH'; then the next S
-    {
-      float part = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < tS.PT; ++s2) {
-        if (threadIdx.x + NT * s2 < tS.NP) {
-          E a[V], d[V];
-          __builtin_memcpy(a, &tS.x[s2], 16);
-          __builtin_memcpy(d, &tdS.x[s2], 16);
-#pragma unroll
-          for (int e = 0; e < V; ++e) part += to_f(a[e]) * to_f(d[e]);
-        }
-      }
-      part = sum16(part);
-      part = sum4(part);
-      if (l == 0) atomicAdd(sdot, part);
-    }
-    if (tile + (int)gridDim.x < ntiles) tS.load_block(wS + (size_t)(tile + (int)gridDim.x) * DV * DK);
     lds_barrier();
     // dq rows over the dead dO; dH'^T over the dead S
 #pragma unroll
@@ -474,6 +491,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
     }
     tdS.store(sS, LK);
     lds_barrier();
+    LRT_G1_LOAD(next, 4)
     lds_to_rows<E, C, DK, NT>(dq + (tok0 * H + h) * DK, (size_t)H * DK, sdQ, LK, nv);
     // dK1^T = e^(g_C - g_j) (dH' U^T) + Q^T dS   (rows d, cols j); a wave's
     // tiles share their column block j
@@ -506,10 +524,12 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
     if (threadIdx.x < C) {
       float x = sdg[threadIdx.x];
       if (threadIdx.x == C - 1) x += __expf(gC) * sdot[0];
-      wdg1[(size_t)tile * C + threadIdx.x] = x;
+      pdg = x;
     }
+    ptile = tile;
     lds_barrier();
   }
+  if (ptile >= 0 && threadIdx.x < C) wdg1[(size_t)ptile * C + threadIdx.x] = pdg;
 #undef LRT_G1_LOAD
 }
 
@@ -589,13 +609,13 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
     const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                                   \
     const int lh = lbh % H;                                                                       \
     if ((PART_) & 1) {                                                                            \
-      tk.load_rows(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                                \
+      tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                        \
       const int tc = min((int)threadIdx.x, C - 1);                                                \
       rg = wG[(size_t)(tile_) * C + tc];                                                          \
       rb = beta[(ltok + min(tc, lnv - 1)) * H + lh];                                              \
       rd = wdg1[(size_t)(tile_) * C + tc];                                                        \
     }                                                                                             \
-    if ((PART_) & 2) tv.load_rows(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                 \
+    if ((PART_) & 2) tv.load_rows_clamped(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv);         \
     if ((PART_) & 4) {                                                                            \
       tt.load_block(wT + (size_t)(tile_) * C * C);                                                \
       tdu.load_block(wdU + (size_t)(tile_) * DV * C);                                             \
@@ -615,9 +635,11 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
     const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
     const int t0 = n * C, nv = min(C, T - t0);
     const size_t tok0 = (size_t)b * T + t0;
-    const int next = tile + (int)gridDim.x;
-    tk.store(sK, LK);
-    tv.store(sV, LV);
+    // the next chunk (the last one again on the final pass: its loads go
+    // unused, but unconditional loads keep the waits on older ones exact)
+    const int next = min(tile + (int)gridDim.x, ntiles - 1);
+    tk.store_masked(sK, LK, nv);
+    tv.store_masked(sV, LV, nv);
     tt.store(sT, LC);
     tdu.store(sdUt, LC);
     tdw.store(sdW, LK);
@@ -643,7 +665,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
       }
     }
     lds_barrier();
-    if (next < ntiles) LRT_G2_LOAD(next, 1)
+    LRT_G2_LOAD(next, 1)
     // dX^T = dW^T Tinv (rows d, cols j): dK += b gamma dX, cx_j = dX_j . k_j
     // (a wave's tiles all lie in column block w % NB, so each wave reduces
     // its column sums once, after its tiles)
@@ -689,7 +711,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
     lds_barrier();
     lds_to_rows<E, C, DV, NT>(dv + (tok0 * H + h) * DV, (size_t)H * DV, sdV, LV, nv);
     lds_barrier();
-    if (next < ntiles) LRT_G2_LOAD(next, 2)
+    LRT_G2_LOAD(next, 2)
     // dT = (dW K^T) diag(b gamma) + (dU V^T) diag(b)   (rows i, cols j) -> dT^T [j][i]
 #pragma unroll
     for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
@@ -703,7 +725,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
       store4<E>(sdTt + j * LC + i0, sb[j] * (__expf(sg[j]) * z1 + z2));
     }
     lds_barrier();
-    if (next < ntiles) LRT_G2_LOAD(next, 4)
+    LRT_G2_LOAD(next, 4)
     // R = dT Tinv^T (rows i, cols k) -> R^T [k][i]
 #pragma unroll
     for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
@@ -715,7 +737,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
       store4<E>(sRt + (tk2 * 16 + (l & 15)) * LC + ti * 16 + (l >> 4) * 4, acc);
     }
     lds_barrier();
-    if (next < ntiles) LRT_G2_LOAD(next, 8)
+    LRT_G2_LOAD(next, 8)
     // dA = -strict_lower(Tinv^T R); with A = b_i (K K^T) o Gamma:
     //   M = dA o b_i Gamma -> M^T [k][i], dbeta_i += sum_k dA o Gamma o KK^T, E = dA o A -> dg
     float ecol = 0.f;  // column kk = jw for every tile of this wave
@@ -754,7 +776,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
     ecol = sum4(ecol);
     if (l < 16) atomicAdd(&sdg[jw], -ecol);
     lds_barrier();
-    if (next < ntiles) LRT_G2_LOAD(next, 16)
+    LRT_G2_LOAD(next, 16)
     // dK^T += K^T M (cols j: sum_i k_i M_ij) + K^T M^T (cols i: sum_j k_j M_ij)
 #pragma unroll
     for (int s = 0; s < KPW; ++s) {

@@ -253,9 +253,33 @@ struct Tile {
     for (int s = 0; s < PT; ++s) {
       const int idx = threadIdx.x + NT * s;
       x[s] = u32x4{0u, 0u, 0u, 0u};
-      if (idx < NP) {
+      if (NP % NT == 0 || idx < NP) {
         const int r = idx / PR, c = (idx % PR) * V;
         if (r < nvalid) x[s] = *(const u32x4*)(g + (size_t)r * gs + c);
+      }
+    }
+  }
+  // as load_rows, but every lane loads (rows >= nvalid repeat row
+  // nvalid - 1, nvalid >= 1): no branch around the loads, so a later wait
+  // on an older load can count them; store_masked zeroes those rows
+  __device__ __forceinline__ void load_rows_clamped(const E* g, size_t gs, int nvalid) {
+#pragma unroll
+    for (int s = 0; s < PT; ++s) {
+      const int idx = threadIdx.x + NT * s;
+      if (NP % NT == 0 || idx < NP) {
+        const int r = idx / PR, c = (idx % PR) * V;
+        x[s] = *(const u32x4*)(g + (size_t)min(r, nvalid - 1) * gs + c);
+      }
+    }
+  }
+  // lds[r * ls + c], rows >= nvalid as zero
+  __device__ __forceinline__ void store_masked(E* lds, int ls, int nvalid) const {
+#pragma unroll
+    for (int s = 0; s < PT; ++s) {
+      const int idx = threadIdx.x + NT * s;
+      if (NP % NT == 0 || idx < NP) {
+        const int r = idx / PR, c = (idx % PR) * V;
+        *(u32x4*)(lds + r * ls + c) = r < nvalid ? x[s] : u32x4{0u, 0u, 0u, 0u};
       }
     }
   }
@@ -264,14 +288,14 @@ struct Tile {
 #pragma unroll
     for (int s = 0; s < PT; ++s) {
       const int idx = threadIdx.x + NT * s;
-      if (idx < NP) x[s] = *(const u32x4*)(g + (size_t)idx * V);
+      if (NP % NT == 0 || idx < NP) x[s] = *(const u32x4*)(g + (size_t)idx * V);
     }
   }
   __device__ __forceinline__ void scale_rows(const float* rs) {
 #pragma unroll
     for (int s = 0; s < PT; ++s) {
       const int idx = threadIdx.x + NT * s;
-      if (idx < NP) x[s] = vec_scale<E>(x[s], rs[idx / PR]);
+      if (NP % NT == 0 || idx < NP) x[s] = vec_scale<E>(x[s], rs[idx / PR]);
     }
   }
   // lds[r * ls + c]
@@ -279,7 +303,7 @@ struct Tile {
 #pragma unroll
     for (int s = 0; s < PT; ++s) {
       const int idx = threadIdx.x + NT * s;
-      if (idx < NP) {
+      if (NP % NT == 0 || idx < NP) {
         const int r = idx / PR, c = (idx % PR) * V;
         *(u32x4*)(lds + r * ls + c) = x[s];
       }
@@ -290,7 +314,7 @@ struct Tile {
 #pragma unroll
     for (int s = 0; s < PT; ++s) {
       const int idx = threadIdx.x + NT * s;
-      if (idx < NP) {
+      if (NP % NT == 0 || idx < NP) {
         const int r = idx / PR, c = (idx % PR) * V;
         x[s] = *(const u32x4*)(lds + r * ls + c);
       }
@@ -301,7 +325,7 @@ struct Tile {
 #pragma unroll
     for (int s = 0; s < PT; ++s) {
       const int idx = threadIdx.x + NT * s;
-      if (idx < NP) {
+      if (NP % NT == 0 || idx < NP) {
         const int r = idx / PR, c = (idx % PR) * V;
         if (r < nvalid) *(u32x4*)(g + (size_t)r * gs + c) = x[s];
       }
@@ -312,7 +336,7 @@ struct Tile {
 #pragma unroll
     for (int s = 0; s < PT; ++s) {
       const int idx = threadIdx.x + NT * s;
-      if (idx < NP) {
+      if (NP % NT == 0 || idx < NP) {
         const int r = idx / PR, c = (idx % PR) * V;
         vec_to_lds_T<E>(lds, ld, r, c, x[s]);
       }
