@@ -199,27 +199,37 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
   Tile<E, C, BV, NT> tO;
   typename Vec4<E>::T rU[UPW];  // packed: unpacked where used, so the fetch does not wait
   float rg = 0.f;
-#define LRT_DSTATE_FETCH(n_)                                                                        \
+  // The previous chunk's operands, fetched in two parts while this chunk
+  // runs (the registers of each part are free once stored or scaled), with
+  // clamped rows and chunk index so no load sits behind a branch.
+#define LRT_DSTATE_FETCH(n_, PART_)                                                                 \
   {                                                                                                 \
     const size_t ft = (size_t)bh * N + (n_);                                                        \
     const int fnv = min(C, T - (n_) * C);                                                           \
     const size_t ftok = (size_t)b * T + (size_t)(n_) * C;                                           \
-    tQ.load_rows(q + (ftok * H + h) * DK, (size_t)H * DK, fnv);                                     \
-    tK.load_rows(k + (ftok * H + h) * DK, (size_t)H * DK, fnv);                                     \
-    tW.load_block(wW + ft * C * DK);                                                                \
-    tO.load_rows(d_o + (ftok * H + h) * DV + v0, (size_t)H * DV, fnv);                              \
-    _Pragma("unroll") for (int s = 0; s < UPW; ++s) {                                               \
-      const int tt = min(w + NW * s, NU - 1);                                                       \
-      rU[s] = load4_raw<E>(wdUl + ft * DV * C + (size_t)(v0 + (tt % NTV) * 16 + (l & 15)) * C +    \
-                           (tt / NTV) * 16 + (l >> 4) * 4);                                         \
+    if ((PART_) & 1) {                                                                              \
+      tQ.load_rows_clamped(q + (ftok * H + h) * DK, (size_t)H * DK, fnv);                           \
+      tW.load_block(wW + ft * C * DK);                                                              \
+      _Pragma("unroll") for (int s = 0; s < UPW; ++s) {                                             \
+        const int tt = min(w + NW * s, NU - 1);                                                     \
+        rU[s] = load4_raw<E>(wdUl + ft * DV * C + (size_t)(v0 + (tt % NTV) * 16 + (l & 15)) * C +  \
+                             (tt / NTV) * 16 + (l >> 4) * 4);                                       \
+      }                                                                                             \
+      rg = wG[ft * C + min((int)threadIdx.x, C - 1)];                                               \
     }                                                                                               \
-    rg = wG[ft * C + min((int)threadIdx.x, C - 1)];                                                 \
+    if ((PART_) & 2) {                                                                              \
+      tK.load_rows_clamped(k + (ftok * H + h) * DK, (size_t)H * DK, fnv);                           \
+      tO.load_rows_clamped(d_o + (ftok * H + h) * DV + v0, (size_t)H * DV, fnv);                    \
+    }                                                                                               \
   }
 
-  LRT_DSTATE_FETCH(N - 1)
+  LRT_DSTATE_FETCH(N - 1, 3)
   for (int n = N - 1; n >= 0; --n) {
     const size_t tile = (size_t)bh * N + n;
+    const int nv = min(C, T - n * C);
+    const int nprev = n > 0 ? n - 1 : 0;
     // gates: g, e^(g_C - g_t), gamma_t (wave 0 holds g of this chunk, one token per lane)
+    asm volatile("" ::"v"(rg));
     if (threadIdx.x < 64) {
       const float gC = __shfl(rg, C - 1, 64);
       if (threadIdx.x < C) {
@@ -237,20 +247,21 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
         store4<E>(sdS + (tv * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, hacc[s]);
       }
     }
-    tQ.store(sQ, LK);
+    tQ.store_masked(sQ, LK, nv);
     tW.store(sW, LK);
     f32x4 du[UPW];
 #pragma unroll
     for (int s = 0; s < UPW; ++s) du[s] = Vec4<E>::unpack(rU[s]);
     lds_barrier();
+    LRT_DSTATE_FETCH(nprev, 1)
     lds_to_block<E, BV, DK, NT>(wdS + (tile * DV + v0) * DK, sdS, LK);
     tK.scale_rows(sgs);
-    tK.store(sKt, LK);
+    tK.store_masked(sKt, LK, nv);
     tO.scale_rows(sgs + C);
-    tO.store(sOg, LB);
-    if (n > 0) LRT_DSTATE_FETCH(n - 1)
+    tO.store_masked(sOg, LB, nv);
     const float dec = __expf(sg[C - 1]);
     lds_barrier();
+    LRT_DSTATE_FETCH(nprev, 2)
     // dU = dU_local + Ktil dH'  (rows t, cols v) -> dU^T
 #pragma unroll
     for (int s = 0; s < UPW; ++s) {

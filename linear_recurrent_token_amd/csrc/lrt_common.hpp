@@ -352,7 +352,7 @@ __device__ __forceinline__ void lds_to_block(E* g, const E* lds, int ls) {
 #pragma unroll
   for (int s = 0; s < (R * PR + NT - 1) / NT; ++s) {
     const int idx = threadIdx.x + NT * s;
-    if (idx < R * PR) {
+    if ((R * PR) % NT == 0 || idx < R * PR) {
       const int r = idx / PR, c = (idx % PR) * V;
       *(u32x4*)(g + (size_t)r * W + c) = *(const u32x4*)(lds + r * ls + c);
     }
@@ -403,7 +403,7 @@ __device__ __forceinline__ void lds_to_rows(E* g, size_t gs, const E* lds, int l
 #pragma unroll
   for (int s = 0; s < (R * PR + NT - 1) / NT; ++s) {
     const int idx = threadIdx.x + NT * s;
-    if (idx < R * PR) {
+    if ((R * PR) % NT == 0 || idx < R * PR) {
       const int r = idx / PR, c = (idx % PR) * V;
       if (r < nvalid) *(u32x4*)(g + (size_t)r * gs + c) = *(const u32x4*)(lds + r * ls + c);
     }
