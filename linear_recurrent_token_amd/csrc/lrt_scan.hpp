@@ -71,26 +71,31 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
   Tile<E, C, DK, NT> tk, tq;
   Tile<E, C, DV, NT> tv;
   float la = 0.f, bt = 0.f;
-#define LRT_WY_LOAD(tile_)                                                                \
+  // The next chunk's operands, in parts (bit mask PART_) spread over this
+  // chunk's phases; rows and chunk index clamped so no load sits behind a
+  // branch (rows past the end are masked where staged).
+#define LRT_WY_LOAD(tile_, PART_)                                                         \
   {                                                                                       \
     const int ln = (tile_) % N, lbh = (tile_) / N;                                        \
     const int lnv = min(C, T - ln * C);                                                   \
     const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                           \
     const int lh = lbh % H;                                                               \
-    tk.load_rows(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
-    if (WRITE_P) tq.load_rows(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);             \
-    tv.load_rows(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                          \
-    {                                                                                     \
+    if ((PART_) & 1) {                                                                    \
+      tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                \
       const int tc = min((int)threadIdx.x, lnv - 1); /* masked where used */              \
       la = log_a[(ltok + tc) * H + lh];                                                   \
       bt = beta[(ltok + tc) * H + lh];                                                    \
     }                                                                                     \
+    if (WRITE_P && ((PART_) & 2)) tq.load_rows_clamped(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv); \
+    if ((PART_) & 4) tv.load_rows_clamped(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv); \
   }
 
   int tile = blockIdx.x;
-  if (tile < ntiles) LRT_WY_LOAD(tile)
+  if (tile < ntiles) LRT_WY_LOAD(tile, 7)
   for (; tile < ntiles; tile += gridDim.x) {
     const int nv = min(C, T - (tile % N) * C);
+    const int next = min(tile + (int)gridDim.x, ntiles - 1);
+    asm volatile("" ::"v"(la), "v"(bt));
     if (threadIdx.x < 64) {
       const bool valid = (int)threadIdx.x < nv;
       const float g = wave_incl_scan(valid ? la : 0.f);
@@ -105,12 +110,12 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
         wG[(size_t)tile * C + t] = g;
       }
     }
-    tk.store(sK, LK);
-    if constexpr (WRITE_P) tq.store(sQ, LK);
+    tk.store_masked(sK, LK, nv);
+    if constexpr (WRITE_P) tq.store_masked(sQ, LK, nv);
     lds_barrier();
+    LRT_WY_LOAD(next, 1)
     tv.scale_rows(sb);
-    tv.store(sV, LV);
-    if (tile + (int)gridDim.x < ntiles) LRT_WY_LOAD(tile + (int)gridDim.x)
+    tv.store_masked(sV, LV, nv);
     // A (lower tiles; the solve reads nothing above the diagonal) and P^T
     // tiles, P^T[j][i] = (k_j . q_i) e^(g_i - g_j) for j <= i, stored as rows of P
     constexpr int NA = NB * (NB + 1) / 2;
@@ -141,7 +146,9 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
       }
     }
     lds_barrier();
+    LRT_WY_LOAD(next, 4)
     unit_lower_inverse<C, NT>(sA);
+    LRT_WY_LOAD(next, 2)
     for (int idx = threadIdx.x; idx < C * C; idx += NT) {
       const int j = idx / C, i = idx % C;
       const float x = j <= i ? sA[j * LA + i] : 0.f;
@@ -153,7 +160,13 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
     // W^T = K^T (T diag(b gamma))^T (rows d, cols t): a lane's 4 values are
     // 4 consecutive d of one row of W; U' = T (b V) (rows t, cols v): 4
     // consecutive t of one row of U'^T
-    for (int tt = w; tt < NWT + NUT; tt += NW) {
+    // unrolled (a known store count keeps the next chunk's wait exact) where
+    // the registers allow
+    constexpr int UWU = WRITE_P ? 1 : (NWT + NUT + NW - 1) / NW;
+#pragma unroll UWU
+    for (int s2 = 0; s2 < (NWT + NUT + NW - 1) / NW; ++s2) {
+      const int tt = w + NW * s2;
+      if (tt >= NWT + NUT) break;
       f32x4 acc = zero4();
       if (tt < NWT) {
         const int td = tt / NB, ti = tt % NB;
