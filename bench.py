@@ -30,12 +30,14 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 MFMA_FP32_PEAK_TFLOPS = 157.3
 WORKLOAD = "gdn_train_bf16_2k"  # the headline workload (default)
-# other named workloads bench.py can time (forward passes; not the headline)
+# other named workloads bench.py can time (context lines; not the headline)
 WORKLOADS = {
     "gdn_train_bf16_2k": ("GDN chunked fwd+bwd tokens/s and % bf16 MFMA peak, B=16 T=2048 H=8 d=128",
                           "gdn_fwd + gdn_bwd"),
     "gdn_bf16_2k": ("GDN chunked fwd tokens/s, B=16 T=2048 H=8 d=128", "gdn_fwd"),
     "ssd_bf16_2k": ("SSD (Mamba2 case) chunked fwd tokens/s, B=16 T=2048 H=8 d=128", "ssd_fwd"),
+    "ssd_train_bf16_2k": ("SSD (Mamba2 case) chunked fwd+bwd tokens/s, B=16 T=2048 H=8 d=128",
+                          "ssd_fwd + ssd_bwd"),
     "kda_bf16_1m": ("KDA chunked fwd tokens/s, B=1 T=2^20 H=16 d=128", "kda_fwd"),
 }
 
@@ -129,6 +131,21 @@ def kernel_model(name, c, esz=2, op="gdn_fwd + gdn_bwd"):
         "k_grad2": ((dk + dv) * e + 8 + C * e + dk * e + dv * e + dk * e + 4 + (dk + dv) * e + 8, 0,
                     2 * C * dk + 2 * C * dv + 2 * C * dk + 2 * C * dv + 4 * C * C + 2 * C * dk + 4 * C * dk),
     }
+    if op.startswith("ssd"):
+        # the fused Mamba2 forward: reads q, k, v, log_a, h0; writes o, ht
+        per["k_fwd"] = ((2 * dk + dv) * e + 4 + dv * e, 2 * st, 2 * C * (dk + dv) + 4 * dk * dv)
+    if op == "ssd_fwd + ssd_bwd":
+        per.update({
+            # reads v, log_a; writes g, V^T
+            "k_ssd_prep": (dv * e + 4 + 4 + dv * e, 0, 0),
+            # reads k, V^T, g, h0; writes the chunk-start states
+            "k_scan_bwd": (dk * e + dv * e + 4 + dk * dv * e / C, st, 2 * dk * dv),
+            # reads q, k, do, g, dU_local, dht; writes dU (= dv), the end-state gradients, dh0
+            "k_dstate": (2 * dk * e + dv * e + 4 + dv * e + dv * e + dk * dv * e / C, 2 * st, 4 * dk * dv),
+            # reads q, k, do, g, states, state gradients, V^T, dU; writes dq, dk, dv, dlog_a
+            "k_grad1": (2 * dk * e + dv * e + 4 + 2 * dk * dv * e / C + 2 * dv * e + 2 * dk * e + dv * e + 4, 0,
+                        6 * C * dk + 2 * C * dv + 4 * dk * dv),
+        })
     if op == "kda_fwd":
         per.update({
             # reads q, k, v, per-dim log_a, beta; writes W, U'^T, Ktil^T, chunk decay, Q o e^G, P
@@ -217,24 +234,26 @@ def main():
     sets = make_sets(L, synth, torch, wl, nsets)
     code = L.LRT_BF16
     opc = {"gdn_fwd + gdn_bwd": L.OP_GDN_BWD, "gdn_fwd": L.OP_GDN_FWD, "ssd_fwd": L.OP_SSD_FWD,
-           "kda_fwd": L.OP_KDA_FWD}[op]
+           "ssd_fwd + ssd_bwd": L.OP_SSD_BWD, "kda_fwd": L.OP_KDA_FWD}[op]
     ws_bytes = max(L.workspace_bytes(L.OP_GDN_FWD, B, T, H, dk, dv, C, code),
                    L.workspace_bytes(opc, B, T, H, dk, dv, C, code))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
     ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     grads = None
-    if op == "gdn_fwd + gdn_bwd":
+    if op.endswith("_bwd"):
         grads = (torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
                  torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
                  torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev),
                  torch.empty((B, T, H), dtype=torch.float32, device=dev),
                  torch.empty((B, T, H), dtype=torch.float32, device=dev),
                  torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev))
+        if op.startswith("ssd"):
+            grads = grads[:4] + grads[5:]
 
     def step(i):
         s = sets[i % len(sets)]
-        if op == "ssd_fwd":
+        if op.startswith("ssd"):
             L.ssd_fwd(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), chunk=C, o=o, ht=ht, workspace=ws)
         elif op == "kda_fwd":
             L.kda_fwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), chunk=C, o=o, ht=ht,
@@ -242,7 +261,10 @@ def main():
         else:
             L.gdn_fwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), chunk=C, o=o, ht=ht,
                       workspace=ws)
-        if grads is not None:
+        if grads is not None and op.startswith("ssd"):
+            L.ssd_bwd(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), s["do"], s.get("dht"), chunk=C, workspace=ws,
+                      out=grads)
+        elif grads is not None:
             L.gdn_bwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), s["do"], s.get("dht"),
                       chunk=C, workspace=ws, out=grads)
 
@@ -311,9 +333,14 @@ def main():
             k["tflops_algorithmic"] = m[1] / (k["avg_us"] / 1e6) / 1e12
 
     # algorithmic step totals: GEMM flops of the method (forward, + backward)
-    per_th = {"ssd_fwd": 2 * C * (dk + dv) + 4 * dk * dv}.get(op, 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv)
-    if grads is not None:
-        per_th += 12 * C * dk + 8 * C * dv + 12 * dk * dv + 4 * C * C
+    if op.startswith("ssd"):
+        per_th = 2 * C * (dk + dv) + 4 * dk * dv
+        if grads is not None:  # Mamba2 backward: 8 GEMM products, state recompute excluded
+            per_th += 4 * C * dk + 4 * C * dv + 8 * dk * dv
+    else:
+        per_th = 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv
+        if grads is not None:
+            per_th += 12 * C * dk + 8 * C * dv + 12 * dk * dv + 4 * C * C
     step_tflops = per_th * B * T * H / (ms_per_step / 1e3) / 1e12
 
     cpu = None

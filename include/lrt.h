@@ -4,7 +4,7 @@
  * The mixers are the linear-recurrent "M" layers of the hybrid stacks in the
  * AMD ROCm blog "Pretraining hybrid LLMs with Primus" (section "How hybrid
  * models are defined in Primus", mixer list under Table 2):
- *   - Mamba2 (ssd_fwd): the state is decayed by one scalar gate per head and a
+ *   - Mamba2 (ssd_fwd, ssd_bwd): the state is decayed by one scalar gate per head and a
  *     rank-one k v^T write is added each token;
  *   - Gated DeltaNet (gdn_fwd, gdn_bwd): Mamba2 plus the delta rule, which
  *     replaces the value stored under the current key instead of only adding;
@@ -32,7 +32,7 @@
  * Supported: B, H >= 1; T >= 0; d_k, d_v in {16, 32, 64, 128};
  * chunk in {16, 32, 64}; B * T and B * H * ceil(T / chunk) * d_v / 16 at
  * most 2^31 - 1.  T need not be a multiple of chunk.  The fp32
- * backward (gdn_bwd with LRT_F32) is limited to d_k, d_v <= 64 and
+ * backward (gdn_bwd or ssd_bwd with LRT_F32) is limited to d_k, d_v <= 64 and
  * chunk <= 32 (LRT_ERR_SHAPE / LRT_ERR_CHUNK otherwise).
  *
  * Ownership and execution: the caller allocates and frees every buffer,
@@ -78,6 +78,7 @@ extern "C" {
 #define LRT_OP_GDN_BWD 1
 #define LRT_OP_KDA_FWD 2
 #define LRT_OP_SSD_FWD 3
+#define LRT_OP_SSD_BWD 4
 
 /*
  * Gated DeltaNet forward.  Writes o and (if not NULL) ht.
@@ -113,6 +114,20 @@ int kda_fwd(const void* q, const void* k, const void* v, const float* log_a, con
 int ssd_fwd(const void* q, const void* k, const void* v, const float* log_a, const float* h0,
             void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk, int dtype,
             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Mamba2 / SSD backward: gradients of L = <do, o> + <dht, ht> with respect to
+ * q, k, v, log_a and h0 for ssd_fwd of the same arguments (the scalar-decay
+ * recurrence of the Mamba2 mixer on the AMD ROCm blog "Pretraining hybrid
+ * LLMs with Primus", section "How hybrid models are defined in Primus",
+ * mixer list under Table 2).  As gdn_bwd without beta and dbeta: the forward
+ * is recomputed internally; dht may be NULL (zero); dh0 may be NULL (not
+ * written); dq, dk, dv and dlog_a are required.  Workspace: LRT_OP_SSD_BWD.
+ */
+int ssd_bwd(const void* q, const void* k, const void* v, const float* log_a, const float* h0,
+            const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dlog_a, float* dh0,
+            int B, int T, int H, int d_k, int d_v, int chunk, int dtype, void* workspace,
+            size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes needed by `op` (LRT_OP_*) at these sizes.  Returns

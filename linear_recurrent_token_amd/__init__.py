@@ -11,6 +11,7 @@ Entry points (names as in include/lrt.h):
   gdn_bwd(q, k, v, log_a, beta, h0, do, dht=None, chunk=64)   -> (dq, dk, dv, dlog_a, dbeta, dh0)
   kda_fwd(q, k, v, log_a, beta, h0=None, chunk=64)            -> (o, ht)
   ssd_fwd(q, k, v, log_a, h0=None, chunk=64)                   -> (o, ht)
+  ssd_bwd(q, k, v, log_a, h0, do, dht=None, chunk=64)          -> (dq, dk, dv, dlog_a, dh0)
 Layouts: q, k [B,T,H,d_k], v [B,T,H,d_v] (fp32 or bf16); log_a, beta fp32
 [B,T,H] (KDA log_a [B,T,H,d_k]); states fp32 [B,H,d_k,d_v].
 """
@@ -23,8 +24,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblrt.so")
 
 LRT_F32, LRT_BF16 = 0, 1
-OP_GDN_FWD, OP_GDN_BWD, OP_KDA_FWD, OP_SSD_FWD = 0, 1, 2, 3
-EXPORTS = ("gdn_fwd", "gdn_bwd", "kda_fwd", "ssd_fwd", "lrt_workspace_bytes", "lrt_status_string",
+OP_GDN_FWD, OP_GDN_BWD, OP_KDA_FWD, OP_SSD_FWD, OP_SSD_BWD = 0, 1, 2, 3, 4
+EXPORTS = ("gdn_fwd", "gdn_bwd", "kda_fwd", "ssd_fwd", "ssd_bwd", "lrt_workspace_bytes", "lrt_status_string",
            "lrt_profile_attach", "lrt_profile_count", "lrt_kernel_name")
 
 _lib = None
@@ -49,7 +50,8 @@ def lib():
         L.kda_fwd.argtypes = [vp] * 8 + [ci] * 7 + [vp, sz, vp]
         L.ssd_fwd.argtypes = [vp] * 7 + [ci] * 7 + [vp, sz, vp]
         L.gdn_bwd.argtypes = [vp] * 14 + [ci] * 7 + [vp, sz, vp]
-        for f in ("gdn_fwd", "kda_fwd", "ssd_fwd", "gdn_bwd"):
+        L.ssd_bwd.argtypes = [vp] * 12 + [ci] * 7 + [vp, sz, vp]
+        for f in ("gdn_fwd", "kda_fwd", "ssd_fwd", "gdn_bwd", "ssd_bwd"):
             getattr(L, f).restype = ci
         L.lrt_workspace_bytes.argtypes = [ci] * 8
         L.lrt_workspace_bytes.restype = sz
@@ -167,6 +169,18 @@ def ssd_fwd(q, k, v, log_a, h0=None, chunk=64, o=None, ht=True, workspace=None):
 
 def gdn_bwd(q, k, v, log_a, beta, h0, do, dht=None, chunk=64, want_dh0=True, workspace=None, out=None):
     """Gated DeltaNet backward -> (dq, dk, dv, dlog_a, dbeta, dh0 or None)."""
+    return _bwd(True, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, workspace, out)
+
+
+def ssd_bwd(q, k, v, log_a, h0, do, dht=None, chunk=64, want_dh0=True, workspace=None, out=None):
+    """Mamba2 / SSD backward -> (dq, dk, dv, dlog_a, dh0 or None)."""
+    if out is not None:
+        out = tuple(out[:4]) + (None,) + tuple(out[4:])
+    g = _bwd(False, q, k, v, log_a, None, h0, do, dht, chunk, want_dh0, workspace, out)
+    return g[:4] + g[5:]
+
+
+def _bwd(delta, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, workspace, out):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -174,7 +188,7 @@ def gdn_bwd(q, k, v, log_a, beta, h0, do, dht=None, chunk=64, want_dh0=True, wor
         raise ValueError("inputs must be on a GPU device")
     for name, t, shp, ty in (("k", k, (B, T, H, dk), dt), ("v", v, (B, T, H, dv), dt),
                              ("log_a", log_a, (B, T, H), torch.float32),
-                             ("beta", beta, (B, T, H), torch.float32),
+                             ("beta", beta if delta else None, (B, T, H), torch.float32),
                              ("h0", h0, (B, H, dk, dv), torch.float32),
                              ("do", do, (B, T, H, dv), dt), ("dht", dht, (B, H, dk, dv), torch.float32)):
         _check(dev, dt, name, t, shp, ty)
@@ -182,15 +196,20 @@ def gdn_bwd(q, k, v, log_a, beta, h0, do, dht=None, chunk=64, want_dh0=True, wor
     if out is None:
         out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
                torch.empty((B, T, H), dtype=torch.float32, device=dev),
-               torch.empty((B, T, H), dtype=torch.float32, device=dev),
+               torch.empty((B, T, H), dtype=torch.float32, device=dev) if delta else None,
                torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dh0 else None)
     gq, gk, gv, gla, gb, gh0 = out
     code = _dtype_code(q)
-    ws, need = _workspace(OP_GDN_BWD, dev, B, T, H, dk, dv, chunk, code, workspace)
+    op = OP_GDN_BWD if delta else OP_SSD_BWD
+    ws, need = _workspace(op, dev, B, T, H, dk, dv, chunk, code, workspace)
     with torch.cuda.device(dev):
-        rc = lib().gdn_bwd(_p(q), _p(k), _p(v), _p(log_a), _p(beta), _p(h0), _p(do), _p(dht), _p(gq), _p(gk),
-                           _p(gv), _p(gla), _p(gb), _p(gh0), B, T, H, dk, dv, chunk, code, _p(ws), need,
-                           _stream(dev))
+        if delta:
+            rc = lib().gdn_bwd(_p(q), _p(k), _p(v), _p(log_a), _p(beta), _p(h0), _p(do), _p(dht), _p(gq), _p(gk),
+                               _p(gv), _p(gla), _p(gb), _p(gh0), B, T, H, dk, dv, chunk, code, _p(ws), need,
+                               _stream(dev))
+        else:
+            rc = lib().ssd_bwd(_p(q), _p(k), _p(v), _p(log_a), _p(h0), _p(do), _p(dht), _p(gq), _p(gk), _p(gv),
+                               _p(gla), _p(gh0), B, T, H, dk, dv, chunk, code, _p(ws), need, _stream(dev))
     if rc != 0:
-        raise LrtError("gdn_bwd", rc)
+        raise LrtError("gdn_bwd" if delta else "ssd_bwd", rc)
     return gq, gk, gv, gla, gb, gh0

@@ -32,7 +32,7 @@ void prof_after(void* stream) {
 
 static const char* const kKernelNames[kKNumKinds] = {"k_prep",  "k_state", "k_out",     "k_bwd_local",
                                                      "k_dstate", "k_grad1", "k_grad2",   "k_kda_prep",
-                                                     "k_state_copy", "k_fwd", "k_wy", "k_scan", "k_wy_bwd", "k_scan_bwd", "k_scan_local", "k_carry"};
+                                                     "k_state_copy", "k_fwd", "k_wy", "k_scan", "k_wy_bwd", "k_scan_bwd", "k_scan_local", "k_carry", "k_ssd_prep"};
 
 int device_cu_count() {
   static int cached[64] = {0};
@@ -70,7 +70,7 @@ static size_t ws_bytes(int op, int B, int T, int H, int dk, int dv, int chunk, i
   const size_t esz = dtype == LRT_BF16 ? 2 : 4;
   const bool kda = op == LRT_OP_KDA_FWD;
   size_t b = fwd_ws_layout(B, T, H, dk, dv, chunk, esz, nullptr, kda).bytes;
-  if (op == LRT_OP_GDN_BWD) b += bwd_ws_extra(B, T, H, dk, dv, chunk, esz);
+  if (op == LRT_OP_GDN_BWD || op == LRT_OP_SSD_BWD) b += bwd_ws_extra(B, T, H, dk, dv, chunk, esz);
   return b < 256 ? 256 : b;
 }
 
@@ -104,6 +104,30 @@ static int fwd_entry(int variant, const void* q, const void* k, const void* v, c
   return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : LRT_ERR_SHAPE);
 }
 
+static int bwd_entry(int variant, const void* q, const void* k, const void* v, const float* log_a,
+                     const float* beta, const float* h0, const void* d_o, const float* dht, void* dq, void* dk,
+                     void* dv, float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v,
+                     int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(B, T, H, d_k, d_v, chunk, dtype);
+  if (rc) return rc;
+  const bool delta = variant == kVarGDN;
+  if (T > 0 && (!q || !k || !v || !log_a || !d_o || !dq || !dk || !dv || !dlog_a || (delta && (!beta || !dbeta))))
+    return LRT_ERR_NULL;
+  const void* vec[] = {q, k, v, d_o, dq, dk, dv, workspace};
+  for (const void* p : vec)
+    if (p && !aligned(p)) return LRT_ERR_ALIGN;
+  const void* sca[] = {log_a, beta, h0, dht, dlog_a, dbeta, dh0};
+  for (const void* p : sca)
+    if (p && !aligned4(p)) return LRT_ERR_ALIGN;
+  const int op = delta ? LRT_OP_GDN_BWD : LRT_OP_SSD_BWD;
+  if (!workspace || workspace_bytes < ws_bytes(op, B, T, H, d_k, d_v, chunk, dtype)) return LRT_ERR_WORKSPACE;
+  if (T == 0) return launch_empty(dht, dh0, B, H, d_k, d_v, stream);
+  BwdArgs a{q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0,
+            B, T, H, d_k, d_v, chunk, dtype, workspace, stream};
+  rc = delta ? bwd_gdn(a) : bwd_ssd(a);
+  return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
+}
+
 }  // namespace lrt
 
 using namespace lrt;
@@ -135,31 +159,22 @@ int gdn_bwd(const void* q, const void* k, const void* v, const float* log_a, con
             const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv,
             float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v, int chunk,
             int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_common(B, T, H, d_k, d_v, chunk, dtype);
-  if (rc) return rc;
-  if (T > 0 && (!q || !k || !v || !log_a || !beta || !d_o || !dq || !dk || !dv || !dlog_a || !dbeta))
-    return LRT_ERR_NULL;
-  const void* vec[] = {q, k, v, d_o, dq, dk, dv, workspace};
-  for (const void* p : vec)
-    if (p && !aligned(p)) return LRT_ERR_ALIGN;
-  const void* sca[] = {log_a, beta, h0, dht, dlog_a, dbeta, dh0};
-  for (const void* p : sca)
-    if (p && !aligned4(p)) return LRT_ERR_ALIGN;
-  if (!workspace || workspace_bytes < ws_bytes(LRT_OP_GDN_BWD, B, T, H, d_k, d_v, chunk, dtype))
-    return LRT_ERR_WORKSPACE;
-  if (T == 0) return launch_empty(dht, dh0, B, H, d_k, d_v, stream);
-  BwdArgs a{q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0,
-            B, T, H, d_k, d_v, chunk, dtype, workspace, stream};
-  rc = bwd_gdn(a);
-  return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
+  return bwd_entry(kVarGDN, q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0, B, T, H, d_k, d_v,
+                   chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+int ssd_bwd(const void* q, const void* k, const void* v, const float* log_a, const float* h0, const void* d_o,
+            const float* dht, void* dq, void* dk, void* dv, float* dlog_a, float* dh0, int B, int T, int H,
+            int d_k, int d_v, int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_entry(kVarSSD, q, k, v, log_a, nullptr, h0, d_o, dht, dq, dk, dv, dlog_a, nullptr, dh0, B, T, H, d_k,
+                   d_v, chunk, dtype, workspace, workspace_bytes, stream);
 }
 
 size_t lrt_workspace_bytes(int op, int B, int T, int H, int d_k, int d_v, int chunk, int dtype) {
-  if (op < LRT_OP_GDN_FWD || op > LRT_OP_SSD_FWD) return (size_t)-1;
+  if (op < LRT_OP_GDN_FWD || op > LRT_OP_SSD_BWD) return (size_t)-1;
   if (check_common(B, T, H, d_k, d_v, chunk, dtype) != LRT_OK) return (size_t)-1;
   return ws_bytes(op, B, T, H, d_k, d_v, chunk, dtype);
 }
-
 int lrt_profile_attach(void** events, int* kinds, int n_kernels) {
   if (events == nullptr || kinds == nullptr || n_kernels <= 0) {
     g_prof.ev = nullptr;

@@ -155,7 +155,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q,
 // waves.  q, W and Ktil stay row-major in LDS; the products contracting over
 // tokens read them with the LDS transpose read, so nothing is transposed by
 // hand.  dH' and dU leave through LDS as coalesced 16-byte rows.
-template <typename E, int C, int DK, int BV, int NW = 8>
+// DELTA = false is the Mamba2 recurrence (W = 0): dH <- gamma_C dH' +
+// Q^T diag(gamma) dO, and dU is dV.
+template <typename E, int C, int DK, int BV, int NW = 8, bool DELTA = true>
 __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, const E* __restrict__ k,
                                                     const E* __restrict__ d_o, const float* __restrict__ wG,
                                                     const E* __restrict__ wW, const E* __restrict__ wdUl,
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
     const size_t ftok = (size_t)b * T + (size_t)(n_) * C;                                           \
     if ((PART_) & 1) {                                                                              \
       tQ.load_rows_clamped(q + (ftok * H + h) * DK, (size_t)H * DK, fnv);                           \
-      tW.load_block(wW + ft * C * DK);                                                              \
+      if constexpr (DELTA) tW.load_block(wW + ft * C * DK);                                         \
       _Pragma("unroll") for (int s = 0; s < UPW; ++s) {                                             \
         const int tt = min(w + NW * s, NU - 1);                                                     \
         rU[s] = load4_raw<E>(wdUl + ft * DV * C + (size_t)(v0 + (tt % NTV) * 16 + (l & 15)) * C +  \
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
       }
     }
     tQ.store_masked(sQ, LK, nv);
-    tW.store(sW, LK);
+    if constexpr (DELTA) tW.store(sW, LK);
     f32x4 du[UPW];
 #pragma unroll
     for (int s = 0; s < UPW; ++s) du[s] = Vec4<E>::unpack(rU[s]);
@@ -281,11 +283,13 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
       const int tt = w + NW * s;
       if (tt < NH) {
         const int td = tt / NTV, tv = tt % NTV;
-        f32x4 wdu = zero4();
         hacc[s] *= dec;
         mma<C, true, true>(hacc[s], sQ + td * 16, LK, sOg + tv * 16, LB);
-        mma<C, true, false>(wdu, sW + td * 16, LK, sdU + tv * 16 * LC, LC);
-        hacc[s] -= wdu;
+        if constexpr (DELTA) {
+          f32x4 wdu = zero4();
+          mma<C, true, false>(wdu, sW + td * 16, LK, sdU + tv * 16 * LC, LC);
+          hacc[s] -= wdu;
+        }
       }
     }
     lds_barrier();
@@ -329,13 +333,19 @@ struct Grad1Lds {
   static constexpr size_t TOTAL = DOT + 16;
 };
 
-template <typename E, int C, int DK, int DV, int NW = 8>
+// DELTA = false is the Mamba2 recurrence (U = V, no W): the dK and dg
+// computed here are then complete, and the kernel writes dk, dv (= dU, read
+// back from its LDS copy) and dlog_a (reverse cumsum of dg) itself; wdW,
+// wdK1 and wdg1 are unused.
+template <typename E, int C, int DK, int DV, int NW = 8, bool DELTA = true>
 __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, const E* __restrict__ k,
                                                     const E* __restrict__ d_o, const float* __restrict__ wG,
                                                     const E* __restrict__ wS, const E* __restrict__ wdS,
                                                     const E* __restrict__ wU, const E* __restrict__ wdU,
                                                     E* __restrict__ dq, E* __restrict__ wdW, E* __restrict__ wdK1,
-                                                    float* __restrict__ wdg1, int T, int H, int N, int ntiles) {
+                                                    float* __restrict__ wdg1, int T, int H, int N, int ntiles,
+                                                    E* __restrict__ dk_out, E* __restrict__ dv_out,
+                                                    float* __restrict__ dlog_a) {
   typedef Grad1Lds<E, C, DK, DV> Lay;
   constexpr int NT = 64 * NW;
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, NB = C / 16;
@@ -406,7 +416,8 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
       sdg[threadIdx.x] = 0.f;
     }
     if (threadIdx.x == 0) sdot[0] = 0.f;
-    if (ptile >= 0 && threadIdx.x < C) wdg1[(size_t)ptile * C + threadIdx.x] = pdg;
+    if constexpr (DELTA)
+      if (ptile >= 0 && threadIdx.x < C) wdg1[(size_t)ptile * C + threadIdx.x] = pdg;
     tdS.load_block(wdS + (size_t)tile * DV * DK);  // dH' of this chunk, needed after dS
     lds_barrier();
     LRT_G1_LOAD(next, 1)
@@ -482,9 +493,11 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
           acc *= gam;
           mma<C, true, true>(acc, sK + td * 16, LK, sdSj + ti * 16, LC);
           dqa[s] = acc;
-          f32x4 dw = zero4();
-          mma<DV, true, true>(dw, sS + td * 16, LK, sdUt + ti * 16, LC);
-          acc_tile_store<E>(wdW + (size_t)tile * C * DK, td * NB + ti, -dw);
+          if constexpr (DELTA) {
+            f32x4 dw = zero4();
+            mma<DV, true, true>(dw, sS + td * 16, LK, sdUt + ti * 16, LC);
+            acc_tile_store<E>(wdW + (size_t)tile * C * DK, td * NB + ti, -dw);
+          }
         }
       }
       esum = sum4(esum * gam);
@@ -507,6 +520,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
     // dK1^T = e^(g_C - g_j) (dH' U^T) + Q^T dS   (rows d, cols j); a wave's
     // tiles share their column block j
     const float gC = sg[C - 1];
+    f32x4 dka[KPW];
     {
       const int tj = w % NB, j = tj * 16 + (l & 15);
       const float kt = __expf(gC - sg[j]);
@@ -522,7 +536,10 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
           for (int r = 0; r < 4; ++r) ssum += acc[r] * to_f(sK[j * LK + d0 + r]);
           acc *= kt;
           mma<C, true, false>(acc, sQ + td * 16, LK, sdSj + tj * 16 * LC, LC);
-          acc_tile_store<E>(wdK1 + (size_t)tile * C * DK, td * NB + tj, acc);
+          if constexpr (DELTA)
+            acc_tile_store<E>(wdK1 + (size_t)tile * C * DK, td * NB + tj, acc);
+          else
+            dka[s] = acc;
         }
       }
       ssum = sum4(ssum * kt);
@@ -537,10 +554,38 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
       if (threadIdx.x == C - 1) x += __expf(gC) * sdot[0];
       pdg = x;
     }
+    if constexpr (!DELTA) {
+      // dk rows over the dead dq rows (copied out before the last barrier)
+#pragma unroll
+      for (int s = 0; s < KPW; ++s) {
+        const int td = w / NB + (NW / NB) * s, tj = w % NB;
+        if (td < DK / 16) store4<E>(sdQ + (tj * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, dka[s]);
+      }
+      // dv rows = dU^T read back column-wise from LDS
+      for (int idx = threadIdx.x; idx < C * (DV / V); idx += NT) {
+        const int t = idx / (DV / V), c0 = (idx % (DV / V)) * V;
+        if (t < nv) {
+          E x[V];
+#pragma unroll
+          for (int e = 0; e < V; ++e) x[e] = sdUt[(c0 + e) * LC + t];
+          u32x4 pk;
+          __builtin_memcpy(&pk, x, 16);
+          *(u32x4*)(dv_out + ((tok0 + t) * H + h) * DV + c0) = pk;
+        }
+      }
+      // dlog_a = reverse cumsum of dg within the chunk (wave 0, one token per lane)
+      if (threadIdx.x < 64) {
+        const float sfx = wave_incl_suffix(threadIdx.x < C ? pdg : 0.f);
+        if ((int)threadIdx.x < nv) dlog_a[(tok0 + threadIdx.x) * H + h] = sfx;
+      }
+      lds_barrier();
+      lds_to_rows<E, C, DK, NT>(dk_out + (tok0 * H + h) * DK, (size_t)H * DK, sdQ, LK, nv);
+    }
     ptile = tile;
     lds_barrier();
   }
-  if (ptile >= 0 && threadIdx.x < C) wdg1[(size_t)ptile * C + threadIdx.x] = pdg;
+  if constexpr (DELTA)
+    if (ptile >= 0 && threadIdx.x < C) wdg1[(size_t)ptile * C + threadIdx.x] = pdg;
 #undef LRT_G1_LOAD
 }
 
@@ -828,6 +873,35 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
 #undef LRT_G2_LOAD
 }
 
+// ------------------------------------------------------------- k_ssd_prep
+// Mamba2 backward, per chunk: g = inclusive cumsum of log a (tokens past the
+// end of a ragged last chunk add 0) and U'^T = V^T [d_v][C] (columns past the
+// end zero): what the state recompute and the gradient kernels read where the
+// Gated DeltaNet path reads the WY pass's g and U (with no delta term U = V).
+template <typename E, int C, int DV>
+__global__ __launch_bounds__(kThreads) void k_ssd_prep(const E* __restrict__ v, const float* __restrict__ log_a,
+                                                       float* __restrict__ wG, E* __restrict__ wUt, int T, int H,
+                                                       int N, int ntiles) {
+  constexpr int LC = C + lds_pad<E>();
+  __shared__ __attribute__((aligned(16))) E sVt[DV * LC];
+  Tile<E, C, DV> tv;
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
+    const int nv = min(C, T - n * C);
+    const size_t tok0 = (size_t)b * T + (size_t)n * C;
+    tv.load_rows(v + (tok0 * H + h) * DV, (size_t)H * DV, nv);
+    if (threadIdx.x < 64) {
+      const int t = threadIdx.x;
+      const float g = wave_incl_scan(t < nv ? log_a[(tok0 + t) * H + h] : 0.f);
+      if (t < C) wG[(size_t)tile * C + t] = g;
+    }
+    tv.store_T(sVt, LC);
+    lds_barrier();
+    lds_to_block<E, DV, C>(wUt + (size_t)tile * DV * C, sVt, LC);
+    lds_barrier();
+  }
+}
+
 // --------------------------------------------------------------- launcher
 template <typename E, int C, int DK, int DV>
 int bwd_impl(const BwdArgs& a) {
@@ -876,7 +950,8 @@ int bwd_impl(const BwdArgs& a) {
                        (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
     LRT_LAUNCH(kKGrad1, (k_grad1<E, C, DK, DV, kGradWaves>), dim3(persistent_grid(tiles, Grad1Lds<E, C, DK, DV>::TOTAL)), dim3(64 * kGradWaves), st, (const E*)a.q,
                        (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.S, (const E*)ws.dS,
-                       (const E*)ws.f.U, (const E*)ws.dU, (E*)a.dq, (E*)ws.dW, (E*)ws.dK1, ws.dg1, a.T, a.H, N, tiles);
+                       (const E*)ws.f.U, (const E*)ws.dU, (E*)a.dq, (E*)ws.dW, (E*)ws.dK1, ws.dg1, a.T, a.H, N, tiles,
+                       (E*)nullptr, (E*)nullptr, (float*)nullptr);
     LRT_LAUNCH(kKGrad2, (k_grad2<E, C, DK, DV, kGradWaves>), dim3(persistent_grid(tiles, Grad2Lds<E, C, DK, DV>::TOTAL)), dim3(64 * kGradWaves), st, (const E*)a.k,
                        (const E*)a.v, a.beta, ws.f.G, (const E*)ws.T, (const E*)ws.dW, (const E*)ws.dU, (const E*)ws.dK1,
                        ws.dg1, (E*)a.dk_out, (E*)a.dv_out, a.dlog_a, a.dbeta, a.T, a.H, N, tiles);
@@ -884,10 +959,64 @@ int bwd_impl(const BwdArgs& a) {
   }
 }
 
-template <typename E>
+// Mamba2 backward: the Gated DeltaNet pipeline without the WY transform
+// (T = I, W = 0, U = V, no beta): prep (g, V^T), the state recompute
+// (chunk-start states only), dU_local, the reverse state scan (dU = dV) and
+// one gradient kernel writing dq, dk, dv and dlog_a.
+template <typename E, int C, int DK, int DV>
+int ssd_bwd_impl(const BwdArgs& a) {
+  if constexpr (sizeof(E) == 4 && (DK > 64 || DV > 64)) {
+    return -2;
+  } else if constexpr (sizeof(E) == 4 && C > 32) {
+    return -3;
+  } else {
+    const int N = (a.T + C - 1) / C;
+    const int tiles = a.B * a.H * N;
+    const BwdWs ws = bwd_ws_layout(a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
+    hipStream_t st = (hipStream_t)a.stream;
+    constexpr int BV = DV < 64 ? DV : 64;
+    const int sgrid = a.B * a.H * (DV / BV);
+    E* Ut = (E*)ws.f.U;  // V^T: U'^T for the scan, U^T for k_grad1
+    LRT_LAUNCH(kKSsdPrep, (k_ssd_prep<E, C, DV>),
+               dim3(persistent_grid(tiles, (size_t)DV * (C + lds_pad<E>()) * sizeof(E))), dim3(kThreads), st,
+               (const E*)a.v, a.log_a, ws.f.G, Ut, a.T, a.H, N, tiles);
+    {
+      ScanArgs<E> sa{};
+      sa.k = (const E*)a.k;
+      sa.Up = Ut;
+      sa.G = ws.f.G;
+      sa.hin = a.h0;
+      sa.hs_ld = DV;
+      sa.S = (E*)ws.f.S;
+      sa.T = a.T;
+      sa.H = a.H;
+      sa.N = N;
+      sa.L = N;
+      sa.nseg = 1;
+      sa.DV = DV;
+      LRT_LAUNCH(kKScanBwd, (k_scan<E, C, DK, BV, kScanBwd, false, kStateWaves, false>), dim3(sgrid),
+                 dim3(64 * kStateWaves), st, sa);
+    }
+    E* dUl = (E*)ws.f.Up;
+    LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV>), dim3(persistent_grid(tiles, LocalLds<E, C, DK, DV>::TOTAL)),
+               dim3(kThreads), st, (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N, tiles);
+    LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, false>), dim3(sgrid), dim3(64 * kStateWaves), st,
+               (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)nullptr, (const E*)dUl, a.dht, a.dh0,
+               (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
+    LRT_LAUNCH(kKGrad1, (k_grad1<E, C, DK, DV, kGradWaves, false>),
+               dim3(persistent_grid(tiles, Grad1Lds<E, C, DK, DV>::TOTAL)), dim3(64 * kGradWaves), st, (const E*)a.q,
+               (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.S, (const E*)ws.dS, (const E*)Ut,
+               (const E*)ws.dU, (E*)a.dq, (E*)nullptr, (E*)nullptr, (float*)nullptr, a.T, a.H, N, tiles,
+               (E*)a.dk_out, (E*)a.dv_out, a.dlog_a);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+  }
+}
+
+template <typename E, bool SSD>
 static int bwd_dtype(const BwdArgs& a) {
-#define LRT_CASE(C_, DK_, DV_) \
-  if (a.chunk == C_ && a.dk == DK_ && a.dv == DV_) return bwd_impl<E, C_, DK_, DV_>(a);
+#define LRT_CASE(C_, DK_, DV_)                     \
+  if (a.chunk == C_ && a.dk == DK_ && a.dv == DV_) \
+    return SSD ? ssd_bwd_impl<E, C_, DK_, DV_>(a) : bwd_impl<E, C_, DK_, DV_>(a);
 #define LRT_DV(C_, DK_) LRT_CASE(C_, DK_, 16) LRT_CASE(C_, DK_, 32) LRT_CASE(C_, DK_, 64) LRT_CASE(C_, DK_, 128)
 #define LRT_DK(C_) LRT_DV(C_, 16) LRT_DV(C_, 32) LRT_DV(C_, 64) LRT_DV(C_, 128)
   LRT_DK(16) LRT_DK(32) LRT_DK(64)
@@ -897,6 +1026,7 @@ static int bwd_dtype(const BwdArgs& a) {
   return -2;
 }
 
-int bwd_gdn(const BwdArgs& a) { return a.dtype == 1 ? bwd_dtype<bf16>(a) : bwd_dtype<float>(a); }
+int bwd_gdn(const BwdArgs& a) { return a.dtype == 1 ? bwd_dtype<bf16, false>(a) : bwd_dtype<float, false>(a); }
+int bwd_ssd(const BwdArgs& a) { return a.dtype == 1 ? bwd_dtype<bf16, true>(a) : bwd_dtype<float, true>(a); }
 
 }  // namespace lrt

@@ -236,7 +236,9 @@ struct ScanLds {
 // from a zero state and also carries d_k identity columns with U' = 0, so
 // its end state holds both the segment's own contribution E and its
 // transition M (the state map is affine: H_end = M H_start + E).
-template <typename E, int C, int DK, int BV, int MODE, bool KDA, int NW = 8>
+// DELTA = false is the Mamba2 recurrence (no delta term: W = 0, U = U' = V,
+// with U'^T supplied in a.Up); the backward recompute then writes only S_n.
+template <typename E, int C, int DK, int BV, int MODE, bool KDA, int NW = 8, bool DELTA = true>
 __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
   typedef ScanLds<E, C, DK, BV, MODE, KDA> Lay;
   constexpr bool FWD = MODE == kScanFwd;
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
     const size_t ft = (size_t)bh * N + n_;
     const int fnv = min(C, T - n_ * C);
     const size_t ftok = (size_t)b * T + (size_t)n_ * C;
-    x.W.load_block(a.W + ft * C * DK);
+    if constexpr (DELTA) x.W.load_block(a.W + ft * C * DK);
     if constexpr (KDA) {
       x.K.load_block(a.Kt + ft * DK * C);
       x.g = a.GC[ft * DK + min((int)threadIdx.x, DK - 1)];
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
         store4<E>(sS + (tv * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, hacc[s]);
       }
     }
-    x.W.store(sW, LK);
+    if constexpr (DELTA) x.W.store(sW, LK);
     x.K.store(sK, KDA ? LC : LK);
     if constexpr (FWD) {
       x.Q.store(sQ, LK);
@@ -380,13 +382,13 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
       if (tt < NU) {
         const int ti = tt / NTV, tv = tt % NTV;
         f32x4 acc = zero4();
-        mma<DK>(acc, sW + ti * 16 * LK, LK, sS + tv * 16 * LK, LK);
+        if constexpr (DELTA) mma<DK>(acc, sW + ti * 16 * LK, LK, sS + tv * 16 * LK, LK);
         const f32x4 u = up[s] - acc;
         const int vv = tv * 16 + (l & 15), t = ti * 16 + (l >> 4) * 4;
         store4<E>(sU + vv * LC + t, u);
         if constexpr (!KDA)
           store4<E>(sUk + vv * LC + t, f32x4{u[0] * skt[t], u[1] * skt[t + 1], u[2] * skt[t + 2], u[3] * skt[t + 3]});
-        if constexpr (MODE == kScanBwd) store4<E>(a.U + (tile * DV + v0 + vv) * C + t, u);
+        if constexpr (MODE == kScanBwd && DELTA) store4<E>(a.U + (tile * DV + v0 + vv) * C + t, u);
       }
     }
     lds_barrier();

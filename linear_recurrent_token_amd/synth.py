@@ -35,6 +35,10 @@ CONFIGS = {
     # Gated DeltaNet training step (forward + backward) at the pretraining shape
     "gdn_train_bf16_2k": dict(op="gdn_fwd_bwd", B=16, T=2048, H=8, dk=128, dv=128, chunk=64,
                               dtype=torch.bfloat16, gate_shift=2.0, h0_std=0.1),
+    # Mamba2 / SSD training step (forward + backward) at the pretraining shape,
+    # with the Mamba2 forward's distributions
+    "ssd_train_bf16_2k": dict(op="ssd_fwd_bwd", B=16, T=2048, H=8, dk=128, dv=128, chunk=64,
+                              dtype=torch.bfloat16, gate_shift=0.0, h0_std=0.0),
     # Kimi Delta Attention forward over one 1M-token sequence, 16 heads
     "kda_bf16_1m": dict(op="kda_fwd", B=1, T=1 << 20, H=16, dk=128, dv=128, chunk=64,
                         dtype=torch.bfloat16, gate="lowrank", rank=16, h0_std=0.0),
@@ -65,7 +69,7 @@ def _unit_rows(x):
 def make_inputs(op, B, T, H, dk, dv, dtype=torch.bfloat16, seed=0, device="cpu",
                 gate_shift=0.0, h0_std=0.0, gate="scalar", rank=16, gate_width=None,
                 with_do=False, dht_std=0.0, chunk=None):
-    """Draw inputs for ``op`` in {'gdn_fwd', 'gdn_fwd_bwd', 'ssd_fwd', 'kda_fwd'}.
+    """Draw inputs for ``op`` in {'gdn_fwd', 'gdn_fwd_bwd', 'ssd_fwd', 'ssd_fwd_bwd', 'kda_fwd'}.
 
     Returns a dict with q, k, v [B,T,H,d] in ``dtype``; log_a fp32 [B,T,H]
     ([B,T,H,dk] for KDA); beta fp32 [B,T,H] (absent for SSD); h0 fp32

@@ -30,7 +30,7 @@ def L():
 
 def test_header_declares_the_entry_points():
     names = declared()
-    for f in ("gdn_fwd", "gdn_bwd", "kda_fwd", "ssd_fwd", "lrt_workspace_bytes", "lrt_status_string"):
+    for f in ("gdn_fwd", "gdn_bwd", "kda_fwd", "ssd_fwd", "ssd_bwd", "lrt_workspace_bytes", "lrt_status_string"):
         assert f in names
 
 
@@ -110,12 +110,43 @@ def test_backward_validation(L):
     assert lib.gdn_bwd(*a) == c["LRT_ERR_DTYPE"]
 
 
+def test_ssd_backward_validation(L):
+    c = codes()
+    lib = L.lib()
+    F = FAKE
+    # q k v log_a h0 do dht dq dk dv dlog_a dh0 | B T H dk dv chunk dtype | ws wsb stream
+    base = [F, F, F, F, None, F, None, F, F, F, F, None, 1, 64, 2, 16, 16, 16, 0, None, 0, None]
+    assert lib.ssd_bwd(*base) == c["LRT_ERR_WORKSPACE"]
+    for i in (0, 1, 2, 3, 5, 7, 8, 9, 10):
+        a = list(base)
+        a[i] = None
+        assert lib.ssd_bwd(*a) == c["LRT_ERR_NULL"], i
+    a = list(base)
+    a[17] = 48
+    assert lib.ssd_bwd(*a) == c["LRT_ERR_CHUNK"]
+    a = list(base)
+    a[18] = 2
+    assert lib.ssd_bwd(*a) == c["LRT_ERR_DTYPE"]
+    a = list(base)
+    a[15] = 24
+    assert lib.ssd_bwd(*a) == c["LRT_ERR_SHAPE"]
+    a = list(base)
+    a[3] = F + 2
+    assert lib.ssd_bwd(*a) == c["LRT_ERR_ALIGN"]
+    need = L.workspace_bytes(L.OP_SSD_BWD, 1, 64, 2, 16, 16, 16, 0)
+    a = list(base)
+    a[19], a[20] = F, need - 1
+    assert lib.ssd_bwd(*a) == c["LRT_ERR_WORKSPACE"]
+
+
 def test_workspace_bytes(L):
     lib = L.lib()
     bad = ctypes.c_size_t(-1).value
     assert lib.lrt_workspace_bytes(9, 1, 64, 2, 16, 16, 16, 0) == bad
+    assert lib.lrt_workspace_bytes(5, 1, 64, 2, 16, 16, 16, 0) == bad
+    assert lib.lrt_workspace_bytes(-1, 1, 64, 2, 16, 16, 16, 0) == bad
     assert lib.lrt_workspace_bytes(0, 1, 64, 2, 16, 16, 17, 0) == bad
-    for op in range(4):
+    for op in range(5):
         n = L.workspace_bytes(op, 16, 2048, 8, 128, 128, 64, 1)
         assert n > 0
     # grows with T and is never zero

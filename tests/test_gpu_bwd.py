@@ -1,8 +1,9 @@
-"""GPU parity of gdn_bwd against the fp64 oracle's back-propagation through
-time, through the C ABI.
+"""GPU parity of gdn_bwd and ssd_bwd against the fp64 oracle's
+back-propagation through time, through the C ABI.
 
 Bar: max|got - oracle| / max|oracle| per gradient tensor (dq, dk, dv,
-dlog_a, dbeta, dh0) <= 1e-4 for fp32 inputs and <= 1e-2 for bf16 inputs.
+dlog_a, dbeta (GDN only), dh0) <= 1e-4 for fp32 inputs and <= 1e-2 for bf16
+inputs.
 """
 import sys
 
@@ -34,14 +35,20 @@ def cpu(x):
     return None if x is None else x.detach().cpu()
 
 
-def check_bwd(inp, chunk, tol):
+def check_bwd(inp, chunk, tol, variant="gdn"):
     import linear_recurrent_token_amd as L
     q, k, v, la, beta, h0, do, dht = (inp.get(n) for n in ("q", "k", "v", "log_a", "beta", "h0", "do", "dht"))
-    got = L.gdn_bwd(q, k, v, la, beta, h0, do, dht, chunk=chunk)
+    if variant == "gdn":
+        got = L.gdn_bwd(q, k, v, la, beta, h0, do, dht, chunk=chunk)
+        names = NAMES
+    else:
+        got = L.ssd_bwd(q, k, v, la, h0, do, dht, chunk=chunk)
+        names = tuple(n for n in NAMES if n != "dbeta")
     torch.cuda.synchronize()
-    ref = oracle.bwd("gdn", cpu(q), cpu(k), cpu(v), cpu(la), cpu(beta), cpu(h0), cpu(do), cpu(dht))
+    ref = oracle.bwd(variant, cpu(q), cpu(k), cpu(v), cpu(la), cpu(beta), cpu(h0), cpu(do), cpu(dht))
+    ref = [r for n, r in zip(NAMES, ref) if n in names]
     errs = {}
-    for name, g, r in zip(NAMES, got, ref):
+    for name, g, r in zip(names, got, ref):
         g = g.float().cpu().numpy()
         assert np.all(np.isfinite(g)), name
         errs[name] = rel(g, r)
@@ -83,9 +90,43 @@ def test_bwd_training_step_workload():
     check_bwd(inp, 64, TOL[torch.bfloat16])
 
 
+SSD_CASES = [
+    # name, B, T, H, dk, dv, chunk, dtype, gate_shift, h0_std, dht_std
+    ("fp32_tiny", 1, 64, 2, 16, 16, 16, torch.float32, 0.0, 0.0, 0.0),
+    ("fp32_slow_h0_dht_T77_C32", 2, 77, 2, 32, 64, 32, torch.float32, -6.0, 0.1, 0.1),
+    ("bf16_slow_T61_C16", 2, 61, 3, 64, 64, 16, torch.bfloat16, -6.0, 0.1, 0.1),
+    ("bf16_slow_C32", 1, 200, 2, 128, 128, 32, torch.bfloat16, -6.0, 0.1, 0.1),
+    ("bf16_slow_C64_T300", 2, 300, 2, 128, 128, 64, torch.bfloat16, -6.0, 0.1, 0.1),
+    ("bf16_default_gates_C64", 2, 256, 2, 128, 128, 64, torch.bfloat16, 0.0, 0.0, 0.0),
+    ("bf16_dk32_dv128", 1, 100, 2, 32, 128, 32, torch.bfloat16, -6.0, 0.1, 0.1),
+    ("bf16_long_slow_C64", 1, 4096 - 7, 2, 128, 128, 64, torch.bfloat16, -6.0, 0.1, 0.1),
+]
+
+
+@pytest.mark.parametrize("case", SSD_CASES, ids=[c[0] for c in SSD_CASES])
+def test_ssd_bwd_small(case):
+    name, B, T, H, dk, dv, chunk, dt, shift, h0s, dhs = case
+    say(f"[ssd_bwd] {name}")
+    inp = synth.make_inputs("ssd_fwd_bwd", B, T, H, dk, dv, dtype=dt, seed=0, device="cuda",
+                            gate_shift=shift, h0_std=h0s, dht_std=dhs)
+    check_bwd(inp, chunk, TOL[dt], variant="ssd")
+
+
+def test_ssd_bwd_workload_shape():
+    """Mamba2 training step at the 2048-token shape (B=16, T=2048, H=8,
+    d=128, chunk 64, bf16, the Mamba2 forward workload's distributions), every
+    gradient element against the oracle."""
+    say("[ssd_bwd] workload ssd_train_bf16_2k")
+    inp = synth.config_inputs("ssd_train_bf16_2k", device="cuda")
+    check_bwd(inp, 64, TOL[torch.bfloat16], variant="ssd")
+
+
 def test_bwd_rejects_unsupported_fp32_sizes():
     import linear_recurrent_token_amd as L
     inp = synth.make_inputs("gdn_fwd_bwd", 1, 64, 1, 128, 128, dtype=torch.float32, device="cuda")
     with pytest.raises(L.LrtError) as e:
         L.gdn_bwd(inp["q"], inp["k"], inp["v"], inp["log_a"], inp["beta"], None, inp["do"], chunk=16)
+    assert e.value.status == -2
+    with pytest.raises(L.LrtError) as e:
+        L.ssd_bwd(inp["q"], inp["k"], inp["v"], inp["log_a"], None, inp["do"], chunk=16)
     assert e.value.status == -2
