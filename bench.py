@@ -133,7 +133,7 @@ def kernel_model(name, c, esz=2, op="gdn_fwd + gdn_bwd"):
     }
     if op.startswith("ssd"):
         # the fused Mamba2 forward: reads q, k, v, log_a, h0; writes o, ht
-        per["k_fwd"] = ((2 * dk + dv) * e + 4 + dv * e, 2 * st, 2 * C * (dk + dv) + 4 * dk * dv)
+        per["k_ssd_fwd"] = ((2 * dk + dv) * e + 4 + dv * e, 2 * st, 2 * C * (dk + dv) + 4 * dk * dv)
     if op == "ssd_fwd + ssd_bwd":
         per.update({
             # reads v, log_a; writes g, V^T

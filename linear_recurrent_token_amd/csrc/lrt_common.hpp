@@ -172,6 +172,48 @@ __device__ __forceinline__ void mma(f32x4& acc, const float* a, int lda, const f
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// NA tiles sharing their B operand: acc[s] += A_s (16 x K) B (K x 16) with
+// A_s = a + s * astep.  B's fragment is read from LDS once per k step for all
+// NA products (mma() per tile would read it NA times).
+template <int K, int NA, bool AK = false, bool BK = false>
+__device__ __forceinline__ void mma_nA(f32x4 (&acc)[NA], const bf16* a, int astep, int lda, const bf16* b,
+                                       int ldb) {
+  const int l = lane_id();
+#pragma unroll
+  for (int k = 0; k + 32 <= K; k += 32) {
+    bf16x8 fb;
+    if constexpr (BK)
+      fb = frag_k8_outer(b, ldb, k, 0);
+    else
+      fb = *(const bf16x8*)(b + (l & 15) * ldb + k + (l >> 4) * 8);
+#pragma unroll
+    for (int s = 0; s < NA; ++s) {
+      const bf16* as = a + s * astep;
+      bf16x8 fa;
+      if constexpr (AK)
+        fa = frag_k8_outer(as, lda, k, 0);
+      else
+        fa = *(const bf16x8*)(as + (l & 15) * lda + k + (l >> 4) * 8);
+      acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc[s], 0, 0, 0);
+    }
+  }
+  if constexpr (K % 32 == 16) {
+    constexpr int k = K - 16;
+    const bf16x8 fb = BK ? frag_k16_outer(b, ldb, k) : frag_k16_inner(b, ldb, k);
+#pragma unroll
+    for (int s = 0; s < NA; ++s) {
+      const bf16x8 fa = AK ? frag_k16_outer(a + s * astep, lda, k) : frag_k16_inner(a + s * astep, lda, k);
+      acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc[s], 0, 0, 0);
+    }
+  }
+}
+template <int K, int NA, bool AK = false, bool BK = false>
+__device__ __forceinline__ void mma_nA(f32x4 (&acc)[NA], const float* a, int astep, int lda, const float* b,
+                                       int ldb) {
+#pragma unroll
+  for (int s = 0; s < NA; ++s) mma<K, AK, BK>(acc[s], a + s * astep, lda, b, ldb);
+}
+
 // ------------------------------------------------------------- vector moves
 // Four consecutive elements of E packed for one store / load.
 template <typename E>

@@ -1,5 +1,5 @@
-// lrt_fused_fwd.hpp -- the whole chunkwise forward of the scalar-gate mixers
-// (Gated DeltaNet and its Mamba2 / SSD special case) in one kernel.
+// lrt_fused_fwd.hpp -- the whole chunkwise forward of Gated DeltaNet in one
+// kernel (used where the WY pass + scan split does not fit in LDS).
 //
 // One workgroup of NW waves per (b, h, block of BV value columns) walks the
 // chunks in order.  Per chunk of C tokens (state Hn = S^T kept in MFMA
@@ -10,7 +10,7 @@
 //   U  = U' - W Hn
 //   O  = diag(gamma) Q Hn + ((Q K^T) o Gamma) U
 //   Hn <- gamma_C Hn + K^T diag(e^(g_C - g)) U
-// (SSD: no b, no A, U = V.)  The state never leaves the chip; q, k, v and the
+// The state never leaves the chip; q, k, v and the
 // gates are read once per chunk (the value-column blocks of one (b, h) share
 // an XCD's L2) and o is written once, so HBM traffic is the method's minimum
 // plus the duplicated q/k reads of the column blocks.  The next chunk's
@@ -22,7 +22,7 @@
 
 namespace lrt {
 
-template <typename E, int C, int DK, int BV, bool DELTA>
+template <typename E, int C, int DK, int BV>
 struct FusedLds {
   static constexpr int P = lds_pad<E>();
   static constexpr int LK = DK + P, LB = BV + P, LC = C + P, LA = tri_ld<C>();
@@ -34,23 +34,23 @@ struct FusedLds {
   static constexpr size_t S = V + (size_t)C * LB * es;                  // Hn^T [v][d]
   static constexpr size_t P_ = S + (size_t)BV * LK * es;                // (Q K^T) o Gamma [i][j]
   static constexpr size_t U = P_ + (size_t)C * LC * es;                 // A, T (fp32, column-major); then U^T, (kt U)^T
-  static constexpr size_t USZ = mx(DELTA ? (size_t)C * LA * 4 : 0, 2 * (size_t)BV * LC * es);
+  static constexpr size_t USZ = mx((size_t)C * LA * 4, 2 * (size_t)BV * LC * es);
   static constexpr size_t TW = U + USZ;                                 // W rows [t][d]
-  static constexpr size_t TWSZ = DELTA ? (size_t)C * LK * es : 0;
+  static constexpr size_t TWSZ = (size_t)C * LK * es;
   static constexpr size_t T = TW + TWSZ;                                // Tinv, Tinv diag(b gamma) (E)
-  static constexpr size_t TSZ = DELTA ? 2 * (size_t)C * LC * es : 0;
+  static constexpr size_t TSZ = 2 * (size_t)C * LC * es;
   static constexpr size_t O = T + TSZ;                                  // o rows [t][v]
   static constexpr size_t OSZ = (size_t)C * LB * es;
   static constexpr size_t G = O + OSZ;                                  // g, gamma, b, b gamma, e^(g_C - g)
   static constexpr size_t TOTAL = G + 5 * C * 4;
 };
 
-template <typename E, int C, int DK, int BV, bool DELTA, int NW = 8>
+template <typename E, int C, int DK, int BV, int NW = 8>
 __global__ __launch_bounds__(64 * NW) void k_fwd(const E* __restrict__ q, const E* __restrict__ k,
                                                  const E* __restrict__ v, const float* __restrict__ log_a,
                                                  const float* __restrict__ beta, const float* h0, float* ht,
                                                  E* __restrict__ o, int T, int H, int N, int DV) {
-  typedef FusedLds<E, C, DK, BV, DELTA> Lay;
+  typedef FusedLds<E, C, DK, BV> Lay;
   constexpr int NT = 64 * NW;
   constexpr int LK = Lay::LK, LB = Lay::LB, LC = Lay::LC, LA = Lay::LA;
   constexpr int NB = C / 16, NTV = BV / 16;
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const E* __restrict__ q, const 
     rb = 0.f;                                                                               \
     if ((int)threadIdx.x < fnv) {                                                           \
       rla = log_a[(ftok + threadIdx.x) * H + h];                                            \
-      if (DELTA) rb = beta[(ftok + threadIdx.x) * H + h];                                   \
+      rb = beta[(ftok + threadIdx.x) * H + h];                                              \
     }                                                                                       \
   }
 
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const E* __restrict__ q, const 
       }
     }
     lds_barrier();
-    if (DELTA) tv.scale_rows(sb);
+    tv.scale_rows(sb);
     tv.store(sV, LB);
     if (n + 1 < N) LRT_FWD_FETCH(n + 1)
     // ---- S2: A and P
@@ -160,35 +160,31 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const E* __restrict__ q, const 
         const int i = i0 + r;
         sP[i * LC + j] = from_f<E>((j <= i) ? qk[r] * __expf(sg[i] - sg[j]) : 0.f);
       }
-      if constexpr (DELTA) {
-        f32x4 kk = zero4();
-        mma<DK>(kk, sK + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
-        f32x4 av;
+      f32x4 kk = zero4();
+      mma<DK>(kk, sK + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
+      f32x4 av;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) av[r] = (j < i0 + r) ? sb[i0 + r] * kk[r] * __expf(sg[i0 + r] - sg[j]) : 0.f;
-        *(f32x4*)(sA + j * LA + i0) = av;  // column-major
-      }
+      for (int r = 0; r < 4; ++r) av[r] = (j < i0 + r) ? sb[i0 + r] * kk[r] * __expf(sg[i0 + r] - sg[j]) : 0.f;
+      *(f32x4*)(sA + j * LA + i0) = av;  // column-major
     }
     lds_barrier();
-    if constexpr (DELTA) {
-      // ---- S3: T = (I + A)^-1, in E twice: T and T diag(b gamma)
-      unit_lower_inverse<C, NT>(sA);
-      for (int idx = threadIdx.x; idx < C * C; idx += NT) {
-        const int j = idx / C, i = idx % C;
-        const float x = j <= i ? sA[j * LA + i] : 0.f;
-        sT[i * LC + j] = from_f<E>(x);
-        sTw[i * LC + j] = from_f<E>(x * sbg[j]);
-      }
-      lds_barrier();
-      // ---- S4: W^T = K^T (T diag(b gamma))^T -> W rows [t][d] (over the dead inverse)
-      for (int tt = w; tt < (DK / 16) * NB; tt += NW) {
-        const int td = tt / NB, ti = tt % NB;
-        f32x4 acc = zero4();
-        mma<C, true, false>(acc, sK + td * 16, LK, sTw + ti * 16 * LC, LC);
-        store4<E>(sW + (ti * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, acc);
-      }
+    // ---- S3: T = (I + A)^-1, in E twice: T and T diag(b gamma)
+    unit_lower_inverse<C, NT>(sA);
+    for (int idx = threadIdx.x; idx < C * C; idx += NT) {
+      const int j = idx / C, i = idx % C;
+      const float x = j <= i ? sA[j * LA + i] : 0.f;
+      sT[i * LC + j] = from_f<E>(x);
+      sTw[i * LC + j] = from_f<E>(x * sbg[j]);
     }
-    // U' = T (b V) (rows t, cols v), in registers (SSD: U = V)
+    lds_barrier();
+    // ---- S4: W^T = K^T (T diag(b gamma))^T -> W rows [t][d] (over the dead inverse)
+    for (int tt = w; tt < (DK / 16) * NB; tt += NW) {
+      const int td = tt / NB, ti = tt % NB;
+      f32x4 acc = zero4();
+      mma<C, true, false>(acc, sK + td * 16, LK, sTw + ti * 16 * LC, LC);
+      store4<E>(sW + (ti * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, acc);
+    }
+    // U' = T (b V) (rows t, cols v), in registers
     f32x4 up[UPW];
 #pragma unroll
     for (int s = 0; s < UPW; ++s) {
@@ -196,14 +192,7 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const E* __restrict__ q, const 
       up[s] = zero4();
       if (tt < NU) {
         const int ti = tt / NTV, tv2 = tt % NTV;
-        if constexpr (DELTA) {
-          mma<C, false, true>(up[s], sT + ti * 16 * LC, LC, sV + tv2 * 16, LB);
-        } else {
-          up[s] = f32x4{to_f(sV[(ti * 16 + (l >> 4) * 4 + 0) * LB + tv2 * 16 + (l & 15)]),
-                        to_f(sV[(ti * 16 + (l >> 4) * 4 + 1) * LB + tv2 * 16 + (l & 15)]),
-                        to_f(sV[(ti * 16 + (l >> 4) * 4 + 2) * LB + tv2 * 16 + (l & 15)]),
-                        to_f(sV[(ti * 16 + (l >> 4) * 4 + 3) * LB + tv2 * 16 + (l & 15)])};
-        }
+        mma<C, false, true>(up[s], sT + ti * 16 * LC, LC, sV + tv2 * 16, LB);
       }
     }
     lds_barrier();
@@ -214,11 +203,9 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const E* __restrict__ q, const 
       if (tt < NU) {
         const int ti = tt / NTV, tv2 = tt % NTV;
         f32x4 u = up[s];
-        if constexpr (DELTA) {
-          f32x4 acc = zero4();
-          mma<DK>(acc, sW + ti * 16 * LK, LK, sS + tv2 * 16 * LK, LK);
-          u -= acc;
-        }
+        f32x4 acc = zero4();
+        mma<DK>(acc, sW + ti * 16 * LK, LK, sS + tv2 * 16 * LK, LK);
+        u -= acc;
         const int vv = tv2 * 16 + (l & 15), t = ti * 16 + (l >> 4) * 4;
         store4<E>(sU + vv * LC + t, u);
         store4<E>(sUk + vv * LC + t, f32x4{u[0] * skt[t], u[1] * skt[t + 1], u[2] * skt[t + 2], u[3] * skt[t + 3]});

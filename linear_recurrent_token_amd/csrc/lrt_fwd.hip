@@ -1,6 +1,7 @@
 // lrt_fwd.hip -- launchers of the chunkwise forward (gdn_fwd, ssd_fwd).
 #include "lrt_fused_fwd.hpp"
 #include "lrt_scan.hpp"
+#include "lrt_ssd_fwd.hpp"
 #include "lrt_fwd_kernels.hpp"
 #include "lrt_internal.hpp"
 
@@ -11,11 +12,35 @@ namespace lrt {
 constexpr bool kFwdSplit = true;
 
 // --------------------------------------------------------------- launchers
+// Mamba2: one fused kernel per (b, h, block of value columns), state on chip.
+constexpr int kSsdBV = 64;   // value columns per workgroup
+constexpr int kSsdPF = 1;    // chunks of operands in flight
+constexpr int kSsdOcc = 1;   // workgroups per CU the registers are sized for
+// the widest column block up to kSsdBV whose tiles fit in LDS
+template <typename E, int C, int DK, int BV>
+constexpr int ssd_bv() {
+  if constexpr (BV > 16 && SsdFwdLds<E, C, DK, BV>::TOTAL > 160 * 1024)
+    return ssd_bv<E, C, DK, BV / 2>();
+  else
+    return BV;
+}
+template <typename E, int C, int DK, int DV>
+int ssd_fwd_impl(const FwdArgs& a) {
+  constexpr int BV = ssd_bv<E, C, DK, (DV < kSsdBV ? DV : kSsdBV)>();
+  static_assert(SsdFwdLds<E, C, DK, BV>::TOTAL <= 160 * 1024, "k_ssd_fwd LDS");
+  const int N = (a.T + C - 1) / C;
+  const int grid = a.B * a.H * (DV / BV);
+  LRT_LAUNCH(kKSsdFwd, (k_ssd_fwd<E, C, DK, BV, kStateWaves, kSsdPF, kSsdOcc>), dim3(grid), dim3(64 * kStateWaves), a.stream,
+             (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.h0, a.ht, (E*)a.o, a.T, a.H, N, DV);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
 template <typename E, int C, int DK, int DV>
 int fwd_impl(const FwdArgs& a) {
+  if (a.variant == kVarSSD) return ssd_fwd_impl<E, C, DK, DV>(a);
   constexpr int BVF = DV < 64 ? DV : 64;
   if constexpr (WyLds<E, C, DK, DV>::TOTAL <= 160 * 1024 && ScanLds<E, C, DK, BVF, kScanFwd, false>::TOTAL <= 160 * 1024) {
-    if (kFwdSplit && a.variant == kVarGDN) {
+    if (kFwdSplit) {
       // chunk-parallel WY pass, then the serial scan
       const int N = (a.T + C - 1) / C;
       const int tiles = a.B * a.H * N;
@@ -29,38 +54,25 @@ int fwd_impl(const FwdArgs& a) {
       return launch_scan_fwd<E, C, DK, DV, false>(a, ws, N);
     }
   }
-  if constexpr (FusedLds<E, C, DK, BVF, true>::TOTAL <= 160 * 1024) {
+  if constexpr (FusedLds<E, C, DK, BVF>::TOTAL <= 160 * 1024) {
     // the whole forward in one kernel: state on chip, inputs read once
     const int N = (a.T + C - 1) / C;
     hipStream_t st = (hipStream_t)a.stream;
     const int grid = a.B * a.H * (DV / BVF);
-    if (a.variant == kVarGDN)
-      LRT_LAUNCH(kKFwd, (k_fwd<E, C, DK, BVF, true, kStateWaves>), dim3(grid), dim3(64 * kStateWaves), st,
-                 (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.h0, a.ht, (E*)a.o, a.T, a.H, N, DV);
-    else
-      LRT_LAUNCH(kKFwd, (k_fwd<E, C, DK, BVF, false, kStateWaves>), dim3(grid), dim3(64 * kStateWaves), st,
-                 (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.h0, a.ht, (E*)a.o, a.T, a.H, N, DV);
+    LRT_LAUNCH(kKFwd, (k_fwd<E, C, DK, BVF, kStateWaves>), dim3(grid), dim3(64 * kStateWaves), st,
+               (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.h0, a.ht, (E*)a.o, a.T, a.H, N, DV);
     return hipGetLastError() == hipSuccess ? 0 : -7;
   }
   const int N = (a.T + C - 1) / C;
   const int tiles = a.B * a.H * N;
   const FwdWs ws = fwd_ws_layout(a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
   hipStream_t st = (hipStream_t)a.stream;
-  const bool delta = a.variant == kVarGDN;
-  if (delta)
-    LRT_LAUNCH(kKPrep, (k_prep<E, C, DK, DV, true>), dim3(persistent_grid(tiles, PrepLds<E, C, DK, DV, true>::TOTAL)), dim3(kThreads), st, (const E*)a.k,
-                       (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.G, (E*)nullptr);
-  else
-    LRT_LAUNCH(kKPrep, (k_prep<E, C, DK, DV, false>), dim3(persistent_grid(tiles, PrepLds<E, C, DK, DV, false>::TOTAL)), dim3(kThreads), st, (const E*)a.k,
-                       (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.G, (E*)nullptr);
+  LRT_LAUNCH(kKPrep, (k_prep<E, C, DK, DV, true>), dim3(persistent_grid(tiles, PrepLds<E, C, DK, DV, true>::TOTAL)), dim3(kThreads), st, (const E*)a.k,
+                     (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.G, (E*)nullptr);
   constexpr int BV = DV < 64 ? DV : 64;  // state columns per workgroup
   const int sgrid = a.B * a.H * (DV / BV);
-  if (delta)
-    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, true, false, kStateWaves>), dim3(sgrid), dim3(64 * kStateWaves), st, (const E*)ws.W,
-                       (const E*)ws.Up, (const E*)ws.Kt, ws.G, (const float*)nullptr, a.h0, a.ht, (E*)ws.U, (E*)ws.S, N, DV);
-  else
-    LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, false, false, kStateWaves>), dim3(sgrid), dim3(64 * kStateWaves), st, (const E*)ws.W,
-                       (const E*)ws.Up, (const E*)ws.Kt, ws.G, (const float*)nullptr, a.h0, a.ht, (E*)ws.U, (E*)ws.S, N, DV);
+  LRT_LAUNCH(kKState, (k_state<E, C, DK, BV, true, false, kStateWaves>), dim3(sgrid), dim3(64 * kStateWaves), st, (const E*)ws.W,
+                     (const E*)ws.Up, (const E*)ws.Kt, ws.G, (const float*)nullptr, a.h0, a.ht, (E*)ws.U, (E*)ws.S, N, DV);
   // fp32 operands need twice the LDS: split the value columns in blocks of 64
   constexpr int BVO = (sizeof(E) == 4 && DV > 64) ? 64 : DV;
   LRT_LAUNCH(kKOut, (k_out<E, C, DK, BVO>), dim3(persistent_grid(tiles * (DV / BVO), out_lds_bytes<E, C, DK, BVO, false>())), dim3(kThreads), st, (const E*)a.q,

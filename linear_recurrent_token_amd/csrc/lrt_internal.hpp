@@ -117,6 +117,7 @@ enum KernelKind {
   kKScanLocal,
   kKCarry,
   kKSsdPrep,
+  kKSsdFwd,
   kKNumKinds
 };
 // Bracket one launch with the timing hook's events (no-ops unless attached).
