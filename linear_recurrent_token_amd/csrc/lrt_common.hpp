@@ -452,6 +452,22 @@ __device__ __forceinline__ void lds_to_rows(E* g, size_t gs, const E* lds, int l
   }
 }
 
+// As lds_to_rows, but every thread stores (rows >= nvalid write row
+// nvalid - 1 again, with its own value; nvalid >= 1): no branch around the
+// stores, so the compiler's waits on older loads can count them exactly.
+template <typename E, int R, int W, int NT = kThreads>
+__device__ __forceinline__ void lds_to_rows_clamped(E* g, size_t gs, const E* lds, int ls, int nvalid) {
+  constexpr int V = 16 / (int)sizeof(E), PR = W / V;
+#pragma unroll
+  for (int s = 0; s < (R * PR + NT - 1) / NT; ++s) {
+    const int idx = threadIdx.x + NT * s;
+    if ((R * PR) % NT == 0 || idx < R * PR) {
+      const int r = min(idx / PR, nvalid - 1), c = (idx % PR) * V;
+      *(u32x4*)(g + (size_t)r * gs + c) = *(const u32x4*)(lds + r * ls + c);
+    }
+  }
+}
+
 // Copy R rows of W elements from global (row stride gs elements) into LDS
 // (row stride ls); rows >= nvalid become zero.
 template <typename E, int R, int W>

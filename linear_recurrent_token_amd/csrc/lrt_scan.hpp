@@ -331,8 +331,6 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
     }
   };
 
-  size_t otok = 0;  // first token of the chunk whose o rows wait in sO
-  int onv = 0;
   auto step = [&](Ops& x, int n) {
     const size_t tile = (size_t)bh * N + n;
     const int nv = min(C, T - n * C);
@@ -367,14 +365,11 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
     f32x4 up[UPW];
 #pragma unroll
     for (int s = 0; s < UPW; ++s) up[s] = ident ? zero4() : Vec4<E>::unpack(x.up[s]);
-    if (n + 2 < n1) fetch(x, n + 2);
+    // chunk n + 2 (the segment's last chunk again near its end: unconditional
+    // loads keep the compiler's wait for the next set exact)
+    fetch(x, min(n + 2, n1 - 1));
     lds_barrier();
-    if constexpr (FWD) {
-      // o rows of the previous chunk (staged in sO by its last step)
-      if (n > n0) lds_to_rows<E, C, BV, NT>(a.o + (otok * H + h) * DV + v0, (size_t)H * DV, sO, LB, onv);
-    } else if constexpr (MODE == kScanBwd) {
-      lds_to_block<E, BV, DK, NT>(a.S + (tile * DV + v0) * DK, sS, LK);
-    }
+    if constexpr (MODE == kScanBwd) lds_to_block<E, BV, DK, NT>(a.S + (tile * DV + v0) * DK, sS, LK);
     // ---- U = U' - W Hn -> U^T (GDN: and (e^(g_C - g) U)^T)
 #pragma unroll
     for (int s = 0; s < UPW; ++s) {
@@ -403,8 +398,6 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
         mma<C>(acc, sU + tv * 16 * LC, LC, sP + ti * 16 * LC, LC);
         store4<E>(sO + i * LB + tv * 16 + (l >> 4) * 4, acc);
       }
-      otok = tok0;
-      onv = nv;
     }
     const float gdec = KDA ? 0.f : __expf(sg[C - 1]);
 #pragma unroll
@@ -422,6 +415,10 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
       }
     }
     lds_barrier();
+    // o rows out, after this chunk's prefetch (clamped rows: a fixed number of
+    // stores, so the next wait for operands leaves them in flight)
+    if constexpr (FWD)
+      lds_to_rows_clamped<E, C, BV, NT>(a.o + (tok0 * H + h) * DV + v0, (size_t)H * DV, sO, LB, nv);
   };
 
   Ops x0, x1;
@@ -430,9 +427,6 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
   for (int n = n0; n < n1; n += 2) {
     step(x0, n);
     if (n + 1 < n1) step(x1, n + 1);
-  }
-  if constexpr (FWD) {
-    if (n1 > n0) lds_to_rows<E, C, BV, NT>(a.o + (otok * H + h) * DV + v0, (size_t)H * DV, sO, LB, onv);
   }
   if (a.hout != nullptr) {
 #pragma unroll

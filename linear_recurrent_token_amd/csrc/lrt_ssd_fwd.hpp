@@ -19,9 +19,10 @@
 //  * V and e^(g_C - g) V stay row-major in LDS and P is stored transposed,
 //    so both products that contract over tokens read their operands with the
 //    LDS transpose read -- no U staging phase;
-//  * the next PF chunks' q, k, v and log a load into registers (clamped rows,
-//    so no load waits at issue) while this chunk computes; the o rows of a
-//    chunk leave during the next one;
+//  * the next PF chunks' q, k, v and log a load into registers while this
+//    chunk computes; loads and the o-row stores are unconditional (clamped
+//    rows and chunk index), so the compiler's wait for a chunk's operands
+//    counts exactly and leaves later loads and the stores in flight;
 //  * a wave's output and state tiles share one operand fragment per k step;
 //  * three barriers per chunk.
 // Measured on MI355X at B=16, T=2048, H=8, d=128: 64 value columns per
@@ -103,8 +104,6 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_ssd_fwd(const E* __restrict__ 
     x.la = log_a[(ftok + min(l, fnv - 1)) * H + h];
   };
 
-  size_t otok = 0;  // first token of the chunk whose o rows wait in sO
-  int onv = 0;
   auto step = [&](Ops& x, int n) {
     const int nv = min(C, T - n * C);
     const size_t tok0 = (size_t)b * T + (size_t)n * C;
@@ -139,9 +138,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_ssd_fwd(const E* __restrict__ 
       }
     }
     lds_barrier();
-    if (n + PF < N) fetch(x, n + PF);
-    // o rows of the previous chunk
-    if (n > 0) lds_to_rows<E, C, BV, NT>(o + (otok * H + h) * DV + v0, (size_t)H * DV, sO, LB, onv);
+    // chunk n + PF (the last chunk again near the end: unconditional loads
+    // keep the wait for this set exact)
+    fetch(x, min(n + PF, N - 1));
     // ---- P^T (rows j, cols i): P_ij = (q_i . k_j) e^(g_i - g_j), j <= i
 #pragma unroll
     for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
@@ -215,19 +214,19 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_ssd_fwd(const E* __restrict__ 
         }
       }
     }
-    otok = tok0;
-    onv = nv;
     lds_barrier();
+    // o rows out; issued after the prefetch, so the next chunk's wait for
+    // its operands leaves these stores in flight
+    lds_to_rows_clamped<E, C, BV, NT>(o + (tok0 * H + h) * DV + v0, (size_t)H * DV, sO, LB, nv);
   };
 
   Ops x0, x1;
   fetch(x0, 0);
-  if (PF > 1 && 1 < N) fetch(x1, 1);
+  if constexpr (PF > 1) fetch(x1, min(1, N - 1));
   for (int n = 0; n < N; n += PF) {
     step(x0, n);
     if (PF > 1 && n + 1 < N) step(x1, n + 1);
   }
-  if (N > 0) lds_to_rows<E, C, BV, NT>(o + (otok * H + h) * DV + v0, (size_t)H * DV, sO, LB, onv);
   if (ht != nullptr) {
 #pragma unroll
     for (int s = 0; s < HPW; ++s) {
