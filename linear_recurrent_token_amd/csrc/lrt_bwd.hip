@@ -111,21 +111,25 @@ __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q,
     const int lnv = min(C, T - ln * C);                                                   \
     const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                           \
     const int lh = lbh % H;                                                               \
-    tq.load_rows(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
-    tk.load_rows(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
-    to.load_rows(d_o + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                        \
+    tq.load_rows_clamped(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                  \
+    tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                  \
+    to.load_rows_clamped(d_o + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                \
     rg = wG[(size_t)(tile_) * C + min((int)threadIdx.x, C - 1)];                          \
   }
 
   int tile = blockIdx.x;
   if (tile < ntiles) LRT_LOCAL_LOAD(tile)
   for (; tile < ntiles; tile += gridDim.x) {
-    tq.store(sQ, LK);
-    tk.store(sK, LK);
-    to.store(sdO, LV);
+    const int nv = min(C, T - (tile % N) * C);
+    tq.store_masked(sQ, LK, nv);
+    tk.store_masked(sK, LK, nv);
+    to.store_masked(sdO, LV, nv);
+    asm volatile("" ::"v"(rg));  // consumed by every lane (no load into it left pending)
     if (threadIdx.x < C) sg[threadIdx.x] = rg;
     lds_barrier();
-    if (tile + (int)gridDim.x < ntiles) LRT_LOCAL_LOAD(tile + (int)gridDim.x)
+    // the next tile (the last one again on the final pass: unconditional
+    // loads keep the waits on older ones exact)
+    LRT_LOCAL_LOAD(min(tile + (int)gridDim.x, ntiles - 1))
     for (int tt = w; tt < NB * NB; tt += kWaves) {
       const int ti = tt / NB, tj = tt % NB;
       f32x4 acc = zero4();
@@ -885,18 +889,33 @@ __global__ __launch_bounds__(kThreads) void k_ssd_prep(const E* __restrict__ v, 
   constexpr int LC = C + lds_pad<E>();
   __shared__ __attribute__((aligned(16))) E sVt[DV * LC];
   Tile<E, C, DV> tv;
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
-    const int nv = min(C, T - n * C);
-    const size_t tok0 = (size_t)b * T + (size_t)n * C;
-    tv.load_rows(v + (tok0 * H + h) * DV, (size_t)H * DV, nv);
+  float rla = 0.f;
+  // the next tile loads while this one is transposed (clamped rows and tile
+  // index: unconditional loads, so no wait lands at their issue)
+  auto load = [&](int tile_) {
+    const int ln = tile_ % N, lbh = tile_ / N;
+    const int lnv = min(C, T - ln * C);
+    const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;
+    tv.load_rows_clamped(v + (ltok * H + lbh % H) * DV, (size_t)H * DV, lnv);
+    rla = log_a[(ltok + min(lane_id(), lnv - 1)) * H + lbh % H];
+  };
+  int tile = blockIdx.x;
+  if (tile < ntiles) load(tile);
+  for (; tile < ntiles; tile += gridDim.x) {
+    const int nv = min(C, T - (tile % N) * C);
+    asm volatile("" ::"v"(rla));
     if (threadIdx.x < 64) {
       const int t = threadIdx.x;
-      const float g = wave_incl_scan(t < nv ? log_a[(tok0 + t) * H + h] : 0.f);
+      const float g = wave_incl_scan(t < nv ? rla : 0.f);
       if (t < C) wG[(size_t)tile * C + t] = g;
     }
+    // rows past the end of a ragged last chunk become zero columns
+#pragma unroll
+    for (int s2 = 0; s2 < tv.PT; ++s2)
+      if ((int)(threadIdx.x + kThreads * s2) / tv.PR >= nv) tv.x[s2] = u32x4{0u, 0u, 0u, 0u};
     tv.store_T(sVt, LC);
     lds_barrier();
+    load(min(tile + (int)gridDim.x, ntiles - 1));
     lds_to_block<E, DV, C>(wUt + (size_t)tile * DV * C, sVt, LC);
     lds_barrier();
   }

@@ -116,10 +116,10 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
     const int lnv = min(C, T - ln * C);                                                   \
     const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                           \
     const int lh = lbh % H;                                                               \
-    tk.load_rows(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
-    tq.load_rows(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                          \
-    tv.load_rows(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                          \
-    tg.load_rows(log_a + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                      \
+    tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                  \
+    tq.load_rows_clamped(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                  \
+    tv.load_rows_clamped(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                  \
+    tg.load_rows_clamped(log_a + (ltok * H + lh) * DK, (size_t)H * DK, lnv);              \
     rb = beta[(ltok + min(tid, lnv - 1)) * H + lh]; /* masked where used */               \
   }
 
@@ -127,15 +127,18 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
   if (tile < ntiles) LRT_KDA_LOAD(tile)
   for (; tile < ntiles; tile += gridDim.x) {
     const int nv = min(C, T - (tile % N) * C);
-    tk.store(sK, LK);
-    tq.store(sQ, LK);
-    tg.store(sG, LG);
+    tk.store_masked(sK, LK, nv);
+    tq.store_masked(sQ, LK, nv);
+    tg.store_masked(sG, LG, nv);
+    asm volatile("" ::"v"(rb));  // consumed by every lane (no load into it left pending)
     if (tid < C) sb[tid] = tid < nv ? rb : 0.f;
     if (tid == 0) *sgmax = 0;
     lds_barrier();
-    tv.scale_rows(sb);
+    tv.scale_rows(sb);  // rows past the end scale by 0
     tv.store(sV, LV);
-    if (tile + (int)gridDim.x < ntiles) LRT_KDA_LOAD(tile + (int)gridDim.x)
+    // the next tile (the last one again on the final pass: unconditional
+    // loads keep the waits on older ones exact)
+    LRT_KDA_LOAD(min(tile + (int)gridDim.x, ntiles - 1))
     // ---- G: inclusive cumsum over the chunk's tokens, per key dimension;
     // thread (d, segment) scans RS rows in registers, then adds the totals of
     // the earlier segments
