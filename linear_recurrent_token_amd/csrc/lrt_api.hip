@@ -61,6 +61,8 @@ static int check_common(int B, int T, int H, int dk, int dv, int chunk, int dtyp
   // 64-bit offsets everywhere; keep token counts within int for the grid math
   if ((long long)B * T > 0x7fffffffLL) return LRT_ERR_SHAPE;
   if (chunk != 16 && chunk != 32 && chunk != 64) return LRT_ERR_CHUNK;
+  // a chunk tile's element offsets are 32-bit in the kernels
+  if ((long long)H * (dk > dv ? dk : dv) >= (1LL << 24)) return LRT_ERR_SHAPE;
   // chunk tiles times value blocks index the grids as int
   if ((long long)B * H * ((T + chunk - 1) / chunk) * (dv / 16) > 0x7fffffffLL) return LRT_ERR_SHAPE;
   return LRT_OK;

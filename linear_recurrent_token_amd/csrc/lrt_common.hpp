@@ -278,9 +278,25 @@ __device__ __forceinline__ u32x4 vec_scale(u32x4 x, float s) {
   return x;
 }
 
+// 16 bytes at element offset `off` of a global array, the byte offset formed
+// in 32 bits (so a shared base pointer plus a 32-bit per-lane offset can be
+// addressed without 64-bit vector arithmetic).
+template <typename E>
+__device__ __forceinline__ const u32x4* g16(const E* base, unsigned off) {
+  return (const u32x4*)((const char*)base + off * (unsigned)sizeof(E));
+}
+template <typename E>
+__device__ __forceinline__ u32x4* g16(E* base, unsigned off) {
+  return (u32x4*)((char*)base + off * (unsigned)sizeof(E));
+}
+
 // An R x W tile of E moved global -> registers -> LDS in 16-byte pieces.
 // Every load of a tile is issued before the first LDS store, so a thread
 // keeps all its loads in flight at once (the loops unroll completely).
+// Element offsets within a tile are 32-bit unsigned (the entry points
+// require H * d < 2^24, so r * gs + c < 2^30): added to a base pointer the
+// workgroup shares, they let the compiler address with a scalar base and a
+// 32-bit vector offset instead of per-lane 64-bit arithmetic.
 template <typename E, int R, int W, int NT = kThreads>
 struct Tile {
   static constexpr int V = 16 / (int)sizeof(E);
@@ -297,7 +313,7 @@ struct Tile {
       x[s] = u32x4{0u, 0u, 0u, 0u};
       if (NP % NT == 0 || idx < NP) {
         const int r = idx / PR, c = (idx % PR) * V;
-        if (r < nvalid) x[s] = *(const u32x4*)(g + (size_t)r * gs + c);
+        if (r < nvalid) x[s] = *g16(g, (unsigned)r * (unsigned)gs + (unsigned)c);
       }
     }
   }
@@ -310,7 +326,7 @@ struct Tile {
       const int idx = threadIdx.x + NT * s;
       if (NP % NT == 0 || idx < NP) {
         const int r = idx / PR, c = (idx % PR) * V;
-        x[s] = *(const u32x4*)(g + (size_t)min(r, nvalid - 1) * gs + c);
+        x[s] = *g16(g, (unsigned)min(r, nvalid - 1) * (unsigned)gs + (unsigned)c);
       }
     }
   }
@@ -330,7 +346,7 @@ struct Tile {
 #pragma unroll
     for (int s = 0; s < PT; ++s) {
       const int idx = threadIdx.x + NT * s;
-      if (NP % NT == 0 || idx < NP) x[s] = *(const u32x4*)(g + (size_t)idx * V);
+      if (NP % NT == 0 || idx < NP) x[s] = *g16(g, (unsigned)idx * (unsigned)V);
     }
   }
   __device__ __forceinline__ void scale_rows(const float* rs) {
@@ -369,7 +385,7 @@ struct Tile {
       const int idx = threadIdx.x + NT * s;
       if (NP % NT == 0 || idx < NP) {
         const int r = idx / PR, c = (idx % PR) * V;
-        if (r < nvalid) *(u32x4*)(g + (size_t)r * gs + c) = x[s];
+        if (r < nvalid) *g16(g, (unsigned)r * (unsigned)gs + (unsigned)c) = x[s];
       }
     }
   }
@@ -396,7 +412,7 @@ __device__ __forceinline__ void lds_to_block(E* g, const E* lds, int ls) {
     const int idx = threadIdx.x + NT * s;
     if ((R * PR) % NT == 0 || idx < R * PR) {
       const int r = idx / PR, c = (idx % PR) * V;
-      *(u32x4*)(g + (size_t)r * W + c) = *(const u32x4*)(lds + r * ls + c);
+      *g16(g, (unsigned)r * (unsigned)W + (unsigned)c) = *(const u32x4*)(lds + r * ls + c);
     }
   }
 }
@@ -408,7 +424,7 @@ __device__ __forceinline__ void lds_to_block(E* g, const E* lds, int ls) {
 // row-major in LDS, X[16tb + l%16][16ta + 4(l/16) + r] = value r of lane l.
 template <typename E>
 __device__ __forceinline__ void acc_tile_store(E* base, int tile_id, f32x4 acc) {
-  store4<E>(base + ((size_t)tile_id * 64 + lane_id()) * 4, acc);
+  store4<E>((E*)((char*)base + ((unsigned)tile_id * 64u + (unsigned)lane_id()) * 4u * (unsigned)sizeof(E)), acc);
 }
 // load() issues the global loads into registers (packed, so nothing waits
 // for them), store() writes X into LDS.
@@ -421,7 +437,7 @@ struct AccTiles {
 #pragma unroll
     for (int s = 0; s < PT; ++s) {
       const int p = min((int)threadIdx.x + NT * s, NS - 1);
-      x[s] = load4_raw<E>(g + (size_t)p * 4);
+      x[s] = load4_raw<E>((const E*)((const char*)g + (unsigned)p * 4u * (unsigned)sizeof(E)));
     }
   }
   __device__ __forceinline__ void store(E* lds, int ld) const {
@@ -447,7 +463,7 @@ __device__ __forceinline__ void lds_to_rows(E* g, size_t gs, const E* lds, int l
     const int idx = threadIdx.x + NT * s;
     if ((R * PR) % NT == 0 || idx < R * PR) {
       const int r = idx / PR, c = (idx % PR) * V;
-      if (r < nvalid) *(u32x4*)(g + (size_t)r * gs + c) = *(const u32x4*)(lds + r * ls + c);
+      if (r < nvalid) *g16(g, (unsigned)r * (unsigned)gs + (unsigned)c) = *(const u32x4*)(lds + r * ls + c);
     }
   }
 }
@@ -463,7 +479,7 @@ __device__ __forceinline__ void lds_to_rows_clamped(E* g, size_t gs, const E* ld
     const int idx = threadIdx.x + NT * s;
     if ((R * PR) % NT == 0 || idx < R * PR) {
       const int r = min(idx / PR, nvalid - 1), c = (idx % PR) * V;
-      *(u32x4*)(g + (size_t)r * gs + c) = *(const u32x4*)(lds + r * ls + c);
+      *g16(g, (unsigned)r * (unsigned)gs + (unsigned)c) = *(const u32x4*)(lds + r * ls + c);
     }
   }
 }
