@@ -73,6 +73,9 @@ def test_validation_errors_before_any_launch(L):
     assert _fwd(L, T=-1, **ok) == c["LRT_ERR_SHAPE"]
     assert _fwd(L, chunk=128, **ok) == c["LRT_ERR_CHUNK"]
     assert _fwd(L, chunk=8, **ok) == c["LRT_ERR_CHUNK"]
+    # a chunk tile's offsets must fit 32 bits: H * max(d_k, d_v) < 2^24
+    assert _fwd(L, H=1 << 17, dk=128, dv=16, **ok) == c["LRT_ERR_SHAPE"]
+    assert _fwd(L, H=(1 << 17) - 1, dk=128, dv=16, **ok) == c["LRT_ERR_WORKSPACE"]
     for missing in ("q", "k", "v", "la", "b", "o"):
         a = dict(ok)
         a[missing] = None
