@@ -1,8 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the Gated DeltaNet training step on one MI355X.
 
-One step = gdn_fwd + gdn_bwd (all six gradients) over one batch of the
-pretraining-shaped workload: B=16 sequences of T=2048 tokens, H=8 heads,
+One step = gdn_fwd_train + gdn_bwd_saved (the forward keeps the WY factors,
+chunk-start states and new values the backward needs; the backward computes
+all six gradients from them) over one batch of the pretraining-shaped
+workload: B=16 sequences of T=2048 tokens, H=8 heads,
 d_k = d_v = 128, chunk 64, bf16 tensors, fp32 gates and state (the shape of
 the 2048-token bf16 runs on the AMD ROCm blog "Pretraining hybrid LLMs with
 Primus", Table 4).  Inputs are synthetic (seeded), resident in HBM before the
@@ -30,16 +32,23 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 MFMA_FP32_PEAK_TFLOPS = 157.3
 WORKLOAD = "gdn_train_bf16_2k"  # the headline workload (default)
-# other named workloads bench.py can time (context lines; not the headline)
+# the headline and other named workloads bench.py can time (context lines)
 WORKLOADS = {
     "gdn_train_bf16_2k": ("GDN chunked fwd+bwd tokens/s and % bf16 MFMA peak, B=16 T=2048 H=8 d=128",
-                          "gdn_fwd + gdn_bwd"),
+                          "gdn_fwd_train + gdn_bwd_saved"),
+    # the same step through the stateless pair (the backward recomputes the forward)
+    "gdn_train_recompute_bf16_2k": ("GDN chunked fwd+bwd (backward recomputes) tokens/s, B=16 T=2048 H=8 d=128",
+                                    "gdn_fwd + gdn_bwd"),
     "gdn_bf16_2k": ("GDN chunked fwd tokens/s, B=16 T=2048 H=8 d=128", "gdn_fwd"),
     "ssd_bf16_2k": ("SSD (Mamba2 case) chunked fwd tokens/s, B=16 T=2048 H=8 d=128", "ssd_fwd"),
     "ssd_train_bf16_2k": ("SSD (Mamba2 case) chunked fwd+bwd tokens/s, B=16 T=2048 H=8 d=128",
                           "ssd_fwd + ssd_bwd"),
     "kda_bf16_1m": ("KDA chunked fwd tokens/s, B=1 T=2^20 H=16 d=128", "kda_fwd"),
 }
+
+
+# workloads that time another op on an existing workload's inputs
+CONFIG_OF = {"gdn_train_recompute_bf16_2k": "gdn_train_bf16_2k"}
 
 
 def parse():
@@ -131,6 +140,13 @@ def kernel_model(name, c, esz=2, op="gdn_fwd + gdn_bwd"):
         "k_grad2": ((dk + dv) * e + 8 + C * e + dk * e + dv * e + dk * e + 4 + (dk + dv) * e + 8, 0,
                     2 * C * dk + 2 * C * dv + 2 * C * dk + 2 * C * dv + 4 * C * C + 2 * C * dk + 4 * C * dk),
     }
+    if op == "gdn_fwd_train + gdn_bwd_saved":
+        # the forward also keeps what the backward reads: the WY pass writes T
+        # beside W, U'^T, g and P; the scan writes the chunk-start states and U^T
+        b_th, b_bh, f_th = per["k_wy"]
+        per["k_wy"] = (b_th + C * e, b_bh, f_th)
+        b_th, b_bh, f_th = per["k_scan"]
+        per["k_scan"] = (b_th + dk * dv * e / C + dv * e, b_bh, f_th)
     if op.startswith("ssd"):
         # the fused Mamba2 forward: reads q, k, v, log_a, h0; writes o, ht
         per["k_ssd_fwd"] = ((2 * dk + dv) * e + 4 + dv * e, 2 * st, 2 * C * (dk + dv) + 4 * dk * dv)
@@ -225,15 +241,16 @@ def main():
     L.lib()
     wl = args.workload
     metric, op = WORKLOADS[wl]
-    c = dict(synth.CONFIGS[wl])
+    cfg = CONFIG_OF.get(wl, wl)
+    c = dict(synth.CONFIGS[cfg])
     B, T, H, dk, dv, C = c["B"], c["T"], c["H"], c["dk"], c["dv"], c["chunk"]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     # input sets larger than the last-level cache need no rotation
     nsets = args.sets if B * T * H * (2 * dk + dv) * 2 < (1 << 30) else 1
-    sets = make_sets(L, synth, torch, wl, nsets)
+    sets = make_sets(L, synth, torch, cfg, nsets)
     code = L.LRT_BF16
-    opc = {"gdn_fwd + gdn_bwd": L.OP_GDN_BWD, "gdn_fwd": L.OP_GDN_FWD, "ssd_fwd": L.OP_SSD_FWD,
+    opc = {"gdn_fwd + gdn_bwd": L.OP_GDN_BWD, "gdn_fwd_train + gdn_bwd_saved": L.OP_GDN_BWD, "gdn_fwd": L.OP_GDN_FWD, "ssd_fwd": L.OP_SSD_FWD,
            "ssd_fwd + ssd_bwd": L.OP_SSD_BWD, "kda_fwd": L.OP_KDA_FWD}[op]
     ws_bytes = max(L.workspace_bytes(L.OP_GDN_FWD, B, T, H, dk, dv, C, code),
                    L.workspace_bytes(opc, B, T, H, dk, dv, C, code))
@@ -241,7 +258,7 @@ def main():
     o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
     ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     grads = None
-    if op.endswith("_bwd"):
+    if op.endswith(("_bwd", "_bwd_saved")):
         grads = (torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
                  torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
                  torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev),
@@ -255,6 +272,12 @@ def main():
         s = sets[i % len(sets)]
         if op.startswith("ssd"):
             L.ssd_fwd(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), chunk=C, o=o, ht=ht, workspace=ws)
+        elif op == "gdn_fwd_train + gdn_bwd_saved":
+            L.gdn_fwd_train(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), chunk=C, o=o, ht=ht,
+                            workspace=ws)
+            L.gdn_bwd_saved(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), s["do"], ws, s.get("dht"),
+                            chunk=C, out=grads)
+            return
         elif op == "kda_fwd":
             L.kda_fwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), chunk=C, o=o, ht=ht,
                       workspace=ws)

@@ -6,9 +6,10 @@
  * models are defined in Primus", mixer list under Table 2):
  *   - Mamba2 (ssd_fwd, ssd_bwd): the state is decayed by one scalar gate per head and a
  *     rank-one k v^T write is added each token;
- *   - Gated DeltaNet (gdn_fwd, gdn_bwd): Mamba2 plus the delta rule, which
- *     replaces the value stored under the current key instead of only adding;
- *     one scalar forget gate per head;
+ *   - Gated DeltaNet (gdn_fwd, gdn_bwd; gdn_fwd_train + gdn_bwd_saved for a
+ *     training step that keeps the forward's intermediates): Mamba2 plus the
+ *     delta rule, which replaces the value stored under the current key
+ *     instead of only adding; one scalar forget gate per head;
  *   - Kimi Delta Attention (kda_fwd): GDN with one gate value per key
  *     dimension (the low-rank projection producing it is the caller's).
  *
@@ -99,6 +100,33 @@ int gdn_bwd(const void* q, const void* k, const void* v, const float* log_a, con
             const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv,
             float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v,
             int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Gated DeltaNet forward for training: gdn_fwd (same arguments, same o and
+ * ht) that also leaves in the workspace what gdn_bwd would recompute -- the
+ * WY factors W and T = (I + A)^-1, the in-chunk gate cumsums, the
+ * chunk-start states and the new values U of the chunkwise form (the Gated
+ * DeltaNet recurrence of the mixer list under Table 2 of the AMD ROCm blog
+ * "Pretraining hybrid LLMs with Primus") -- for gdn_bwd_saved.  The
+ * workspace must hold lrt_workspace_bytes(LRT_OP_GDN_BWD, ...) bytes.
+ * Shape limits are gdn_bwd's (LRT_F32: d_k, d_v <= 64, chunk <= 32).
+ */
+int gdn_fwd_train(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                  const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk,
+                  int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_bwd without the recompute: the workspace must be the one a preceding
+ * gdn_fwd_train of the same q, k, v, log_a, beta, h0 and sizes filled (stream
+ * ordered after it), unmodified since.  Arguments, outputs and errors as
+ * gdn_bwd.  The saved tensors stay in place (the backward's own scratch
+ * lies elsewhere in the workspace), so further gdn_bwd_saved calls, e.g. for
+ * another d_o, may follow.
+ */
+int gdn_bwd_saved(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                  const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv,
+                  float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v,
+                  int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Kimi Delta Attention forward: as gdn_fwd, with log_a of shape [B, T, H, d_k]

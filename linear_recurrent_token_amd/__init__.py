@@ -9,6 +9,8 @@ is missing, every call raises.
 Entry points (names as in include/lrt.h):
   gdn_fwd(q, k, v, log_a, beta, h0=None, chunk=64)            -> (o, ht)
   gdn_bwd(q, k, v, log_a, beta, h0, do, dht=None, chunk=64)   -> (dq, dk, dv, dlog_a, dbeta, dh0)
+  gdn_fwd_train(q, k, v, log_a, beta, h0=None, chunk=64)      -> (o, ht, saved)
+  gdn_bwd_saved(q, k, v, log_a, beta, h0, do, saved, dht=None, chunk=64) -> as gdn_bwd
   kda_fwd(q, k, v, log_a, beta, h0=None, chunk=64)            -> (o, ht)
   ssd_fwd(q, k, v, log_a, h0=None, chunk=64)                   -> (o, ht)
   ssd_bwd(q, k, v, log_a, h0, do, dht=None, chunk=64)          -> (dq, dk, dv, dlog_a, dh0)
@@ -25,7 +27,7 @@ LIB_PATH = os.path.join(HERE, "liblrt.so")
 
 LRT_F32, LRT_BF16 = 0, 1
 OP_GDN_FWD, OP_GDN_BWD, OP_KDA_FWD, OP_SSD_FWD, OP_SSD_BWD = 0, 1, 2, 3, 4
-EXPORTS = ("gdn_fwd", "gdn_bwd", "kda_fwd", "ssd_fwd", "ssd_bwd", "lrt_workspace_bytes", "lrt_status_string",
+EXPORTS = ("gdn_fwd", "gdn_bwd", "gdn_fwd_train", "gdn_bwd_saved", "kda_fwd", "ssd_fwd", "ssd_bwd", "lrt_workspace_bytes", "lrt_status_string",
            "lrt_profile_attach", "lrt_profile_count", "lrt_kernel_name")
 
 _lib = None
@@ -51,7 +53,9 @@ def lib():
         L.ssd_fwd.argtypes = [vp] * 7 + [ci] * 7 + [vp, sz, vp]
         L.gdn_bwd.argtypes = [vp] * 14 + [ci] * 7 + [vp, sz, vp]
         L.ssd_bwd.argtypes = [vp] * 12 + [ci] * 7 + [vp, sz, vp]
-        for f in ("gdn_fwd", "kda_fwd", "ssd_fwd", "gdn_bwd", "ssd_bwd"):
+        L.gdn_fwd_train.argtypes = [vp] * 8 + [ci] * 7 + [vp, sz, vp]
+        L.gdn_bwd_saved.argtypes = [vp] * 14 + [ci] * 7 + [vp, sz, vp]
+        for f in ("gdn_fwd", "kda_fwd", "ssd_fwd", "gdn_bwd", "ssd_bwd", "gdn_fwd_train", "gdn_bwd_saved"):
             getattr(L, f).restype = ci
         L.lrt_workspace_bytes.argtypes = [ci] * 8
         L.lrt_workspace_bytes.restype = sz
@@ -115,7 +119,7 @@ def _workspace(op, dev, B, T, H, dk, dv, chunk, dt, workspace):
     return workspace, need
 
 
-def _fwd(fn, op, q, k, v, log_a, beta, h0, chunk, o, ht, workspace, kda=False):
+def _fwd(fn, op, q, k, v, log_a, beta, h0, chunk, o, ht, workspace, kda=False, want_ws=False):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -149,12 +153,27 @@ def _fwd(fn, op, q, k, v, log_a, beta, h0, chunk, o, ht, workspace, kda=False):
                     code, _p(ws), need, _stream(dev))
     if rc != 0:
         raise LrtError(fn.__name__, rc)
-    return o, ht
+    return (o, ht, ws) if want_ws else (o, ht)
 
 
 def gdn_fwd(q, k, v, log_a, beta, h0=None, chunk=64, o=None, ht=True, workspace=None):
     """Gated DeltaNet forward -> (o, ht).  ht=False skips the final state."""
     return _fwd(lib().gdn_fwd, OP_GDN_FWD, q, k, v, log_a, beta, h0, chunk, o, ht, workspace)
+
+
+def gdn_fwd_train(q, k, v, log_a, beta, h0=None, chunk=64, o=None, ht=True, workspace=None):
+    """Gated DeltaNet forward that keeps what the backward needs -> (o, ht,
+    saved); pass ``saved`` (a uint8 workspace of the backward's size) to
+    gdn_bwd_saved."""
+    return _fwd(lib().gdn_fwd_train, OP_GDN_BWD, q, k, v, log_a, beta, h0, chunk, o, ht, workspace, want_ws=True)
+
+
+def gdn_bwd_saved(q, k, v, log_a, beta, h0, do, saved, dht=None, chunk=64, want_dh0=True, out=None):
+    """Gated DeltaNet backward from gdn_fwd_train's ``saved`` workspace (no
+    recompute) -> (dq, dk, dv, dlog_a, dbeta, dh0 or None)."""
+    if saved is None:
+        raise ValueError("saved: the workspace gdn_fwd_train returned")
+    return _bwd(True, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, saved, out, fn="gdn_bwd_saved")
 
 
 def kda_fwd(q, k, v, log_a, beta, h0=None, chunk=64, o=None, ht=True, workspace=None):
@@ -180,7 +199,7 @@ def ssd_bwd(q, k, v, log_a, h0, do, dht=None, chunk=64, want_dh0=True, workspace
     return g[:4] + g[5:]
 
 
-def _bwd(delta, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, workspace, out):
+def _bwd(delta, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, workspace, out, fn="gdn_bwd"):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -204,12 +223,12 @@ def _bwd(delta, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, workspace, o
     ws, need = _workspace(op, dev, B, T, H, dk, dv, chunk, code, workspace)
     with torch.cuda.device(dev):
         if delta:
-            rc = lib().gdn_bwd(_p(q), _p(k), _p(v), _p(log_a), _p(beta), _p(h0), _p(do), _p(dht), _p(gq), _p(gk),
-                               _p(gv), _p(gla), _p(gb), _p(gh0), B, T, H, dk, dv, chunk, code, _p(ws), need,
-                               _stream(dev))
+            rc = getattr(lib(), fn)(_p(q), _p(k), _p(v), _p(log_a), _p(beta), _p(h0), _p(do), _p(dht), _p(gq),
+                                    _p(gk), _p(gv), _p(gla), _p(gb), _p(gh0), B, T, H, dk, dv, chunk, code, _p(ws),
+                                    need, _stream(dev))
         else:
             rc = lib().ssd_bwd(_p(q), _p(k), _p(v), _p(log_a), _p(h0), _p(do), _p(dht), _p(gq), _p(gk), _p(gv),
                                _p(gla), _p(gh0), B, T, H, dk, dv, chunk, code, _p(ws), need, _stream(dev))
     if rc != 0:
-        raise LrtError("gdn_bwd" if delta else "ssd_bwd", rc)
+        raise LrtError(fn if delta else "ssd_bwd", rc)
     return gq, gk, gv, gla, gb, gh0

@@ -85,7 +85,8 @@ static int launch_empty(const float* h0, float* ht, int B, int H, int dk, int dv
 
 static int fwd_entry(int variant, const void* q, const void* k, const void* v, const float* log_a,
                      const float* beta, const float* h0, void* o, float* ht, int B, int T, int H, int dk,
-                     int dv, int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                     int dv, int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                     bool train = false) {
   int rc = check_common(B, T, H, dk, dv, chunk, dtype);
   if (rc) return rc;
   // with T == 0 the token tensors are empty and may carry NULL pointers
@@ -98,18 +99,20 @@ static int fwd_entry(int variant, const void* q, const void* k, const void* v, c
   const void* sca[] = {log_a, beta, h0, ht};
   for (const void* p : sca)
     if (p && !aligned4(p)) return LRT_ERR_ALIGN;
-  const int op = variant == kVarGDN ? LRT_OP_GDN_FWD : variant == kVarSSD ? LRT_OP_SSD_FWD : LRT_OP_KDA_FWD;
+  const int op = train ? LRT_OP_GDN_BWD
+                       : variant == kVarGDN ? LRT_OP_GDN_FWD : variant == kVarSSD ? LRT_OP_SSD_FWD : LRT_OP_KDA_FWD;
   if (!workspace || workspace_bytes < ws_bytes(op, B, T, H, dk, dv, chunk, dtype)) return LRT_ERR_WORKSPACE;
   if (T == 0) return launch_empty(h0, ht, B, H, dk, dv, stream);
   FwdArgs a{variant, q, k, v, log_a, beta, h0, o, ht, B, T, H, dk, dv, chunk, dtype, workspace, stream};
-  rc = variant == kVarKDA ? fwd_kda(a) : fwd_scalar_gate(a);
-  return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : LRT_ERR_SHAPE);
+  rc = train ? fwd_gdn_train(a) : variant == kVarKDA ? fwd_kda(a) : fwd_scalar_gate(a);
+  return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
 }
 
 static int bwd_entry(int variant, const void* q, const void* k, const void* v, const float* log_a,
                      const float* beta, const float* h0, const void* d_o, const float* dht, void* dq, void* dk,
                      void* dv, float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v,
-                     int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                     int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                     bool saved = false) {
   int rc = check_common(B, T, H, d_k, d_v, chunk, dtype);
   if (rc) return rc;
   const bool delta = variant == kVarGDN;
@@ -126,7 +129,7 @@ static int bwd_entry(int variant, const void* q, const void* k, const void* v, c
   if (T == 0) return launch_empty(dht, dh0, B, H, d_k, d_v, stream);
   BwdArgs a{q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0,
             B, T, H, d_k, d_v, chunk, dtype, workspace, stream};
-  rc = delta ? bwd_gdn(a) : bwd_ssd(a);
+  rc = delta ? bwd_gdn(a, saved) : bwd_ssd(a);
   return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
 }
 
@@ -163,6 +166,21 @@ int gdn_bwd(const void* q, const void* k, const void* v, const float* log_a, con
             int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_entry(kVarGDN, q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0, B, T, H, d_k, d_v,
                    chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+int gdn_fwd_train(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                  const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk,
+                  int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_entry(kVarGDN, q, k, v, log_a, beta, h0, o, ht, B, T, H, d_k, d_v, chunk, dtype, workspace,
+                   workspace_bytes, stream, true);
+}
+
+int gdn_bwd_saved(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                  const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv,
+                  float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v, int chunk,
+                  int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_entry(kVarGDN, q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0, B, T, H, d_k, d_v,
+                   chunk, dtype, workspace, workspace_bytes, stream, true);
 }
 
 int ssd_bwd(const void* q, const void* k, const void* v, const float* log_a, const float* h0, const void* d_o,

@@ -922,8 +922,42 @@ __global__ __launch_bounds__(kThreads) void k_ssd_prep(const E* __restrict__ v, 
 }
 
 // --------------------------------------------------------------- launcher
+// The forward quantities the gradient kernels read, recomputed: WY factors
+// with T (k_wy), then the chunk-start states S_n and U (k_scan, backward mode).
 template <typename E, int C, int DK, int DV>
-int bwd_impl(const BwdArgs& a) {
+void bwd_recompute(const BwdWs& ws, const void* k, const void* v, const float* log_a, const float* beta,
+                   const float* h0, int B, int T, int H, void* stream) {
+  const int N = (T + C - 1) / C;
+  const int tiles = B * H * N;
+  hipStream_t st = (hipStream_t)stream;
+  constexpr int BV = DV < 64 ? DV : 64;  // state columns per workgroup
+  LRT_LAUNCH(kKWyBwd, (k_wy<E, C, DK, DV, false, true, kWyWaves>),
+             dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), st, (const E*)nullptr,
+             (const E*)k, (const E*)v, log_a, beta, T, H, N, tiles, (E*)ws.f.W, (E*)ws.f.Up, ws.f.G, (E*)nullptr,
+             (E*)ws.T);
+  ScanArgs<E> sa{};
+  sa.k = (const E*)k;
+  sa.W = (const E*)ws.f.W;
+  sa.Up = (const E*)ws.f.Up;
+  sa.G = ws.f.G;
+  sa.hin = h0;
+  sa.hs_ld = DV;
+  sa.U = (E*)ws.f.U;
+  sa.S = (E*)ws.f.S;
+  sa.T = T;
+  sa.H = H;
+  sa.N = N;
+  sa.L = N;
+  sa.nseg = 1;
+  sa.DV = DV;
+  LRT_LAUNCH(kKScanBwd, (k_scan<E, C, DK, BV, kScanBwd, false, kStateWaves>), dim3(B * H * (DV / BV)),
+             dim3(64 * kStateWaves), st, sa);
+}
+
+// saved: the workspace already holds W, g, T, S_n and U from gdn_fwd_train
+// of the same arguments, so the recompute is skipped.
+template <typename E, int C, int DK, int DV>
+int bwd_impl(const BwdArgs& a, bool saved) {
   // fp32 gradient tiles need twice the LDS of bf16 ones: the fp32 backward
   // is limited to d_k, d_v <= 64 and chunk <= 32
   if constexpr (sizeof(E) == 4 && (DK > 64 || DV > 64)) {
@@ -937,30 +971,7 @@ int bwd_impl(const BwdArgs& a) {
     hipStream_t st = (hipStream_t)a.stream;
     constexpr int BV = DV < 64 ? DV : 64;  // state columns per workgroup
     const int sgrid = a.B * a.H * (DV / BV);
-    // recompute: WY factors with T, then the chunk-start states and U
-    LRT_LAUNCH(kKWyBwd, (k_wy<E, C, DK, DV, false, true, kWyWaves>),
-               dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), st, (const E*)nullptr,
-               (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.f.W, (E*)ws.f.Up, ws.f.G,
-               (E*)nullptr, (E*)ws.T);
-    {
-      ScanArgs<E> sa{};
-      sa.k = (const E*)a.k;
-      sa.W = (const E*)ws.f.W;
-      sa.Up = (const E*)ws.f.Up;
-      sa.G = ws.f.G;
-      sa.hin = a.h0;
-      sa.hs_ld = DV;
-      sa.U = (E*)ws.f.U;
-      sa.S = (E*)ws.f.S;
-      sa.T = a.T;
-      sa.H = a.H;
-      sa.N = N;
-      sa.L = N;
-      sa.nseg = 1;
-      sa.DV = DV;
-      LRT_LAUNCH(kKScanBwd, (k_scan<E, C, DK, BV, kScanBwd, false, kStateWaves>), dim3(sgrid),
-                 dim3(64 * kStateWaves), st, sa);
-    }
+    if (!saved) bwd_recompute<E, C, DK, DV>(ws, a.k, a.v, a.log_a, a.beta, a.h0, a.B, a.T, a.H, a.stream);
     E* dUl = (E*)ws.f.Up;
     LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV>), dim3(persistent_grid(tiles, LocalLds<E, C, DK, DV>::TOTAL)), dim3(kThreads), st,
                (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N, tiles);
@@ -1031,11 +1042,43 @@ int ssd_bwd_impl(const BwdArgs& a) {
   }
 }
 
-template <typename E, bool SSD>
-static int bwd_dtype(const BwdArgs& a) {
-#define LRT_CASE(C_, DK_, DV_)                     \
-  if (a.chunk == C_ && a.dk == DK_ && a.dv == DV_) \
-    return SSD ? ssd_bwd_impl<E, C_, DK_, DV_>(a) : bwd_impl<E, C_, DK_, DV_>(a);
+// Gated DeltaNet forward for training: the forward (o, ht) written into the
+// backward's workspace together with what the backward reads -- W, g and T
+// from the WY pass (which also writes P for the scan), S_n and U from the scan
+// -- so that gdn_bwd_saved skips the recompute.
+template <typename E, int C, int DK, int DV>
+int fwd_train_impl(const FwdArgs& a) {
+  if constexpr (sizeof(E) == 4 && (DK > 64 || DV > 64)) {
+    return -2;
+  } else if constexpr (sizeof(E) == 4 && C > 32) {
+    return -3;
+  } else {
+    const BwdWs ws = bwd_ws_layout(a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
+    constexpr int BV64 = DV < 64 ? DV : 64;
+    if constexpr (WyLds<E, C, DK, DV>::TOTAL <= 160 * 1024 &&
+                  ScanLds<E, C, DK, BV64, kScanFwd, false>::TOTAL <= 160 * 1024) {
+      const int N = (a.T + C - 1) / C;
+      const int tiles = a.B * a.H * N;
+      LRT_LAUNCH(kKWy, (k_wy<E, C, DK, DV, true, true, kWyWaves>),
+                 dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), a.stream,
+                 (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.f.W,
+                 (E*)ws.f.Up, ws.f.G, (E*)ws.f.P, (E*)ws.T);
+      if (hipGetLastError() != hipSuccess) return -7;
+      return launch_scan_fwd<E, C, DK, DV, false, true>(a, ws.f, N);
+    } else {
+      // no split forward at this size: the plain forward, then the recompute
+      const int rc = fwd_scalar_gate(a);
+      if (rc != 0) return rc;
+      bwd_recompute<E, C, DK, DV>(ws, a.k, a.v, a.log_a, a.beta, a.h0, a.B, a.T, a.H, a.stream);
+      return hipGetLastError() == hipSuccess ? 0 : -7;
+    }
+  }
+}
+
+template <typename E>
+static int fwd_train_dtype(const FwdArgs& a) {
+#define LRT_CASE(C_, DK_, DV_) \
+  if (a.chunk == C_ && a.dk == DK_ && a.dv == DV_) return fwd_train_impl<E, C_, DK_, DV_>(a);
 #define LRT_DV(C_, DK_) LRT_CASE(C_, DK_, 16) LRT_CASE(C_, DK_, 32) LRT_CASE(C_, DK_, 64) LRT_CASE(C_, DK_, 128)
 #define LRT_DK(C_) LRT_DV(C_, 16) LRT_DV(C_, 32) LRT_DV(C_, 64) LRT_DV(C_, 128)
   LRT_DK(16) LRT_DK(32) LRT_DK(64)
@@ -1045,7 +1088,25 @@ static int bwd_dtype(const BwdArgs& a) {
   return -2;
 }
 
-int bwd_gdn(const BwdArgs& a) { return a.dtype == 1 ? bwd_dtype<bf16, false>(a) : bwd_dtype<float, false>(a); }
-int bwd_ssd(const BwdArgs& a) { return a.dtype == 1 ? bwd_dtype<bf16, true>(a) : bwd_dtype<float, true>(a); }
+int fwd_gdn_train(const FwdArgs& a) { return a.dtype == 1 ? fwd_train_dtype<bf16>(a) : fwd_train_dtype<float>(a); }
+
+template <typename E, bool SSD>
+static int bwd_dtype(const BwdArgs& a, bool saved) {
+#define LRT_CASE(C_, DK_, DV_)                     \
+  if (a.chunk == C_ && a.dk == DK_ && a.dv == DV_) \
+    return SSD ? ssd_bwd_impl<E, C_, DK_, DV_>(a) : bwd_impl<E, C_, DK_, DV_>(a, saved);
+#define LRT_DV(C_, DK_) LRT_CASE(C_, DK_, 16) LRT_CASE(C_, DK_, 32) LRT_CASE(C_, DK_, 64) LRT_CASE(C_, DK_, 128)
+#define LRT_DK(C_) LRT_DV(C_, 16) LRT_DV(C_, 32) LRT_DV(C_, 64) LRT_DV(C_, 128)
+  LRT_DK(16) LRT_DK(32) LRT_DK(64)
+#undef LRT_DK
+#undef LRT_DV
+#undef LRT_CASE
+  return -2;
+}
+
+int bwd_gdn(const BwdArgs& a, bool saved) {
+  return a.dtype == 1 ? bwd_dtype<bf16, false>(a, saved) : bwd_dtype<float, false>(a, saved);
+}
+int bwd_ssd(const BwdArgs& a) { return a.dtype == 1 ? bwd_dtype<bf16, true>(a, false) : bwd_dtype<float, true>(a, false); }
 
 }  // namespace lrt

@@ -238,7 +238,9 @@ struct ScanLds {
 // transition M (the state map is affine: H_end = M H_start + E).
 // DELTA = false is the Mamba2 recurrence (no delta term: W = 0, U = U' = V,
 // with U'^T supplied in a.Up); the backward recompute then writes only S_n.
-template <typename E, int C, int DK, int BV, int MODE, bool KDA, int NW = 8, bool DELTA = true>
+// SAVE (forward mode) also writes S_n and U, as the backward recompute does,
+// for a backward that reuses them.
+template <typename E, int C, int DK, int BV, int MODE, bool KDA, int NW = 8, bool DELTA = true, bool SAVE = false>
 __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
   typedef ScanLds<E, C, DK, BV, MODE, KDA> Lay;
   constexpr bool FWD = MODE == kScanFwd;
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
     // loads keep the compiler's wait for the next set exact)
     fetch(x, min(n + 2, n1 - 1));
     lds_barrier();
-    if constexpr (MODE == kScanBwd) lds_to_block<E, BV, DK, NT>(a.S + (tile * DV + v0) * DK, sS, LK);
+    if constexpr (MODE == kScanBwd || SAVE) lds_to_block<E, BV, DK, NT>(a.S + (tile * DV + v0) * DK, sS, LK);
     // ---- U = U' - W Hn -> U^T (GDN: and (e^(g_C - g) U)^T)
 #pragma unroll
     for (int s = 0; s < UPW; ++s) {
@@ -383,7 +385,7 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
         store4<E>(sU + vv * LC + t, u);
         if constexpr (!KDA)
           store4<E>(sUk + vv * LC + t, f32x4{u[0] * skt[t], u[1] * skt[t + 1], u[2] * skt[t + 2], u[3] * skt[t + 3]});
-        if constexpr (MODE == kScanBwd && DELTA) store4<E>(a.U + (tile * DV + v0 + vv) * C + t, u);
+        if constexpr ((MODE == kScanBwd || SAVE) && DELTA) store4<E>(a.U + (tile * DV + v0 + vv) * C + t, u);
       }
     }
     lds_barrier();
@@ -539,7 +541,7 @@ __global__ __launch_bounds__(64 * NW) void k_carry(const float* __restrict__ hlo
 // few to occupy the device the sequence is cut into segments: a local pass
 // per segment, the carry over segments, and the scan from the true segment
 // start states.
-template <typename E, int C, int DK, int DV, int BV, bool KDA>
+template <typename E, int C, int DK, int DV, int BV, bool KDA, bool SAVE = false>
 int launch_scan_fwd_bv(const FwdArgs& a, const FwdWs& ws, int N, int nseg) {
   hipStream_t st = (hipStream_t)a.stream;
   ScanArgs<E> s{};
@@ -553,6 +555,8 @@ int launch_scan_fwd_bv(const FwdArgs& a, const FwdWs& ws, int N, int nseg) {
   s.G = ws.G;
   s.GC = ws.GC;
   s.o = (E*)a.o;
+  s.S = (E*)ws.S;  // written only by SAVE
+  s.U = (E*)ws.U;
   s.T = a.T;
   s.H = a.H;
   s.N = N;
@@ -564,7 +568,8 @@ int launch_scan_fwd_bv(const FwdArgs& a, const FwdWs& ws, int N, int nseg) {
     s.hs_ld = DV;
     s.L = N;
     s.nseg = 1;
-    LRT_LAUNCH(kKScan, (k_scan<E, C, DK, BV, kScanFwd, KDA, kStateWaves>), dim3(bhv), dim3(64 * kStateWaves), st, s);
+    LRT_LAUNCH(kKScan, (k_scan<E, C, DK, BV, kScanFwd, KDA, kStateWaves, true, SAVE>), dim3(bhv),
+               dim3(64 * kStateWaves), st, s);
   } else {
     s.L = (N + nseg - 1) / nseg;
     s.nseg = nseg;
@@ -578,21 +583,21 @@ int launch_scan_fwd_bv(const FwdArgs& a, const FwdWs& ws, int N, int nseg) {
     s.hin = ws.SegStart;
     s.hout = nullptr;
     s.hs_ld = DV;
-    LRT_LAUNCH(kKScan, (k_scan<E, C, DK, BV, kScanFwd, KDA, kStateWaves>), dim3(bhv * nseg),
+    LRT_LAUNCH(kKScan, (k_scan<E, C, DK, BV, kScanFwd, KDA, kStateWaves, true, SAVE>), dim3(bhv * nseg),
                dim3(64 * kStateWaves), st, s);
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
-template <typename E, int C, int DK, int DV, bool KDA>
+template <typename E, int C, int DK, int DV, bool KDA, bool SAVE = false>
 int launch_scan_fwd(const FwdArgs& a, const FwdWs& ws, int N) {
   constexpr int BV64 = DV < 64 ? DV : 64;
   constexpr int BV128 = DV < 128 ? DV : 128;
   const ScanPlan pl = scan_plan(a.B, a.H, DK, DV, N);
   if constexpr (BV128 != BV64 && DK % BV128 == 0 && ScanLds<E, C, DK, BV128, kScanFwd, KDA>::TOTAL <= 160 * 1024) {
-    if (pl.bv == BV128) return launch_scan_fwd_bv<E, C, DK, DV, BV128, KDA>(a, ws, N, pl.nseg);
+    if (pl.bv == BV128) return launch_scan_fwd_bv<E, C, DK, DV, BV128, KDA, SAVE>(a, ws, N, pl.nseg);
   }
-  return launch_scan_fwd_bv<E, C, DK, DV, BV64, KDA>(a, ws, N, pl.bv == BV64 ? pl.nseg : 1);
+  return launch_scan_fwd_bv<E, C, DK, DV, BV64, KDA, SAVE>(a, ws, N, pl.bv == BV64 ? pl.nseg : 1);
 }
 
 }  // namespace lrt

@@ -113,6 +113,32 @@ def test_backward_validation(L):
     assert lib.gdn_bwd(*a) == c["LRT_ERR_DTYPE"]
 
 
+def test_training_pair_validation(L):
+    c = codes()
+    lib = L.lib()
+    F = FAKE
+    # gdn_fwd_train needs the backward's workspace, not the forward's
+    fwd_need = L.workspace_bytes(L.OP_GDN_FWD, 1, 64, 2, 16, 16, 16, 0)
+    bwd_need = L.workspace_bytes(L.OP_GDN_BWD, 1, 64, 2, 16, 16, 16, 0)
+    assert bwd_need > fwd_need
+    args = [F, F, F, F, F, None, F, None, 1, 64, 2, 16, 16, 16, 0, F, fwd_need, None]
+    assert lib.gdn_fwd_train(*args) == c["LRT_ERR_WORKSPACE"]
+    for i in (0, 1, 2, 3, 4, 6):
+        a = list(args)
+        a[i] = None
+        assert lib.gdn_fwd_train(*a) == c["LRT_ERR_NULL"], i
+    # the fp32 backward's size limits apply to the training forward too
+    a = list(args)
+    a[11], a[12], a[16] = 128, 128, 1 << 40  # rejected before any launch
+    assert lib.gdn_fwd_train(*a) == c["LRT_ERR_SHAPE"]
+    base = [F, F, F, F, F, None, F, None, F, F, F, F, F, None, 1, 64, 2, 16, 16, 16, 0, None, 0, None]
+    assert lib.gdn_bwd_saved(*base) == c["LRT_ERR_WORKSPACE"]
+    for i in (0, 1, 2, 3, 4, 6, 8, 9, 10, 11, 12):
+        a = list(base)
+        a[i] = None
+        assert lib.gdn_bwd_saved(*a) == c["LRT_ERR_NULL"], i
+
+
 def test_ssd_backward_validation(L):
     c = codes()
     lib = L.lib()

@@ -90,6 +90,67 @@ def test_bwd_training_step_workload():
     check_bwd(inp, 64, TOL[torch.bfloat16])
 
 
+SAVED_CASES = ["fp32_tiny_cfg", "fp32_slow_h0_dht", "bf16_slow_T61_C16", "bf16_slow_C32", "bf16_slow_C64",
+               "bf16_d16_dv32", "bf16_long_slow_C64"]
+
+
+@pytest.mark.parametrize("name", SAVED_CASES)
+def test_fwd_train_and_bwd_saved(name):
+    """gdn_fwd_train's outputs and gdn_bwd_saved's gradients against the
+    oracle; a second gdn_bwd_saved on the same saved workspace (another
+    upstream gradient) matches the stateless gdn_bwd for it.  The long case
+    runs the segment-parallel forward scan (B*H small), whose saved states
+    come from the segments' true starts."""
+    import linear_recurrent_token_amd as L
+    case = next(c for c in CASES if c[0] == name)
+    _, B, T, H, dk, dv, chunk, dt, shift, h0s, dhs = case
+    say(f"[fwd_train/bwd_saved] {name}")
+    inp = synth.make_inputs("gdn_fwd_bwd", B, T, H, dk, dv, dtype=dt, seed=0, device="cuda",
+                            gate_shift=shift, h0_std=h0s, dht_std=dhs)
+    q, k, v, la, beta, h0, do, dht = (inp.get(n) for n in ("q", "k", "v", "log_a", "beta", "h0", "do", "dht"))
+    o, ht, saved = L.gdn_fwd_train(q, k, v, la, beta, h0, chunk=chunk)
+    got = L.gdn_bwd_saved(q, k, v, la, beta, h0, do, saved, dht, chunk=chunk)
+    torch.cuda.synchronize()
+    ro, rh = oracle.fwd("gdn", cpu(q), cpu(k), cpu(v), cpu(la), cpu(beta), cpu(h0))
+    ref = oracle.bwd("gdn", cpu(q), cpu(k), cpu(v), cpu(la), cpu(beta), cpu(h0), cpu(do), cpu(dht))
+    errs = {"o": rel(o.float().cpu().numpy(), ro), "ht": rel(ht.cpu().numpy(), rh)}
+    for n, g, r in zip(NAMES, got, ref):
+        g = g.float().cpu().numpy()
+        assert np.all(np.isfinite(g)), n
+        errs[n] = rel(g, r)
+    say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if e > TOL[dt]}
+    assert not bad, bad
+    # the saved tensors survive a backward: reuse them for another do
+    do2 = (torch.randn(do.shape, device="cuda", generator=torch.Generator("cuda").manual_seed(5))).to(dt)
+    again = L.gdn_bwd_saved(q, k, v, la, beta, h0, do2, saved, dht, chunk=chunk)
+    plain = L.gdn_bwd(q, k, v, la, beta, h0, do2, dht, chunk=chunk)
+    torch.cuda.synchronize()
+    for n, x, y in zip(NAMES, again, plain):
+        x, y = x.float().cpu().numpy(), y.float().cpu().numpy()
+        assert rel(x, y) <= TOL[dt], (n, rel(x, y))
+
+
+def test_fwd_train_and_bwd_saved_workload():
+    """The training-step workload (B=16, T=2048, H=8, d=128, chunk 64,
+    bf16) through gdn_fwd_train + gdn_bwd_saved, every element against the
+    oracle."""
+    import linear_recurrent_token_amd as L
+    say("[fwd_train/bwd_saved] workload gdn_train_bf16_2k")
+    inp = synth.config_inputs("gdn_train_bf16_2k", device="cuda")
+    q, k, v, la, beta, h0, do, dht = (inp.get(n) for n in ("q", "k", "v", "log_a", "beta", "h0", "do", "dht"))
+    o, ht, saved = L.gdn_fwd_train(q, k, v, la, beta, h0, chunk=64)
+    got = L.gdn_bwd_saved(q, k, v, la, beta, h0, do, saved, dht, chunk=64)
+    torch.cuda.synchronize()
+    ro, rh = oracle.fwd("gdn", cpu(q), cpu(k), cpu(v), cpu(la), cpu(beta), cpu(h0))
+    ref = oracle.bwd("gdn", cpu(q), cpu(k), cpu(v), cpu(la), cpu(beta), cpu(h0), cpu(do), cpu(dht))
+    errs = {"o": rel(o.float().cpu().numpy(), ro), "ht": rel(ht.cpu().numpy(), rh)}
+    errs.update({n: rel(g.float().cpu().numpy(), r) for n, g, r in zip(NAMES, got, ref)})
+    say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if e > TOL[torch.bfloat16]}
+    assert not bad, bad
+
+
 SSD_CASES = [
     # name, B, T, H, dk, dv, chunk, dtype, gate_shift, h0_std, dht_std
     ("fp32_tiny", 1, 64, 2, 16, 16, 16, torch.float32, 0.0, 0.0, 0.0),
