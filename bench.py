@@ -147,6 +147,8 @@ def kernel_model(name, c, esz=2, op="gdn_fwd + gdn_bwd"):
         per["k_wy"] = (b_th + C * e, b_bh, f_th)
         b_th, b_bh, f_th = per["k_scan"]
         per["k_scan"] = (b_th + dk * dv * e / C + dv * e, b_bh, f_th)
+        # the backward forms dU_local = P^T dO from the stored P: reads P, do; writes dU_local
+        per["k_bwd_local"] = (C * e + dv * e + dv * e, 0, 2 * C * dv)
     if op.startswith("ssd"):
         # the fused Mamba2 forward: reads q, k, v, log_a, h0; writes o, ht
         per["k_ssd_fwd"] = ((2 * dk + dv) * e + 4 + dv * e, 2 * st, 2 * C * (dk + dv) + 4 * dk * dv)

@@ -87,10 +87,13 @@ struct LocalLds {
   static constexpr size_t TOTAL = G + C * 4;
 };
 
-template <typename E, int C, int DK, int DV>
+// READ_P: P is read from the workspace (the training forward's WY pass wrote
+// it, rows [i][j], zero above the diagonal) instead of formed from q and k.
+template <typename E, int C, int DK, int DV, bool READ_P = false>
 __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q, const E* __restrict__ k,
                                                         const E* __restrict__ d_o, const float* __restrict__ wG,
-                                                        E* __restrict__ wdUl, int T, int H, int N, int ntiles) {
+                                                        E* __restrict__ wdUl, int T, int H, int N, int ntiles,
+                                                        const E* __restrict__ wP = nullptr) {
   typedef LocalLds<E, C, DK, DV> Lay;
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, NB = C / 16;
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
@@ -104,6 +107,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q,
 
   Tile<E, C, DK> tq, tk;
   Tile<E, C, DV> to;
+  Tile<E, C, C> tp;
   float rg = 0.f;
 #define LRT_LOCAL_LOAD(tile_)                                                             \
   {                                                                                       \
@@ -111,25 +115,46 @@ __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q,
     const int lnv = min(C, T - ln * C);                                                   \
     const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                           \
     const int lh = lbh % H;                                                               \
-    tq.load_rows_clamped(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                  \
-    tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                  \
+    if constexpr (READ_P) {                                                               \
+      tp.load_block(wP + (size_t)(tile_) * C * C);                                        \
+    } else {                                                                              \
+      tq.load_rows_clamped(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                \
+      tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                \
+      rg = wG[(size_t)(tile_) * C + min((int)threadIdx.x, C - 1)];                        \
+    }                                                                                     \
     to.load_rows_clamped(d_o + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                \
-    rg = wG[(size_t)(tile_) * C + min((int)threadIdx.x, C - 1)];                          \
   }
 
   int tile = blockIdx.x;
   if (tile < ntiles) LRT_LOCAL_LOAD(tile)
   for (; tile < ntiles; tile += gridDim.x) {
     const int nv = min(C, T - (tile % N) * C);
-    tq.store_masked(sQ, LK, nv);
-    tk.store_masked(sK, LK, nv);
+    if constexpr (READ_P) {
+      tp.store(sPt, LC);  // P rows [i][j]
+    } else {
+      tq.store_masked(sQ, LK, nv);
+      tk.store_masked(sK, LK, nv);
+      asm volatile("" ::"v"(rg));  // consumed by every lane (no load into it left pending)
+      if (threadIdx.x < C) sg[threadIdx.x] = rg;
+    }
     to.store_masked(sdO, LV, nv);
-    asm volatile("" ::"v"(rg));  // consumed by every lane (no load into it left pending)
-    if (threadIdx.x < C) sg[threadIdx.x] = rg;
     lds_barrier();
     // the next tile (the last one again on the final pass: unconditional
     // loads keep the waits on older ones exact)
     LRT_LOCAL_LOAD(min(tile + (int)gridDim.x, ntiles - 1))
+    if constexpr (READ_P) {
+      // dU_local = P^T dO (rows j, cols v) -> [v][t] over the q, k area
+      for (int tt = w; tt < NB * (DV / 16); tt += kWaves) {
+        const int tj = tt / (DV / 16), tv = tt % (DV / 16);
+        f32x4 acc = zero4();
+        mma<C, true, true>(acc, sPt + tj * 16, LC, sdO + tv * 16, LV);
+        store4<E>(sUl + (tv * 16 + (l & 15)) * LC + tj * 16 + (l >> 4) * 4, acc);
+      }
+      lds_barrier();
+      lds_to_block<E, DV, C>(wdUl + (size_t)tile * DV * C, sUl, LC);
+      lds_barrier();
+      continue;
+    }
     for (int tt = w; tt < NB * NB; tt += kWaves) {
       const int ti = tt / NB, tj = tt % NB;
       f32x4 acc = zero4();
@@ -973,8 +998,13 @@ int bwd_impl(const BwdArgs& a, bool saved) {
     const int sgrid = a.B * a.H * (DV / BV);
     if (!saved) bwd_recompute<E, C, DK, DV>(ws, a.k, a.v, a.log_a, a.beta, a.h0, a.B, a.T, a.H, a.stream);
     E* dUl = (E*)ws.f.Up;
-    LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV>), dim3(persistent_grid(tiles, LocalLds<E, C, DK, DV>::TOTAL)), dim3(kThreads), st,
-               (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N, tiles);
+    if (saved)  // P from the training forward's WY pass
+      LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV, true>),
+                 dim3(persistent_grid(tiles, LocalLds<E, C, DK, DV>::TOTAL)), dim3(kThreads), st, (const E*)a.q,
+                 (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N, tiles, (const E*)ws.f.P);
+    else
+      LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV>), dim3(persistent_grid(tiles, LocalLds<E, C, DK, DV>::TOTAL)),
+                 dim3(kThreads), st, (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N, tiles);
     LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves>), dim3(sgrid), dim3(64 * kStateWaves), st, (const E*)a.q,
                        (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.W, (const E*)dUl, a.dht, a.dh0,
                        (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
@@ -1043,9 +1073,9 @@ int ssd_bwd_impl(const BwdArgs& a) {
 }
 
 // Gated DeltaNet forward for training: the forward (o, ht) written into the
-// backward's workspace together with what the backward reads -- W, g and T
-// from the WY pass (which also writes P for the scan), S_n and U from the scan
-// -- so that gdn_bwd_saved skips the recompute.
+// backward's workspace together with what the backward reads -- W, g, T and
+// P from the WY pass, S_n and U from the scan -- so that gdn_bwd_saved skips
+// the recompute and forms dU_local from the stored P.
 template <typename E, int C, int DK, int DV>
 int fwd_train_impl(const FwdArgs& a) {
   if constexpr (sizeof(E) == 4 && (DK > 64 || DV > 64)) {
@@ -1066,11 +1096,9 @@ int fwd_train_impl(const FwdArgs& a) {
       if (hipGetLastError() != hipSuccess) return -7;
       return launch_scan_fwd<E, C, DK, DV, false, true>(a, ws.f, N);
     } else {
-      // no split forward at this size: the plain forward, then the recompute
-      const int rc = fwd_scalar_gate(a);
-      if (rc != 0) return rc;
-      bwd_recompute<E, C, DK, DV>(ws, a.k, a.v, a.log_a, a.beta, a.h0, a.B, a.T, a.H, a.stream);
-      return hipGetLastError() == hipSuccess ? 0 : -7;
+      // the WY pass or the forward scan does not fit in LDS at this size (no
+      // size the backward supports)
+      return -2;
     }
   }
 }
