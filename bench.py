@@ -42,13 +42,15 @@ WORKLOADS = {
     "gdn_bf16_2k": ("GDN chunked fwd tokens/s, B=16 T=2048 H=8 d=128", "gdn_fwd"),
     "ssd_bf16_2k": ("SSD (Mamba2 case) chunked fwd tokens/s, B=16 T=2048 H=8 d=128", "ssd_fwd"),
     "ssd_train_bf16_2k": ("SSD (Mamba2 case) chunked fwd+bwd tokens/s, B=16 T=2048 H=8 d=128",
-                          "ssd_fwd + ssd_bwd"),
+                          "ssd_fwd_train + ssd_bwd_saved"),
+    "ssd_train_recompute_bf16_2k": ("SSD (Mamba2 case) chunked fwd+bwd (backward recomputes) tokens/s, "
+                                    "B=16 T=2048 H=8 d=128", "ssd_fwd + ssd_bwd"),
     "kda_bf16_1m": ("KDA chunked fwd tokens/s, B=1 T=2^20 H=16 d=128", "kda_fwd"),
 }
 
 
 # workloads that time another op on an existing workload's inputs
-CONFIG_OF = {"gdn_train_recompute_bf16_2k": "gdn_train_bf16_2k"}
+CONFIG_OF = {"gdn_train_recompute_bf16_2k": "gdn_train_bf16_2k", "ssd_train_recompute_bf16_2k": "ssd_train_bf16_2k"}
 
 
 def parse():
@@ -152,7 +154,11 @@ def kernel_model(name, c, esz=2, op="gdn_fwd + gdn_bwd"):
     if op.startswith("ssd"):
         # the fused Mamba2 forward: reads q, k, v, log_a, h0; writes o, ht
         per["k_ssd_fwd"] = ((2 * dk + dv) * e + 4 + dv * e, 2 * st, 2 * C * (dk + dv) + 4 * dk * dv)
-    if op == "ssd_fwd + ssd_bwd":
+    if op.startswith("ssd_fwd_train"):
+        # the training forward also writes the chunk-start states and g
+        b_th, b_bh, f_th = per["k_ssd_fwd"]
+        per["k_ssd_fwd"] = (b_th + dk * dv * e / C + 4, b_bh, f_th)
+    if op in ("ssd_fwd + ssd_bwd", "ssd_fwd_train + ssd_bwd_saved"):
         per.update({
             # reads v, log_a; writes g, V^T
             "k_ssd_prep": (dv * e + 4 + 4 + dv * e, 0, 0),
@@ -253,7 +259,8 @@ def main():
     sets = make_sets(L, synth, torch, cfg, nsets)
     code = L.LRT_BF16
     opc = {"gdn_fwd + gdn_bwd": L.OP_GDN_BWD, "gdn_fwd_train + gdn_bwd_saved": L.OP_GDN_BWD, "gdn_fwd": L.OP_GDN_FWD, "ssd_fwd": L.OP_SSD_FWD,
-           "ssd_fwd + ssd_bwd": L.OP_SSD_BWD, "kda_fwd": L.OP_KDA_FWD}[op]
+           "ssd_fwd + ssd_bwd": L.OP_SSD_BWD, "ssd_fwd_train + ssd_bwd_saved": L.OP_SSD_BWD,
+           "kda_fwd": L.OP_KDA_FWD}[op]
     ws_bytes = max(L.workspace_bytes(L.OP_GDN_FWD, B, T, H, dk, dv, C, code),
                    L.workspace_bytes(opc, B, T, H, dk, dv, C, code))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -272,6 +279,11 @@ def main():
 
     def step(i):
         s = sets[i % len(sets)]
+        if op == "ssd_fwd_train + ssd_bwd_saved":
+            L.ssd_fwd_train(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), chunk=C, o=o, ht=ht, workspace=ws)
+            L.ssd_bwd_saved(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), s["do"], ws, s.get("dht"), chunk=C,
+                            out=grads)
+            return
         if op.startswith("ssd"):
             L.ssd_fwd(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), chunk=C, o=o, ht=ht, workspace=ws)
         elif op == "gdn_fwd_train + gdn_bwd_saved":

@@ -4,8 +4,9 @@
  * The mixers are the linear-recurrent "M" layers of the hybrid stacks in the
  * AMD ROCm blog "Pretraining hybrid LLMs with Primus" (section "How hybrid
  * models are defined in Primus", mixer list under Table 2):
- *   - Mamba2 (ssd_fwd, ssd_bwd): the state is decayed by one scalar gate per head and a
- *     rank-one k v^T write is added each token;
+ *   - Mamba2 (ssd_fwd, ssd_bwd; ssd_fwd_train + ssd_bwd_saved): the state
+ *     is decayed by one scalar gate per head and a rank-one k v^T write is
+ *     added each token;
  *   - Gated DeltaNet (gdn_fwd, gdn_bwd; gdn_fwd_train + gdn_bwd_saved for a
  *     training step that keeps the forward's intermediates): Mamba2 plus the
  *     delta rule, which replaces the value stored under the current key
@@ -156,6 +157,27 @@ int ssd_bwd(const void* q, const void* k, const void* v, const float* log_a, con
             const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dlog_a, float* dh0,
             int B, int T, int H, int d_k, int d_v, int chunk, int dtype, void* workspace,
             size_t workspace_bytes, void* stream);
+
+/*
+ * Mamba2 / SSD forward for training: ssd_fwd (same arguments, same o and ht)
+ * that also leaves each chunk's start state and in-chunk gate cumsums in a
+ * workspace of lrt_workspace_bytes(LRT_OP_SSD_BWD, ...) bytes for
+ * ssd_bwd_saved.  Shape limits are ssd_bwd's.
+ */
+int ssd_fwd_train(const void* q, const void* k, const void* v, const float* log_a, const float* h0,
+                  void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ssd_bwd without the recompute, from the workspace a preceding
+ * ssd_fwd_train of the same inputs and sizes filled (stream ordered after it,
+ * unmodified since).  Arguments, outputs and errors as ssd_bwd; the saved
+ * tensors stay in place, so several backward passes may follow.
+ */
+int ssd_bwd_saved(const void* q, const void* k, const void* v, const float* log_a, const float* h0,
+                  const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dlog_a,
+                  float* dh0, int B, int T, int H, int d_k, int d_v, int chunk, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes needed by `op` (LRT_OP_*) at these sizes.  Returns

@@ -14,6 +14,8 @@ Entry points (names as in include/lrt.h):
   kda_fwd(q, k, v, log_a, beta, h0=None, chunk=64)            -> (o, ht)
   ssd_fwd(q, k, v, log_a, h0=None, chunk=64)                   -> (o, ht)
   ssd_bwd(q, k, v, log_a, h0, do, dht=None, chunk=64)          -> (dq, dk, dv, dlog_a, dh0)
+  ssd_fwd_train(q, k, v, log_a, h0=None, chunk=64)             -> (o, ht, saved)
+  ssd_bwd_saved(q, k, v, log_a, h0, do, saved, dht=None, chunk=64) -> as ssd_bwd
 Layouts: q, k [B,T,H,d_k], v [B,T,H,d_v] (fp32 or bf16); log_a, beta fp32
 [B,T,H] (KDA log_a [B,T,H,d_k]); states fp32 [B,H,d_k,d_v].
 """
@@ -27,7 +29,8 @@ LIB_PATH = os.path.join(HERE, "liblrt.so")
 
 LRT_F32, LRT_BF16 = 0, 1
 OP_GDN_FWD, OP_GDN_BWD, OP_KDA_FWD, OP_SSD_FWD, OP_SSD_BWD = 0, 1, 2, 3, 4
-EXPORTS = ("gdn_fwd", "gdn_bwd", "gdn_fwd_train", "gdn_bwd_saved", "kda_fwd", "ssd_fwd", "ssd_bwd", "lrt_workspace_bytes", "lrt_status_string",
+EXPORTS = ("gdn_fwd", "gdn_bwd", "gdn_fwd_train", "gdn_bwd_saved", "kda_fwd", "ssd_fwd", "ssd_bwd",
+           "ssd_fwd_train", "ssd_bwd_saved", "lrt_workspace_bytes", "lrt_status_string",
            "lrt_profile_attach", "lrt_profile_count", "lrt_kernel_name")
 
 _lib = None
@@ -55,7 +58,10 @@ def lib():
         L.ssd_bwd.argtypes = [vp] * 12 + [ci] * 7 + [vp, sz, vp]
         L.gdn_fwd_train.argtypes = [vp] * 8 + [ci] * 7 + [vp, sz, vp]
         L.gdn_bwd_saved.argtypes = [vp] * 14 + [ci] * 7 + [vp, sz, vp]
-        for f in ("gdn_fwd", "kda_fwd", "ssd_fwd", "gdn_bwd", "ssd_bwd", "gdn_fwd_train", "gdn_bwd_saved"):
+        L.ssd_fwd_train.argtypes = [vp] * 7 + [ci] * 7 + [vp, sz, vp]
+        L.ssd_bwd_saved.argtypes = [vp] * 12 + [ci] * 7 + [vp, sz, vp]
+        for f in ("gdn_fwd", "kda_fwd", "ssd_fwd", "gdn_bwd", "ssd_bwd", "gdn_fwd_train", "gdn_bwd_saved",
+                  "ssd_fwd_train", "ssd_bwd_saved"):
             getattr(L, f).restype = ci
         L.lrt_workspace_bytes.argtypes = [ci] * 8
         L.lrt_workspace_bytes.restype = sz
@@ -129,7 +135,8 @@ def _fwd(fn, op, q, k, v, log_a, beta, h0, chunk, o, ht, workspace, kda=False, w
     _check(dev, dt, "v", v, (B, T, H, dv), dt)
     _check(dev, dt, "q", q, (B, T, H, dk), dt)
     _check(dev, dt, "log_a", log_a, (B, T, H, dk) if kda else (B, T, H), torch.float32)
-    if op != OP_SSD_FWD:
+    ssd = fn.__name__.startswith("ssd")
+    if not ssd:
         if beta is None:
             raise ValueError("beta is required")
         _check(dev, dt, "beta", beta, (B, T, H), torch.float32)
@@ -145,7 +152,7 @@ def _fwd(fn, op, q, k, v, log_a, beta, h0, chunk, o, ht, workspace, kda=False, w
     code = _dtype_code(q)
     ws, need = _workspace(op, dev, B, T, H, dk, dv, chunk, code, workspace)
     with torch.cuda.device(dev):
-        if op == OP_SSD_FWD:
+        if ssd:
             rc = fn(_p(q), _p(k), _p(v), _p(log_a), _p(h0), _p(o), _p(ht), B, T, H, dk, dv, chunk, code,
                     _p(ws), need, _stream(dev))
         else:
@@ -166,6 +173,23 @@ def gdn_fwd_train(q, k, v, log_a, beta, h0=None, chunk=64, o=None, ht=True, work
     saved); pass ``saved`` (a uint8 workspace of the backward's size) to
     gdn_bwd_saved."""
     return _fwd(lib().gdn_fwd_train, OP_GDN_BWD, q, k, v, log_a, beta, h0, chunk, o, ht, workspace, want_ws=True)
+
+
+def ssd_fwd_train(q, k, v, log_a, h0=None, chunk=64, o=None, ht=True, workspace=None):
+    """Mamba2 forward that keeps the chunk-start states and gate cumsums ->
+    (o, ht, saved) for ssd_bwd_saved."""
+    return _fwd(lib().ssd_fwd_train, OP_SSD_BWD, q, k, v, log_a, None, h0, chunk, o, ht, workspace, want_ws=True)
+
+
+def ssd_bwd_saved(q, k, v, log_a, h0, do, saved, dht=None, chunk=64, want_dh0=True, out=None):
+    """Mamba2 backward from ssd_fwd_train's ``saved`` workspace -> (dq, dk,
+    dv, dlog_a, dh0 or None)."""
+    if saved is None:
+        raise ValueError("saved: the workspace ssd_fwd_train returned")
+    if out is not None:
+        out = tuple(out[:4]) + (None,) + tuple(out[4:])
+    g = _bwd(False, q, k, v, log_a, None, h0, do, dht, chunk, want_dh0, saved, out, fn="ssd_bwd_saved")
+    return g[:4] + g[5:]
 
 
 def gdn_bwd_saved(q, k, v, log_a, beta, h0, do, saved, dht=None, chunk=64, want_dh0=True, out=None):
@@ -227,8 +251,11 @@ def _bwd(delta, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, workspace, o
                                     _p(gk), _p(gv), _p(gla), _p(gb), _p(gh0), B, T, H, dk, dv, chunk, code, _p(ws),
                                     need, _stream(dev))
         else:
-            rc = lib().ssd_bwd(_p(q), _p(k), _p(v), _p(log_a), _p(h0), _p(do), _p(dht), _p(gq), _p(gk), _p(gv),
-                               _p(gla), _p(gh0), B, T, H, dk, dv, chunk, code, _p(ws), need, _stream(dev))
+            fs = "ssd_bwd_saved" if fn.endswith("_saved") else "ssd_bwd"
+            rc = getattr(lib(), fs)(_p(q), _p(k), _p(v), _p(log_a), _p(h0), _p(do), _p(dht), _p(gq), _p(gk),
+                                    _p(gv), _p(gla), _p(gh0), B, T, H, dk, dv, chunk, code, _p(ws), need,
+                                    _stream(dev))
+            fn = fs
     if rc != 0:
-        raise LrtError(fn if delta else "ssd_bwd", rc)
+        raise LrtError(fn, rc)
     return gq, gk, gv, gla, gb, gh0

@@ -99,12 +99,12 @@ static int fwd_entry(int variant, const void* q, const void* k, const void* v, c
   const void* sca[] = {log_a, beta, h0, ht};
   for (const void* p : sca)
     if (p && !aligned4(p)) return LRT_ERR_ALIGN;
-  const int op = train ? LRT_OP_GDN_BWD
+  const int op = train ? (variant == kVarSSD ? LRT_OP_SSD_BWD : LRT_OP_GDN_BWD)
                        : variant == kVarGDN ? LRT_OP_GDN_FWD : variant == kVarSSD ? LRT_OP_SSD_FWD : LRT_OP_KDA_FWD;
   if (!workspace || workspace_bytes < ws_bytes(op, B, T, H, dk, dv, chunk, dtype)) return LRT_ERR_WORKSPACE;
   if (T == 0) return launch_empty(h0, ht, B, H, dk, dv, stream);
   FwdArgs a{variant, q, k, v, log_a, beta, h0, o, ht, B, T, H, dk, dv, chunk, dtype, workspace, stream};
-  rc = train ? fwd_gdn_train(a) : variant == kVarKDA ? fwd_kda(a) : fwd_scalar_gate(a);
+  rc = train ? fwd_train(a) : variant == kVarKDA ? fwd_kda(a) : fwd_scalar_gate(a);
   return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
 }
 
@@ -129,7 +129,7 @@ static int bwd_entry(int variant, const void* q, const void* k, const void* v, c
   if (T == 0) return launch_empty(dht, dh0, B, H, d_k, d_v, stream);
   BwdArgs a{q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0,
             B, T, H, d_k, d_v, chunk, dtype, workspace, stream};
-  rc = delta ? bwd_gdn(a, saved) : bwd_ssd(a);
+  rc = delta ? bwd_gdn(a, saved) : bwd_ssd(a, saved);
   return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
 }
 
@@ -181,6 +181,21 @@ int gdn_bwd_saved(const void* q, const void* k, const void* v, const float* log_
                   int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_entry(kVarGDN, q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0, B, T, H, d_k, d_v,
                    chunk, dtype, workspace, workspace_bytes, stream, true);
+}
+
+int ssd_fwd_train(const void* q, const void* k, const void* v, const float* log_a, const float* h0, void* o,
+                  float* ht, int B, int T, int H, int d_k, int d_v, int chunk, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  return fwd_entry(kVarSSD, q, k, v, log_a, nullptr, h0, o, ht, B, T, H, d_k, d_v, chunk, dtype, workspace,
+                   workspace_bytes, stream, true);
+}
+
+int ssd_bwd_saved(const void* q, const void* k, const void* v, const float* log_a, const float* h0,
+                  const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dlog_a, float* dh0,
+                  int B, int T, int H, int d_k, int d_v, int chunk, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  return bwd_entry(kVarSSD, q, k, v, log_a, nullptr, h0, d_o, dht, dq, dk, dv, dlog_a, nullptr, dh0, B, T, H, d_k,
+                   d_v, chunk, dtype, workspace, workspace_bytes, stream, true);
 }
 
 int ssd_bwd(const void* q, const void* k, const void* v, const float* log_a, const float* h0, const void* d_o,

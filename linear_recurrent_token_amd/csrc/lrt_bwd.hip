@@ -24,9 +24,12 @@
 //   k_dstate     per (b, h, d_v block), chunks in reverse: dU and dH'
 //   k_grad1      per chunk: dQ, the dS/state part of dK, dW, part of dg
 //   k_grad2      per chunk: the WY part of dK, dV, dbeta, dg -> dlog_a
+#include <type_traits>
+
 #include "lrt_fwd_kernels.hpp"
 #include "lrt_internal.hpp"
 #include "lrt_scan.hpp"
+#include "lrt_ssd_fwd.hpp"
 
 namespace lrt {
 
@@ -352,8 +355,8 @@ struct Grad1Lds {
   static constexpr size_t Q = 0;                                  // q rows [t][d]
   static constexpr size_t K = Q + (size_t)C * LK * es;            // k rows [t][d]
   static constexpr size_t DO = K + (size_t)C * LK * es;           // do rows [t][v]; later dq rows
-  static constexpr size_t UT = DO + mx((size_t)C * LV, (size_t)C * LK) * es;  // U^T [v][t]
-  static constexpr size_t ST = UT + (size_t)DV * LC * es;         // S_n = Hn^T [v][d]; later dH'^T
+  static constexpr size_t UT = DO + mx((size_t)C * LV, (size_t)C * LK) * es;  // U^T [v][t] (Mamba2: v rows [t][v])
+  static constexpr size_t ST = UT + mx((size_t)DV * LC, (size_t)C * LV) * es;  // S_n = Hn^T [v][d]; later dH'^T
   static constexpr size_t DUT = ST + (size_t)DV * LK * es;        // dU^T [v][t]
   static constexpr size_t DSJ = DUT + (size_t)DV * LC * es;       // dS^T [j][i]
   static constexpr size_t G = DSJ + (size_t)C * LC * es;
@@ -365,7 +368,8 @@ struct Grad1Lds {
 // DELTA = false is the Mamba2 recurrence (U = V, no W): the dK and dg
 // computed here are then complete, and the kernel writes dk, dv (= dU, read
 // back from its LDS copy) and dlog_a (reverse cumsum of dg) itself; wdW,
-// wdK1 and wdg1 are unused.
+// wdK1 and wdg1 are unused, and wU is the value rows v [B, T, H, d_v]
+// themselves (staged as rows; the products read them k-inner).
 template <typename E, int C, int DK, int DV, int NW = 8, bool DELTA = true>
 __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, const E* __restrict__ k,
                                                     const E* __restrict__ d_o, const float* __restrict__ wG,
@@ -397,7 +401,9 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
 
   Tile<E, C, DK, NT> tq, tk;
   Tile<E, C, DV, NT> to;
-  Tile<E, DV, C, NT> tu, tdu;
+  // U^T tiles, or (Mamba2) the v rows of the chunk
+  typename std::conditional<DELTA, Tile<E, DV, C, NT>, Tile<E, C, DV, NT>>::type tu;
+  Tile<E, DV, C, NT> tdu;
   Tile<E, DV, DK, NT> tS, tdS;
   float rg = 0.f;
   // this chunk's dg partials, written out during the next chunk
@@ -418,7 +424,10 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
     }                                                                                     \
     if ((PART_) & 2) {                                                                    \
       to.load_rows_clamped(d_o + (ltok * H + lh) * DV, (size_t)H * DV, lnv);              \
-      tu.load_block(wU + (size_t)(tile_) * DV * C);                                       \
+      if constexpr (DELTA)                                                                \
+        tu.load_block(wU + (size_t)(tile_) * DV * C);                                     \
+      else                                                                                \
+        tu.load_rows_clamped(wU + (ltok * H + lh) * DV, (size_t)H * DV, lnv);             \
     }                                                                                     \
     if ((PART_) & 4) tdu.load_block(wdU + (size_t)(tile_) * DV * C);                      \
     if ((PART_) & 8) tS.load_block(wS + (size_t)(tile_) * DV * DK);                       \
@@ -436,7 +445,10 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
     tq.store_masked(sQ, LK, nv);
     tk.store_masked(sK, LK, nv);
     to.store_masked(sdO, LV, nv);
-    tu.store(sUt, LC);
+    if constexpr (DELTA)
+      tu.store(sUt, LC);
+    else
+      tu.store_masked(sUt, LV, nv);
     tdu.store(sdUt, LC);
     tS.store(sS, LK);
     asm volatile("" ::"v"(rg));  // consumed by every lane (no load into it left pending)
@@ -464,7 +476,10 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
       if (tj <= ti) {
         f32x4 qk = zero4(), dp = zero4(), ev;
         mma<DK>(qk, sQ + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
-        mma<DV, false, true>(dp, sdO + ti * 16 * LV, LV, sUt + tj * 16, LC);
+        if constexpr (DELTA)
+          mma<DV, false, true>(dp, sdO + ti * 16 * LV, LV, sUt + tj * 16, LC);
+        else
+          mma<DV>(dp, sdO + ti * 16 * LV, LV, sUt + tj * 16 * LV, LV);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = i0 + r;
@@ -560,7 +575,10 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
         if (td < DK / 16) {
           const int d0 = td * 16 + (l >> 4) * 4;
           f32x4 acc = zero4();
-          mma<DV, true, true>(acc, sS + td * 16, LK, sUt + tj * 16, LC);
+          if constexpr (DELTA)
+            mma<DV, true, true>(acc, sS + td * 16, LK, sUt + tj * 16, LC);
+          else
+            mma<DV, true, false>(acc, sS + td * 16, LK, sUt + tj * 16 * LV, LV);
 #pragma unroll
           for (int r = 0; r < 4; ++r) ssum += acc[r] * to_f(sK[j * LK + d0 + r]);
           acc *= kt;
@@ -1023,8 +1041,10 @@ int bwd_impl(const BwdArgs& a, bool saved) {
 // (T = I, W = 0, U = V, no beta): prep (g, V^T), the state recompute
 // (chunk-start states only), dU_local, the reverse state scan (dU = dV) and
 // one gradient kernel writing dq, dk, dv and dlog_a.
+// saved: the workspace holds S_n and g from ssd_fwd_train of the same
+// arguments, so the prep and the state recompute are skipped.
 template <typename E, int C, int DK, int DV>
-int ssd_bwd_impl(const BwdArgs& a) {
+int ssd_bwd_impl(const BwdArgs& a, bool saved) {
   if constexpr (sizeof(E) == 4 && (DK > 64 || DV > 64)) {
     return -2;
   } else if constexpr (sizeof(E) == 4 && C > 32) {
@@ -1036,26 +1056,28 @@ int ssd_bwd_impl(const BwdArgs& a) {
     hipStream_t st = (hipStream_t)a.stream;
     constexpr int BV = DV < 64 ? DV : 64;
     const int sgrid = a.B * a.H * (DV / BV);
-    E* Ut = (E*)ws.f.U;  // V^T: U'^T for the scan, U^T for k_grad1
-    LRT_LAUNCH(kKSsdPrep, (k_ssd_prep<E, C, DV>),
-               dim3(persistent_grid(tiles, (size_t)DV * (C + lds_pad<E>()) * sizeof(E))), dim3(kThreads), st,
-               (const E*)a.v, a.log_a, ws.f.G, Ut, a.T, a.H, N, tiles);
-    {
-      ScanArgs<E> sa{};
-      sa.k = (const E*)a.k;
-      sa.Up = Ut;
-      sa.G = ws.f.G;
-      sa.hin = a.h0;
-      sa.hs_ld = DV;
-      sa.S = (E*)ws.f.S;
-      sa.T = a.T;
-      sa.H = a.H;
-      sa.N = N;
-      sa.L = N;
-      sa.nseg = 1;
-      sa.DV = DV;
-      LRT_LAUNCH(kKScanBwd, (k_scan<E, C, DK, BV, kScanBwd, false, kStateWaves, false>), dim3(sgrid),
-                 dim3(64 * kStateWaves), st, sa);
+    if (!saved) {
+      E* Ut = (E*)ws.f.U;  // V^T, the scan's U'^T
+      LRT_LAUNCH(kKSsdPrep, (k_ssd_prep<E, C, DV>),
+                 dim3(persistent_grid(tiles, (size_t)DV * (C + lds_pad<E>()) * sizeof(E))), dim3(kThreads), st,
+                 (const E*)a.v, a.log_a, ws.f.G, Ut, a.T, a.H, N, tiles);
+      {
+        ScanArgs<E> sa{};
+        sa.k = (const E*)a.k;
+        sa.Up = Ut;
+        sa.G = ws.f.G;
+        sa.hin = a.h0;
+        sa.hs_ld = DV;
+        sa.S = (E*)ws.f.S;
+        sa.T = a.T;
+        sa.H = a.H;
+        sa.N = N;
+        sa.L = N;
+        sa.nseg = 1;
+        sa.DV = DV;
+        LRT_LAUNCH(kKScanBwd, (k_scan<E, C, DK, BV, kScanBwd, false, kStateWaves, false>), dim3(sgrid),
+                   dim3(64 * kStateWaves), st, sa);
+      }
     }
     E* dUl = (E*)ws.f.Up;
     LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV>), dim3(persistent_grid(tiles, LocalLds<E, C, DK, DV>::TOTAL)),
@@ -1065,7 +1087,7 @@ int ssd_bwd_impl(const BwdArgs& a) {
                (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
     LRT_LAUNCH(kKGrad1, (k_grad1<E, C, DK, DV, kGradWaves, false>),
                dim3(persistent_grid(tiles, Grad1Lds<E, C, DK, DV>::TOTAL)), dim3(64 * kGradWaves), st, (const E*)a.q,
-               (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.S, (const E*)ws.dS, (const E*)Ut,
+               (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.S, (const E*)ws.dS, (const E*)a.v,
                (const E*)ws.dU, (E*)a.dq, (E*)nullptr, (E*)nullptr, (float*)nullptr, a.T, a.H, N, tiles,
                (E*)a.dk_out, (E*)a.dv_out, a.dlog_a);
     return hipGetLastError() == hipSuccess ? 0 : -7;
@@ -1103,10 +1125,25 @@ int fwd_train_impl(const FwdArgs& a) {
   }
 }
 
+// Mamba2 forward for training: ssd_fwd's kernel also writing S_n and g into
+// the backward's workspace for ssd_bwd_saved.
+template <typename E, int C, int DK, int DV>
+int fwd_ssd_train_impl(const FwdArgs& a) {
+  if constexpr (sizeof(E) == 4 && (DK > 64 || DV > 64)) {
+    return -2;
+  } else if constexpr (sizeof(E) == 4 && C > 32) {
+    return -3;
+  } else {
+    const BwdWs ws = bwd_ws_layout(a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
+    return launch_ssd_fwd<E, C, DK, DV, true>(a, (E*)ws.f.S, ws.f.G);
+  }
+}
+
 template <typename E>
 static int fwd_train_dtype(const FwdArgs& a) {
-#define LRT_CASE(C_, DK_, DV_) \
-  if (a.chunk == C_ && a.dk == DK_ && a.dv == DV_) return fwd_train_impl<E, C_, DK_, DV_>(a);
+#define LRT_CASE(C_, DK_, DV_)                                                             \
+  if (a.chunk == C_ && a.dk == DK_ && a.dv == DV_)                                         \
+    return a.variant == kVarSSD ? fwd_ssd_train_impl<E, C_, DK_, DV_>(a) : fwd_train_impl<E, C_, DK_, DV_>(a);
 #define LRT_DV(C_, DK_) LRT_CASE(C_, DK_, 16) LRT_CASE(C_, DK_, 32) LRT_CASE(C_, DK_, 64) LRT_CASE(C_, DK_, 128)
 #define LRT_DK(C_) LRT_DV(C_, 16) LRT_DV(C_, 32) LRT_DV(C_, 64) LRT_DV(C_, 128)
   LRT_DK(16) LRT_DK(32) LRT_DK(64)
@@ -1116,13 +1153,13 @@ static int fwd_train_dtype(const FwdArgs& a) {
   return -2;
 }
 
-int fwd_gdn_train(const FwdArgs& a) { return a.dtype == 1 ? fwd_train_dtype<bf16>(a) : fwd_train_dtype<float>(a); }
+int fwd_train(const FwdArgs& a) { return a.dtype == 1 ? fwd_train_dtype<bf16>(a) : fwd_train_dtype<float>(a); }
 
 template <typename E, bool SSD>
 static int bwd_dtype(const BwdArgs& a, bool saved) {
 #define LRT_CASE(C_, DK_, DV_)                     \
   if (a.chunk == C_ && a.dk == DK_ && a.dv == DV_) \
-    return SSD ? ssd_bwd_impl<E, C_, DK_, DV_>(a) : bwd_impl<E, C_, DK_, DV_>(a, saved);
+    return SSD ? ssd_bwd_impl<E, C_, DK_, DV_>(a, saved) : bwd_impl<E, C_, DK_, DV_>(a, saved);
 #define LRT_DV(C_, DK_) LRT_CASE(C_, DK_, 16) LRT_CASE(C_, DK_, 32) LRT_CASE(C_, DK_, 64) LRT_CASE(C_, DK_, 128)
 #define LRT_DK(C_) LRT_DV(C_, 16) LRT_DV(C_, 32) LRT_DV(C_, 64) LRT_DV(C_, 128)
   LRT_DK(16) LRT_DK(32) LRT_DK(64)
@@ -1135,6 +1172,8 @@ static int bwd_dtype(const BwdArgs& a, bool saved) {
 int bwd_gdn(const BwdArgs& a, bool saved) {
   return a.dtype == 1 ? bwd_dtype<bf16, false>(a, saved) : bwd_dtype<float, false>(a, saved);
 }
-int bwd_ssd(const BwdArgs& a) { return a.dtype == 1 ? bwd_dtype<bf16, true>(a, false) : bwd_dtype<float, true>(a, false); }
+int bwd_ssd(const BwdArgs& a, bool saved) {
+  return a.dtype == 1 ? bwd_dtype<bf16, true>(a, saved) : bwd_dtype<float, true>(a, saved);
+}
 
 }  // namespace lrt

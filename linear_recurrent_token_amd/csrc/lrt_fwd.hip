@@ -12,32 +12,9 @@ namespace lrt {
 constexpr bool kFwdSplit = true;
 
 // --------------------------------------------------------------- launchers
-// Mamba2: one fused kernel per (b, h, block of value columns), state on chip.
-constexpr int kSsdBV = 64;   // value columns per workgroup
-constexpr int kSsdPF = 1;    // chunks of operands in flight
-constexpr int kSsdOcc = 1;   // workgroups per CU the registers are sized for
-// the widest column block up to kSsdBV whose tiles fit in LDS
-template <typename E, int C, int DK, int BV>
-constexpr int ssd_bv() {
-  if constexpr (BV > 16 && SsdFwdLds<E, C, DK, BV>::TOTAL > 160 * 1024)
-    return ssd_bv<E, C, DK, BV / 2>();
-  else
-    return BV;
-}
-template <typename E, int C, int DK, int DV>
-int ssd_fwd_impl(const FwdArgs& a) {
-  constexpr int BV = ssd_bv<E, C, DK, (DV < kSsdBV ? DV : kSsdBV)>();
-  static_assert(SsdFwdLds<E, C, DK, BV>::TOTAL <= 160 * 1024, "k_ssd_fwd LDS");
-  const int N = (a.T + C - 1) / C;
-  const int grid = a.B * a.H * (DV / BV);
-  LRT_LAUNCH(kKSsdFwd, (k_ssd_fwd<E, C, DK, BV, kStateWaves, kSsdPF, kSsdOcc>), dim3(grid), dim3(64 * kStateWaves), a.stream,
-             (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.h0, a.ht, (E*)a.o, a.T, a.H, N, DV);
-  return hipGetLastError() == hipSuccess ? 0 : -7;
-}
-
 template <typename E, int C, int DK, int DV>
 int fwd_impl(const FwdArgs& a) {
-  if (a.variant == kVarSSD) return ssd_fwd_impl<E, C, DK, DV>(a);
+  if (a.variant == kVarSSD) return launch_ssd_fwd<E, C, DK, DV>(a);
   constexpr int BVF = DV < 64 ? DV : 64;
   if constexpr (WyLds<E, C, DK, DV>::TOTAL <= 160 * 1024 && ScanLds<E, C, DK, BVF, kScanFwd, false>::TOTAL <= 160 * 1024) {
     if (kFwdSplit) {

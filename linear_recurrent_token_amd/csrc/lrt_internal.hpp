@@ -153,8 +153,8 @@ inline int persistent_grid(int tiles, size_t lds_bytes) {
 int fwd_scalar_gate(const FwdArgs& a);
 int fwd_kda(const FwdArgs& a);
 int bwd_gdn(const BwdArgs& a, bool saved);
-int fwd_gdn_train(const FwdArgs& a);
-int bwd_ssd(const BwdArgs& a);
+int fwd_train(const FwdArgs& a);  // GDN or SSD by a.variant
+int bwd_ssd(const BwdArgs& a, bool saved);
 // workspace bytes the backward needs beyond the forward's tiles
 size_t bwd_ws_extra(int B, int T, int H, int dk, int dv, int C, size_t esz);
 

@@ -25,11 +25,14 @@
 //    counts exactly and leaves later loads and the stores in flight;
 //  * a wave's output and state tiles share one operand fragment per k step;
 //  * three barriers per chunk.
+// SAVE (the training forward) also writes each chunk's start state S_n
+// ([d_v][d_k] per chunk, as the backward reads it) and the gate cumsums g.
 // Measured on MI355X at B=16, T=2048, H=8, d=128: 64 value columns per
 // workgroup beat 32 (two workgroups per CU, but each recomputes Q K^T for
 // half the columns) and 16, and PF = 2 gains nothing over PF = 1.
 #pragma once
 #include "lrt_common.hpp"
+#include "lrt_internal.hpp"
 
 namespace lrt {
 
@@ -48,11 +51,12 @@ struct SsdFwdLds {
   static constexpr size_t TOTAL = O + (size_t)C * LB * es;
 };
 
-template <typename E, int C, int DK, int BV, int NW = 8, int PF = 1, int OCC = 2>
+template <typename E, int C, int DK, int BV, int NW = 8, int PF = 1, int OCC = 2, bool SAVE = false>
 __global__ __launch_bounds__(64 * NW, OCC) void k_ssd_fwd(const E* __restrict__ q, const E* __restrict__ k,
                                                         const E* __restrict__ v, const float* __restrict__ log_a,
                                                         const float* h0, float* ht, E* __restrict__ o, int T,
-                                                        int H, int N, int DV) {
+                                                        int H, int N, int DV, E* __restrict__ wS = nullptr,
+                                                        float* __restrict__ wG = nullptr) {
   typedef SsdFwdLds<E, C, DK, BV> Lay;
   constexpr int NT = 64 * NW;
   constexpr int LK = Lay::LK, LB = Lay::LB, LC = Lay::LC;
@@ -141,6 +145,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_ssd_fwd(const E* __restrict__ 
     // chunk n + PF (the last chunk again near the end: unconditional loads
     // keep the wait for this set exact)
     fetch(x, min(n + PF, N - 1));
+    if constexpr (SAVE) {
+      // S_n, and g from every lane of every wave (lanes past C hold g of
+      // token C - 1, so the duplicate writes agree): a fixed store count
+      const size_t tile = (size_t)bh * N + n;
+      lds_to_block<E, BV, DK, NT>(wS + (tile * DV + v0) * DK, sS, LK);
+      wG[tile * C + min(l, C - 1)] = g;
+    }
     // ---- P^T (rows j, cols i): P_ij = (q_i . k_j) e^(g_i - g_j), j <= i
 #pragma unroll
     for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
@@ -239,6 +250,31 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_ssd_fwd(const E* __restrict__ 
       }
     }
   }
+}
+
+// --------------------------------------------------------------- launcher
+constexpr int kSsdBV = 64;   // value columns per workgroup
+constexpr int kSsdPF = 1;    // chunks of operands in flight
+constexpr int kSsdOcc = 1;   // workgroups per CU the registers are sized for
+// the widest column block up to kSsdBV whose tiles fit in LDS
+template <typename E, int C, int DK, int BV>
+constexpr int ssd_bv() {
+  if constexpr (BV > 16 && SsdFwdLds<E, C, DK, BV>::TOTAL > 160 * 1024)
+    return ssd_bv<E, C, DK, BV / 2>();
+  else
+    return BV;
+}
+// One workgroup per (b, h, block of value columns); SAVE also writes S_n and g.
+template <typename E, int C, int DK, int DV, bool SAVE = false>
+int launch_ssd_fwd(const FwdArgs& a, E* wS = nullptr, float* wG = nullptr) {
+  constexpr int BV = ssd_bv<E, C, DK, (DV < kSsdBV ? DV : kSsdBV)>();
+  static_assert(SsdFwdLds<E, C, DK, BV>::TOTAL <= 160 * 1024, "k_ssd_fwd LDS");
+  const int N = (a.T + C - 1) / C;
+  const int grid = a.B * a.H * (DV / BV);
+  LRT_LAUNCH(kKSsdFwd, (k_ssd_fwd<E, C, DK, BV, kStateWaves, kSsdPF, kSsdOcc, SAVE>), dim3(grid),
+             dim3(64 * kStateWaves), a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.h0, a.ht,
+             (E*)a.o, a.T, a.H, N, DV, wS, wG);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
 }  // namespace lrt

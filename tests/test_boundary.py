@@ -139,6 +139,31 @@ def test_training_pair_validation(L):
         assert lib.gdn_bwd_saved(*a) == c["LRT_ERR_NULL"], i
 
 
+def test_ssd_training_pair_validation(L):
+    c = codes()
+    lib = L.lib()
+    F = FAKE
+    fwd_need = L.workspace_bytes(L.OP_SSD_FWD, 1, 64, 2, 16, 16, 16, 0)
+    bwd_need = L.workspace_bytes(L.OP_SSD_BWD, 1, 64, 2, 16, 16, 16, 0)
+    assert bwd_need > fwd_need
+    # q k v log_a h0 o ht | B T H dk dv chunk dtype | ws wsb stream
+    args = [F, F, F, F, None, F, None, 1, 64, 2, 16, 16, 16, 0, F, fwd_need, None]
+    assert lib.ssd_fwd_train(*args) == c["LRT_ERR_WORKSPACE"]
+    for i in (0, 1, 2, 3, 5):
+        a = list(args)
+        a[i] = None
+        assert lib.ssd_fwd_train(*a) == c["LRT_ERR_NULL"], i
+    a = list(args)
+    a[10], a[11], a[15] = 128, 128, 1 << 40  # fp32 beyond the backward's limits: rejected before any launch
+    assert lib.ssd_fwd_train(*a) == c["LRT_ERR_SHAPE"]
+    base = [F, F, F, F, None, F, None, F, F, F, F, None, 1, 64, 2, 16, 16, 16, 0, None, 0, None]
+    assert lib.ssd_bwd_saved(*base) == c["LRT_ERR_WORKSPACE"]
+    for i in (0, 1, 2, 3, 5, 7, 8, 9, 10):
+        a = list(base)
+        a[i] = None
+        assert lib.ssd_bwd_saved(*a) == c["LRT_ERR_NULL"], i
+
+
 def test_ssd_backward_validation(L):
     c = codes()
     lib = L.lib()

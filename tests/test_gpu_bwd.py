@@ -182,6 +182,67 @@ def test_ssd_bwd_workload_shape():
     check_bwd(inp, 64, TOL[torch.bfloat16], variant="ssd")
 
 
+SSD_SAVED_CASES = ["fp32_tiny", "fp32_slow_h0_dht_T77_C32", "bf16_slow_T61_C16", "bf16_slow_C64_T300",
+                   "bf16_dk32_dv128", "bf16_long_slow_C64"]
+
+
+@pytest.mark.parametrize("name", SSD_SAVED_CASES)
+def test_ssd_fwd_train_and_bwd_saved(name):
+    """ssd_fwd_train's outputs and ssd_bwd_saved's gradients against the
+    oracle; a second ssd_bwd_saved on the same saved workspace matches the
+    stateless ssd_bwd for another upstream gradient."""
+    import linear_recurrent_token_amd as L
+    case = next(c for c in SSD_CASES if c[0] == name)
+    _, B, T, H, dk, dv, chunk, dt, shift, h0s, dhs = case
+    say(f"[ssd_fwd_train/ssd_bwd_saved] {name}")
+    inp = synth.make_inputs("ssd_fwd_bwd", B, T, H, dk, dv, dtype=dt, seed=0, device="cuda",
+                            gate_shift=shift, h0_std=h0s, dht_std=dhs)
+    q, k, v, la, h0, do, dht = (inp.get(n) for n in ("q", "k", "v", "log_a", "h0", "do", "dht"))
+    o, ht, saved = L.ssd_fwd_train(q, k, v, la, h0, chunk=chunk)
+    got = L.ssd_bwd_saved(q, k, v, la, h0, do, saved, dht, chunk=chunk)
+    torch.cuda.synchronize()
+    ro, rh = oracle.fwd("ssd", cpu(q), cpu(k), cpu(v), cpu(la), None, cpu(h0))
+    ref = oracle.bwd("ssd", cpu(q), cpu(k), cpu(v), cpu(la), None, cpu(h0), cpu(do), cpu(dht))
+    names = tuple(n for n in NAMES if n != "dbeta")
+    ref = [r for n, r in zip(NAMES, ref) if n != "dbeta"]
+    errs = {"o": rel(o.float().cpu().numpy(), ro), "ht": rel(ht.cpu().numpy(), rh)}
+    for n, g, r in zip(names, got, ref):
+        g = g.float().cpu().numpy()
+        assert np.all(np.isfinite(g)), n
+        errs[n] = rel(g, r)
+    say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if e > TOL[dt]}
+    assert not bad, bad
+    do2 = (torch.randn(do.shape, device="cuda", generator=torch.Generator("cuda").manual_seed(5))).to(dt)
+    again = L.ssd_bwd_saved(q, k, v, la, h0, do2, saved, dht, chunk=chunk)
+    plain = L.ssd_bwd(q, k, v, la, h0, do2, dht, chunk=chunk)
+    torch.cuda.synchronize()
+    for n, x, y in zip(names, again, plain):
+        x, y = x.float().cpu().numpy(), y.float().cpu().numpy()
+        assert rel(x, y) <= TOL[dt], (n, rel(x, y))
+
+
+def test_ssd_fwd_train_and_bwd_saved_workload():
+    """The Mamba2 training step at the 2048-token shape through the saved
+    pair, every element against the oracle."""
+    import linear_recurrent_token_amd as L
+    say("[ssd_fwd_train/ssd_bwd_saved] workload ssd_train_bf16_2k")
+    inp = synth.config_inputs("ssd_train_bf16_2k", device="cuda")
+    q, k, v, la, h0, do, dht = (inp.get(n) for n in ("q", "k", "v", "log_a", "h0", "do", "dht"))
+    o, ht, saved = L.ssd_fwd_train(q, k, v, la, h0, chunk=64)
+    got = L.ssd_bwd_saved(q, k, v, la, h0, do, saved, dht, chunk=64)
+    torch.cuda.synchronize()
+    ro, rh = oracle.fwd("ssd", cpu(q), cpu(k), cpu(v), cpu(la), None, cpu(h0))
+    ref = oracle.bwd("ssd", cpu(q), cpu(k), cpu(v), cpu(la), None, cpu(h0), cpu(do), cpu(dht))
+    ref = [r for n, r in zip(NAMES, ref) if n != "dbeta"]
+    errs = {"o": rel(o.float().cpu().numpy(), ro), "ht": rel(ht.cpu().numpy(), rh)}
+    errs.update({n: rel(g.float().cpu().numpy(), r)
+                 for n, g, r in zip(("dq", "dk", "dv", "dlog_a", "dh0"), got, ref)})
+    say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if e > TOL[torch.bfloat16]}
+    assert not bad, bad
+
+
 def test_bwd_rejects_unsupported_fp32_sizes():
     import linear_recurrent_token_amd as L
     inp = synth.make_inputs("gdn_fwd_bwd", 1, 64, 1, 128, 128, dtype=torch.float32, device="cuda")
