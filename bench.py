@@ -122,8 +122,9 @@ def kernel_model(name, c, esz=2, op="gdn_fwd + gdn_bwd"):
                  2 * C * dk + 2 * C * dk + 2 * C * dk + 2 * C * dv),
         # serial scan of the forward: reads q, k, W, U'^T, g, P, h0; writes o, ht
         "k_scan": (2 * dk * e + (dk + dv) * e + 4 + C * e + dv * e, 2 * st, 6 * dk * dv + 2 * C * dv),
-        # WY pass of the backward recompute: reads k, v, log_a, beta; writes W, U'^T, g, Tinv
-        "k_wy_bwd": ((dk + dv) * e + 8 + (dk + dv) * e + 4 + C * e, 0, 2 * C * dk + 2 * C * dk + 2 * C * dv),
+        # WY pass of the backward recompute: reads q, k, v, log_a, beta; writes W, U'^T, g, Tinv, P
+        "k_wy_bwd": ((2 * dk + dv) * e + 8 + (dk + dv) * e + 4 + C * e + C * e, 0,
+                     2 * C * dk + 2 * C * dk + 2 * C * dk + 2 * C * dv),
         # scan of the backward recompute: reads k, W, U'^T, g, h0; writes U^T and the chunk-start states
         "k_scan_bwd": (2 * dk * e + dv * e + 4 + dv * e + dk * dv * e / C, st, 4 * dk * dv),
         # reads k, v, log_a, beta; writes W, U'^T, Ktil^T, g, Tinv
@@ -133,8 +134,10 @@ def kernel_model(name, c, esz=2, op="gdn_fwd + gdn_bwd"):
         "k_state": ((2 * dk + dv) * e + 4 + dv * e + dk * dv * e / C, st, 4 * dk * dv),
         # reads q, k, do, g; writes dU_local
         "k_bwd_local": (2 * dk * e + 2 * dv * e + 4, 0, 2 * C * dk + 2 * C * dv),
-        # reads q, k, do, g, W, dU_local, dht; writes dU, the end-state gradients, dh0
-        "k_dstate": (3 * dk * e + 2 * dv * e + 4 + dv * e + dk * dv * e / C, 2 * st, 6 * dk * dv),
+        # reads q, k, do, g, W, P, dht; writes dU, the end-state gradients, dh0
+        # (dU_local = P^T dO formed in the kernel)
+        "k_dstate": (3 * dk * e + dv * e + C * e + 4 + dv * e + dk * dv * e / C, 2 * st,
+                     6 * dk * dv + 2 * C * dv),
         # reads q, k, do, g, states, state gradients, U, dU; writes dq, dW, dK part, dg part
         "k_grad1": (2 * dk * e + dv * e + 4 + 2 * dk * dv * e / C + 2 * dv * e + 3 * dk * e + 4, 0,
                     2 * C * dk + 2 * C * dv + 2 * dk * dv + 2 * C * dk + 2 * dk * dv + 2 * dk * dv + 2 * C * dk),
@@ -149,8 +152,6 @@ def kernel_model(name, c, esz=2, op="gdn_fwd + gdn_bwd"):
         per["k_wy"] = (b_th + C * e, b_bh, f_th)
         b_th, b_bh, f_th = per["k_scan"]
         per["k_scan"] = (b_th + dk * dv * e / C + dv * e, b_bh, f_th)
-        # the backward forms dU_local = P^T dO from the stored P: reads P, do; writes dU_local
-        per["k_bwd_local"] = (C * e + dv * e + dv * e, 0, 2 * C * dv)
     if op.startswith("ssd"):
         # the fused Mamba2 forward: reads q, k, v, log_a, h0; writes o, ht
         per["k_ssd_fwd"] = ((2 * dk + dv) * e + 4 + dv * e, 2 * st, 2 * C * (dk + dv) + 4 * dk * dv)

@@ -18,12 +18,16 @@
 //          s_j = e^(g_C - g_j) k_j . (U dH'^T)_j and dg_C += sum(s) + gamma_C <dH', Hn>
 //   dlog_a = reverse cumsum of dg within the chunk;  dh0 = dH at chunk 0.
 //
-// Kernels (256 threads each), in stream order:
-//   k_prep (WRITE_T) / k_state   recompute W, U', Ktil, Tinv, S_n and U
-//   k_bwd_local  per chunk: dU_local = P^T dO
-//   k_dstate     per (b, h, d_v block), chunks in reverse: dU and dH'
+// Kernels, in stream order:
+//   k_wy (writes T and P) / k_scan (backward mode)   recompute W, U', g, T, P,
+//                S_n and U -- skipped after gdn_fwd_train, which leaves them
+//   k_dstate     per (b, h, d_v block), chunks in reverse: dU (with
+//                dU_local = P^T dO from the stored P) and dH'
 //   k_grad1      per chunk: dQ, the dS/state part of dK, dW, part of dg
 //   k_grad2      per chunk: the WY part of dK, dV, dbeta, dg -> dlog_a
+// The Mamba2 backward (ssd_bwd) runs k_ssd_prep, k_scan, k_bwd_local
+// (dU_local = P^T dO from q and k), k_dstate and k_grad1 in their no-delta
+// modes; after ssd_fwd_train only the last three.
 #include <type_traits>
 
 #include "lrt_fwd_kernels.hpp"
@@ -90,13 +94,10 @@ struct LocalLds {
   static constexpr size_t TOTAL = G + C * 4;
 };
 
-// READ_P: P is read from the workspace (the training forward's WY pass wrote
-// it, rows [i][j], zero above the diagonal) instead of formed from q and k.
-template <typename E, int C, int DK, int DV, bool READ_P = false>
+template <typename E, int C, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q, const E* __restrict__ k,
                                                         const E* __restrict__ d_o, const float* __restrict__ wG,
-                                                        E* __restrict__ wdUl, int T, int H, int N, int ntiles,
-                                                        const E* __restrict__ wP = nullptr) {
+                                                        E* __restrict__ wdUl, int T, int H, int N, int ntiles) {
   typedef LocalLds<E, C, DK, DV> Lay;
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, NB = C / 16;
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
@@ -110,7 +111,6 @@ __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q,
 
   Tile<E, C, DK> tq, tk;
   Tile<E, C, DV> to;
-  Tile<E, C, C> tp;
   float rg = 0.f;
 #define LRT_LOCAL_LOAD(tile_)                                                             \
   {                                                                                       \
@@ -118,13 +118,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q,
     const int lnv = min(C, T - ln * C);                                                   \
     const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                           \
     const int lh = lbh % H;                                                               \
-    if constexpr (READ_P) {                                                               \
-      tp.load_block(wP + (size_t)(tile_) * C * C);                                        \
-    } else {                                                                              \
-      tq.load_rows_clamped(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                \
-      tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                \
-      rg = wG[(size_t)(tile_) * C + min((int)threadIdx.x, C - 1)];                        \
-    }                                                                                     \
+    tq.load_rows_clamped(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                  \
+    tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                  \
+    rg = wG[(size_t)(tile_) * C + min((int)threadIdx.x, C - 1)];                          \
     to.load_rows_clamped(d_o + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                \
   }
 
@@ -132,32 +128,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q,
   if (tile < ntiles) LRT_LOCAL_LOAD(tile)
   for (; tile < ntiles; tile += gridDim.x) {
     const int nv = min(C, T - (tile % N) * C);
-    if constexpr (READ_P) {
-      tp.store(sPt, LC);  // P rows [i][j]
-    } else {
-      tq.store_masked(sQ, LK, nv);
-      tk.store_masked(sK, LK, nv);
-      asm volatile("" ::"v"(rg));  // consumed by every lane (no load into it left pending)
-      if (threadIdx.x < C) sg[threadIdx.x] = rg;
-    }
+    tq.store_masked(sQ, LK, nv);
+    tk.store_masked(sK, LK, nv);
+    asm volatile("" ::"v"(rg));  // consumed by every lane (no load into it left pending)
+    if (threadIdx.x < C) sg[threadIdx.x] = rg;
     to.store_masked(sdO, LV, nv);
     lds_barrier();
     // the next tile (the last one again on the final pass: unconditional
     // loads keep the waits on older ones exact)
     LRT_LOCAL_LOAD(min(tile + (int)gridDim.x, ntiles - 1))
-    if constexpr (READ_P) {
-      // dU_local = P^T dO (rows j, cols v) -> [v][t] over the q, k area
-      for (int tt = w; tt < NB * (DV / 16); tt += kWaves) {
-        const int tj = tt / (DV / 16), tv = tt % (DV / 16);
-        f32x4 acc = zero4();
-        mma<C, true, true>(acc, sPt + tj * 16, LC, sdO + tv * 16, LV);
-        store4<E>(sUl + (tv * 16 + (l & 15)) * LC + tj * 16 + (l >> 4) * 4, acc);
-      }
-      lds_barrier();
-      lds_to_block<E, DV, C>(wdUl + (size_t)tile * DV * C, sUl, LC);
-      lds_barrier();
-      continue;
-    }
     for (int tt = w; tt < NB * NB; tt += kWaves) {
       const int ti = tt / NB, tj = tt % NB;
       f32x4 acc = zero4();
@@ -189,7 +168,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q,
 // hand.  dH' and dU leave through LDS as coalesced 16-byte rows.
 // DELTA = false is the Mamba2 recurrence (W = 0): dH <- gamma_C dH' +
 // Q^T diag(gamma) dO, and dU is dV.
-template <typename E, int C, int DK, int BV, int NW = 8, bool DELTA = true>
+// READ_P: wdUl is the stored P = (Q K^T) o Gamma (rows [i][j] per chunk, zero
+// above the diagonal) and the kernel forms dU_local = P^T dO itself, in the
+// phase that adds Ktil dH' (no separate dU_local pass).
+template <typename E, int C, int DK, int BV, int NW = 8, bool DELTA = true, bool READ_P = false>
 __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, const E* __restrict__ k,
                                                     const E* __restrict__ d_o, const float* __restrict__ wG,
                                                     const E* __restrict__ wW, const E* __restrict__ wdUl,
@@ -207,6 +189,8 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
   __shared__ __attribute__((aligned(16))) E sOg[C * LB];   // gamma_t dO rows (this block's columns)
   __shared__ __attribute__((aligned(16))) E sdU[BV * LC];  // dU^T
   __shared__ __attribute__((aligned(16))) E sdS[BV * LK];  // dH'^T
+  __shared__ __attribute__((aligned(16))) E sP[READ_P ? C * LC : 8];  // P rows [i][j]
+  __shared__ __attribute__((aligned(16))) E sO[READ_P ? C * LB : 8];  // dO rows (this block's columns)
   __shared__ float sg[C];
   __shared__ float sgs[2 * C];
 
@@ -231,6 +215,7 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
 
   Tile<E, C, DK, NT> tQ, tK, tW;
   Tile<E, C, BV, NT> tO;
+  Tile<E, C, C, NT> tP;
   typename Vec4<E>::T rU[UPW];  // packed: unpacked where used, so the fetch does not wait
   float rg = 0.f;
   // The previous chunk's operands, fetched in two parts while this chunk
@@ -244,10 +229,14 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
     if ((PART_) & 1) {                                                                              \
       tQ.load_rows_clamped(q + (ftok * H + h) * DK, (size_t)H * DK, fnv);                           \
       if constexpr (DELTA) tW.load_block(wW + ft * C * DK);                                         \
-      _Pragma("unroll") for (int s = 0; s < UPW; ++s) {                                             \
-        const int tt = min(w + NW * s, NU - 1);                                                     \
-        rU[s] = load4_raw<E>(wdUl + ft * DV * C + (size_t)(v0 + (tt % NTV) * 16 + (l & 15)) * C +  \
-                             (tt / NTV) * 16 + (l >> 4) * 4);                                       \
+      if constexpr (READ_P) {                                                                       \
+        tP.load_block(wdUl + ft * C * C);                                                           \
+      } else {                                                                                      \
+        _Pragma("unroll") for (int s = 0; s < UPW; ++s) {                                           \
+          const int tt = min(w + NW * s, NU - 1);                                                   \
+          rU[s] = load4_raw<E>(wdUl + ft * DV * C + (size_t)(v0 + (tt % NTV) * 16 + (l & 15)) * C + \
+                               (tt / NTV) * 16 + (l >> 4) * 4);                                     \
+        }                                                                                           \
       }                                                                                             \
       rg = wG[ft * C + min((int)threadIdx.x, C - 1)];                                               \
     }                                                                                               \
@@ -284,13 +273,18 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
     tQ.store_masked(sQ, LK, nv);
     if constexpr (DELTA) tW.store(sW, LK);
     f32x4 du[UPW];
+    if constexpr (READ_P) {
+      tP.store(sP, LC);
+    } else {
 #pragma unroll
-    for (int s = 0; s < UPW; ++s) du[s] = Vec4<E>::unpack(rU[s]);
+      for (int s = 0; s < UPW; ++s) du[s] = Vec4<E>::unpack(rU[s]);
+    }
     lds_barrier();
     LRT_DSTATE_FETCH(nprev, 1)
     lds_to_block<E, BV, DK, NT>(wdS + (tile * DV + v0) * DK, sdS, LK);
     tK.scale_rows(sgs);
     tK.store_masked(sKt, LK, nv);
+    if constexpr (READ_P) tO.store_masked(sO, LB, nv);
     tO.scale_rows(sgs + C);
     tO.store_masked(sOg, LB, nv);
     const float dec = __expf(sg[C - 1]);
@@ -302,7 +296,13 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
       const int tt = w + NW * s;
       if (tt < NU) {
         const int ti = tt / NTV, tv = tt % NTV;
-        f32x4 acc = du[s];
+        f32x4 acc;
+        if constexpr (READ_P) {
+          acc = zero4();
+          mma<C, true, true>(acc, sP + ti * 16, LC, sO + tv * 16, LB);  // dU_local = P^T dO
+        } else {
+          acc = du[s];
+        }
         mma<DK>(acc, sKt + ti * 16 * LK, LK, sdS + tv * 16 * LK, LK);
         store4<E>(sdU + (tv * 16 + (l & 15)) * LC + ti * 16 + (l >> 4) * 4, acc);
       }
@@ -966,17 +966,18 @@ __global__ __launch_bounds__(kThreads) void k_ssd_prep(const E* __restrict__ v, 
 
 // --------------------------------------------------------------- launcher
 // The forward quantities the gradient kernels read, recomputed: WY factors
-// with T (k_wy), then the chunk-start states S_n and U (k_scan, backward mode).
+// with T and P (k_wy), then the chunk-start states S_n and U (k_scan,
+// backward mode).
 template <typename E, int C, int DK, int DV>
-void bwd_recompute(const BwdWs& ws, const void* k, const void* v, const float* log_a, const float* beta,
-                   const float* h0, int B, int T, int H, void* stream) {
+void bwd_recompute(const BwdWs& ws, const void* q, const void* k, const void* v, const float* log_a,
+                   const float* beta, const float* h0, int B, int T, int H, void* stream) {
   const int N = (T + C - 1) / C;
   const int tiles = B * H * N;
   hipStream_t st = (hipStream_t)stream;
   constexpr int BV = DV < 64 ? DV : 64;  // state columns per workgroup
-  LRT_LAUNCH(kKWyBwd, (k_wy<E, C, DK, DV, false, true, kWyWaves>),
-             dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), st, (const E*)nullptr,
-             (const E*)k, (const E*)v, log_a, beta, T, H, N, tiles, (E*)ws.f.W, (E*)ws.f.Up, ws.f.G, (E*)nullptr,
+  LRT_LAUNCH(kKWyBwd, (k_wy<E, C, DK, DV, true, true, kWyWaves>),
+             dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), st, (const E*)q,
+             (const E*)k, (const E*)v, log_a, beta, T, H, N, tiles, (E*)ws.f.W, (E*)ws.f.Up, ws.f.G, (E*)ws.f.P,
              (E*)ws.T);
   ScanArgs<E> sa{};
   sa.k = (const E*)k;
@@ -997,8 +998,9 @@ void bwd_recompute(const BwdWs& ws, const void* k, const void* v, const float* l
              dim3(64 * kStateWaves), st, sa);
 }
 
-// saved: the workspace already holds W, g, T, S_n and U from gdn_fwd_train
-// of the same arguments, so the recompute is skipped.
+// saved: the workspace already holds W, g, T, P, S_n and U from
+// gdn_fwd_train of the same arguments, so the recompute is skipped.  The
+// reverse state scan forms dU_local = P^T dO from the stored P.
 template <typename E, int C, int DK, int DV>
 int bwd_impl(const BwdArgs& a, bool saved) {
   // fp32 gradient tiles need twice the LDS of bf16 ones: the fp32 backward
@@ -1014,18 +1016,10 @@ int bwd_impl(const BwdArgs& a, bool saved) {
     hipStream_t st = (hipStream_t)a.stream;
     constexpr int BV = DV < 64 ? DV : 64;  // state columns per workgroup
     const int sgrid = a.B * a.H * (DV / BV);
-    if (!saved) bwd_recompute<E, C, DK, DV>(ws, a.k, a.v, a.log_a, a.beta, a.h0, a.B, a.T, a.H, a.stream);
-    E* dUl = (E*)ws.f.Up;
-    if (saved)  // P from the training forward's WY pass
-      LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV, true>),
-                 dim3(persistent_grid(tiles, LocalLds<E, C, DK, DV>::TOTAL)), dim3(kThreads), st, (const E*)a.q,
-                 (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N, tiles, (const E*)ws.f.P);
-    else
-      LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV>), dim3(persistent_grid(tiles, LocalLds<E, C, DK, DV>::TOTAL)),
-                 dim3(kThreads), st, (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N, tiles);
-    LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves>), dim3(sgrid), dim3(64 * kStateWaves), st, (const E*)a.q,
-                       (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.W, (const E*)dUl, a.dht, a.dh0,
-                       (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
+    if (!saved) bwd_recompute<E, C, DK, DV>(ws, a.q, a.k, a.v, a.log_a, a.beta, a.h0, a.B, a.T, a.H, a.stream);
+    LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, true, true>), dim3(sgrid), dim3(64 * kStateWaves), st,
+               (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.W, (const E*)ws.f.P, a.dht,
+               a.dh0, (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
     LRT_LAUNCH(kKGrad1, (k_grad1<E, C, DK, DV, kGradWaves>), dim3(persistent_grid(tiles, Grad1Lds<E, C, DK, DV>::TOTAL)), dim3(64 * kGradWaves), st, (const E*)a.q,
                        (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.S, (const E*)ws.dS,
                        (const E*)ws.f.U, (const E*)ws.dU, (E*)a.dq, (E*)ws.dW, (E*)ws.dK1, ws.dg1, a.T, a.H, N, tiles,
