@@ -156,9 +156,9 @@ def kernel_model(name, c, esz=2, op="gdn_fwd + gdn_bwd"):
         # the fused Mamba2 forward: reads q, k, v, log_a, h0; writes o, ht
         per["k_ssd_fwd"] = ((2 * dk + dv) * e + 4 + dv * e, 2 * st, 2 * C * (dk + dv) + 4 * dk * dv)
     if op.startswith("ssd_fwd_train"):
-        # the training forward also writes the chunk-start states and g
+        # the training forward also writes the chunk-start states, g and P^T
         b_th, b_bh, f_th = per["k_ssd_fwd"]
-        per["k_ssd_fwd"] = (b_th + dk * dv * e / C + 4, b_bh, f_th)
+        per["k_ssd_fwd"] = (b_th + dk * dv * e / C + 4 + C * e, b_bh, f_th)
     if op in ("ssd_fwd + ssd_bwd", "ssd_fwd_train + ssd_bwd_saved"):
         per.update({
             # reads v, log_a; writes g, V^T
@@ -171,6 +171,10 @@ def kernel_model(name, c, esz=2, op="gdn_fwd + gdn_bwd"):
             "k_grad1": (2 * dk * e + dv * e + 4 + 2 * dk * dv * e / C + 2 * dv * e + 2 * dk * e + dv * e + 4, 0,
                         6 * C * dk + 2 * C * dv + 4 * dk * dv),
         })
+    if op == "ssd_fwd_train + ssd_bwd_saved":
+        # reads q, k, do, g, the stored P^T, dht; writes dU (= dv), the end-state gradients, dh0
+        per["k_dstate"] = (2 * dk * e + dv * e + 4 + C * e + dv * e + dk * dv * e / C, 2 * st,
+                           4 * dk * dv + 2 * C * dv)
     if op == "kda_fwd":
         per.update({
             # reads q, k, v, per-dim log_a, beta; writes W, U'^T, Ktil^T, chunk decay, Q o e^G, P

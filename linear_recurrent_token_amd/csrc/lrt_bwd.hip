@@ -169,9 +169,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q,
 // DELTA = false is the Mamba2 recurrence (W = 0): dH <- gamma_C dH' +
 // Q^T diag(gamma) dO, and dU is dV.
 // READ_P: wdUl is the stored P = (Q K^T) o Gamma (rows [i][j] per chunk, zero
-// above the diagonal) and the kernel forms dU_local = P^T dO itself, in the
-// phase that adds Ktil dH' (no separate dU_local pass).
-template <typename E, int C, int DK, int BV, int NW = 8, bool DELTA = true, bool READ_P = false>
+// above the diagonal; PT: stored transposed, rows [j][i]) and the kernel
+// forms dU_local = P^T dO itself, in the phase that adds Ktil dH' (no
+// separate dU_local pass).
+template <typename E, int C, int DK, int BV, int NW = 8, bool DELTA = true, bool READ_P = false, bool PT = false>
 __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, const E* __restrict__ k,
                                                     const E* __restrict__ d_o, const float* __restrict__ wG,
                                                     const E* __restrict__ wW, const E* __restrict__ wdUl,
@@ -299,7 +300,10 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
         f32x4 acc;
         if constexpr (READ_P) {
           acc = zero4();
-          mma<C, true, true>(acc, sP + ti * 16, LC, sO + tv * 16, LB);  // dU_local = P^T dO
+          if constexpr (PT)
+            mma<C, false, true>(acc, sP + ti * 16 * LC, LC, sO + tv * 16, LB);  // dU_local = P^T dO
+          else
+            mma<C, true, true>(acc, sP + ti * 16, LC, sO + tv * 16, LB);
         } else {
           acc = du[s];
         }
@@ -1073,12 +1077,18 @@ int ssd_bwd_impl(const BwdArgs& a, bool saved) {
                    dim3(64 * kStateWaves), st, sa);
       }
     }
-    E* dUl = (E*)ws.f.Up;
-    LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV>), dim3(persistent_grid(tiles, LocalLds<E, C, DK, DV>::TOTAL)),
-               dim3(kThreads), st, (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N, tiles);
-    LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, false>), dim3(sgrid), dim3(64 * kStateWaves), st,
-               (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)nullptr, (const E*)dUl, a.dht, a.dh0,
-               (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
+    if (saved) {  // dU_local from the P^T the training forward stored
+      LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, false, true, true>), dim3(sgrid),
+                 dim3(64 * kStateWaves), st, (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)nullptr,
+                 (const E*)ws.f.P, a.dht, a.dh0, (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
+    } else {
+      E* dUl = (E*)ws.f.Up;
+      LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV>), dim3(persistent_grid(tiles, LocalLds<E, C, DK, DV>::TOTAL)),
+                 dim3(kThreads), st, (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N, tiles);
+      LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, false>), dim3(sgrid), dim3(64 * kStateWaves), st,
+                 (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)nullptr, (const E*)dUl, a.dht, a.dh0,
+                 (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
+    }
     LRT_LAUNCH(kKGrad1, (k_grad1<E, C, DK, DV, kGradWaves, false>),
                dim3(persistent_grid(tiles, Grad1Lds<E, C, DK, DV>::TOTAL)), dim3(64 * kGradWaves), st, (const E*)a.q,
                (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.S, (const E*)ws.dS, (const E*)a.v,
@@ -1129,7 +1139,7 @@ int fwd_ssd_train_impl(const FwdArgs& a) {
     return -3;
   } else {
     const BwdWs ws = bwd_ws_layout(a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
-    return launch_ssd_fwd<E, C, DK, DV, true>(a, (E*)ws.f.S, ws.f.G);
+    return launch_ssd_fwd<E, C, DK, DV, true>(a, (E*)ws.f.S, ws.f.G, (E*)ws.f.P);
   }
 }
 

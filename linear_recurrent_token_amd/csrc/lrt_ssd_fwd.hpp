@@ -26,7 +26,9 @@
 //  * a wave's output and state tiles share one operand fragment per k step;
 //  * three barriers per chunk.
 // SAVE (the training forward) also writes each chunk's start state S_n
-// ([d_v][d_k] per chunk, as the backward reads it) and the gate cumsums g.
+// ([d_v][d_k] per chunk, as the backward reads it), the gate cumsums g and
+// P^T ([j][i] per chunk; the column blocks of one (b, h) write identical
+// values).
 // Measured on MI355X at B=16, T=2048, H=8, d=128: 64 value columns per
 // workgroup beat 32 (two workgroups per CU, but each recomputes Q K^T for
 // half the columns) and 16, and PF = 2 gains nothing over PF = 1.
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_ssd_fwd(const E* __restrict__ 
                                                         const E* __restrict__ v, const float* __restrict__ log_a,
                                                         const float* h0, float* ht, E* __restrict__ o, int T,
                                                         int H, int N, int DV, E* __restrict__ wS = nullptr,
-                                                        float* __restrict__ wG = nullptr) {
+                                                        float* __restrict__ wG = nullptr, E* __restrict__ wPt = nullptr) {
   typedef SsdFwdLds<E, C, DK, BV> Lay;
   constexpr int NT = 64 * NW;
   constexpr int LK = Lay::LK, LB = Lay::LB, LC = Lay::LC;
@@ -173,6 +175,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_ssd_fwd(const E* __restrict__ 
       }
     }
     lds_barrier();
+    if constexpr (SAVE) lds_to_block<E, C, C, NT>(wPt + ((size_t)bh * N + n) * C * C, sPt, LC);
     // ---- O^T = Hn^T (Q diag(gamma))^T + V^T P^T  (rows v, cols i) -> o rows
     if constexpr (NO % NW == 0 && NW % NB == 0) {
       // a wave's tiles share their column block i: one Q and one P^T
@@ -264,16 +267,16 @@ constexpr int ssd_bv() {
   else
     return BV;
 }
-// One workgroup per (b, h, block of value columns); SAVE also writes S_n and g.
+// One workgroup per (b, h, block of value columns); SAVE also writes S_n, g and P^T.
 template <typename E, int C, int DK, int DV, bool SAVE = false>
-int launch_ssd_fwd(const FwdArgs& a, E* wS = nullptr, float* wG = nullptr) {
+int launch_ssd_fwd(const FwdArgs& a, E* wS = nullptr, float* wG = nullptr, E* wPt = nullptr) {
   constexpr int BV = ssd_bv<E, C, DK, (DV < kSsdBV ? DV : kSsdBV)>();
   static_assert(SsdFwdLds<E, C, DK, BV>::TOTAL <= 160 * 1024, "k_ssd_fwd LDS");
   const int N = (a.T + C - 1) / C;
   const int grid = a.B * a.H * (DV / BV);
   LRT_LAUNCH(kKSsdFwd, (k_ssd_fwd<E, C, DK, BV, kStateWaves, kSsdPF, kSsdOcc, SAVE>), dim3(grid),
              dim3(64 * kStateWaves), a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.h0, a.ht,
-             (E*)a.o, a.T, a.H, N, DV, wS, wG);
+             (E*)a.o, a.T, a.H, N, DV, wS, wG, wPt);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
