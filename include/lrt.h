@@ -33,9 +33,10 @@
  *
  * Supported: B, H >= 1; T >= 0; d_k, d_v in {16, 32, 64, 128};
  * chunk in {16, 32, 64}; B * T and B * H * ceil(T / chunk) * d_v / 16 at
- * most 2^31 - 1; H * max(d_k, d_v) below 2^24.  T need not be a multiple of chunk.  The fp32
- * backward (gdn_bwd or ssd_bwd with LRT_F32) is limited to d_k, d_v <= 64 and
- * chunk <= 32 (LRT_ERR_SHAPE / LRT_ERR_CHUNK otherwise).
+ * most 2^31 - 1; H * max(d_k, d_v) below 2^24.  T need not be a multiple of
+ * chunk.  With LRT_F32 the backward entry points and the training forwards
+ * (gdn_bwd, ssd_bwd, *_fwd_train, *_bwd_saved) are limited to
+ * d_k, d_v <= 64 and chunk <= 32 (LRT_ERR_SHAPE / LRT_ERR_CHUNK otherwise).
  *
  * Ownership and execution: the caller allocates and frees every buffer,
  * including the workspace (size from lrt_workspace_bytes).  The library never
