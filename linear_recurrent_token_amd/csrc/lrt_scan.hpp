@@ -385,10 +385,11 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
         store4<E>(sU + vv * LC + t, u);
         if constexpr (!KDA)
           store4<E>(sUk + vv * LC + t, f32x4{u[0] * skt[t], u[1] * skt[t + 1], u[2] * skt[t + 2], u[3] * skt[t + 3]});
-        if constexpr ((MODE == kScanBwd || SAVE) && DELTA) store4<E>(a.U + (tile * DV + v0 + vv) * C + t, u);
       }
     }
     lds_barrier();
+    // U^T rows out from their LDS copy (16 bytes per access)
+    if constexpr ((MODE == kScanBwd || SAVE) && DELTA) lds_to_block<E, BV, C, NT>(a.U + (tile * DV + v0) * C, sU, LC);
     // ---- O^T = Hn^T (Q diag(gamma))^T + U^T P^T -> o rows; state update
     if constexpr (FWD) {
       for (int tt = w; tt < NO; tt += NW) {
