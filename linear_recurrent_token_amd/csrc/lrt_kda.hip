@@ -365,8 +365,9 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
       }
     }
     lds_barrier();
-    // W^T = X^T (T diag(b))^T (rows d, cols t): 4 consecutive d of one row of W per lane;
-    // U' = T (b V) (rows t, cols v): 4 consecutive t of one row of U'^T
+    // W^T = X^T (T diag(b))^T (rows d, cols t): 4 consecutive d of one row of W
+    // per lane; U' = T (b V) (rows t, cols v) in accumulator-tile order (a
+    // wave's 64 lanes write 512 contiguous bytes; the scan reads it per lane)
     constexpr int NWT = (DK / 16) * NB, NUT = NB * (DV / 16);
     for (int tt = w; tt < NWT + NUT; tt += NW) {
       f32x4 acc = zero4();
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
       } else {
         const int u = tt - NWT, ti = u / (DV / 16), tvb = u % (DV / 16);
         mma<C, false, true>(acc, sT + ti * 16 * LC, LC, sV + tvb * 16, LV);
-        store4<E>(wUp + ((size_t)tile * DV + tvb * 16 + (l & 15)) * C + ti * 16 + (l >> 4) * 4, acc);
+        acc_tile_store<E>(wUp + (size_t)tile * DV * C, ti * (DV / 16) + tvb, acc);
       }
     }
     lds_barrier();

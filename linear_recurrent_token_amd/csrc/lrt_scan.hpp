@@ -42,8 +42,9 @@ struct WyLds {
   static constexpr size_t TOTAL = G + 4 * C * 4;
 };
 
-// Outputs per tile (chunk-major per (b, h)): W [C][d_k] rows, U'^T [d_v][C],
-// g [C]; WRITE_P: P [C][C] rows (zero above the diagonal); WRITE_T: T [C][C].
+// Outputs per tile (chunk-major per (b, h)): W [C][d_k] rows, U' [C][d_v] in
+// accumulator-tile order (acc_tile_store), g [C]; WRITE_P: P [C][C] rows
+// (zero above the diagonal); WRITE_T: T [C][C].
 template <typename E, int C, int DK, int DV, bool WRITE_P, bool WRITE_T, int NW = 8>
 __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, const E* __restrict__ k,
                                                 const E* __restrict__ v, const float* __restrict__ log_a,
@@ -158,8 +159,10 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
     lds_barrier();
     if constexpr (WRITE_T) lds_to_block<E, C, C, NT>(wT + (size_t)tile * C * C, sT, LC);
     // W^T = K^T (T diag(b gamma))^T (rows d, cols t): a lane's 4 values are
-    // 4 consecutive d of one row of W; U' = T (b V) (rows t, cols v): 4
-    // consecutive t of one row of U'^T
+    // 4 consecutive d of one row of W; U' = T (b V) (rows t, cols v) in
+    // accumulator-tile order (a wave's 64 lanes write 512 contiguous bytes;
+    // the scan reads it per lane).  W stays row-major: its readers stage it in
+    // LDS, where rebuilding rows from tile order costs more than it saves.
     // unrolled (a known store count keeps the next chunk's wait exact) where
     // the registers allow
     constexpr int UWU = WRITE_P ? 1 : (NWT + NUT + NW - 1) / NW;
@@ -171,13 +174,11 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
       if (tt < NWT) {
         const int td = tt / NB, ti = tt % NB;
         mma<C, true, false>(acc, sK + td * 16, LK, sTw + ti * 16 * LC, LC);
-        const int t = ti * 16 + (l & 15), d0 = td * 16 + (l >> 4) * 4;
-        store4<E>(wW + ((size_t)tile * C + t) * DK + d0, acc);
+        store4<E>(wW + ((size_t)tile * C + ti * 16 + (l & 15)) * DK + td * 16 + (l >> 4) * 4, acc);
       } else {
         const int u = tt - NWT, ti = u / (DV / 16), tvb = u % (DV / 16);
         mma<C, false, true>(acc, sT + ti * 16 * LC, LC, sV + tvb * 16, LV);
-        const int vv = tvb * 16 + (l & 15), t0 = ti * 16 + (l >> 4) * 4;
-        store4<E>(wUp + ((size_t)tile * DV + vv) * C + t0, acc);
+        acc_tile_store<E>(wUp + (size_t)tile * DV * C, ti * (DV / 16) + tvb, acc);
       }
     }
     lds_barrier();
@@ -197,7 +198,7 @@ struct ScanArgs {
   const E* q;       // q rows (GDN forward)
   const E* k;       // k rows (GDN)
   const E* W;       // W rows [C][d_k]
-  const E* Up;      // U'^T [d_v][C]
+  const E* Up;      // U' [C][d_v], accumulator-tile order (Mamba2: V^T rows [d_v][C])
   const E* P;       // P rows [C][C] (forward)
   const E* Qg;      // (Q o e^G) rows [C][d_k] (KDA forward)
   const E* Kt;      // Ktil^T [d_k][C] (KDA)
@@ -328,7 +329,11 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
 #pragma unroll
       for (int s = 0; s < UPW; ++s) {
         const int tt = min(w + NW * s, NU - 1);
-        x.up[s] = load4_raw<E>(a.Up + (ft * DV + v0 + (tt % NTV) * 16 + (l & 15)) * C + (tt / NTV) * 16 + (l >> 4) * 4);
+        if constexpr (DELTA)  // U'^T in accumulator-tile order: one tile's 64 lanes are contiguous
+          x.up[s] = load4_raw<E>(a.Up + ft * DV * C +
+                                 ((size_t)((tt / NTV) * (DV / 16) + v0 / 16 + tt % NTV) * 64 + l) * 4);
+        else  // the Mamba2 recompute's V^T rows
+          x.up[s] = load4_raw<E>(a.Up + (ft * DV + v0 + (tt % NTV) * 16 + (l & 15)) * C + (tt / NTV) * 16 + (l >> 4) * 4);
       }
     }
   };
