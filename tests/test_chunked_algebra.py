@@ -43,3 +43,15 @@ def test_chunked_gdn_backward_equals_bptt(C, T):
     got = cr.gdn_bwd(q, k, v, la, beta, h0, do, dht, C)
     for name, a, b in zip(["dq", "dk", "dv", "dlog_a", "dbeta", "dh0"], got, ref):
         np.testing.assert_allclose(a, b, rtol=0, atol=1e-11 * max(1, np.abs(b).max()), err_msg=name)
+
+
+@pytest.mark.parametrize("C", [1, 4, 16])
+@pytest.mark.parametrize("T", [1, 7, 61])
+def test_chunked_kda_backward_equals_bptt(C, T):
+    """The effective-operand chunk backward of KDA (per-dimension gates)
+    equals back-propagation through the sequential recurrence."""
+    q, k, v, la, beta, h0, do, dht = _inp(T * 17 + C, T, 4, kda=True)
+    ref = oracle.bwd("kda", q, k, v, la, beta, h0, do, dht)
+    got = cr.kda_bwd(q, k, v, la, beta, h0, do, dht, C)
+    for name, a, b in zip(["dq", "dk", "dv", "dlog_a", "dbeta", "dh0"], got, ref):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-11 * max(1, np.abs(b).max()), err_msg=name)
