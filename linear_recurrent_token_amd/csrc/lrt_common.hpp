@@ -537,14 +537,24 @@ __device__ __forceinline__ float sum4(float x) {
   return x;
 }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
+// x moved across lanes by the DPP control CTRL (rows of 16 lanes outside
+// ROW_MASK, and lanes whose source lies outside their row, read 0).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave, in DPP moves (no LDS
+// round trip): a Hillis-Steele scan inside each row of 16 lanes (row_shr 1,
+// 2, 4, 8), then lane 15 of rows 0 and 2 added into rows 1 and 3
+// (row_bcast:15) and lane 31 into rows 2 and 3 (row_bcast:31).
 __device__ __forceinline__ float wave_incl_scan(float x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const float y = __shfl_up(x, d, 64);
-    if (l >= d) x += y;
-  }
+  x += dpp_or_zero<0x111>(x);
+  x += dpp_or_zero<0x112>(x);
+  x += dpp_or_zero<0x114>(x);
+  x += dpp_or_zero<0x118>(x);
+  x += dpp_or_zero<0x142, 0xa>(x);
+  x += dpp_or_zero<0x143, 0xc>(x);
   return x;
 }
 
