@@ -11,12 +11,23 @@ Primus", Table 4).  Inputs are synthetic (seeded), resident in HBM before the
 timed region, and rotated over three independent sets so that no step reads
 the previous step's inputs out of the 256 MB last-level cache.
 
-Prints one JSON line with the step throughput (tokens/s), a roofline entry
-for the kernel that takes most of the step's time (its algorithmic bytes or
-flops per launch over its average duration, timed with HIP events on its own
-stream) and a CPU baseline (the fp64 oracle on a bounded sample).
+Prints one JSON line:
+  value / ms_per_step   step throughput (tokens/s) and its median, p10, p90;
+  step                  the method's minimum HBM bytes and GEMM flops per step
+                        (per (token, head): forward 1,032 B / 180,224 flop,
+                        backward 1,808 B / 376,832 flop at d = 128, C = 64,
+                        plus the fp32 states read and written) over the step
+                        time, against 8 TB/s and 2,516.6 TFLOP/s; the
+                        hardware-counter bytes of all the step's kernels when
+                        counters of this build are committed;
+  roofline              the kernel with the largest share of the step: the
+                        method bytes of the pass it belongs to (forward or
+                        backward) per launch over its average duration, timed
+                        with HIP events on the launch stream;
+  copy_gbs              a 1 GiB device copy timed in the same run;
+  cpu_baseline          the fp64 oracle on a bounded sample, with the CPU model.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
 """
 import argparse
 import ctypes
@@ -28,9 +39,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
-MFMA_FP32_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4,096 dense bf16 flop/clk/CU
 WORKLOAD = "gdn_train_bf16_2k"  # the headline workload (default)
 # the headline and other named workloads bench.py can time (context lines)
 WORKLOADS = {
@@ -47,10 +57,11 @@ WORKLOADS = {
                                     "B=16 T=2048 H=8 d=128", "ssd_fwd + ssd_bwd"),
     "kda_bf16_1m": ("KDA chunked fwd tokens/s, B=1 T=2^20 H=16 d=128", "kda_fwd"),
 }
-
-
 # workloads that time another op on an existing workload's inputs
 CONFIG_OF = {"gdn_train_recompute_bf16_2k": "gdn_train_bf16_2k", "ssd_train_recompute_bf16_2k": "ssd_train_bf16_2k"}
+
+# the library kernels of each pass (the forward's and the backward's share of a step)
+FWD_KERNELS = {"k_wy", "k_scan", "k_scan_local", "k_carry", "k_ssd_fwd", "k_kda_prep", "k_state_copy"}
 
 
 def parse():
@@ -76,7 +87,6 @@ class Hip:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def events(self, n):
@@ -88,6 +98,11 @@ class Hip:
                 raise RuntimeError(f"hipEventCreate failed ({rc})")
             arr[i] = e.value
         return arr
+
+    def record(self, ev, stream):
+        rc = self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_ms(self, a, b):
         out = ctypes.c_float()
@@ -101,94 +116,32 @@ class Hip:
             self.lib.hipEventDestroy(e)
 
 
-def kernel_model(name, c, esz=2, op="gdn_fwd + gdn_bwd"):
-    """Algorithmic (bytes, flops) of one launch of a library kernel on workload c.
-
-    Bytes: each tensor the kernel must read or write, counted once per
-    launch (a tensor two workgroups both read counts once).  Flops: the dense
-    GEMM products the kernel's step of the method needs (2*M*N*K each; the
-    (I + A)^-1 solve and elementwise work excluded).  Per (token, head) terms
-    scale with B*T*H, per-state terms (fp32 d_k x d_v) with B*H.
-    """
+def method_model(op, c, has_h0, has_dht, esz=2):
+    """The method's minimum HBM bytes and GEMM flops of each pass of `op` on
+    workload c, per the per-(token, head) figures: every input read once and
+    every output written once (q, k, v, gates, beta in; o out; for the
+    backward also do in and dq, dk, dv and the gate/beta gradients out), plus
+    the fp32 states (h0 / ht, dht / dh0) per (b, h); flops = the dense GEMM
+    products of the chunkwise form (2*M*N*K each), no recompute.
+    Returns {"fwd": (bytes, flops), "bwd": (bytes, flops)} (no "bwd" for a
+    forward-only op)."""
     B, T, H, dk, dv, C = c["B"], c["T"], c["H"], c["dk"], c["dv"], c["chunk"]
     n_th, n_bh, st = B * T * H, B * H, dk * dv * 4
     e = esz
-    per = {
-        # whole forward: reads q, k, v, log_a, beta, h0; writes o, ht
-        "k_fwd": ((2 * dk + dv) * e + 8 + dv * e, 2 * st,
-                  2 * C * (3 * dk + 2 * dv) + 6 * dk * dv),
-        # WY pass of the forward: reads q, k, v, log_a, beta; writes W, U'^T, g, P
-        "k_wy": ((2 * dk + dv) * e + 8 + (dk + dv) * e + 4 + C * e, 0,
-                 2 * C * dk + 2 * C * dk + 2 * C * dk + 2 * C * dv),
-        # serial scan of the forward: reads q, k, W, U'^T, g, P, h0; writes o, ht
-        "k_scan": (2 * dk * e + (dk + dv) * e + 4 + C * e + dv * e, 2 * st, 6 * dk * dv + 2 * C * dv),
-        # WY pass of the backward recompute: reads q, k, v, log_a, beta; writes W, U'^T, g, Tinv, P
-        "k_wy_bwd": ((2 * dk + dv) * e + 8 + (dk + dv) * e + 4 + C * e + C * e, 0,
-                     2 * C * dk + 2 * C * dk + 2 * C * dk + 2 * C * dv),
-        # scan of the backward recompute: reads k, W, U'^T, g, h0; writes U^T and the chunk-start states
-        "k_scan_bwd": (2 * dk * e + dv * e + 4 + dv * e + dk * dv * e / C, st, 4 * dk * dv),
-        # reads k, v, log_a, beta; writes W, U'^T, Ktil^T, g, Tinv
-        "k_prep": ((dk + dv) * e + 8 + (2 * dk + dv) * e + 4 + C * e, 0,
-                   2 * C * dk + 2 * C * dk + 2 * C * dv),
-        # reads W, U'^T, Ktil^T, g, h0; writes U^T and the chunk-start states
-        "k_state": ((2 * dk + dv) * e + 4 + dv * e + dk * dv * e / C, st, 4 * dk * dv),
-        # reads q, k, do, g; writes dU_local
-        "k_bwd_local": (2 * dk * e + 2 * dv * e + 4, 0, 2 * C * dk + 2 * C * dv),
-        # reads q, k, do, g, W, P, dht; writes dU, the end-state gradients, dh0
-        # (dU_local = P^T dO formed in the kernel)
-        "k_dstate": (3 * dk * e + dv * e + C * e + 4 + dv * e + dk * dv * e / C, 2 * st,
-                     6 * dk * dv + 2 * C * dv),
-        # reads q, k, do, g, states, state gradients, U, dU; writes dq, dW, dK part, dg part
-        "k_grad1": (2 * dk * e + dv * e + 4 + 2 * dk * dv * e / C + 2 * dv * e + 3 * dk * e + 4, 0,
-                    2 * C * dk + 2 * C * dv + 2 * dk * dv + 2 * C * dk + 2 * dk * dv + 2 * dk * dv + 2 * C * dk),
-        # reads k, v, beta, g, Tinv, dW, dU, dK part, dg part; writes dk, dv, dlog_a, dbeta
-        "k_grad2": ((dk + dv) * e + 8 + C * e + dk * e + dv * e + dk * e + 4 + (dk + dv) * e + 8, 0,
-                    2 * C * dk + 2 * C * dv + 2 * C * dk + 2 * C * dv + 4 * C * C + 2 * C * dk + 4 * C * dk),
-    }
-    if op == "gdn_fwd_train + gdn_bwd_saved":
-        # the forward also keeps what the backward reads: the WY pass writes T
-        # beside W, U'^T, g and P; the scan writes the chunk-start states and U^T
-        b_th, b_bh, f_th = per["k_wy"]
-        per["k_wy"] = (b_th + C * e, b_bh, f_th)
-        b_th, b_bh, f_th = per["k_scan"]
-        per["k_scan"] = (b_th + dk * dv * e / C + dv * e, b_bh, f_th)
-    if op.startswith("ssd"):
-        # the fused Mamba2 forward: reads q, k, v, log_a, h0; writes o, ht
-        per["k_ssd_fwd"] = ((2 * dk + dv) * e + 4 + dv * e, 2 * st, 2 * C * (dk + dv) + 4 * dk * dv)
-    if op.startswith("ssd_fwd_train"):
-        # the training forward also writes the chunk-start states, g and P^T
-        b_th, b_bh, f_th = per["k_ssd_fwd"]
-        per["k_ssd_fwd"] = (b_th + dk * dv * e / C + 4 + C * e, b_bh, f_th)
-    if op in ("ssd_fwd + ssd_bwd", "ssd_fwd_train + ssd_bwd_saved"):
-        per.update({
-            # reads v, log_a; writes g, V^T
-            "k_ssd_prep": (dv * e + 4 + 4 + dv * e, 0, 0),
-            # reads k, V^T, g, h0; writes the chunk-start states
-            "k_scan_bwd": (dk * e + dv * e + 4 + dk * dv * e / C, st, 2 * dk * dv),
-            # reads q, k, do, g, dU_local, dht; writes dU (= dv), the end-state gradients, dh0
-            "k_dstate": (2 * dk * e + dv * e + 4 + dv * e + dv * e + dk * dv * e / C, 2 * st, 4 * dk * dv),
-            # reads q, k, do, g, states, state gradients, V^T, dU; writes dq, dk, dv, dlog_a
-            "k_grad1": (2 * dk * e + dv * e + 4 + 2 * dk * dv * e / C + 2 * dv * e + 2 * dk * e + dv * e + 4, 0,
-                        6 * C * dk + 2 * C * dv + 4 * dk * dv),
-        })
-    if op == "ssd_fwd_train + ssd_bwd_saved":
-        # reads q, k, do, g, the stored P^T, dht; writes dU (= dv), the end-state gradients, dh0
-        per["k_dstate"] = (2 * dk * e + dv * e + 4 + C * e + dv * e + dk * dv * e / C, 2 * st,
-                           4 * dk * dv + 2 * C * dv)
-    if op == "kda_fwd":
-        per.update({
-            # reads q, k, v, per-dim log_a, beta; writes W, U'^T, Ktil^T, chunk decay, Q o e^G, P
-            "k_kda_prep": ((2 * dk + dv) * e + dk * 4 + 4 + (2 * dk + dv) * e + dk * 4 / C + dk * e + C * e, 0,
-                           2 * C * dk + 2 * C * dk + 2 * C * dk + 2 * C * dv),
-            # reads W, U'^T, Ktil^T, chunk decay; writes U^T and the chunk-start states, ht
-            "k_state": ((2 * dk + dv) * e + dk * 4 / C + dv * e + dk * dv * e / C, st, 4 * dk * dv),
-            # reads Q o e^G, P, states, U; writes o
-            "k_out": (dk * e + C * e + dk * dv * e / C + dv * e + dv * e, 0, 2 * C * dv + 2 * dk * dv),
-        })
-    if name not in per:
-        return None
-    b_th, b_bh, f_th = per[name]
-    return b_th * n_th + b_bh * n_bh, f_th * n_th
+    ssd, kda = op.startswith("ssd"), op.startswith("kda")
+    gate = 4 * dk if kda else 4
+    beta = 0 if ssd else 4
+    fwd_b = (2 * dk + dv) * e + gate + beta + dv * e
+    fwd_f = 2 * C * (dk + dv) + 4 * dk * dv if ssd else 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv
+    out = {"fwd": (fwd_b * n_th + (int(has_h0) + 1) * st * n_bh, fwd_f * n_th)}
+    if "bwd" in op:
+        bwd_b = (2 * dk + 2 * dv) * e + 4 + beta + (2 * dk + dv) * e + 4 + beta
+        if ssd:
+            bwd_f = 4 * C * dk + 4 * C * dv + 8 * dk * dv
+        else:
+            bwd_f = 12 * C * dk + 8 * C * dv + 12 * dk * dv + 4 * C * C
+        out["bwd"] = (bwd_b * n_th + (int(has_h0) + int(has_dht) + 1) * st * n_bh, bwd_f * n_th)
+    return out
 
 
 def src_digest():
@@ -205,23 +158,44 @@ def src_digest():
     return h.hexdigest()[:16]
 
 
-def counted_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel factor), or
-    None when there is none for this kernel or the sources have changed."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{WORKLOAD}.json")
+def counted_traffic(workload):
+    """{kernel: HBM bytes per launch} from the committed rocprofv3 counter
+    summary of this workload (FETCH_SIZE + WRITE_SIZE scaled by the
+    copy-kernel factors), or None when there is none or the sources changed."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
     if rec.get("src_digest") != src_digest():
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else int(k["hbm_bytes_per_launch"])
+    return {k: int(v["hbm_bytes_per_launch"]) for k, v in rec.get("kernels", {}).items()}
+
+
+def copy_gbs(torch, hip, stream, dev, nbytes=1 << 30, reps=3):
+    """A plain 1 GiB device copy (read + write), timed with HIP events: the
+    achievable HBM bandwidth of this run.  Its buffers are freed after."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = hip.events(2)
+    hip.record(ev[0], stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    hip.record(ev[1], stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(ev[0], ev[1])
+    hip.destroy(ev)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes * reps / (ms / 1e3) / 1e9
 
 
 def copy_probe(torch, dev, nbytes=1 << 30):
-    """A plain device copy of known size, for scaling the byte counters."""
+    """Three plain device copies of known size, for scaling the byte counters
+    of a rocprofv3 --pmc run."""
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     src.fill_(1)
@@ -232,12 +206,21 @@ def copy_probe(torch, dev, nbytes=1 << 30):
     del src, dst
 
 
-def make_sets(L, synth, torch, wl, nsets):
-    sets = []
-    for s in range(nsets):
-        inp = synth.config_inputs(wl, device="cuda", seed=s)
-        sets.append(inp)
-    return sets
+def pct(xs, p):
+    s = sorted(xs)
+    i = min(len(s) - 1, max(0, int(round(p / 100.0 * (len(s) - 1)))))
+    return s[i]
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -259,12 +242,15 @@ def main():
     B, T, H, dk, dv, C = c["B"], c["T"], c["H"], c["dk"], c["dv"], c["chunk"]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    hip = Hip()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    copy = copy_gbs(torch, hip, stream, dev)
     # input sets larger than the last-level cache need no rotation
     nsets = args.sets if B * T * H * (2 * dk + dv) * 2 < (1 << 30) else 1
-    sets = make_sets(L, synth, torch, cfg, nsets)
+    sets = [synth.config_inputs(cfg, device="cuda", seed=s) for s in range(nsets)]
     code = L.LRT_BF16
-    opc = {"gdn_fwd + gdn_bwd": L.OP_GDN_BWD, "gdn_fwd_train + gdn_bwd_saved": L.OP_GDN_BWD, "gdn_fwd": L.OP_GDN_FWD, "ssd_fwd": L.OP_SSD_FWD,
-           "ssd_fwd + ssd_bwd": L.OP_SSD_BWD, "ssd_fwd_train + ssd_bwd_saved": L.OP_SSD_BWD,
+    opc = {"gdn_fwd + gdn_bwd": L.OP_GDN_BWD, "gdn_fwd_train + gdn_bwd_saved": L.OP_GDN_BWD, "gdn_fwd": L.OP_GDN_FWD,
+           "ssd_fwd": L.OP_SSD_FWD, "ssd_fwd + ssd_bwd": L.OP_SSD_BWD, "ssd_fwd_train + ssd_bwd_saved": L.OP_SSD_BWD,
            "kda_fwd": L.OP_KDA_FWD}[op]
     ws_bytes = max(L.workspace_bytes(L.OP_GDN_FWD, B, T, H, dk, dv, C, code),
                    L.workspace_bytes(opc, B, T, H, dk, dv, C, code))
@@ -272,7 +258,7 @@ def main():
     o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
     ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     grads = None
-    if op.endswith(("_bwd", "_bwd_saved")):
+    if "bwd" in op:
         grads = (torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
                  torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
                  torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev),
@@ -289,14 +275,14 @@ def main():
             L.ssd_bwd_saved(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), s["do"], ws, s.get("dht"), chunk=C,
                             out=grads)
             return
-        if op.startswith("ssd"):
-            L.ssd_fwd(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), chunk=C, o=o, ht=ht, workspace=ws)
-        elif op == "gdn_fwd_train + gdn_bwd_saved":
+        if op == "gdn_fwd_train + gdn_bwd_saved":
             L.gdn_fwd_train(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), chunk=C, o=o, ht=ht,
                             workspace=ws)
             L.gdn_bwd_saved(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), s["do"], ws, s.get("dht"),
                             chunk=C, out=grads)
             return
+        if op.startswith("ssd"):
+            L.ssd_fwd(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), chunk=C, o=o, ht=ht, workspace=ws)
         elif op == "kda_fwd":
             L.kda_fwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), chunk=C, o=o, ht=ht,
                       workspace=ws)
@@ -310,26 +296,24 @@ def main():
             L.gdn_bwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), s["do"], s.get("dht"),
                       chunk=C, workspace=ws, out=grads)
 
-    hip = Hip()
-    stream = torch.cuda.current_stream(dev).cuda_stream
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: throughput
-    ev = hip.events(2)
+    # timed region: throughput, one event per step boundary
+    ev = hip.events(args.steps + 1)
     t0 = time.perf_counter()
-    hip.lib.hipEventRecord(ctypes.c_void_p(ev[0]), ctypes.c_void_p(stream))
+    hip.record(ev[0], stream)
     for i in range(args.steps):
         step(i)
-    hip.lib.hipEventRecord(ctypes.c_void_p(ev[1]), ctypes.c_void_p(stream))
+        hip.record(ev[i + 1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = hip.elapsed_ms(ev[0], ev[1])
+    per = [hip.elapsed_ms(ev[i], ev[i + 1]) for i in range(args.steps)]
+    ms = hip.elapsed_ms(ev[0], ev[args.steps])
     hip.destroy(ev)
     ms_per_step = ms / args.steps
-    tokens = B * T
-    value = tokens * args.steps / (ms / 1e3)
+    value = B * T * args.steps / (ms / 1e3)
 
     # timed region again, every library kernel bracketed by HIP events
     per_step_kernels = 16
@@ -347,48 +331,59 @@ def main():
         name = L.lib().lrt_kernel_name(kinds[i]).decode()
         dur.setdefault(name, []).append(hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]))
     hip.destroy(kev)
-    kernels = {n: {"launches": len(d), "avg_us": 1e3 * sum(d) / len(d), "total_us_per_step": 1e3 * sum(d) / args.steps}
-               for n, d in dur.items()}
-    dom = max(kernels, key=lambda n: kernels[n]["total_us_per_step"])
-    model = kernel_model(dom, c, op=op)
-    roof = None
-    if model is not None:
-        # every launch of a kernel in a step carries the same work
-        per_launch_bytes, per_launch_flops = model
-        avg_s = kernels[dom]["avg_us"] / 1e6
-        ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-        common = {"kernel": dom, "algorithmic_bytes": int(per_launch_bytes),
-                  "algorithmic_flops": int(per_launch_flops), "avg_us": round(kernels[dom]["avg_us"], 2),
-                  "traffic": counted_traffic(dom) if wl == WORKLOAD else None}
-        if per_launch_flops / per_launch_bytes < ridge:
-            ach = per_launch_bytes / avg_s / 1e9
-            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), **common}
-        else:
-            ach = per_launch_flops / avg_s / 1e12
-            roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), **common}
-    for n, k in kernels.items():
-        m = kernel_model(n, c, op=op)
-        if m is not None:
-            k["gbs_algorithmic"] = m[0] / (k["avg_us"] / 1e6) / 1e9
-            k["tflops_algorithmic"] = m[1] / (k["avg_us"] / 1e6) / 1e12
+    kernels = {n: {"launches": len(d), "avg_us": 1e3 * sum(d) / len(d),
+                   "total_us_per_step": 1e3 * sum(d) / args.steps} for n, d in dur.items()}
 
-    # algorithmic step totals: GEMM flops of the method (forward, + backward)
-    if op.startswith("ssd"):
-        per_th = 2 * C * (dk + dv) + 4 * dk * dv
-        if grads is not None:  # Mamba2 backward: 8 GEMM products, state recompute excluded
-            per_th += 4 * C * dk + 4 * C * dv + 8 * dk * dv
+    has_h0 = sets[0].get("h0") is not None
+    has_dht = sets[0].get("dht") is not None
+    model = method_model(op, c, has_h0, has_dht)
+    step_bytes = sum(b for b, _ in model.values())
+    step_flops = sum(f for _, f in model.values())
+    step_s = ms_per_step / 1e3
+    traffic = counted_traffic(wl)
+    traffic_total = None
+    if traffic is not None and all(n in traffic for n in kernels):
+        traffic_total = int(sum(traffic[n] * k["launches"] / args.steps for n, k in kernels.items()))
+    for n, k in kernels.items():
+        k["share_of_step"] = k["total_us_per_step"] / 1e3 / ms_per_step
+        if traffic is not None and n in traffic:
+            k["counted_bytes_per_launch"] = traffic[n]
+            k["counted_gbs"] = traffic[n] / (k["avg_us"] / 1e6) / 1e9
+
+    dom = max(kernels, key=lambda n: kernels[n]["total_us_per_step"])
+    pas = "fwd" if dom in FWD_KERNELS or "bwd" not in model else "bwd"
+    mb, mf = model[pas]
+    avg_s = kernels[dom]["avg_us"] / 1e6
+    launches = kernels[dom]["launches"] / args.steps  # launches per step: the pass's units split among them
+    mb_launch, mf_launch = mb / launches, mf / launches
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    common = {"kernel": dom, "pass": pas, "method_bytes_per_launch": int(mb_launch),
+              "method_flops_per_launch": int(mf_launch), "avg_us": round(kernels[dom]["avg_us"], 2),
+              "traffic": traffic.get(dom) if traffic is not None else None}
+    if mf_launch / mb_launch < ridge:
+        ach = mb_launch / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), **common}
     else:
-        per_th = 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv
-        if grads is not None:
-            per_th += 12 * C * dk + 8 * C * dv + 12 * dk * dv + 4 * C * C
-    step_tflops = per_th * B * T * H / (ms_per_step / 1e3) / 1e12
+        ach = mf_launch / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), **common}
 
     cpu = None
-    if not args.no_cpu_baseline and wl == WORKLOAD:
-        cpu = cpu_baseline(sets[0], C, args.cpu_seconds)
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(op, sets[0], C, args.cpu_seconds)
 
+    step_rec = {
+        "method_bytes": int(step_bytes),
+        "method_flops": int(step_flops),
+        "hbm_gbs": round(step_bytes / step_s / 1e9, 1),
+        "hbm_frac": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "hbm_frac_of_copy": round(step_bytes / step_s / 1e9 / copy, 4),
+        "tflops": round(step_flops / step_s / 1e12, 2),
+        "mfma_frac": round(step_flops / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "traffic_total": traffic_total,
+        "kernel_us_sum": round(sum(k["total_us_per_step"] for k in kernels.values()), 2),
+    }
     line = {
         "metric": metric,
         "value": round(value, 1),
@@ -397,17 +392,21 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_p10": round(pct(per, 10), 4),
+        "ms_per_step_p50": round(pct(per, 50), 4),
+        "ms_per_step_p90": round(pct(per, 90), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": f"synthetic (seeded normal inputs; {nsets} rotating input set(s) resident in HBM)",
         "config": {"workload": wl, "B": B, "T": T, "H": H, "d_k": dk, "d_v": dv, "chunk": C, "op": op},
-        "step_tflops": round(step_tflops, 2),
-        "mfma_frac_of_bf16_peak": round(step_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "step": step_rec,
+        "mfma_frac_of_bf16_peak": step_rec["mfma_frac"],
+        "copy_gbs": round(copy, 1),
         "wall_s_timed": round(wall, 4),
         "roofline": roof,
-        "kernels": {n: {k: round(v, 2) if isinstance(v, float) else v for k, v in d.items()}
+        "kernels": {n: {k: round(v, 4) if isinstance(v, float) else v for k, v in d.items()}
                     for n, d in kernels.items()},
         "cpu_baseline": cpu,
     }
@@ -416,29 +415,53 @@ def main():
         copy_probe(torch, dev)
 
 
-def cpu_baseline(inp, C, target_s):
-    """The fp64 oracle (forward + backward) on whole sequences of the first
-    batch rows, adding rows until about target_s seconds of CPU work."""
+def cpu_baseline(op, inp, C, target_s):
+    """The fp64 oracle on a bounded sample of the workload: whole sequences of
+    the first batch rows (forward, plus the backward for a training step),
+    adding rows until about target_s seconds of CPU work; for a single long
+    sequence, a prefix of it doubled in length until the target is reached."""
     import oracle
 
-    cpu = {k: (v.detach().cpu() if v is not None else None) for k, v in inp.items()}
+    variant = "ssd" if op.startswith("ssd") else "kda" if op.startswith("kda") else "gdn"
+    train = "bwd" in op
+    cpu = {k: (v.detach().cpu() if v is not None and k != "qidx" else None) for k, v in inp.items()}
     B, T, H = cpu["q"].shape[:3]
     cores = oracle.max_threads()
-    per = max(1, min(B, -(-cores // H)))  # rows per call: enough (b, h) tasks for every core
-    done_tokens, spent, rows = 0, 0.0, 0
-    while rows < B and spent < target_s:
-        sl = slice(rows, min(B, rows + per))
-        a = {k: (v[sl].contiguous() if v is not None else None) for k, v in cpu.items()}
+
+    def run(a):
         t0 = time.perf_counter()
-        oracle.fwd("gdn", a["q"], a["k"], a["v"], a["log_a"], a["beta"], a["h0"])
-        oracle.bwd("gdn", a["q"], a["k"], a["v"], a["log_a"], a["beta"], a["h0"], a["do"], a.get("dht"))
-        spent += time.perf_counter() - t0
-        done_tokens += T * (sl.stop - sl.start)
-        rows = sl.stop
-    return {"value": round(done_tokens / spent, 1), "unit": "tokens/s", "cores": min(cores, per * H),
-            "kind": "oracle",
-            "sample": f"{rows} of {B} sequences x {T} tokens x {H} heads, fp64 forward + backward "
-                      f"({spent:.1f} s)"}
+        oracle.fwd(variant, a["q"], a["k"], a["v"], a["log_a"], a.get("beta"), a.get("h0"))
+        if train:
+            oracle.bwd(variant, a["q"], a["k"], a["v"], a["log_a"], a.get("beta"), a.get("h0"), a["do"], a.get("dht"))
+        return time.perf_counter() - t0
+
+    what = "forward + backward" if train else "forward"
+    if B == 1:
+        n, spent, done = 1024, 0.0, 0
+        while True:
+            a = {k: (v[:, :n].contiguous() if v is not None and v.dim() >= 3 and v.shape[1] == T else v)
+                 for k, v in cpu.items()}
+            spent = run(a)
+            done = n
+            if spent >= target_s / 2 or n >= T:
+                break
+            n = min(T, n * 2)
+        sample = f"first {done} of {T} tokens x {H} heads, fp64 {what} ({spent:.1f} s)"
+        tok = done
+        used = min(cores, H)
+    else:
+        per = max(1, min(B, -(-cores // H)))  # rows per call: enough (b, h) tasks for every core
+        tok, spent, rows = 0, 0.0, 0
+        while rows < B and spent < target_s:
+            sl = slice(rows, min(B, rows + per))
+            a = {k: (v[sl].contiguous() if v is not None else None) for k, v in cpu.items()}
+            spent += run(a)
+            tok += T * (sl.stop - sl.start)
+            rows = sl.stop
+        sample = f"{rows} of {B} sequences x {T} tokens x {H} heads, fp64 {what} ({spent:.1f} s)"
+        used = min(cores, per * H)
+    return {"value": round(tok / spent, 1), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "cpu_model": cpu_model(), "sample": sample}
 
 
 if __name__ == "__main__":

@@ -190,9 +190,11 @@ size_t lrt_workspace_bytes(int op, int B, int T, int H, int d_k, int d_v, int ch
 const char* lrt_status_string(int status);
 
 /*
- * Per-kernel timing hook for benchmarks (the only process-wide state of the
- * library; not thread-safe).  After lrt_profile_attach(events, kinds, n),
- * the next n kernels the library enqueues are each bracketed by
+ * Per-kernel timing hook for benchmarks.  It is per calling thread (kept in
+ * thread-local storage): it brackets only kernels enqueued by the thread
+ * that attached it, and calls from other threads neither see nor change it.
+ * After lrt_profile_attach(events, kinds, n) on a thread, the next n kernels
+ * the library enqueues from that thread are each bracketed by
  * hipEventRecord(events[2i]) and hipEventRecord(events[2i + 1]) on the
  * kernel's own stream, and kinds[i] receives the kernel's id.  `events`
  * holds 2n hipEvent_t created by the caller; `kinds` holds n ints.  Passing

@@ -10,13 +10,16 @@
 namespace lrt {
 
 // ---------------------------------------------------------------- timing hook
-// Process-wide; only the benchmark attaches it.
-static struct {
+// Per calling thread (only the benchmark attaches it): entry points called
+// from other threads are never bracketed, and no state is shared between
+// threads.
+struct ProfHook {
   hipEvent_t* ev = nullptr;
   int* kinds = nullptr;
   int n = 0;     // kernels that fit
   int next = 0;  // kernels recorded
-} g_prof;
+};
+static thread_local ProfHook g_prof;
 
 void prof_before(int kind, void* stream) {
   if (g_prof.ev == nullptr || g_prof.next >= g_prof.n) return;
@@ -34,14 +37,13 @@ static const char* const kKernelNames[kKNumKinds] = {"k_prep",  "k_state", "k_ou
                                                      "k_dstate", "k_grad1", "k_grad2",   "k_kda_prep",
                                                      "k_state_copy", "k_fwd", "k_wy", "k_scan", "k_wy_bwd", "k_scan_bwd", "k_scan_local", "k_carry", "k_ssd_prep", "k_ssd_fwd"};
 
+// Queried on every call (a device attribute read; nothing is cached between
+// calls).
 int device_cu_count() {
-  static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  if (dev < 64) cached[dev] = n;
   return n;
 }
 

@@ -364,9 +364,9 @@ struct Grad1Lds {
   static constexpr size_t DUT = ST + (size_t)DV * LK * es;        // dU^T [v][t]
   static constexpr size_t DSJ = DUT + (size_t)DV * LC * es;       // dS^T [j][i]
   static constexpr size_t G = DSJ + (size_t)C * LC * es;
-  static constexpr size_t DG = G + C * 4;
-  static constexpr size_t DOT = DG + C * 4;
-  static constexpr size_t TOTAL = DOT + 16;
+  static constexpr size_t DG = G + C * 4;                         // per-wave dg partials [NW][C]
+  static constexpr size_t DOT = DG + (size_t)kGradWaves * C * 4;  // per-wave <dH', Hn>, dg_C partials
+  static constexpr size_t TOTAL = DOT + 2 * kGradWaves * 4;
 };
 
 // DELTA = false is the Mamba2 recurrence (U = V, no W): the dK and dg
@@ -389,6 +389,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
   constexpr int V = 16 / (int)sizeof(E);
   constexpr int NKT = (DK / 16) * NB, KPW = (NKT + NW - 1) / NW;
   static_assert(NW % NB == 0, "waves must cover whole column blocks");
+  static_assert(NW == kGradWaves, "LDS partial slots are sized for kGradWaves");
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
   E* sQ = (E*)(smem + Lay::Q);
   E* sK = (E*)(smem + Lay::K);
@@ -399,8 +400,10 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
   E* sdUt = (E*)(smem + Lay::DUT);
   E* sdSj = (E*)(smem + Lay::DSJ);
   float* sg = (float*)(smem + Lay::G);
-  float* sdg = (float*)(smem + Lay::DG);
-  float* sdot = (float*)(smem + Lay::DOT);
+  float* sdg = (float*)(smem + Lay::DG);      // [NW][C] per-wave dg partials
+  float* sdot = (float*)(smem + Lay::DOT);    // [NW] per-wave <dH', Hn>
+  float* slast = sdot + NW;                   // [NW] per-wave terms of dg_C
+  float* mydg = sdg + wave_id() * C;
   const int w = wave_id(), l = lane_id();
 
   Tile<E, C, DK, NT> tq, tk;
@@ -456,11 +459,8 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
     tdu.store(sdUt, LC);
     tS.store(sS, LK);
     asm volatile("" ::"v"(rg));  // consumed by every lane (no load into it left pending)
-    if (threadIdx.x < C) {
-      sg[threadIdx.x] = rg;
-      sdg[threadIdx.x] = 0.f;
-    }
-    if (threadIdx.x == 0) sdot[0] = 0.f;
+    if (threadIdx.x < C) sg[threadIdx.x] = rg;
+    slot_zero<NW, C>(sdg);
     if constexpr (DELTA)
       if (ptile >= 0 && threadIdx.x < C) wdg1[(size_t)ptile * C + threadIdx.x] = pdg;
     tdS.load_block(wdS + (size_t)tile * DV * DK);  // dH' of this chunk, needed after dS
@@ -492,12 +492,14 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
           ecol += ev[r];
         }
         const float er = rowsum4(ev);
-        if ((l & 3) == 0) atomicAdd(&sdg[i0 + ((l >> 2) & 3)], er);
+        // a wave's tiles have distinct row blocks: one lane per row
+        if ((l & 3) == 0) mydg[i0 + ((l >> 2) & 3)] += er;
       }
       store4<E>(sdSj + j * LC + i0, ds);
     }
     ecol = sum4(ecol);
-    if (l < 16) atomicAdd(&sdg[(w % NB) * 16 + (l & 15)], -ecol);
+    wave_order();
+    if (l < 16) mydg[(w % NB) * 16 + (l & 15)] -= ecol;
     lds_barrier();
     // <dH', Hn> from the registers of this chunk's S and dH' (before any
     // store of this chunk, so the wait for dH' leaves the prefetch in flight);
@@ -516,7 +518,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
       }
       part = sum16(part);
       part = sum4(part);
-      if (l == 0) atomicAdd(sdot, part);
+      if (l == 0) sdot[w] = part;
     }
     LRT_G1_LOAD(next, 10)
     // dQ^T = gamma (Hn dO^T) + K^T dS^T (rows d, cols i), kept in registers;
@@ -549,7 +551,8 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
         }
       }
       esum = sum4(esum * gam);
-      if (l < 16) atomicAdd(&sdg[i], esum);
+      wave_order();
+      if (l < 16) mydg[i] += esum;
     }
     lds_barrier();
     // dq rows over the dead dO; dH'^T over the dead S
@@ -594,15 +597,23 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
         }
       }
       ssum = sum4(ssum * kt);
-      if (l < 16) {
-        atomicAdd(&sdg[j], -ssum);
-        atomicAdd(&sdg[C - 1], ssum);
-      }
+      const float stot = sum16(ssum);  // over the wave's 16 columns j (lanes 0..15)
+      wave_order();
+      if (l < 16) mydg[j] -= ssum;
+      if (l == 0) slast[w] = stot;
     }
     lds_barrier();
     if (threadIdx.x < C) {
-      float x = sdg[threadIdx.x];
-      if (threadIdx.x == C - 1) x += __expf(gC) * sdot[0];
+      float x = slot_sum<NW, C>(sdg, threadIdx.x);
+      if (threadIdx.x == C - 1) {
+        float last = 0.f, dot = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+          last += slast[w2];
+          dot += sdot[w2];
+        }
+        x += last + __expf(gC) * dot;
+      }
       pdg = x;
     }
     if constexpr (!DELTA) {
@@ -657,8 +668,11 @@ struct Grad2Lds {
   static constexpr size_t F = DUT + (size_t)DV * LC * es;          // dv rows; later dT^T, R^T, M^T
   static constexpr size_t FS = mx((size_t)C * LV * es, 3 * (size_t)C * LC * es);
   static constexpr size_t G = F + FS;
-  static constexpr size_t BB = G + C * 4, DG = BB + C * 4, DB = DG + C * 4, CX = DB + C * 4;
-  static constexpr size_t TOTAL = CX + C * 4;
+  static constexpr size_t BB = G + C * 4, DG = BB + C * 4;
+  // per-wave partials [NW][C] of dg, dbeta and cx (fixed-order reductions)
+  static constexpr size_t PDG = DG + C * 4, PDB = PDG + (size_t)kGradWaves * C * 4,
+                          PCX = PDB + (size_t)kGradWaves * C * 4;
+  static constexpr size_t TOTAL = PCX + (size_t)kGradWaves * C * 4;
 };
 
 template <typename E, int C, int DK, int DV, int NW = 8>
@@ -674,6 +688,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, NB = C / 16;
   constexpr int NKT = (DK / 16) * NB, KPW = (NKT + NW - 1) / NW;
   static_assert(NW % NB == 0, "waves must cover whole column blocks");
+  static_assert(NW == kGradWaves, "LDS partial slots are sized for kGradWaves");
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
   E* sK = (E*)(smem + Lay::K);
   E* sV = (E*)(smem + Lay::VV);
@@ -687,9 +702,13 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
   E* sMt = sRt + C * LC;
   float* sg = (float*)(smem + Lay::G);
   float* sb = (float*)(smem + Lay::BB);
-  float* sdg = (float*)(smem + Lay::DG);
-  float* sdb = (float*)(smem + Lay::DB);
-  float* scx = (float*)(smem + Lay::CX);
+  float* sdg = (float*)(smem + Lay::DG);    // dg from the first gradient kernel
+  float* pdgs = (float*)(smem + Lay::PDG);  // [NW][C] partials of dg
+  float* pdbs = (float*)(smem + Lay::PDB);  // [NW][C] partials of dbeta
+  float* pcxs = (float*)(smem + Lay::PCX);  // [NW][C] partials of cx
+  float* mydg = pdgs + wave_id() * C;
+  float* mydb = pdbs + wave_id() * C;
+  float* mycx = pcxs + wave_id() * C;
   const int w = wave_id(), l = lane_id();
 
   Tile<E, C, DK, NT> tk;
@@ -758,9 +777,10 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
       sg[t] = rg;
       sb[t] = t < nv ? rb : 0.f;
       sdg[t] = rd;
-      sdb[t] = 0.f;
-      scx[t] = 0.f;
     }
+    slot_zero<NW, C>(pdgs);
+    slot_zero<NW, C>(pdbs);
+    slot_zero<NW, C>(pcxs);
     f32x4 dka[KPW];
 #pragma unroll
     for (int s = 0; s < KPW; ++s) dka[s] = Vec4<E>::unpack(rk1[s]);
@@ -794,7 +814,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
         }
       }
       e = sum4(e);
-      if (l < 16) atomicAdd(&scx[jw], e);
+      if (l < 16) mycx[jw] += e;
     }
     // dY^T = dU^T Tinv (rows v, cols j): dV = b dY (rows staged), dbeta += dY_j . v_j
     {
@@ -813,7 +833,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
         for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sV[jw * LV + v0 + r]);
       }
       e = sum4(e);
-      if (l < 16) atomicAdd(&sdb[jw], e);
+      if (l < 16) mydb[jw] += e;
     }
     lds_barrier();
     lds_to_rows<E, C, DV, NT>(dv + (tok0 * H + h) * DV, (size_t)H * DV, sdV, LV, nv);
@@ -872,16 +892,18 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
           ecol += ev[r];
         }
         const float er = rowsum4(ev), br = rowsum4(bv);
+        // a wave's tiles have distinct row blocks: one lane per row
         if ((l & 3) == 0) {
           const int ir = i0 + ((l >> 2) & 3);
-          atomicAdd(&sdg[ir], er);
-          atomicAdd(&sdb[ir], br);
+          mydg[ir] += er;
+          mydb[ir] += br;
         }
       }
       store4<E>(sMt + kk * LC + i0, m);
     }
     ecol = sum4(ecol);
-    if (l < 16) atomicAdd(&sdg[jw], -ecol);
+    wave_order();
+    if (l < 16) mydg[jw] -= ecol;
     lds_barrier();
     LRT_G2_LOAD(next, 16)
     // dK^T += K^T M (cols j: sum_i k_i M_ij) + K^T M^T (cols i: sum_j k_j M_ij)
@@ -901,8 +923,9 @@ __global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, cons
       float dg = 0.f, db = 0.f;
       if (t < C) {
         const float gam = __expf(sg[t]);
-        dg = sdg[t] + sb[t] * gam * scx[t];
-        db = sdb[t] + gam * scx[t];
+        const float cx = slot_sum<NW, C>(pcxs, t);
+        dg = sdg[t] + slot_sum<NW, C>(pdgs, t) + sb[t] * gam * cx;
+        db = slot_sum<NW, C>(pdbs, t) + gam * cx;
       }
       pdla = wave_incl_suffix(dg);
       pdb = db;

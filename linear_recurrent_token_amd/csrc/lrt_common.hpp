@@ -43,6 +43,30 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 // LDS only.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Compiler-only ordering of one wave's LDS accesses: the LDS unit executes a
+// wave's instructions in order, so a later access of the same wave (any lane)
+// sees an earlier write once the compiler keeps the two in program order.
+__device__ __forceinline__ void wave_order() { asm volatile("" ::: "memory"); }
+
+// Reductions over the tokens of a chunk without atomics, so that repeated
+// runs give bitwise-identical sums: every wave adds its terms into its own
+// slot of NW x C partials (one lane per address per instruction, in program
+// order), and after a workgroup barrier the slots of token t are added in
+// wave order.
+template <int NW, int C>
+__device__ __forceinline__ void slot_zero(float* slots) {
+  float* s = slots + wave_id() * C;
+  for (int t = lane_id(); t < C; t += 64) s[t] = 0.f;
+  wave_order();
+}
+template <int NW, int C>
+__device__ __forceinline__ float slot_sum(const float* slots, int t) {
+  float x = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) x += slots[w * C + t];
+  return x;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
 // L2.  Renumber them so that consecutive logical ids run on one XCD (when
 // the grid divides evenly): work items that read the same data share a cache.

@@ -455,25 +455,26 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
 // columns): from the local pass's end states [E | M] of each segment,
 //   Hstart(s) = H,  H <- M(s) H + E(s)
 // starting from h0 (or zero); writes every segment's start state and the
-// final state.  M and H enter the MFMA as bf16, with fp32 accumulation, as
-// the state does in the chunk scan.
-template <int DK, int BV>
+// final state.  M and H enter the MFMA in the call's element type E (bf16, or
+// fp32 on the fp32 MFMA), with fp32 accumulation, as the state does in the
+// chunk scan.
+template <typename E, int DK, int BV>
 struct CarryLds {
-  static constexpr int LK = DK + 8;
-  static constexpr size_t M = 0;                                 // M rows [d][e] (bf16)
-  static constexpr size_t HT = M + (size_t)DK * LK * 2;          // H^T [c][e] (bf16)
-  static constexpr size_t TOTAL = HT + (size_t)BV * LK * 2;
+  static constexpr int LK = DK + lds_pad<E>();
+  static constexpr size_t M = 0;                                          // M rows [d][e]
+  static constexpr size_t HT = M + (size_t)DK * LK * sizeof(E);           // H^T [c][e]
+  static constexpr size_t TOTAL = HT + (size_t)BV * LK * sizeof(E);
 };
 
-template <int DK, int BV, int NW = 8>
+template <typename E, int DK, int BV, int NW = 8>
 __global__ __launch_bounds__(64 * NW) void k_carry(const float* __restrict__ hloc, const float* h0,
                                                    float* __restrict__ hstart, float* ht, int nseg, int DV) {
-  typedef CarryLds<DK, BV> Lay;
+  typedef CarryLds<E, DK, BV> Lay;
   constexpr int NT = 64 * NW, LK = Lay::LK, NTV = BV / 16;
   constexpr int NH = (DK / 16) * NTV, HPW = (NH + NW - 1) / NW;
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
-  bf16* sM = (bf16*)(smem + Lay::M);
-  bf16* sH = (bf16*)(smem + Lay::HT);
+  E* sM = (E*)(smem + Lay::M);
+  E* sH = (E*)(smem + Lay::HT);
   const int nvb = DV / BV;
   const int vb = blockIdx.x % nvb, bh = blockIdx.x / nvb, v0 = vb * BV;
   const int w = wave_id(), l = lane_id();
@@ -493,7 +494,7 @@ __global__ __launch_bounds__(64 * NW) void k_carry(const float* __restrict__ hlo
   }
   for (int sg = 0; sg < nseg; ++sg) {
     const float* base = hloc + ((size_t)bh * nseg + sg) * DK * LDX;
-    // this segment's start state; H^T -> LDS (bf16)
+    // this segment's start state; H^T -> LDS
 #pragma unroll
     for (int s = 0; s < HPW; ++s) {
       const int tt = w + NW * s;
@@ -503,13 +504,13 @@ __global__ __launch_bounds__(64 * NW) void k_carry(const float* __restrict__ hlo
         for (int r = 0; r < 4; ++r)
           hstart[(((size_t)bh * nseg + sg) * DK + td * 16 + (l >> 4) * 4 + r) * DV + v0 + tv * 16 + (l & 15)] =
               hacc[s][r];
-        store4<bf16>(sH + (tv * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, hacc[s]);
+        store4<E>(sH + (tv * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, hacc[s]);
       }
     }
-    // M rows -> LDS (bf16)
+    // M rows -> LDS
     for (int p = threadIdx.x; p < DK * (DK / 4); p += NT) {
       const int d = p / (DK / 4), e0 = (p % (DK / 4)) * 4;
-      store4<bf16>(sM + d * LK + e0, *(const f32x4*)(base + (size_t)d * LDX + DV + e0));
+      store4<E>(sM + d * LK + e0, *(const f32x4*)(base + (size_t)d * LDX + DV + e0));
     }
     lds_barrier();
     // H <- M H + E
@@ -584,7 +585,8 @@ int launch_scan_fwd_bv(const FwdArgs& a, const FwdWs& ws, int N, int nseg) {
     s.hs_ld = DV + DK;
     LRT_LAUNCH(kKScanLocal, (k_scan<E, C, DK, BV, kScanLocal, KDA, kStateWaves>),
                dim3(a.B * a.H * ((DV + DK) / BV) * nseg), dim3(64 * kStateWaves), st, s);
-    LRT_LAUNCH(kKCarry, (k_carry<DK, BV, kStateWaves>), dim3(bhv), dim3(64 * kStateWaves), st,
+    static_assert(CarryLds<E, DK, BV>::TOTAL <= 160 * 1024, "k_carry LDS");
+    LRT_LAUNCH(kKCarry, (k_carry<E, DK, BV, kStateWaves>), dim3(bhv), dim3(64 * kStateWaves), st,
                (const float*)ws.SegLoc, a.h0, ws.SegStart, a.ht, nseg, DV);
     s.hin = ws.SegStart;
     s.hout = nullptr;

@@ -66,9 +66,27 @@ def _unit_rows(x):
     return x / x.norm(dim=-1, keepdim=True)
 
 
+def orthonormal_keys(B, T, H, dk, seed, device="cpu"):
+    """Keys k_t, t < T <= dk, that are rows of one random orthogonal dk x dk
+    matrix per (b, h) (QR of a Gaussian matrix in fp64), as [B, T, H, dk]
+    fp32, and query indices j(t) drawn uniformly from [0, t] (int64 [B, T, H])."""
+    if T > dk:
+        raise ValueError("orthonormal keys need T <= d_k")
+    g = torch.Generator().manual_seed(int(seed) * 1000003 + _SLOTS["k"])
+    z = torch.randn((B, H, dk, dk), generator=g, dtype=torch.float64)
+    qmat, r = torch.linalg.qr(z)
+    qmat = qmat * torch.sign(torch.diagonal(r, dim1=-2, dim2=-1)).unsqueeze(-2)
+    keys = qmat.transpose(-1, -2)[:, :, :T, :].permute(0, 2, 1, 3).contiguous()  # rows -> [B, T, H, dk]
+    gq = torch.Generator().manual_seed(int(seed) * 1000003 + _SLOTS["q"])
+    u = torch.rand((B, T, H), generator=gq, dtype=torch.float64)
+    idx = torch.floor(u * (torch.arange(T, dtype=torch.float64).view(1, T, 1) + 1)).long()
+    return keys.to(torch.float32).to(device), idx.to(device)
+
+
 def make_inputs(op, B, T, H, dk, dv, dtype=torch.bfloat16, seed=0, device="cpu",
                 gate_shift=0.0, h0_std=0.0, gate="scalar", rank=16, gate_width=None,
-                with_do=False, dht_std=0.0, chunk=None):
+                with_do=False, dht_std=0.0, chunk=None, beta_shift=0.0, beta_kind="sigmoid",
+                keys="normal"):
     """Draw inputs for ``op`` in {'gdn_fwd', 'gdn_fwd_bwd', 'ssd_fwd', 'ssd_fwd_bwd', 'kda_fwd'}.
 
     Returns a dict with q, k, v [B,T,H,d] in ``dtype``; log_a fp32 [B,T,H]
@@ -82,15 +100,31 @@ def make_inputs(op, B, T, H, dk, dv, dtype=torch.bfloat16, seed=0, device="cpu",
       'lowrank' log a = -softplus(W_up (W_down x)), x ~ N(0,1) of width
                 ``gate_width`` (default H*dk), W ~ 0.02 N(0,1), rank ``rank``;
                 computed in fp32 on ``device`` in blocks of tokens.
+      'zero'    log a = 0 (no decay)
+    beta_kind: 'sigmoid' (b = sigmoid(N(0,1) + beta_shift)) or 'one' (b = 1).
+    keys: 'normal' (q, k ~ N(0,1), L2-normalised) or 'orthonormal' (k_t rows
+          of a random orthogonal matrix per (b, h), T <= d_k, and q_t = k_j(t)
+          with j(t) uniform in [0, t]; the indices are returned as 'qidx').
     """
     kda = op.startswith("kda")
     out = {}
-    out["q"] = _unit_rows(randn((B, T, H, dk), seed, "q", device)).to(dtype)
-    out["k"] = _unit_rows(randn((B, T, H, dk), seed, "k", device)).to(dtype)
+    if keys == "orthonormal":
+        kk, idx = orthonormal_keys(B, T, H, dk, seed, device)
+        out["k"] = kk.to(dtype)
+        out["q"] = torch.gather(kk, 1, idx[..., None].expand(B, T, H, dk)).to(dtype)
+        out["qidx"] = idx
+    else:
+        out["q"] = _unit_rows(randn((B, T, H, dk), seed, "q", device)).to(dtype)
+        out["k"] = _unit_rows(randn((B, T, H, dk), seed, "k", device)).to(dtype)
     out["v"] = randn((B, T, H, dv), seed, "v", device).to(dtype)
     if not op.startswith("ssd"):
-        out["beta"] = torch.sigmoid(randn((B, T, H), seed, "beta", device))
-    if kda and gate == "lowrank":
+        if beta_kind == "one":
+            out["beta"] = torch.ones((B, T, H), dtype=torch.float32, device=device)
+        else:
+            out["beta"] = torch.sigmoid(randn((B, T, H), seed, "beta", device) + beta_shift)
+    if gate == "zero":
+        out["log_a"] = torch.zeros((B, T, H, dk) if kda else (B, T, H), dtype=torch.float32, device=device)
+    elif kda and gate == "lowrank":
         out["log_a"] = lowrank_gate(B, T, H, dk, seed, device, rank=rank, width=gate_width)
     elif kda and gate == "perdim":
         out["log_a"] = -torch.nn.functional.softplus(randn((B, T, H, dk), seed, "gate", device) + gate_shift)

@@ -106,8 +106,10 @@ def test_backward_validation(L):
         a[i] = None
         assert lib.gdn_bwd(*a) == c["LRT_ERR_NULL"], i
     a = list(base)
-    a[19] = 32
-    assert lib.gdn_bwd(*a) == c["LRT_ERR_CHUNK"] or True  # chunk 32 is valid for fp32 at d = 16
+    a[19] = 48
+    assert lib.gdn_bwd(*a) == c["LRT_ERR_CHUNK"]
+    a[19] = 32  # a valid chunk: validation gets as far as the (missing) workspace
+    assert lib.gdn_bwd(*a) == c["LRT_ERR_WORKSPACE"]
     a = list(base)
     a[20] = 2
     assert lib.gdn_bwd(*a) == c["LRT_ERR_DTYPE"]
