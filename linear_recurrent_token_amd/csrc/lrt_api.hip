@@ -34,7 +34,7 @@ void prof_after(void* stream) {
 }
 
 static const char* const kKernelNames[kKNumKinds] = {"k_prep",  "k_state", "k_out",     "k_bwd_local",
-                                                     "k_dstate", "k_grad1", "k_grad2",   "k_kda_prep",
+                                                     "k_dstate", "k_grad",   "k_kda_prep",
                                                      "k_state_copy", "k_fwd", "k_wy", "k_scan", "k_wy_bwd", "k_scan_bwd", "k_scan_local", "k_carry", "k_ssd_prep", "k_ssd_fwd"};
 
 // Queried on every call (a device attribute read; nothing is cached between

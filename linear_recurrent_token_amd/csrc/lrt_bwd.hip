@@ -23,11 +23,11 @@
 //                S_n and U -- skipped after gdn_fwd_train, which leaves them
 //   k_dstate     per (b, h, d_v block), chunks in reverse: dU (with
 //                dU_local = P^T dO from the stored P) and dH'
-//   k_grad1      per chunk: dQ, the dS/state part of dK, dW, part of dg
-//   k_grad2      per chunk: the WY part of dK, dV, dbeta, dg -> dlog_a
+//   k_grad       per chunk: dQ, dK, dV, dbeta, dg -> dlog_a (dW and the
+//                state part of dK stay on chip)
 // The Mamba2 backward (ssd_bwd) runs k_ssd_prep, k_scan, k_bwd_local
-// (dU_local = P^T dO from q and k), k_dstate and k_grad1 in their no-delta
-// modes; after ssd_fwd_train only the last three.
+// (dU_local = P^T dO from q and k), k_dstate and k_grad in their no-delta
+// modes; after ssd_fwd_train only the last two.
 #include <type_traits>
 
 #include "lrt_fwd_kernels.hpp"
@@ -41,14 +41,10 @@ namespace lrt {
 //   T   [C][C]   E    Tinv
 //   dS  [dv][dk] E    dH'^T, gradient of each chunk's end state
 //   dU  [dv][C]  E    dU^T
-//   dW  [C][dk]  E    dW
-//   dK1 [C][dk]  E    the dS / state part of dK (accumulator-tile order, as dW)
-//   dg1 [C]      f32  part of dg
 // dU_local reuses the forward's U' tiles (dead once the state pass has run).
 struct BwdWs {
   FwdWs f;
-  void *T, *dS, *dU, *dW, *dK1;
-  float* dg1;
+  void *T, *dS, *dU;
   size_t bytes;
 };
 
@@ -66,9 +62,6 @@ static BwdWs bwd_ws_layout(int B, int T, int H, int dk, int dv, int C, size_t es
   w.T = take(tiles * C * C * esz);
   w.dS = take(tiles * dv * dk * esz);
   w.dU = take(tiles * dv * C * esz);
-  w.dW = take(tiles * C * dk * esz);
-  w.dK1 = take(tiles * C * dk * esz);
-  w.dg1 = (float*)take(tiles * C * sizeof(float));
   w.bytes = off;
   return w;
 }
@@ -345,66 +338,101 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
   }
 }
 
-// ----------------------------------------------------------------- k_grad1
-// Per chunk: dS, dQ (final), dW and the dS^T Q + Ktil-path part of dK (both
-// in accumulator-tile order), and the Gamma / output / Ktil / gamma_C parts
-// of dg.  Operands stay in their natural layouts; products contracting over
-// their rows use the LDS transpose read.
-template <typename E, int C, int DK, int DV>
-struct Grad1Lds {
+// ------------------------------------------------------------------ k_grad
+// Per chunk, the whole chunk-parallel part of the backward, once the reverse
+// state scan has produced dH' (the gradient of the chunk's end state) and dU:
+//   phase 1 (the state and intra-chunk attention part)
+//     dS  = (dO U^T) o Gamma_incl
+//     dQ  = diag(gamma) dO Hn^T + dS K                         (final)
+//     dW  = -dU Hn^T                                           (kept on chip)
+//     dK1 = diag(e^(g_C - g)) U dH'^T + dS^T Q                 (kept in registers)
+//   phase 2 (Gated DeltaNet: the WY part, W = Tinv X, U' = Tinv Y, X = diag(b gamma) K, Y = diag(b) V)
+//     dX = Tinv^T dW,  dY = Tinv^T dU,  dV = diag(b) dY
+//     dT = dW X^T + dU Y^T,  dA = -strict_lower(Tinv^T dT Tinv^T),  M = dA o diag(b) Gamma
+//     dK = dK1 + diag(b gamma) dX + M K + M^T K
+//   dg (the Gamma, gamma, Ktil, gamma_C, A and X terms) and dbeta are summed
+//   in a fixed order (per-wave partials); dlog_a = reverse cumsum of dg.
+// Phase 2's buffers lie over phase 1's, which are dead by then; dW, dK1 and
+// the dg partials never leave the chip.  Operands stay in their natural
+// layouts; products contracting over their rows use the LDS transpose read.
+// DELTA = false is the Mamba2 recurrence (U = V, no W, T = I): phase 1 alone,
+// dK = dK1, dV = dU; wU is then the value rows v [B, T, H, d_v] themselves.
+template <typename E, int C, int DK, int DV, bool DELTA, int NW = kGradWaves>
+struct GradLds {
   static constexpr int P = lds_pad<E>();
   static constexpr int LK = DK + P, LV = DV + P, LC = C + P;
   static constexpr size_t es = sizeof(E);
   static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
-  static constexpr size_t Q = 0;                                  // q rows [t][d]
-  static constexpr size_t K = Q + (size_t)C * LK * es;            // k rows [t][d]
-  static constexpr size_t DO = K + (size_t)C * LK * es;           // do rows [t][v]; later dq rows
+  // live through the whole chunk
+  static constexpr size_t K = 0;                                          // k rows [t][d]
+  static constexpr size_t DUT = K + (size_t)C * LK * es;                  // dU^T [v][t]
+  static constexpr size_t G = DUT + (size_t)DV * LC * es;                 // g [C]
+  static constexpr size_t BB = G + C * 4;                                 // beta [C]
+  static constexpr size_t PDG = BB + C * 4;                               // [NW][C] dg partials
+  static constexpr size_t PDB = PDG + (size_t)NW * C * 4;                 // [NW][C] dbeta partials
+  static constexpr size_t PCX = PDB + (DELTA ? (size_t)NW * C * 4 : 0);   // [NW][C] cx partials
+  static constexpr size_t DOT = PCX + (DELTA ? (size_t)NW * C * 4 : 0);   // [NW] <dH', Hn>, [NW] dg_C terms
+  static constexpr size_t U0 = (DOT + 2 * NW * 4 + 15) & ~(size_t)15;
+  // phase 1
+  static constexpr size_t Q = U0;                                         // q rows [t][d]
+  static constexpr size_t DO = Q + (size_t)C * LK * es;                   // do rows [t][v]; later dq rows
   static constexpr size_t UT = DO + mx((size_t)C * LV, (size_t)C * LK) * es;  // U^T [v][t] (Mamba2: v rows [t][v])
   static constexpr size_t ST = UT + mx((size_t)DV * LC, (size_t)C * LV) * es;  // S_n = Hn^T [v][d]; later dH'^T
-  static constexpr size_t DUT = ST + (size_t)DV * LK * es;        // dU^T [v][t]
-  static constexpr size_t DSJ = DUT + (size_t)DV * LC * es;       // dS^T [j][i]
-  static constexpr size_t G = DSJ + (size_t)C * LC * es;
-  static constexpr size_t DG = G + C * 4;                         // per-wave dg partials [NW][C]
-  static constexpr size_t DOT = DG + (size_t)kGradWaves * C * 4;  // per-wave <dH', Hn>, dg_C partials
-  static constexpr size_t TOTAL = DOT + 2 * kGradWaves * 4;
+  static constexpr size_t DSJ = ST + (size_t)DV * LK * es;                // dS^T [j][i]
+  static constexpr size_t END1 = DSJ + (size_t)C * LC * es;
+  // phase 2, over phase 1's buffers
+  static constexpr size_t VV = U0;                                        // v rows [t][v]
+  static constexpr size_t TT = VV + (size_t)C * LV * es;                  // Tinv [i][j]
+  static constexpr size_t DW = TT + (size_t)C * LC * es;                  // dW rows [i][d]; later dk rows
+  static constexpr size_t F = DW + (size_t)C * LK * es;                   // dv rows; later dT^T, R^T, M^T
+  static constexpr size_t END2 = F + mx((size_t)C * LV, 3 * (size_t)C * LC) * es;
+  static constexpr size_t TOTAL = DELTA ? mx(END1, END2) : END1;
 };
 
-// DELTA = false is the Mamba2 recurrence (U = V, no W): the dK and dg
-// computed here are then complete, and the kernel writes dk, dv (= dU, read
-// back from its LDS copy) and dlog_a (reverse cumsum of dg) itself; wdW,
-// wdK1 and wdg1 are unused, and wU is the value rows v [B, T, H, d_v]
-// themselves (staged as rows; the products read them k-inner).
 template <typename E, int C, int DK, int DV, int NW = 8, bool DELTA = true>
-__global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, const E* __restrict__ k,
-                                                    const E* __restrict__ d_o, const float* __restrict__ wG,
-                                                    const E* __restrict__ wS, const E* __restrict__ wdS,
-                                                    const E* __restrict__ wU, const E* __restrict__ wdU,
-                                                    E* __restrict__ dq, E* __restrict__ wdW, E* __restrict__ wdK1,
-                                                    float* __restrict__ wdg1, int T, int H, int N, int ntiles,
-                                                    E* __restrict__ dk_out, E* __restrict__ dv_out,
-                                                    float* __restrict__ dlog_a) {
-  typedef Grad1Lds<E, C, DK, DV> Lay;
+__global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const E* __restrict__ k,
+                                                   const E* __restrict__ v, const E* __restrict__ d_o,
+                                                   const float* __restrict__ beta, const float* __restrict__ wG,
+                                                   const E* __restrict__ wS, const E* __restrict__ wdS,
+                                                   const E* __restrict__ wU, const E* __restrict__ wdU,
+                                                   const E* __restrict__ wT, E* __restrict__ dq,
+                                                   E* __restrict__ dk_out, E* __restrict__ dv_out,
+                                                   float* __restrict__ dlog_a, float* __restrict__ dbeta, int T,
+                                                   int H, int N, int ntiles) {
+  typedef GradLds<E, C, DK, DV, DELTA, NW> Lay;
   constexpr int NT = 64 * NW;
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, NB = C / 16;
   constexpr int V = 16 / (int)sizeof(E);
   constexpr int NKT = (DK / 16) * NB, KPW = (NKT + NW - 1) / NW;
   static_assert(NW % NB == 0, "waves must cover whole column blocks");
-  static_assert(NW == kGradWaves, "LDS partial slots are sized for kGradWaves");
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
-  E* sQ = (E*)(smem + Lay::Q);
   E* sK = (E*)(smem + Lay::K);
+  E* sdUt = (E*)(smem + Lay::DUT);
+  float* sg = (float*)(smem + Lay::G);
+  float* sb = (float*)(smem + Lay::BB);
+  float* pdgs = (float*)(smem + Lay::PDG);
+  float* pdbs = (float*)(smem + Lay::PDB);
+  float* pcxs = (float*)(smem + Lay::PCX);
+  float* sdot = (float*)(smem + Lay::DOT);  // [NW] <dH', Hn>
+  float* slast = sdot + NW;                 // [NW] terms of dg_C
+  E* sQ = (E*)(smem + Lay::Q);
   E* sdO = (E*)(smem + Lay::DO);
   E* sdQ = (E*)(smem + Lay::DO);
   E* sUt = (E*)(smem + Lay::UT);
   E* sS = (E*)(smem + Lay::ST);
-  E* sdUt = (E*)(smem + Lay::DUT);
   E* sdSj = (E*)(smem + Lay::DSJ);
-  float* sg = (float*)(smem + Lay::G);
-  float* sdg = (float*)(smem + Lay::DG);      // [NW][C] per-wave dg partials
-  float* sdot = (float*)(smem + Lay::DOT);    // [NW] per-wave <dH', Hn>
-  float* slast = sdot + NW;                   // [NW] per-wave terms of dg_C
-  float* mydg = sdg + wave_id() * C;
+  E* sV = (E*)(smem + Lay::VV);
+  E* sT = (E*)(smem + Lay::TT);
+  E* sdW = (E*)(smem + Lay::DW);
+  E* sdK = (E*)(smem + Lay::DW);
+  E* sdV = (E*)(smem + Lay::F);
+  E* sdTt = (E*)(smem + Lay::F);
+  E* sRt = sdTt + C * LC;
+  E* sMt = sRt + C * LC;
   const int w = wave_id(), l = lane_id();
+  float* mydg = pdgs + w * C;
+  float* mydb = pdbs + w * C;
+  float* mycx = pcxs + w * C;
 
   Tile<E, C, DK, NT> tq, tk;
   Tile<E, C, DV, NT> to;
@@ -412,13 +440,19 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
   typename std::conditional<DELTA, Tile<E, DV, C, NT>, Tile<E, C, DV, NT>>::type tu;
   Tile<E, DV, C, NT> tdu;
   Tile<E, DV, DK, NT> tS, tdS;
-  float rg = 0.f;
-  // this chunk's dg partials, written out during the next chunk
-  float pdg = 0.f;
-  int ptile = -1;
+  Tile<E, C, DV, NT> tv;  // phase 2 (GDN): this chunk's v rows
+  Tile<E, C, C, NT> tt;   // phase 2 (GDN): this chunk's Tinv
+  float rg = 0.f, rb = 0.f;
+  // The previous chunk's dk rows, d log a and dbeta (GDN), written out while
+  // this chunk runs: stores left at the end of an iteration would be waited
+  // for by the next iteration's first wait on its prefetched loads.
+  Tile<E, C, DK, NT> pdk;
+  float pdla = 0.f, pdb = 0.f;
+  size_t ptok = 0;
+  int ph = 0, pnv = 0;
   // The next chunk's operands are fetched in parts (bit mask PART_) spread
   // over this chunk's phases, so no wave stalls on a full memory queue.
-#define LRT_G1_LOAD(tile_, PART_)                                                         \
+#define LRT_G_LOAD(tile_, PART_)                                                          \
   {                                                                                       \
     const int ln = (tile_) % N, lbh = (tile_) / N;                                        \
     const int lnv = min(C, T - ln * C);                                                   \
@@ -441,7 +475,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
   }
 
   int tile = blockIdx.x;
-  if (tile < ntiles) LRT_G1_LOAD(tile, 15)
+  if (tile < ntiles) LRT_G_LOAD(tile, 15)
   for (; tile < ntiles; tile += gridDim.x) {
     const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
     const int t0 = n * C, nv = min(C, T - t0);
@@ -460,21 +494,30 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
     tS.store(sS, LK);
     asm volatile("" ::"v"(rg));  // consumed by every lane (no load into it left pending)
     if (threadIdx.x < C) sg[threadIdx.x] = rg;
-    slot_zero<NW, C>(sdg);
-    if constexpr (DELTA)
-      if (ptile >= 0 && threadIdx.x < C) wdg1[(size_t)ptile * C + threadIdx.x] = pdg;
+    slot_zero<NW, C>(pdgs);
+    if constexpr (DELTA) {
+      slot_zero<NW, C>(pdbs);
+      slot_zero<NW, C>(pcxs);
+      if (pnv > 0) {
+        pdk.store_rows(dk_out + (ptok * H + ph) * DK, (size_t)H * DK, pnv);
+        if ((int)threadIdx.x < pnv) {
+          dlog_a[(ptok + threadIdx.x) * H + ph] = pdla;
+          dbeta[(ptok + threadIdx.x) * H + ph] = pdb;
+        }
+      }
+    }
     tdS.load_block(wdS + (size_t)tile * DV * DK);  // dH' of this chunk, needed after dS
     lds_barrier();
-    LRT_G1_LOAD(next, 1)
+    LRT_G_LOAD(next, 1)
 
     // dS = (dO U^T) o Gamma (inclusive); E = dS o (Q K^T) -> dg rows +, cols -
     // (a wave's tiles share column block w % NB: one column sum per wave)
     float ecol = 0.f;
 #pragma unroll
     for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
-      const int tt = w + NW * s2;
-      if (tt >= NB * NB) break;
-      const int ti = tt / NB, tj = tt % NB;
+      const int tt2 = w + NW * s2;
+      if (tt2 >= NB * NB) break;
+      const int ti = tt2 / NB, tj = tt2 % NB;
       const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
       f32x4 ds = zero4();
       if (tj <= ti) {
@@ -496,6 +539,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
         if ((l & 3) == 0) mydg[i0 + ((l >> 2) & 3)] += er;
       }
       store4<E>(sdSj + j * LC + i0, ds);
+      tile_fence();
     }
     ecol = sum4(ecol);
     wave_order();
@@ -520,12 +564,14 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
       part = sum4(part);
       if (l == 0) sdot[w] = part;
     }
-    LRT_G1_LOAD(next, 10)
+    // (GDN: the next do, U and S wait until after the dQ products, where
+    // register use peaks)
+    if constexpr (!DELTA) LRT_G_LOAD(next, 10)
     // dQ^T = gamma (Hn dO^T) + K^T dS^T (rows d, cols i), kept in registers;
-    // dW^T = -Hn dU^T -> workspace in accumulator-tile order.  A wave's tiles
-    // share their column block, so its dO, dS and dU fragments are the same
-    // for every tile (loaded once) and its dg term is one sum.
-    f32x4 dqa[KPW];
+    // dW^T = -Hn dU^T (GDN), kept in registers.  A wave's tiles share their
+    // column block, so its dO, dS and dU fragments are the same for every
+    // tile and its dg term is one sum.
+    f32x4 dqa[KPW], dwa[KPW];
     {
       const int ti = w % NB, i = ti * 16 + (l & 15);
       const float gam = __expf(sg[i]);
@@ -534,6 +580,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
       for (int s = 0; s < KPW; ++s) {
         const int td = w / NB + (NW / NB) * s;
         dqa[s] = zero4();
+        dwa[s] = zero4();
         if (td < DK / 16) {
           const int d0 = td * 16 + (l >> 4) * 4;
           f32x4 acc = zero4();
@@ -546,9 +593,10 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
           if constexpr (DELTA) {
             f32x4 dw = zero4();
             mma<DV, true, true>(dw, sS + td * 16, LK, sdUt + ti * 16, LC);
-            acc_tile_store<E>(wdW + (size_t)tile * C * DK, td * NB + ti, -dw);
+            dwa[s] = -dw;
           }
         }
+        tile_fence();
       }
       esum = sum4(esum * gam);
       wave_order();
@@ -558,15 +606,19 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
     // dq rows over the dead dO; dH'^T over the dead S
 #pragma unroll
     for (int s = 0; s < KPW; ++s) {
-      const int tt = w + NW * s;
-      if (tt < NKT) {
-        const int td = tt / NB, ti = tt % NB;
-        store4<E>(sdQ + (ti * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, dqa[s]);
-      }
+      const int td = w / NB + (NW / NB) * s, ti = w % NB;
+      if (td < DK / 16) store4<E>(sdQ + (ti * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, dqa[s]);
     }
     tdS.store(sS, LK);
     lds_barrier();
-    LRT_G1_LOAD(next, 4)
+    LRT_G_LOAD(next, DELTA ? 6 : 4)
+    if constexpr (DELTA) {
+      // phase 2's operands of this chunk (clamped rows: unconditional loads),
+      // issued here so their registers are not held through the dQ products
+      tv.load_rows_clamped(v + (tok0 * H + h) * DV, (size_t)H * DV, nv);
+      tt.load_block(wT + (size_t)tile * C * C);
+      rb = beta[(tok0 + min((int)threadIdx.x, nv - 1)) * H + h];
+    }
     lds_to_rows<E, C, DK, NT>(dq + (tok0 * H + h) * DK, (size_t)H * DK, sdQ, LK, nv);
     // dK1^T = e^(g_C - g_j) (dH' U^T) + Q^T dS   (rows d, cols j); a wave's
     // tiles share their column block j
@@ -579,6 +631,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
 #pragma unroll
       for (int s = 0; s < KPW; ++s) {
         const int td = w / NB + (NW / NB) * s;
+        dka[s] = zero4();
         if (td < DK / 16) {
           const int d0 = td * 16 + (l >> 4) * 4;
           f32x4 acc = zero4();
@@ -590,11 +643,9 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
           for (int r = 0; r < 4; ++r) ssum += acc[r] * to_f(sK[j * LK + d0 + r]);
           acc *= kt;
           mma<C, true, false>(acc, sQ + td * 16, LK, sdSj + tj * 16 * LC, LC);
-          if constexpr (DELTA)
-            acc_tile_store<E>(wdK1 + (size_t)tile * C * DK, td * NB + tj, acc);
-          else
-            dka[s] = acc;
+          dka[s] = acc;
         }
+        tile_fence();
       }
       ssum = sum4(ssum * kt);
       const float stot = sum16(ssum);  // over the wave's 16 columns j (lanes 0..15)
@@ -603,20 +654,192 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
       if (l == 0) slast[w] = stot;
     }
     lds_barrier();
-    if (threadIdx.x < C) {
-      float x = slot_sum<NW, C>(sdg, threadIdx.x);
-      if (threadIdx.x == C - 1) {
-        float last = 0.f, dot = 0.f;
+    if constexpr (DELTA) {
+      // ---- phase 2 operands over phase 1's dead buffers: v rows, Tinv, dW rows
+      tv.store_masked(sV, LV, nv);
+      tt.store(sT, LC);
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) {
-          last += slast[w2];
-          dot += sdot[w2];
-        }
-        x += last + __expf(gC) * dot;
+      for (int s = 0; s < KPW; ++s) {
+        const int td = w / NB + (NW / NB) * s, ti = w % NB;
+        if (td < DK / 16) store4<E>(sdW + (ti * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, dwa[s]);
       }
-      pdg = x;
-    }
-    if constexpr (!DELTA) {
+      asm volatile("" ::"v"(rb));
+      if (threadIdx.x < C) sb[threadIdx.x] = (int)threadIdx.x < nv ? rb : 0.f;
+      lds_barrier();
+      // dX^T = dW^T Tinv (rows d, cols j): dK += b gamma dX, cx_j = dX_j . k_j
+      // (a wave's tiles all lie in column block w % NB: one column sum per wave)
+      const int jw = (w % NB) * 16 + (l & 15);
+      {
+        const float bgj = sb[jw] * __expf(sg[jw]);
+        float e = 0.f;
+#pragma unroll
+        for (int s = 0; s < KPW; ++s) {
+          const int kt = w + NW * s;
+          if (kt < NKT) {
+            const int td = kt / NB, tj = kt % NB;
+            const int d0 = td * 16 + (l >> 4) * 4;
+            f32x4 acc = zero4();
+            mma<C, true, true>(acc, sdW + td * 16, LK, sT + tj * 16, LC);
+            dka[s] += bgj * acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sK[jw * LK + d0 + r]);
+          }
+          tile_fence();
+        }
+        e = sum4(e);
+        if (l < 16) mycx[jw] += e;
+      }
+      // dY^T = dU^T Tinv (rows v, cols j): dV = b dY (rows staged), dbeta += dY_j . v_j
+      {
+        const float bj = sb[jw];
+        float e = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < ((DV / 16) * NB + NW - 1) / NW; ++s2) {
+          const int tt2 = w + NW * s2;
+          if (tt2 >= (DV / 16) * NB) break;
+          const int tvv = tt2 / NB, tj = tt2 % NB;
+          const int v0 = tvv * 16 + (l >> 4) * 4;
+          f32x4 acc = zero4();
+          mma<C, false, true>(acc, sdUt + tvv * 16 * LC, LC, sT + tj * 16, LC);
+          store4<E>(sdV + jw * LV + v0, bj * acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sV[jw * LV + v0 + r]);
+          tile_fence();
+        }
+        e = sum4(e);
+        if (l < 16) mydb[jw] += e;
+      }
+      lds_barrier();
+      lds_to_rows<E, C, DV, NT>(dv_out + (tok0 * H + h) * DV, (size_t)H * DV, sdV, LV, nv);
+      lds_barrier();
+      LRT_G_LOAD(next, 8)
+      // dT = (dW K^T) diag(b gamma) + (dU V^T) diag(b)   (rows i, cols j) -> dT^T [j][i]
+#pragma unroll
+      for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
+        const int t2 = w + NW * s2;
+        if (t2 >= NB * NB) break;
+        const int ti = t2 / NB, tj = t2 % NB;
+        const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
+        f32x4 z1 = zero4(), z2 = zero4();
+        mma<DK>(z1, sdW + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
+        mma<DV, true, false>(z2, sdUt + ti * 16, LC, sV + tj * 16 * LV, LV);
+        store4<E>(sdTt + j * LC + i0, sb[j] * (__expf(sg[j]) * z1 + z2));
+        tile_fence();
+      }
+      lds_barrier();
+      // R = dT Tinv^T (rows i, cols k) -> R^T [k][i]
+#pragma unroll
+      for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
+        const int t2 = w + NW * s2;
+        if (t2 >= NB * NB) break;
+        const int ti = t2 / NB, tk2 = t2 % NB;
+        f32x4 acc = zero4();
+        mma<C, true, false>(acc, sdTt + ti * 16, LC, sT + tk2 * 16 * LC, LC);
+        store4<E>(sRt + (tk2 * 16 + (l & 15)) * LC + ti * 16 + (l >> 4) * 4, acc);
+        tile_fence();
+      }
+      lds_barrier();
+      // dA = -strict_lower(Tinv^T R); with A = b_i (K K^T) o Gamma:
+      //   M = dA o b_i Gamma -> M^T [k][i], dbeta_i += sum_k dA o Gamma o KK^T, E = dA o A -> dg
+      float ecol2 = 0.f;  // column kk = jw for every tile of this wave
+#pragma unroll
+      for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
+        const int t2 = w + NW * s2;
+        if (t2 >= NB * NB) break;
+        const int ti = t2 / NB, tk2 = t2 % NB;
+        const int kk = tk2 * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
+        f32x4 m = zero4();
+        if (tk2 <= ti) {
+          f32x4 acc = zero4(), kkt = zero4();
+          mma<C, true, false>(acc, sT + ti * 16, LC, sRt + tk2 * 16 * LC, LC);
+          mma<DK>(kkt, sK + ti * 16 * LK, LK, sK + tk2 * 16 * LK, LK);
+          f32x4 ev, bv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = i0 + r;
+            const float gam = (kk < i) ? __expf(sg[i] - sg[kk]) : 0.f;
+            const float da = -acc[r];
+            const float a = sb[i] * kkt[r] * gam;
+            m[r] = da * sb[i] * gam;
+            ev[r] = da * a;
+            bv[r] = da * gam * kkt[r];
+            ecol2 += ev[r];
+          }
+          const float er = rowsum4(ev), br = rowsum4(bv);
+          // a wave's tiles have distinct row blocks: one lane per row
+          if ((l & 3) == 0) {
+            const int ir = i0 + ((l >> 2) & 3);
+            mydg[ir] += er;
+            mydb[ir] += br;
+          }
+        }
+        store4<E>(sMt + kk * LC + i0, m);
+        tile_fence();
+      }
+      ecol2 = sum4(ecol2);
+      wave_order();
+      if (l < 16) mydg[jw] -= ecol2;
+      lds_barrier();
+      // dK^T += K^T M (cols j: sum_i k_i M_ij) + K^T M^T (cols i: sum_j k_j M_ij) -> dk rows over dW
+#pragma unroll
+      for (int s = 0; s < KPW; ++s) {
+        const int kt = w + NW * s;
+        if (kt < NKT) {
+          const int td = kt / NB, tj = kt % NB;
+          mma<C, true, false>(dka[s], sK + td * 16, LK, sMt + tj * 16 * LC, LC);
+          mma<C, true, true>(dka[s], sK + td * 16, LK, sMt + tj * 16, LC);
+          store4<E>(sdK + (tj * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, dka[s]);
+        }
+        tile_fence();
+      }
+      // dg (+ the X = diag(b gamma) K term), reverse cumsum -> dlog_a; dbeta
+      if (threadIdx.x < 64) {
+        const int t = threadIdx.x;
+        float dg = 0.f, db = 0.f;
+        if (t < C) {
+          const float gam = __expf(sg[t]);
+          const float cx = slot_sum<NW, C>(pcxs, t);
+          dg = slot_sum<NW, C>(pdgs, t) + sb[t] * gam * cx;
+          if (t == C - 1) {
+            float last = 0.f, dot = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) {
+              last += slast[w2];
+              dot += sdot[w2];
+            }
+            dg += last + __expf(gC) * dot;
+          }
+          db = slot_sum<NW, C>(pdbs, t) + gam * cx;
+        }
+        pdla = wave_incl_suffix(dg);
+        pdb = db;
+      }
+      lds_barrier();
+      pdk.load_lds(sdK, LK);
+      ptok = tok0;
+      ph = h;
+      pnv = nv;
+      lds_barrier();
+    } else {
+      // dg, reverse cumsum -> dlog_a (wave 0, one token per lane)
+      if (threadIdx.x < 64) {
+        const int t = threadIdx.x;
+        float dg = 0.f;
+        if (t < C) {
+          dg = slot_sum<NW, C>(pdgs, t);
+          if (t == C - 1) {
+            float last = 0.f, dot = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) {
+              last += slast[w2];
+              dot += sdot[w2];
+            }
+            dg += last + __expf(gC) * dot;
+          }
+        }
+        const float sfx = wave_incl_suffix(dg);
+        if (t < nv) dlog_a[(tok0 + t) * H + h] = sfx;
+      }
       // dk rows over the dead dq rows (copied out before the last barrier)
 #pragma unroll
       for (int s = 0; s < KPW; ++s) {
@@ -635,316 +858,21 @@ __global__ __launch_bounds__(64 * NW) void k_grad1(const E* __restrict__ q, cons
           *(u32x4*)(dv_out + ((tok0 + t) * H + h) * DV + c0) = pk;
         }
       }
-      // dlog_a = reverse cumsum of dg within the chunk (wave 0, one token per lane)
-      if (threadIdx.x < 64) {
-        const float sfx = wave_incl_suffix(threadIdx.x < C ? pdg : 0.f);
-        if ((int)threadIdx.x < nv) dlog_a[(tok0 + threadIdx.x) * H + h] = sfx;
-      }
       lds_barrier();
       lds_to_rows<E, C, DK, NT>(dk_out + (tok0 * H + h) * DK, (size_t)H * DK, sdQ, LK, nv);
+      lds_barrier();
     }
-    ptile = tile;
-    lds_barrier();
   }
-  if constexpr (DELTA)
-    if (ptile >= 0 && threadIdx.x < C) wdg1[(size_t)ptile * C + threadIdx.x] = pdg;
-#undef LRT_G1_LOAD
-}
-
-// ----------------------------------------------------------------- k_grad2
-// Per chunk: the WY part of the gradient (through Tinv, W = Tinv X, U' = Tinv Y
-// and A), dV, dbeta and dlog_a.
-template <typename E, int C, int DK, int DV>
-struct Grad2Lds {
-  static constexpr int P = lds_pad<E>();
-  static constexpr int LK = DK + P, LV = DV + P, LC = C + P;
-  static constexpr size_t es = sizeof(E);
-  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
-  static constexpr size_t K = 0;                                   // k rows [t][d]
-  static constexpr size_t VV = K + (size_t)C * LK * es;            // v rows [t][v]
-  static constexpr size_t TT = VV + (size_t)C * LV * es;           // Tinv [i][j]
-  static constexpr size_t DW = TT + (size_t)C * LC * es;           // dW [i][d]; later dk rows
-  static constexpr size_t DUT = DW + (size_t)C * LK * es;          // dU^T [v][t]
-  static constexpr size_t F = DUT + (size_t)DV * LC * es;          // dv rows; later dT^T, R^T, M^T
-  static constexpr size_t FS = mx((size_t)C * LV * es, 3 * (size_t)C * LC * es);
-  static constexpr size_t G = F + FS;
-  static constexpr size_t BB = G + C * 4, DG = BB + C * 4;
-  // per-wave partials [NW][C] of dg, dbeta and cx (fixed-order reductions)
-  static constexpr size_t PDG = DG + C * 4, PDB = PDG + (size_t)kGradWaves * C * 4,
-                          PCX = PDB + (size_t)kGradWaves * C * 4;
-  static constexpr size_t TOTAL = PCX + (size_t)kGradWaves * C * 4;
-};
-
-template <typename E, int C, int DK, int DV, int NW = 8>
-__global__ __launch_bounds__(64 * NW) void k_grad2(const E* __restrict__ k, const E* __restrict__ v,
-                                                    const float* __restrict__ beta, const float* __restrict__ wG,
-                                                    const E* __restrict__ wT, const E* __restrict__ wdW,
-                                                    const E* __restrict__ wdU, const E* __restrict__ wdK1,
-                                                    const float* __restrict__ wdg1, E* __restrict__ dk,
-                                                    E* __restrict__ dv, float* __restrict__ dlog_a,
-                                                    float* __restrict__ dbeta, int T, int H, int N, int ntiles) {
-  typedef Grad2Lds<E, C, DK, DV> Lay;
-  constexpr int NT = 64 * NW;
-  constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, NB = C / 16;
-  constexpr int NKT = (DK / 16) * NB, KPW = (NKT + NW - 1) / NW;
-  static_assert(NW % NB == 0, "waves must cover whole column blocks");
-  static_assert(NW == kGradWaves, "LDS partial slots are sized for kGradWaves");
-  __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
-  E* sK = (E*)(smem + Lay::K);
-  E* sV = (E*)(smem + Lay::VV);
-  E* sT = (E*)(smem + Lay::TT);
-  E* sdW = (E*)(smem + Lay::DW);
-  E* sdK = (E*)(smem + Lay::DW);
-  E* sdUt = (E*)(smem + Lay::DUT);
-  E* sdV = (E*)(smem + Lay::F);
-  E* sdTt = (E*)(smem + Lay::F);
-  E* sRt = sdTt + C * LC;
-  E* sMt = sRt + C * LC;
-  float* sg = (float*)(smem + Lay::G);
-  float* sb = (float*)(smem + Lay::BB);
-  float* sdg = (float*)(smem + Lay::DG);    // dg from the first gradient kernel
-  float* pdgs = (float*)(smem + Lay::PDG);  // [NW][C] partials of dg
-  float* pdbs = (float*)(smem + Lay::PDB);  // [NW][C] partials of dbeta
-  float* pcxs = (float*)(smem + Lay::PCX);  // [NW][C] partials of cx
-  float* mydg = pdgs + wave_id() * C;
-  float* mydb = pdbs + wave_id() * C;
-  float* mycx = pcxs + wave_id() * C;
-  const int w = wave_id(), l = lane_id();
-
-  Tile<E, C, DK, NT> tk;
-  Tile<E, C, DV, NT> tv;
-  Tile<E, C, C, NT> tt;
-  Tile<E, DV, C, NT> tdu;
-  AccTiles<E, DK / 16, NB, NT> tdw;  // dW in accumulator-tile order
-  typename Vec4<E>::T rk1[KPW];  // the first part of dK, accumulator layout (rows d, cols j), packed
-  float rg = 0.f, rb = 0.f, rd = 0.f;
-  // The previous chunk's dK rows, d log a and dbeta, written out while this
-  // chunk runs: stores left at the end of an iteration would be waited for
-  // by the next iteration's first wait on its prefetched loads.
-  Tile<E, C, DK, NT> pdk;
-  float pdla = 0.f, pdb = 0.f;
-  size_t ptok = 0;
-  int ph = 0, pnv = 0;
-  // The next chunk's operands are fetched in parts (bit mask PART_), one
-  // part per phase of this chunk: a wave that issues all of them at once
-  // stalls on the full memory queue instead of computing.
-#define LRT_G2_LOAD(tile_, PART_)                                                                 \
-  {                                                                                               \
-    const int ln = (tile_) % N, lbh = (tile_) / N;                                                \
-    const int lnv = min(C, T - ln * C);                                                           \
-    const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                                   \
-    const int lh = lbh % H;                                                                       \
-    if ((PART_) & 1) {                                                                            \
-      tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                        \
-      const int tc = min((int)threadIdx.x, C - 1);                                                \
-      rg = wG[(size_t)(tile_) * C + tc];                                                          \
-      rb = beta[(ltok + min(tc, lnv - 1)) * H + lh];                                              \
-      rd = wdg1[(size_t)(tile_) * C + tc];                                                        \
-    }                                                                                             \
-    if ((PART_) & 2) tv.load_rows_clamped(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv);         \
-    if ((PART_) & 4) {                                                                            \
-      tt.load_block(wT + (size_t)(tile_) * C * C);                                                \
-      tdu.load_block(wdU + (size_t)(tile_) * DV * C);                                             \
-    }                                                                                             \
-    if ((PART_) & 8) tdw.load(wdW + (size_t)(tile_) * C * DK);                                    \
-    if ((PART_) & 16) {                                                                           \
-      _Pragma("unroll") for (int s = 0; s < KPW; ++s) {                                           \
-        const int kt_ = w + NW * s;                                                               \
-        rk1[s] = load4_raw<E>(wdK1 + (size_t)(tile_) * C * DK + ((size_t)min(kt_, NKT - 1) * 64 + l) * 4); \
-      }                                                                                           \
-    }                                                                                             \
-  }
-
-  int tile = blockIdx.x;
-  if (tile < ntiles) LRT_G2_LOAD(tile, 31)
-  for (; tile < ntiles; tile += gridDim.x) {
-    const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
-    const int t0 = n * C, nv = min(C, T - t0);
-    const size_t tok0 = (size_t)b * T + t0;
-    // the next chunk (the last one again on the final pass: its loads go
-    // unused, but unconditional loads keep the waits on older ones exact)
-    const int next = min(tile + (int)gridDim.x, ntiles - 1);
-    tk.store_masked(sK, LK, nv);
-    tv.store_masked(sV, LV, nv);
-    tt.store(sT, LC);
-    tdu.store(sdUt, LC);
-    tdw.store(sdW, LK);
-    // every lane consumes the gate registers here, so no load into them is
-    // still pending (and waited for) when the next prefetch overwrites them
-    asm volatile("" ::"v"(rg), "v"(rb), "v"(rd));
-    if (threadIdx.x < C) {
-      const int t = threadIdx.x;
-      sg[t] = rg;
-      sb[t] = t < nv ? rb : 0.f;
-      sdg[t] = rd;
-    }
-    slot_zero<NW, C>(pdgs);
-    slot_zero<NW, C>(pdbs);
-    slot_zero<NW, C>(pcxs);
-    f32x4 dka[KPW];
-#pragma unroll
-    for (int s = 0; s < KPW; ++s) dka[s] = Vec4<E>::unpack(rk1[s]);
+  if constexpr (DELTA) {
     if (pnv > 0) {
-      pdk.store_rows(dk + (ptok * H + ph) * DK, (size_t)H * DK, pnv);
+      pdk.store_rows(dk_out + (ptok * H + ph) * DK, (size_t)H * DK, pnv);
       if ((int)threadIdx.x < pnv) {
         dlog_a[(ptok + threadIdx.x) * H + ph] = pdla;
         dbeta[(ptok + threadIdx.x) * H + ph] = pdb;
       }
     }
-    lds_barrier();
-    LRT_G2_LOAD(next, 1)
-    // dX^T = dW^T Tinv (rows d, cols j): dK += b gamma dX, cx_j = dX_j . k_j
-    // (a wave's tiles all lie in column block w % NB, so each wave reduces
-    // its column sums once, after its tiles)
-    const int jw = (w % NB) * 16 + (l & 15);
-    {
-      const float bgj = sb[jw] * __expf(sg[jw]);
-      float e = 0.f;
-#pragma unroll
-      for (int s = 0; s < KPW; ++s) {
-        const int kt = w + NW * s;
-        if (kt < NKT) {
-          const int td = kt / NB, tj = kt % NB;
-          const int d0 = td * 16 + (l >> 4) * 4;
-          f32x4 acc = zero4();
-          mma<C, true, true>(acc, sdW + td * 16, LK, sT + tj * 16, LC);
-          dka[s] += bgj * acc;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sK[jw * LK + d0 + r]);
-        }
-      }
-      e = sum4(e);
-      if (l < 16) mycx[jw] += e;
-    }
-    // dY^T = dU^T Tinv (rows v, cols j): dV = b dY (rows staged), dbeta += dY_j . v_j
-    {
-      const float bj = sb[jw];
-      float e = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < ((DV / 16) * NB + NW - 1) / NW; ++s2) {
-        const int tt2 = w + NW * s2;
-        if (tt2 >= (DV / 16) * NB) break;
-        const int tvv = tt2 / NB, tj = tt2 % NB;
-        const int v0 = tvv * 16 + (l >> 4) * 4;
-        f32x4 acc = zero4();
-        mma<C, false, true>(acc, sdUt + tvv * 16 * LC, LC, sT + tj * 16, LC);
-        store4<E>(sdV + jw * LV + v0, bj * acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sV[jw * LV + v0 + r]);
-      }
-      e = sum4(e);
-      if (l < 16) mydb[jw] += e;
-    }
-    lds_barrier();
-    lds_to_rows<E, C, DV, NT>(dv + (tok0 * H + h) * DV, (size_t)H * DV, sdV, LV, nv);
-    lds_barrier();
-    LRT_G2_LOAD(next, 2)
-    // dT = (dW K^T) diag(b gamma) + (dU V^T) diag(b)   (rows i, cols j) -> dT^T [j][i]
-#pragma unroll
-    for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
-      const int t2 = w + NW * s2;
-      if (t2 >= NB * NB) break;
-      const int ti = t2 / NB, tj = t2 % NB;
-      const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
-      f32x4 z1 = zero4(), z2 = zero4();
-      mma<DK>(z1, sdW + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
-      mma<DV, true, false>(z2, sdUt + ti * 16, LC, sV + tj * 16 * LV, LV);
-      store4<E>(sdTt + j * LC + i0, sb[j] * (__expf(sg[j]) * z1 + z2));
-    }
-    lds_barrier();
-    LRT_G2_LOAD(next, 4)
-    // R = dT Tinv^T (rows i, cols k) -> R^T [k][i]
-#pragma unroll
-    for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
-      const int t2 = w + NW * s2;
-      if (t2 >= NB * NB) break;
-      const int ti = t2 / NB, tk2 = t2 % NB;
-      f32x4 acc = zero4();
-      mma<C, true, false>(acc, sdTt + ti * 16, LC, sT + tk2 * 16 * LC, LC);
-      store4<E>(sRt + (tk2 * 16 + (l & 15)) * LC + ti * 16 + (l >> 4) * 4, acc);
-    }
-    lds_barrier();
-    LRT_G2_LOAD(next, 8)
-    // dA = -strict_lower(Tinv^T R); with A = b_i (K K^T) o Gamma:
-    //   M = dA o b_i Gamma -> M^T [k][i], dbeta_i += sum_k dA o Gamma o KK^T, E = dA o A -> dg
-    float ecol = 0.f;  // column kk = jw for every tile of this wave
-#pragma unroll
-    for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
-      const int t2 = w + NW * s2;
-      if (t2 >= NB * NB) break;
-      const int ti = t2 / NB, tk2 = t2 % NB;
-      const int kk = tk2 * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
-      f32x4 m = zero4();
-      if (tk2 <= ti) {
-        f32x4 acc = zero4(), kkt = zero4();
-        mma<C, true, false>(acc, sT + ti * 16, LC, sRt + tk2 * 16 * LC, LC);
-        mma<DK>(kkt, sK + ti * 16 * LK, LK, sK + tk2 * 16 * LK, LK);
-        f32x4 ev, bv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = i0 + r;
-          const float gam = (kk < i) ? __expf(sg[i] - sg[kk]) : 0.f;
-          const float da = -acc[r];
-          const float a = sb[i] * kkt[r] * gam;
-          m[r] = da * sb[i] * gam;
-          ev[r] = da * a;
-          bv[r] = da * gam * kkt[r];
-          ecol += ev[r];
-        }
-        const float er = rowsum4(ev), br = rowsum4(bv);
-        // a wave's tiles have distinct row blocks: one lane per row
-        if ((l & 3) == 0) {
-          const int ir = i0 + ((l >> 2) & 3);
-          mydg[ir] += er;
-          mydb[ir] += br;
-        }
-      }
-      store4<E>(sMt + kk * LC + i0, m);
-    }
-    ecol = sum4(ecol);
-    wave_order();
-    if (l < 16) mydg[jw] -= ecol;
-    lds_barrier();
-    LRT_G2_LOAD(next, 16)
-    // dK^T += K^T M (cols j: sum_i k_i M_ij) + K^T M^T (cols i: sum_j k_j M_ij)
-#pragma unroll
-    for (int s = 0; s < KPW; ++s) {
-      const int kt = w + NW * s;
-      if (kt < NKT) {
-        const int td = kt / NB, tj = kt % NB;
-        mma<C, true, false>(dka[s], sK + td * 16, LK, sMt + tj * 16 * LC, LC);
-        mma<C, true, true>(dka[s], sK + td * 16, LK, sMt + tj * 16, LC);
-        store4<E>(sdK + (tj * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, dka[s]);
-      }
-    }
-    // dg (+ the X = diag(b gamma) K term), reverse cumsum -> dlog_a; dbeta
-    if (threadIdx.x < 64) {
-      const int t = threadIdx.x;
-      float dg = 0.f, db = 0.f;
-      if (t < C) {
-        const float gam = __expf(sg[t]);
-        const float cx = slot_sum<NW, C>(pcxs, t);
-        dg = sdg[t] + slot_sum<NW, C>(pdgs, t) + sb[t] * gam * cx;
-        db = slot_sum<NW, C>(pdbs, t) + gam * cx;
-      }
-      pdla = wave_incl_suffix(dg);
-      pdb = db;
-    }
-    lds_barrier();
-    pdk.load_lds(sdK, LK);
-    ptok = tok0;
-    ph = h;
-    pnv = nv;
-    lds_barrier();
   }
-  if (pnv > 0) {
-    pdk.store_rows(dk + (ptok * H + ph) * DK, (size_t)H * DK, pnv);
-    if ((int)threadIdx.x < pnv) {
-      dlog_a[(ptok + threadIdx.x) * H + ph] = pdla;
-      dbeta[(ptok + threadIdx.x) * H + ph] = pdb;
-    }
-  }
-#undef LRT_G2_LOAD
+#undef LRT_G_LOAD
 }
 
 // ------------------------------------------------------------- k_ssd_prep
@@ -1047,13 +975,11 @@ int bwd_impl(const BwdArgs& a, bool saved) {
     LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, true, true>), dim3(sgrid), dim3(64 * kStateWaves), st,
                (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.W, (const E*)ws.f.P, a.dht,
                a.dh0, (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
-    LRT_LAUNCH(kKGrad1, (k_grad1<E, C, DK, DV, kGradWaves>), dim3(persistent_grid(tiles, Grad1Lds<E, C, DK, DV>::TOTAL)), dim3(64 * kGradWaves), st, (const E*)a.q,
-                       (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.S, (const E*)ws.dS,
-                       (const E*)ws.f.U, (const E*)ws.dU, (E*)a.dq, (E*)ws.dW, (E*)ws.dK1, ws.dg1, a.T, a.H, N, tiles,
-                       (E*)nullptr, (E*)nullptr, (float*)nullptr);
-    LRT_LAUNCH(kKGrad2, (k_grad2<E, C, DK, DV, kGradWaves>), dim3(persistent_grid(tiles, Grad2Lds<E, C, DK, DV>::TOTAL)), dim3(64 * kGradWaves), st, (const E*)a.k,
-                       (const E*)a.v, a.beta, ws.f.G, (const E*)ws.T, (const E*)ws.dW, (const E*)ws.dU, (const E*)ws.dK1,
-                       ws.dg1, (E*)a.dk_out, (E*)a.dv_out, a.dlog_a, a.dbeta, a.T, a.H, N, tiles);
+    LRT_LAUNCH(kKGrad, (k_grad<E, C, DK, DV, kGradWaves, true>),
+               dim3(persistent_grid(tiles, GradLds<E, C, DK, DV, true>::TOTAL)), dim3(64 * kGradWaves), st,
+               (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.d_o, a.beta, ws.f.G, (const E*)ws.f.S,
+               (const E*)ws.dS, (const E*)ws.f.U, (const E*)ws.dU, (const E*)ws.T, (E*)a.dq, (E*)a.dk_out,
+               (E*)a.dv_out, a.dlog_a, a.dbeta, a.T, a.H, N, tiles);
     return hipGetLastError() == hipSuccess ? 0 : -7;
   }
 }
@@ -1112,11 +1038,11 @@ int ssd_bwd_impl(const BwdArgs& a, bool saved) {
                  (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)nullptr, (const E*)dUl, a.dht, a.dh0,
                  (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
     }
-    LRT_LAUNCH(kKGrad1, (k_grad1<E, C, DK, DV, kGradWaves, false>),
-               dim3(persistent_grid(tiles, Grad1Lds<E, C, DK, DV>::TOTAL)), dim3(64 * kGradWaves), st, (const E*)a.q,
-               (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.S, (const E*)ws.dS, (const E*)a.v,
-               (const E*)ws.dU, (E*)a.dq, (E*)nullptr, (E*)nullptr, (float*)nullptr, a.T, a.H, N, tiles,
-               (E*)a.dk_out, (E*)a.dv_out, a.dlog_a);
+    LRT_LAUNCH(kKGrad, (k_grad<E, C, DK, DV, kGradWaves, false>),
+               dim3(persistent_grid(tiles, GradLds<E, C, DK, DV, false>::TOTAL)), dim3(64 * kGradWaves), st,
+               (const E*)a.q, (const E*)a.k, (const E*)nullptr, (const E*)a.d_o, (const float*)nullptr, ws.f.G,
+               (const E*)ws.f.S, (const E*)ws.dS, (const E*)a.v, (const E*)ws.dU, (const E*)nullptr, (E*)a.dq,
+               (E*)a.dk_out, (E*)a.dv_out, a.dlog_a, (float*)nullptr, a.T, a.H, N, tiles);
     return hipGetLastError() == hipSuccess ? 0 : -7;
   }
 }

@@ -48,6 +48,11 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // sees an earlier write once the compiler keeps the two in program order.
 __device__ __forceinline__ void wave_order() { asm volatile("" ::: "memory"); }
 
+// Instruction-scheduling fence: nothing moves across it, so the operand
+// fragments of the products after it are not loaded early into registers
+// (bounds register use where one wave computes several output tiles).
+__device__ __forceinline__ void tile_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Reductions over the tokens of a chunk without atomics, so that repeated
 // runs give bitwise-identical sums: every wave adds its terms into its own
 // slot of NW x C partials (one lane per address per instruction, in program

@@ -105,8 +105,7 @@ enum KernelKind {
   kKOut,
   kKBwdLocal,
   kKDState,
-  kKGrad1,
-  kKGrad2,
+  kKGrad,
   kKKdaPrep,
   kKStateCopy,
   kKFwd,
@@ -133,7 +132,7 @@ void prof_after(void* stream);
 
 // Waves per workgroup of the serial state passes.
 constexpr int kStateWaves = 8;
-// Waves per workgroup of the chunk-parallel gradient kernels.
+// Waves per workgroup of the chunk-parallel gradient kernel.
 constexpr int kGradWaves = 8;
 // Waves per workgroup of the chunk-parallel WY pass.
 constexpr int kWyWaves = 8;
