@@ -34,9 +34,16 @@
  * Supported: B, H >= 1; T >= 0; d_k, d_v in {16, 32, 64, 128};
  * chunk in {16, 32, 64}; B * T and B * H * ceil(T / chunk) * d_v / 16 at
  * most 2^31 - 1; H * max(d_k, d_v) below 2^24.  T need not be a multiple of
- * chunk.  With LRT_F32 the backward entry points and the training forwards
- * (gdn_bwd, ssd_bwd, *_fwd_train, *_bwd_saved) are limited to
- * d_k, d_v <= 64 and chunk <= 32 (LRT_ERR_SHAPE / LRT_ERR_CHUNK otherwise).
+ * chunk.  Every entry point accepts every such size in both dtypes.
+ *
+ * chunk is the tile length of the chunkwise form, an exact rewrite of the
+ * recurrence for every chunk size (only the rounding of the results depends
+ * on it).  The kernels run the requested chunk or, where their fp32
+ * operands would not fit in the 160 KB of LDS of a workgroup, the largest
+ * smaller one that fits: with LRT_F32, kda_fwd at d_k = 128 or d_v = 128
+ * (and at d_k = d_v = 64) runs 32-token chunks, and the backward and
+ * training entry points run 16-token chunks at d_k or d_v = 128 (32 at
+ * d_k = 128, d_v = 64 and the like).  lrt_workspace_bytes accounts for it.
  *
  * Ownership and execution: the caller allocates and frees every buffer,
  * including the workspace (size from lrt_workspace_bytes).  The library never
@@ -111,7 +118,6 @@ int gdn_bwd(const void* q, const void* k, const void* v, const float* log_a, con
  * DeltaNet recurrence of the mixer list under Table 2 of the AMD ROCm blog
  * "Pretraining hybrid LLMs with Primus") -- for gdn_bwd_saved.  The
  * workspace must hold lrt_workspace_bytes(LRT_OP_GDN_BWD, ...) bytes.
- * Shape limits are gdn_bwd's (LRT_F32: d_k, d_v <= 64, chunk <= 32).
  */
 int gdn_fwd_train(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
                   const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk,
@@ -163,7 +169,7 @@ int ssd_bwd(const void* q, const void* k, const void* v, const float* log_a, con
  * Mamba2 / SSD forward for training: ssd_fwd (same arguments, same o and ht)
  * that also leaves each chunk's start state and in-chunk gate cumsums in a
  * workspace of lrt_workspace_bytes(LRT_OP_SSD_BWD, ...) bytes for
- * ssd_bwd_saved.  Shape limits are ssd_bwd's.
+ * ssd_bwd_saved.
  */
 int ssd_fwd_train(const void* q, const void* k, const void* v, const float* log_a, const float* h0,
                   void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk, int dtype,

@@ -29,8 +29,8 @@ LIB_PATH = os.path.join(HERE, "liblrt.so")
 
 LRT_F32, LRT_BF16 = 0, 1
 OP_GDN_FWD, OP_GDN_BWD, OP_KDA_FWD, OP_SSD_FWD, OP_SSD_BWD = 0, 1, 2, 3, 4
-EXPORTS = ("gdn_fwd", "gdn_bwd", "gdn_fwd_train", "gdn_bwd_saved", "kda_fwd", "ssd_fwd", "ssd_bwd",
-           "ssd_fwd_train", "ssd_bwd_saved", "lrt_workspace_bytes", "lrt_status_string",
+EXPORTS = ("gdn_fwd", "gdn_bwd", "gdn_fwd_train", "gdn_bwd_saved", "kda_fwd", "ssd_fwd",
+           "ssd_bwd", "ssd_fwd_train", "ssd_bwd_saved", "lrt_workspace_bytes", "lrt_status_string",
            "lrt_profile_attach", "lrt_profile_count", "lrt_kernel_name")
 
 _lib = None

@@ -3,7 +3,6 @@
 // frees or synchronises.
 #include <stdint.h>
 
-#include "../../include/lrt.h"
 #include "lrt_common.hpp"
 #include "lrt_internal.hpp"
 
@@ -33,9 +32,9 @@ void prof_after(void* stream) {
   ++g_prof.next;
 }
 
-static const char* const kKernelNames[kKNumKinds] = {"k_prep",  "k_state", "k_out",     "k_bwd_local",
-                                                     "k_dstate", "k_grad",   "k_kda_prep",
-                                                     "k_state_copy", "k_fwd", "k_wy", "k_scan", "k_wy_bwd", "k_scan_bwd", "k_scan_local", "k_carry", "k_ssd_prep", "k_ssd_fwd"};
+static const char* const kKernelNames[kKNumKinds] = {
+    "k_bwd_local", "k_dstate",   "k_grad",       "k_kda_prep", "k_state_copy", "k_wy",     "k_scan",
+    "k_wy_bwd",    "k_scan_bwd", "k_scan_local", "k_carry",    "k_ssd_prep",   "k_ssd_fwd"};
 
 // Queried on every call (a device attribute read; nothing is cached between
 // calls).
@@ -70,11 +69,24 @@ static int check_common(int B, int T, int H, int dk, int dv, int chunk, int dtyp
   return LRT_OK;
 }
 
+// The chunk the kernels of `op` run: the requested one, or the largest
+// smaller one at which all of them fit in LDS (fp32 at d_k or d_v = 128).
+// The chunkwise form is exact for every chunk size; only rounding depends
+// on it.  The training forwards run the backward's chunk, so that the saved
+// tensors match the backward's tiles.
+static int run_chunk(int op, int dtype, int dk, int dv, int chunk) {
+  int m = 64;
+  if (op == LRT_OP_GDN_FWD) m = fwd_max_chunk(dtype, dk, dv);
+  if (op == LRT_OP_KDA_FWD) m = kda_max_chunk(dtype, dk, dv);
+  if (op == LRT_OP_GDN_BWD || op == LRT_OP_SSD_BWD) m = bwd_max_chunk(op, dtype, dk, dv);
+  return chunk < m ? chunk : m;
+}
+
 static size_t ws_bytes(int op, int B, int T, int H, int dk, int dv, int chunk, int dtype) {
   const size_t esz = dtype == LRT_BF16 ? 2 : 4;
-  const bool kda = op == LRT_OP_KDA_FWD;
-  size_t b = fwd_ws_layout(B, T, H, dk, dv, chunk, esz, nullptr, kda).bytes;
-  if (op == LRT_OP_GDN_BWD || op == LRT_OP_SSD_BWD) b += bwd_ws_extra(B, T, H, dk, dv, chunk, esz);
+  const int c = run_chunk(op, dtype, dk, dv, chunk);
+  size_t b = fwd_ws_layout(op, B, T, H, dk, dv, c, esz, nullptr).bytes;
+  if (op == LRT_OP_GDN_BWD || op == LRT_OP_SSD_BWD) b += bwd_ws_extra(op, B, T, H, dk, dv, c, esz);
   return b < 256 ? 256 : b;
 }
 
@@ -105,7 +117,8 @@ static int fwd_entry(int variant, const void* q, const void* k, const void* v, c
                        : variant == kVarGDN ? LRT_OP_GDN_FWD : variant == kVarSSD ? LRT_OP_SSD_FWD : LRT_OP_KDA_FWD;
   if (!workspace || workspace_bytes < ws_bytes(op, B, T, H, dk, dv, chunk, dtype)) return LRT_ERR_WORKSPACE;
   if (T == 0) return launch_empty(h0, ht, B, H, dk, dv, stream);
-  FwdArgs a{variant, q, k, v, log_a, beta, h0, o, ht, B, T, H, dk, dv, chunk, dtype, workspace, stream};
+  FwdArgs a{variant, q, k, v, log_a, beta, h0, o, ht, B, T, H, dk, dv, run_chunk(op, dtype, dk, dv, chunk), dtype,
+            workspace, stream};
   rc = train ? fwd_train(a) : variant == kVarKDA ? fwd_kda(a) : fwd_scalar_gate(a);
   return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
 }
@@ -130,7 +143,7 @@ static int bwd_entry(int variant, const void* q, const void* k, const void* v, c
   if (!workspace || workspace_bytes < ws_bytes(op, B, T, H, d_k, d_v, chunk, dtype)) return LRT_ERR_WORKSPACE;
   if (T == 0) return launch_empty(dht, dh0, B, H, d_k, d_v, stream);
   BwdArgs a{q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0,
-            B, T, H, d_k, d_v, chunk, dtype, workspace, stream};
+            B, T, H, d_k, d_v, run_chunk(op, dtype, d_k, d_v, chunk), dtype, workspace, stream};
   rc = delta ? bwd_gdn(a, saved) : bwd_ssd(a, saved);
   return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
 }

@@ -48,9 +48,11 @@ struct BwdWs {
   size_t bytes;
 };
 
-static BwdWs bwd_ws_layout(int B, int T, int H, int dk, int dv, int C, size_t esz, void* base) {
+// op: LRT_OP_GDN_BWD (also the Gated DeltaNet training forward) or
+// LRT_OP_SSD_BWD (also the Mamba2 training forward; no Tinv)
+static BwdWs bwd_ws_layout(int op, int B, int T, int H, int dk, int dv, int C, size_t esz, void* base) {
   BwdWs w;
-  w.f = fwd_ws_layout(B, T, H, dk, dv, C, esz, base);
+  w.f = fwd_ws_layout(op, B, T, H, dk, dv, C, esz, base);
   const size_t tiles = (size_t)B * H * ((size_t)(T + C - 1) / C);
   size_t off = w.f.bytes;
   char* p = (char*)base;
@@ -59,15 +61,15 @@ static BwdWs bwd_ws_layout(int B, int T, int H, int dk, int dv, int C, size_t es
     off += align256(bytes);
     return r;
   };
-  w.T = take(tiles * C * C * esz);
+  w.T = op == LRT_OP_GDN_BWD ? take(tiles * C * C * esz) : nullptr;
   w.dS = take(tiles * dv * dk * esz);
   w.dU = take(tiles * dv * C * esz);
   w.bytes = off;
   return w;
 }
 
-size_t bwd_ws_extra(int B, int T, int H, int dk, int dv, int C, size_t esz) {
-  const BwdWs w = bwd_ws_layout(B, T, H, dk, dv, C, esz, nullptr);
+size_t bwd_ws_extra(int op, int B, int T, int H, int dk, int dv, int C, size_t esz) {
+  const BwdWs w = bwd_ws_layout(op, B, T, H, dk, dv, C, esz, nullptr);
   return w.bytes - w.f.bytes;
 }
 
@@ -152,6 +154,24 @@ __global__ __launch_bounds__(kThreads) void k_bwd_local(const E* __restrict__ q,
     lds_barrier();
   }
 #undef LRT_LOCAL_LOAD
+}
+
+// LDS of k_dstate (its __shared__ arrays below), and the widest column
+// block (at most 64 columns) whose arrays fit.
+template <typename E, int C, int DK, int BV, bool READ_P>
+constexpr size_t dstate_lds() {
+  constexpr size_t P = lds_pad<E>(), LK = DK + P, LC = C + P, LB = BV + P;
+  return (3 * C * LK + C * LB + BV * LC + BV * LK + (READ_P ? C * LC + C * LB : 16)) * sizeof(E) + 3 * C * 4 + 160;
+}
+template <typename E, int C, int DK, int DV, bool READ_P, int cap = 64>
+constexpr int dstate_bv() {
+  constexpr int b0 = DV < cap ? DV : cap;
+  if constexpr (dstate_lds<E, C, DK, b0, READ_P>() <= kLdsMax)
+    return b0;
+  else if constexpr (b0 > 16)
+    return dstate_bv<E, C, DK, DV, READ_P, b0 / 2>();
+  else
+    return 0;
 }
 
 // ---------------------------------------------------------------- k_dstate
@@ -920,6 +940,23 @@ __global__ __launch_bounds__(kThreads) void k_ssd_prep(const E* __restrict__ v, 
 }
 
 // --------------------------------------------------------------- launcher
+// Whether every kernel of the Gated DeltaNet / Mamba2 training step (the
+// training forward, the recompute, the reverse scan and the gradient kernel)
+// fits in LDS at this chunk size.
+template <typename E, int C, int DK, int DV>
+constexpr bool gdn_bwd_fits() {
+  return WyLds<E, C, DK, DV>::TOTAL <= kLdsMax && scan_bv<E, C, DK, DV, kScanFwd, false>() > 0 &&
+         scan_bv<E, C, DK, DV, kScanBwd, false>() > 0 && dstate_bv<E, C, DK, DV, true>() > 0 &&
+         GradLds<E, C, DK, DV, true>::TOTAL <= kLdsMax;
+}
+template <typename E, int C, int DK, int DV>
+constexpr bool ssd_bwd_fits() {
+  return scan_bv<E, C, DK, DV, kScanBwd, false>() > 0 && LocalLds<E, C, DK, DV>::TOTAL <= kLdsMax &&
+         dstate_bv<E, C, DK, DV, true>() > 0 && dstate_bv<E, C, DK, DV, false>() > 0 &&
+         GradLds<E, C, DK, DV, false>::TOTAL <= kLdsMax &&
+         (size_t)DV * (C + lds_pad<E>()) * sizeof(E) <= kLdsMax;
+}
+
 // The forward quantities the gradient kernels read, recomputed: WY factors
 // with T and P (k_wy), then the chunk-start states S_n and U (k_scan,
 // backward mode).
@@ -929,7 +966,7 @@ void bwd_recompute(const BwdWs& ws, const void* q, const void* k, const void* v,
   const int N = (T + C - 1) / C;
   const int tiles = B * H * N;
   hipStream_t st = (hipStream_t)stream;
-  constexpr int BV = DV < 64 ? DV : 64;  // state columns per workgroup
+  constexpr int BV = scan_bv<E, C, DK, DV, kScanBwd, false>();  // state columns per workgroup
   LRT_LAUNCH(kKWyBwd, (k_wy<E, C, DK, DV, true, true, kWyWaves>),
              dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), st, (const E*)q,
              (const E*)k, (const E*)v, log_a, beta, T, H, N, tiles, (E*)ws.f.W, (E*)ws.f.Up, ws.f.G, (E*)ws.f.P,
@@ -958,18 +995,14 @@ void bwd_recompute(const BwdWs& ws, const void* q, const void* k, const void* v,
 // reverse state scan forms dU_local = P^T dO from the stored P.
 template <typename E, int C, int DK, int DV>
 int bwd_impl(const BwdArgs& a, bool saved) {
-  // fp32 gradient tiles need twice the LDS of bf16 ones: the fp32 backward
-  // is limited to d_k, d_v <= 64 and chunk <= 32
-  if constexpr (sizeof(E) == 4 && (DK > 64 || DV > 64)) {
-    return -2;
-  } else if constexpr (sizeof(E) == 4 && C > 32) {
-    return -3;
+  if constexpr (!gdn_bwd_fits<E, C, DK, DV>()) {
+    return -3;  // not reached: the entry point runs a chunk that fits (bwd_max_chunk)
   } else {
     const int N = (a.T + C - 1) / C;
     const int tiles = a.B * a.H * N;
-    const BwdWs ws = bwd_ws_layout(a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
+    const BwdWs ws = bwd_ws_layout(LRT_OP_GDN_BWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
     hipStream_t st = (hipStream_t)a.stream;
-    constexpr int BV = DV < 64 ? DV : 64;  // state columns per workgroup
+    constexpr int BV = dstate_bv<E, C, DK, DV, true>();  // state columns per workgroup
     const int sgrid = a.B * a.H * (DV / BV);
     if (!saved) bwd_recompute<E, C, DK, DV>(ws, a.q, a.k, a.v, a.log_a, a.beta, a.h0, a.B, a.T, a.H, a.stream);
     LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, true, true>), dim3(sgrid), dim3(64 * kStateWaves), st,
@@ -987,56 +1020,54 @@ int bwd_impl(const BwdArgs& a, bool saved) {
 // Mamba2 backward: the Gated DeltaNet pipeline without the WY transform
 // (T = I, W = 0, U = V, no beta): prep (g, V^T), the state recompute
 // (chunk-start states only), dU_local, the reverse state scan (dU = dV) and
-// one gradient kernel writing dq, dk, dv and dlog_a.
-// saved: the workspace holds S_n and g from ssd_fwd_train of the same
-// arguments, so the prep and the state recompute are skipped.
+// the gradient kernel writing dq, dk, dv and dlog_a.
+// saved: the workspace holds S_n, g and P^T from ssd_fwd_train of the same
+// arguments, so the prep, the state recompute and dU_local are skipped (the
+// reverse scan forms dU_local from the stored P^T).
 template <typename E, int C, int DK, int DV>
 int ssd_bwd_impl(const BwdArgs& a, bool saved) {
-  if constexpr (sizeof(E) == 4 && (DK > 64 || DV > 64)) {
-    return -2;
-  } else if constexpr (sizeof(E) == 4 && C > 32) {
-    return -3;
+  if constexpr (!ssd_bwd_fits<E, C, DK, DV>()) {
+    return -3;  // not reached: the entry point runs a chunk that fits (bwd_max_chunk)
   } else {
     const int N = (a.T + C - 1) / C;
     const int tiles = a.B * a.H * N;
-    const BwdWs ws = bwd_ws_layout(a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
+    const BwdWs ws = bwd_ws_layout(LRT_OP_SSD_BWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
     hipStream_t st = (hipStream_t)a.stream;
-    constexpr int BV = DV < 64 ? DV : 64;
-    const int sgrid = a.B * a.H * (DV / BV);
     if (!saved) {
+      constexpr int BVS = scan_bv<E, C, DK, DV, kScanBwd, false>();
       E* Ut = (E*)ws.f.U;  // V^T, the scan's U'^T
       LRT_LAUNCH(kKSsdPrep, (k_ssd_prep<E, C, DV>),
                  dim3(persistent_grid(tiles, (size_t)DV * (C + lds_pad<E>()) * sizeof(E))), dim3(kThreads), st,
                  (const E*)a.v, a.log_a, ws.f.G, Ut, a.T, a.H, N, tiles);
-      {
-        ScanArgs<E> sa{};
-        sa.k = (const E*)a.k;
-        sa.Up = Ut;
-        sa.G = ws.f.G;
-        sa.hin = a.h0;
-        sa.hs_ld = DV;
-        sa.S = (E*)ws.f.S;
-        sa.T = a.T;
-        sa.H = a.H;
-        sa.N = N;
-        sa.L = N;
-        sa.nseg = 1;
-        sa.DV = DV;
-        LRT_LAUNCH(kKScanBwd, (k_scan<E, C, DK, BV, kScanBwd, false, kStateWaves, false>), dim3(sgrid),
-                   dim3(64 * kStateWaves), st, sa);
-      }
+      ScanArgs<E> sa{};
+      sa.k = (const E*)a.k;
+      sa.Up = Ut;
+      sa.G = ws.f.G;
+      sa.hin = a.h0;
+      sa.hs_ld = DV;
+      sa.S = (E*)ws.f.S;
+      sa.T = a.T;
+      sa.H = a.H;
+      sa.N = N;
+      sa.L = N;
+      sa.nseg = 1;
+      sa.DV = DV;
+      LRT_LAUNCH(kKScanBwd, (k_scan<E, C, DK, BVS, kScanBwd, false, kStateWaves, false>), dim3(a.B * a.H * (DV / BVS)),
+                 dim3(64 * kStateWaves), st, sa);
     }
     if (saved) {  // dU_local from the P^T the training forward stored
-      LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, false, true, true>), dim3(sgrid),
+      constexpr int BV = dstate_bv<E, C, DK, DV, true>();
+      LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, false, true, true>), dim3(a.B * a.H * (DV / BV)),
                  dim3(64 * kStateWaves), st, (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)nullptr,
                  (const E*)ws.f.P, a.dht, a.dh0, (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
     } else {
+      constexpr int BV = dstate_bv<E, C, DK, DV, false>();
       E* dUl = (E*)ws.f.Up;
       LRT_LAUNCH(kKBwdLocal, (k_bwd_local<E, C, DK, DV>), dim3(persistent_grid(tiles, LocalLds<E, C, DK, DV>::TOTAL)),
                  dim3(kThreads), st, (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N, tiles);
-      LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, false>), dim3(sgrid), dim3(64 * kStateWaves), st,
-                 (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)nullptr, (const E*)dUl, a.dht, a.dh0,
-                 (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
+      LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, false>), dim3(a.B * a.H * (DV / BV)),
+                 dim3(64 * kStateWaves), st, (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)nullptr,
+                 (const E*)dUl, a.dht, a.dh0, (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
     }
     LRT_LAUNCH(kKGrad, (k_grad<E, C, DK, DV, kGradWaves, false>),
                dim3(persistent_grid(tiles, GradLds<E, C, DK, DV, false>::TOTAL)), dim3(64 * kGradWaves), st,
@@ -1053,80 +1084,95 @@ int ssd_bwd_impl(const BwdArgs& a, bool saved) {
 // the recompute and forms dU_local from the stored P.
 template <typename E, int C, int DK, int DV>
 int fwd_train_impl(const FwdArgs& a) {
-  if constexpr (sizeof(E) == 4 && (DK > 64 || DV > 64)) {
-    return -2;
-  } else if constexpr (sizeof(E) == 4 && C > 32) {
-    return -3;
+  if constexpr (!gdn_bwd_fits<E, C, DK, DV>()) {
+    return -3;  // not reached: the entry point runs a chunk that fits (bwd_max_chunk)
   } else {
-    const BwdWs ws = bwd_ws_layout(a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
-    constexpr int BV64 = DV < 64 ? DV : 64;
-    if constexpr (WyLds<E, C, DK, DV>::TOTAL <= 160 * 1024 &&
-                  ScanLds<E, C, DK, BV64, kScanFwd, false>::TOTAL <= 160 * 1024) {
-      const int N = (a.T + C - 1) / C;
-      const int tiles = a.B * a.H * N;
-      LRT_LAUNCH(kKWy, (k_wy<E, C, DK, DV, true, true, kWyWaves>),
-                 dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), a.stream,
-                 (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.f.W,
-                 (E*)ws.f.Up, ws.f.G, (E*)ws.f.P, (E*)ws.T);
-      if (hipGetLastError() != hipSuccess) return -7;
-      return launch_scan_fwd<E, C, DK, DV, false, true>(a, ws.f, N);
-    } else {
-      // the WY pass or the forward scan does not fit in LDS at this size (no
-      // size the backward supports)
-      return -2;
-    }
+    const BwdWs ws = bwd_ws_layout(LRT_OP_GDN_BWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
+    const int N = (a.T + C - 1) / C;
+    const int tiles = a.B * a.H * N;
+    LRT_LAUNCH(kKWy, (k_wy<E, C, DK, DV, true, true, kWyWaves>),
+               dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), a.stream,
+               (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.f.W,
+               (E*)ws.f.Up, ws.f.G, (E*)ws.f.P, (E*)ws.T);
+    if (hipGetLastError() != hipSuccess) return -7;
+    return launch_scan_fwd<E, C, DK, DV, false, true>(a, ws.f, N);
   }
 }
 
-// Mamba2 forward for training: ssd_fwd's kernel also writing S_n and g into
-// the backward's workspace for ssd_bwd_saved.
+// Mamba2 forward for training: ssd_fwd's kernel also writing S_n, g and P^T
+// into the backward's workspace for ssd_bwd_saved.
 template <typename E, int C, int DK, int DV>
 int fwd_ssd_train_impl(const FwdArgs& a) {
-  if constexpr (sizeof(E) == 4 && (DK > 64 || DV > 64)) {
-    return -2;
-  } else if constexpr (sizeof(E) == 4 && C > 32) {
-    return -3;
+  if constexpr (!ssd_bwd_fits<E, C, DK, DV>()) {
+    return -3;  // not reached: the entry point runs a chunk that fits (bwd_max_chunk)
   } else {
-    const BwdWs ws = bwd_ws_layout(a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
+    const BwdWs ws = bwd_ws_layout(LRT_OP_SSD_BWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
     return launch_ssd_fwd<E, C, DK, DV, true>(a, (E*)ws.f.S, ws.f.G, (E*)ws.f.P);
   }
 }
 
+template <typename E, int DK, int DV>
+constexpr int gdn_bwd_max_chunk_t() {
+  return gdn_bwd_fits<E, 64, DK, DV>() ? 64 : gdn_bwd_fits<E, 32, DK, DV>() ? 32 : 16;
+}
+template <typename E, int DK, int DV>
+constexpr int ssd_bwd_max_chunk_t() {
+  return ssd_bwd_fits<E, 64, DK, DV>() ? 64 : ssd_bwd_fits<E, 32, DK, DV>() ? 32 : 16;
+}
+
+#define LRT_DV(DK_) LRT_CASE(DK_, 16) LRT_CASE(DK_, 32) LRT_CASE(DK_, 64) LRT_CASE(DK_, 128)
+#define LRT_DK LRT_DV(16) LRT_DV(32) LRT_DV(64) LRT_DV(128)
+
+int bwd_max_chunk(int op, int dtype, int dk, int dv) {
+  const bool ssd = op == LRT_OP_SSD_BWD;
+#define LRT_CASE(DK_, DV_)                                                                                     \
+  if (dk == DK_ && dv == DV_) {                                                                                \
+    if (dtype == LRT_BF16) return ssd ? ssd_bwd_max_chunk_t<bf16, DK_, DV_>() : gdn_bwd_max_chunk_t<bf16, DK_, DV_>(); \
+    return ssd ? ssd_bwd_max_chunk_t<float, DK_, DV_>() : gdn_bwd_max_chunk_t<float, DK_, DV_>();              \
+  }
+  LRT_DK
+#undef LRT_CASE
+  return 16;
+}
+
 template <typename E>
 static int fwd_train_dtype(const FwdArgs& a) {
-#define LRT_CASE(C_, DK_, DV_)                                                             \
-  if (a.chunk == C_ && a.dk == DK_ && a.dv == DV_)                                         \
-    return a.variant == kVarSSD ? fwd_ssd_train_impl<E, C_, DK_, DV_>(a) : fwd_train_impl<E, C_, DK_, DV_>(a);
-#define LRT_DV(C_, DK_) LRT_CASE(C_, DK_, 16) LRT_CASE(C_, DK_, 32) LRT_CASE(C_, DK_, 64) LRT_CASE(C_, DK_, 128)
-#define LRT_DK(C_) LRT_DV(C_, 16) LRT_DV(C_, 32) LRT_DV(C_, 64) LRT_DV(C_, 128)
-  LRT_DK(16) LRT_DK(32) LRT_DK(64)
-#undef LRT_DK
-#undef LRT_DV
+#define LRT_CASE(DK_, DV_)                                                                           \
+  if (a.dk == DK_ && a.dv == DV_) {                                                                  \
+    if (a.chunk == 16)                                                                               \
+      return a.variant == kVarSSD ? fwd_ssd_train_impl<E, 16, DK_, DV_>(a) : fwd_train_impl<E, 16, DK_, DV_>(a); \
+    if (a.chunk == 32)                                                                               \
+      return a.variant == kVarSSD ? fwd_ssd_train_impl<E, 32, DK_, DV_>(a) : fwd_train_impl<E, 32, DK_, DV_>(a); \
+    if (a.chunk == 64)                                                                               \
+      return a.variant == kVarSSD ? fwd_ssd_train_impl<E, 64, DK_, DV_>(a) : fwd_train_impl<E, 64, DK_, DV_>(a); \
+  }
+  LRT_DK
 #undef LRT_CASE
   return -2;
 }
 
-int fwd_train(const FwdArgs& a) { return a.dtype == 1 ? fwd_train_dtype<bf16>(a) : fwd_train_dtype<float>(a); }
+int fwd_train(const FwdArgs& a) { return a.dtype == LRT_BF16 ? fwd_train_dtype<bf16>(a) : fwd_train_dtype<float>(a); }
 
 template <typename E, bool SSD>
 static int bwd_dtype(const BwdArgs& a, bool saved) {
-#define LRT_CASE(C_, DK_, DV_)                     \
-  if (a.chunk == C_ && a.dk == DK_ && a.dv == DV_) \
-    return SSD ? ssd_bwd_impl<E, C_, DK_, DV_>(a, saved) : bwd_impl<E, C_, DK_, DV_>(a, saved);
-#define LRT_DV(C_, DK_) LRT_CASE(C_, DK_, 16) LRT_CASE(C_, DK_, 32) LRT_CASE(C_, DK_, 64) LRT_CASE(C_, DK_, 128)
-#define LRT_DK(C_) LRT_DV(C_, 16) LRT_DV(C_, 32) LRT_DV(C_, 64) LRT_DV(C_, 128)
-  LRT_DK(16) LRT_DK(32) LRT_DK(64)
-#undef LRT_DK
-#undef LRT_DV
+#define LRT_CASE(DK_, DV_)                                                                                   \
+  if (a.dk == DK_ && a.dv == DV_) {                                                                          \
+    if (a.chunk == 16) return SSD ? ssd_bwd_impl<E, 16, DK_, DV_>(a, saved) : bwd_impl<E, 16, DK_, DV_>(a, saved); \
+    if (a.chunk == 32) return SSD ? ssd_bwd_impl<E, 32, DK_, DV_>(a, saved) : bwd_impl<E, 32, DK_, DV_>(a, saved); \
+    if (a.chunk == 64) return SSD ? ssd_bwd_impl<E, 64, DK_, DV_>(a, saved) : bwd_impl<E, 64, DK_, DV_>(a, saved); \
+  }
+  LRT_DK
 #undef LRT_CASE
   return -2;
 }
+#undef LRT_DK
+#undef LRT_DV
 
 int bwd_gdn(const BwdArgs& a, bool saved) {
-  return a.dtype == 1 ? bwd_dtype<bf16, false>(a, saved) : bwd_dtype<float, false>(a, saved);
+  return a.dtype == LRT_BF16 ? bwd_dtype<bf16, false>(a, saved) : bwd_dtype<float, false>(a, saved);
 }
 int bwd_ssd(const BwdArgs& a, bool saved) {
-  return a.dtype == 1 ? bwd_dtype<bf16, true>(a, saved) : bwd_dtype<float, true>(a, saved);
+  return a.dtype == LRT_BF16 ? bwd_dtype<bf16, true>(a, saved) : bwd_dtype<float, true>(a, saved);
 }
 
 }  // namespace lrt

@@ -3,7 +3,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/lrt.h"
+
 namespace lrt {
+
+// LDS of one workgroup on gfx950.
+constexpr size_t kLdsMax = 160 * 1024;
 
 enum { kVarGDN = 0, kVarSSD = 1, kVarKDA = 2 };
 
@@ -32,18 +37,21 @@ struct BwdArgs {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Per-chunk workspace tiles of the forward, chunk-major per (b, h):
-//   W   [C][dk]   E   W = Tinv diag(b gamma) K           (delta variants)
-//   Up  [dv][C]   E   U'^T = (Tinv diag(b) V)^T          (SSD: V^T)
-//   Kt  [dk][C]   E   Ktil^T, Ktil_j = e^(g_C - g_j) k_j
-//   U   [dv][C]   E   U^T = (U' - W Hn)^T
-//   S   [dv][dk]  E   S_n = Hn^T, the state at the chunk start
-//   G   [C]       f32 within-chunk inclusive cumsum of log a
-//   GC  [dk]      f32 per-key-dim chunk log-decay (KDA)
-//   Qg  [C][dk]   E   Q o e^G (KDA)
-//   P   [C][C]    E   intra-chunk attention matrix (Q K^T) o Gamma
+// Per-chunk workspace tiles, chunk-major per (b, h); each op reserves only
+// the tiles its kernels use (lrt_workspace_bytes op codes):
+//   W   [C][dk]   E   W = Tinv diag(b gamma) K           GDN_FWD, KDA_FWD, GDN_BWD
+//   Up  [dv][C]   E   U' = Tinv diag(b) V (tile order)   GDN_FWD, KDA_FWD, GDN_BWD; SSD_BWD: dU_local^T
+//   Kt  [dk][C]   E   Ktil^T, Ktil_j = e^(G_C - G_j) k_j KDA_FWD
+//   U   [dv][C]   E   U^T = (U' - W Hn)^T                GDN_BWD; SSD_BWD: V^T
+//   S   [dv][dk]  E   S_n = Hn^T, the chunk-start state  GDN_BWD, SSD_BWD
+//   G   [C]       f32 within-chunk inclusive cumsum of log a   GDN_FWD, GDN_BWD, SSD_BWD
+//   GC  [dk]      f32 per-key-dim chunk log-decay        KDA_FWD
+//   Qg  [C][dk]   E   Q o e^G                            KDA_FWD
+//   P   [C][C]    E   (Q K^T) o Gamma (SSD_BWD: P^T)     GDN_FWD, KDA_FWD, GDN_BWD, SSD_BWD
 //   SegLoc   [b*h][seg][dk][dv+dk] f32  end state of each segment from zero, and its map
 //   SegStart [b*h][seg][dk][dv]    f32  true start state of each segment
+//                                       (segmented scans: GDN_FWD, KDA_FWD, GDN_BWD)
+// The backward's own tiles (T, dS, dU) follow (bwd_ws_layout).
 struct FwdWs {
   void *W, *Up, *Kt, *U, *S, *Qg, *P;
   float *G, *GC, *SegLoc, *SegStart;
@@ -55,7 +63,9 @@ struct FwdWs {
 // would leave the device mostly idle; then 128-column blocks (when d_k is a
 // multiple, for the identity columns of the local pass) and enough segments
 // for about 512 workgroups, each at least 16 chunks long.  Depends on the
-// shape only, so the workspace size does not depend on the device.
+// shape only, so the workspace size does not depend on the device.  (The
+// scan may run narrower column blocks where its operands need more LDS; the
+// segments stay as planned.)
 struct ScanPlan {
   int bv, nseg;
 };
@@ -71,44 +81,43 @@ inline ScanPlan scan_plan(int B, int H, int DK, int DV, int N) {
   return {bv, ns < 1 ? 1 : (int)ns};
 }
 
-inline FwdWs fwd_ws_layout(int B, int T, int H, int dk, int dv, int C, size_t esz, void* base, bool kda = false) {
+inline FwdWs fwd_ws_layout(int op, int B, int T, int H, int dk, int dv, int C, size_t esz, void* base) {
   const size_t N = (size_t)(T + C - 1) / C;
   const size_t tiles = (size_t)B * H * N;
+  const bool gf = op == LRT_OP_GDN_FWD, kf = op == LRT_OP_KDA_FWD, gb = op == LRT_OP_GDN_BWD,
+             sb = op == LRT_OP_SSD_BWD;
   size_t off = 0;
   FwdWs w;
   char* p = (char*)base;
-  auto take = [&](size_t bytes) {
+  auto take = [&](bool need, size_t bytes) {
+    if (!need) return (void*)nullptr;
     void* r = p ? (void*)(p + off) : nullptr;
     off += align256(bytes);
     return r;
   };
-  w.W = take(tiles * C * dk * esz);
-  w.Up = take(tiles * dv * C * esz);
-  w.Kt = take(tiles * dk * C * esz);
-  w.U = take(tiles * dv * C * esz);
-  w.S = take(tiles * dv * dk * esz);
-  w.G = (float*)take(tiles * C * sizeof(float));
-  w.GC = kda ? (float*)take(tiles * dk * sizeof(float)) : nullptr;
-  w.Qg = kda ? take(tiles * C * dk * esz) : nullptr;
-  w.P = take(tiles * C * C * esz);
-  const int nseg = scan_plan(B, H, dk, dv, (int)N).nseg;
-  w.SegLoc = nseg > 1 ? (float*)take((size_t)B * H * nseg * dk * (dv + dk) * sizeof(float)) : nullptr;
-  w.SegStart = nseg > 1 ? (float*)take((size_t)B * H * nseg * dk * dv * sizeof(float)) : nullptr;
+  w.W = take(gf || kf || gb, tiles * C * dk * esz);
+  w.Up = take(gf || kf || gb || sb, tiles * dv * C * esz);
+  w.Kt = take(kf, tiles * dk * C * esz);
+  w.U = take(gb || sb, tiles * dv * C * esz);
+  w.S = take(gb || sb, tiles * dv * dk * esz);
+  w.G = (float*)take(gf || gb || sb, tiles * C * sizeof(float));
+  w.GC = (float*)take(kf, tiles * dk * sizeof(float));
+  w.Qg = take(kf, tiles * C * dk * esz);
+  w.P = take(gf || kf || gb || sb, tiles * C * C * esz);
+  const int nseg = (gf || kf || gb) ? scan_plan(B, H, dk, dv, (int)N).nseg : 1;
+  w.SegLoc = (float*)take(nseg > 1, (size_t)B * H * nseg * dk * (dv + dk) * sizeof(float));
+  w.SegStart = (float*)take(nseg > 1, (size_t)B * H * nseg * dk * dv * sizeof(float));
   w.bytes = off;
   return w;
 }
 
 // Kernel ids reported by the benchmark timing hook (lrt_profile_attach).
 enum KernelKind {
-  kKPrep = 0,
-  kKState,
-  kKOut,
-  kKBwdLocal,
+  kKBwdLocal = 0,
   kKDState,
   kKGrad,
   kKKdaPrep,
   kKStateCopy,
-  kKFwd,
   kKWy,
   kKScan,
   kKWyBwd,
@@ -155,6 +164,15 @@ int bwd_gdn(const BwdArgs& a, bool saved);
 int fwd_train(const FwdArgs& a);  // GDN or SSD by a.variant
 int bwd_ssd(const BwdArgs& a, bool saved);
 // workspace bytes the backward needs beyond the forward's tiles
-size_t bwd_ws_extra(int B, int T, int H, int dk, int dv, int C, size_t esz);
+size_t bwd_ws_extra(int op, int B, int T, int H, int dk, int dv, int C, size_t esz);
+
+// The largest chunk in {16, 32, 64} at which every kernel of `op` (an
+// LRT_OP_* code; the training forwards count as the backward's op) fits in
+// LDS for this dtype and d_k, d_v.  The kernels run min(requested chunk,
+// this); the chunkwise form is exact for every chunk size, so only the
+// rounding of the result depends on it.
+int fwd_max_chunk(int dtype, int dk, int dv);  // GDN_FWD, SSD_FWD
+int kda_max_chunk(int dtype, int dk, int dv);
+int bwd_max_chunk(int op, int dtype, int dk, int dv);  // GDN_BWD, SSD_BWD
 
 }  // namespace lrt

@@ -19,9 +19,8 @@
 // for any finite log a <= 0.
 //
 // k_kda_prep (persistent over the chunks) writes W, U'^T, Ktil^T, Q o e^G, P and
-// the per-dimension chunk decay; the generic state pass (per-dimension decay)
-// and output kernel (operands from the workspace) then finish the chunk.
-#include "lrt_fwd_kernels.hpp"
+// the per-dimension chunk decay; the serial scan in KDA mode (per-dimension
+// decay, operands from the workspace) then carries the state and forms o.
 #include "lrt_internal.hpp"
 #include "lrt_scan.hpp"
 
@@ -387,13 +386,18 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
 }
 
 template <typename E, int C, int DK, int DV>
+constexpr bool kda_fits() {
+  return KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL <= kLdsMax && scan_bv<E, C, DK, DV, kScanFwd, true>() > 0;
+}
+
+template <typename E, int C, int DK, int DV>
 int kda_impl(const FwdArgs& a) {
-  if constexpr (KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL > 160 * 1024) {
-    return -2;  // fp32 operands at d_k = 128 do not fit in LDS
+  if constexpr (!kda_fits<E, C, DK, DV>()) {
+    return -3;  // not reached: the entry point runs a chunk that fits (kda_max_chunk)
   } else {
     const int N = (a.T + C - 1) / C;
     const int tiles = a.B * a.H * N;
-    const FwdWs ws = fwd_ws_layout(a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace, true);
+    const FwdWs ws = fwd_ws_layout(LRT_OP_KDA_FWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
     hipStream_t st = (hipStream_t)a.stream;
     LRT_LAUNCH(kKKdaPrep, (k_kda_prep<E, C, DK, DV, kWyWaves>),
                dim3(persistent_grid(tiles, KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL)), dim3(64 * kWyWaves), st,
@@ -404,19 +408,37 @@ int kda_impl(const FwdArgs& a) {
   }
 }
 
+template <typename E, int DK, int DV>
+constexpr int kda_max_chunk_t() {
+  return kda_fits<E, 64, DK, DV>() ? 64 : kda_fits<E, 32, DK, DV>() ? 32 : 16;
+}
+
+#define LRT_DV(DK_) LRT_CASE(DK_, 16) LRT_CASE(DK_, 32) LRT_CASE(DK_, 64) LRT_CASE(DK_, 128)
+#define LRT_DK LRT_DV(16) LRT_DV(32) LRT_DV(64) LRT_DV(128)
+
+int kda_max_chunk(int dtype, int dk, int dv) {
+#define LRT_CASE(DK_, DV_) \
+  if (dk == DK_ && dv == DV_) return dtype == LRT_BF16 ? kda_max_chunk_t<bf16, DK_, DV_>() : kda_max_chunk_t<float, DK_, DV_>();
+  LRT_DK
+#undef LRT_CASE
+  return 16;
+}
+
 template <typename E>
 static int kda_dtype(const FwdArgs& a) {
-#define LRT_CASE(C_, DK_, DV_) \
-  if (a.chunk == C_ && a.dk == DK_ && a.dv == DV_) return kda_impl<E, C_, DK_, DV_>(a);
-#define LRT_DV(C_, DK_) LRT_CASE(C_, DK_, 16) LRT_CASE(C_, DK_, 32) LRT_CASE(C_, DK_, 64) LRT_CASE(C_, DK_, 128)
-#define LRT_DK(C_) LRT_DV(C_, 16) LRT_DV(C_, 32) LRT_DV(C_, 64) LRT_DV(C_, 128)
-  LRT_DK(16) LRT_DK(32) LRT_DK(64)
-#undef LRT_DK
-#undef LRT_DV
+#define LRT_CASE(DK_, DV_)                                   \
+  if (a.dk == DK_ && a.dv == DV_) {                          \
+    if (a.chunk == 16) return kda_impl<E, 16, DK_, DV_>(a);  \
+    if (a.chunk == 32) return kda_impl<E, 32, DK_, DV_>(a);  \
+    if (a.chunk == 64) return kda_impl<E, 64, DK_, DV_>(a);  \
+  }
+  LRT_DK
 #undef LRT_CASE
   return -2;
 }
+#undef LRT_DK
+#undef LRT_DV
 
-int fwd_kda(const FwdArgs& a) { return a.dtype == 1 ? kda_dtype<bf16>(a) : kda_dtype<float>(a); }
+int fwd_kda(const FwdArgs& a) { return a.dtype == LRT_BF16 ? kda_dtype<bf16>(a) : kda_dtype<float>(a); }
 
 }  // namespace lrt

@@ -597,15 +597,29 @@ int launch_scan_fwd_bv(const FwdArgs& a, const FwdWs& ws, int N, int nseg) {
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
+// The widest column block (at most `cap` columns, at least 16) whose
+// operands of scan mode MODE fit in LDS; 0 if none does.
+template <typename E, int C, int DK, int DV, int MODE, bool KDA, int cap = 64>
+constexpr int scan_bv() {
+  constexpr int b0 = DV < cap ? DV : cap;
+  if constexpr (ScanLds<E, C, DK, b0, MODE, KDA>::TOTAL <= kLdsMax && CarryLds<E, DK, b0>::TOTAL <= kLdsMax)
+    return b0;
+  else if constexpr (b0 > 16)
+    return scan_bv<E, C, DK, DV, MODE, KDA, b0 / 2>();
+  else
+    return 0;
+}
+
 template <typename E, int C, int DK, int DV, bool KDA, bool SAVE = false>
 int launch_scan_fwd(const FwdArgs& a, const FwdWs& ws, int N) {
-  constexpr int BV64 = DV < 64 ? DV : 64;
-  constexpr int BV128 = DV < 128 ? DV : 128;
+  constexpr int BV64 = scan_bv<E, C, DK, DV, kScanFwd, KDA, 64>();
+  constexpr int BV128 = scan_bv<E, C, DK, DV, kScanFwd, KDA, 128>();
+  static_assert(BV64 > 0, "no column block of the forward scan fits in LDS");
   const ScanPlan pl = scan_plan(a.B, a.H, DK, DV, N);
-  if constexpr (BV128 != BV64 && DK % BV128 == 0 && ScanLds<E, C, DK, BV128, kScanFwd, KDA>::TOTAL <= 160 * 1024) {
-    if (pl.bv == BV128) return launch_scan_fwd_bv<E, C, DK, DV, BV128, KDA, SAVE>(a, ws, N, pl.nseg);
+  if constexpr (BV128 > BV64) {
+    if (pl.bv > 64) return launch_scan_fwd_bv<E, C, DK, DV, BV128, KDA, SAVE>(a, ws, N, pl.nseg);
   }
-  return launch_scan_fwd_bv<E, C, DK, DV, BV64, KDA, SAVE>(a, ws, N, pl.bv == BV64 ? pl.nseg : 1);
+  return launch_scan_fwd_bv<E, C, DK, DV, BV64, KDA, SAVE>(a, ws, N, pl.nseg);
 }
 
 }  // namespace lrt

@@ -129,10 +129,13 @@ def test_training_pair_validation(L):
         a = list(args)
         a[i] = None
         assert lib.gdn_fwd_train(*a) == c["LRT_ERR_NULL"], i
-    # the fp32 backward's size limits apply to the training forward too
+    # fp32 at d_k = d_v = 128 is accepted (the kernels run a chunk that fits
+    # in LDS); a too-small workspace is still rejected before any launch
+    need128 = L.workspace_bytes(L.OP_GDN_BWD, 1, 64, 2, 128, 128, 64, 0)
+    assert 0 < need128 < (1 << 40)
     a = list(args)
-    a[11], a[12], a[16] = 128, 128, 1 << 40  # rejected before any launch
-    assert lib.gdn_fwd_train(*a) == c["LRT_ERR_SHAPE"]
+    a[11], a[12], a[13], a[16] = 128, 128, 64, need128 - 1
+    assert lib.gdn_fwd_train(*a) == c["LRT_ERR_WORKSPACE"]
     base = [F, F, F, F, F, None, F, None, F, F, F, F, F, None, 1, 64, 2, 16, 16, 16, 0, None, 0, None]
     assert lib.gdn_bwd_saved(*base) == c["LRT_ERR_WORKSPACE"]
     for i in (0, 1, 2, 3, 4, 6, 8, 9, 10, 11, 12):
@@ -155,9 +158,11 @@ def test_ssd_training_pair_validation(L):
         a = list(args)
         a[i] = None
         assert lib.ssd_fwd_train(*a) == c["LRT_ERR_NULL"], i
+    # fp32 at d = 128 is accepted; a too-small workspace is rejected before any launch
+    need128 = L.workspace_bytes(L.OP_SSD_BWD, 1, 64, 2, 128, 128, 64, 0)
     a = list(args)
-    a[10], a[11], a[15] = 128, 128, 1 << 40  # fp32 beyond the backward's limits: rejected before any launch
-    assert lib.ssd_fwd_train(*a) == c["LRT_ERR_SHAPE"]
+    a[10], a[11], a[12], a[15] = 128, 128, 64, need128 - 1
+    assert lib.ssd_fwd_train(*a) == c["LRT_ERR_WORKSPACE"]
     base = [F, F, F, F, None, F, None, F, F, F, F, None, 1, 64, 2, 16, 16, 16, 0, None, 0, None]
     assert lib.ssd_bwd_saved(*base) == c["LRT_ERR_WORKSPACE"]
     for i in (0, 1, 2, 3, 5, 7, 8, 9, 10):
@@ -210,6 +215,16 @@ def test_workspace_bytes(L):
     assert L.workspace_bytes(0, 1, 4096, 1, 16, 16, 16, 0) > L.workspace_bytes(0, 1, 64, 1, 16, 16, 16, 0)
     # the backward needs more than the forward
     assert L.workspace_bytes(1, 2, 256, 2, 64, 64, 64, 1) > L.workspace_bytes(0, 2, 256, 2, 64, 64, 64, 1)
+    # the fused Mamba2 forward needs none beyond the minimum
+    assert L.workspace_bytes(3, 16, 2048, 8, 128, 128, 64, 1) == 256
+    # every dtype and size of the supported set has a workspace (fp32 at
+    # d = 128 runs a smaller chunk: its workspace is sized for that chunk)
+    for op in range(5):
+        for dt in (0, 1):
+            for dk in (16, 32, 64, 128):
+                for dv in (16, 32, 64, 128):
+                    for ch in (16, 32, 64):
+                        assert 0 < L.workspace_bytes(op, 2, 100, 2, dk, dv, ch, dt) < (1 << 40)
 
 
 def test_python_binding_rejects_cpu_tensors(L):

@@ -70,6 +70,11 @@ CASES = [
     ("bf16_dk32_dv128", 1, 100, 2, 32, 128, 32, torch.bfloat16, -6.0, 0.1, 0.1),
     # long sequence, slow gates: the state carry spans 64 chunks both ways
     ("bf16_long_slow_C64", 1, 4096 - 7, 2, 128, 128, 64, torch.bfloat16, -6.0, 0.1, 0.1),
+    # fp32 at d = 128 with chunk 64 requested (the kernels run 16-token chunks,
+    # the largest whose fp32 operands fit in LDS), and at d = 64, chunk 64
+    ("fp32_d128_C64", 1, 150, 2, 128, 128, 64, torch.float32, -6.0, 0.1, 0.1),
+    ("fp32_dk128_dv64_C64", 1, 100, 2, 128, 64, 64, torch.float32, -2.0, 0.1, 0.1),
+    ("fp32_d64_C64", 2, 130, 2, 64, 64, 64, torch.float32, -6.0, 0.1, 0.1),
 ]
 
 
@@ -91,7 +96,7 @@ def test_bwd_training_step_workload():
 
 
 SAVED_CASES = ["fp32_tiny_cfg", "fp32_slow_h0_dht", "bf16_slow_T61_C16", "bf16_slow_C32", "bf16_slow_C64",
-               "bf16_d16_dv32", "bf16_long_slow_C64"]
+               "bf16_d16_dv32", "bf16_long_slow_C64", "fp32_d128_C64", "fp32_d64_C64"]
 
 
 @pytest.mark.parametrize("name", SAVED_CASES)
@@ -161,6 +166,7 @@ SSD_CASES = [
     ("bf16_default_gates_C64", 2, 256, 2, 128, 128, 64, torch.bfloat16, 0.0, 0.0, 0.0),
     ("bf16_dk32_dv128", 1, 100, 2, 32, 128, 32, torch.bfloat16, -6.0, 0.1, 0.1),
     ("bf16_long_slow_C64", 1, 4096 - 7, 2, 128, 128, 64, torch.bfloat16, -6.0, 0.1, 0.1),
+    ("fp32_d128_C64", 1, 150, 2, 128, 128, 64, torch.float32, -6.0, 0.1, 0.1),
 ]
 
 
@@ -183,7 +189,7 @@ def test_ssd_bwd_workload_shape():
 
 
 SSD_SAVED_CASES = ["fp32_tiny", "fp32_slow_h0_dht_T77_C32", "bf16_slow_T61_C16", "bf16_slow_C64_T300",
-                   "bf16_dk32_dv128", "bf16_long_slow_C64"]
+                   "bf16_dk32_dv128", "bf16_long_slow_C64", "fp32_d128_C64"]
 
 
 @pytest.mark.parametrize("name", SSD_SAVED_CASES)
@@ -241,14 +247,3 @@ def test_ssd_fwd_train_and_bwd_saved_workload():
     say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     bad = {n: e for n, e in errs.items() if e > TOL[torch.bfloat16]}
     assert not bad, bad
-
-
-def test_bwd_rejects_unsupported_fp32_sizes():
-    import linear_recurrent_token_amd as L
-    inp = synth.make_inputs("gdn_fwd_bwd", 1, 64, 1, 128, 128, dtype=torch.float32, device="cuda")
-    with pytest.raises(L.LrtError) as e:
-        L.gdn_bwd(inp["q"], inp["k"], inp["v"], inp["log_a"], inp["beta"], None, inp["do"], chunk=16)
-    assert e.value.status == -2
-    with pytest.raises(L.LrtError) as e:
-        L.ssd_bwd(inp["q"], inp["k"], inp["v"], inp["log_a"], None, inp["do"], chunk=16)
-    assert e.value.status == -2

@@ -63,6 +63,8 @@ CASES = [
     ("gdn_fp32_tiny_cfg", "gdn", 1, 64, 2, 16, 16, 16, torch.float32, 0.0, 0.0),
     ("gdn_fp32_slow_h0", "gdn", 2, 150, 2, 32, 64, 32, torch.float32, -6.0, 0.1),
     ("gdn_fp32_d128", "gdn", 1, 130, 2, 128, 128, 64, torch.float32, -6.0, 0.1),
+    ("gdn_fp32_dk64_dv128_C64", "gdn", 2, 100, 2, 64, 128, 64, torch.float32, -2.0, 0.1),
+    ("ssd_fp32_d128_C64", "ssd", 1, 130, 2, 128, 128, 64, torch.float32, -6.0, 0.1),
     ("gdn_bf16_slow_T61_C16", "gdn", 2, 61, 3, 64, 64, 16, torch.bfloat16, -6.0, 0.1),
     ("gdn_bf16_slow_C32", "gdn", 2, 200, 2, 128, 128, 32, torch.bfloat16, -6.0, 0.1),
     ("gdn_bf16_slow_C64", "gdn", 2, 300, 2, 128, 128, 64, torch.bfloat16, -6.0, 0.1),
@@ -149,6 +151,9 @@ KDA_CASES = [
     ("kda_bf16_perdim_fast_C32", 1, 130, 2, 128, 128, 32, torch.bfloat16, "perdim", 2.0, 0.1),
     ("kda_bf16_slow_T61_C16", 2, 61, 2, 64, 32, 16, torch.bfloat16, "perdim", -6.0, 0.1),
     ("kda_bf16_lowrank_C64", 1, 256, 4, 128, 128, 64, torch.bfloat16, "lowrank", 0.0, 0.0),
+    # fp32 at d = 128, chunk 64 requested (the kernels run 32-token chunks)
+    ("kda_fp32_d128_C64", 1, 150, 2, 128, 128, 64, torch.float32, "perdim", -2.0, 0.1),
+    ("kda_fp32_d64_C64", 1, 150, 2, 64, 64, 64, torch.float32, "perdim", 0.0, 0.1),
 ]
 
 
