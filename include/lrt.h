@@ -78,6 +78,7 @@ extern "C" {
 #define LRT_ERR_ALIGN (-6)     /* a pointer is under-aligned (see Ownership) */
 #define LRT_ERR_LAUNCH (-7)    /* the HIP runtime rejected a launch */
 #define LRT_ERR_OP (-8)        /* unknown op code */
+#define LRT_ERR_TOO_LARGE (-9) /* gdn_fwd_noalloc: the sizes need more than LRT_NOALLOC_MAX_BYTES */
 
 /* dtypes of q, k, v, o, do and the q/k/v gradients */
 #define LRT_F32 0
@@ -135,6 +136,24 @@ int gdn_bwd_saved(const void* q, const void* k, const void* v, const float* log_
                   const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv,
                   float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v,
                   int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_fwd for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same arguments,
+ * outputs and kernels, without the workspace arguments.  The workspace is a
+ * static device array of LRT_NOALLOC_MAX_BYTES (64 MiB) inside the library,
+ * one per GPU, held until the process ends; its device address is looked up
+ * on the first call on each device.  Sizes whose workspace
+ * (lrt_workspace_bytes(LRT_OP_GDN_FWD, ...)) exceeds it are rejected with
+ * LRT_ERR_TOO_LARGE before anything is enqueued; other errors as gdn_fwd.
+ * Every call on a GPU uses that GPU's one array: calls that overlap on one
+ * GPU (other streams, other threads) race and give undefined results.
+ * Nothing is allocated, freed or synchronised.
+ */
+#define LRT_NOALLOC_MAX_BYTES (64u << 20)
+int gdn_fwd_noalloc(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                    const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk,
+                    int dtype, void* stream);
 
 /*
  * Kimi Delta Attention forward: as gdn_fwd, with log_a of shape [B, T, H, d_k]

@@ -11,6 +11,7 @@ Entry points (names as in include/lrt.h):
   gdn_bwd(q, k, v, log_a, beta, h0, do, dht=None, chunk=64)   -> (dq, dk, dv, dlog_a, dbeta, dh0)
   gdn_fwd_train(q, k, v, log_a, beta, h0=None, chunk=64)      -> (o, ht, saved)
   gdn_bwd_saved(q, k, v, log_a, beta, h0, do, saved, dht=None, chunk=64) -> as gdn_bwd
+  gdn_fwd_noalloc(q, k, v, log_a, beta, h0=None, chunk=64)    -> (o, ht)   (static workspace)
   kda_fwd(q, k, v, log_a, beta, h0=None, chunk=64)            -> (o, ht)
   ssd_fwd(q, k, v, log_a, h0=None, chunk=64)                   -> (o, ht)
   ssd_bwd(q, k, v, log_a, h0, do, dht=None, chunk=64)          -> (dq, dk, dv, dlog_a, dh0)
@@ -29,9 +30,10 @@ LIB_PATH = os.path.join(HERE, "liblrt.so")
 
 LRT_F32, LRT_BF16 = 0, 1
 OP_GDN_FWD, OP_GDN_BWD, OP_KDA_FWD, OP_SSD_FWD, OP_SSD_BWD = 0, 1, 2, 3, 4
-EXPORTS = ("gdn_fwd", "gdn_bwd", "gdn_fwd_train", "gdn_bwd_saved", "kda_fwd", "ssd_fwd",
+EXPORTS = ("gdn_fwd", "gdn_bwd", "gdn_fwd_train", "gdn_bwd_saved", "gdn_fwd_noalloc", "kda_fwd", "ssd_fwd",
            "ssd_bwd", "ssd_fwd_train", "ssd_bwd_saved", "lrt_workspace_bytes", "lrt_status_string",
            "lrt_profile_attach", "lrt_profile_count", "lrt_kernel_name")
+NOALLOC_MAX_BYTES = 64 << 20  # LRT_NOALLOC_MAX_BYTES
 
 _lib = None
 
@@ -60,8 +62,9 @@ def lib():
         L.gdn_bwd_saved.argtypes = [vp] * 14 + [ci] * 7 + [vp, sz, vp]
         L.ssd_fwd_train.argtypes = [vp] * 7 + [ci] * 7 + [vp, sz, vp]
         L.ssd_bwd_saved.argtypes = [vp] * 12 + [ci] * 7 + [vp, sz, vp]
+        L.gdn_fwd_noalloc.argtypes = [vp] * 8 + [ci] * 7 + [vp]
         for f in ("gdn_fwd", "kda_fwd", "ssd_fwd", "gdn_bwd", "ssd_bwd", "gdn_fwd_train", "gdn_bwd_saved",
-                  "ssd_fwd_train", "ssd_bwd_saved"):
+                  "ssd_fwd_train", "ssd_bwd_saved", "gdn_fwd_noalloc"):
             getattr(L, f).restype = ci
         L.lrt_workspace_bytes.argtypes = [ci] * 8
         L.lrt_workspace_bytes.restype = sz
@@ -198,6 +201,36 @@ def gdn_bwd_saved(q, k, v, log_a, beta, h0, do, saved, dht=None, chunk=64, want_
     if saved is None:
         raise ValueError("saved: the workspace gdn_fwd_train returned")
     return _bwd(True, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, saved, out, fn="gdn_bwd_saved")
+
+
+def gdn_fwd_noalloc(q, k, v, log_a, beta, h0=None, chunk=64, o=None, ht=True):
+    """gdn_fwd with the library's static per-GPU workspace (nothing is
+    allocated by the library; pass preallocated o / ht to allocate nothing
+    at all) -> (o, ht).  Sizes whose workspace exceeds NOALLOC_MAX_BYTES raise
+    LrtError (LRT_ERR_TOO_LARGE)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    for name, t, shp, ty in (("k", k, (B, T, H, dk), dt), ("v", v, (B, T, H, dv), dt),
+                             ("log_a", log_a, (B, T, H), torch.float32), ("beta", beta, (B, T, H), torch.float32),
+                             ("h0", h0, (B, H, dk, dv), torch.float32)):
+        _check(dev, dt, name, t, shp, ty)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check(dev, dt, "o", o, (B, T, H, dv), dt)
+    if ht is True:
+        ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif ht is False:
+        ht = None
+    _check(dev, dt, "ht", ht, (B, H, dk, dv), torch.float32)
+    with torch.cuda.device(dev):
+        rc = lib().gdn_fwd_noalloc(_p(q), _p(k), _p(v), _p(log_a), _p(beta), _p(h0), _p(o), _p(ht), B, T, H, dk, dv,
+                                   chunk, _dtype_code(q), _stream(dev))
+    if rc != 0:
+        raise LrtError("gdn_fwd_noalloc", rc)
+    return o, ht
 
 
 def kda_fwd(q, k, v, log_a, beta, h0=None, chunk=64, o=None, ht=True, workspace=None):

@@ -3,10 +3,37 @@
 // frees or synchronises.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "lrt_common.hpp"
 #include "lrt_internal.hpp"
 
 namespace lrt {
+
+// --------------------------------------------------- static scratch (noalloc)
+// The workspace of gdn_fwd_noalloc: a device array of LRT_NOALLOC_MAX_BYTES,
+// one copy per GPU the library runs on, held until the process ends.  Host
+// code never uses the array's name as an address: the device address of
+// each GPU's copy is looked up once per device (hipGetSymbolAddress, with
+// that device current) and kept in g_scratch_addr.
+static __device__ __align__(256) unsigned char scratch[LRT_NOALLOC_MAX_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_addr[kMaxDevices];  // per device id; nullptr until looked up
+
+// The current device's copy of `scratch`, or nullptr if it cannot be found.
+static void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_addr[dev] = ptr;
+  }
+  return g_scratch_addr[dev];
+}
 
 // ---------------------------------------------------------------- timing hook
 // Per calling thread (only the benchmark attaches it): entry points called
@@ -161,6 +188,19 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* log_a, con
                    workspace_bytes, stream);
 }
 
+int gdn_fwd_noalloc(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                    const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk,
+                    int dtype, void* stream) {
+  const size_t need = lrt_workspace_bytes(LRT_OP_GDN_FWD, B, T, H, d_k, d_v, chunk, dtype);
+  if (need != (size_t)-1 && need > (size_t)LRT_NOALLOC_MAX_BYTES) return LRT_ERR_TOO_LARGE;
+  void* ws = scratch_address();
+  if (ws == nullptr) return LRT_ERR_LAUNCH;
+  // gdn_fwd validates every other argument; its kernels write every
+  // workspace tile they read, so the array's earlier contents do not matter
+  return fwd_entry(kVarGDN, q, k, v, log_a, beta, h0, o, ht, B, T, H, d_k, d_v, chunk, dtype, ws,
+                   (size_t)LRT_NOALLOC_MAX_BYTES, stream);
+}
+
 int kda_fwd(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
             const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk,
             int dtype, void* workspace, size_t workspace_bytes, void* stream) {
@@ -256,6 +296,7 @@ const char* lrt_status_string(int status) {
     case LRT_ERR_ALIGN: return "a pointer is under-aligned (token tensors and workspace: 16 bytes; gates and states: 4)";
     case LRT_ERR_LAUNCH: return "kernel launch failed";
     case LRT_ERR_OP: return "unknown op";
+    case LRT_ERR_TOO_LARGE: return "the workspace these sizes need exceeds LRT_NOALLOC_MAX_BYTES (use gdn_fwd with a workspace)";
     default: return "unknown status";
   }
 }
