@@ -90,6 +90,10 @@ extern "C" {
 #define LRT_OP_KDA_FWD 2
 #define LRT_OP_SSD_FWD 3
 #define LRT_OP_SSD_BWD 4
+/* packed variable-length sequences: B = number of sequences, T = total tokens */
+#define LRT_OP_GDN_FWD_VARLEN 5
+#define LRT_OP_GDN_BWD_VARLEN 6
+#define LRT_OP_KDA_FWD_VARLEN 7
 
 /*
  * Gated DeltaNet forward.  Writes o and (if not NULL) ht.
@@ -204,6 +208,36 @@ int ssd_bwd_saved(const void* q, const void* k, const void* v, const float* log_
                   const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dlog_a,
                   float* dh0, int B, int T, int H, int d_k, int d_v, int chunk, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Packed variable-length sequences (the packed batches of long-context
+ * training, where many sequences of different lengths share one
+ * [1, T, H, d] tensor; the 1M-context 7-MLA / 21-GDN hybrid guide packs
+ * 20-160 sequences per 1M tokens).  gdn_fwd, kda_fwd and gdn_bwd for
+ * n_seq >= 1 sequences: sequence s spans tokens [cu_seqlens[s],
+ * cu_seqlens[s + 1]) of q, k, v, log_a, beta, o (and do, dq, dk, dv,
+ * dlog_a, dbeta), each laid out as [1, T, H, d] ([1, T, H] for gates;
+ * KDA log_a [1, T, H, d_k]).  cu_seqlens is a device array of n_seq + 1
+ * int32 (cu[0] = 0, non-decreasing, cu[n_seq] = T).  Every sequence starts
+ * from its own initial state: h0, ht, dht, dh0 are [n_seq, H, d_k, d_v]
+ * fp32 (h0 / dht NULL = zeros).  The result for each sequence is that of
+ * the dense entry point on that sequence alone; chunks never straddle a
+ * sequence boundary (a sequence shorter than `chunk` is one short chunk).
+ * Entries outside [0, T] or decreasing are clamped (running maximum) so
+ * that no kernel touches memory outside the tensors; the results are then
+ * undefined.  Workspace: lrt_workspace_bytes(LRT_OP_*_VARLEN, n_seq, T, ...).
+ * Arguments, outputs and other errors as the dense entry points.
+ */
+int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                   const float* h0, void* o, float* ht, const int* cu_seqlens, int n_seq, int T, int H, int d_k,
+                   int d_v, int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+int kda_fwd_varlen(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                   const float* h0, void* o, float* ht, const int* cu_seqlens, int n_seq, int T, int H, int d_k,
+                   int d_v, int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+int gdn_bwd_varlen(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                   const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dlog_a,
+                   float* dbeta, float* dh0, const int* cu_seqlens, int n_seq, int T, int H, int d_k, int d_v,
+                   int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes needed by `op` (LRT_OP_*) at these sizes.  Returns

@@ -12,6 +12,8 @@ Entry points (names as in include/lrt.h):
   gdn_fwd_train(q, k, v, log_a, beta, h0=None, chunk=64)      -> (o, ht, saved)
   gdn_bwd_saved(q, k, v, log_a, beta, h0, do, saved, dht=None, chunk=64) -> as gdn_bwd
   gdn_fwd_noalloc(q, k, v, log_a, beta, h0=None, chunk=64)    -> (o, ht)   (static workspace)
+  gdn_fwd_varlen / kda_fwd_varlen(q, k, v, log_a, beta, cu_seqlens, h0=None, chunk=64) -> (o, ht)
+  gdn_bwd_varlen(q, k, v, log_a, beta, cu_seqlens, h0, do, dht=None, chunk=64) -> as gdn_bwd
   kda_fwd(q, k, v, log_a, beta, h0=None, chunk=64)            -> (o, ht)
   ssd_fwd(q, k, v, log_a, h0=None, chunk=64)                   -> (o, ht)
   ssd_bwd(q, k, v, log_a, h0, do, dht=None, chunk=64)          -> (dq, dk, dv, dlog_a, dh0)
@@ -30,9 +32,11 @@ LIB_PATH = os.path.join(HERE, "liblrt.so")
 
 LRT_F32, LRT_BF16 = 0, 1
 OP_GDN_FWD, OP_GDN_BWD, OP_KDA_FWD, OP_SSD_FWD, OP_SSD_BWD = 0, 1, 2, 3, 4
+OP_GDN_FWD_VARLEN, OP_GDN_BWD_VARLEN, OP_KDA_FWD_VARLEN = 5, 6, 7
 EXPORTS = ("gdn_fwd", "gdn_bwd", "gdn_fwd_train", "gdn_bwd_saved", "gdn_fwd_noalloc", "kda_fwd", "ssd_fwd",
-           "ssd_bwd", "ssd_fwd_train", "ssd_bwd_saved", "lrt_workspace_bytes", "lrt_status_string",
-           "lrt_profile_attach", "lrt_profile_count", "lrt_kernel_name")
+           "ssd_bwd", "ssd_fwd_train", "ssd_bwd_saved", "gdn_fwd_varlen", "kda_fwd_varlen", "gdn_bwd_varlen",
+           "lrt_workspace_bytes", "lrt_status_string", "lrt_profile_attach", "lrt_profile_count",
+           "lrt_kernel_name")
 NOALLOC_MAX_BYTES = 64 << 20  # LRT_NOALLOC_MAX_BYTES
 
 _lib = None
@@ -63,8 +67,12 @@ def lib():
         L.ssd_fwd_train.argtypes = [vp] * 7 + [ci] * 7 + [vp, sz, vp]
         L.ssd_bwd_saved.argtypes = [vp] * 12 + [ci] * 7 + [vp, sz, vp]
         L.gdn_fwd_noalloc.argtypes = [vp] * 8 + [ci] * 7 + [vp]
+        L.gdn_fwd_varlen.argtypes = [vp] * 9 + [ci] * 7 + [vp, sz, vp]
+        L.kda_fwd_varlen.argtypes = [vp] * 9 + [ci] * 7 + [vp, sz, vp]
+        L.gdn_bwd_varlen.argtypes = [vp] * 15 + [ci] * 7 + [vp, sz, vp]
         for f in ("gdn_fwd", "kda_fwd", "ssd_fwd", "gdn_bwd", "ssd_bwd", "gdn_fwd_train", "gdn_bwd_saved",
-                  "ssd_fwd_train", "ssd_bwd_saved", "gdn_fwd_noalloc"):
+                  "ssd_fwd_train", "ssd_bwd_saved", "gdn_fwd_noalloc", "gdn_fwd_varlen", "kda_fwd_varlen",
+                  "gdn_bwd_varlen"):
             getattr(L, f).restype = ci
         L.lrt_workspace_bytes.argtypes = [ci] * 8
         L.lrt_workspace_bytes.restype = sz
@@ -231,6 +239,75 @@ def gdn_fwd_noalloc(q, k, v, log_a, beta, h0=None, chunk=64, o=None, ht=True):
     if rc != 0:
         raise LrtError("gdn_fwd_noalloc", rc)
     return o, ht
+
+
+def _varlen_check(q, cu_seqlens):
+    if q.shape[0] != 1:
+        raise ValueError("packed sequences are laid out as [1, T, H, d]")
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.device != q.device or \
+            cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2 or \
+            not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 tensor [n_seq + 1] on the inputs' device")
+    return cu_seqlens.numel() - 1
+
+
+def _fwd_varlen(fn, op, q, k, v, log_a, beta, cu_seqlens, h0, chunk, kda):
+    n = _varlen_check(q, cu_seqlens)
+    _, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    for name, t, shp, ty in (("k", k, (1, T, H, dk), dt), ("v", v, (1, T, H, dv), dt),
+                             ("log_a", log_a, (1, T, H, dk) if kda else (1, T, H), torch.float32),
+                             ("beta", beta, (1, T, H), torch.float32), ("h0", h0, (n, H, dk, dv), torch.float32)):
+        _check(dev, dt, name, t, shp, ty)
+    o = torch.empty((1, T, H, dv), dtype=dt, device=dev)
+    ht = torch.empty((n, H, dk, dv), dtype=torch.float32, device=dev)
+    code = _dtype_code(q)
+    ws, need = _workspace(op, dev, n, T, H, dk, dv, chunk, code, None)
+    with torch.cuda.device(dev):
+        rc = fn(_p(q), _p(k), _p(v), _p(log_a), _p(beta), _p(h0), _p(o), _p(ht), _p(cu_seqlens), n, T, H, dk, dv,
+                chunk, code, _p(ws), need, _stream(dev))
+    if rc != 0:
+        raise LrtError(fn.__name__, rc)
+    return o, ht
+
+
+def gdn_fwd_varlen(q, k, v, log_a, beta, cu_seqlens, h0=None, chunk=64):
+    """Gated DeltaNet forward over packed sequences (q [1, T, H, d_k], ...;
+    cu_seqlens int32 [n_seq + 1]; h0 [n_seq, H, d_k, d_v] or None) -> (o, ht)."""
+    return _fwd_varlen(lib().gdn_fwd_varlen, OP_GDN_FWD_VARLEN, q, k, v, log_a, beta, cu_seqlens, h0, chunk, False)
+
+
+def kda_fwd_varlen(q, k, v, log_a, beta, cu_seqlens, h0=None, chunk=64):
+    """Kimi Delta Attention forward over packed sequences -> (o, ht)."""
+    return _fwd_varlen(lib().kda_fwd_varlen, OP_KDA_FWD_VARLEN, q, k, v, log_a, beta, cu_seqlens, h0, chunk, True)
+
+
+def gdn_bwd_varlen(q, k, v, log_a, beta, cu_seqlens, h0, do, dht=None, chunk=64, want_dh0=True):
+    """Gated DeltaNet backward over packed sequences -> (dq, dk, dv, dlog_a,
+    dbeta, dh0 [n_seq, H, d_k, d_v] or None)."""
+    n = _varlen_check(q, cu_seqlens)
+    _, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    for name, t, shp, ty in (("k", k, (1, T, H, dk), dt), ("v", v, (1, T, H, dv), dt),
+                             ("log_a", log_a, (1, T, H), torch.float32), ("beta", beta, (1, T, H), torch.float32),
+                             ("h0", h0, (n, H, dk, dv), torch.float32), ("do", do, (1, T, H, dv), dt),
+                             ("dht", dht, (n, H, dk, dv), torch.float32)):
+        _check(dev, dt, name, t, shp, ty)
+    gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    gla = torch.empty((1, T, H), dtype=torch.float32, device=dev)
+    gb = torch.empty((1, T, H), dtype=torch.float32, device=dev)
+    gh0 = torch.empty((n, H, dk, dv), dtype=torch.float32, device=dev) if want_dh0 else None
+    code = _dtype_code(q)
+    ws, need = _workspace(OP_GDN_BWD_VARLEN, dev, n, T, H, dk, dv, chunk, code, None)
+    with torch.cuda.device(dev):
+        rc = lib().gdn_bwd_varlen(_p(q), _p(k), _p(v), _p(log_a), _p(beta), _p(h0), _p(do), _p(dht), _p(gq), _p(gk),
+                                  _p(gv), _p(gla), _p(gb), _p(gh0), _p(cu_seqlens), n, T, H, dk, dv, chunk, code,
+                                  _p(ws), need, _stream(dev))
+    if rc != 0:
+        raise LrtError("gdn_bwd_varlen", rc)
+    return gq, gk, gv, gla, gb, gh0
 
 
 def kda_fwd(q, k, v, log_a, beta, h0=None, chunk=64, o=None, ht=True, workspace=None):

@@ -61,7 +61,8 @@ void prof_after(void* stream) {
 
 static const char* const kKernelNames[kKNumKinds] = {
     "k_bwd_local", "k_dstate",   "k_grad",       "k_kda_prep", "k_state_copy", "k_wy",     "k_scan",
-    "k_wy_bwd",    "k_scan_bwd", "k_scan_local", "k_carry",    "k_ssd_prep",   "k_ssd_fwd"};
+    "k_wy_bwd",    "k_scan_bwd", "k_scan_local", "k_carry",    "k_ssd_prep",   "k_ssd_fwd",
+    "k_varlen_plan"};
 
 // Queried on every call (a device attribute read; nothing is cached between
 // calls).
@@ -83,17 +84,28 @@ static bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 static bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
-static int check_common(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
+// packed: B sequences of T tokens in all (cu_seqlens), else B sequences of T tokens each
+static int check_common(int B, int T, int H, int dk, int dv, int chunk, int dtype, bool packed = false) {
   if (dtype != LRT_F32 && dtype != LRT_BF16) return LRT_ERR_DTYPE;
   if (B < 1 || H < 1 || T < 0 || !dim_ok(dk) || !dim_ok(dv)) return LRT_ERR_SHAPE;
   // 64-bit offsets everywhere; keep token counts within int for the grid math
-  if ((long long)B * T > 0x7fffffffLL) return LRT_ERR_SHAPE;
+  if (!packed && (long long)B * T > 0x7fffffffLL) return LRT_ERR_SHAPE;
   if (chunk != 16 && chunk != 32 && chunk != 64) return LRT_ERR_CHUNK;
   // a chunk tile's element offsets are 32-bit in the kernels
   if ((long long)H * (dk > dv ? dk : dv) >= (1LL << 24)) return LRT_ERR_SHAPE;
   // chunk tiles times value blocks index the grids as int
-  if ((long long)B * H * ((T + chunk - 1) / chunk) * (dv / 16) > 0x7fffffffLL) return LRT_ERR_SHAPE;
+  const long long tiles = packed ? (long long)H * ((T + chunk - 1) / chunk + B) : (long long)B * H * ((T + chunk - 1) / chunk);
+  if (tiles * (dv / 16) > 0x7fffffffLL || (long long)B * H * (dv / 16) > 0x7fffffffLL) return LRT_ERR_SHAPE;
   return LRT_OK;
+}
+
+// the base op of a workspace op code, and whether it is the packed form
+static int base_op(int op, bool* packed) {
+  *packed = op >= LRT_OP_GDN_FWD_VARLEN;
+  if (op == LRT_OP_GDN_FWD_VARLEN) return LRT_OP_GDN_FWD;
+  if (op == LRT_OP_GDN_BWD_VARLEN) return LRT_OP_GDN_BWD;
+  if (op == LRT_OP_KDA_FWD_VARLEN) return LRT_OP_KDA_FWD;
+  return op;
 }
 
 // The chunk the kernels of `op` run: the requested one, or the largest
@@ -109,11 +121,13 @@ static int run_chunk(int op, int dtype, int dk, int dv, int chunk) {
   return chunk < m ? chunk : m;
 }
 
-static size_t ws_bytes(int op, int B, int T, int H, int dk, int dv, int chunk, int dtype) {
+static size_t ws_bytes(int op_code, int B, int T, int H, int dk, int dv, int chunk, int dtype) {
+  bool packed = false;
+  const int op = base_op(op_code, &packed);
   const size_t esz = dtype == LRT_BF16 ? 2 : 4;
   const int c = run_chunk(op, dtype, dk, dv, chunk);
-  size_t b = fwd_ws_layout(op, B, T, H, dk, dv, c, esz, nullptr).bytes;
-  if (op == LRT_OP_GDN_BWD || op == LRT_OP_SSD_BWD) b += bwd_ws_extra(op, B, T, H, dk, dv, c, esz);
+  size_t b = fwd_ws_layout(op, B, T, H, dk, dv, c, esz, nullptr, packed).bytes;
+  if (op == LRT_OP_GDN_BWD || op == LRT_OP_SSD_BWD) b += bwd_ws_extra(op, B, T, H, dk, dv, c, esz, packed);
   return b < 256 ? 256 : b;
 }
 
@@ -127,9 +141,11 @@ static int launch_empty(const float* h0, float* ht, int B, int H, int dk, int dv
 static int fwd_entry(int variant, const void* q, const void* k, const void* v, const float* log_a,
                      const float* beta, const float* h0, void* o, float* ht, int B, int T, int H, int dk,
                      int dv, int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream,
-                     bool train = false) {
-  int rc = check_common(B, T, H, dk, dv, chunk, dtype);
+                     bool train = false, const int* cu = nullptr, bool packed = false) {
+  int rc = check_common(B, T, H, dk, dv, chunk, dtype, packed);
   if (rc) return rc;
+  if (packed && !cu) return LRT_ERR_NULL;
+  if (packed && !aligned4(cu)) return LRT_ERR_ALIGN;
   // with T == 0 the token tensors are empty and may carry NULL pointers
   if (T > 0 && (!q || !k || !v || !log_a || !o || (variant != kVarSSD && !beta))) return LRT_ERR_NULL;
   // token tensors and the workspace are read with 16-byte vectors; gates and
@@ -142,10 +158,11 @@ static int fwd_entry(int variant, const void* q, const void* k, const void* v, c
     if (p && !aligned4(p)) return LRT_ERR_ALIGN;
   const int op = train ? (variant == kVarSSD ? LRT_OP_SSD_BWD : LRT_OP_GDN_BWD)
                        : variant == kVarGDN ? LRT_OP_GDN_FWD : variant == kVarSSD ? LRT_OP_SSD_FWD : LRT_OP_KDA_FWD;
-  if (!workspace || workspace_bytes < ws_bytes(op, B, T, H, dk, dv, chunk, dtype)) return LRT_ERR_WORKSPACE;
+  const int ws_op = !packed ? op : op == LRT_OP_GDN_FWD ? LRT_OP_GDN_FWD_VARLEN : LRT_OP_KDA_FWD_VARLEN;
+  if (!workspace || workspace_bytes < ws_bytes(ws_op, B, T, H, dk, dv, chunk, dtype)) return LRT_ERR_WORKSPACE;
   if (T == 0) return launch_empty(h0, ht, B, H, dk, dv, stream);
   FwdArgs a{variant, q, k, v, log_a, beta, h0, o, ht, B, T, H, dk, dv, run_chunk(op, dtype, dk, dv, chunk), dtype,
-            workspace, stream};
+            workspace, stream, packed ? cu : nullptr};
   rc = train ? fwd_train(a) : variant == kVarKDA ? fwd_kda(a) : fwd_scalar_gate(a);
   return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
 }
@@ -154,9 +171,11 @@ static int bwd_entry(int variant, const void* q, const void* k, const void* v, c
                      const float* beta, const float* h0, const void* d_o, const float* dht, void* dq, void* dk,
                      void* dv, float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v,
                      int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream,
-                     bool saved = false) {
-  int rc = check_common(B, T, H, d_k, d_v, chunk, dtype);
+                     bool saved = false, const int* cu = nullptr, bool packed = false) {
+  int rc = check_common(B, T, H, d_k, d_v, chunk, dtype, packed);
   if (rc) return rc;
+  if (packed && !cu) return LRT_ERR_NULL;
+  if (packed && !aligned4(cu)) return LRT_ERR_ALIGN;
   const bool delta = variant == kVarGDN;
   if (T > 0 && (!q || !k || !v || !log_a || !d_o || !dq || !dk || !dv || !dlog_a || (delta && (!beta || !dbeta))))
     return LRT_ERR_NULL;
@@ -167,10 +186,11 @@ static int bwd_entry(int variant, const void* q, const void* k, const void* v, c
   for (const void* p : sca)
     if (p && !aligned4(p)) return LRT_ERR_ALIGN;
   const int op = delta ? LRT_OP_GDN_BWD : LRT_OP_SSD_BWD;
-  if (!workspace || workspace_bytes < ws_bytes(op, B, T, H, d_k, d_v, chunk, dtype)) return LRT_ERR_WORKSPACE;
+  const int ws_op = packed ? LRT_OP_GDN_BWD_VARLEN : op;
+  if (!workspace || workspace_bytes < ws_bytes(ws_op, B, T, H, d_k, d_v, chunk, dtype)) return LRT_ERR_WORKSPACE;
   if (T == 0) return launch_empty(dht, dh0, B, H, d_k, d_v, stream);
   BwdArgs a{q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0,
-            B, T, H, d_k, d_v, run_chunk(op, dtype, d_k, d_v, chunk), dtype, workspace, stream};
+            B, T, H, d_k, d_v, run_chunk(op, dtype, d_k, d_v, chunk), dtype, workspace, stream, packed ? cu : nullptr};
   rc = delta ? bwd_gdn(a, saved) : bwd_ssd(a, saved);
   return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
 }
@@ -261,9 +281,33 @@ int ssd_bwd(const void* q, const void* k, const void* v, const float* log_a, con
 }
 
 size_t lrt_workspace_bytes(int op, int B, int T, int H, int d_k, int d_v, int chunk, int dtype) {
-  if (op < LRT_OP_GDN_FWD || op > LRT_OP_SSD_BWD) return (size_t)-1;
-  if (check_common(B, T, H, d_k, d_v, chunk, dtype) != LRT_OK) return (size_t)-1;
+  if (op < LRT_OP_GDN_FWD || op > LRT_OP_KDA_FWD_VARLEN) return (size_t)-1;
+  bool packed = false;
+  base_op(op, &packed);
+  if (check_common(B, T, H, d_k, d_v, chunk, dtype, packed) != LRT_OK) return (size_t)-1;
   return ws_bytes(op, B, T, H, d_k, d_v, chunk, dtype);
+}
+
+int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                   const float* h0, void* o, float* ht, const int* cu_seqlens, int n_seq, int T, int H, int d_k,
+                   int d_v, int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_entry(kVarGDN, q, k, v, log_a, beta, h0, o, ht, n_seq, T, H, d_k, d_v, chunk, dtype, workspace,
+                   workspace_bytes, stream, false, cu_seqlens, true);
+}
+
+int kda_fwd_varlen(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                   const float* h0, void* o, float* ht, const int* cu_seqlens, int n_seq, int T, int H, int d_k,
+                   int d_v, int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_entry(kVarKDA, q, k, v, log_a, beta, h0, o, ht, n_seq, T, H, d_k, d_v, chunk, dtype, workspace,
+                   workspace_bytes, stream, false, cu_seqlens, true);
+}
+
+int gdn_bwd_varlen(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                   const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dlog_a,
+                   float* dbeta, float* dh0, const int* cu_seqlens, int n_seq, int T, int H, int d_k, int d_v,
+                   int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_entry(kVarGDN, q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0, n_seq, T, H, d_k,
+                   d_v, chunk, dtype, workspace, workspace_bytes, stream, false, cu_seqlens, true);
 }
 int lrt_profile_attach(void** events, int* kinds, int n_kernels) {
   if (events == nullptr || kinds == nullptr || n_kernels <= 0) {

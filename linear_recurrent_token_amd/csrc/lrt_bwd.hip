@@ -50,10 +50,11 @@ struct BwdWs {
 
 // op: LRT_OP_GDN_BWD (also the Gated DeltaNet training forward) or
 // LRT_OP_SSD_BWD (also the Mamba2 training forward; no Tinv)
-static BwdWs bwd_ws_layout(int op, int B, int T, int H, int dk, int dv, int C, size_t esz, void* base) {
+static BwdWs bwd_ws_layout(int op, int B, int T, int H, int dk, int dv, int C, size_t esz, void* base,
+                           bool packed = false) {
   BwdWs w;
-  w.f = fwd_ws_layout(op, B, T, H, dk, dv, C, esz, base);
-  const size_t tiles = (size_t)B * H * ((size_t)(T + C - 1) / C);
+  w.f = fwd_ws_layout(op, B, T, H, dk, dv, C, esz, base, packed);
+  const size_t tiles = ws_tiles(B, T, H, C, packed);
   size_t off = w.f.bytes;
   char* p = (char*)base;
   auto take = [&](size_t bytes) {
@@ -68,8 +69,8 @@ static BwdWs bwd_ws_layout(int op, int B, int T, int H, int dk, int dv, int C, s
   return w;
 }
 
-size_t bwd_ws_extra(int op, int B, int T, int H, int dk, int dv, int C, size_t esz) {
-  const BwdWs w = bwd_ws_layout(op, B, T, H, dk, dv, C, esz, nullptr);
+size_t bwd_ws_extra(int op, int B, int T, int H, int dk, int dv, int C, size_t esz, bool packed) {
+  const BwdWs w = bwd_ws_layout(op, B, T, H, dk, dv, C, esz, nullptr, packed);
   return w.bytes - w.f.bytes;
 }
 
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
                                                     const E* __restrict__ d_o, const float* __restrict__ wG,
                                                     const E* __restrict__ wW, const E* __restrict__ wdUl,
                                                     const float* dht, float* dh0, E* __restrict__ wdS,
-                                                    E* __restrict__ wdU, int T, int H, int N, int DV) {
+                                                    E* __restrict__ wdU, SeqMap m, int DV) {
   constexpr int NT = 64 * NW;
   constexpr int P = lds_pad<E>();
   constexpr int LK = DK + P, LC = C + P, LB = BV + P;
@@ -211,7 +212,8 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
   const int nvb = DV / BV;
   const int wg = xcd_group(blockIdx.x, gridDim.x);  // the d_v blocks of one (b, h) share an L2
   const int vb = wg % nvb, bh = wg / nvb;
-  const int b = bh / H, h = bh % H, v0 = vb * BV;
+  const SeqPos sp = seq_pos(m, bh);
+  const int H = m.H, h = sp.h, v0 = vb * BV;
   const int w = wave_id(), l = lane_id();
 
   f32x4 hacc[HPW];
@@ -237,9 +239,9 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
   // clamped rows and chunk index so no load sits behind a branch.
 #define LRT_DSTATE_FETCH(n_, PART_)                                                                 \
   {                                                                                                 \
-    const size_t ft = (size_t)bh * N + (n_);                                                        \
-    const int fnv = min(C, T - (n_) * C);                                                           \
-    const size_t ftok = (size_t)b * T + (size_t)(n_) * C;                                           \
+    const size_t ft = sp.tile0 + (n_);                                                              \
+    const int fnv = min(C, sp.len - (n_) * C);                                                      \
+    const size_t ftok = sp.tok0 + (size_t)(n_) * C;                                                 \
     if ((PART_) & 1) {                                                                              \
       tQ.load_rows_clamped(q + (ftok * H + h) * DK, (size_t)H * DK, fnv);                           \
       if constexpr (DELTA) tW.load_block(wW + ft * C * DK);                                         \
@@ -260,10 +262,10 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
     }                                                                                               \
   }
 
-  LRT_DSTATE_FETCH(N - 1, 3)
-  for (int n = N - 1; n >= 0; --n) {
-    const size_t tile = (size_t)bh * N + n;
-    const int nv = min(C, T - n * C);
+  if (sp.nch > 0) LRT_DSTATE_FETCH(sp.nch - 1, 3)
+  for (int n = sp.nch - 1; n >= 0; --n) {
+    const size_t tile = sp.tile0 + n;
+    const int nv = min(C, sp.len - n * C);
     const int nprev = n > 0 ? n - 1 : 0;
     // gates: g, e^(g_C - g_t), gamma_t (wave 0 holds g of this chunk, one token per lane)
     asm volatile("" ::"v"(rg));
@@ -417,9 +419,10 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
                                                    const E* __restrict__ wU, const E* __restrict__ wdU,
                                                    const E* __restrict__ wT, E* __restrict__ dq,
                                                    E* __restrict__ dk_out, E* __restrict__ dv_out,
-                                                   float* __restrict__ dlog_a, float* __restrict__ dbeta, int T,
-                                                   int H, int N, int ntiles) {
+                                                   float* __restrict__ dlog_a, float* __restrict__ dbeta,
+                                                   SeqMap m) {
   typedef GradLds<E, C, DK, DV, DELTA, NW> Lay;
+  const int H = m.H, ntiles = tile_count(m);
   constexpr int NT = 64 * NW;
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, NB = C / 16;
   constexpr int V = 16 / (int)sizeof(E);
@@ -472,12 +475,11 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
   int ph = 0, pnv = 0;
   // The next chunk's operands are fetched in parts (bit mask PART_) spread
   // over this chunk's phases, so no wave stalls on a full memory queue.
-#define LRT_G_LOAD(tile_, PART_)                                                          \
+#define LRT_G_LOAD(tile_, P_, N_, PART_)                                                  \
   {                                                                                       \
-    const int ln = (tile_) % N, lbh = (tile_) / N;                                        \
-    const int lnv = min(C, T - ln * C);                                                   \
-    const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                           \
-    const int lh = lbh % H;                                                               \
+    const int lnv = min(C, (P_).len - (N_) * C);                                          \
+    const size_t ltok = (P_).tok0 + (size_t)(N_) * C;                                     \
+    const int lh = (P_).h;                                                                \
     if ((PART_) & 1) {                                                                    \
       tq.load_rows_clamped(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                \
       tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                \
@@ -495,14 +497,22 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
   }
 
   int tile = blockIdx.x;
-  if (tile < ntiles) LRT_G_LOAD(tile, 15)
+  if (tile < ntiles) {
+    int n0;
+    const SeqPos p0 = tile_pos(m, tile, n0);
+    LRT_G_LOAD(tile, p0, n0, 15)
+  }
   for (; tile < ntiles; tile += gridDim.x) {
-    const int n = tile % N, bh = tile / N, h = bh % H, b = bh / H;
-    const int t0 = n * C, nv = min(C, T - t0);
-    const size_t tok0 = (size_t)b * T + t0;
+    int n;
+    const SeqPos cp = tile_pos(m, tile, n);
+    const int h = cp.h;
+    const int nv = min(C, cp.len - n * C);
+    const size_t tok0 = cp.tok0 + (size_t)n * C;
     // the next chunk (the last one again on the final pass: its loads go
     // unused, but unconditional loads keep the waits on older ones exact)
     const int next = min(tile + (int)gridDim.x, ntiles - 1);
+    int nn;
+    const SeqPos np = tile_pos(m, next, nn);
     tq.store_masked(sQ, LK, nv);
     tk.store_masked(sK, LK, nv);
     to.store_masked(sdO, LV, nv);
@@ -528,7 +538,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
     }
     tdS.load_block(wdS + (size_t)tile * DV * DK);  // dH' of this chunk, needed after dS
     lds_barrier();
-    LRT_G_LOAD(next, 1)
+    LRT_G_LOAD(next, np, nn, 1)
 
     // dS = (dO U^T) o Gamma (inclusive); E = dS o (Q K^T) -> dg rows +, cols -
     // (a wave's tiles share column block w % NB: one column sum per wave)
@@ -586,7 +596,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
     }
     // (GDN: the next do, U and S wait until after the dQ products, where
     // register use peaks)
-    if constexpr (!DELTA) LRT_G_LOAD(next, 10)
+    if constexpr (!DELTA) LRT_G_LOAD(next, np, nn, 10)
     // dQ^T = gamma (Hn dO^T) + K^T dS^T (rows d, cols i), kept in registers;
     // dW^T = -Hn dU^T (GDN), kept in registers.  A wave's tiles share their
     // column block, so its dO, dS and dU fragments are the same for every
@@ -631,7 +641,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
     }
     tdS.store(sS, LK);
     lds_barrier();
-    LRT_G_LOAD(next, DELTA ? 6 : 4)
+    LRT_G_LOAD(next, np, nn, DELTA ? 6 : 4)
     if constexpr (DELTA) {
       // phase 2's operands of this chunk (clamped rows: unconditional loads),
       // issued here so their registers are not held through the dQ products
@@ -732,7 +742,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
       lds_barrier();
       lds_to_rows<E, C, DV, NT>(dv_out + (tok0 * H + h) * DV, (size_t)H * DV, sdV, LV, nv);
       lds_barrier();
-      LRT_G_LOAD(next, 8)
+      LRT_G_LOAD(next, np, nn, 8)
       // dT = (dW K^T) diag(b gamma) + (dU V^T) diag(b)   (rows i, cols j) -> dT^T [j][i]
 #pragma unroll
       for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
@@ -962,15 +972,13 @@ constexpr bool ssd_bwd_fits() {
 // backward mode).
 template <typename E, int C, int DK, int DV>
 void bwd_recompute(const BwdWs& ws, const void* q, const void* k, const void* v, const float* log_a,
-                   const float* beta, const float* h0, int B, int T, int H, void* stream) {
-  const int N = (T + C - 1) / C;
-  const int tiles = B * H * N;
+                   const float* beta, const float* h0, const SeqMap& sm, int tiles, void* stream) {
+  const int B = sm.B, H = sm.H;
   hipStream_t st = (hipStream_t)stream;
   constexpr int BV = scan_bv<E, C, DK, DV, kScanBwd, false>();  // state columns per workgroup
   LRT_LAUNCH(kKWyBwd, (k_wy<E, C, DK, DV, true, true, kWyWaves>),
              dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), st, (const E*)q,
-             (const E*)k, (const E*)v, log_a, beta, T, H, N, tiles, (E*)ws.f.W, (E*)ws.f.Up, ws.f.G, (E*)ws.f.P,
-             (E*)ws.T);
+             (const E*)k, (const E*)v, log_a, beta, sm, (E*)ws.f.W, (E*)ws.f.Up, ws.f.G, (E*)ws.f.P, (E*)ws.T);
   ScanArgs<E> sa{};
   sa.k = (const E*)k;
   sa.W = (const E*)ws.f.W;
@@ -980,10 +988,8 @@ void bwd_recompute(const BwdWs& ws, const void* q, const void* k, const void* v,
   sa.hs_ld = DV;
   sa.U = (E*)ws.f.U;
   sa.S = (E*)ws.f.S;
-  sa.T = T;
-  sa.H = H;
-  sa.N = N;
-  sa.L = N;
+  sa.m = sm;
+  sa.L = 1 << 30;
   sa.nseg = 1;
   sa.DV = DV;
   LRT_LAUNCH(kKScanBwd, (k_scan<E, C, DK, BV, kScanBwd, false, kStateWaves>), dim3(B * H * (DV / BV)),
@@ -998,21 +1004,23 @@ int bwd_impl(const BwdArgs& a, bool saved) {
   if constexpr (!gdn_bwd_fits<E, C, DK, DV>()) {
     return -3;  // not reached: the entry point runs a chunk that fits (bwd_max_chunk)
   } else {
-    const int N = (a.T + C - 1) / C;
-    const int tiles = a.B * a.H * N;
-    const BwdWs ws = bwd_ws_layout(LRT_OP_GDN_BWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
+    const bool packed = a.cu != nullptr;
+    const int tiles = (int)ws_tiles(a.B, a.T, a.H, C, packed);
+    const BwdWs ws = bwd_ws_layout(LRT_OP_GDN_BWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace, packed);
+    const SeqMap sm = seq_map(a.B, a.T, a.H, C, a.cu, ws.f);
     hipStream_t st = (hipStream_t)a.stream;
     constexpr int BV = dstate_bv<E, C, DK, DV, true>();  // state columns per workgroup
     const int sgrid = a.B * a.H * (DV / BV);
-    if (!saved) bwd_recompute<E, C, DK, DV>(ws, a.q, a.k, a.v, a.log_a, a.beta, a.h0, a.B, a.T, a.H, a.stream);
+    if (packed && launch_varlen_plan(a.cu, a.B, a.T, C, ws.f, a.stream) != 0) return -7;
+    if (!saved) bwd_recompute<E, C, DK, DV>(ws, a.q, a.k, a.v, a.log_a, a.beta, a.h0, sm, tiles, a.stream);
     LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, true, true>), dim3(sgrid), dim3(64 * kStateWaves), st,
                (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)ws.f.W, (const E*)ws.f.P, a.dht,
-               a.dh0, (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
+               a.dh0, (E*)ws.dS, (E*)ws.dU, sm, DV);
     LRT_LAUNCH(kKGrad, (k_grad<E, C, DK, DV, kGradWaves, true>),
                dim3(persistent_grid(tiles, GradLds<E, C, DK, DV, true>::TOTAL)), dim3(64 * kGradWaves), st,
                (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.d_o, a.beta, ws.f.G, (const E*)ws.f.S,
                (const E*)ws.dS, (const E*)ws.f.U, (const E*)ws.dU, (const E*)ws.T, (E*)a.dq, (E*)a.dk_out,
-               (E*)a.dv_out, a.dlog_a, a.dbeta, a.T, a.H, N, tiles);
+               (E*)a.dv_out, a.dlog_a, a.dbeta, sm);
     return hipGetLastError() == hipSuccess ? 0 : -7;
   }
 }
@@ -1032,6 +1040,7 @@ int ssd_bwd_impl(const BwdArgs& a, bool saved) {
     const int N = (a.T + C - 1) / C;
     const int tiles = a.B * a.H * N;
     const BwdWs ws = bwd_ws_layout(LRT_OP_SSD_BWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
+    const SeqMap sm = seq_map(a.B, a.T, a.H, C, nullptr, ws.f);
     hipStream_t st = (hipStream_t)a.stream;
     if (!saved) {
       constexpr int BVS = scan_bv<E, C, DK, DV, kScanBwd, false>();
@@ -1046,10 +1055,8 @@ int ssd_bwd_impl(const BwdArgs& a, bool saved) {
       sa.hin = a.h0;
       sa.hs_ld = DV;
       sa.S = (E*)ws.f.S;
-      sa.T = a.T;
-      sa.H = a.H;
-      sa.N = N;
-      sa.L = N;
+      sa.m = sm;
+      sa.L = 1 << 30;
       sa.nseg = 1;
       sa.DV = DV;
       LRT_LAUNCH(kKScanBwd, (k_scan<E, C, DK, BVS, kScanBwd, false, kStateWaves, false>), dim3(a.B * a.H * (DV / BVS)),
@@ -1059,7 +1066,7 @@ int ssd_bwd_impl(const BwdArgs& a, bool saved) {
       constexpr int BV = dstate_bv<E, C, DK, DV, true>();
       LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, false, true, true>), dim3(a.B * a.H * (DV / BV)),
                  dim3(64 * kStateWaves), st, (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)nullptr,
-                 (const E*)ws.f.P, a.dht, a.dh0, (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
+                 (const E*)ws.f.P, a.dht, a.dh0, (E*)ws.dS, (E*)ws.dU, sm, DV);
     } else {
       constexpr int BV = dstate_bv<E, C, DK, DV, false>();
       E* dUl = (E*)ws.f.Up;
@@ -1067,13 +1074,13 @@ int ssd_bwd_impl(const BwdArgs& a, bool saved) {
                  dim3(kThreads), st, (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, dUl, a.T, a.H, N, tiles);
       LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, false>), dim3(a.B * a.H * (DV / BV)),
                  dim3(64 * kStateWaves), st, (const E*)a.q, (const E*)a.k, (const E*)a.d_o, ws.f.G, (const E*)nullptr,
-                 (const E*)dUl, a.dht, a.dh0, (E*)ws.dS, (E*)ws.dU, a.T, a.H, N, DV);
+                 (const E*)dUl, a.dht, a.dh0, (E*)ws.dS, (E*)ws.dU, sm, DV);
     }
     LRT_LAUNCH(kKGrad, (k_grad<E, C, DK, DV, kGradWaves, false>),
                dim3(persistent_grid(tiles, GradLds<E, C, DK, DV, false>::TOTAL)), dim3(64 * kGradWaves), st,
                (const E*)a.q, (const E*)a.k, (const E*)nullptr, (const E*)a.d_o, (const float*)nullptr, ws.f.G,
                (const E*)ws.f.S, (const E*)ws.dS, (const E*)a.v, (const E*)ws.dU, (const E*)nullptr, (E*)a.dq,
-               (E*)a.dk_out, (E*)a.dv_out, a.dlog_a, (float*)nullptr, a.T, a.H, N, tiles);
+               (E*)a.dk_out, (E*)a.dv_out, a.dlog_a, (float*)nullptr, sm);
     return hipGetLastError() == hipSuccess ? 0 : -7;
   }
 }
@@ -1092,7 +1099,7 @@ int fwd_train_impl(const FwdArgs& a) {
     const int tiles = a.B * a.H * N;
     LRT_LAUNCH(kKWy, (k_wy<E, C, DK, DV, true, true, kWyWaves>),
                dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), a.stream,
-               (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.f.W,
+               (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, seq_map(a, ws.f, C), (E*)ws.f.W,
                (E*)ws.f.Up, ws.f.G, (E*)ws.f.P, (E*)ws.T);
     if (hipGetLastError() != hipSuccess) return -7;
     return launch_scan_fwd<E, C, DK, DV, false, true>(a, ws.f, N);

@@ -80,6 +80,67 @@ __device__ __forceinline__ int xcd_group(int bid, int nblocks) {
   return (bid % 8) * (nblocks / 8) + bid / 8;
 }
 
+// ------------------------------------------------------------ sequence map
+// Where the chunk tiles of the kernels lie.  Dense (cs == nullptr): B
+// sequences of T tokens each, N = ceil(T / C) chunks, the tiles of (b, h) from
+// (b H + h) N on.  Packed variable-length sequences (cs != nullptr): one
+// [1, T, H, d] tensor holds B sequences, sequence s at tokens
+// [cs[s], cs[s] + cl[s]) with co[s] chunks before it; its chunks never straddle
+// a sequence boundary, and the tiles of (s, h) start at
+// co[s] H + h ceil(cl[s] / C).  Workspace tiles stay chunk-major per (b, h),
+// and states are indexed b H + h in both layouts.
+struct SeqMap {
+  const int* cs;  // packed: sequence starts [B] (clamped into [0, T]); nullptr when dense
+  const int* cl;  // packed: sequence lengths [B]
+  const int* co;  // packed: chunks before each sequence [B + 1]
+  int T, H, C, N, B;
+};
+struct SeqPos {
+  size_t tok0;   // the sequence's first token (its rows of a [.., H, d] tensor start at tok0 H + h)
+  size_t tile0;  // workspace tile of its chunk 0
+  int len, nch;  // tokens, chunks
+  int h, bh;     // head; state index b H + h
+};
+__device__ __forceinline__ SeqPos seq_pos(const SeqMap& m, int bh) {
+  SeqPos p;
+  p.bh = bh;
+  p.h = bh % m.H;
+  const int b = bh / m.H;
+  if (m.cs == nullptr) {
+    p.tok0 = (size_t)b * m.T;
+    p.len = m.T;
+    p.nch = m.N;
+    p.tile0 = (size_t)bh * m.N;
+  } else {
+    p.tok0 = (size_t)m.cs[b];
+    p.len = m.cl[b];
+    p.nch = (p.len + m.C - 1) / m.C;
+    p.tile0 = (size_t)m.co[b] * m.H + (size_t)p.h * p.nch;
+  }
+  return p;
+}
+// The (sequence, head) and the chunk n of workspace tile `tile` (which must
+// be below tile_count).
+__device__ __forceinline__ SeqPos tile_pos(const SeqMap& m, int tile, int& n) {
+  if (m.cs == nullptr) {
+    n = tile % m.N;
+    return seq_pos(m, tile / m.N);
+  }
+  // the last sequence whose first tile is <= tile (empty sequences own none)
+  int lo = 0, hi = m.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (m.co[mid] * m.H <= tile) lo = mid;
+    else hi = mid - 1;
+  }
+  const int nch = m.co[lo + 1] - m.co[lo];
+  const int local = tile - m.co[lo] * m.H;
+  n = local % nch;
+  return seq_pos(m, lo * m.H + local / nch);
+}
+// Tiles in use: B H N (dense), or H times the chunks of all sequences (packed).
+__device__ __forceinline__ int tile_count(const SeqMap& m) { return m.cs == nullptr ? m.B * m.H * m.N : m.co[m.B] * m.H; }
+
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 

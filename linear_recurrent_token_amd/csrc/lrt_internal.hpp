@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "../../include/lrt.h"
+#include "lrt_common.hpp"
 
 namespace lrt {
 
@@ -21,6 +22,7 @@ struct FwdArgs {
   int B, T, H, dk, dv, chunk, dtype;
   void* workspace;
   void* stream;
+  const int* cu = nullptr;  // packed sequences: cu_seqlens [B + 1] (B sequences in [1, T, H, d]); nullptr: dense
 };
 
 struct BwdArgs {
@@ -33,6 +35,7 @@ struct BwdArgs {
   int B, T, H, dk, dv, chunk, dtype;
   void* workspace;
   void* stream;
+  const int* cu = nullptr;  // as FwdArgs::cu
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -52,9 +55,11 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 //   SegStart [b*h][seg][dk][dv]    f32  true start state of each segment
 //                                       (segmented scans: GDN_FWD, KDA_FWD, GDN_BWD)
 // The backward's own tiles (T, dS, dU) follow (bwd_ws_layout).
+//   cs, cl [B], co [B + 1]  int  packed sequences: starts, lengths, chunk offsets
 struct FwdWs {
   void *W, *Up, *Kt, *U, *S, *Qg, *P;
   float *G, *GC, *SegLoc, *SegStart;
+  int *cs, *cl, *co;
   size_t bytes;
 };
 
@@ -81,9 +86,18 @@ inline ScanPlan scan_plan(int B, int H, int DK, int DV, int N) {
   return {bv, ns < 1 ? 1 : (int)ns};
 }
 
-inline FwdWs fwd_ws_layout(int op, int B, int T, int H, int dk, int dv, int C, size_t esz, void* base) {
+// Chunk tiles of a workspace: B H ceil(T / C) (dense), or, for B packed
+// sequences of T tokens in all, at most H (ceil(T / C) + B) (each sequence
+// adds at most one partial chunk).
+inline size_t ws_tiles(int B, int T, int H, int C, bool packed) {
   const size_t N = (size_t)(T + C - 1) / C;
-  const size_t tiles = (size_t)B * H * N;
+  return packed ? (size_t)H * (N + B) : (size_t)B * H * N;
+}
+
+inline FwdWs fwd_ws_layout(int op, int B, int T, int H, int dk, int dv, int C, size_t esz, void* base,
+                           bool packed = false) {
+  const size_t N = (size_t)(T + C - 1) / C;
+  const size_t tiles = ws_tiles(B, T, H, C, packed);
   const bool gf = op == LRT_OP_GDN_FWD, kf = op == LRT_OP_KDA_FWD, gb = op == LRT_OP_GDN_BWD,
              sb = op == LRT_OP_SSD_BWD;
   size_t off = 0;
@@ -104,12 +118,23 @@ inline FwdWs fwd_ws_layout(int op, int B, int T, int H, int dk, int dv, int C, s
   w.GC = (float*)take(kf, tiles * dk * sizeof(float));
   w.Qg = take(kf, tiles * C * dk * esz);
   w.P = take(gf || kf || gb || sb, tiles * C * C * esz);
-  const int nseg = (gf || kf || gb) ? scan_plan(B, H, dk, dv, (int)N).nseg : 1;
+  const int nseg = (gf || kf || gb) && !packed ? scan_plan(B, H, dk, dv, (int)N).nseg : 1;
   w.SegLoc = (float*)take(nseg > 1, (size_t)B * H * nseg * dk * (dv + dk) * sizeof(float));
   w.SegStart = (float*)take(nseg > 1, (size_t)B * H * nseg * dk * dv * sizeof(float));
+  w.cs = (int*)take(packed, (size_t)B * sizeof(int));
+  w.cl = (int*)take(packed, (size_t)B * sizeof(int));
+  w.co = (int*)take(packed, (size_t)(B + 1) * sizeof(int));
   w.bytes = off;
   return w;
 }
+
+// The kernels' view of the sequences (the packed layout's tables live in
+// the workspace, filled by k_varlen_plan).
+inline SeqMap seq_map(int B, int T, int H, int C, const int* cu, const FwdWs& ws) {
+  if (cu == nullptr) return SeqMap{nullptr, nullptr, nullptr, T, H, C, (T + C - 1) / C, B};
+  return SeqMap{ws.cs, ws.cl, ws.co, T, H, C, 0, B};
+}
+inline SeqMap seq_map(const FwdArgs& a, const FwdWs& ws, int C) { return seq_map(a.B, a.T, a.H, C, a.cu, ws); }
 
 // Kernel ids reported by the benchmark timing hook (lrt_profile_attach).
 enum KernelKind {
@@ -126,6 +151,7 @@ enum KernelKind {
   kKCarry,
   kKSsdPrep,
   kKSsdFwd,
+  kKVarlenPlan,
   kKNumKinds
 };
 // Bracket one launch with the timing hook's events (no-ops unless attached).
@@ -148,6 +174,10 @@ constexpr int kWyWaves = 8;
 
 // Compute units of the current device (cached per device id).
 int device_cu_count();
+// Packed sequences: fills the workspace's sequence tables from cu_seqlens
+// (on the caller's stream, before any kernel that reads them).
+int launch_varlen_plan(const int* cu, int B, int T, int C, const FwdWs& ws, void* stream);
+
 // Grid of a chunk-parallel kernel that walks its tiles persistently: enough
 // workgroups to fill every CU at the occupancy its LDS allows, never more
 // than there are tiles.
@@ -164,7 +194,7 @@ int bwd_gdn(const BwdArgs& a, bool saved);
 int fwd_train(const FwdArgs& a);  // GDN or SSD by a.variant
 int bwd_ssd(const BwdArgs& a, bool saved);
 // workspace bytes the backward needs beyond the forward's tiles
-size_t bwd_ws_extra(int op, int B, int T, int H, int dk, int dv, int C, size_t esz);
+size_t bwd_ws_extra(int op, int B, int T, int H, int dk, int dv, int C, size_t esz, bool packed = false);
 
 // The largest chunk in {16, 32, 64} at which every kernel of `op` (an
 // LRT_OP_* code; the training forwards count as the backward's op) fits in

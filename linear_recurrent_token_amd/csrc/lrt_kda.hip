@@ -83,8 +83,8 @@ __device__ __forceinline__ void lds_f32_load(const float* p, float* x) {
 template <typename E, int C, int DK, int DV, int NW = 8>
 __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, const E* __restrict__ k,
                                                       const E* __restrict__ v, const float* __restrict__ log_a,
-                                                      const float* __restrict__ beta, int T, int H, int N,
-                                                      int ntiles, E* __restrict__ wW, E* __restrict__ wUp,
+                                                      const float* __restrict__ beta, SeqMap m,
+                                                      E* __restrict__ wW, E* __restrict__ wUp,
                                                       E* __restrict__ wKt, float* __restrict__ wGC,
                                                       E* __restrict__ wQg, E* __restrict__ wP) {
   constexpr int NT = 64 * NW;
@@ -104,6 +104,7 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
   int* sgmax = (int*)(smem + Lay::FL);
   const int w = wave_id(), l = lane_id();
   const int tid = threadIdx.x;
+  const int H = m.H, ntiles = tile_count(m);
 
   Tile<E, C, DK, NT> tk, tq;
   Tile<E, C, DV, NT> tv;
@@ -111,10 +112,11 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
   float rb = 0.f;
 #define LRT_KDA_LOAD(tile_)                                                               \
   {                                                                                       \
-    const int ln = (tile_) % N, lbh = (tile_) / N;                                        \
-    const int lnv = min(C, T - ln * C);                                                   \
-    const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                           \
-    const int lh = lbh % H;                                                               \
+    int ln;                                                                               \
+    const SeqPos lp = tile_pos(m, (tile_), ln);                                           \
+    const int lnv = min(C, lp.len - ln * C);                                              \
+    const size_t ltok = lp.tok0 + (size_t)ln * C;                                         \
+    const int lh = lp.h;                                                                  \
     tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                  \
     tq.load_rows_clamped(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                  \
     tv.load_rows_clamped(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                  \
@@ -125,7 +127,8 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
   int tile = blockIdx.x;
   if (tile < ntiles) LRT_KDA_LOAD(tile)
   for (; tile < ntiles; tile += gridDim.x) {
-    const int nv = min(C, T - (tile % N) * C);
+    int cn;
+    const int nv = min(C, tile_pos(m, tile, cn).len - cn * C);
     tk.store_masked(sK, LK, nv);
     tq.store_masked(sQ, LK, nv);
     tg.store_masked(sG, LG, nv);
@@ -395,13 +398,15 @@ int kda_impl(const FwdArgs& a) {
   if constexpr (!kda_fits<E, C, DK, DV>()) {
     return -3;  // not reached: the entry point runs a chunk that fits (kda_max_chunk)
   } else {
+    const bool packed = a.cu != nullptr;
     const int N = (a.T + C - 1) / C;
-    const int tiles = a.B * a.H * N;
-    const FwdWs ws = fwd_ws_layout(LRT_OP_KDA_FWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
+    const int tiles = (int)ws_tiles(a.B, a.T, a.H, C, packed);
+    const FwdWs ws = fwd_ws_layout(LRT_OP_KDA_FWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace, packed);
     hipStream_t st = (hipStream_t)a.stream;
+    if (packed && launch_varlen_plan(a.cu, a.B, a.T, C, ws, a.stream) != 0) return -7;
     LRT_LAUNCH(kKKdaPrep, (k_kda_prep<E, C, DK, DV, kWyWaves>),
                dim3(persistent_grid(tiles, KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL)), dim3(64 * kWyWaves), st,
-               (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, a.T, a.H, N, tiles, (E*)ws.W,
+               (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, seq_map(a, ws, C), (E*)ws.W,
                (E*)ws.Up, (E*)ws.Kt, ws.GC, (E*)ws.Qg, (E*)ws.P);
     if (hipGetLastError() != hipSuccess) return -7;
     return launch_scan_fwd<E, C, DK, DV, true>(a, ws, N);

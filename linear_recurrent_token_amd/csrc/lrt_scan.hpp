@@ -48,10 +48,11 @@ struct WyLds {
 template <typename E, int C, int DK, int DV, bool WRITE_P, bool WRITE_T, int NW = 8>
 __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, const E* __restrict__ k,
                                                 const E* __restrict__ v, const float* __restrict__ log_a,
-                                                const float* __restrict__ beta, int T, int H, int N, int ntiles,
+                                                const float* __restrict__ beta, SeqMap m,
                                                 E* __restrict__ wW, E* __restrict__ wUp, float* __restrict__ wG,
                                                 E* __restrict__ wP, E* __restrict__ wT) {
   typedef WyLds<E, C, DK, DV> Lay;
+  const int H = m.H, ntiles = tile_count(m);
   constexpr int NT = 64 * NW;
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, LA = Lay::LA;
   constexpr int NB = C / 16;
@@ -75,12 +76,11 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
   // The next chunk's operands, in parts (bit mask PART_) spread over this
   // chunk's phases; rows and chunk index clamped so no load sits behind a
   // branch (rows past the end are masked where staged).
-#define LRT_WY_LOAD(tile_, PART_)                                                         \
+#define LRT_WY_LOAD(P_, N_, PART_)                                                        \
   {                                                                                       \
-    const int ln = (tile_) % N, lbh = (tile_) / N;                                        \
-    const int lnv = min(C, T - ln * C);                                                   \
-    const size_t ltok = (size_t)(lbh / H) * T + (size_t)ln * C;                           \
-    const int lh = lbh % H;                                                               \
+    const int lnv = min(C, (P_).len - (N_) * C);                                          \
+    const size_t ltok = (P_).tok0 + (size_t)(N_) * C;                                     \
+    const int lh = (P_).h;                                                                \
     if ((PART_) & 1) {                                                                    \
       tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                \
       const int tc = min((int)threadIdx.x, lnv - 1); /* masked where used */              \
@@ -92,10 +92,17 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
   }
 
   int tile = blockIdx.x;
-  if (tile < ntiles) LRT_WY_LOAD(tile, 7)
+  if (tile < ntiles) {
+    int n0;
+    const SeqPos p0 = tile_pos(m, tile, n0);
+    LRT_WY_LOAD(p0, n0, 7)
+  }
   for (; tile < ntiles; tile += gridDim.x) {
-    const int nv = min(C, T - (tile % N) * C);
+    int cn;
+    const int nv = min(C, tile_pos(m, tile, cn).len - cn * C);
     const int next = min(tile + (int)gridDim.x, ntiles - 1);
+    int nn;
+    const SeqPos np = tile_pos(m, next, nn);
     asm volatile("" ::"v"(la), "v"(bt));
     if (threadIdx.x < 64) {
       const bool valid = (int)threadIdx.x < nv;
@@ -114,7 +121,7 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
     tk.store_masked(sK, LK, nv);
     if constexpr (WRITE_P) tq.store_masked(sQ, LK, nv);
     lds_barrier();
-    LRT_WY_LOAD(next, 1)
+    LRT_WY_LOAD(np, nn, 1)
     tv.scale_rows(sb);
     tv.store_masked(sV, LV, nv);
     // A (lower tiles; the solve reads nothing above the diagonal) and P^T
@@ -147,9 +154,9 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
       }
     }
     lds_barrier();
-    LRT_WY_LOAD(next, 4)
+    LRT_WY_LOAD(np, nn, 4)
     unit_lower_inverse<C, NT>(sA);
-    LRT_WY_LOAD(next, 2)
+    LRT_WY_LOAD(np, nn, 2)
     for (int idx = threadIdx.x; idx < C * C; idx += NT) {
       const int j = idx / C, i = idx % C;
       const float x = j <= i ? sA[j * LA + i] : 0.f;
@@ -210,7 +217,7 @@ struct ScanArgs {
   E* U;             // U^T [d_v][C] (backward recompute)
   E* S;             // chunk-start states [d_v][d_k] (backward recompute)
   int hs_ld;        // columns of a state row in hin / hout
-  int T, H, N;      // tokens, heads, chunks per sequence
+  SeqMap m;         // where each (sequence, head)'s chunks lie
   int L, nseg;      // chunks per segment, segments per sequence
   int DV;           // value columns (local mode appends d_k identity columns)
 };
@@ -270,11 +277,12 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
   // XCD and its L2 (they read the same W, K, Q and P tiles)
   const int wg = xcd_group(blockIdx.x, gridDim.x);
   const int vb = wg % nvb, seg = (wg / nvb) % a.nseg, bh = wg / nvb / a.nseg;
-  const int T = a.T, H = a.H, N = a.N, DV = a.DV;
-  const int h = bh % H, b = bh / H;
+  const SeqPos sp = seq_pos(a.m, bh);
+  const int H = a.m.H, DV = a.DV;
+  const int h = sp.h;
   const int v0 = vb * BV;
   const bool ident = MODE == kScanLocal && v0 >= DV;  // identity columns (U' = 0)
-  const int n0 = seg * a.L, n1 = min(N, n0 + a.L);
+  const int n0 = seg * a.L, n1 = min(sp.nch, n0 + a.L);
   const int w = wave_id(), l = lane_id();
   const size_t st0 = ((size_t)bh * a.nseg + seg) * DK;  // first state row of this segment
 
@@ -306,9 +314,9 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
     float g;  // GDN: g of token tid; KDA: G_C of key dimension tid
   };
   auto fetch = [&](Ops& x, int n_) {
-    const size_t ft = (size_t)bh * N + n_;
-    const int fnv = min(C, T - n_ * C);
-    const size_t ftok = (size_t)b * T + (size_t)n_ * C;
+    const size_t ft = sp.tile0 + n_;
+    const int fnv = min(C, sp.len - n_ * C);
+    const size_t ftok = sp.tok0 + (size_t)n_ * C;
     if constexpr (DELTA) x.W.load_block(a.W + ft * C * DK);
     if constexpr (KDA) {
       x.K.load_block(a.Kt + ft * DK * C);
@@ -339,9 +347,9 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
   };
 
   auto step = [&](Ops& x, int n) {
-    const size_t tile = (size_t)bh * N + n;
-    const int nv = min(C, T - n * C);
-    const size_t tok0 = (size_t)b * T + (size_t)n * C;
+    const size_t tile = sp.tile0 + n;
+    const int nv = min(C, sp.len - n * C);
+    const size_t tok0 = sp.tok0 + (size_t)n * C;
     // ---- this chunk's operands and start state into LDS
     if constexpr (KDA) {
       if (threadIdx.x < DK) sg[threadIdx.x] = __expf(x.g);  // per-dim chunk decay
@@ -564,16 +572,14 @@ int launch_scan_fwd_bv(const FwdArgs& a, const FwdWs& ws, int N, int nseg) {
   s.o = (E*)a.o;
   s.S = (E*)ws.S;  // written only by SAVE
   s.U = (E*)ws.U;
-  s.T = a.T;
-  s.H = a.H;
-  s.N = N;
+  s.m = seq_map(a, ws, C);
   s.DV = DV;
   const int bhv = a.B * a.H * (DV / BV);
   if (nseg == 1) {
     s.hin = a.h0;
     s.hout = a.ht;
     s.hs_ld = DV;
-    s.L = N;
+    s.L = 1 << 30;  // one segment: every chunk of the sequence
     s.nseg = 1;
     LRT_LAUNCH(kKScan, (k_scan<E, C, DK, BV, kScanFwd, KDA, kStateWaves, true, SAVE>), dim3(bhv),
                dim3(64 * kStateWaves), st, s);
@@ -615,7 +621,8 @@ int launch_scan_fwd(const FwdArgs& a, const FwdWs& ws, int N) {
   constexpr int BV64 = scan_bv<E, C, DK, DV, kScanFwd, KDA, 64>();
   constexpr int BV128 = scan_bv<E, C, DK, DV, kScanFwd, KDA, 128>();
   static_assert(BV64 > 0, "no column block of the forward scan fits in LDS");
-  const ScanPlan pl = scan_plan(a.B, a.H, DK, DV, N);
+  // packed sequences: one segment per (sequence, head) (their count is the parallelism)
+  const ScanPlan pl = a.cu != nullptr ? ScanPlan{64, 1} : scan_plan(a.B, a.H, DK, DV, N);
   if constexpr (BV128 > BV64) {
     if (pl.bv > 64) return launch_scan_fwd_bv<E, C, DK, DV, BV128, KDA, SAVE>(a, ws, N, pl.nseg);
   }

@@ -204,7 +204,7 @@ def test_workspace_bytes(L):
     lib = L.lib()
     bad = ctypes.c_size_t(-1).value
     assert lib.lrt_workspace_bytes(9, 1, 64, 2, 16, 16, 16, 0) == bad
-    assert lib.lrt_workspace_bytes(5, 1, 64, 2, 16, 16, 16, 0) == bad
+    assert lib.lrt_workspace_bytes(8, 1, 64, 2, 16, 16, 16, 0) == bad
     assert lib.lrt_workspace_bytes(-1, 1, 64, 2, 16, 16, 16, 0) == bad
     assert lib.lrt_workspace_bytes(0, 1, 64, 2, 16, 16, 17, 0) == bad
     for op in range(5):
@@ -219,7 +219,7 @@ def test_workspace_bytes(L):
     assert L.workspace_bytes(3, 16, 2048, 8, 128, 128, 64, 1) == 256
     # every dtype and size of the supported set has a workspace (fp32 at
     # d = 128 runs a smaller chunk: its workspace is sized for that chunk)
-    for op in range(5):
+    for op in range(8):
         for dt in (0, 1):
             for dk in (16, 32, 64, 128):
                 for dv in (16, 32, 64, 128):
@@ -232,3 +232,43 @@ def test_python_binding_rejects_cpu_tensors(L):
     x = torch.zeros((1, 8, 1, 16))
     with pytest.raises(ValueError):
         L.gdn_fwd(x, x, x, torch.zeros((1, 8, 1)), torch.zeros((1, 8, 1)))
+
+
+def test_varlen_validation(L):
+    """Packed-sequence entry points: cu_seqlens required and 4-byte aligned,
+    n_seq >= 1, workspace of the packed op code; all before any launch."""
+    c = codes()
+    lib = L.lib()
+    F = FAKE
+    n, T, H, d, ch = 3, 100, 2, 16, 16
+    need = L.workspace_bytes(L.OP_GDN_FWD_VARLEN, n, T, H, d, d, ch, 0)
+    # the packed layout reserves room for a partial chunk per sequence
+    assert need > L.workspace_bytes(L.OP_GDN_FWD, 1, T, H, d, d, ch, 0)
+    # q k v log_a beta h0 o ht cu | n T H dk dv chunk dtype | ws wsb stream
+    args = [F, F, F, F, F, None, F, None, F, n, T, H, d, d, ch, 0, F, need - 1, None]
+    for fn in ("gdn_fwd_varlen", "kda_fwd_varlen"):
+        f = getattr(lib, fn)
+        assert f(*args) == c["LRT_ERR_WORKSPACE"], fn
+        a = list(args)
+        a[8] = None
+        assert f(*a) == c["LRT_ERR_NULL"], fn
+        a = list(args)
+        a[8] = F + 2
+        assert f(*a) == c["LRT_ERR_ALIGN"], fn
+        a = list(args)
+        a[9] = 0
+        assert f(*a) == c["LRT_ERR_SHAPE"], fn
+        a = list(args)
+        a[14] = 48
+        assert f(*a) == c["LRT_ERR_CHUNK"], fn
+    bneed = L.workspace_bytes(L.OP_GDN_BWD_VARLEN, n, T, H, d, d, ch, 0)
+    # q k v log_a beta h0 do dht dq dk dv dlog_a dbeta dh0 cu | n T H dk dv chunk dtype | ws wsb stream
+    b = [F, F, F, F, F, None, F, None, F, F, F, F, F, None, F, n, T, H, d, d, ch, 0, F, bneed - 1, None]
+    assert lib.gdn_bwd_varlen(*b) == c["LRT_ERR_WORKSPACE"]
+    a = list(b)
+    a[14] = None
+    assert lib.gdn_bwd_varlen(*a) == c["LRT_ERR_NULL"]
+    for i in (0, 1, 2, 3, 4, 6, 8, 9, 10, 11, 12):
+        a = list(b)
+        a[i] = None
+        assert lib.gdn_bwd_varlen(*a) == c["LRT_ERR_NULL"], i
