@@ -56,9 +56,16 @@ WORKLOADS = {
     "ssd_train_recompute_bf16_2k": ("SSD (Mamba2 case) chunked fwd+bwd (backward recomputes) tokens/s, "
                                     "B=16 T=2048 H=8 d=128", "ssd_fwd + ssd_bwd"),
     "kda_bf16_1m": ("KDA chunked fwd tokens/s, B=1 T=2^20 H=16 d=128", "kda_fwd"),
+    # the forwards on the raw projections, activations fused into the kernels
+    # (the line also times the unfused pipeline: torch activations + the plain forward)
+    "gdn_fused_bf16_2k": ("GDN chunked fwd, fused prologue (raw q/k/beta/gate in) tokens/s, B=16 T=2048 H=8 d=128",
+                          "gdn_fwd_fused"),
+    "kda_fused_bf16_1m": ("KDA chunked fwd, fused prologue (raw q/k/beta/gate in) tokens/s, B=1 T=2^20 H=16 d=128",
+                          "kda_fwd_fused"),
 }
 # workloads that time another op on an existing workload's inputs
-CONFIG_OF = {"gdn_train_recompute_bf16_2k": "gdn_train_bf16_2k", "ssd_train_recompute_bf16_2k": "ssd_train_bf16_2k"}
+CONFIG_OF = {"gdn_train_recompute_bf16_2k": "gdn_train_bf16_2k", "ssd_train_recompute_bf16_2k": "ssd_train_bf16_2k",
+             "gdn_fused_bf16_2k": "gdn_bf16_2k", "kda_fused_bf16_1m": "kda_bf16_1m"}
 
 # the library kernels of each pass (the forward's and the backward's share of a step)
 FWD_KERNELS = {"k_wy", "k_scan", "k_scan_local", "k_carry", "k_ssd_fwd", "k_kda_prep", "k_state_copy"}
@@ -129,7 +136,8 @@ def method_model(op, c, has_h0, has_dht, esz=2):
     n_th, n_bh, st = B * T * H, B * H, dk * dv * 4
     e = esz
     ssd, kda = op.startswith("ssd"), op.startswith("kda")
-    gate = 4 * dk if kda else 4
+    # the fused KDA forward reads the gate pre-activation in the call's dtype
+    gate = (dk * e if op.endswith("fused") else 4 * dk) if kda else 4
     beta = 0 if ssd else 4
     fwd_b = (2 * dk + dv) * e + gate + beta + dv * e
     fwd_f = 2 * C * (dk + dv) + 4 * dk * dv if ssd else 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv
@@ -247,11 +255,15 @@ def main():
     copy = copy_gbs(torch, hip, stream, dev)
     # input sets larger than the last-level cache need no rotation
     nsets = args.sets if B * T * H * (2 * dk + dv) * 2 < (1 << 30) else 1
-    sets = [synth.config_inputs(cfg, device="cuda", seed=s) for s in range(nsets)]
+    fused = op.endswith("_fused")
+    if fused:
+        sets = [synth.raw_inputs(cfg, device="cuda", seed=s) for s in range(nsets)]
+    else:
+        sets = [synth.config_inputs(cfg, device="cuda", seed=s) for s in range(nsets)]
     code = L.LRT_BF16
     opc = {"gdn_fwd + gdn_bwd": L.OP_GDN_BWD, "gdn_fwd_train + gdn_bwd_saved": L.OP_GDN_BWD, "gdn_fwd": L.OP_GDN_FWD,
            "ssd_fwd": L.OP_SSD_FWD, "ssd_fwd + ssd_bwd": L.OP_SSD_BWD, "ssd_fwd_train + ssd_bwd_saved": L.OP_SSD_BWD,
-           "kda_fwd": L.OP_KDA_FWD}[op]
+           "kda_fwd": L.OP_KDA_FWD, "gdn_fwd_fused": L.OP_GDN_FWD, "kda_fwd_fused": L.OP_KDA_FWD}[op]
     ws_bytes = max(L.workspace_bytes(L.OP_GDN_FWD, B, T, H, dk, dv, C, code),
                    L.workspace_bytes(opc, B, T, H, dk, dv, C, code))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -268,8 +280,28 @@ def main():
         if op.startswith("ssd"):
             grads = grads[:4] + grads[5:]
 
+    def activate(s):
+        """The unfused pipeline's activation passes (torch), for the comparison line."""
+        def l2(x):
+            x = x.float()
+            return (x / torch.sqrt((x * x).sum(-1, keepdim=True) + 1e-6)).to(x_dtype)
+        x_dtype = s["q_raw"].dtype
+        return (l2(s["q_raw"]), l2(s["k_raw"]), -torch.nn.functional.softplus(s["gate_raw"].float()),
+                torch.sigmoid(s["beta_raw"]))
+
+    def step_unfused(i):
+        s = sets[i % len(sets)]
+        q, k, la, beta = activate(s)
+        f = L.kda_fwd if op == "kda_fwd_fused" else L.gdn_fwd
+        f(q, k, s["v"], la, beta, s.get("h0"), chunk=C, o=o, ht=ht, workspace=ws)
+
     def step(i):
         s = sets[i % len(sets)]
+        if fused:
+            f = L.kda_fwd_fused if op == "kda_fwd_fused" else L.gdn_fwd_fused
+            f(s["q_raw"], s["k_raw"], s["v"], s["gate_raw"], s["beta_raw"], s.get("h0"), chunk=C, o=o, ht=ht,
+              workspace=ws)
+            return
         if op == "ssd_fwd_train + ssd_bwd_saved":
             L.ssd_fwd_train(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), chunk=C, o=o, ht=ht, workspace=ws)
             L.ssd_bwd_saved(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), s["do"], ws, s.get("dht"), chunk=C,
@@ -369,9 +401,30 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), **common}
 
+    unfused = None
+    if fused:
+        # the same step through the unfused pipeline (activation passes + plain forward), same events
+        for i in range(2):
+            step_unfused(i)
+        torch.cuda.synchronize()
+        ev = hip.events(2)
+        hip.record(ev[0], stream)
+        for i in range(args.steps):
+            step_unfused(i)
+        hip.record(ev[1], stream)
+        torch.cuda.synchronize()
+        ums = hip.elapsed_ms(ev[0], ev[1]) / args.steps
+        hip.destroy(ev)
+        unfused = {"ms_per_step": round(ums, 4), "fused_speedup": round(ums / ms_per_step, 3),
+                   "what": "torch l2norm(q), l2norm(k), -softplus(gate), sigmoid(beta) then the plain forward"}
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(op, sets[0], C, args.cpu_seconds)
+        cpu_inp = sets[0]
+        if fused:
+            q, k, la, beta = activate(sets[0])
+            cpu_inp = {"q": q, "k": k, "v": sets[0]["v"], "log_a": la, "beta": beta, "h0": sets[0].get("h0")}
+        cpu = cpu_baseline(op, cpu_inp, C, args.cpu_seconds)
 
     step_rec = {
         "method_bytes": int(step_bytes),
@@ -410,6 +463,8 @@ def main():
                     for n, d in kernels.items()},
         "cpu_baseline": cpu,
     }
+    if unfused is not None:
+        line["unfused_pipeline"] = unfused
     print(json.dumps(line), flush=True)
     if args.copy_probe:
         copy_probe(torch, dev)

@@ -210,6 +210,29 @@ int ssd_bwd_saved(const void* q, const void* k, const void* v, const float* log_
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The mixer with its input activations fused into the kernels' load stage
+ * (the fused-kernel recipe of the AMD ROCm blog "Pretraining hybrid LLMs with
+ * Primus", section "Recipe", Table 4 and the paragraph on the use_fla_*
+ * flags: unfused elementwise passes cost throughput).  Same outputs and
+ * arguments as gdn_fwd / kda_fwd, for the raw projections:
+ *   q = q_raw / sqrt(sum_d q_raw^2 + 1e-6)   per (b, t, h) row over d_k, in
+ *   k = k_raw / sqrt(sum_d k_raw^2 + 1e-6)   fp32, rounded to dtype
+ *   beta = sigmoid(beta_raw)                  beta_raw fp32 [B, T, H]
+ *   log a = -softplus(gate_raw) = -(max(z, 0) + log(1 + exp(-|z|)))
+ * gdn_fwd_fused: gate_raw fp32 [B, T, H].  kda_fwd_fused: gate_raw is the
+ * per-key-dimension pre-activation (the low-rank projection's output) in
+ * dtype, [B, T, H, d_k], 16-byte aligned -- half the bytes of an fp32 log-gate
+ * for bf16.  The normalised q, k, the gates and beta are never written: one
+ * read of the raw projections replaces the separate activation passes.
+ */
+int gdn_fwd_fused(const void* q_raw, const void* k_raw, const void* v, const float* gate_raw,
+                  const float* beta_raw, const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v,
+                  int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+int kda_fwd_fused(const void* q_raw, const void* k_raw, const void* v, const void* gate_raw, const float* beta_raw,
+                  const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Packed variable-length sequences (the packed batches of long-context
  * training, where many sequences of different lengths share one
  * [1, T, H, d] tensor; the 1M-context 7-MLA / 21-GDN hybrid guide packs

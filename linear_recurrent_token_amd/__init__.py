@@ -13,6 +13,7 @@ Entry points (names as in include/lrt.h):
   gdn_bwd_saved(q, k, v, log_a, beta, h0, do, saved, dht=None, chunk=64) -> as gdn_bwd
   gdn_fwd_noalloc(q, k, v, log_a, beta, h0=None, chunk=64)    -> (o, ht)   (static workspace)
   gdn_fwd_varlen / kda_fwd_varlen(q, k, v, log_a, beta, cu_seqlens, h0=None, chunk=64) -> (o, ht)
+  gdn_fwd_fused / kda_fwd_fused(q_raw, k_raw, v, gate_raw, beta_raw, h0=None, chunk=64) -> (o, ht)
   gdn_bwd_varlen(q, k, v, log_a, beta, cu_seqlens, h0, do, dht=None, chunk=64) -> as gdn_bwd
   kda_fwd(q, k, v, log_a, beta, h0=None, chunk=64)            -> (o, ht)
   ssd_fwd(q, k, v, log_a, h0=None, chunk=64)                   -> (o, ht)
@@ -35,6 +36,7 @@ OP_GDN_FWD, OP_GDN_BWD, OP_KDA_FWD, OP_SSD_FWD, OP_SSD_BWD = 0, 1, 2, 3, 4
 OP_GDN_FWD_VARLEN, OP_GDN_BWD_VARLEN, OP_KDA_FWD_VARLEN = 5, 6, 7
 EXPORTS = ("gdn_fwd", "gdn_bwd", "gdn_fwd_train", "gdn_bwd_saved", "gdn_fwd_noalloc", "kda_fwd", "ssd_fwd",
            "ssd_bwd", "ssd_fwd_train", "ssd_bwd_saved", "gdn_fwd_varlen", "kda_fwd_varlen", "gdn_bwd_varlen",
+           "gdn_fwd_fused", "kda_fwd_fused",
            "lrt_workspace_bytes", "lrt_status_string", "lrt_profile_attach", "lrt_profile_count",
            "lrt_kernel_name")
 NOALLOC_MAX_BYTES = 64 << 20  # LRT_NOALLOC_MAX_BYTES
@@ -70,9 +72,11 @@ def lib():
         L.gdn_fwd_varlen.argtypes = [vp] * 9 + [ci] * 7 + [vp, sz, vp]
         L.kda_fwd_varlen.argtypes = [vp] * 9 + [ci] * 7 + [vp, sz, vp]
         L.gdn_bwd_varlen.argtypes = [vp] * 15 + [ci] * 7 + [vp, sz, vp]
+        L.gdn_fwd_fused.argtypes = [vp] * 8 + [ci] * 7 + [vp, sz, vp]
+        L.kda_fwd_fused.argtypes = [vp] * 8 + [ci] * 7 + [vp, sz, vp]
         for f in ("gdn_fwd", "kda_fwd", "ssd_fwd", "gdn_bwd", "ssd_bwd", "gdn_fwd_train", "gdn_bwd_saved",
                   "ssd_fwd_train", "ssd_bwd_saved", "gdn_fwd_noalloc", "gdn_fwd_varlen", "kda_fwd_varlen",
-                  "gdn_bwd_varlen"):
+                  "gdn_bwd_varlen", "gdn_fwd_fused", "kda_fwd_fused"):
             getattr(L, f).restype = ci
         L.lrt_workspace_bytes.argtypes = [ci] * 8
         L.lrt_workspace_bytes.restype = sz
@@ -136,7 +140,8 @@ def _workspace(op, dev, B, T, H, dk, dv, chunk, dt, workspace):
     return workspace, need
 
 
-def _fwd(fn, op, q, k, v, log_a, beta, h0, chunk, o, ht, workspace, kda=False, want_ws=False):
+def _fwd(fn, op, q, k, v, log_a, beta, h0, chunk, o, ht, workspace, kda=False, want_ws=False,
+         gate_dtype=torch.float32):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -145,7 +150,7 @@ def _fwd(fn, op, q, k, v, log_a, beta, h0, chunk, o, ht, workspace, kda=False, w
     _check(dev, dt, "k", k, (B, T, H, dk), dt)
     _check(dev, dt, "v", v, (B, T, H, dv), dt)
     _check(dev, dt, "q", q, (B, T, H, dk), dt)
-    _check(dev, dt, "log_a", log_a, (B, T, H, dk) if kda else (B, T, H), torch.float32)
+    _check(dev, dt, "log_a", log_a, (B, T, H, dk) if kda else (B, T, H), gate_dtype)
     ssd = fn.__name__.startswith("ssd")
     if not ssd:
         if beta is None:
@@ -239,6 +244,21 @@ def gdn_fwd_noalloc(q, k, v, log_a, beta, h0=None, chunk=64, o=None, ht=True):
     if rc != 0:
         raise LrtError("gdn_fwd_noalloc", rc)
     return o, ht
+
+
+def gdn_fwd_fused(q_raw, k_raw, v, gate_raw, beta_raw, h0=None, chunk=64, o=None, ht=True, workspace=None):
+    """Gated DeltaNet forward on the raw projections (q, k L2-normalised,
+    beta = sigmoid(beta_raw), log a = -softplus(gate_raw), all inside the
+    kernels) -> (o, ht).  gate_raw, beta_raw fp32 [B, T, H]."""
+    return _fwd(lib().gdn_fwd_fused, OP_GDN_FWD, q_raw, k_raw, v, gate_raw, beta_raw, h0, chunk, o, ht, workspace)
+
+
+def kda_fwd_fused(q_raw, k_raw, v, gate_raw, beta_raw, h0=None, chunk=64, o=None, ht=True, workspace=None):
+    """Kimi Delta Attention forward on the raw projections -> (o, ht).
+    gate_raw: the per-key-dimension gate pre-activation [B, T, H, d_k] in the
+    dtype of q (log a = -softplus(gate_raw) inside the kernels)."""
+    return _fwd(lib().kda_fwd_fused, OP_KDA_FWD, q_raw, k_raw, v, gate_raw, beta_raw, h0, chunk, o, ht, workspace,
+                kda=True, gate_dtype=q_raw.dtype)
 
 
 def _varlen_check(q, cu_seqlens):

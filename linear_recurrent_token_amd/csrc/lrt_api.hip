@@ -141,7 +141,7 @@ static int launch_empty(const float* h0, float* ht, int B, int H, int dk, int dv
 static int fwd_entry(int variant, const void* q, const void* k, const void* v, const float* log_a,
                      const float* beta, const float* h0, void* o, float* ht, int B, int T, int H, int dk,
                      int dv, int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream,
-                     bool train = false, const int* cu = nullptr, bool packed = false) {
+                     bool train = false, const int* cu = nullptr, bool packed = false, bool fuse = false) {
   int rc = check_common(B, T, H, dk, dv, chunk, dtype, packed);
   if (rc) return rc;
   if (packed && !cu) return LRT_ERR_NULL;
@@ -156,13 +156,15 @@ static int fwd_entry(int variant, const void* q, const void* k, const void* v, c
   const void* sca[] = {log_a, beta, h0, ht};
   for (const void* p : sca)
     if (p && !aligned4(p)) return LRT_ERR_ALIGN;
+  // the fused KDA gate pre-activation is read in 16-byte pieces
+  if (fuse && variant == kVarKDA && log_a && !aligned(log_a)) return LRT_ERR_ALIGN;
   const int op = train ? (variant == kVarSSD ? LRT_OP_SSD_BWD : LRT_OP_GDN_BWD)
                        : variant == kVarGDN ? LRT_OP_GDN_FWD : variant == kVarSSD ? LRT_OP_SSD_FWD : LRT_OP_KDA_FWD;
   const int ws_op = !packed ? op : op == LRT_OP_GDN_FWD ? LRT_OP_GDN_FWD_VARLEN : LRT_OP_KDA_FWD_VARLEN;
   if (!workspace || workspace_bytes < ws_bytes(ws_op, B, T, H, dk, dv, chunk, dtype)) return LRT_ERR_WORKSPACE;
   if (T == 0) return launch_empty(h0, ht, B, H, dk, dv, stream);
   FwdArgs a{variant, q, k, v, log_a, beta, h0, o, ht, B, T, H, dk, dv, run_chunk(op, dtype, dk, dv, chunk), dtype,
-            workspace, stream, packed ? cu : nullptr};
+            workspace, stream, packed ? cu : nullptr, fuse};
   rc = train ? fwd_train(a) : variant == kVarKDA ? fwd_kda(a) : fwd_scalar_gate(a);
   return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
 }
@@ -286,6 +288,20 @@ size_t lrt_workspace_bytes(int op, int B, int T, int H, int d_k, int d_v, int ch
   base_op(op, &packed);
   if (check_common(B, T, H, d_k, d_v, chunk, dtype, packed) != LRT_OK) return (size_t)-1;
   return ws_bytes(op, B, T, H, d_k, d_v, chunk, dtype);
+}
+
+int gdn_fwd_fused(const void* q_raw, const void* k_raw, const void* v, const float* gate_raw,
+                  const float* beta_raw, const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v,
+                  int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_entry(kVarGDN, q_raw, k_raw, v, gate_raw, beta_raw, h0, o, ht, B, T, H, d_k, d_v, chunk, dtype,
+                   workspace, workspace_bytes, stream, false, nullptr, false, true);
+}
+
+int kda_fwd_fused(const void* q_raw, const void* k_raw, const void* v, const void* gate_raw, const float* beta_raw,
+                  const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_entry(kVarKDA, q_raw, k_raw, v, (const float*)gate_raw, beta_raw, h0, o, ht, B, T, H, d_k, d_v, chunk,
+                   dtype, workspace, workspace_bytes, stream, false, nullptr, false, true);
 }
 
 int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* log_a, const float* beta,

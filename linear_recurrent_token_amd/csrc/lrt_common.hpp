@@ -80,6 +80,18 @@ __device__ __forceinline__ int xcd_group(int bid, int nblocks) {
   return (bid % 8) * (nblocks / 8) + bid / 8;
 }
 
+// ------------------------------------------------------------ fused prologue
+// The mixers' input activations, applied in the kernels' load stage by the
+// *_fused entry points to the raw projections:
+//   q, k  <- x / sqrt(sum x^2 + kL2Eps) per (token, head) row over d_k;
+//   beta  <- sigmoid(z);   log a <- -softplus(z) = -(max(z, 0) + log(1 + e^-|z|))
+// (the stable form; the hardware exp / log, a few ulp in fp32).
+constexpr float kL2Eps = 1e-6f;
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + __expf(-z)); }
+__device__ __forceinline__ float neg_softplus_f(float z) {
+  return -(fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z))));
+}
+
 // ------------------------------------------------------------ sequence map
 // Where the chunk tiles of the kernels lie.  Dense (cs == nullptr): B
 // sequences of T tokens each, N = ceil(T / C) chunks, the tiles of (b, h) from
@@ -437,6 +449,27 @@ struct Tile {
     for (int s = 0; s < PT; ++s) {
       const int idx = threadIdx.x + NT * s;
       if (NP % NT == 0 || idx < NP) x[s] = *g16(g, (unsigned)idx * (unsigned)V);
+    }
+  }
+  // Every row scaled to unit L2 norm, x / sqrt(sum_row x^2 + eps): the sum
+  // in fp32 over the row's PR pieces, which sit on PR consecutive lanes
+  // (butterfly over them), the result rounded back to E.  Rows of zeros
+  // stay zero.
+  __device__ __forceinline__ void normalize_rows(float eps) {
+    static_assert(PR <= 64 && (PR & (PR - 1)) == 0, "a row's pieces must be a power-of-two lane group");
+#pragma unroll
+    for (int s = 0; s < PT; ++s) {
+      E e[V];
+      __builtin_memcpy(e, &x[s], 16);
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < V; ++i) ss += to_f(e[i]) * to_f(e[i]);
+#pragma unroll
+      for (int m = 1; m < PR; m <<= 1) ss += __shfl_xor(ss, m, 64);
+      const float sc = 1.f / sqrtf(ss + eps);
+#pragma unroll
+      for (int i = 0; i < V; ++i) e[i] = from_f<E>(to_f(e[i]) * sc);
+      __builtin_memcpy(&x[s], e, 16);
     }
   }
   __device__ __forceinline__ void scale_rows(const float* rs) {

@@ -79,9 +79,8 @@ constexpr bool gdn_fwd_fits() {
   return WyLds<E, C, DK, DV>::TOTAL <= kLdsMax && scan_bv<E, C, DK, DV, kScanFwd, false>() > 0;
 }
 
-template <typename E, int C, int DK, int DV>
-int fwd_impl(const FwdArgs& a) {
-  if (a.variant == kVarSSD) return launch_ssd_fwd<E, C, DK, DV>(a);
+template <typename E, int C, int DK, int DV, bool FUSE>
+int gdn_fwd_impl(const FwdArgs& a) {
   if constexpr (!gdn_fwd_fits<E, C, DK, DV>()) {
     return -3;  // not reached: the entry point runs a chunk that fits (fwd_max_chunk)
   } else {
@@ -90,13 +89,19 @@ int fwd_impl(const FwdArgs& a) {
     const int tiles = (int)ws_tiles(a.B, a.T, a.H, C, packed);
     const FwdWs ws = fwd_ws_layout(LRT_OP_GDN_FWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace, packed);
     if (packed && launch_varlen_plan(a.cu, a.B, a.T, C, ws, a.stream) != 0) return -7;
-    LRT_LAUNCH(kKWy, (k_wy<E, C, DK, DV, true, false, kWyWaves>),
+    LRT_LAUNCH(kKWy, (k_wy<E, C, DK, DV, true, false, kWyWaves, FUSE>),
                dim3(persistent_grid(tiles, WyLds<E, C, DK, DV>::TOTAL)), dim3(64 * kWyWaves), a.stream,
                (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, seq_map(a, ws, C), (E*)ws.W,
                (E*)ws.Up, ws.G, (E*)ws.P, (E*)nullptr);
     if (hipGetLastError() != hipSuccess) return -7;
-    return launch_scan_fwd<E, C, DK, DV, false>(a, ws, N);
+    return launch_scan_fwd<E, C, DK, DV, false, false, FUSE>(a, ws, N);
   }
+}
+
+template <typename E, int C, int DK, int DV>
+int fwd_impl(const FwdArgs& a) {
+  if (a.variant == kVarSSD) return launch_ssd_fwd<E, C, DK, DV>(a);
+  return a.fuse ? gdn_fwd_impl<E, C, DK, DV, true>(a) : gdn_fwd_impl<E, C, DK, DV, false>(a);
 }
 
 template <typename E, int DK, int DV>

@@ -23,6 +23,7 @@ struct FwdArgs {
   void* workspace;
   void* stream;
   const int* cu = nullptr;  // packed sequences: cu_seqlens [B + 1] (B sequences in [1, T, H, d]); nullptr: dense
+  bool fuse = false;        // q, k, log_a, beta are raw projections (the fused prologue)
 };
 
 struct BwdArgs {

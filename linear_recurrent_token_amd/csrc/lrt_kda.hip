@@ -21,6 +21,8 @@
 // k_kda_prep (persistent over the chunks) writes W, U'^T, Ktil^T, Q o e^G, P and
 // the per-dimension chunk decay; the serial scan in KDA mode (per-dimension
 // decay, operands from the workspace) then carries the state and forms o.
+#include <type_traits>
+
 #include "lrt_internal.hpp"
 #include "lrt_scan.hpp"
 
@@ -79,10 +81,13 @@ __device__ __forceinline__ void lds_f32_load(const float* p, float* x) {
 }
 
 // Persistent over the chunk tiles; the next tile's inputs load into
-// registers while this one computes.
-template <typename E, int C, int DK, int DV, int NW = 8>
+// registers while this one computes.  FUSE: q, k, log_a and beta are the raw
+// projections -- the gate pre-activation in E ([B, T, H, d_k]) -- and the
+// fused prologue (L2-normalised q, k rows; log a = -softplus; sigmoid) is
+// applied as they are staged.
+template <typename E, int C, int DK, int DV, int NW = 8, bool FUSE = false>
 __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, const E* __restrict__ k,
-                                                      const E* __restrict__ v, const float* __restrict__ log_a,
+                                                      const E* __restrict__ v, const void* __restrict__ log_a_,
                                                       const float* __restrict__ beta, SeqMap m,
                                                       E* __restrict__ wW, E* __restrict__ wUp,
                                                       E* __restrict__ wKt, float* __restrict__ wGC,
@@ -106,9 +111,11 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
   const int tid = threadIdx.x;
   const int H = m.H, ntiles = tile_count(m);
 
+  typedef typename std::conditional<FUSE, E, float>::type GE;  // element type of the gate input
+  const GE* log_a = (const GE*)log_a_;
   Tile<E, C, DK, NT> tk, tq;
   Tile<E, C, DV, NT> tv;
-  Tile<float, C, DK, NT> tg;
+  Tile<GE, C, DK, NT> tg;
   float rb = 0.f;
 #define LRT_KDA_LOAD(tile_)                                                               \
   {                                                                                       \
@@ -129,11 +136,36 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
   for (; tile < ntiles; tile += gridDim.x) {
     int cn;
     const int nv = min(C, tile_pos(m, tile, cn).len - cn * C);
+    if constexpr (FUSE) {
+      tk.normalize_rows(kL2Eps);
+      tq.normalize_rows(kL2Eps);
+    }
     tk.store_masked(sK, LK, nv);
     tq.store_masked(sQ, LK, nv);
-    tg.store_masked(sG, LG, nv);
+    if constexpr (FUSE) {
+      // log a = -softplus(z) in fp32, rows past the end zero (as store_masked)
+      constexpr int GV = 16 / (int)sizeof(GE), GPR = DK / GV;
+#pragma unroll
+      for (int s2 = 0; s2 < tg.PT; ++s2) {
+        const int idx = tid + NT * s2;
+        if (tg.NP % NT == 0 || idx < tg.NP) {
+          const int r = idx / GPR, c0 = (idx % GPR) * GV;
+          GE e[GV];
+          __builtin_memcpy(e, &tg.x[s2], 16);
+#pragma unroll
+          for (int i = 0; i < GV; i += 4) {
+            f32x4 y;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = r < nv ? neg_softplus_f(to_f(e[i + j])) : 0.f;
+            *(f32x4*)(sG + r * LG + c0 + i) = y;
+          }
+        }
+      }
+    } else {
+      tg.store_masked(sG, LG, nv);
+    }
     asm volatile("" ::"v"(rb));  // consumed by every lane (no load into it left pending)
-    if (tid < C) sb[tid] = tid < nv ? rb : 0.f;
+    if (tid < C) sb[tid] = tid < nv ? (FUSE ? sigmoid_f(rb) : rb) : 0.f;
     if (tid == 0) *sgmax = 0;
     lds_barrier();
     tv.scale_rows(sb);  // rows past the end scale by 0
@@ -393,8 +425,8 @@ constexpr bool kda_fits() {
   return KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL <= kLdsMax && scan_bv<E, C, DK, DV, kScanFwd, true>() > 0;
 }
 
-template <typename E, int C, int DK, int DV>
-int kda_impl(const FwdArgs& a) {
+template <typename E, int C, int DK, int DV, bool FUSE>
+int kda_impl_t(const FwdArgs& a) {
   if constexpr (!kda_fits<E, C, DK, DV>()) {
     return -3;  // not reached: the entry point runs a chunk that fits (kda_max_chunk)
   } else {
@@ -404,13 +436,17 @@ int kda_impl(const FwdArgs& a) {
     const FwdWs ws = fwd_ws_layout(LRT_OP_KDA_FWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace, packed);
     hipStream_t st = (hipStream_t)a.stream;
     if (packed && launch_varlen_plan(a.cu, a.B, a.T, C, ws, a.stream) != 0) return -7;
-    LRT_LAUNCH(kKKdaPrep, (k_kda_prep<E, C, DK, DV, kWyWaves>),
+    LRT_LAUNCH(kKKdaPrep, (k_kda_prep<E, C, DK, DV, kWyWaves, FUSE>),
                dim3(persistent_grid(tiles, KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL)), dim3(64 * kWyWaves), st,
                (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, seq_map(a, ws, C), (E*)ws.W,
                (E*)ws.Up, (E*)ws.Kt, ws.GC, (E*)ws.Qg, (E*)ws.P);
     if (hipGetLastError() != hipSuccess) return -7;
     return launch_scan_fwd<E, C, DK, DV, true>(a, ws, N);
   }
+}
+template <typename E, int C, int DK, int DV>
+int kda_impl(const FwdArgs& a) {
+  return a.fuse ? kda_impl_t<E, C, DK, DV, true>(a) : kda_impl_t<E, C, DK, DV, false>(a);
 }
 
 template <typename E, int DK, int DV>

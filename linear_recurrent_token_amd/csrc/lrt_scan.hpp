@@ -44,8 +44,10 @@ struct WyLds {
 
 // Outputs per tile (chunk-major per (b, h)): W [C][d_k] rows, U' [C][d_v] in
 // accumulator-tile order (acc_tile_store), g [C]; WRITE_P: P [C][C] rows
-// (zero above the diagonal); WRITE_T: T [C][C].
-template <typename E, int C, int DK, int DV, bool WRITE_P, bool WRITE_T, int NW = 8>
+// (zero above the diagonal); WRITE_T: T [C][C].  FUSE: q, k, log_a and beta
+// are the raw projections (the fused prologue: L2-normalised rows, -softplus,
+// sigmoid, applied as they are staged).
+template <typename E, int C, int DK, int DV, bool WRITE_P, bool WRITE_T, int NW = 8, bool FUSE = false>
 __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, const E* __restrict__ k,
                                                 const E* __restrict__ v, const float* __restrict__ log_a,
                                                 const float* __restrict__ beta, SeqMap m,
@@ -106,11 +108,11 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
     asm volatile("" ::"v"(la), "v"(bt));
     if (threadIdx.x < 64) {
       const bool valid = (int)threadIdx.x < nv;
-      const float g = wave_incl_scan(valid ? la : 0.f);
+      const float g = wave_incl_scan(valid ? (FUSE ? neg_softplus_f(la) : la) : 0.f);
       if (threadIdx.x < C) {
         const int t = threadIdx.x;
         const float gam = __expf(g);
-        const float b_ = valid ? bt : 0.f;
+        const float b_ = valid ? (FUSE ? sigmoid_f(bt) : bt) : 0.f;
         sg[t] = g;
         sgam[t] = gam;
         sb[t] = b_;
@@ -118,8 +120,12 @@ __global__ __launch_bounds__(64 * NW, 4) void k_wy(const E* __restrict__ q, cons
         wG[(size_t)tile * C + t] = g;
       }
     }
+    if constexpr (FUSE) tk.normalize_rows(kL2Eps);
     tk.store_masked(sK, LK, nv);
-    if constexpr (WRITE_P) tq.store_masked(sQ, LK, nv);
+    if constexpr (WRITE_P) {
+      if constexpr (FUSE) tq.normalize_rows(kL2Eps);
+      tq.store_masked(sQ, LK, nv);
+    }
     lds_barrier();
     LRT_WY_LOAD(np, nn, 1)
     tv.scale_rows(sb);
@@ -248,7 +254,10 @@ struct ScanLds {
 // with U'^T supplied in a.Up); the backward recompute then writes only S_n.
 // SAVE (forward mode) also writes S_n and U, as the backward recompute does,
 // for a backward that reuses them.
-template <typename E, int C, int DK, int BV, int MODE, bool KDA, int NW = 8, bool DELTA = true, bool SAVE = false>
+// FUSE (forward of the fused prologue): the q and k rows read here are the
+// raw projections, L2-normalised as they are staged.
+template <typename E, int C, int DK, int BV, int MODE, bool KDA, int NW = 8, bool DELTA = true, bool SAVE = false,
+          bool FUSE = false>
 __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
   typedef ScanLds<E, C, DK, BV, MODE, KDA> Lay;
   constexpr bool FWD = MODE == kScanFwd;
@@ -372,8 +381,10 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
       }
     }
     if constexpr (DELTA) x.W.store(sW, LK);
+    if constexpr (FUSE && !KDA) x.K.normalize_rows(kL2Eps);
     x.K.store(sK, KDA ? LC : LK);
     if constexpr (FWD) {
+      if constexpr (FUSE && !KDA) x.Q.normalize_rows(kL2Eps);
       x.Q.store(sQ, LK);
       x.P.store(sP, LC);
     }
@@ -556,7 +567,7 @@ __global__ __launch_bounds__(64 * NW) void k_carry(const float* __restrict__ hlo
 // few to occupy the device the sequence is cut into segments: a local pass
 // per segment, the carry over segments, and the scan from the true segment
 // start states.
-template <typename E, int C, int DK, int DV, int BV, bool KDA, bool SAVE = false>
+template <typename E, int C, int DK, int DV, int BV, bool KDA, bool SAVE = false, bool FUSE = false>
 int launch_scan_fwd_bv(const FwdArgs& a, const FwdWs& ws, int N, int nseg) {
   hipStream_t st = (hipStream_t)a.stream;
   ScanArgs<E> s{};
@@ -581,7 +592,7 @@ int launch_scan_fwd_bv(const FwdArgs& a, const FwdWs& ws, int N, int nseg) {
     s.hs_ld = DV;
     s.L = 1 << 30;  // one segment: every chunk of the sequence
     s.nseg = 1;
-    LRT_LAUNCH(kKScan, (k_scan<E, C, DK, BV, kScanFwd, KDA, kStateWaves, true, SAVE>), dim3(bhv),
+    LRT_LAUNCH(kKScan, (k_scan<E, C, DK, BV, kScanFwd, KDA, kStateWaves, true, SAVE, FUSE>), dim3(bhv),
                dim3(64 * kStateWaves), st, s);
   } else {
     s.L = (N + nseg - 1) / nseg;
@@ -589,7 +600,7 @@ int launch_scan_fwd_bv(const FwdArgs& a, const FwdWs& ws, int N, int nseg) {
     s.hin = nullptr;
     s.hout = ws.SegLoc;
     s.hs_ld = DV + DK;
-    LRT_LAUNCH(kKScanLocal, (k_scan<E, C, DK, BV, kScanLocal, KDA, kStateWaves>),
+    LRT_LAUNCH(kKScanLocal, (k_scan<E, C, DK, BV, kScanLocal, KDA, kStateWaves, true, false, FUSE>),
                dim3(a.B * a.H * ((DV + DK) / BV) * nseg), dim3(64 * kStateWaves), st, s);
     static_assert(CarryLds<E, DK, BV>::TOTAL <= 160 * 1024, "k_carry LDS");
     LRT_LAUNCH(kKCarry, (k_carry<E, DK, BV, kStateWaves>), dim3(bhv), dim3(64 * kStateWaves), st,
@@ -597,7 +608,7 @@ int launch_scan_fwd_bv(const FwdArgs& a, const FwdWs& ws, int N, int nseg) {
     s.hin = ws.SegStart;
     s.hout = nullptr;
     s.hs_ld = DV;
-    LRT_LAUNCH(kKScan, (k_scan<E, C, DK, BV, kScanFwd, KDA, kStateWaves, true, SAVE>), dim3(bhv * nseg),
+    LRT_LAUNCH(kKScan, (k_scan<E, C, DK, BV, kScanFwd, KDA, kStateWaves, true, SAVE, FUSE>), dim3(bhv * nseg),
                dim3(64 * kStateWaves), st, s);
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
@@ -616,7 +627,7 @@ constexpr int scan_bv() {
     return 0;
 }
 
-template <typename E, int C, int DK, int DV, bool KDA, bool SAVE = false>
+template <typename E, int C, int DK, int DV, bool KDA, bool SAVE = false, bool FUSE = false>
 int launch_scan_fwd(const FwdArgs& a, const FwdWs& ws, int N) {
   constexpr int BV64 = scan_bv<E, C, DK, DV, kScanFwd, KDA, 64>();
   constexpr int BV128 = scan_bv<E, C, DK, DV, kScanFwd, KDA, 128>();
@@ -624,9 +635,9 @@ int launch_scan_fwd(const FwdArgs& a, const FwdWs& ws, int N) {
   // packed sequences: one segment per (sequence, head) (their count is the parallelism)
   const ScanPlan pl = a.cu != nullptr ? ScanPlan{64, 1} : scan_plan(a.B, a.H, DK, DV, N);
   if constexpr (BV128 > BV64) {
-    if (pl.bv > 64) return launch_scan_fwd_bv<E, C, DK, DV, BV128, KDA, SAVE>(a, ws, N, pl.nseg);
+    if (pl.bv > 64) return launch_scan_fwd_bv<E, C, DK, DV, BV128, KDA, SAVE, FUSE>(a, ws, N, pl.nseg);
   }
-  return launch_scan_fwd_bv<E, C, DK, DV, BV64, KDA, SAVE>(a, ws, N, pl.nseg);
+  return launch_scan_fwd_bv<E, C, DK, DV, BV64, KDA, SAVE, FUSE>(a, ws, N, pl.nseg);
 }
 
 }  // namespace lrt

@@ -138,19 +138,43 @@ def make_inputs(op, B, T, H, dk, dv, dtype=torch.bfloat16, seed=0, device="cpu",
     return out
 
 
-def lowrank_gate(B, T, H, dk, seed, device, rank=16, width=None, block=1 << 16):
-    """log a = -softplus(W_up (W_down x)) in fp32, [B,T,H,dk]; x drawn per token block."""
+def lowrank_gate(B, T, H, dk, seed, device, rank=16, width=None, block=1 << 16, preact=False,
+                 out_dtype=torch.float32):
+    """log a = -softplus(W_up (W_down x)) in fp32, [B,T,H,dk]; x drawn per token block.
+    preact=True returns the pre-activation W_up (W_down x) itself (in out_dtype)."""
     D = H * dk if width is None else int(width)
     w_down = randn((rank, D), seed, "w_down", device, std=0.02)
     w_up = randn((H * dk, rank), seed, "w_up", device, std=0.02)
-    out = torch.empty((B, T, H, dk), dtype=torch.float32, device=device)
+    out = torch.empty((B, T, H, dk), dtype=out_dtype, device=device)
     g = _gen(seed, "x", device)
     for b in range(B):
         for t0 in range(0, T, block):
             t1 = min(T, t0 + block)
             x = torch.randn((t1 - t0, D), generator=g, device=device, dtype=torch.float32)
             z = (x @ w_down.t()) @ w_up.t()
-            out[b, t0:t1] = (-torch.nn.functional.softplus(z)).view(t1 - t0, H, dk)
+            out[b, t0:t1] = (z if preact else -torch.nn.functional.softplus(z)).view(t1 - t0, H, dk).to(out_dtype)
+    return out
+
+
+def raw_inputs(name, device="cpu", seed=0):
+    """The raw projections of a named workload, for the fused-prologue entry
+    points: q_raw, k_raw ~ N(0,1) (not normalised), v, beta_raw ~ N(0,1)
+    (the beta logits), gate_raw = the gate pre-activation (fp32 N(0,1) +
+    gate_shift for a scalar gate; the rank-16 projection W_up (W_down x) in
+    the workload's dtype for KDA), h0."""
+    c = dict(CONFIGS[name])
+    B, T, H, dk, dv, dtype = c["B"], c["T"], c["H"], c["dk"], c["dv"], c["dtype"]
+    out = {"q_raw": randn((B, T, H, dk), seed, "q", device).to(dtype),
+           "k_raw": randn((B, T, H, dk), seed, "k", device).to(dtype),
+           "v": randn((B, T, H, dv), seed, "v", device).to(dtype),
+           "beta_raw": randn((B, T, H), seed, "beta", device)}
+    if c.get("gate") == "lowrank":
+        out["gate_raw"] = lowrank_gate(B, T, H, dk, seed, device, rank=c.get("rank", 16), preact=True,
+                                       out_dtype=dtype)
+    else:
+        out["gate_raw"] = randn((B, T, H), seed, "gate", device, mean=c.get("gate_shift", 0.0))
+    h0s = c.get("h0_std", 0.0)
+    out["h0"] = randn((B, H, dk, dv), seed, "h0", device, std=h0s) if h0s > 0 else None
     return out
 
 

@@ -1,0 +1,89 @@
+"""GPU parity of the fused-prologue forwards (gdn_fwd_fused, kda_fwd_fused)
+through the C ABI.
+
+They take the raw projections and apply the mixer's input activations inside
+the kernels (the FLA-style fusions the AMD ROCm blog "Pretraining hybrid
+LLMs with Primus" lists as throughput-critical, section "Recipe", Table 4):
+q, k rows L2-normalised (x / sqrt(sum x^2 + 1e-6)), beta = sigmoid,
+log a = -softplus.  Here the same activations are applied on the host in
+fp32 (then rounded to the dtype) and the oracle runs on those unfused
+inputs; the fused outputs must match it at the dtype's bar (1e-4 fp32,
+1e-2 bf16), and match the unfused GPU entry point on the same activated
+inputs.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_recurrent_token_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-2}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def rel(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+def activated(raw, dt):
+    """The unfused reference: the activations applied on the host in fp32."""
+    def l2(x):
+        x = x.float()
+        return (x / torch.sqrt((x * x).sum(-1, keepdim=True) + 1e-6)).to(dt)
+    return {"q": l2(raw["q_raw"]), "k": l2(raw["k_raw"]),
+            "beta": torch.sigmoid(raw["beta_raw"].float()),
+            "log_a": -torch.nn.functional.softplus(raw["gate_raw"].float())}
+
+
+CASES = [
+    # op, B, T, H, d_k, d_v, chunk, dtype, gate shift
+    ("gdn", 2, 300, 2, 128, 128, 64, torch.bfloat16, 2.0),
+    ("gdn", 1, 130, 2, 64, 32, 32, torch.float32, -6.0),
+    ("gdn", 1, 2560 - 3, 1, 128, 128, 64, torch.bfloat16, -6.0),  # segment-parallel scan
+    ("kda", 2, 300, 2, 128, 128, 64, torch.bfloat16, 0.0),
+    ("kda", 1, 130, 2, 64, 64, 32, torch.float32, -2.0),
+    ("kda", 1, 4096, 2, 128, 128, 64, torch.bfloat16, -4.0),  # segment-parallel scan
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}_T{c[2]}_C{c[6]}_{str(c[7])[6:]}" for c in CASES])
+def test_fused_forward(case):
+    import linear_recurrent_token_amd as L
+    op, B, T, H, dk, dv, chunk, dt, shift = case
+    say(f"[fused] {case}")
+    seed = 21
+    raw = {
+        # raw projections: not unit rows (scale 3), so the normalisation matters
+        "q_raw": synth.randn((B, T, H, dk), seed, "q", "cuda", std=3.0).to(dt),
+        "k_raw": synth.randn((B, T, H, dk), seed, "k", "cuda", std=3.0).to(dt),
+        "beta_raw": synth.randn((B, T, H), seed, "beta", "cuda"),
+        "gate_raw": (synth.randn((B, T, H, dk), seed, "gate", "cuda", mean=shift).to(dt) if op == "kda"
+                     else synth.randn((B, T, H), seed, "gate", "cuda", mean=shift)),
+    }
+    v = synth.randn((B, T, H, dv), seed, "v", "cuda").to(dt)
+    h0 = synth.randn((B, H, dk, dv), seed, "h0", "cuda", std=0.1)
+    f = L.gdn_fwd_fused if op == "gdn" else L.kda_fwd_fused
+    o, ht = f(raw["q_raw"], raw["k_raw"], v, raw["gate_raw"], raw["beta_raw"], h0, chunk=chunk)
+    ref = activated(raw, dt)
+    g = L.gdn_fwd if op == "gdn" else L.kda_fwd
+    ou, hu = g(ref["q"], ref["k"], v, ref["log_a"].contiguous(), ref["beta"], h0, chunk=chunk)
+    torch.cuda.synchronize()
+    c = lambda x: x.detach().cpu()
+    ro, rh = oracle.fwd(op, c(ref["q"]), c(ref["k"]), c(v), c(ref["log_a"].contiguous()), c(ref["beta"]), c(h0))
+    eo, eh = rel(o.float().cpu().numpy(), ro), rel(ht.cpu().numpy(), rh)
+    uo, uh = rel(o.float().cpu().numpy(), ou.float().cpu().numpy()), rel(ht.cpu().numpy(), hu.cpu().numpy())
+    say(f"  vs oracle o={eo:.2e} ht={eh:.2e}; vs unfused GPU o={uo:.2e} ht={uh:.2e}")
+    assert np.all(np.isfinite(o.float().cpu().numpy()))
+    assert eo <= TOL[dt] and eh <= TOL[dt], (eo, eh)
+    assert uo <= TOL[dt] and uh <= TOL[dt], (uo, uh)
