@@ -94,6 +94,8 @@ extern "C" {
 #define LRT_OP_GDN_FWD_VARLEN 5
 #define LRT_OP_GDN_BWD_VARLEN 6
 #define LRT_OP_KDA_FWD_VARLEN 7
+#define LRT_OP_KDA_BWD 8
+#define LRT_OP_KDA_BWD_VARLEN 9
 
 /*
  * Gated DeltaNet forward.  Writes o and (if not NULL) ht.
@@ -111,6 +113,24 @@ int gdn_fwd(const void* q, const void* k, const void* v, const float* log_a, con
  * dlog_a and dbeta are required.
  */
 int gdn_bwd(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+            const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv,
+            float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v,
+            int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Kimi Delta Attention backward: gradients of L = <do, o> + <dht, ht> for
+ * the forward of kda_fwd with the same arguments (the KDA mixer of the AMD
+ * ROCm blog "Pretraining hybrid LLMs with Primus", section "How hybrid
+ * models are defined in Primus", mixer list under Table 2; a pure-KDA
+ * model is among the models trained there, Table 1).  As gdn_bwd, except
+ * that the gate is per key dimension: log_a and dlog_a are [B, T, H, d_k]
+ * fp32.  The forward is recomputed internally.  dht may be NULL (zero);
+ * dh0 may be NULL (not written); dq, dk, dv, dlog_a and dbeta are
+ * required.  Workspace: lrt_workspace_bytes(LRT_OP_KDA_BWD, ...).  Exact
+ * for any finite log_a <= 0 (no factor of the decay that could overflow is
+ * ever formed).
+ */
+int kda_bwd(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
             const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv,
             float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v,
             int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);
@@ -236,7 +256,7 @@ int kda_fwd_fused(const void* q_raw, const void* k_raw, const void* v, const voi
  * Packed variable-length sequences (the packed batches of long-context
  * training, where many sequences of different lengths share one
  * [1, T, H, d] tensor; the 1M-context 7-MLA / 21-GDN hybrid guide packs
- * 20-160 sequences per 1M tokens).  gdn_fwd, kda_fwd and gdn_bwd for
+ * 20-160 sequences per 1M tokens).  gdn_fwd, kda_fwd, gdn_bwd and kda_bwd for
  * n_seq >= 1 sequences: sequence s spans tokens [cu_seqlens[s],
  * cu_seqlens[s + 1]) of q, k, v, log_a, beta, o (and do, dq, dk, dv,
  * dlog_a, dbeta), each laid out as [1, T, H, d] ([1, T, H] for gates;
@@ -258,6 +278,10 @@ int kda_fwd_varlen(const void* q, const void* k, const void* v, const float* log
                    const float* h0, void* o, float* ht, const int* cu_seqlens, int n_seq, int T, int H, int d_k,
                    int d_v, int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 int gdn_bwd_varlen(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                   const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dlog_a,
+                   float* dbeta, float* dh0, const int* cu_seqlens, int n_seq, int T, int H, int d_k, int d_v,
+                   int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+int kda_bwd_varlen(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
                    const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dlog_a,
                    float* dbeta, float* dh0, const int* cu_seqlens, int n_seq, int T, int H, int d_k, int d_v,
                    int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);

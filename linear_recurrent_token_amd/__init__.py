@@ -34,9 +34,10 @@ LIB_PATH = os.path.join(HERE, "liblrt.so")
 LRT_F32, LRT_BF16 = 0, 1
 OP_GDN_FWD, OP_GDN_BWD, OP_KDA_FWD, OP_SSD_FWD, OP_SSD_BWD = 0, 1, 2, 3, 4
 OP_GDN_FWD_VARLEN, OP_GDN_BWD_VARLEN, OP_KDA_FWD_VARLEN = 5, 6, 7
+OP_KDA_BWD, OP_KDA_BWD_VARLEN = 8, 9
 EXPORTS = ("gdn_fwd", "gdn_bwd", "gdn_fwd_train", "gdn_bwd_saved", "gdn_fwd_noalloc", "kda_fwd", "ssd_fwd",
            "ssd_bwd", "ssd_fwd_train", "ssd_bwd_saved", "gdn_fwd_varlen", "kda_fwd_varlen", "gdn_bwd_varlen",
-           "gdn_fwd_fused", "kda_fwd_fused",
+           "gdn_fwd_fused", "kda_fwd_fused", "kda_bwd", "kda_bwd_varlen",
            "lrt_workspace_bytes", "lrt_status_string", "lrt_profile_attach", "lrt_profile_count",
            "lrt_kernel_name")
 NOALLOC_MAX_BYTES = 64 << 20  # LRT_NOALLOC_MAX_BYTES
@@ -74,9 +75,11 @@ def lib():
         L.gdn_bwd_varlen.argtypes = [vp] * 15 + [ci] * 7 + [vp, sz, vp]
         L.gdn_fwd_fused.argtypes = [vp] * 8 + [ci] * 7 + [vp, sz, vp]
         L.kda_fwd_fused.argtypes = [vp] * 8 + [ci] * 7 + [vp, sz, vp]
+        L.kda_bwd.argtypes = [vp] * 14 + [ci] * 7 + [vp, sz, vp]
+        L.kda_bwd_varlen.argtypes = [vp] * 15 + [ci] * 7 + [vp, sz, vp]
         for f in ("gdn_fwd", "kda_fwd", "ssd_fwd", "gdn_bwd", "ssd_bwd", "gdn_fwd_train", "gdn_bwd_saved",
                   "ssd_fwd_train", "ssd_bwd_saved", "gdn_fwd_noalloc", "gdn_fwd_varlen", "kda_fwd_varlen",
-                  "gdn_bwd_varlen", "gdn_fwd_fused", "kda_fwd_fused"):
+                  "gdn_bwd_varlen", "gdn_fwd_fused", "kda_fwd_fused", "kda_bwd", "kda_bwd_varlen"):
             getattr(L, f).restype = ci
         L.lrt_workspace_bytes.argtypes = [ci] * 8
         L.lrt_workspace_bytes.restype = sz
@@ -303,31 +306,43 @@ def kda_fwd_varlen(q, k, v, log_a, beta, cu_seqlens, h0=None, chunk=64):
     return _fwd_varlen(lib().kda_fwd_varlen, OP_KDA_FWD_VARLEN, q, k, v, log_a, beta, cu_seqlens, h0, chunk, True)
 
 
-def gdn_bwd_varlen(q, k, v, log_a, beta, cu_seqlens, h0, do, dht=None, chunk=64, want_dh0=True):
-    """Gated DeltaNet backward over packed sequences -> (dq, dk, dv, dlog_a,
-    dbeta, dh0 [n_seq, H, d_k, d_v] or None)."""
+def _bwd_varlen(fn, op, kda, q, k, v, log_a, beta, cu_seqlens, h0, do, dht, chunk, want_dh0):
     n = _varlen_check(q, cu_seqlens)
     _, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
+    gshape = (1, T, H, dk) if kda else (1, T, H)
     for name, t, shp, ty in (("k", k, (1, T, H, dk), dt), ("v", v, (1, T, H, dv), dt),
-                             ("log_a", log_a, (1, T, H), torch.float32), ("beta", beta, (1, T, H), torch.float32),
+                             ("log_a", log_a, gshape, torch.float32), ("beta", beta, (1, T, H), torch.float32),
                              ("h0", h0, (n, H, dk, dv), torch.float32), ("do", do, (1, T, H, dv), dt),
                              ("dht", dht, (n, H, dk, dv), torch.float32)):
         _check(dev, dt, name, t, shp, ty)
     gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    gla = torch.empty((1, T, H), dtype=torch.float32, device=dev)
+    gla = torch.empty(gshape, dtype=torch.float32, device=dev)
     gb = torch.empty((1, T, H), dtype=torch.float32, device=dev)
     gh0 = torch.empty((n, H, dk, dv), dtype=torch.float32, device=dev) if want_dh0 else None
     code = _dtype_code(q)
-    ws, need = _workspace(OP_GDN_BWD_VARLEN, dev, n, T, H, dk, dv, chunk, code, None)
+    ws, need = _workspace(op, dev, n, T, H, dk, dv, chunk, code, None)
     with torch.cuda.device(dev):
-        rc = lib().gdn_bwd_varlen(_p(q), _p(k), _p(v), _p(log_a), _p(beta), _p(h0), _p(do), _p(dht), _p(gq), _p(gk),
-                                  _p(gv), _p(gla), _p(gb), _p(gh0), _p(cu_seqlens), n, T, H, dk, dv, chunk, code,
-                                  _p(ws), need, _stream(dev))
+        rc = fn(_p(q), _p(k), _p(v), _p(log_a), _p(beta), _p(h0), _p(do), _p(dht), _p(gq), _p(gk), _p(gv), _p(gla),
+                _p(gb), _p(gh0), _p(cu_seqlens), n, T, H, dk, dv, chunk, code, _p(ws), need, _stream(dev))
     if rc != 0:
-        raise LrtError("gdn_bwd_varlen", rc)
+        raise LrtError(fn.__name__, rc)
     return gq, gk, gv, gla, gb, gh0
+
+
+def gdn_bwd_varlen(q, k, v, log_a, beta, cu_seqlens, h0, do, dht=None, chunk=64, want_dh0=True):
+    """Gated DeltaNet backward over packed sequences -> (dq, dk, dv, dlog_a,
+    dbeta, dh0 [n_seq, H, d_k, d_v] or None)."""
+    return _bwd_varlen(lib().gdn_bwd_varlen, OP_GDN_BWD_VARLEN, False, q, k, v, log_a, beta, cu_seqlens, h0, do, dht,
+                       chunk, want_dh0)
+
+
+def kda_bwd_varlen(q, k, v, log_a, beta, cu_seqlens, h0, do, dht=None, chunk=64, want_dh0=True):
+    """Kimi Delta Attention backward over packed sequences -> (dq, dk, dv,
+    dlog_a [1, T, H, d_k], dbeta, dh0 [n_seq, H, d_k, d_v] or None)."""
+    return _bwd_varlen(lib().kda_bwd_varlen, OP_KDA_BWD_VARLEN, True, q, k, v, log_a, beta, cu_seqlens, h0, do, dht,
+                       chunk, want_dh0)
 
 
 def kda_fwd(q, k, v, log_a, beta, h0=None, chunk=64, o=None, ht=True, workspace=None):
@@ -345,6 +360,12 @@ def gdn_bwd(q, k, v, log_a, beta, h0, do, dht=None, chunk=64, want_dh0=True, wor
     return _bwd(True, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, workspace, out)
 
 
+def kda_bwd(q, k, v, log_a, beta, h0, do, dht=None, chunk=64, want_dh0=True, workspace=None, out=None):
+    """Kimi Delta Attention backward (log_a and dlog_a per key dimension,
+    [B, T, H, d_k]) -> (dq, dk, dv, dlog_a, dbeta, dh0 or None)."""
+    return _bwd(True, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, workspace, out, fn="kda_bwd")
+
+
 def ssd_bwd(q, k, v, log_a, h0, do, dht=None, chunk=64, want_dh0=True, workspace=None, out=None):
     """Mamba2 / SSD backward -> (dq, dk, dv, dlog_a, dh0 or None)."""
     if out is not None:
@@ -357,10 +378,12 @@ def _bwd(delta, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, workspace, o
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
+    kda = fn == "kda_bwd"
+    gshape = (B, T, H, dk) if kda else (B, T, H)
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU device")
     for name, t, shp, ty in (("k", k, (B, T, H, dk), dt), ("v", v, (B, T, H, dv), dt),
-                             ("log_a", log_a, (B, T, H), torch.float32),
+                             ("log_a", log_a, gshape, torch.float32),
                              ("beta", beta if delta else None, (B, T, H), torch.float32),
                              ("h0", h0, (B, H, dk, dv), torch.float32),
                              ("do", do, (B, T, H, dv), dt), ("dht", dht, (B, H, dk, dv), torch.float32)):
@@ -368,12 +391,12 @@ def _bwd(delta, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, workspace, o
     _check(dev, dt, "q", q, (B, T, H, dk), dt)
     if out is None:
         out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
-               torch.empty((B, T, H), dtype=torch.float32, device=dev),
+               torch.empty(gshape, dtype=torch.float32, device=dev),
                torch.empty((B, T, H), dtype=torch.float32, device=dev) if delta else None,
                torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dh0 else None)
     gq, gk, gv, gla, gb, gh0 = out
     code = _dtype_code(q)
-    op = OP_GDN_BWD if delta else OP_SSD_BWD
+    op = OP_KDA_BWD if kda else OP_GDN_BWD if delta else OP_SSD_BWD
     ws, need = _workspace(op, dev, B, T, H, dk, dv, chunk, code, workspace)
     with torch.cuda.device(dev):
         if delta:

@@ -62,7 +62,7 @@ void prof_after(void* stream) {
 static const char* const kKernelNames[kKNumKinds] = {
     "k_bwd_local", "k_dstate",   "k_grad",       "k_kda_prep", "k_state_copy", "k_wy",     "k_scan",
     "k_wy_bwd",    "k_scan_bwd", "k_scan_local", "k_carry",    "k_ssd_prep",   "k_ssd_fwd",
-    "k_varlen_plan"};
+    "k_varlen_plan", "k_kda_prep_bwd", "k_grad_kda"};
 
 // Queried on every call (a device attribute read; nothing is cached between
 // calls).
@@ -101,11 +101,14 @@ static int check_common(int B, int T, int H, int dk, int dv, int chunk, int dtyp
 
 // the base op of a workspace op code, and whether it is the packed form
 static int base_op(int op, bool* packed) {
-  *packed = op >= LRT_OP_GDN_FWD_VARLEN;
-  if (op == LRT_OP_GDN_FWD_VARLEN) return LRT_OP_GDN_FWD;
-  if (op == LRT_OP_GDN_BWD_VARLEN) return LRT_OP_GDN_BWD;
-  if (op == LRT_OP_KDA_FWD_VARLEN) return LRT_OP_KDA_FWD;
-  return op;
+  *packed = true;
+  switch (op) {
+    case LRT_OP_GDN_FWD_VARLEN: return LRT_OP_GDN_FWD;
+    case LRT_OP_GDN_BWD_VARLEN: return LRT_OP_GDN_BWD;
+    case LRT_OP_KDA_FWD_VARLEN: return LRT_OP_KDA_FWD;
+    case LRT_OP_KDA_BWD_VARLEN: return LRT_OP_KDA_BWD;
+    default: *packed = false; return op;
+  }
 }
 
 // The chunk the kernels of `op` run: the requested one, or the largest
@@ -118,6 +121,7 @@ static int run_chunk(int op, int dtype, int dk, int dv, int chunk) {
   if (op == LRT_OP_GDN_FWD) m = fwd_max_chunk(dtype, dk, dv);
   if (op == LRT_OP_KDA_FWD) m = kda_max_chunk(dtype, dk, dv);
   if (op == LRT_OP_GDN_BWD || op == LRT_OP_SSD_BWD) m = bwd_max_chunk(op, dtype, dk, dv);
+  if (op == LRT_OP_KDA_BWD) m = kda_bwd_max_chunk(dtype, dk, dv);
   return chunk < m ? chunk : m;
 }
 
@@ -127,7 +131,8 @@ static size_t ws_bytes(int op_code, int B, int T, int H, int dk, int dv, int chu
   const size_t esz = dtype == LRT_BF16 ? 2 : 4;
   const int c = run_chunk(op, dtype, dk, dv, chunk);
   size_t b = fwd_ws_layout(op, B, T, H, dk, dv, c, esz, nullptr, packed).bytes;
-  if (op == LRT_OP_GDN_BWD || op == LRT_OP_SSD_BWD) b += bwd_ws_extra(op, B, T, H, dk, dv, c, esz, packed);
+  if (op == LRT_OP_GDN_BWD || op == LRT_OP_SSD_BWD || op == LRT_OP_KDA_BWD)
+    b += bwd_ws_extra(op, B, T, H, dk, dv, c, esz, packed);
   return b < 256 ? 256 : b;
 }
 
@@ -178,7 +183,7 @@ static int bwd_entry(int variant, const void* q, const void* k, const void* v, c
   if (rc) return rc;
   if (packed && !cu) return LRT_ERR_NULL;
   if (packed && !aligned4(cu)) return LRT_ERR_ALIGN;
-  const bool delta = variant == kVarGDN;
+  const bool delta = variant != kVarSSD;
   if (T > 0 && (!q || !k || !v || !log_a || !d_o || !dq || !dk || !dv || !dlog_a || (delta && (!beta || !dbeta))))
     return LRT_ERR_NULL;
   const void* vec[] = {q, k, v, d_o, dq, dk, dv, workspace};
@@ -187,13 +192,13 @@ static int bwd_entry(int variant, const void* q, const void* k, const void* v, c
   const void* sca[] = {log_a, beta, h0, dht, dlog_a, dbeta, dh0};
   for (const void* p : sca)
     if (p && !aligned4(p)) return LRT_ERR_ALIGN;
-  const int op = delta ? LRT_OP_GDN_BWD : LRT_OP_SSD_BWD;
-  const int ws_op = packed ? LRT_OP_GDN_BWD_VARLEN : op;
+  const int op = variant == kVarGDN ? LRT_OP_GDN_BWD : variant == kVarKDA ? LRT_OP_KDA_BWD : LRT_OP_SSD_BWD;
+  const int ws_op = !packed ? op : op == LRT_OP_GDN_BWD ? LRT_OP_GDN_BWD_VARLEN : LRT_OP_KDA_BWD_VARLEN;
   if (!workspace || workspace_bytes < ws_bytes(ws_op, B, T, H, d_k, d_v, chunk, dtype)) return LRT_ERR_WORKSPACE;
   if (T == 0) return launch_empty(dht, dh0, B, H, d_k, d_v, stream);
   BwdArgs a{q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0,
             B, T, H, d_k, d_v, run_chunk(op, dtype, d_k, d_v, chunk), dtype, workspace, stream, packed ? cu : nullptr};
-  rc = delta ? bwd_gdn(a, saved) : bwd_ssd(a, saved);
+  rc = variant == kVarGDN ? bwd_gdn(a, saved) : variant == kVarKDA ? bwd_kda(a) : bwd_ssd(a, saved);
   return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
 }
 
@@ -245,6 +250,14 @@ int gdn_bwd(const void* q, const void* k, const void* v, const float* log_a, con
                    chunk, dtype, workspace, workspace_bytes, stream);
 }
 
+int kda_bwd(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+            const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv,
+            float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v, int chunk,
+            int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_entry(kVarKDA, q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0, B, T, H, d_k, d_v,
+                   chunk, dtype, workspace, workspace_bytes, stream);
+}
+
 int gdn_fwd_train(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
                   const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk,
                   int dtype, void* workspace, size_t workspace_bytes, void* stream) {
@@ -283,7 +296,7 @@ int ssd_bwd(const void* q, const void* k, const void* v, const float* log_a, con
 }
 
 size_t lrt_workspace_bytes(int op, int B, int T, int H, int d_k, int d_v, int chunk, int dtype) {
-  if (op < LRT_OP_GDN_FWD || op > LRT_OP_KDA_FWD_VARLEN) return (size_t)-1;
+  if (op < LRT_OP_GDN_FWD || op > LRT_OP_KDA_BWD_VARLEN) return (size_t)-1;
   bool packed = false;
   base_op(op, &packed);
   if (check_common(B, T, H, d_k, d_v, chunk, dtype, packed) != LRT_OK) return (size_t)-1;
@@ -323,6 +336,13 @@ int gdn_bwd_varlen(const void* q, const void* k, const void* v, const float* log
                    float* dbeta, float* dh0, const int* cu_seqlens, int n_seq, int T, int H, int d_k, int d_v,
                    int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_entry(kVarGDN, q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0, n_seq, T, H, d_k,
+                   d_v, chunk, dtype, workspace, workspace_bytes, stream, false, cu_seqlens, true);
+}
+int kda_bwd_varlen(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                   const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dlog_a,
+                   float* dbeta, float* dh0, const int* cu_seqlens, int n_seq, int T, int H, int d_k, int d_v,
+                   int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_entry(kVarKDA, q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0, n_seq, T, H, d_k,
                    d_v, chunk, dtype, workspace, workspace_bytes, stream, false, cu_seqlens, true);
 }
 int lrt_profile_attach(void** events, int* kinds, int n_kernels) {

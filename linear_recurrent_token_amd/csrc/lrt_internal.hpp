@@ -43,15 +43,15 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Per-chunk workspace tiles, chunk-major per (b, h); each op reserves only
 // the tiles its kernels use (lrt_workspace_bytes op codes):
-//   W   [C][dk]   E   W = Tinv diag(b gamma) K           GDN_FWD, KDA_FWD, GDN_BWD
-//   Up  [dv][C]   E   U' = Tinv diag(b) V (tile order)   GDN_FWD, KDA_FWD, GDN_BWD; SSD_BWD: dU_local^T
-//   Kt  [dk][C]   E   Ktil^T, Ktil_j = e^(G_C - G_j) k_j KDA_FWD
-//   U   [dv][C]   E   U^T = (U' - W Hn)^T                GDN_BWD; SSD_BWD: V^T
-//   S   [dv][dk]  E   S_n = Hn^T, the chunk-start state  GDN_BWD, SSD_BWD
+//   W   [C][dk]   E   W = Tinv diag(b gamma) K           GDN_FWD, KDA_FWD, GDN_BWD, KDA_BWD
+//   Up  [dv][C]   E   U' = Tinv diag(b) V (tile order)   GDN_FWD, KDA_FWD, GDN_BWD, KDA_BWD; SSD_BWD: dU_local^T
+//   Kt  [dk][C]   E   Ktil^T, Ktil_j = e^(G_C - G_j) k_j KDA_FWD, KDA_BWD
+//   U   [dv][C]   E   U^T = (U' - W Hn)^T                GDN_BWD, KDA_BWD; SSD_BWD: V^T
+//   S   [dv][dk]  E   S_n = Hn^T, the chunk-start state  GDN_BWD, SSD_BWD, KDA_BWD
 //   G   [C]       f32 within-chunk inclusive cumsum of log a   GDN_FWD, GDN_BWD, SSD_BWD
-//   GC  [dk]      f32 per-key-dim chunk log-decay        KDA_FWD
-//   Qg  [C][dk]   E   Q o e^G                            KDA_FWD
-//   P   [C][C]    E   (Q K^T) o Gamma (SSD_BWD: P^T)     GDN_FWD, KDA_FWD, GDN_BWD, SSD_BWD
+//   GC  [dk]      f32 per-key-dim chunk log-decay        KDA_FWD, KDA_BWD
+//   Qg  [C][dk]   E   Q o e^G                            KDA_FWD, KDA_BWD
+//   P   [C][C]    E   (Q K^T) o Gamma (SSD_BWD: P^T)     GDN_FWD, KDA_FWD, GDN_BWD, SSD_BWD, KDA_BWD
 //   SegLoc   [b*h][seg][dk][dv+dk] f32  end state of each segment from zero, and its map
 //   SegStart [b*h][seg][dk][dv]    f32  true start state of each segment
 //                                       (segmented scans: GDN_FWD, KDA_FWD, GDN_BWD)
@@ -100,7 +100,7 @@ inline FwdWs fwd_ws_layout(int op, int B, int T, int H, int dk, int dv, int C, s
   const size_t N = (size_t)(T + C - 1) / C;
   const size_t tiles = ws_tiles(B, T, H, C, packed);
   const bool gf = op == LRT_OP_GDN_FWD, kf = op == LRT_OP_KDA_FWD, gb = op == LRT_OP_GDN_BWD,
-             sb = op == LRT_OP_SSD_BWD;
+             sb = op == LRT_OP_SSD_BWD, kb = op == LRT_OP_KDA_BWD;
   size_t off = 0;
   FwdWs w;
   char* p = (char*)base;
@@ -110,15 +110,15 @@ inline FwdWs fwd_ws_layout(int op, int B, int T, int H, int dk, int dv, int C, s
     off += align256(bytes);
     return r;
   };
-  w.W = take(gf || kf || gb, tiles * C * dk * esz);
-  w.Up = take(gf || kf || gb || sb, tiles * dv * C * esz);
-  w.Kt = take(kf, tiles * dk * C * esz);
-  w.U = take(gb || sb, tiles * dv * C * esz);
-  w.S = take(gb || sb, tiles * dv * dk * esz);
+  w.W = take(gf || kf || gb || kb, tiles * C * dk * esz);
+  w.Up = take(gf || kf || gb || sb || kb, tiles * dv * C * esz);
+  w.Kt = take(kf || kb, tiles * dk * C * esz);
+  w.U = take(gb || sb || kb, tiles * dv * C * esz);
+  w.S = take(gb || sb || kb, tiles * dv * dk * esz);
   w.G = (float*)take(gf || gb || sb, tiles * C * sizeof(float));
-  w.GC = (float*)take(kf, tiles * dk * sizeof(float));
-  w.Qg = take(kf, tiles * C * dk * esz);
-  w.P = take(gf || kf || gb || sb, tiles * C * C * esz);
+  w.GC = (float*)take(kf || kb, tiles * dk * sizeof(float));
+  w.Qg = take(kf || kb, tiles * C * dk * esz);
+  w.P = take(gf || kf || gb || sb || kb, tiles * C * C * esz);
   const int nseg = (gf || kf || gb) && !packed ? scan_plan(B, H, dk, dv, (int)N).nseg : 1;
   w.SegLoc = (float*)take(nseg > 1, (size_t)B * H * nseg * dk * (dv + dk) * sizeof(float));
   w.SegStart = (float*)take(nseg > 1, (size_t)B * H * nseg * dk * dv * sizeof(float));
@@ -127,6 +127,43 @@ inline FwdWs fwd_ws_layout(int op, int B, int T, int H, int dk, int dv, int C, s
   w.co = (int*)take(packed, (size_t)(B + 1) * sizeof(int));
   w.bytes = off;
   return w;
+}
+
+// Backward-only workspace tiles, after the forward's (chunk-major per (b, h)):
+//   T   [C][C]   E    Tinv
+//   dS  [dv][dk] E    dH'^T, gradient of each chunk's end state
+//   dU  [dv][C]  E    dU^T
+// dU_local reuses the forward's U' tiles (dead once the state pass has run).
+struct BwdWs {
+  FwdWs f;
+  void *T, *dS, *dU;
+  size_t bytes;
+};
+
+// op: LRT_OP_GDN_BWD (also the Gated DeltaNet training forward),
+// LRT_OP_KDA_BWD, or LRT_OP_SSD_BWD (also the Mamba2 training forward; no Tinv)
+inline BwdWs bwd_ws_layout(int op, int B, int T, int H, int dk, int dv, int C, size_t esz, void* base,
+                           bool packed = false) {
+  BwdWs w;
+  w.f = fwd_ws_layout(op, B, T, H, dk, dv, C, esz, base, packed);
+  const size_t tiles = ws_tiles(B, T, H, C, packed);
+  size_t off = w.f.bytes;
+  char* p = (char*)base;
+  auto take = [&](size_t bytes) {
+    void* r = p ? (void*)(p + off) : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  w.T = op == LRT_OP_GDN_BWD || op == LRT_OP_KDA_BWD ? take(tiles * C * C * esz) : nullptr;
+  w.dS = take(tiles * dv * dk * esz);
+  w.dU = take(tiles * dv * C * esz);
+  w.bytes = off;
+  return w;
+}
+
+inline size_t bwd_ws_extra(int op, int B, int T, int H, int dk, int dv, int C, size_t esz, bool packed = false) {
+  const BwdWs w = bwd_ws_layout(op, B, T, H, dk, dv, C, esz, nullptr, packed);
+  return w.bytes - w.f.bytes;
 }
 
 // The kernels' view of the sequences (the packed layout's tables live in
@@ -153,6 +190,8 @@ enum KernelKind {
   kKSsdPrep,
   kKSsdFwd,
   kKVarlenPlan,
+  kKKdaPrepBwd,
+  kKGradKda,
   kKNumKinds
 };
 // Bracket one launch with the timing hook's events (no-ops unless attached).
@@ -194,8 +233,7 @@ int fwd_kda(const FwdArgs& a);
 int bwd_gdn(const BwdArgs& a, bool saved);
 int fwd_train(const FwdArgs& a);  // GDN or SSD by a.variant
 int bwd_ssd(const BwdArgs& a, bool saved);
-// workspace bytes the backward needs beyond the forward's tiles
-size_t bwd_ws_extra(int op, int B, int T, int H, int dk, int dv, int C, size_t esz, bool packed = false);
+int bwd_kda(const BwdArgs& a);
 
 // The largest chunk in {16, 32, 64} at which every kernel of `op` (an
 // LRT_OP_* code; the training forwards count as the backward's op) fits in
@@ -205,5 +243,6 @@ size_t bwd_ws_extra(int op, int B, int T, int H, int dk, int dv, int C, size_t e
 int fwd_max_chunk(int dtype, int dk, int dv);  // GDN_FWD, SSD_FWD
 int kda_max_chunk(int dtype, int dk, int dv);
 int bwd_max_chunk(int op, int dtype, int dk, int dv);  // GDN_BWD, SSD_BWD
+int kda_bwd_max_chunk(int dtype, int dk, int dv);
 
 }  // namespace lrt

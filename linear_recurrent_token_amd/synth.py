@@ -39,6 +39,10 @@ CONFIGS = {
     # with the Mamba2 forward's distributions
     "ssd_train_bf16_2k": dict(op="ssd_fwd_bwd", B=16, T=2048, H=8, dk=128, dv=128, chunk=64,
                               dtype=torch.bfloat16, gate_shift=0.0, h0_std=0.0),
+    # Kimi Delta Attention training step (forward + backward) at the 2048-token
+    # pretraining shape, the rank-16 low-rank per-dimension gate
+    "kda_train_bf16_2k": dict(op="kda_fwd_bwd", B=16, T=2048, H=8, dk=128, dv=128, chunk=64,
+                              dtype=torch.bfloat16, gate="lowrank", rank=16, h0_std=0.1),
     # Kimi Delta Attention forward over one 1M-token sequence, 16 heads
     "kda_bf16_1m": dict(op="kda_fwd", B=1, T=1 << 20, H=16, dk=128, dv=128, chunk=64,
                         dtype=torch.bfloat16, gate="lowrank", rank=16, h0_std=0.0),

@@ -203,8 +203,8 @@ def test_ssd_backward_validation(L):
 def test_workspace_bytes(L):
     lib = L.lib()
     bad = ctypes.c_size_t(-1).value
-    assert lib.lrt_workspace_bytes(9, 1, 64, 2, 16, 16, 16, 0) == bad
-    assert lib.lrt_workspace_bytes(8, 1, 64, 2, 16, 16, 16, 0) == bad
+    assert lib.lrt_workspace_bytes(11, 1, 64, 2, 16, 16, 16, 0) == bad
+    assert lib.lrt_workspace_bytes(10, 1, 64, 2, 16, 16, 16, 0) == bad
     assert lib.lrt_workspace_bytes(-1, 1, 64, 2, 16, 16, 16, 0) == bad
     assert lib.lrt_workspace_bytes(0, 1, 64, 2, 16, 16, 17, 0) == bad
     for op in range(5):
@@ -213,13 +213,14 @@ def test_workspace_bytes(L):
     # grows with T and is never zero
     assert L.workspace_bytes(0, 1, 0, 1, 16, 16, 16, 0) > 0
     assert L.workspace_bytes(0, 1, 4096, 1, 16, 16, 16, 0) > L.workspace_bytes(0, 1, 64, 1, 16, 16, 16, 0)
-    # the backward needs more than the forward
+    # the backward needs more than the forward (Gated DeltaNet, KDA)
     assert L.workspace_bytes(1, 2, 256, 2, 64, 64, 64, 1) > L.workspace_bytes(0, 2, 256, 2, 64, 64, 64, 1)
+    assert L.workspace_bytes(8, 2, 256, 2, 64, 64, 64, 1) > L.workspace_bytes(2, 2, 256, 2, 64, 64, 64, 1)
     # the fused Mamba2 forward needs none beyond the minimum
     assert L.workspace_bytes(3, 16, 2048, 8, 128, 128, 64, 1) == 256
     # every dtype and size of the supported set has a workspace (fp32 at
     # d = 128 runs a smaller chunk: its workspace is sized for that chunk)
-    for op in range(8):
+    for op in range(10):
         for dt in (0, 1):
             for dk in (16, 32, 64, 128):
                 for dv in (16, 32, 64, 128):

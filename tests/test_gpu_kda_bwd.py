@@ -1,0 +1,186 @@
+"""GPU parity of kda_bwd (and kda_bwd_varlen) against the fp64 oracle's
+back-propagation through time of the KDA recurrence, through the C ABI.
+
+KDA's gate is one log-decay per key dimension (the KDA mixer of the AMD
+ROCm blog "Pretraining hybrid LLMs with Primus", mixer list under Table 2;
+a pure-KDA model is among the models trained there, Table 1), so dlog_a is
+[B, T, H, d_k].  Bar: max|got - oracle| / max|oracle| per gradient tensor
+(dq, dk, dv, dlog_a, dbeta, dh0) <= 1e-4 for fp32 inputs and <= 1e-2 for
+bf16 inputs.  The gate cases span slow decay (log a ~ -0.0025 per token),
+the default, strong per-dimension decay (the chunk's total decay far past
+e^-60, so no factor e^(-G) of a whole chunk would be representable) and
+extreme decay (e^(G_i - G_j) underflows inside one 16-token block).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_recurrent_token_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-2}
+NAMES = ("dq", "dk", "dv", "dlog_a", "dbeta", "dh0")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def rel(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+def cpu(x):
+    return None if x is None else x.detach().cpu()
+
+
+def errors(got, ref):
+    errs = {}
+    for name, g, r in zip(NAMES, got, ref):
+        g = g.float().cpu().numpy()
+        assert np.all(np.isfinite(g)), name
+        errs[name] = rel(g, r)
+    return errs
+
+
+def oracle_bwd(inp):
+    q, k, v, la, beta, h0, do, dht = (inp.get(n) for n in ("q", "k", "v", "log_a", "beta", "h0", "do", "dht"))
+    return oracle.bwd("kda", cpu(q), cpu(k), cpu(v), cpu(la), cpu(beta), cpu(h0), cpu(do), cpu(dht))
+
+
+def run(inp, chunk):
+    import linear_recurrent_token_amd as L
+    q, k, v, la, beta, h0, do, dht = (inp.get(n) for n in ("q", "k", "v", "log_a", "beta", "h0", "do", "dht"))
+    got = L.kda_bwd(q, k, v, la, beta, h0, do, dht, chunk=chunk)
+    torch.cuda.synchronize()
+    return got
+
+
+CASES = [
+    # name, B, T, H, dk, dv, chunk, dtype, gate, gate_shift, h0_std, dht_std
+    ("fp32_tiny_C16", 1, 64, 2, 16, 16, 16, torch.float32, "perdim", 0.0, 0.0, 0.0),
+    ("fp32_T77_C32_h0_dht", 2, 77, 2, 32, 64, 32, torch.float32, "perdim", 0.0, 0.1, 0.1),
+    ("fp32_d64_C64_strong", 1, 150, 2, 64, 64, 64, torch.float32, "perdim", 2.0, 0.1, 0.1),
+    ("fp32_d64_C64_slow", 2, 130, 2, 64, 64, 64, torch.float32, "perdim", -6.0, 0.1, 0.1),
+    # fp32 at d = 128 with chunk 64 requested: the kernels run the largest
+    # chunk whose fp32 operands fit in LDS
+    ("fp32_d128_C64", 1, 100, 2, 128, 128, 64, torch.float32, "perdim", 0.0, 0.1, 0.1),
+    ("bf16_T61_C16", 2, 61, 3, 64, 64, 16, torch.bfloat16, "perdim", 0.0, 0.1, 0.1),
+    ("bf16_C32", 1, 200, 2, 128, 128, 32, torch.bfloat16, "perdim", 0.0, 0.1, 0.1),
+    ("bf16_C64_T300", 2, 300, 2, 128, 128, 64, torch.bfloat16, "perdim", 0.0, 0.1, 0.1),
+    ("bf16_C64_strong", 1, 256, 2, 128, 128, 64, torch.bfloat16, "perdim", 3.0, 0.1, 0.1),
+    ("bf16_C64_extreme", 1, 200, 2, 128, 128, 64, torch.bfloat16, "perdim", 8.0, 0.1, 0.1),
+    ("bf16_C64_slow", 1, 256, 2, 128, 128, 64, torch.bfloat16, "perdim", -6.0, 0.1, 0.1),
+    ("bf16_C64_lowrank", 2, 192, 2, 128, 128, 64, torch.bfloat16, "lowrank", 0.0, 0.1, 0.0),
+    ("bf16_d16_dv32", 1, 100, 2, 16, 32, 16, torch.bfloat16, "perdim", 0.0, 0.1, 0.1),
+    ("bf16_dk32_dv128_C32", 1, 100, 2, 32, 128, 32, torch.bfloat16, "perdim", 0.0, 0.1, 0.1),
+    ("bf16_dk128_dv64_C64", 1, 130, 2, 128, 64, 64, torch.bfloat16, "perdim", 1.0, 0.1, 0.1),
+    # long sequence, slow gates: the state carry spans 64 chunks both ways
+    ("bf16_long_slow_C64", 1, 4096 - 7, 2, 128, 128, 64, torch.bfloat16, "perdim", -6.0, 0.1, 0.1),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_kda_bwd(case):
+    name, B, T, H, dk, dv, chunk, dt, gate, shift, h0s, dhs = case
+    say(f"[kda_bwd] {name}")
+    inp = synth.make_inputs("kda_fwd_bwd", B, T, H, dk, dv, dtype=dt, seed=3, device="cuda", gate=gate,
+                            gate_shift=shift, h0_std=h0s, dht_std=dhs)
+    got = run(inp, chunk)
+    errs = errors(got, oracle_bwd(inp))
+    say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if e > TOL[dt]}
+    assert not bad, bad
+
+
+def test_kda_bwd_is_deterministic():
+    """Every reduction is summed in a fixed order: two calls are bitwise equal."""
+    inp = synth.make_inputs("kda_fwd_bwd", 2, 300, 2, 128, 128, dtype=torch.bfloat16, seed=4, device="cuda",
+                            gate="perdim", h0_std=0.1, dht_std=0.1)
+    a = run(inp, 64)
+    b = run(inp, 64)
+    for n, x, y in zip(NAMES, a, b):
+        assert torch.equal(x, y), n
+
+
+def test_kda_bwd_uniform_gate_equals_gdn_bwd():
+    """With the same log-decay on every key dimension KDA is Gated DeltaNet:
+    dq, dk, dv, dbeta, dh0 agree with gdn_bwd and dlog_a summed over the key
+    dimensions is GDN's dlog_a (both at the fp32 bar)."""
+    import linear_recurrent_token_amd as L
+    inp = synth.make_inputs("kda_fwd_bwd", 1, 130, 2, 64, 64, dtype=torch.float32, seed=5, device="cuda",
+                            gate="uniform", h0_std=0.1, dht_std=0.1)
+    q, k, v, la, beta, h0, do, dht = (inp.get(n) for n in ("q", "k", "v", "log_a", "beta", "h0", "do", "dht"))
+    gk = L.kda_bwd(q, k, v, la, beta, h0, do, dht, chunk=32)
+    gg = L.gdn_bwd(q, k, v, la[..., 0].contiguous(), beta, h0, do, dht, chunk=32)
+    torch.cuda.synchronize()
+    for n, x, y in zip(NAMES, gk, gg):
+        x = x.sum(-1) if n == "dlog_a" else x
+        e = rel(x.cpu().numpy(), y.cpu().numpy())
+        assert e <= 1e-4, (n, e)
+
+
+def test_kda_training_step_workload():
+    """The KDA training-step workload at full size (B=16, T=2048, H=8,
+    d=128, chunk 64, bf16, rank-16 low-rank gate), every gradient element
+    against the oracle."""
+    say("[kda_bwd] workload kda_train_bf16_2k")
+    inp = synth.config_inputs("kda_train_bf16_2k", device="cuda", dht_std=0.1)
+    got = run(inp, 64)
+    errs = errors(got, oracle_bwd(inp))
+    say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if e > TOL[torch.bfloat16]}
+    assert not bad, bad
+
+
+VARLEN = [
+    # lengths, H, d_k, d_v, chunk, dtype, gate_shift
+    ([130, 7, 64, 1, 300, 0, 65], 2, 128, 128, 64, torch.bfloat16, 0.0),
+    ([50, 16, 3, 97], 2, 64, 32, 16, torch.float32, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=[f"{len(c[0])}seq_C{c[4]}_{str(c[5])[6:]}" for c in VARLEN])
+def test_kda_bwd_varlen(case):
+    """Packed sequences: each sequence's gradients equal the dense kda_bwd on
+    that sequence alone (bitwise) and the oracle at the dtype's bar."""
+    import linear_recurrent_token_amd as L
+    lens, H, dk, dv, chunk, dt, shift = case
+    say(f"[kda_bwd_varlen] {case}")
+    T = int(sum(lens))
+    n = len(lens)
+    inp = synth.make_inputs("kda_fwd_bwd", 1, T, H, dk, dv, dtype=dt, seed=6, device="cuda", gate="perdim",
+                            gate_shift=shift)
+    h0 = synth.randn((n, H, dk, dv), 6, "h0", "cuda", std=0.1)
+    dht = synth.randn((n, H, dk, dv), 6, "dht", "cuda", std=0.1)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
+    q, k, v, la, beta, do = (inp[x] for x in ("q", "k", "v", "log_a", "beta", "do"))
+    g = L.kda_bwd_varlen(q, k, v, la, beta, cu, h0, do, dht, chunk=chunk)
+    torch.cuda.synchronize()
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    worst = {x: 0.0 for x in NAMES}
+    sl = lambda x, a, b: x[:, a:b].contiguous()
+    for s, (a, b) in enumerate(zip(starts[:-1], starts[1:])):
+        hs, ds = h0[s:s + 1].contiguous(), dht[s:s + 1].contiguous()
+        gd = L.kda_bwd(sl(q, a, b), sl(k, a, b), sl(v, a, b), sl(la, a, b), sl(beta, a, b), hs, sl(do, a, b), ds,
+                       chunk=chunk)
+        torch.cuda.synchronize()
+        for name, x, y in zip(NAMES, g, gd):
+            part = x[s:s + 1] if name == "dh0" else x[:, a:b]
+            assert torch.equal(part, y), (name, s, a, b)
+        if b > a:
+            ref = oracle.bwd("kda", cpu(sl(q, a, b)), cpu(sl(k, a, b)), cpu(sl(v, a, b)), cpu(sl(la, a, b)),
+                             cpu(sl(beta, a, b)), cpu(hs), cpu(sl(do, a, b)), cpu(ds))
+            for name, x, r in zip(NAMES, g, ref):
+                part = x[s:s + 1] if name == "dh0" else x[:, a:b]
+                worst[name] = max(worst[name], rel(part.float().cpu().numpy(), r))
+    say("  worst per-sequence " + " ".join(f"{x}={e:.2e}" for x, e in worst.items()))
+    bad = {x: e for x, e in worst.items() if e > TOL[dt]}
+    assert not bad, bad
