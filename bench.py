@@ -56,6 +56,8 @@ WORKLOADS = {
     "ssd_train_recompute_bf16_2k": ("SSD (Mamba2 case) chunked fwd+bwd (backward recomputes) tokens/s, "
                                     "B=16 T=2048 H=8 d=128", "ssd_fwd + ssd_bwd"),
     "kda_bf16_1m": ("KDA chunked fwd tokens/s, B=1 T=2^20 H=16 d=128", "kda_fwd"),
+    # the KDA training step (the backward recomputes the forward)
+    "kda_train_bf16_2k": ("KDA chunked fwd+bwd tokens/s, B=16 T=2048 H=8 d=128", "kda_fwd + kda_bwd"),
     # the forwards on the raw projections, activations fused into the kernels
     # (the line also times the unfused pipeline: torch activations + the plain forward)
     "gdn_fused_bf16_2k": ("GDN chunked fwd, fused prologue (raw q/k/beta/gate in) tokens/s, B=16 T=2048 H=8 d=128",
@@ -69,6 +71,7 @@ CONFIG_OF = {"gdn_train_recompute_bf16_2k": "gdn_train_bf16_2k", "ssd_train_reco
 
 # the library kernels of each pass (the forward's and the backward's share of a step)
 FWD_KERNELS = {"k_wy", "k_scan", "k_scan_local", "k_carry", "k_ssd_fwd", "k_kda_prep", "k_state_copy"}
+# (k_kda_prep_bwd is the backward's recompute of the KDA forward pass)
 
 
 def parse():
@@ -143,7 +146,9 @@ def method_model(op, c, has_h0, has_dht, esz=2):
     fwd_f = 2 * C * (dk + dv) + 4 * dk * dv if ssd else 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv
     out = {"fwd": (fwd_b * n_th + (int(has_h0) + 1) * st * n_bh, fwd_f * n_th)}
     if "bwd" in op:
-        bwd_b = (2 * dk + 2 * dv) * e + 4 + beta + (2 * dk + dv) * e + 4 + beta
+        # q, k, v, do, log a, beta in; dq, dk, dv, dlog_a, dbeta out (KDA: log a and dlog_a per key dim)
+        g = 4 * dk if kda else 4
+        bwd_b = (2 * dk + 2 * dv) * e + g + beta + (2 * dk + dv) * e + g + beta
         if ssd:
             bwd_f = 4 * C * dk + 4 * C * dv + 8 * dk * dv
         else:
@@ -263,9 +268,10 @@ def main():
     code = L.LRT_BF16
     opc = {"gdn_fwd + gdn_bwd": L.OP_GDN_BWD, "gdn_fwd_train + gdn_bwd_saved": L.OP_GDN_BWD, "gdn_fwd": L.OP_GDN_FWD,
            "ssd_fwd": L.OP_SSD_FWD, "ssd_fwd + ssd_bwd": L.OP_SSD_BWD, "ssd_fwd_train + ssd_bwd_saved": L.OP_SSD_BWD,
-           "kda_fwd": L.OP_KDA_FWD, "gdn_fwd_fused": L.OP_GDN_FWD, "kda_fwd_fused": L.OP_KDA_FWD}[op]
-    ws_bytes = max(L.workspace_bytes(L.OP_GDN_FWD, B, T, H, dk, dv, C, code),
-                   L.workspace_bytes(opc, B, T, H, dk, dv, C, code))
+           "kda_fwd": L.OP_KDA_FWD, "gdn_fwd_fused": L.OP_GDN_FWD, "kda_fwd_fused": L.OP_KDA_FWD,
+           "kda_fwd + kda_bwd": L.OP_KDA_BWD}[op]
+    ws_bytes = max(L.workspace_bytes(L.OP_KDA_FWD if op.startswith("kda") else L.OP_GDN_FWD, B, T, H, dk, dv, C,
+                                     code), L.workspace_bytes(opc, B, T, H, dk, dv, C, code))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
     ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
@@ -274,7 +280,7 @@ def main():
         grads = (torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
                  torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
                  torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev),
-                 torch.empty((B, T, H), dtype=torch.float32, device=dev),
+                 torch.empty((B, T, H, dk) if op.startswith("kda") else (B, T, H), dtype=torch.float32, device=dev),
                  torch.empty((B, T, H), dtype=torch.float32, device=dev),
                  torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev))
         if op.startswith("ssd"):
@@ -315,7 +321,7 @@ def main():
             return
         if op.startswith("ssd"):
             L.ssd_fwd(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), chunk=C, o=o, ht=ht, workspace=ws)
-        elif op == "kda_fwd":
+        elif op.startswith("kda"):
             L.kda_fwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), chunk=C, o=o, ht=ht,
                       workspace=ws)
         else:
@@ -324,6 +330,9 @@ def main():
         if grads is not None and op.startswith("ssd"):
             L.ssd_bwd(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), s["do"], s.get("dht"), chunk=C, workspace=ws,
                       out=grads)
+        elif grads is not None and op.startswith("kda"):
+            L.kda_bwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), s["do"], s.get("dht"),
+                      chunk=C, workspace=ws, out=grads)
         elif grads is not None:
             L.gdn_bwd(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), s["do"], s.get("dht"),
                       chunk=C, workspace=ws, out=grads)

@@ -30,9 +30,11 @@
 // the outer factors scale operand rows (Kend_j = k_j e^(G_s - G_j),
 // Qst_i = q_i e^(G_i - G_r)) or the product's output, the middle one is a
 // per-dimension scale of one 16-token block product on MFMA, and every
-// exponent is <= 0 -- nothing overflows for any finite log a <= 0.  Pairs
-// inside a diagonal block are summed element by element with the exact
-// exponent difference.
+// exponent is <= 0 -- nothing overflows for any finite log a <= 0.  While no
+// block decays by more than e^60 in any dimension, r moves to the last row
+// of block si itself (the first factor then in [1, e^60]) and the diagonal
+// blocks (i, j in one block) are block products too; past that their pairs
+// are summed element by element with the exact exponent difference.
 //
 // Kernels, in stream order: k_kda_prep (the forward's chunk-parallel pass,
 // also writing T), k_scan (KDA, backward mode: chunk-start states S_n and U),
@@ -67,7 +69,8 @@ struct KdaGradLds {
   static constexpr size_t PCOL = PDB + (size_t)NW * C * 4;   // [NB][d_k] per-block sums of k o Kt-part
   static constexpr size_t PDEC = PCOL + (size_t)NB * DK * 4; // [NW][d_k] partials of rowsum(dH' o Hn)
   static constexpr size_t STOT = PDEC + (size_t)NW * DK * 4; // [NQ][d_k] segment totals of the cumsums
-  static constexpr size_t U0 = al(STOT + (size_t)NQ * DK * 4);
+  static constexpr size_t FL = STOT + (size_t)NQ * DK * 4;    // largest decay of a 16-token block (float bits)
+  static constexpr size_t U0 = al(FL + 16);
   // phase A
   static constexpr size_t SA = U0;    // Hn^T [v][d]; then dH'^T
   static constexpr size_t DOA = SA + VK;  // dO rows [t][v]
@@ -125,6 +128,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
   float* pcol = (float*)(smem + Lay::PCOL);
   float* pdec = (float*)(smem + Lay::PDEC);
   float* stot = (float*)(smem + Lay::STOT);
+  int* sbmax = (int*)(smem + Lay::FL);
   E* sS = (E*)(smem + Lay::SA);
   E* sdO = (E*)(smem + Lay::DOA);
   E* sUt = (E*)(smem + Lay::UTA);
@@ -290,6 +294,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     tt.store(sT, LC);
     asm volatile("" ::"v"(rb));  // consumed by every lane (no load into it left pending)
     if (tid < C) sb[tid] = tid < nv ? rb : 0.f;
+    if (tid == 0) *sbmax = 0;
     lds_barrier();
     // G = inclusive cumsum of log a over the chunk, per key dimension: thread
     // (d, segment) scans RS rows in registers, then adds the earlier segments' totals
@@ -368,6 +373,18 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
       *(u32x4*)(sH + t * LK + d0) = vec_pack<E>(x);
     }
     if (tid < DK) sgce[tid] = __expf(sG[(C - 1) * LG + tid]);
+    {
+      // the largest decay of one 16-token block, max over (block, d) of
+      // G(row before the block) - G(the block's last row)
+      float bm = 0.f;
+      if (tid < DK) {
+        for (int b2 = 0; b2 < NB; ++b2)
+          bm = fmaxf(bm, (b2 > 0 ? sG[(b2 * 16 - 1) * LG + tid] : 0.f) - sG[(b2 * 16 + 15) * LG + tid]);
+      }
+#pragma unroll
+      for (int msk = 1; msk < 64; msk <<= 1) bm = fmaxf(bm, __shfl_xor(bm, msk, 64));
+      if (l == 0 && w * 64 < DK) atomicMax(sbmax, __float_as_int(bm));  // non-negative floats order as ints
+    }
     lds_barrier();
     // Z = dX (K o E)^T + dY V^T, then Z diag(b) = dX X^T + dY Y^T; tiles (ti, tk), tk <= ti
     f32x4 za[ZPW];
@@ -445,20 +462,32 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     lds_barrier();
 
     // ================================================ phase C: the decayed token sums
-    // q rows over dU^T; Qst_i = q_i e^(G_i - G_r) from this thread's own q
-    // pieces, before the registers take the next chunk's q
+    // Regime: "fast" while no 16-token block decays by more than e^60 in any
+    // dimension.  Every pair i >= j splits its decay as
+    //   e^(G_i - G_j) = e^(G_i - G_ref(i)) e^(G_ref(i) - G_s(j)) e^(G_s(j) - G_j),
+    // s(j) = the last row of j's block; ref(i) = the last row of i's block
+    // (fast: the first factor in [1, e^60]) or the row before i's block
+    // (exact: every factor <= 1, diagonal blocks pair by pair).  Staged rows:
+    //   Kend_j = k_j e^(G_s(j) - G_j),  Qx_i = q_i e^(G_i - G_ref(i)),  bKx_i = b_i k_i e^(G_i - G_ref(i)).
+    // In the fast regime both halves of a pair's dG term (row side +, column
+    // side -) are formed from the same rounded staged rows, so they cancel
+    // in the reverse cumsum as they do in exact arithmetic.
+    const bool fastd = __int_as_float(*sbmax) <= 60.f;
+    // q rows over dU^T; Qx from this thread's own q pieces, before the
+    // registers take the next chunk's q
     tq.store_masked(sQ, LK, nv);
 #pragma unroll
     for (int s2 = 0; s2 < tq.PT; ++s2) {
       const int idx = tid + NT * s2;
       if (tq.NP % NT == 0 || idx < tq.NP) {
         const int t = idx / (DK / V), d0 = (idx % (DK / V)) * V, blk = t >> 4;
+        const int ref = fastd ? blk * 16 + 15 : blk * 16 - 1;
         E e[V];
         __builtin_memcpy(e, &tq.x[s2], 16);
         float g[V], gr[V], x[V];
         lds_f32_load<V>(sG + t * LG + d0, g);
-        if (blk > 0)
-          lds_f32_load<V>(sG + (blk * 16 - 1) * LG + d0, gr);
+        if (ref >= 0)
+          lds_f32_load<V>(sG + ref * LG + d0, gr);
         else
 #pragma unroll
           for (int i = 0; i < V; ++i) gr[i] = 0.f;
@@ -468,15 +497,15 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
       }
     }
     LRT_KG_LOAD(next, np, nn, 1)
-    // Kend_j = k_j e^(G_s - G_j) (s = the last row of j's block), b_i k_i e^(G_i - G_r)
     for (int p = tid; p < C * (DK / V); p += NT) {
       const int t = p / (DK / V), d0 = (p % (DK / V)) * V, blk = t >> 4;
+      const int ref = fastd ? blk * 16 + 15 : blk * 16 - 1;
       float kx[V], g[V], gs[V], gr[V], a[V], b2[V];
       lds_vec_load<E>(sK + t * LK + d0, kx);
       lds_f32_load<V>(sG + t * LG + d0, g);
       lds_f32_load<V>(sG + (blk * 16 + 15) * LG + d0, gs);
-      if (blk > 0)
-        lds_f32_load<V>(sG + (blk * 16 - 1) * LG + d0, gr);
+      if (ref >= 0)
+        lds_f32_load<V>(sG + ref * LG + d0, gr);
       else
 #pragma unroll
         for (int i = 0; i < V; ++i) gr[i] = 0.f;
@@ -491,111 +520,112 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     }
     lds_barrier();
     // R over the tokens j <= i of this lane's token i (rows d, cols i):
-    //   e^(G_i - G_r) sum_{sj < si} e^(G_r - G_s(sj)) (M_{si,sj} Kend_{sj})  +  the diagonal block
-    // dq += R(dP); dk += b R(dA); dbeta += rowsum(k o R(dA))
+    //   R = e^(G_i - G_ref) sum_{sj} e^(G_ref - G_s(sj)) (M_{si,sj} Kend_{sj})  [+ exact diagonal]
+    // dq += R(dP); dk += b R(dA); dbeta += rowsum(k o R(dA)); dG += q o dq + b k o R(dA)
 #pragma unroll
     for (int s = 0; s < KPW; ++s) {
       const int td = w / NB + WPB * s;
       if (td < NDT) {
         const int d0 = td * 16 + dsub;
         const f32x4 gi = *(const f32x4*)(sG + tl * LG + d0);
+        const int ref = fastd ? tb * 16 + 15 : tb * 16 - 1;
+        const f32x4 gref = ref >= 0 ? *(const f32x4*)(sG + ref * LG + d0) : zero4();
+        const f32x4 kk = load4<E>(sK + tl * LK + d0), qq = load4<E>(sQ + tl * LK + d0);
         f32x4 rp = zero4(), ra = zero4();
-        if (tb > 0) {
-          const f32x4 gr = *(const f32x4*)(sG + (tb * 16 - 1) * LG + d0);
-          for (int sj = 0; sj < tb; ++sj) {
-            f32x4 xp = zero4(), xa = zero4();
-            mma<16, true, true>(xp, sKe + sj * 16 * LK + td * 16, LK, sdPT + sj * 16 * LC + tb * 16, LC);
-            mma<16, true, true>(xa, sKe + sj * 16 * LK + td * 16, LK, sdAT + sj * 16 * LC + tb * 16, LC);
-            if (sj + 1 < tb) {
-              const f32x4 gs = *(const f32x4*)(sG + (sj * 16 + 15) * LG + d0);
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float f = __expf(gr[r] - gs[r]);
-                xp[r] *= f;
-                xa[r] *= f;
-              }
-            }
-            rp += xp;
-            ra += xa;
-          }
+        const int nsj = fastd ? tb + 1 : tb;
+        for (int sj = 0; sj < nsj; ++sj) {
+          f32x4 xp = zero4(), xa = zero4();
+          mma<16, true, true>(xp, sKe + sj * 16 * LK + td * 16, LK, sdPT + sj * 16 * LC + tb * 16, LC);
+          mma<16, true, true>(xa, sKe + sj * 16 * LK + td * 16, LK, sdAT + sj * 16 * LC + tb * 16, LC);
+          const f32x4 gs = *(const f32x4*)(sG + (sj * 16 + 15) * LG + d0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float e = __expf(gi[r] - gr[r]);
-            rp[r] *= e;
-            ra[r] *= e;
+            const float f = __expf(gref[r] - gs[r]);
+            rp[r] += f * xp[r];
+            ra[r] += f * xa[r];
           }
         }
+        f32x4 dg = qq * dqa[s];  // dG's q o (E o dO Hn^T) term
+        if (fastd) {
+          const f32x4 qx = load4<E>(sQs + tl * LK + d0), kx = load4<E>(sKs + tl * LK + d0);
+          dg += qx * rp + kx * ra;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __expf(gi[r] - gref[r]);
+          rp[r] *= e;
+          ra[r] *= e;
+        }
+        if (!fastd) {
 #pragma unroll 1
-        for (int jj = 0; jj < 16; ++jj) {
-          const int j = tb * 16 + jj;
-          const f32x4 gj = *(const f32x4*)(sG + j * LG + d0);
-          const f32x4 kj = load4<E>(sK + j * LK + d0);
-          const float dp = to_f(sdPT[j * LC + tl]);  // zero for j > i
-          const float da = to_f(sdAT[j * LC + tl]);  // zero for j >= i
+          for (int jj = 0; jj < 16; ++jj) {
+            const int j = tb * 16 + jj;
+            const f32x4 gj = *(const f32x4*)(sG + j * LG + d0);
+            const f32x4 kj = load4<E>(sK + j * LK + d0);
+            const float dp = to_f(sdPT[j * LC + tl]);  // zero for j > i
+            const float da = to_f(sdAT[j * LC + tl]);  // zero for j >= i
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float D = j <= tl ? __expf(gi[r] - gj[r]) : 0.f;  // never e^(positive)
-            rp[r] += dp * kj[r] * D;
-            ra[r] += da * kj[r] * D;
+            for (int r = 0; r < 4; ++r) {
+              const float D = j <= tl ? __expf(gi[r] - gj[r]) : 0.f;  // never e^(positive)
+              rp[r] += dp * kj[r] * D;
+              ra[r] += da * kj[r] * D;
+            }
           }
+          dg += qq * rp + btl * kk * ra;
         }
-        const f32x4 kk = load4<E>(sK + tl * LK + d0);
+        dga[s] += dg;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           dqa[s][r] += rp[r];
           dka[s][r] += btl * ra[r];
-          dga[s][r] += kk[r] * btl * ra[r];
           dbp += kk[r] * ra[r];
         }
       }
       tile_fence();
     }
     // C over the tokens i >= j of this lane's token j (rows d, cols j):
-    //   e^(G_s - G_j) sum_{si > sj} e^(G_r(si) - G_s) (Qst_si^T dP_{si,sj} + (b Kst)_si^T dA_{si,sj})  +  diagonal
-    // dk += C; dg -= k o C
+    //   C = e^(G_s(sj) - G_j) sum_{si} e^(G_ref(si) - G_s(sj)) (Qx_si^T dP_{si,sj} + bKx_si^T dA_{si,sj})
+    //   [+ exact diagonal];  dk += C; dG -= k o C
 #pragma unroll
     for (int s = 0; s < KPW; ++s) {
       const int td = w / NB + WPB * s;
       if (td < NDT) {
         const int d0 = td * 16 + dsub;
         const f32x4 gj = *(const f32x4*)(sG + tl * LG + d0);
+        const f32x4 gs = *(const f32x4*)(sG + (tb * 16 + 15) * LG + d0);
         f32x4 cc = zero4();
-        if (tb + 1 < NB) {
-          const f32x4 gs = *(const f32x4*)(sG + (tb * 16 + 15) * LG + d0);
-          for (int si = tb + 1; si < NB; ++si) {
-            f32x4 x = zero4();
-            mma<16, true, false>(x, sQs + si * 16 * LK + td * 16, LK, sdPT + tb * 16 * LC + si * 16, LC);
-            mma<16, true, false>(x, sKs + si * 16 * LK + td * 16, LK, sdAT + tb * 16 * LC + si * 16, LC);
-            if (si > tb + 1) {
-              const f32x4 gr = *(const f32x4*)(sG + (si * 16 - 1) * LG + d0);
+        for (int si = fastd ? tb : tb + 1; si < NB; ++si) {
+          f32x4 x = zero4();
+          mma<16, true, false>(x, sQs + si * 16 * LK + td * 16, LK, sdPT + tb * 16 * LC + si * 16, LC);
+          mma<16, true, false>(x, sKs + si * 16 * LK + td * 16, LK, sdAT + tb * 16 * LC + si * 16, LC);
+          const int ref = fastd ? si * 16 + 15 : si * 16 - 1;
+          const f32x4 gr = *(const f32x4*)(sG + ref * LG + d0);
 #pragma unroll
-              for (int r = 0; r < 4; ++r) x[r] *= __expf(gr[r] - gs[r]);
-            }
-            cc += x;
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) cc[r] *= __expf(gs[r] - gj[r]);
+          for (int r = 0; r < 4; ++r) cc[r] += __expf(gr[r] - gs[r]) * x[r];
         }
+        f32x4 dg = zero4();
+        if (fastd) dg = load4<E>(sKe + tl * LK + d0) * cc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cc[r] *= __expf(gs[r] - gj[r]);
+        if (!fastd) {
 #pragma unroll 1
-        for (int ii = 0; ii < 16; ++ii) {
-          const int i = tb * 16 + ii;
-          const f32x4 gi = *(const f32x4*)(sG + i * LG + d0);
-          const f32x4 qi = load4<E>(sQ + i * LK + d0);
-          const f32x4 ki = load4<E>(sK + i * LK + d0);
-          const float dp = to_f(sdPT[tl * LC + i]);            // zero for i < j
-          const float bda = sb[i] * to_f(sdAT[tl * LC + i]);  // zero for i <= j
+          for (int ii = 0; ii < 16; ++ii) {
+            const int i = tb * 16 + ii;
+            const f32x4 gi = *(const f32x4*)(sG + i * LG + d0);
+            const f32x4 qi = load4<E>(sQ + i * LK + d0);
+            const f32x4 ki = load4<E>(sK + i * LK + d0);
+            const float dp = to_f(sdPT[tl * LC + i]);            // zero for i < j
+            const float bda = sb[i] * to_f(sdAT[tl * LC + i]);  // zero for i <= j
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float D = i >= tl ? __expf(gi[r] - gj[r]) : 0.f;
-            cc[r] += (dp * qi[r] + bda * ki[r]) * D;
+            for (int r = 0; r < 4; ++r) {
+              const float D = i >= tl ? __expf(gi[r] - gj[r]) : 0.f;
+              cc[r] += (dp * qi[r] + bda * ki[r]) * D;
+            }
           }
+          dg = load4<E>(sK + tl * LK + d0) * cc;
         }
-        const f32x4 kk = load4<E>(sK + tl * LK + d0), qq = load4<E>(sQ + tl * LK + d0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          dka[s][r] += cc[r];
-          dga[s][r] += qq[r] * dqa[s][r] - kk[r] * cc[r];  // with dG's q o dq term
-        }
+        dka[s] += cc;
+        dga[s] -= dg;
       }
       tile_fence();
     }

@@ -69,6 +69,8 @@ CASES = [
     ("fp32_T77_C32_h0_dht", 2, 77, 2, 32, 64, 32, torch.float32, "perdim", 0.0, 0.1, 0.1),
     ("fp32_d64_C64_strong", 1, 150, 2, 64, 64, 64, torch.float32, "perdim", 2.0, 0.1, 0.1),
     ("fp32_d64_C64_slow", 2, 130, 2, 64, 64, 64, torch.float32, "perdim", -6.0, 0.1, 0.1),
+    # a 16-token block decays past e^60: the diagonal blocks' exact path
+    ("fp32_d64_C64_extreme", 1, 150, 2, 64, 64, 64, torch.float32, "perdim", 6.0, 0.1, 0.1),
     # fp32 at d = 128 with chunk 64 requested: the kernels run the largest
     # chunk whose fp32 operands fit in LDS
     ("fp32_d128_C64", 1, 100, 2, 128, 128, 64, torch.float32, "perdim", 0.0, 0.1, 0.1),
