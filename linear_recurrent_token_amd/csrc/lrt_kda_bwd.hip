@@ -119,37 +119,8 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
   constexpr int NZ = NB * NB, ZPW = (NZ + NW - 1) / NW;
   static_assert(NW % NB == 0, "waves must cover whole token blocks");
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
-  E* sdPT = (E*)(smem + Lay::DPT);
-  E* sdUt = (E*)(smem + Lay::DUT);
-  E* sQ = (E*)(smem + Lay::DUT);
-  float* sb = (float*)(smem + Lay::BB);
-  float* sgce = (float*)(smem + Lay::GCE);
-  float* pdb = (float*)(smem + Lay::PDB);
-  float* pcol = (float*)(smem + Lay::PCOL);
-  float* pdec = (float*)(smem + Lay::PDEC);
-  float* stot = (float*)(smem + Lay::STOT);
-  int* sbmax = (int*)(smem + Lay::FL);
-  E* sS = (E*)(smem + Lay::SA);
-  E* sdO = (E*)(smem + Lay::DOA);
-  E* sUt = (E*)(smem + Lay::UTA);
-  float* sG = (float*)(smem + Lay::GL);
-  E* sK = (E*)(smem + Lay::KR);
-  E* sdAT = (E*)(smem + Lay::DAT);
-  E* sT = (E*)(smem + Lay::TB);
-  E* sX = (E*)(smem + Lay::XB);
-  E* sH = (E*)(smem + Lay::HB);
-  E* sZT = (E*)(smem + Lay::ZB);
-  E* sKe = (E*)(smem + Lay::KE);
-  E* sQs = (E*)(smem + Lay::QS);
-  E* sKs = (E*)(smem + Lay::KS);
-  E* sDq = (E*)(smem + Lay::KE);
-  E* sDk = (E*)(smem + Lay::QS);
-
   const int H = m.H, ntiles = tile_count(m);
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  const int tb = w % NB;                // token block of this wave's tiles
-  const int tl = tb * 16 + (l & 15);    // this lane's token
-  const int dsub = (l >> 4) * 4;        // first of this lane's four rows inside a tile
+  int tid = threadIdx.x;  // (re-derived per chunk below, opaque to the compiler)
 
   Tile<E, DV, DK, NT> tS, tdS;
   Tile<E, C, DV, NT> to, tv;
@@ -167,29 +138,74 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     const int lh = (P_).h;                                                         \
     const size_t lt = (size_t)(tile_);                                             \
     if ((PART_) & 1) {                                                             \
-      tS.load_block(wS + lt * DV * DK);                                            \
-      to.load_rows_clamped(d_o + (ltok * H + lh) * DV, (size_t)H * DV, lnv);       \
-      tu.load_block(wU + lt * DV * C);                                             \
-      tdu.load_block(wdU + lt * DV * C);                                           \
+      tS.load_block(wS_ + lt * DV * DK);                                            \
+      to.load_rows_clamped(do_ + (ltok * H + lh) * DV, (size_t)H * DV, lnv);       \
+      tu.load_block(wU_ + lt * DV * C);                                             \
+      tdu.load_block(wdU_ + lt * DV * C);                                           \
     }                                                                              \
-    if ((PART_) & 2) tdS.load_block(wdS + lt * DV * DK);                           \
+    if ((PART_) & 2) tdS.load_block(wdS_ + lt * DV * DK);                           \
     if ((PART_) & 4) {                                                             \
-      tg.load_rows_clamped(log_a + (ltok * H + lh) * DK, (size_t)H * DK, lnv);     \
-      tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);         \
-      tt.load_block(wT + lt * C * C);                                              \
-      rb = beta[(ltok + min(tid, lnv - 1)) * H + lh];                              \
+      tg.load_rows_clamped(la_ + (ltok * H + lh) * DK, (size_t)H * DK, lnv);     \
+      tk.load_rows_clamped(k_ + (ltok * H + lh) * DK, (size_t)H * DK, lnv);         \
+      tt.load_block(wT_ + lt * C * C);                                              \
+      rb = beta_[(ltok + min(tid, lnv - 1)) * H + lh];                              \
     }                                                                              \
-    if ((PART_) & 8) tv.load_rows_clamped(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv); \
-    if ((PART_) & 16) tq.load_rows_clamped(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv); \
+    if ((PART_) & 8) tv.load_rows_clamped(v_ + (ltok * H + lh) * DV, (size_t)H * DV, lnv); \
+    if ((PART_) & 16) tq.load_rows_clamped(q_ + (ltok * H + lh) * DK, (size_t)H * DK, lnv); \
   }
 
   int tile = blockIdx.x;
   if (tile < ntiles) {
+    const E *q_ = q, *k_ = k, *v_ = v, *do_ = d_o, *wS_ = wS, *wdS_ = wdS, *wU_ = wU, *wdU_ = wdU, *wT_ = wT;
+    const float *la_ = log_a, *beta_ = beta;
     int n0;
     const SeqPos p0 = tile_pos(m, tile, n0);
     LRT_KG_LOAD(tile, p0, n0, 3)
   }
   for (; tile < ntiles; tile += gridDim.x) {
+    const E *q_ = q, *k_ = k, *v_ = v, *do_ = d_o, *wS_ = wS, *wdS_ = wdS, *wU_ = wU, *wdU_ = wdU, *wT_ = wT;
+    const float *la_ = log_a, *beta_ = beta;
+    E *dq_ = dq, *dk_ = dk_out, *dv_ = dv_out;
+    float *dla_ = dlog_a, *db_ = dbeta;
+    asm volatile("" : "+s"(q_), "+s"(k_), "+s"(v_), "+s"(do_), "+s"(wS_), "+s"(wdS_), "+s"(wU_), "+s"(wdU_));
+    asm volatile("" : "+s"(wT_), "+s"(la_), "+s"(beta_), "+s"(dq_), "+s"(dk_), "+s"(dv_), "+s"(dla_), "+s"(db_));
+    // Per-chunk opaque copies of the buffer and global base addresses: the
+    // compiler recomputes addresses inside the loop instead of hoisting
+    // hundreds of lane-dependent ones out of it (and spilling them).
+    int z0 = 0;
+    asm volatile("" : "+s"(z0));
+    tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int w = tid >> 6, l = tid & 63;
+    const int tb = w % NB;                // token block of this wave's tiles
+    const int tl = tb * 16 + (l & 15);    // this lane's token
+    const int dsub = (l >> 4) * 4;        // first of this lane's four rows inside a tile
+    char* smz = smem + z0;
+    E* sdPT = (E*)(smz + Lay::DPT);
+    E* sdUt = (E*)(smz + Lay::DUT);
+    E* sQ = (E*)(smz + Lay::DUT);
+    float* sb = (float*)(smz + Lay::BB);
+    float* sgce = (float*)(smz + Lay::GCE);
+    float* pdb = (float*)(smz + Lay::PDB);
+    float* pcol = (float*)(smz + Lay::PCOL);
+    float* pdec = (float*)(smz + Lay::PDEC);
+    float* stot = (float*)(smz + Lay::STOT);
+    int* sbmax = (int*)(smz + Lay::FL);
+    E* sS = (E*)(smz + Lay::SA);
+    E* sdO = (E*)(smz + Lay::DOA);
+    E* sUt = (E*)(smz + Lay::UTA);
+    float* sG = (float*)(smz + Lay::GL);
+    E* sK = (E*)(smz + Lay::KR);
+    E* sdAT = (E*)(smz + Lay::DAT);
+    E* sT = (E*)(smz + Lay::TB);
+    E* sX = (E*)(smz + Lay::XB);
+    E* sH = (E*)(smz + Lay::HB);
+    E* sZT = (E*)(smz + Lay::ZB);
+    E* sKe = (E*)(smz + Lay::KE);
+    E* sQs = (E*)(smz + Lay::QS);
+    E* sKs = (E*)(smz + Lay::KS);
+    E* sDq = (E*)(smz + Lay::KE);
+    E* sDk = (E*)(smz + Lay::QS);
     int n;
     const SeqPos cp = tile_pos(m, tile, n);
     const int h = cp.h;
@@ -457,7 +473,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     for (int p = tid; p < C * (DV / V); p += NT) {
       const int t = p / (DV / V), c0 = (p % (DV / V)) * V;
       if (t < nv)
-        *(u32x4*)(dv_out + ((tok0 + t) * H + h) * DV + c0) = vec_scale<E>(*(const u32x4*)(sX + t * LV + c0), sb[t]);
+        *(u32x4*)(dv_ + ((tok0 + t) * H + h) * DV + c0) = vec_scale<E>(*(const u32x4*)(sX + t * LV + c0), sb[t]);
     }
     lds_barrier();
 
@@ -675,14 +691,14 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
       lds_barrier();
     }
     LRT_KG_LOAD(next, np, nn, 2)
-    lds_to_rows<float, C, DK, NT>(dlog_a + (tok0 * H + h) * DK, (size_t)H * DK, sG, LG, nv);
-    lds_to_rows<E, C, DK, NT>(dq + (tok0 * H + h) * DK, (size_t)H * DK, sDq, LK, nv);
-    lds_to_rows<E, C, DK, NT>(dk_out + (tok0 * H + h) * DK, (size_t)H * DK, sDk, LK, nv);
+    lds_to_rows<float, C, DK, NT>(dla_ + (tok0 * H + h) * DK, (size_t)H * DK, sG, LG, nv);
+    lds_to_rows<E, C, DK, NT>(dq_ + (tok0 * H + h) * DK, (size_t)H * DK, sDq, LK, nv);
+    lds_to_rows<E, C, DK, NT>(dk_ + (tok0 * H + h) * DK, (size_t)H * DK, sDk, LK, nv);
     if (tid < nv) {
       const int bt = tid >> 4;
       float sum = 0.f;
       for (int i2 = 0; i2 < WPB; ++i2) sum += pdb[(bt + NB * i2) * C + tid];
-      dbeta[(tok0 + tid) * H + h] = sum;
+      db_[(tok0 + tid) * H + h] = sum;
     }
     lds_barrier();
   }
