@@ -190,33 +190,6 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
   constexpr int NKT = (DK / 16) * NB, KPW = (NKT + NW - 1) / NW;
   static_assert(NW % NB == 0, "waves must cover whole column blocks");
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
-  E* sK = (E*)(smem + Lay::K);
-  E* sdUt = (E*)(smem + Lay::DUT);
-  float* sg = (float*)(smem + Lay::G);
-  float* sb = (float*)(smem + Lay::BB);
-  float* pdgs = (float*)(smem + Lay::PDG);
-  float* pdbs = (float*)(smem + Lay::PDB);
-  float* pcxs = (float*)(smem + Lay::PCX);
-  float* sdot = (float*)(smem + Lay::DOT);  // [NW] <dH', Hn>
-  float* slast = sdot + NW;                 // [NW] terms of dg_C
-  E* sQ = (E*)(smem + Lay::Q);
-  E* sdO = (E*)(smem + Lay::DO);
-  E* sdQ = (E*)(smem + Lay::DO);
-  E* sUt = (E*)(smem + Lay::UT);
-  E* sS = (E*)(smem + Lay::ST);
-  E* sdSj = (E*)(smem + Lay::DSJ);
-  E* sV = (E*)(smem + Lay::VV);
-  E* sT = (E*)(smem + Lay::TT);
-  E* sdW = (E*)(smem + Lay::DW);
-  E* sdK = (E*)(smem + Lay::DW);
-  E* sdV = (E*)(smem + Lay::F);
-  E* sdTt = (E*)(smem + Lay::F);
-  E* sRt = sdTt + C * LC;
-  E* sMt = sRt + C * LC;
-  const int w = wave_id(), l = lane_id();
-  float* mydg = pdgs + w * C;
-  float* mydb = pdbs + w * C;
-  float* mycx = pcxs + w * C;
 
   Tile<E, C, DK, NT> tq, tk;
   Tile<E, C, DV, NT> to;
@@ -264,6 +237,46 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
     LRT_G_LOAD(tile, p0, n0, 15)
   }
   for (; tile < ntiles; tile += gridDim.x) {
+    // fp32 (twice the operand registers): per-chunk opaque copies of the
+    // buffer and global base addresses and of the lane index, so the compiler
+    // recomputes addresses inside the loop instead of hoisting lane-dependent
+    // ones out of it and spilling them (bf16 has the registers to keep them).
+    int z0 = 0;
+    if constexpr (sizeof(E) == 4) {
+      asm volatile("" : "+s"(z0));
+      asm volatile("" : "+s"(q), "+s"(k), "+s"(v), "+s"(d_o), "+s"(beta), "+s"(wG), "+s"(wS), "+s"(wdS));
+      asm volatile("" : "+s"(wU), "+s"(wdU), "+s"(wT), "+s"(dq), "+s"(dk_out), "+s"(dv_out), "+s"(dlog_a), "+s"(dbeta));
+    }
+    char* smz = smem + z0;
+    E* sK = (E*)(smz + Lay::K);
+    E* sdUt = (E*)(smz + Lay::DUT);
+    float* sg = (float*)(smz + Lay::G);
+    float* sb = (float*)(smz + Lay::BB);
+    float* pdgs = (float*)(smz + Lay::PDG);
+    float* pdbs = (float*)(smz + Lay::PDB);
+    float* pcxs = (float*)(smz + Lay::PCX);
+    float* sdot = (float*)(smz + Lay::DOT);  // [NW] <dH', Hn>
+    float* slast = sdot + NW;                 // [NW] terms of dg_C
+    E* sQ = (E*)(smz + Lay::Q);
+    E* sdO = (E*)(smz + Lay::DO);
+    E* sdQ = (E*)(smz + Lay::DO);
+    E* sUt = (E*)(smz + Lay::UT);
+    E* sS = (E*)(smz + Lay::ST);
+    E* sdSj = (E*)(smz + Lay::DSJ);
+    E* sV = (E*)(smz + Lay::VV);
+    E* sT = (E*)(smz + Lay::TT);
+    E* sdW = (E*)(smz + Lay::DW);
+    E* sdK = (E*)(smz + Lay::DW);
+    E* sdV = (E*)(smz + Lay::F);
+    E* sdTt = (E*)(smz + Lay::F);
+    E* sRt = sdTt + C * LC;
+    E* sMt = sRt + C * LC;
+    int tidv = threadIdx.x;
+    if constexpr (sizeof(E) == 4) asm volatile("" : "+v"(tidv));
+    const int w = tidv >> 6, l = tidv & 63;
+    float* mydg = pdgs + w * C;
+    float* mydb = pdbs + w * C;
+    float* mycx = pcxs + w * C;
     int n;
     const SeqPos cp = tile_pos(m, tile, n);
     const int h = cp.h;

@@ -101,18 +101,7 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, LG = Lay::LG, LA = Lay::LA, NB = Lay::NB;
   constexpr int V = 16 / (int)sizeof(E);
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
-  E* sK = (E*)(smem + Lay::K);
-  E* sQ = (E*)(smem + Lay::Q);
-  E* sV = (E*)(smem + Lay::V);
-  float* sG = (float*)(smem + Lay::G);
-  E* sS = (E*)(smem + Lay::S);
-  float* sA = (float*)(smem + Lay::A);
-  E* sT = (E*)(smem + Lay::T);
-  E* sTw = sT + C * LC;
-  float* sb = (float*)(smem + Lay::BB);
-  int* sgmax = (int*)(smem + Lay::FL);
-  const int w = wave_id(), l = lane_id();
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;  // (re-derived per chunk below, opaque to the compiler)
   const int H = m.H, ntiles = tile_count(m);
 
   typedef typename std::conditional<FUSE, E, float>::type GE;  // element type of the gate input
@@ -138,6 +127,30 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
   int tile = blockIdx.x;
   if (tile < ntiles) LRT_KDA_LOAD(tile)
   for (; tile < ntiles; tile += gridDim.x) {
+    // fp32 (twice the operand registers): per-chunk opaque copies of the
+    // buffer and global base addresses and of the thread index, so addresses
+    // are recomputed inside the loop instead of hoisted out of it and spilled
+    // (bf16 has the registers to keep them).
+    int z0 = 0;
+    tid = threadIdx.x;
+    if constexpr (sizeof(E) == 4) {
+      asm volatile("" : "+s"(z0));
+      asm volatile("" : "+s"(q), "+s"(k), "+s"(v), "+s"(log_a), "+s"(beta), "+s"(wW), "+s"(wUp), "+s"(wKt));
+      asm volatile("" : "+s"(wGC), "+s"(wQg), "+s"(wP), "+s"(wT));
+      asm volatile("" : "+v"(tid));
+    }
+    const int w = tid >> 6, l = tid & 63;
+    char* smz = smem + z0;
+    E* sK = (E*)(smz + Lay::K);
+    E* sQ = (E*)(smz + Lay::Q);
+    E* sV = (E*)(smz + Lay::V);
+    float* sG = (float*)(smz + Lay::G);
+    E* sS = (E*)(smz + Lay::S);
+    float* sA = (float*)(smz + Lay::A);
+    E* sT = (E*)(smz + Lay::T);
+    E* sTw = sT + C * LC;
+    float* sb = (float*)(smz + Lay::BB);
+    int* sgmax = (int*)(smz + Lay::FL);
     int cn;
     const int nv = min(C, tile_pos(m, tile, cn).len - cn * C);
     if constexpr (FUSE) {
