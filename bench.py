@@ -56,8 +56,10 @@ WORKLOADS = {
     "ssd_train_recompute_bf16_2k": ("SSD (Mamba2 case) chunked fwd+bwd (backward recomputes) tokens/s, "
                                     "B=16 T=2048 H=8 d=128", "ssd_fwd + ssd_bwd"),
     "kda_bf16_1m": ("KDA chunked fwd tokens/s, B=1 T=2^20 H=16 d=128", "kda_fwd"),
-    # the KDA training step (the backward recomputes the forward)
-    "kda_train_bf16_2k": ("KDA chunked fwd+bwd tokens/s, B=16 T=2048 H=8 d=128", "kda_fwd + kda_bwd"),
+    "kda_train_bf16_2k": ("KDA chunked fwd+bwd tokens/s, B=16 T=2048 H=8 d=128", "kda_fwd_train + kda_bwd_saved"),
+    # the same step through the stateless pair (the backward recomputes the forward)
+    "kda_train_recompute_bf16_2k": ("KDA chunked fwd+bwd (backward recomputes) tokens/s, B=16 T=2048 H=8 d=128",
+                                    "kda_fwd + kda_bwd"),
     # the forwards on the raw projections, activations fused into the kernels
     # (the line also times the unfused pipeline: torch activations + the plain forward)
     "gdn_fused_bf16_2k": ("GDN chunked fwd, fused prologue (raw q/k/beta/gate in) tokens/s, B=16 T=2048 H=8 d=128",
@@ -67,6 +69,7 @@ WORKLOADS = {
 }
 # workloads that time another op on an existing workload's inputs
 CONFIG_OF = {"gdn_train_recompute_bf16_2k": "gdn_train_bf16_2k", "ssd_train_recompute_bf16_2k": "ssd_train_bf16_2k",
+             "kda_train_recompute_bf16_2k": "kda_train_bf16_2k",
              "gdn_fused_bf16_2k": "gdn_bf16_2k", "kda_fused_bf16_1m": "kda_bf16_1m"}
 
 # the library kernels of each pass (the forward's and the backward's share of a step)
@@ -269,7 +272,7 @@ def main():
     opc = {"gdn_fwd + gdn_bwd": L.OP_GDN_BWD, "gdn_fwd_train + gdn_bwd_saved": L.OP_GDN_BWD, "gdn_fwd": L.OP_GDN_FWD,
            "ssd_fwd": L.OP_SSD_FWD, "ssd_fwd + ssd_bwd": L.OP_SSD_BWD, "ssd_fwd_train + ssd_bwd_saved": L.OP_SSD_BWD,
            "kda_fwd": L.OP_KDA_FWD, "gdn_fwd_fused": L.OP_GDN_FWD, "kda_fwd_fused": L.OP_KDA_FWD,
-           "kda_fwd + kda_bwd": L.OP_KDA_BWD}[op]
+           "kda_fwd + kda_bwd": L.OP_KDA_BWD, "kda_fwd_train + kda_bwd_saved": L.OP_KDA_BWD}[op]
     ws_bytes = max(L.workspace_bytes(L.OP_KDA_FWD if op.startswith("kda") else L.OP_GDN_FWD, B, T, H, dk, dv, C,
                                      code), L.workspace_bytes(opc, B, T, H, dk, dv, C, code))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -312,6 +315,12 @@ def main():
             L.ssd_fwd_train(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), chunk=C, o=o, ht=ht, workspace=ws)
             L.ssd_bwd_saved(s["q"], s["k"], s["v"], s["log_a"], s.get("h0"), s["do"], ws, s.get("dht"), chunk=C,
                             out=grads)
+            return
+        if op == "kda_fwd_train + kda_bwd_saved":
+            L.kda_fwd_train(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), chunk=C, o=o, ht=ht,
+                            workspace=ws)
+            L.kda_bwd_saved(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), s["do"], ws, s.get("dht"),
+                            chunk=C, out=grads)
             return
         if op == "gdn_fwd_train + gdn_bwd_saved":
             L.gdn_fwd_train(s["q"], s["k"], s["v"], s["log_a"], s["beta"], s.get("h0"), chunk=C, o=o, ht=ht,

@@ -136,6 +136,24 @@ int kda_bwd(const void* q, const void* k, const void* v, const float* log_a, con
             int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Kimi Delta Attention forward for training and the backward that reuses
+ * it: kda_fwd_train is kda_fwd (same arguments, same o and ht) that also
+ * leaves in the workspace what kda_bwd would recompute -- the chunk-parallel
+ * pass's W, U', Ktil, G_C, Q o e^G, P and T = (I + A)^-1, the chunk-start
+ * states and U; kda_bwd_saved, given that workspace unchanged and the same
+ * q, k, v, log_a, beta, h0, skips the recompute and returns kda_bwd's
+ * gradients.  Workspace: lrt_workspace_bytes(LRT_OP_KDA_BWD, ...); it may be
+ * passed to kda_bwd_saved any number of times (other do / dht).
+ */
+int kda_fwd_train(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                  const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk,
+                  int dtype, void* workspace, size_t workspace_bytes, void* stream);
+int kda_bwd_saved(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                  const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv,
+                  float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v, int chunk,
+                  int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Gated DeltaNet forward for training: gdn_fwd (same arguments, same o and
  * ht) that also leaves in the workspace what gdn_bwd would recompute -- the
  * WY factors W and T = (I + A)^-1, the in-chunk gate cumsums, the

@@ -37,7 +37,7 @@ OP_GDN_FWD_VARLEN, OP_GDN_BWD_VARLEN, OP_KDA_FWD_VARLEN = 5, 6, 7
 OP_KDA_BWD, OP_KDA_BWD_VARLEN = 8, 9
 EXPORTS = ("gdn_fwd", "gdn_bwd", "gdn_fwd_train", "gdn_bwd_saved", "gdn_fwd_noalloc", "kda_fwd", "ssd_fwd",
            "ssd_bwd", "ssd_fwd_train", "ssd_bwd_saved", "gdn_fwd_varlen", "kda_fwd_varlen", "gdn_bwd_varlen",
-           "gdn_fwd_fused", "kda_fwd_fused", "kda_bwd", "kda_bwd_varlen",
+           "gdn_fwd_fused", "kda_fwd_fused", "kda_bwd", "kda_bwd_varlen", "kda_fwd_train", "kda_bwd_saved",
            "lrt_workspace_bytes", "lrt_status_string", "lrt_profile_attach", "lrt_profile_count",
            "lrt_kernel_name")
 NOALLOC_MAX_BYTES = 64 << 20  # LRT_NOALLOC_MAX_BYTES
@@ -77,9 +77,12 @@ def lib():
         L.kda_fwd_fused.argtypes = [vp] * 8 + [ci] * 7 + [vp, sz, vp]
         L.kda_bwd.argtypes = [vp] * 14 + [ci] * 7 + [vp, sz, vp]
         L.kda_bwd_varlen.argtypes = [vp] * 15 + [ci] * 7 + [vp, sz, vp]
+        L.kda_fwd_train.argtypes = [vp] * 8 + [ci] * 7 + [vp, sz, vp]
+        L.kda_bwd_saved.argtypes = [vp] * 14 + [ci] * 7 + [vp, sz, vp]
         for f in ("gdn_fwd", "kda_fwd", "ssd_fwd", "gdn_bwd", "ssd_bwd", "gdn_fwd_train", "gdn_bwd_saved",
                   "ssd_fwd_train", "ssd_bwd_saved", "gdn_fwd_noalloc", "gdn_fwd_varlen", "kda_fwd_varlen",
-                  "gdn_bwd_varlen", "gdn_fwd_fused", "kda_fwd_fused", "kda_bwd", "kda_bwd_varlen"):
+                  "gdn_bwd_varlen", "gdn_fwd_fused", "kda_fwd_fused", "kda_bwd", "kda_bwd_varlen",
+                  "kda_fwd_train", "kda_bwd_saved"):
             getattr(L, f).restype = ci
         L.lrt_workspace_bytes.argtypes = [ci] * 8
         L.lrt_workspace_bytes.restype = sz
@@ -192,6 +195,21 @@ def gdn_fwd_train(q, k, v, log_a, beta, h0=None, chunk=64, o=None, ht=True, work
     saved); pass ``saved`` (a uint8 workspace of the backward's size) to
     gdn_bwd_saved."""
     return _fwd(lib().gdn_fwd_train, OP_GDN_BWD, q, k, v, log_a, beta, h0, chunk, o, ht, workspace, want_ws=True)
+
+
+def kda_fwd_train(q, k, v, log_a, beta, h0=None, chunk=64, o=None, ht=True, workspace=None):
+    """Kimi Delta Attention forward that keeps what the backward needs ->
+    (o, ht, saved); pass ``saved`` to kda_bwd_saved."""
+    return _fwd(lib().kda_fwd_train, OP_KDA_BWD, q, k, v, log_a, beta, h0, chunk, o, ht, workspace, kda=True,
+                want_ws=True)
+
+
+def kda_bwd_saved(q, k, v, log_a, beta, h0, do, saved, dht=None, chunk=64, want_dh0=True, out=None):
+    """Kimi Delta Attention backward from kda_fwd_train's ``saved`` workspace
+    (no recompute) -> (dq, dk, dv, dlog_a, dbeta, dh0 or None)."""
+    if saved is None:
+        raise ValueError("saved: the workspace kda_fwd_train returned")
+    return _bwd(True, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, saved, out, fn="kda_bwd_saved")
 
 
 def ssd_fwd_train(q, k, v, log_a, h0=None, chunk=64, o=None, ht=True, workspace=None):
@@ -378,7 +396,7 @@ def _bwd(delta, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, workspace, o
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
-    kda = fn == "kda_bwd"
+    kda = fn.startswith("kda")
     gshape = (B, T, H, dk) if kda else (B, T, H)
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU device")

@@ -163,14 +163,15 @@ static int fwd_entry(int variant, const void* q, const void* k, const void* v, c
     if (p && !aligned4(p)) return LRT_ERR_ALIGN;
   // the fused KDA gate pre-activation is read in 16-byte pieces
   if (fuse && variant == kVarKDA && log_a && !aligned(log_a)) return LRT_ERR_ALIGN;
-  const int op = train ? (variant == kVarSSD ? LRT_OP_SSD_BWD : LRT_OP_GDN_BWD)
+  const int op = train ? (variant == kVarSSD ? LRT_OP_SSD_BWD : variant == kVarKDA ? LRT_OP_KDA_BWD : LRT_OP_GDN_BWD)
                        : variant == kVarGDN ? LRT_OP_GDN_FWD : variant == kVarSSD ? LRT_OP_SSD_FWD : LRT_OP_KDA_FWD;
   const int ws_op = !packed ? op : op == LRT_OP_GDN_FWD ? LRT_OP_GDN_FWD_VARLEN : LRT_OP_KDA_FWD_VARLEN;
   if (!workspace || workspace_bytes < ws_bytes(ws_op, B, T, H, dk, dv, chunk, dtype)) return LRT_ERR_WORKSPACE;
   if (T == 0) return launch_empty(h0, ht, B, H, dk, dv, stream);
   FwdArgs a{variant, q, k, v, log_a, beta, h0, o, ht, B, T, H, dk, dv, run_chunk(op, dtype, dk, dv, chunk), dtype,
             workspace, stream, packed ? cu : nullptr, fuse};
-  rc = train ? fwd_train(a) : variant == kVarKDA ? fwd_kda(a) : fwd_scalar_gate(a);
+  rc = train ? (variant == kVarKDA ? fwd_train_kda(a) : fwd_train(a)) : variant == kVarKDA ? fwd_kda(a)
+                                                                      : fwd_scalar_gate(a);
   return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
 }
 
@@ -198,7 +199,7 @@ static int bwd_entry(int variant, const void* q, const void* k, const void* v, c
   if (T == 0) return launch_empty(dht, dh0, B, H, d_k, d_v, stream);
   BwdArgs a{q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0,
             B, T, H, d_k, d_v, run_chunk(op, dtype, d_k, d_v, chunk), dtype, workspace, stream, packed ? cu : nullptr};
-  rc = variant == kVarGDN ? bwd_gdn(a, saved) : variant == kVarKDA ? bwd_kda(a) : bwd_ssd(a, saved);
+  rc = variant == kVarGDN ? bwd_gdn(a, saved) : variant == kVarKDA ? bwd_kda(a, saved) : bwd_ssd(a, saved);
   return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
 }
 
@@ -256,6 +257,21 @@ int kda_bwd(const void* q, const void* k, const void* v, const float* log_a, con
             int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_entry(kVarKDA, q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0, B, T, H, d_k, d_v,
                    chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+int kda_fwd_train(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                  const float* h0, void* o, float* ht, int B, int T, int H, int d_k, int d_v, int chunk,
+                  int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_entry(kVarKDA, q, k, v, log_a, beta, h0, o, ht, B, T, H, d_k, d_v, chunk, dtype, workspace,
+                   workspace_bytes, stream, true);
+}
+
+int kda_bwd_saved(const void* q, const void* k, const void* v, const float* log_a, const float* beta,
+                  const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv,
+                  float* dlog_a, float* dbeta, float* dh0, int B, int T, int H, int d_k, int d_v, int chunk,
+                  int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_entry(kVarKDA, q, k, v, log_a, beta, h0, d_o, dht, dq, dk, dv, dlog_a, dbeta, dh0, B, T, H, d_k, d_v,
+                   chunk, dtype, workspace, workspace_bytes, stream, true);
 }
 
 int gdn_fwd_train(const void* q, const void* k, const void* v, const float* log_a, const float* beta,

@@ -119,7 +119,7 @@ inline FwdWs fwd_ws_layout(int op, int B, int T, int H, int dk, int dv, int C, s
   w.GC = (float*)take(kf || kb, tiles * dk * sizeof(float));
   w.Qg = take(kf || kb, tiles * C * dk * esz);
   w.P = take(gf || kf || gb || sb || kb, tiles * C * C * esz);
-  const int nseg = (gf || kf || gb) && !packed ? scan_plan(B, H, dk, dv, (int)N).nseg : 1;
+  const int nseg = (gf || kf || gb || kb) && !packed ? scan_plan(B, H, dk, dv, (int)N).nseg : 1;
   w.SegLoc = (float*)take(nseg > 1, (size_t)B * H * nseg * dk * (dv + dk) * sizeof(float));
   w.SegStart = (float*)take(nseg > 1, (size_t)B * H * nseg * dk * dv * sizeof(float));
   w.cs = (int*)take(packed, (size_t)B * sizeof(int));
@@ -233,7 +233,8 @@ int fwd_kda(const FwdArgs& a);
 int bwd_gdn(const BwdArgs& a, bool saved);
 int fwd_train(const FwdArgs& a);  // GDN or SSD by a.variant
 int bwd_ssd(const BwdArgs& a, bool saved);
-int bwd_kda(const BwdArgs& a);
+int bwd_kda(const BwdArgs& a, bool saved);
+int fwd_train_kda(const FwdArgs& a);  // kda_fwd_train
 
 // The largest chunk in {16, 32, 64} at which every kernel of `op` (an
 // LRT_OP_* code; the training forwards count as the backward's op) fits in

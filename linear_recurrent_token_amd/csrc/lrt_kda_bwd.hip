@@ -708,11 +708,15 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
 template <typename E, int C, int DK, int DV>
 constexpr bool kda_bwd_fits() {
   return KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL <= kLdsMax && scan_bv<E, C, DK, DV, kScanBwd, true>() > 0 &&
+         scan_bv<E, C, DK, DV, kScanFwd, true>() > 0 &&
          dstate_bv<E, C, DK, DV, true, 64, true>() > 0 && KdaGradLds<E, C, DK, DV, kGradWaves>::TOTAL <= kLdsMax;
 }
 
+// saved: the workspace already holds W, U', Ktil, G_C, Q o e^G, P, Tinv, S_n
+// and U from kda_fwd_train of the same arguments, so the recompute is
+// skipped.
 template <typename E, int C, int DK, int DV>
-int kda_bwd_impl(const BwdArgs& a) {
+int kda_bwd_impl(const BwdArgs& a, bool saved) {
   if constexpr (!kda_bwd_fits<E, C, DK, DV>()) {
     return -3;  // not reached: the entry point runs a chunk that fits (kda_bwd_max_chunk)
   } else {
@@ -722,28 +726,30 @@ int kda_bwd_impl(const BwdArgs& a) {
     const SeqMap sm = seq_map(a.B, a.T, a.H, C, a.cu, ws.f);
     hipStream_t st = (hipStream_t)a.stream;
     if (packed && launch_varlen_plan(a.cu, a.B, a.T, C, ws.f, a.stream) != 0) return -7;
-    // the forward recomputed: the chunk-parallel pass (with Tinv), then the
-    // state scan writing the chunk-start states and U
-    LRT_LAUNCH(kKKdaPrepBwd, (k_kda_prep<E, C, DK, DV, kWyWaves, false>),
-               dim3(persistent_grid(tiles, KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL)), dim3(64 * kWyWaves), st,
-               (const E*)a.q, (const E*)a.k, (const E*)a.v, (const void*)a.log_a, a.beta, sm, (E*)ws.f.W,
-               (E*)ws.f.Up, (E*)ws.f.Kt, ws.f.GC, (E*)ws.f.Qg, (E*)ws.f.P, (E*)ws.T);
-    constexpr int BVS = scan_bv<E, C, DK, DV, kScanBwd, true>();
-    ScanArgs<E> sa{};
-    sa.W = (const E*)ws.f.W;
-    sa.Up = (const E*)ws.f.Up;
-    sa.Kt = (const E*)ws.f.Kt;
-    sa.GC = ws.f.GC;
-    sa.hin = a.h0;
-    sa.hs_ld = DV;
-    sa.U = (E*)ws.f.U;
-    sa.S = (E*)ws.f.S;
-    sa.m = sm;
-    sa.L = 1 << 30;
-    sa.nseg = 1;
-    sa.DV = DV;
-    LRT_LAUNCH(kKScanBwd, (k_scan<E, C, DK, BVS, kScanBwd, true, kStateWaves>), dim3(a.B * a.H * (DV / BVS)),
-               dim3(64 * kStateWaves), st, sa);
+    if (!saved) {
+      // the forward recomputed: the chunk-parallel pass (with Tinv), then the
+      // state scan writing the chunk-start states and U
+      LRT_LAUNCH(kKKdaPrepBwd, (k_kda_prep<E, C, DK, DV, kWyWaves, false>),
+                 dim3(persistent_grid(tiles, KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL)), dim3(64 * kWyWaves), st,
+                 (const E*)a.q, (const E*)a.k, (const E*)a.v, (const void*)a.log_a, a.beta, sm, (E*)ws.f.W,
+                 (E*)ws.f.Up, (E*)ws.f.Kt, ws.f.GC, (E*)ws.f.Qg, (E*)ws.f.P, (E*)ws.T);
+      constexpr int BVS = scan_bv<E, C, DK, DV, kScanBwd, true>();
+      ScanArgs<E> sa{};
+      sa.W = (const E*)ws.f.W;
+      sa.Up = (const E*)ws.f.Up;
+      sa.Kt = (const E*)ws.f.Kt;
+      sa.GC = ws.f.GC;
+      sa.hin = a.h0;
+      sa.hs_ld = DV;
+      sa.U = (E*)ws.f.U;
+      sa.S = (E*)ws.f.S;
+      sa.m = sm;
+      sa.L = 1 << 30;
+      sa.nseg = 1;
+      sa.DV = DV;
+      LRT_LAUNCH(kKScanBwd, (k_scan<E, C, DK, BVS, kScanBwd, true, kStateWaves>), dim3(a.B * a.H * (DV / BVS)),
+                 dim3(64 * kStateWaves), st, sa);
+    }
     constexpr int BV = dstate_bv<E, C, DK, DV, true, 64, true>();
     LRT_LAUNCH(kKDState, (k_dstate<E, C, DK, BV, kStateWaves, true, true, false, true>), dim3(a.B * a.H * (DV / BV)),
                dim3(64 * kStateWaves), st, (const E*)ws.f.Qg, (const E*)ws.f.Kt, (const E*)a.d_o, ws.f.GC,
@@ -754,6 +760,27 @@ int kda_bwd_impl(const BwdArgs& a) {
                (const E*)ws.dS, (const E*)ws.f.U, (const E*)ws.dU, (const E*)ws.T, (E*)a.dq, (E*)a.dk_out,
                (E*)a.dv_out, a.dlog_a, a.dbeta, sm);
     return hipGetLastError() == hipSuccess ? 0 : -7;
+  }
+}
+
+// KDA forward for training: kda_fwd's kernels writing into the backward's
+// workspace what kda_bwd_saved reads -- the chunk-parallel pass with Tinv,
+// the forward scan also saving the chunk-start states and U.
+template <typename E, int C, int DK, int DV>
+int kda_fwd_train_impl(const FwdArgs& a) {
+  if constexpr (!kda_bwd_fits<E, C, DK, DV>()) {
+    return -3;  // not reached: the entry point runs a chunk that fits (kda_bwd_max_chunk)
+  } else {
+    const BwdWs ws = bwd_ws_layout(LRT_OP_KDA_BWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
+    const int N = (a.T + C - 1) / C;
+    const int tiles = a.B * a.H * N;
+    LRT_LAUNCH(kKKdaPrep, (k_kda_prep<E, C, DK, DV, kWyWaves, false>),
+               dim3(persistent_grid(tiles, KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL)), dim3(64 * kWyWaves),
+               a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, (const void*)a.log_a, a.beta,
+               seq_map(a, ws.f, C), (E*)ws.f.W, (E*)ws.f.Up, (E*)ws.f.Kt, ws.f.GC, (E*)ws.f.Qg, (E*)ws.f.P,
+               (E*)ws.T);
+    if (hipGetLastError() != hipSuccess) return -7;
+    return launch_scan_fwd<E, C, DK, DV, true, true>(a, ws.f, N);
   }
 }
 
@@ -774,12 +801,24 @@ int kda_bwd_max_chunk(int dtype, int dk, int dv) {
 }
 
 template <typename E>
-static int kda_bwd_dtype(const BwdArgs& a) {
-#define LRT_CASE(DK_, DV_)                                      \
-  if (a.dk == DK_ && a.dv == DV_) {                             \
-    if (a.chunk == 16) return kda_bwd_impl<E, 16, DK_, DV_>(a); \
-    if (a.chunk == 32) return kda_bwd_impl<E, 32, DK_, DV_>(a); \
-    if (a.chunk == 64) return kda_bwd_impl<E, 64, DK_, DV_>(a); \
+static int kda_bwd_dtype(const BwdArgs& a, bool saved) {
+#define LRT_CASE(DK_, DV_)                                             \
+  if (a.dk == DK_ && a.dv == DV_) {                                    \
+    if (a.chunk == 16) return kda_bwd_impl<E, 16, DK_, DV_>(a, saved); \
+    if (a.chunk == 32) return kda_bwd_impl<E, 32, DK_, DV_>(a, saved); \
+    if (a.chunk == 64) return kda_bwd_impl<E, 64, DK_, DV_>(a, saved); \
+  }
+  LRT_DK
+#undef LRT_CASE
+  return -2;
+}
+template <typename E>
+static int kda_fwd_train_dtype(const FwdArgs& a) {
+#define LRT_CASE(DK_, DV_)                                         \
+  if (a.dk == DK_ && a.dv == DV_) {                                \
+    if (a.chunk == 16) return kda_fwd_train_impl<E, 16, DK_, DV_>(a); \
+    if (a.chunk == 32) return kda_fwd_train_impl<E, 32, DK_, DV_>(a); \
+    if (a.chunk == 64) return kda_fwd_train_impl<E, 64, DK_, DV_>(a); \
   }
   LRT_DK
 #undef LRT_CASE
@@ -788,6 +827,11 @@ static int kda_bwd_dtype(const BwdArgs& a) {
 #undef LRT_DK
 #undef LRT_DV
 
-int bwd_kda(const BwdArgs& a) { return a.dtype == LRT_BF16 ? kda_bwd_dtype<bf16>(a) : kda_bwd_dtype<float>(a); }
+int bwd_kda(const BwdArgs& a, bool saved) {
+  return a.dtype == LRT_BF16 ? kda_bwd_dtype<bf16>(a, saved) : kda_bwd_dtype<float>(a, saved);
+}
+int fwd_train_kda(const FwdArgs& a) {
+  return a.dtype == LRT_BF16 ? kda_fwd_train_dtype<bf16>(a) : kda_fwd_train_dtype<float>(a);
+}
 
 }  // namespace lrt

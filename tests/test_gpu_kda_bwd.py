@@ -186,3 +186,45 @@ def test_kda_bwd_varlen(case):
     say("  worst per-sequence " + " ".join(f"{x}={e:.2e}" for x, e in worst.items()))
     bad = {x: e for x, e in worst.items() if e > TOL[dt]}
     assert not bad, bad
+
+
+SAVED = ["fp32_T77_C32_h0_dht", "fp32_d128_C64", "bf16_T61_C16", "bf16_C64_T300", "bf16_C64_extreme",
+         "bf16_long_slow_C64"]
+
+
+@pytest.mark.parametrize("name", SAVED)
+def test_kda_fwd_train_and_bwd_saved(name):
+    """kda_fwd_train's outputs and kda_bwd_saved's gradients against the
+    oracle; a second kda_bwd_saved on the same saved workspace (another
+    upstream gradient) equals the stateless kda_bwd for it -- bitwise, except
+    in the long case: it runs the segment-parallel forward scan (B*H small),
+    whose saved states come from the segment carry, equal to the serial
+    recompute at the bar."""
+    import linear_recurrent_token_amd as L
+    case = next(c for c in CASES if c[0] == name)
+    _, B, T, H, dk, dv, chunk, dt, gate, shift, h0s, dhs = case
+    say(f"[kda_fwd_train/bwd_saved] {name}")
+    inp = synth.make_inputs("kda_fwd_bwd", B, T, H, dk, dv, dtype=dt, seed=3, device="cuda", gate=gate,
+                            gate_shift=shift, h0_std=h0s, dht_std=dhs)
+    q, k, v, la, beta, h0, do, dht = (inp.get(n) for n in ("q", "k", "v", "log_a", "beta", "h0", "do", "dht"))
+    o, ht, saved = L.kda_fwd_train(q, k, v, la, beta, h0, chunk=chunk)
+    got = L.kda_bwd_saved(q, k, v, la, beta, h0, do, saved, dht, chunk=chunk)
+    torch.cuda.synchronize()
+    ro, rh = oracle.fwd("kda", cpu(q), cpu(k), cpu(v), cpu(la), cpu(beta), cpu(h0))
+    errs = {"o": rel(o.float().cpu().numpy(), ro), "ht": rel(ht.cpu().numpy(), rh)}
+    errs.update(errors(got, oracle_bwd(inp)))
+    say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if e > TOL[dt]}
+    assert not bad, bad
+    do2 = (torch.randn(do.shape, device="cuda", generator=torch.Generator("cuda").manual_seed(5))).to(dt)
+    again = L.kda_bwd_saved(q, k, v, la, beta, h0, do2, saved, dht, chunk=chunk)
+    plain = L.kda_bwd(q, k, v, la, beta, h0, do2, dht, chunk=chunk)
+    torch.cuda.synchronize()
+    segmented = T >= 2048  # B*H = 2: the training forward's scan runs in segments
+    for n, x, y in zip(NAMES, again, plain):
+        if segmented:
+            # chunk-start states from the segment carry (bf16 transition
+            # products) against the backward's serial recompute: equal at the bar
+            assert rel(x.float().cpu().numpy(), y.float().cpu().numpy()) <= TOL[dt], n
+        else:
+            assert torch.equal(x, y), n
