@@ -66,11 +66,15 @@ WORKLOADS = {
                           "gdn_fwd_fused"),
     "kda_fused_bf16_1m": ("KDA chunked fwd, fused prologue (raw q/k/beta/gate in) tokens/s, B=1 T=2^20 H=16 d=128",
                           "kda_fwd_fused"),
+    # the same with the gate as its rank-16 factors (z = W_down x per token, W_up)
+    "kda_fused_lowrank_bf16_1m": ("KDA chunked fwd, fused prologue with the rank-16 gate (raw q/k/beta, z, W_up in) "
+                                  "tokens/s, B=1 T=2^20 H=16 d=128", "kda_fwd_fused_lowrank"),
 }
 # workloads that time another op on an existing workload's inputs
 CONFIG_OF = {"gdn_train_recompute_bf16_2k": "gdn_train_bf16_2k", "ssd_train_recompute_bf16_2k": "ssd_train_bf16_2k",
              "kda_train_recompute_bf16_2k": "kda_train_bf16_2k",
-             "gdn_fused_bf16_2k": "gdn_bf16_2k", "kda_fused_bf16_1m": "kda_bf16_1m"}
+             "gdn_fused_bf16_2k": "gdn_bf16_2k", "kda_fused_bf16_1m": "kda_bf16_1m",
+             "kda_fused_lowrank_bf16_1m": "kda_bf16_1m"}
 
 # the library kernels of each pass (the forward's and the backward's share of a step)
 FWD_KERNELS = {"k_wy", "k_scan", "k_scan_local", "k_carry", "k_ssd_fwd", "k_kda_prep", "k_state_copy"}
@@ -142,12 +146,16 @@ def method_model(op, c, has_h0, has_dht, esz=2):
     n_th, n_bh, st = B * T * H, B * H, dk * dv * 4
     e = esz
     ssd, kda = op.startswith("ssd"), op.startswith("kda")
-    # the fused KDA forward reads the gate pre-activation in the call's dtype
-    gate = (dk * e if op.endswith("fused") else 4 * dk) if kda else 4
+    # the fused KDA forward reads the gate pre-activation in the call's dtype;
+    # with the low-rank gate, 16 values per token shared by the H heads
+    if kda and op.endswith("lowrank"):
+        gate = 16 * e / H
+    else:
+        gate = (dk * e if op.endswith("fused") else 4 * dk) if kda else 4
     beta = 0 if ssd else 4
     fwd_b = (2 * dk + dv) * e + gate + beta + dv * e
     fwd_f = 2 * C * (dk + dv) + 4 * dk * dv if ssd else 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv
-    out = {"fwd": (fwd_b * n_th + (int(has_h0) + 1) * st * n_bh, fwd_f * n_th)}
+    out = {"fwd": (int(fwd_b * n_th) + (int(has_h0) + 1) * st * n_bh, fwd_f * n_th)}
     if "bwd" in op:
         # q, k, v, do, log a, beta in; dq, dk, dv, dlog_a, dbeta out (KDA: log a and dlog_a per key dim)
         g = 4 * dk if kda else 4
@@ -263,15 +271,17 @@ def main():
     copy = copy_gbs(torch, hip, stream, dev)
     # input sets larger than the last-level cache need no rotation
     nsets = args.sets if B * T * H * (2 * dk + dv) * 2 < (1 << 30) else 1
-    fused = op.endswith("_fused")
+    fused = op.endswith("_fused") or op.endswith("_lowrank")
     if fused:
-        sets = [synth.raw_inputs(cfg, device="cuda", seed=s) for s in range(nsets)]
+        sets = [synth.raw_inputs(cfg, device="cuda", seed=s, lowrank_factors_too=op.endswith("_lowrank"))
+                for s in range(nsets)]
     else:
         sets = [synth.config_inputs(cfg, device="cuda", seed=s) for s in range(nsets)]
     code = L.LRT_BF16
     opc = {"gdn_fwd + gdn_bwd": L.OP_GDN_BWD, "gdn_fwd_train + gdn_bwd_saved": L.OP_GDN_BWD, "gdn_fwd": L.OP_GDN_FWD,
            "ssd_fwd": L.OP_SSD_FWD, "ssd_fwd + ssd_bwd": L.OP_SSD_BWD, "ssd_fwd_train + ssd_bwd_saved": L.OP_SSD_BWD,
            "kda_fwd": L.OP_KDA_FWD, "gdn_fwd_fused": L.OP_GDN_FWD, "kda_fwd_fused": L.OP_KDA_FWD,
+           "kda_fwd_fused_lowrank": L.OP_KDA_FWD,
            "kda_fwd + kda_bwd": L.OP_KDA_BWD, "kda_fwd_train + kda_bwd_saved": L.OP_KDA_BWD}[op]
     ws_bytes = max(L.workspace_bytes(L.OP_KDA_FWD if op.startswith("kda") else L.OP_GDN_FWD, B, T, H, dk, dv, C,
                                      code), L.workspace_bytes(opc, B, T, H, dk, dv, C, code))
@@ -295,17 +305,26 @@ def main():
             x = x.float()
             return (x / torch.sqrt((x * x).sum(-1, keepdim=True) + 1e-6)).to(x_dtype)
         x_dtype = s["q_raw"].dtype
-        return (l2(s["q_raw"]), l2(s["k_raw"]), -torch.nn.functional.softplus(s["gate_raw"].float()),
+        if "z" in s:  # the low-rank gate: W_up z first (a torch GEMM)
+            B_, T_, H_, dk_ = s["q_raw"].shape
+            pre = (s["z"].view(B_ * T_, -1) @ s["w_up"].t()).view(B_, T_, H_, dk_)
+        else:
+            pre = s["gate_raw"]
+        return (l2(s["q_raw"]), l2(s["k_raw"]), -torch.nn.functional.softplus(pre.float()),
                 torch.sigmoid(s["beta_raw"]))
 
     def step_unfused(i):
         s = sets[i % len(sets)]
         q, k, la, beta = activate(s)
-        f = L.kda_fwd if op == "kda_fwd_fused" else L.gdn_fwd
+        f = L.kda_fwd if op.startswith("kda") else L.gdn_fwd
         f(q, k, s["v"], la, beta, s.get("h0"), chunk=C, o=o, ht=ht, workspace=ws)
 
     def step(i):
         s = sets[i % len(sets)]
+        if op == "kda_fwd_fused_lowrank":
+            L.kda_fwd_fused_lowrank(s["q_raw"], s["k_raw"], s["v"], s["z"], s["w_up"], s["beta_raw"], s.get("h0"),
+                                    chunk=C, o=o, ht=ht, workspace=ws)
+            return
         if fused:
             f = L.kda_fwd_fused if op == "kda_fwd_fused" else L.gdn_fwd_fused
             f(s["q_raw"], s["k_raw"], s["v"], s["gate_raw"], s["beta_raw"], s.get("h0"), chunk=C, o=o, ht=ht,
@@ -434,7 +453,8 @@ def main():
         ums = hip.elapsed_ms(ev[0], ev[1]) / args.steps
         hip.destroy(ev)
         unfused = {"ms_per_step": round(ums, 4), "fused_speedup": round(ums / ms_per_step, 3),
-                   "what": "torch l2norm(q), l2norm(k), -softplus(gate), sigmoid(beta) then the plain forward"}
+                   "what": ("torch " + ("gate = W_up z (GEMM), " if op.endswith("_lowrank") else "")
+                            + "l2norm(q), l2norm(k), -softplus(gate), sigmoid(beta) then the plain forward")}
 
     cpu = None
     if not args.no_cpu_baseline:

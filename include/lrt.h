@@ -271,6 +271,22 @@ int kda_fwd_fused(const void* q_raw, const void* k_raw, const void* v, const voi
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_fwd_fused with the gate given as its low-rank factors (KDA's gate is
+ * a projection through a bottleneck, the KDA mixer of the AMD ROCm blog
+ * "Pretraining hybrid LLMs with Primus", mixer list under Table 2): z
+ * [B, T, rank] in dtype holds each token's bottleneck activations (W_down x,
+ * shared by the heads) and w_up [H * d_k, rank] in dtype the up-projection;
+ * the kernels form the pre-activation w_up z per (token, head) in fp32 and
+ * apply -softplus, so only rank values per token are read for the gate
+ * instead of H * d_k.  rank must be 16 (else LRT_ERR_SHAPE); z and w_up
+ * 16-byte aligned.  Other arguments, outputs and workspace as kda_fwd_fused.
+ */
+int kda_fwd_fused_lowrank(const void* q_raw, const void* k_raw, const void* v, const void* z, const void* w_up,
+                          int rank, const float* beta_raw, const float* h0, void* o, float* ht, int B, int T, int H,
+                          int d_k, int d_v, int chunk, int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
  * Packed variable-length sequences (the packed batches of long-context
  * training, where many sequences of different lengths share one
  * [1, T, H, d] tensor; the 1M-context 7-MLA / 21-GDN hybrid guide packs

@@ -38,6 +38,7 @@ OP_KDA_BWD, OP_KDA_BWD_VARLEN = 8, 9
 EXPORTS = ("gdn_fwd", "gdn_bwd", "gdn_fwd_train", "gdn_bwd_saved", "gdn_fwd_noalloc", "kda_fwd", "ssd_fwd",
            "ssd_bwd", "ssd_fwd_train", "ssd_bwd_saved", "gdn_fwd_varlen", "kda_fwd_varlen", "gdn_bwd_varlen",
            "gdn_fwd_fused", "kda_fwd_fused", "kda_bwd", "kda_bwd_varlen", "kda_fwd_train", "kda_bwd_saved",
+           "kda_fwd_fused_lowrank",
            "lrt_workspace_bytes", "lrt_status_string", "lrt_profile_attach", "lrt_profile_count",
            "lrt_kernel_name")
 NOALLOC_MAX_BYTES = 64 << 20  # LRT_NOALLOC_MAX_BYTES
@@ -78,11 +79,12 @@ def lib():
         L.kda_bwd.argtypes = [vp] * 14 + [ci] * 7 + [vp, sz, vp]
         L.kda_bwd_varlen.argtypes = [vp] * 15 + [ci] * 7 + [vp, sz, vp]
         L.kda_fwd_train.argtypes = [vp] * 8 + [ci] * 7 + [vp, sz, vp]
+        L.kda_fwd_fused_lowrank.argtypes = [vp] * 5 + [ci] + [vp] * 4 + [ci] * 7 + [vp, sz, vp]
         L.kda_bwd_saved.argtypes = [vp] * 14 + [ci] * 7 + [vp, sz, vp]
         for f in ("gdn_fwd", "kda_fwd", "ssd_fwd", "gdn_bwd", "ssd_bwd", "gdn_fwd_train", "gdn_bwd_saved",
                   "ssd_fwd_train", "ssd_bwd_saved", "gdn_fwd_noalloc", "gdn_fwd_varlen", "kda_fwd_varlen",
                   "gdn_bwd_varlen", "gdn_fwd_fused", "kda_fwd_fused", "kda_bwd", "kda_bwd_varlen",
-                  "kda_fwd_train", "kda_bwd_saved"):
+                  "kda_fwd_train", "kda_bwd_saved", "kda_fwd_fused_lowrank"):
             getattr(L, f).restype = ci
         L.lrt_workspace_bytes.argtypes = [ci] * 8
         L.lrt_workspace_bytes.restype = sz
@@ -280,6 +282,43 @@ def kda_fwd_fused(q_raw, k_raw, v, gate_raw, beta_raw, h0=None, chunk=64, o=None
     dtype of q (log a = -softplus(gate_raw) inside the kernels)."""
     return _fwd(lib().kda_fwd_fused, OP_KDA_FWD, q_raw, k_raw, v, gate_raw, beta_raw, h0, chunk, o, ht, workspace,
                 kda=True, gate_dtype=q_raw.dtype)
+
+
+GATE_RANK = 16  # the rank of KDA's low-rank gate that kda_fwd_fused_lowrank takes
+
+
+def kda_fwd_fused_lowrank(q_raw, k_raw, v, z, w_up, beta_raw, h0=None, chunk=64, o=None, ht=True, workspace=None):
+    """Kimi Delta Attention forward on raw projections with the gate as its
+    low-rank factors: z [B, T, 16] (each token's bottleneck activations) and
+    w_up [H*d_k, 16], both in q's dtype; log a = -softplus(w_up z) is formed
+    in the kernels -> (o, ht)."""
+    B, T, H, dk = q_raw.shape
+    dv = v.shape[-1]
+    dev, dt = q_raw.device, q_raw.dtype
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    for name, t, shp, ty in (("k_raw", k_raw, (B, T, H, dk), dt), ("v", v, (B, T, H, dv), dt),
+                             ("z", z, (B, T, GATE_RANK), dt), ("w_up", w_up, (H * dk, GATE_RANK), dt),
+                             ("beta_raw", beta_raw, (B, T, H), torch.float32),
+                             ("h0", h0, (B, H, dk, dv), torch.float32)):
+        _check(dev, dt, name, t, shp, ty)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check(dev, dt, "o", o, (B, T, H, dv), dt)
+    if ht is True:
+        ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif ht is False:
+        ht = None
+    _check(dev, dt, "ht", ht, (B, H, dk, dv), torch.float32)
+    code = _dtype_code(q_raw)
+    ws, need = _workspace(OP_KDA_FWD, dev, B, T, H, dk, dv, chunk, code, workspace)
+    with torch.cuda.device(dev):
+        rc = lib().kda_fwd_fused_lowrank(_p(q_raw), _p(k_raw), _p(v), _p(z), _p(w_up), GATE_RANK, _p(beta_raw),
+                                         _p(h0), _p(o), _p(ht), B, T, H, dk, dv, chunk, code, _p(ws), need,
+                                         _stream(dev))
+    if rc != 0:
+        raise LrtError("kda_fwd_fused_lowrank", rc)
+    return o, ht
 
 
 def _varlen_check(q, cu_seqlens):

@@ -146,7 +146,8 @@ static int launch_empty(const float* h0, float* ht, int B, int H, int dk, int dv
 static int fwd_entry(int variant, const void* q, const void* k, const void* v, const float* log_a,
                      const float* beta, const float* h0, void* o, float* ht, int B, int T, int H, int dk,
                      int dv, int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream,
-                     bool train = false, const int* cu = nullptr, bool packed = false, bool fuse = false) {
+                     bool train = false, const int* cu = nullptr, bool packed = false, bool fuse = false,
+                     const void* gate_up = nullptr) {
   int rc = check_common(B, T, H, dk, dv, chunk, dtype, packed);
   if (rc) return rc;
   if (packed && !cu) return LRT_ERR_NULL;
@@ -161,15 +162,16 @@ static int fwd_entry(int variant, const void* q, const void* k, const void* v, c
   const void* sca[] = {log_a, beta, h0, ht};
   for (const void* p : sca)
     if (p && !aligned4(p)) return LRT_ERR_ALIGN;
-  // the fused KDA gate pre-activation is read in 16-byte pieces
+  // the fused KDA gate pre-activation (or its low-rank factors) is read in 16-byte pieces
   if (fuse && variant == kVarKDA && log_a && !aligned(log_a)) return LRT_ERR_ALIGN;
+  if (gate_up && !aligned(gate_up)) return LRT_ERR_ALIGN;
   const int op = train ? (variant == kVarSSD ? LRT_OP_SSD_BWD : variant == kVarKDA ? LRT_OP_KDA_BWD : LRT_OP_GDN_BWD)
                        : variant == kVarGDN ? LRT_OP_GDN_FWD : variant == kVarSSD ? LRT_OP_SSD_FWD : LRT_OP_KDA_FWD;
   const int ws_op = !packed ? op : op == LRT_OP_GDN_FWD ? LRT_OP_GDN_FWD_VARLEN : LRT_OP_KDA_FWD_VARLEN;
   if (!workspace || workspace_bytes < ws_bytes(ws_op, B, T, H, dk, dv, chunk, dtype)) return LRT_ERR_WORKSPACE;
   if (T == 0) return launch_empty(h0, ht, B, H, dk, dv, stream);
   FwdArgs a{variant, q, k, v, log_a, beta, h0, o, ht, B, T, H, dk, dv, run_chunk(op, dtype, dk, dv, chunk), dtype,
-            workspace, stream, packed ? cu : nullptr, fuse};
+            workspace, stream, packed ? cu : nullptr, fuse, gate_up};
   rc = train ? (variant == kVarKDA ? fwd_train_kda(a) : fwd_train(a)) : variant == kVarKDA ? fwd_kda(a)
                                                                       : fwd_scalar_gate(a);
   return rc == 0 ? LRT_OK : (rc == -7 ? LRT_ERR_LAUNCH : rc == -3 ? LRT_ERR_CHUNK : LRT_ERR_SHAPE);
@@ -331,6 +333,16 @@ int kda_fwd_fused(const void* q_raw, const void* k_raw, const void* v, const voi
                   void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_entry(kVarKDA, q_raw, k_raw, v, (const float*)gate_raw, beta_raw, h0, o, ht, B, T, H, d_k, d_v, chunk,
                    dtype, workspace, workspace_bytes, stream, false, nullptr, false, true);
+}
+
+int kda_fwd_fused_lowrank(const void* q_raw, const void* k_raw, const void* v, const void* z, const void* w_up,
+                          int rank, const float* beta_raw, const float* h0, void* o, float* ht, int B, int T, int H,
+                          int d_k, int d_v, int chunk, int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (rank != kGateRank) return LRT_ERR_SHAPE;
+  if (T > 0 && !w_up) return LRT_ERR_NULL;
+  return fwd_entry(kVarKDA, q_raw, k_raw, v, (const float*)z, beta_raw, h0, o, ht, B, T, H, d_k, d_v, chunk, dtype,
+                   workspace, workspace_bytes, stream, false, nullptr, false, true, T > 0 ? w_up : nullptr);
 }
 
 int gdn_fwd_varlen(const void* q, const void* k, const void* v, const float* log_a, const float* beta,

@@ -10,6 +10,9 @@ namespace lrt {
 
 // LDS of one workgroup on gfx950.
 constexpr size_t kLdsMax = 160 * 1024;
+// Rank of KDA's low-rank gate projection (the bottleneck of the fused
+// prologue's gate input).
+constexpr int kGateRank = 16;
 
 enum { kVarGDN = 0, kVarSSD = 1, kVarKDA = 2 };
 
@@ -24,6 +27,7 @@ struct FwdArgs {
   void* stream;
   const int* cu = nullptr;  // packed sequences: cu_seqlens [B + 1] (B sequences in [1, T, H, d]); nullptr: dense
   bool fuse = false;        // q, k, log_a, beta are raw projections (the fused prologue)
+  const void* gate_up = nullptr;  // KDA fused prologue with the low-rank gate: W_up [H*d_k][kGateRank]; log_a = z
 };
 
 struct BwdArgs {

@@ -21,7 +21,7 @@ constexpr bool kda_fits() {
   return KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL <= kLdsMax && scan_bv<E, C, DK, DV, kScanFwd, true>() > 0;
 }
 
-template <typename E, int C, int DK, int DV, bool FUSE>
+template <typename E, int C, int DK, int DV, bool FUSE, bool LOWRANK = false>
 int kda_impl_t(const FwdArgs& a) {
   if constexpr (!kda_fits<E, C, DK, DV>()) {
     return -3;  // not reached: the entry point runs a chunk that fits (kda_max_chunk)
@@ -32,17 +32,18 @@ int kda_impl_t(const FwdArgs& a) {
     const FwdWs ws = fwd_ws_layout(LRT_OP_KDA_FWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace, packed);
     hipStream_t st = (hipStream_t)a.stream;
     if (packed && launch_varlen_plan(a.cu, a.B, a.T, C, ws, a.stream) != 0) return -7;
-    LRT_LAUNCH(kKKdaPrep, (k_kda_prep<E, C, DK, DV, kWyWaves, FUSE>),
+    LRT_LAUNCH(kKKdaPrep, (k_kda_prep<E, C, DK, DV, kWyWaves, FUSE, LOWRANK>),
                dim3(persistent_grid(tiles, KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL)), dim3(64 * kWyWaves), st,
                (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, seq_map(a, ws, C), (E*)ws.W,
-               (E*)ws.Up, (E*)ws.Kt, ws.GC, (E*)ws.Qg, (E*)ws.P, (E*)nullptr);
+               (E*)ws.Up, (E*)ws.Kt, ws.GC, (E*)ws.Qg, (E*)ws.P, (E*)nullptr, (const E*)a.gate_up);
     if (hipGetLastError() != hipSuccess) return -7;
     return launch_scan_fwd<E, C, DK, DV, true>(a, ws, N);
   }
 }
 template <typename E, int C, int DK, int DV>
 int kda_impl(const FwdArgs& a) {
-  return a.fuse ? kda_impl_t<E, C, DK, DV, true>(a) : kda_impl_t<E, C, DK, DV, false>(a);
+  if (!a.fuse) return kda_impl_t<E, C, DK, DV, false>(a);
+  return a.gate_up ? kda_impl_t<E, C, DK, DV, true, true>(a) : kda_impl_t<E, C, DK, DV, true>(a);
 }
 
 template <typename E, int DK, int DV>

@@ -732,7 +732,7 @@ int kda_bwd_impl(const BwdArgs& a, bool saved) {
       LRT_LAUNCH(kKKdaPrepBwd, (k_kda_prep<E, C, DK, DV, kWyWaves, false>),
                  dim3(persistent_grid(tiles, KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL)), dim3(64 * kWyWaves), st,
                  (const E*)a.q, (const E*)a.k, (const E*)a.v, (const void*)a.log_a, a.beta, sm, (E*)ws.f.W,
-                 (E*)ws.f.Up, (E*)ws.f.Kt, ws.f.GC, (E*)ws.f.Qg, (E*)ws.f.P, (E*)ws.T);
+                 (E*)ws.f.Up, (E*)ws.f.Kt, ws.f.GC, (E*)ws.f.Qg, (E*)ws.f.P, (E*)ws.T, (const E*)nullptr);
       constexpr int BVS = scan_bv<E, C, DK, DV, kScanBwd, true>();
       ScanArgs<E> sa{};
       sa.W = (const E*)ws.f.W;
@@ -778,7 +778,7 @@ int kda_fwd_train_impl(const FwdArgs& a) {
                dim3(persistent_grid(tiles, KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL)), dim3(64 * kWyWaves),
                a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, (const void*)a.log_a, a.beta,
                seq_map(a, ws.f, C), (E*)ws.f.W, (E*)ws.f.Up, (E*)ws.f.Kt, ws.f.GC, (E*)ws.f.Qg, (E*)ws.f.P,
-               (E*)ws.T);
+               (E*)ws.T, (const E*)nullptr);
     if (hipGetLastError() != hipSuccess) return -7;
     return launch_scan_fwd<E, C, DK, DV, true, true>(a, ws.f, N);
   }

@@ -84,18 +84,23 @@ __device__ __forceinline__ void lds_f32_load(const float* p, float* x) {
 
 // Persistent over the chunk tiles; the next tile's inputs load into
 // registers while this one computes.  wT (nullable): Tinv rows [C][C] per
-// chunk (zero above the diagonal), for the backward.  FUSE: q, k, log_a and beta are the raw
+// chunk (zero above the diagonal), for the backward.  LOWRANK (with FUSE):
+// the gate comes as its rank-kGateRank bottleneck, log_a_ = z [tokens][R]
+// (the activations W_down x of each token, shared by the heads) and wup =
+// W_up [H * d_k][R]; the kernel forms W_up z per chunk on MFMA and applies
+// -softplus.  FUSE: q, k, log_a and beta are the raw
 // projections -- the gate pre-activation in E ([B, T, H, d_k]) -- and the
 // fused prologue (L2-normalised q, k rows; log a = -softplus; sigmoid) is
 // applied as they are staged.
-template <typename E, int C, int DK, int DV, int NW = 8, bool FUSE = false>
+template <typename E, int C, int DK, int DV, int NW = 8, bool FUSE = false, bool LOWRANK = false>
 __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, const E* __restrict__ k,
                                                       const E* __restrict__ v, const void* __restrict__ log_a_,
                                                       const float* __restrict__ beta, SeqMap m,
                                                       E* __restrict__ wW, E* __restrict__ wUp,
                                                       E* __restrict__ wKt, float* __restrict__ wGC,
                                                       E* __restrict__ wQg, E* __restrict__ wP,
-                                                      E* __restrict__ wT) {
+                                                      E* __restrict__ wT, const E* __restrict__ wup) {
+  static_assert(!LOWRANK || FUSE, "the low-rank gate is a fused-prologue input");
   constexpr int NT = 64 * NW;
   typedef KdaLds<E, C, DK, DV, NT> Lay;
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, LG = Lay::LG, LA = Lay::LA, NB = Lay::NB;
@@ -105,10 +110,13 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
   const int H = m.H, ntiles = tile_count(m);
 
   typedef typename std::conditional<FUSE, E, float>::type GE;  // element type of the gate input
-  const GE* log_a = (const GE*)log_a_;
+  const GE* log_a = (const GE*)log_a_;  // LOWRANK: the bottleneck activations z [tokens][kGateRank]
+  constexpr int R = kGateRank, LZ = R + lds_pad<E>();
   Tile<E, C, DK, NT> tk, tq;
   Tile<E, C, DV, NT> tv;
-  Tile<GE, C, DK, NT> tg;
+  Tile<GE, C, LOWRANK ? R : DK, NT> tg;
+  Tile<E, LOWRANK ? DK : 16, LOWRANK ? R : 16, NT> tw;  // LOWRANK: this head's W_up rows [d_k][R]
+  static_assert(!LOWRANK || (size_t)(C + DK) * LZ * sizeof(E) <= Lay::SSZ, "z and W_up are staged in S");
   float rb = 0.f;
 #define LRT_KDA_LOAD(tile_)                                                               \
   {                                                                                       \
@@ -120,7 +128,12 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
     tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                  \
     tq.load_rows_clamped(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);                  \
     tv.load_rows_clamped(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv);                  \
-    tg.load_rows_clamped(log_a + (ltok * H + lh) * DK, (size_t)H * DK, lnv);              \
+    if constexpr (LOWRANK) {                                                              \
+      tg.load_rows_clamped(log_a + ltok * R, (size_t)R, lnv);                             \
+      tw.load_block(wup + (size_t)lh * DK * R);                                           \
+    } else {                                                                              \
+      tg.load_rows_clamped(log_a + (ltok * H + lh) * DK, (size_t)H * DK, lnv);            \
+    }                                                                                     \
     rb = beta[(ltok + min(tid, lnv - 1)) * H + lh]; /* masked where used */               \
   }
 
@@ -136,7 +149,7 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
     if constexpr (sizeof(E) == 4) {
       asm volatile("" : "+s"(z0));
       asm volatile("" : "+s"(q), "+s"(k), "+s"(v), "+s"(log_a), "+s"(beta), "+s"(wW), "+s"(wUp), "+s"(wKt));
-      asm volatile("" : "+s"(wGC), "+s"(wQg), "+s"(wP), "+s"(wT));
+      asm volatile("" : "+s"(wGC), "+s"(wQg), "+s"(wP), "+s"(wT), "+s"(wup));
       asm volatile("" : "+v"(tid));
     }
     const int w = tid >> 6, l = tid & 63;
@@ -159,7 +172,11 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
     }
     tk.store_masked(sK, LK, nv);
     tq.store_masked(sQ, LK, nv);
-    if constexpr (FUSE) {
+    if constexpr (LOWRANK) {
+      // z rows and W_up rows into S (the gate is formed after the barrier)
+      tg.store_masked(sS, LZ, nv);
+      tw.store(sS + C * LZ, LZ);
+    } else if constexpr (FUSE) {
       // log a = -softplus(z) in fp32, rows past the end zero (as store_masked)
       constexpr int GV = 16 / (int)sizeof(GE), GPR = DK / GV;
 #pragma unroll
@@ -190,6 +207,21 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
     // the next tile (the last one again on the final pass: unconditional
     // loads keep the waits on older ones exact)
     LRT_KDA_LOAD(min(tile + (int)gridDim.x, ntiles - 1))
+    if constexpr (LOWRANK) {
+      // the gate pre-activation W_up z (rows d, cols t; one 16-long MFMA
+      // product per tile), then log a = -softplus, rows past the end zero
+      for (int tt = w; tt < (DK / 16) * NB; tt += NW) {
+        const int td = tt / NB, ti = tt % NB;
+        f32x4 acc = zero4();
+        mma<R>(acc, sS + C * LZ + td * 16 * LZ, LZ, sS + ti * 16 * LZ, LZ);
+        const int t = ti * 16 + (l & 15);
+        f32x4 y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = t < nv ? neg_softplus_f(acc[r]) : 0.f;
+        *(f32x4*)(sG + t * LG + td * 16 + (l >> 4) * 4) = y;
+      }
+      lds_barrier();
+    }
     // ---- G: inclusive cumsum over the chunk's tokens, per key dimension;
     // thread (d, segment) scans RS rows in registers, then adds the totals of
     // the earlier segments

@@ -160,19 +160,39 @@ def lowrank_gate(B, T, H, dk, seed, device, rank=16, width=None, block=1 << 16, 
     return out
 
 
-def raw_inputs(name, device="cpu", seed=0):
+def lowrank_factors(B, T, H, dk, seed, device, rank=16, width=None, block=1 << 16, out_dtype=torch.bfloat16):
+    """The low-rank gate's factors, drawn as lowrank_gate draws them: z = W_down x
+    [B, T, rank] (each token's bottleneck activations) and W_up [H*dk, rank],
+    both in out_dtype; the gate pre-activation is W_up z."""
+    D = H * dk if width is None else int(width)
+    w_down = randn((rank, D), seed, "w_down", device, std=0.02)
+    w_up = randn((H * dk, rank), seed, "w_up", device, std=0.02)
+    z = torch.empty((B, T, rank), dtype=out_dtype, device=device)
+    g = _gen(seed, "x", device)
+    for b in range(B):
+        for t0 in range(0, T, block):
+            t1 = min(T, t0 + block)
+            x = torch.randn((t1 - t0, D), generator=g, device=device, dtype=torch.float32)
+            z[b, t0:t1] = (x @ w_down.t()).to(out_dtype)
+    return z, w_up.to(out_dtype)
+
+
+def raw_inputs(name, device="cpu", seed=0, lowrank_factors_too=False):
     """The raw projections of a named workload, for the fused-prologue entry
     points: q_raw, k_raw ~ N(0,1) (not normalised), v, beta_raw ~ N(0,1)
     (the beta logits), gate_raw = the gate pre-activation (fp32 N(0,1) +
     gate_shift for a scalar gate; the rank-16 projection W_up (W_down x) in
-    the workload's dtype for KDA), h0."""
+    the workload's dtype for KDA -- or, with lowrank_factors_too, its factors
+    z = W_down x and W_up instead), h0."""
     c = dict(CONFIGS[name])
     B, T, H, dk, dv, dtype = c["B"], c["T"], c["H"], c["dk"], c["dv"], c["dtype"]
     out = {"q_raw": randn((B, T, H, dk), seed, "q", device).to(dtype),
            "k_raw": randn((B, T, H, dk), seed, "k", device).to(dtype),
            "v": randn((B, T, H, dv), seed, "v", device).to(dtype),
            "beta_raw": randn((B, T, H), seed, "beta", device)}
-    if c.get("gate") == "lowrank":
+    if c.get("gate") == "lowrank" and lowrank_factors_too:
+        out["z"], out["w_up"] = lowrank_factors(B, T, H, dk, seed, device, rank=c.get("rank", 16), out_dtype=dtype)
+    elif c.get("gate") == "lowrank":
         out["gate_raw"] = lowrank_gate(B, T, H, dk, seed, device, rank=c.get("rank", 16), preact=True,
                                        out_dtype=dtype)
     else:

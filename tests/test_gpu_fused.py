@@ -87,3 +87,45 @@ def test_fused_forward(case):
     assert np.all(np.isfinite(o.float().cpu().numpy()))
     assert eo <= TOL[dt] and eh <= TOL[dt], (eo, eh)
     assert uo <= TOL[dt] and uh <= TOL[dt], (uo, uh)
+
+
+LOWRANK = [
+    # B, T, H, d_k, d_v, chunk, dtype
+    (2, 300, 2, 128, 128, 64, torch.bfloat16),
+    (1, 130, 2, 64, 64, 32, torch.float32),
+    (1, 77, 3, 16, 32, 16, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", LOWRANK, ids=[f"T{c[1]}_d{c[3]}_C{c[5]}_{str(c[6])[6:]}" for c in LOWRANK])
+def test_kda_fused_lowrank_gate(case):
+    """kda_fwd_fused_lowrank forms the gate from its rank-16 factors in the
+    kernels: against the oracle fed log a = -softplus(W_up z) computed on the
+    host in fp32 from the same factors (and the activated q, k, beta), and
+    against the unfused GPU forward on those inputs."""
+    import linear_recurrent_token_amd as L
+    B, T, H, dk, dv, chunk, dt = case
+    say(f"[fused lowrank] {case}")
+    seed = 22
+    q_raw = synth.randn((B, T, H, dk), seed, "q", "cuda", std=3.0).to(dt)
+    k_raw = synth.randn((B, T, H, dk), seed, "k", "cuda", std=3.0).to(dt)
+    beta_raw = synth.randn((B, T, H), seed, "beta", "cuda")
+    v = synth.randn((B, T, H, dv), seed, "v", "cuda").to(dt)
+    h0 = synth.randn((B, H, dk, dv), seed, "h0", "cuda", std=0.1)
+    # a wide bottleneck so the gates vary visibly: z ~ N(0, 1), W_up ~ 0.3 N(0, 1)
+    z = synth.randn((B, T, 16), seed, "x", "cuda").to(dt)
+    w_up = synth.randn((H * dk, 16), seed, "w_up", "cuda", std=0.3).to(dt)
+    o, ht = L.kda_fwd_fused_lowrank(q_raw, k_raw, v, z, w_up, beta_raw, h0, chunk=chunk)
+    pre = (z.float() @ w_up.float().t()).view(B, T, H, dk)
+    ref = activated({"q_raw": q_raw, "k_raw": k_raw, "beta_raw": beta_raw, "gate_raw": pre}, dt)
+    la = ref["log_a"].contiguous()
+    ou, hu = L.kda_fwd(ref["q"], ref["k"], v, la, ref["beta"], h0, chunk=chunk)
+    torch.cuda.synchronize()
+    c = lambda x: x.detach().cpu()
+    ro, rh = oracle.fwd("kda", c(ref["q"]), c(ref["k"]), c(v), c(la), c(ref["beta"]), c(h0))
+    eo, eh = rel(o.float().cpu().numpy(), ro), rel(ht.cpu().numpy(), rh)
+    uo, uh = rel(o.float().cpu().numpy(), ou.float().cpu().numpy()), rel(ht.cpu().numpy(), hu.cpu().numpy())
+    say(f"  vs oracle o={eo:.2e} ht={eh:.2e}; vs unfused GPU o={uo:.2e} ht={uh:.2e}")
+    assert np.all(np.isfinite(o.float().cpu().numpy()))
+    assert eo <= TOL[dt] and eh <= TOL[dt], (eo, eh)
+    assert uo <= TOL[dt] and uh <= TOL[dt], (uo, uh)
