@@ -273,3 +273,47 @@ def test_varlen_validation(L):
         a = list(b)
         a[i] = None
         assert lib.gdn_bwd_varlen(*a) == c["LRT_ERR_NULL"], i
+
+
+def test_kda_backward_and_training_pair_validation(L):
+    """kda_bwd, kda_bwd_saved, kda_fwd_train and kda_fwd_fused_lowrank reject
+    missing pointers, bad sizes and short workspaces before any launch."""
+    c = codes()
+    lib = L.lib()
+    F = FAKE
+    base = [F, F, F, F, F, None, F, None, F, F, F, F, F, None, 1, 64, 2, 16, 16, 16, 0, None, 0, None]
+    for fn in (lib.kda_bwd, lib.kda_bwd_saved):
+        assert fn(*base) == c["LRT_ERR_WORKSPACE"]
+        for i in (0, 1, 2, 3, 4, 6, 8, 9, 10, 11, 12):
+            a = list(base)
+            a[i] = None
+            assert fn(*a) == c["LRT_ERR_NULL"], i
+        a = list(base)
+        a[17] = 24
+        assert fn(*a) == c["LRT_ERR_SHAPE"]
+    # the KDA training forward needs the KDA backward's workspace, which holds
+    # more than the forward's
+    fwd_need = L.workspace_bytes(L.OP_KDA_FWD, 1, 64, 2, 16, 16, 16, 0)
+    bwd_need = L.workspace_bytes(L.OP_KDA_BWD, 1, 64, 2, 16, 16, 16, 0)
+    assert bwd_need > fwd_need
+    args = [F, F, F, F, F, None, F, None, 1, 64, 2, 16, 16, 16, 0, F, fwd_need, None]
+    assert lib.kda_fwd_train(*args) == c["LRT_ERR_WORKSPACE"]
+    for i in (0, 1, 2, 3, 4, 6):
+        a = list(args)
+        a[i] = None
+        assert lib.kda_fwd_train(*a) == c["LRT_ERR_NULL"], i
+    # the low-rank gate: rank 16 only, W_up required, 16-byte aligned factors
+    need = L.workspace_bytes(L.OP_KDA_FWD, 1, 64, 2, 16, 16, 16, 1)
+    lr = [F, F, F, F, F, 16, F, None, F, None, 1, 64, 2, 16, 16, 16, 1, F, need, None]
+    a = list(lr)
+    a[5] = 8
+    assert lib.kda_fwd_fused_lowrank(*a) == c["LRT_ERR_SHAPE"]
+    a = list(lr)
+    a[4] = None
+    assert lib.kda_fwd_fused_lowrank(*a) == c["LRT_ERR_NULL"]
+    a = list(lr)
+    a[4] = FAKE + 2
+    assert lib.kda_fwd_fused_lowrank(*a) == c["LRT_ERR_ALIGN"]
+    a = list(lr)
+    a[18] = need - 1
+    assert lib.kda_fwd_fused_lowrank(*a) == c["LRT_ERR_WORKSPACE"]
