@@ -77,8 +77,9 @@ CONFIG_OF = {"gdn_train_recompute_bf16_2k": "gdn_train_bf16_2k", "ssd_train_reco
              "kda_fused_lowrank_bf16_1m": "kda_bf16_1m"}
 
 # the library kernels of each pass (the forward's and the backward's share of a step)
-FWD_KERNELS = {"k_wy", "k_scan", "k_scan_local", "k_carry", "k_ssd_fwd", "k_kda_prep", "k_state_copy"}
-# (k_kda_prep_bwd is the backward's recompute of the KDA forward pass)
+FWD_KERNELS = {"k_wy", "k_scan", "k_scan_local", "k_carry", "k_ssd_fwd", "k_kda_prep", "k_kda_prep_fast", "k_list_reset",
+               "k_state_copy"}
+# (k_kda_prep_bwd and k_kda_prep_fast_bwd are the backward's recompute of the KDA forward pass)
 
 
 def parse():

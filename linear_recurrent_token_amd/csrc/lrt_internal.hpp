@@ -65,6 +65,7 @@ struct FwdWs {
   void *W, *Up, *Kt, *U, *S, *Qg, *P;
   float *G, *GC, *SegLoc, *SegStart;
   int *cs, *cl, *co;
+  int* slow;  // KDA: the exact-path chunk list k_kda_prep_fast leaves (count, then tiles)
   size_t bytes;
 };
 
@@ -129,6 +130,7 @@ inline FwdWs fwd_ws_layout(int op, int B, int T, int H, int dk, int dv, int C, s
   w.cs = (int*)take(packed, (size_t)B * sizeof(int));
   w.cl = (int*)take(packed, (size_t)B * sizeof(int));
   w.co = (int*)take(packed, (size_t)(B + 1) * sizeof(int));
+  w.slow = (int*)take(kf || kb, (tiles + 1) * sizeof(int));
   w.bytes = off;
   return w;
 }
@@ -196,6 +198,9 @@ enum KernelKind {
   kKVarlenPlan,
   kKKdaPrepBwd,
   kKGradKda,
+  kKKdaPrepFast,
+  kKKdaPrepFastBwd,
+  kKListReset,
   kKNumKinds
 };
 // Bracket one launch with the timing hook's events (no-ops unless attached).

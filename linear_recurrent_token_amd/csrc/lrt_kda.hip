@@ -4,7 +4,7 @@
 // "Pretraining hybrid LLMs with Primus", section "How hybrid models are
 // defined in Primus", mixer list under Table 2).  With the state H = S^T:
 //   H_t = (I - b_t k_t k_t^T) Diag(a_t) H_{t-1} + b_t k_t v_t^T,  o_t = H_t^T q_t.
-// The chunk-parallel pass k_kda_prep (lrt_kda_prep.hpp) writes the WY
+// The chunk-parallel pass (k_kda_prep_fast and k_kda_prep, lrt_kda_prep.hpp) writes the WY
 // factors and decayed operands per chunk; the serial scan in KDA mode
 // (per-dimension decay, operands from the workspace) then carries the state
 // and forms o.
@@ -32,11 +32,9 @@ int kda_impl_t(const FwdArgs& a) {
     const FwdWs ws = fwd_ws_layout(LRT_OP_KDA_FWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace, packed);
     hipStream_t st = (hipStream_t)a.stream;
     if (packed && launch_varlen_plan(a.cu, a.B, a.T, C, ws, a.stream) != 0) return -7;
-    LRT_LAUNCH(kKKdaPrep, (k_kda_prep<E, C, DK, DV, kWyWaves, FUSE, LOWRANK>),
-               dim3(persistent_grid(tiles, KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL)), dim3(64 * kWyWaves), st,
-               (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_a, a.beta, seq_map(a, ws, C), (E*)ws.W,
-               (E*)ws.Up, (E*)ws.Kt, ws.GC, (E*)ws.Qg, (E*)ws.P, (E*)nullptr, (const E*)a.gate_up);
-    if (hipGetLastError() != hipSuccess) return -7;
+    if (launch_kda_prep<E, C, DK, DV, FUSE, LOWRANK>(a.q, a.k, a.v, a.log_a, a.beta, seq_map(a, ws, C), ws,
+                                                     (E*)nullptr, a.gate_up, tiles, kKKdaPrepFast, kKKdaPrep, st) != 0)
+      return -7;
     return launch_scan_fwd<E, C, DK, DV, true>(a, ws, N);
   }
 }

@@ -729,10 +729,9 @@ int kda_bwd_impl(const BwdArgs& a, bool saved) {
     if (!saved) {
       // the forward recomputed: the chunk-parallel pass (with Tinv), then the
       // state scan writing the chunk-start states and U
-      LRT_LAUNCH(kKKdaPrepBwd, (k_kda_prep<E, C, DK, DV, kWyWaves, false>),
-                 dim3(persistent_grid(tiles, KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL)), dim3(64 * kWyWaves), st,
-                 (const E*)a.q, (const E*)a.k, (const E*)a.v, (const void*)a.log_a, a.beta, sm, (E*)ws.f.W,
-                 (E*)ws.f.Up, (E*)ws.f.Kt, ws.f.GC, (E*)ws.f.Qg, (E*)ws.f.P, (E*)ws.T, (const E*)nullptr);
+      if (launch_kda_prep<E, C, DK, DV, false>(a.q, a.k, a.v, a.log_a, a.beta, sm, ws.f, (E*)ws.T, nullptr, tiles,
+                                               kKKdaPrepFastBwd, kKKdaPrepBwd, st) != 0)
+        return -7;
       constexpr int BVS = scan_bv<E, C, DK, DV, kScanBwd, true>();
       ScanArgs<E> sa{};
       sa.W = (const E*)ws.f.W;
@@ -774,12 +773,9 @@ int kda_fwd_train_impl(const FwdArgs& a) {
     const BwdWs ws = bwd_ws_layout(LRT_OP_KDA_BWD, a.B, a.T, a.H, DK, DV, C, sizeof(E), a.workspace);
     const int N = (a.T + C - 1) / C;
     const int tiles = a.B * a.H * N;
-    LRT_LAUNCH(kKKdaPrep, (k_kda_prep<E, C, DK, DV, kWyWaves, false>),
-               dim3(persistent_grid(tiles, KdaLds<E, C, DK, DV, 64 * kWyWaves>::TOTAL)), dim3(64 * kWyWaves),
-               a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, (const void*)a.log_a, a.beta,
-               seq_map(a, ws.f, C), (E*)ws.f.W, (E*)ws.f.Up, (E*)ws.f.Kt, ws.f.GC, (E*)ws.f.Qg, (E*)ws.f.P,
-               (E*)ws.T, (const E*)nullptr);
-    if (hipGetLastError() != hipSuccess) return -7;
+    if (launch_kda_prep<E, C, DK, DV, false>(a.q, a.k, a.v, a.log_a, a.beta, seq_map(a, ws.f, C), ws.f, (E*)ws.T,
+                                             nullptr, tiles, kKKdaPrepFast, kKKdaPrep, (hipStream_t)a.stream) != 0)
+      return -7;
     return launch_scan_fwd<E, C, DK, DV, true, true>(a, ws.f, N);
   }
 }

@@ -84,7 +84,9 @@ __device__ __forceinline__ void lds_f32_load(const float* p, float* x) {
 
 // Persistent over the chunk tiles; the next tile's inputs load into
 // registers while this one computes.  wT (nullable): Tinv rows [C][C] per
-// chunk (zero above the diagonal), for the backward.  LOWRANK (with FUSE):
+// chunk (zero above the diagonal), for the backward.  list (nullable): walk
+// only the tiles listed there (count in list[0], tiles from list[1]) -- the
+// exact-path chunks k_kda_prep_fast left.  LOWRANK (with FUSE):
 // the gate comes as its rank-kGateRank bottleneck, log_a_ = z [tokens][R]
 // (the activations W_down x of each token, shared by the heads) and wup =
 // W_up [H * d_k][R]; the kernel forms W_up z per chunk on MFMA and applies
@@ -99,7 +101,8 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
                                                       E* __restrict__ wW, E* __restrict__ wUp,
                                                       E* __restrict__ wKt, float* __restrict__ wGC,
                                                       E* __restrict__ wQg, E* __restrict__ wP,
-                                                      E* __restrict__ wT, const E* __restrict__ wup) {
+                                                      E* __restrict__ wT, const E* __restrict__ wup,
+                                                      const int* __restrict__ list) {
   static_assert(!LOWRANK || FUSE, "the low-rank gate is a fused-prologue input");
   constexpr int NT = 64 * NW;
   typedef KdaLds<E, C, DK, DV, NT> Lay;
@@ -137,9 +140,12 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
     rb = beta[(ltok + min(tid, lnv - 1)) * H + lh]; /* masked where used */               \
   }
 
-  int tile = blockIdx.x;
-  if (tile < ntiles) LRT_KDA_LOAD(tile)
-  for (; tile < ntiles; tile += gridDim.x) {
+  const int nitems = list != nullptr ? list[0] : ntiles;
+  auto tile_of = [&](int i) { return list != nullptr ? list[1 + i] : i; };
+  int it = blockIdx.x;
+  if (it < nitems) LRT_KDA_LOAD(tile_of(it))
+  for (; it < nitems; it += gridDim.x) {
+    const int tile = tile_of(it);
     // fp32 (twice the operand registers): per-chunk opaque copies of the
     // buffer and global base addresses and of the thread index, so addresses
     // are recomputed inside the loop instead of hoisted out of it and spilled
@@ -206,7 +212,7 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
     tv.store(sV, LV);
     // the next tile (the last one again on the final pass: unconditional
     // loads keep the waits on older ones exact)
-    LRT_KDA_LOAD(min(tile + (int)gridDim.x, ntiles - 1))
+    LRT_KDA_LOAD(tile_of(min(it + (int)gridDim.x, nitems - 1)))
     if constexpr (LOWRANK) {
       // the gate pre-activation W_up z (rows d, cols t; one 16-long MFMA
       // product per tile), then log a = -softplus, rows past the end zero
@@ -310,13 +316,29 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
       }
       // Ktil^T [d][t] = KF[t][d] e^(G_C[d]), and G_C
       E* kt = wKt + (size_t)tile * DK * C;
-      for (int p = tid; p < DK * (C / V); p += NT) {
-        const int d = p / (C / V), t0 = (p % (C / V)) * V;
-        const float eC = __expf(sG[(C - 1) * LG + d]);
-        float x[V];
+      if constexpr (std::is_same<E, bf16>::value && C >= 32) {
+        // the LDS transpose read hands each lane 8 consecutive tokens of one
+        // dimension (16 dimensions x 32 tokens per wave and step): one
+        // 16-byte piece of a Ktil^T row, without bank conflicts
+        for (int blk = w; blk < (DK / 16) * (C / 32); blk += NW) {
+          const int n0 = (blk / (C / 32)) * 16, k0 = (blk % (C / 32)) * 32;
+          const bf16x8 f = frag_k8_outer(sK, LK, k0, n0);
+          const int d = n0 + (l & 15), t0 = k0 + 8 * (l >> 4);
+          const float eC = __expf(sG[(C - 1) * LG + d]);
+          float x[8];
 #pragma unroll
-        for (int e = 0; e < V; ++e) x[e] = to_f(sK[(t0 + e) * LK + d]) * eC;
-        *(u32x4*)(kt + (size_t)d * C + t0) = vec_pack<E>(x);
+          for (int e = 0; e < 8; ++e) x[e] = (float)f[e] * eC;
+          *(u32x4*)(kt + (size_t)d * C + t0) = vec_pack<E>(x);
+        }
+      } else {
+        for (int p = tid; p < DK * (C / V); p += NT) {
+          const int d = p % DK, t0 = (p / DK) * V;  // consecutive lanes, consecutive dimensions
+          const float eC = __expf(sG[(C - 1) * LG + d]);
+          float x[V];
+#pragma unroll
+          for (int e = 0; e < V; ++e) x[e] = to_f(sK[(t0 + e) * LK + d]) * eC;
+          *(u32x4*)(kt + (size_t)d * C + t0) = vec_pack<E>(x);
+        }
       }
       for (int d = tid; d < DK; d += NT) wGC[(size_t)tile * DK + d] = sG[(C - 1) * LG + d];
     } else {
@@ -430,11 +452,18 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
     unit_lower_inverse<C, NT>(sA);
     // T and T diag(b) in E; X = K o e^G rows (the fast path staged them already)
     E* sX = sS;
-    for (int idx = tid; idx < C * C; idx += NT) {
-      const int j = idx / C, i = idx % C;
-      const float x = j <= i ? sA[j * LA + i] : 0.f;
-      sT[i * LC + j] = from_f<E>(x);
-      sTw[i * LC + j] = from_f<E>(x * sb[j]);
+    // (a thread fills V consecutive columns of one row: consecutive lanes read
+    // consecutive rows of the column-major inverse and write 16-byte pieces)
+    for (int p = tid; p < C * (C / V); p += NT) {
+      const int i = p % C, j0 = (p / C) * V;
+      float x[V], xw[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        x[e] = j0 + e <= i ? sA[(j0 + e) * LA + i] : 0.f;
+        xw[e] = x[e] * sb[j0 + e];
+      }
+      *(u32x4*)(sT + i * LC + j0) = vec_pack<E>(x);
+      *(u32x4*)(sTw + i * LC + j0) = vec_pack<E>(xw);
     }
     if (!fast) {
       for (int p = tid; p < C * (DK / V); p += NT) {
@@ -468,6 +497,320 @@ __global__ __launch_bounds__(64 * NW) void k_kda_prep(const E* __restrict__ q, c
     lds_barrier();
   }
 #undef LRT_KDA_LOAD
+}
+
+}  // namespace lrt
+
+namespace lrt {
+
+// ------------------------------------------------------------ k_kda_prep_fast
+// k_kda_prep's fast path (every |G| <= 60 in the chunk, so A and P are one
+// MFMA product each) in 4-wave workgroups that need at most half of a CU's
+// LDS: two workgroups share a CU and one's barriers overlap the other's work.
+// G is formed and consumed one half of d_k at a time (cumsum, then the scaled
+// rows K o e^G, K o e^-G, Q o e^G of that half); A, then the b v rows, reuse
+// the half-G area, T and T diag(b) the dead K o e^-G and Q o e^G areas.  A
+// chunk whose |G| exceeds 60 is appended to `slow` (count in slow[0], tiles
+// from slow[1]) and left to k_kda_prep's exact path.  Outputs as k_kda_prep.
+template <typename E, int C, int DK, int DV>
+struct KdaFastLds {
+  static constexpr int NT = 256;
+  static constexpr int P = lds_pad<E>();
+  static constexpr int LK = DK + P, LV = DV + P, LC = C + P, DH = DK / 2, LGH = DH + 4, LA = tri_ld<C>();
+  static constexpr int NQ = NT / DH < C ? NT / DH : C;  // row segments of the cumsum
+  static constexpr size_t es = sizeof(E);
+  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+  static constexpr size_t al(size_t x) { return (x + 15) & ~(size_t)15; }
+  static constexpr size_t RKQ = al(mx((size_t)C * LK * es, (size_t)C * LC * es));
+  static constexpr size_t K = 0;          // k rows -> K o e^-G -> T
+  static constexpr size_t Q = K + RKQ;    // q rows -> Q o e^G -> T diag(b)
+  static constexpr size_t S = Q + RKQ;    // K o e^G (X)
+  static constexpr size_t GA = S + al((size_t)C * LK * es);  // G (half of d_k) -> A (fp32) -> b v rows
+  static constexpr size_t GASZ = mx(mx((size_t)C * LGH * 4, (size_t)C * LA * 4), (size_t)C * LV * es);
+  static constexpr size_t BB = GA + al(GASZ);           // b [C]
+  static constexpr size_t GCA = BB + C * 4;             // G_C [d_k]
+  static constexpr size_t STOT = GCA + DK * 4;          // [NQ][DH] segment totals
+  static constexpr size_t FL = STOT + (size_t)NQ * DH * 4;  // max |G| over the chunk (float bits)
+  static constexpr size_t TOTAL = FL + 16;
+};
+
+// slow[0] = 0 before k_kda_prep_fast appends to the list.
+template <int = 0>
+__global__ void k_list_reset(int* slow) {
+  if (threadIdx.x == 0) slow[0] = 0;
+}
+
+template <typename E, int C, int DK, int DV, bool FUSE = false>
+__global__ __launch_bounds__(256, 2) void k_kda_prep_fast(const E* __restrict__ q, const E* __restrict__ k,
+                                                          const E* __restrict__ v, const void* __restrict__ log_a_,
+                                                          const float* __restrict__ beta, SeqMap m,
+                                                          E* __restrict__ wW, E* __restrict__ wUp,
+                                                          E* __restrict__ wKt, float* __restrict__ wGC,
+                                                          E* __restrict__ wQg, E* __restrict__ wP,
+                                                          E* __restrict__ wT, int* __restrict__ slow) {
+  typedef KdaFastLds<E, C, DK, DV> Lay;
+  constexpr int NT = 256, NW = 4;
+  constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, DH = Lay::DH, LGH = Lay::LGH, LA = Lay::LA;
+  constexpr int NQ = Lay::NQ, NB = C / 16;
+  constexpr int V = 16 / (int)sizeof(E);
+  static_assert(DH % V == 0, "a half of d_k holds whole 16-byte pieces");
+  static_assert(C % NQ == 0 && NQ * DH <= NT, "cumsum segments");
+  __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
+  E* sK = (E*)(smem + Lay::K);
+  E* sT = sK;
+  E* sQ = (E*)(smem + Lay::Q);
+  E* sTw = sQ;
+  E* sS = (E*)(smem + Lay::S);
+  float* sG = (float*)(smem + Lay::GA);
+  float* sA = sG;
+  E* sV = (E*)(smem + Lay::GA);
+  float* sb = (float*)(smem + Lay::BB);
+  float* sGC = (float*)(smem + Lay::GCA);
+  float* stot = (float*)(smem + Lay::STOT);
+  int* sgmax = (int*)(smem + Lay::FL);
+  const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
+  const int H = m.H, ntiles = tile_count(m);
+
+  typedef typename std::conditional<FUSE, E, float>::type GE;  // element type of the gate input
+  const GE* log_a = (const GE*)log_a_;
+  constexpr int GV = 16 / (int)sizeof(GE), GPR = DK / GV;  // gate elements per piece, pieces per row
+  static_assert(DH % GV == 0, "a gate piece lies in one half of d_k");
+  Tile<E, C, DK, NT> tk, tq;
+  Tile<E, C, DV, NT> tv;
+  Tile<GE, C, DK, NT> tg;
+  float rb = 0.f;
+  // the next tile's inputs in three parts, each issued once the current
+  // tile's copy of it has reached LDS: 1 k, q, beta; 2 the gate; 4 v
+#define LRT_KF_LOAD(tile_, PART_)                                                       \
+  {                                                                                     \
+    int ln;                                                                             \
+    const SeqPos lp = tile_pos(m, (tile_), ln);                                         \
+    const int lnv = min(C, lp.len - ln * C);                                            \
+    const size_t ltok = lp.tok0 + (size_t)ln * C;                                       \
+    const int lh = lp.h;                                                                \
+    if ((PART_) & 1) {                                                                  \
+      tk.load_rows_clamped(k + (ltok * H + lh) * DK, (size_t)H * DK, lnv);              \
+      tq.load_rows_clamped(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);              \
+      rb = beta[(ltok + min(tid, lnv - 1)) * H + lh]; /* masked where used */           \
+    }                                                                                   \
+    if ((PART_) & 2) tg.load_rows_clamped(log_a + (ltok * H + lh) * DK, (size_t)H * DK, lnv); \
+    if ((PART_) & 4) tv.load_rows_clamped(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv); \
+  }
+
+  int tile = blockIdx.x;
+  if (tile < ntiles) LRT_KF_LOAD(tile, 7)
+  for (; tile < ntiles; tile += gridDim.x) {
+    int cn;
+    const int nv = min(C, tile_pos(m, tile, cn).len - cn * C);
+    const int next = min(tile + (int)gridDim.x, ntiles - 1);
+    if constexpr (FUSE) {
+      tk.normalize_rows(kL2Eps);
+      tq.normalize_rows(kL2Eps);
+    }
+    tk.store_masked(sK, LK, nv);
+    tq.store_masked(sQ, LK, nv);
+    asm volatile("" ::"v"(rb));  // consumed by every lane (no load into it left pending)
+    if (tid < C) sb[tid] = tid < nv ? (FUSE ? sigmoid_f(rb) : rb) : 0.f;
+    if (tid == 0) *sgmax = 0;
+    LRT_KF_LOAD(next, 1)
+    // ---- per half of d_k: G (cumsum of log a, rows past the end add 0), then
+    // the scaled rows of that half
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int s2 = 0; s2 < tg.PT; ++s2) {
+        const int idx = tid + NT * s2;
+        if (tg.NP % NT == 0 || idx < tg.NP) {
+          const int r = idx / GPR, c0 = (idx % GPR) * GV;
+          if (c0 / DH == hf) {
+            GE e[GV];
+            __builtin_memcpy(e, &tg.x[s2], 16);
+#pragma unroll
+            for (int i = 0; i < GV; i += 4) {
+              f32x4 y;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float z = to_f(e[i + j]);
+                y[j] = r < nv ? (FUSE ? neg_softplus_f(z) : z) : 0.f;
+              }
+              *(f32x4*)(sG + r * LGH + c0 - hf * DH + i) = y;
+            }
+          }
+        }
+      }
+      if (hf == 1) LRT_KF_LOAD(next, 2)
+      lds_barrier();
+      {
+        constexpr int RS = C / NQ;
+        const int d = tid % DH, seg = tid / DH;
+        float x[RS];
+        if (seg < NQ) {
+#pragma unroll
+          for (int r = 0; r < RS; ++r) x[r] = sG[(seg * RS + r) * LGH + d];
+#pragma unroll
+          for (int r = 1; r < RS; ++r) x[r] += x[r - 1];
+          stot[seg * DH + d] = x[RS - 1];
+        }
+        lds_barrier();
+        if (seg < NQ) {
+          float off = 0.f, mm = 0.f;
+          for (int s2 = 0; s2 < seg; ++s2) off += stot[s2 * DH + d];
+#pragma unroll
+          for (int r = 0; r < RS; ++r) {
+            sG[(seg * RS + r) * LGH + d] = x[r] + off;
+            mm = fmaxf(mm, fabsf(x[r] + off));
+          }
+          if (seg == NQ - 1) sGC[hf * DH + d] = x[RS - 1] + off;
+          atomicMax(sgmax, __float_as_int(mm));  // non-negative floats order as ints
+        }
+        lds_barrier();
+      }
+      // KE = K o e^G (into S), KF = K o e^-G (in place of K), QE = Q o e^G
+      // (in place of Q), for this half's columns
+      for (int p = tid; p < C * (DH / V); p += NT) {
+        const int t = p / (DH / V), dh = (p % (DH / V)) * V, d0 = hf * DH + dh;
+        float kx[V], qx[V], g[V], ke[V];
+        lds_vec_load<E>(sK + t * LK + d0, kx);
+        lds_vec_load<E>(sQ + t * LK + d0, qx);
+        lds_f32_load<V>(sG + t * LGH + dh, g);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const float ep = __expf(g[e]), em = __expf(-g[e]);
+          ke[e] = kx[e] * ep;
+          qx[e] *= ep;
+          kx[e] *= em;
+        }
+        *(u32x4*)(sS + t * LK + d0) = vec_pack<E>(ke);
+        *(u32x4*)(sK + t * LK + d0) = vec_pack<E>(kx);
+        *(u32x4*)(sQ + t * LK + d0) = vec_pack<E>(qx);
+      }
+      lds_barrier();  // (the next half overwrites G)
+    }
+    if (__int_as_float(*sgmax) > 60.f) {
+      // the exact path's chunk: k_kda_prep takes it from the list
+      if (tid == 0) slow[1 + atomicAdd(slow, 1)] = tile;
+      lds_barrier();  // every wave has read the flag before the next chunk resets it
+      LRT_KF_LOAD(next, 4)
+      continue;
+    }
+    // ---- A (lower tiles) = b_i (KE KF^T); P rows from P^T tiles = KF QE^T;
+    // Q o e^G rows out; Ktil^T [d][t] = KF[t][d] e^(G_C[d]); G_C
+    E* pout = wP + (size_t)tile * C * C;
+    lds_to_block<E, C, DK, NT>(wQg + (size_t)tile * C * DK, sQ, LK);
+    constexpr int NA = NB * (NB + 1) / 2;
+    for (int tt = w; tt < NA + NB * NB; tt += NW) {
+      if (tt < NA) {
+        int ti = 0, r0 = tt;
+        while (r0 > ti) {
+          r0 -= ti + 1;
+          ++ti;
+        }
+        const int tj = r0;
+        f32x4 acc = zero4();
+        mma<DK>(acc, sS + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
+        const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
+        f32x4 av;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) av[r] = (j < i0 + r) ? sb[i0 + r] * acc[r] : 0.f;
+        *(f32x4*)(sA + j * LA + i0) = av;  // column-major
+      } else {
+        const int t2 = tt - NA, rj = t2 / NB, ci = t2 % NB;
+        f32x4 acc = zero4();
+        if (rj <= ci) mma<DK>(acc, sK + rj * 16 * LK, LK, sQ + ci * 16 * LK, LK);
+        const int i = ci * 16 + (l & 15), j0 = rj * 16 + (l >> 4) * 4;
+        f32x4 p4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p4[r] = (j0 + r <= i) ? acc[r] : 0.f;
+        store4<E>(pout + (size_t)i * C + j0, p4);
+      }
+    }
+    E* kt = wKt + (size_t)tile * DK * C;
+    if constexpr (std::is_same<E, bf16>::value && C >= 32) {
+      for (int blk = w; blk < (DK / 16) * (C / 32); blk += NW) {
+        const int n0 = (blk / (C / 32)) * 16, k0 = (blk % (C / 32)) * 32;
+        const bf16x8 f = frag_k8_outer(sK, LK, k0, n0);
+        const int d = n0 + (l & 15), t0 = k0 + 8 * (l >> 4);
+        const float eC = __expf(sGC[d]);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (float)f[e] * eC;
+        *(u32x4*)(kt + (size_t)d * C + t0) = vec_pack<E>(x);
+      }
+    } else {
+      for (int p = tid; p < DK * (C / V); p += NT) {
+        const int d = p % DK, t0 = (p / DK) * V;
+        const float eC = __expf(sGC[d]);
+        float x[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) x[e] = to_f(sK[(t0 + e) * LK + d]) * eC;
+        *(u32x4*)(kt + (size_t)d * C + t0) = vec_pack<E>(x);
+      }
+    }
+    for (int d = tid; d < DK; d += NT) wGC[(size_t)tile * DK + d] = sGC[d];
+    lds_barrier();
+    unit_lower_inverse<C, NT>(sA);
+    // T and T diag(b) over the dead KF and QE rows
+    for (int p = tid; p < C * (C / V); p += NT) {
+      const int i = p % C, j0 = (p / C) * V;
+      float x[V], xw[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        x[e] = j0 + e <= i ? sA[(j0 + e) * LA + i] : 0.f;
+        xw[e] = x[e] * sb[j0 + e];
+      }
+      *(u32x4*)(sT + i * LC + j0) = vec_pack<E>(x);
+      *(u32x4*)(sTw + i * LC + j0) = vec_pack<E>(xw);
+    }
+    lds_barrier();
+    if (wT != nullptr) lds_to_block<E, C, C, NT>(wT + (size_t)tile * C * C, sT, LC);
+    tv.scale_rows(sb);  // rows past the end scale by 0
+    tv.store(sV, LV);   // b v rows over the dead A
+    LRT_KF_LOAD(next, 4)
+    lds_barrier();
+    // W^T = X^T (T diag(b))^T; U' = T (b V) in accumulator-tile order
+    constexpr int NWT = (DK / 16) * NB, NUT = NB * (DV / 16);
+    for (int tt = w; tt < NWT + NUT; tt += NW) {
+      f32x4 acc = zero4();
+      if (tt < NWT) {
+        const int td = tt / NB, ti = tt % NB;
+        mma<C, true, false>(acc, sS + td * 16, LK, sTw + ti * 16 * LC, LC);
+        store4<E>(wW + ((size_t)tile * C + ti * 16 + (l & 15)) * DK + td * 16 + (l >> 4) * 4, acc);
+      } else {
+        const int u = tt - NWT, ti = u / (DV / 16), tvb = u % (DV / 16);
+        mma<C, false, true>(acc, sT + ti * 16 * LC, LC, sV + tvb * 16, LV);
+        acc_tile_store<E>(wUp + (size_t)tile * DV * C, ti * (DV / 16) + tvb, acc);
+      }
+    }
+    lds_barrier();
+  }
+#undef LRT_KF_LOAD
+}
+
+// The chunk-parallel pass of the KDA forward: k_kda_prep_fast (two
+// workgroups per CU) where it fits in half of a CU's LDS, with k_kda_prep
+// taking the chunks it leaves to the exact path; k_kda_prep alone otherwise
+// (and for the low-rank gate).  wT (nullable): also write Tinv.  fast_kind /
+// kind: the timing hook's ids of the two kernels.
+template <typename E, int C, int DK, int DV, bool FUSE, bool LOWRANK = false>
+int launch_kda_prep(const void* q, const void* k, const void* v, const void* log_a, const float* beta,
+                    const SeqMap& sm, const FwdWs& ws, E* wT, const void* wup, int tiles, int fast_kind, int kind,
+                    hipStream_t st) {
+  typedef KdaLds<E, C, DK, DV, 64 * kWyWaves> Lay;
+  if constexpr (!LOWRANK && KdaFastLds<E, C, DK, DV>::TOTAL <= kLdsMax / 2) {
+    LRT_LAUNCH(kKListReset, k_list_reset<>, dim3(1), dim3(64), st, ws.slow);
+    LRT_LAUNCH(fast_kind, (k_kda_prep_fast<E, C, DK, DV, FUSE>),
+               dim3(persistent_grid(tiles, KdaFastLds<E, C, DK, DV>::TOTAL)), dim3(256), st, (const E*)q, (const E*)k,
+               (const E*)v, log_a, beta, sm, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.GC, (E*)ws.Qg, (E*)ws.P, wT,
+               ws.slow);
+    LRT_LAUNCH(kind, (k_kda_prep<E, C, DK, DV, kWyWaves, FUSE, false>), dim3(persistent_grid(tiles, Lay::TOTAL)),
+               dim3(64 * kWyWaves), st, (const E*)q, (const E*)k, (const E*)v, log_a, beta, sm, (E*)ws.W,
+               (E*)ws.Up, (E*)ws.Kt, ws.GC, (E*)ws.Qg, (E*)ws.P, wT, (const E*)nullptr, (const int*)ws.slow);
+  } else {
+    LRT_LAUNCH(kind, (k_kda_prep<E, C, DK, DV, kWyWaves, FUSE, LOWRANK>), dim3(persistent_grid(tiles, Lay::TOTAL)),
+               dim3(64 * kWyWaves), st, (const E*)q, (const E*)k, (const E*)v, log_a, beta, sm, (E*)ws.W,
+               (E*)ws.Up, (E*)ws.Kt, ws.GC, (E*)ws.Qg, (E*)ws.P, wT, (const E*)wup, (const int*)nullptr);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
 }  // namespace lrt

@@ -39,6 +39,16 @@ def cpu(x):
     return None if x is None else x.detach().cpu()
 
 
+def mixed_shift(T, H, chunk, device):
+    """A gate shift per (token, head) that alternates by chunk: +3 (the
+    chunk's decay far past e^60, the exact path) on chunks n with
+    (n + h) % 3 == 0, -2 (the whole-chunk factorised path) elsewhere, so both
+    paths and their interleaving over the chunks are exercised."""
+    n = torch.arange(T, device=device).view(T, 1) // chunk
+    h = torch.arange(H, device=device).view(1, H)
+    return torch.where((n + h) % 3 == 0, 3.0, -2.0).view(1, T, H, 1)
+
+
 def run_fwd(op, inp, chunk, cols=None):
     L = lrt()
     q, k, v, la = inp["q"], inp["k"], inp["v"], inp["log_a"]
@@ -154,6 +164,10 @@ KDA_CASES = [
     # fp32 at d = 128, chunk 64 requested (the kernels run 32-token chunks)
     ("kda_fp32_d128_C64", 1, 150, 2, 128, 128, 64, torch.float32, "perdim", -2.0, 0.1),
     ("kda_fp32_d64_C64", 1, 150, 2, 64, 64, 64, torch.float32, "perdim", 0.0, 0.1),
+    # chunks on both paths, interleaved over heads and tokens
+    ("kda_bf16_mixed_C64", 2, 443, 3, 128, 128, 64, torch.bfloat16, "perdim", "mixed", 0.1),
+    ("kda_fp32_mixed_d64_C64", 1, 300, 3, 64, 64, 64, torch.float32, "perdim", "mixed", 0.1),
+    ("kda_bf16_mixed_C16", 1, 150, 2, 32, 64, 16, torch.bfloat16, "perdim", "mixed", 0.1),
 ]
 
 
@@ -161,6 +175,8 @@ KDA_CASES = [
 def test_kda_fwd_small(case):
     name, B, T, H, dk, dv, chunk, dt, gate, shift, h0s = case
     say(f"[fwd] {name}")
+    if shift == "mixed":
+        shift = mixed_shift(T, H, chunk, "cuda")
     inp = synth.make_inputs("kda_fwd", B, T, H, dk, dv, dtype=dt, seed=0, device="cuda", gate=gate,
                             gate_shift=shift, h0_std=h0s)
     eo, eh = run_fwd("kda", inp, chunk)

@@ -50,6 +50,16 @@ def errors(got, ref):
     return errs
 
 
+def mixed_shift(T, H, chunk, device):
+    """A gate shift per (token, head) that alternates by chunk: +3 (the
+    chunk's decay far past e^60, the exact path) on chunks n with
+    (n + h) % 3 == 0, -2 (the whole-chunk factorised path) elsewhere, so both
+    paths and their interleaving over the chunks are exercised."""
+    n = torch.arange(T, device=device).view(T, 1) // chunk
+    h = torch.arange(H, device=device).view(1, H)
+    return torch.where((n + h) % 3 == 0, 3.0, -2.0).view(1, T, H, 1)
+
+
 def oracle_bwd(inp):
     q, k, v, la, beta, h0, do, dht = (inp.get(n) for n in ("q", "k", "v", "log_a", "beta", "h0", "do", "dht"))
     return oracle.bwd("kda", cpu(q), cpu(k), cpu(v), cpu(la), cpu(beta), cpu(h0), cpu(do), cpu(dht))
@@ -84,6 +94,9 @@ CASES = [
     ("bf16_d16_dv32", 1, 100, 2, 16, 32, 16, torch.bfloat16, "perdim", 0.0, 0.1, 0.1),
     ("bf16_dk32_dv128_C32", 1, 100, 2, 32, 128, 32, torch.bfloat16, "perdim", 0.0, 0.1, 0.1),
     ("bf16_dk128_dv64_C64", 1, 130, 2, 128, 64, 64, torch.bfloat16, "perdim", 1.0, 0.1, 0.1),
+    # chunks on both paths of the forward's chunk-parallel pass, interleaved
+    ("bf16_C64_mixed", 2, 443, 3, 128, 128, 64, torch.bfloat16, "perdim", "mixed", 0.1, 0.1),
+    ("fp32_d64_C64_mixed", 1, 300, 3, 64, 64, 64, torch.float32, "perdim", "mixed", 0.1, 0.1),
     # long sequence, slow gates: the state carry spans 64 chunks both ways
     ("bf16_long_slow_C64", 1, 4096 - 7, 2, 128, 128, 64, torch.bfloat16, "perdim", -6.0, 0.1, 0.1),
 ]
@@ -93,6 +106,8 @@ CASES = [
 def test_kda_bwd(case):
     name, B, T, H, dk, dv, chunk, dt, gate, shift, h0s, dhs = case
     say(f"[kda_bwd] {name}")
+    if shift == "mixed":
+        shift = mixed_shift(T, H, chunk, "cuda")
     inp = synth.make_inputs("kda_fwd_bwd", B, T, H, dk, dv, dtype=dt, seed=3, device="cuda", gate=gate,
                             gate_shift=shift, h0_std=h0s, dht_std=dhs)
     got = run(inp, chunk)
@@ -189,7 +204,7 @@ def test_kda_bwd_varlen(case):
 
 
 SAVED = ["fp32_T77_C32_h0_dht", "fp32_d128_C64", "bf16_T61_C16", "bf16_C64_T300", "bf16_C64_extreme",
-         "bf16_long_slow_C64"]
+         "bf16_C64_mixed", "fp32_d64_C64_mixed", "bf16_long_slow_C64"]
 
 
 @pytest.mark.parametrize("name", SAVED)
@@ -204,6 +219,8 @@ def test_kda_fwd_train_and_bwd_saved(name):
     case = next(c for c in CASES if c[0] == name)
     _, B, T, H, dk, dv, chunk, dt, gate, shift, h0s, dhs = case
     say(f"[kda_fwd_train/bwd_saved] {name}")
+    if shift == "mixed":
+        shift = mixed_shift(T, H, chunk, "cuda")
     inp = synth.make_inputs("kda_fwd_bwd", B, T, H, dk, dv, dtype=dt, seed=3, device="cuda", gate=gate,
                             gate_shift=shift, h0_std=h0s, dht_std=dhs)
     q, k, v, la, beta, h0, do, dht = (inp.get(n) for n in ("q", "k", "v", "log_a", "beta", "h0", "do", "dht"))
