@@ -66,6 +66,9 @@ WORKLOADS = {
                           "gdn_fwd_fused"),
     "kda_fused_bf16_1m": ("KDA chunked fwd, fused prologue (raw q/k/beta/gate in) tokens/s, B=1 T=2^20 H=16 d=128",
                           "kda_fwd_fused"),
+    # the steps either side of the mixer: short conv on q/k/v and the gated output norm, fwd + bwd
+    "conv_norm_bf16_2k": ("short conv (q, k, v) + gated RMSNorm fwd+bwd tokens/s, B=16 T=2048 H=8 d=128",
+                          "short_conv fwd+bwd + gated_rmsnorm fwd+bwd"),
     # the same with the gate as its rank-16 factors (z = W_down x per token, W_up)
     "kda_fused_lowrank_bf16_1m": ("KDA chunked fwd, fused prologue with the rank-16 gate (raw q/k/beta, z, W_up in) "
                                   "tokens/s, B=1 T=2^20 H=16 d=128", "kda_fwd_fused_lowrank"),
@@ -261,6 +264,8 @@ def main():
 
     L.lib()
     wl = args.workload
+    if wl == "conv_norm_bf16_2k":
+        return main_conv_norm(args, wl)
     metric, op = WORKLOADS[wl]
     cfg = CONFIG_OF.get(wl, wl)
     c = dict(synth.CONFIGS[cfg])
@@ -504,6 +509,151 @@ def main():
     }
     if unfused is not None:
         line["unfused_pipeline"] = unfused
+    print(json.dumps(line), flush=True)
+    if args.copy_probe:
+        copy_probe(torch, dev)
+
+
+def main_conv_norm(args, wl):
+    """The steps either side of the mixer in one training step of the
+    2048-token workload: short_conv fwd + bwd over q, k and v as the 3 x 1024
+    columns of one [16, 2048, 3072] tensor (W = 4), and gated_rmsnorm fwd + bwd
+    over the mixer output [16, 2048, 8, 128].  Each kernel is an exact stream,
+    so its method bytes are its own reads and writes.  Also timed: the same
+    step through torch (conv1d + silu, rms_norm * silu, autograd)."""
+    import torch
+    import torch.nn.functional as F
+
+    import linear_recurrent_token_amd as L
+
+    L.lib()
+    metric, op = WORKLOADS[wl]
+    B, T, H, d, W = 16, 2048, 8, 128, 4
+    D = 3 * H * d
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    hip = Hip()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    copy = copy_gbs(torch, hip, stream, dev)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn((B, T, D), generator=g, device=dev).to(torch.bfloat16)
+    dy = torch.randn((B, T, D), generator=g, device=dev).to(torch.bfloat16)
+    wc = 0.5 * torch.randn((D, W), generator=g, device=dev)
+    o = torch.randn((B, T, H, d), generator=g, device=dev).to(torch.bfloat16)
+    z = torch.randn((B, T, H, d), generator=g, device=dev).to(torch.bfloat16)
+    dyn = torch.randn((B, T, H, d), generator=g, device=dev).to(torch.bfloat16)
+    wn = 1.0 + 0.1 * torch.randn((d,), generator=g, device=dev)
+    wsc = torch.empty(L.lib().short_conv_bwd_workspace_bytes(B * T, D, W), dtype=torch.uint8, device=dev)
+    wsn = torch.empty(L.lib().gated_rmsnorm_bwd_workspace_bytes(B * T * H, d), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        L.short_conv(x, wc)
+        L.short_conv_bwd(x, wc, dy, workspace=wsc)
+        L.gated_rmsnorm(o, z, wn)
+        L.gated_rmsnorm_bwd(o, z, wn, dyn, workspace=wsn)
+
+    def step_torch(i):
+        xs = x.detach().requires_grad_(True)
+        ws = wc.detach().requires_grad_(True)
+        pre = F.conv1d(xs.transpose(1, 2), ws.to(x.dtype).view(D, 1, W), padding=W - 1, groups=D)[..., :T]
+        yc = F.silu(pre).transpose(1, 2)
+        os_, zs, wns = o.detach().requires_grad_(True), z.detach().requires_grad_(True), wn.detach().requires_grad_(True)
+        yn = F.rms_norm(os_, (d,), weight=wns.to(o.dtype), eps=1e-6) * F.silu(zs)
+        torch.autograd.backward([yc, yn], [dy, dyn])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = hip.events(args.steps + 1)
+    t0 = time.perf_counter()
+    hip.record(ev[0], stream)
+    for i in range(args.steps):
+        step(i)
+        hip.record(ev[i + 1], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [hip.elapsed_ms(ev[i], ev[i + 1]) for i in range(args.steps)]
+    ms = hip.elapsed_ms(ev[0], ev[args.steps])
+    hip.destroy(ev)
+    ms_per_step = ms / args.steps
+    value = B * T * args.steps / (ms / 1e3)
+
+    nk = 8 * args.steps
+    kev = hip.events(2 * nk)
+    kinds = (ctypes.c_int * nk)()
+    L.lib().lrt_profile_attach(ctypes.cast(kev, ctypes.c_void_p), ctypes.cast(kinds, ctypes.c_void_p), nk)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    n_rec = L.lib().lrt_profile_count()
+    L.lib().lrt_profile_attach(None, None, 0)
+    dur = {}
+    for i in range(n_rec):
+        dur.setdefault(L.lib().lrt_kernel_name(kinds[i]).decode(), []).append(hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]))
+    hip.destroy(kev)
+    kernels = {n: {"launches": len(v), "avg_us": 1e3 * sum(v) / len(v), "total_us_per_step": 1e3 * sum(v) / args.steps}
+               for n, v in dur.items()}
+    # each kernel's method bytes per launch: its reads and writes of the token tensors (bf16)
+    xb, nb_ = B * T * D * 2, B * T * H * d * 2
+    own = {"k_conv_fwd": 2 * xb, "k_conv_bwd": 3 * xb, "k_gnorm_fwd": 3 * nb_, "k_gnorm_bwd": 5 * nb_,
+           "k_rows_reduce(conv dw)": 0, "k_rows_reduce(norm dw)": 0}
+    step_bytes = sum(own.get(n, 0) * k["launches"] / args.steps for n, k in kernels.items())
+    for n, k in kernels.items():
+        k["share_of_step"] = k["total_us_per_step"] / 1e3 / ms_per_step
+        if own.get(n):
+            k["method_gbs"] = own[n] / (k["avg_us"] / 1e6) / 1e9
+    dom = max(kernels, key=lambda n: kernels[n]["total_us_per_step"])
+    ach = own[dom] / (kernels[dom]["avg_us"] / 1e6) / 1e9
+    traffic = counted_traffic(wl)
+    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic.get(dom) if traffic is not None else None,
+            "kernel": dom, "method_bytes_per_launch": int(own[dom]), "avg_us": round(kernels[dom]["avg_us"], 2)}
+
+    for i in range(2):
+        step_torch(i)
+    torch.cuda.synchronize()
+    ev = hip.events(2)
+    hip.record(ev[0], stream)
+    for i in range(args.steps):
+        step_torch(i)
+    hip.record(ev[1], stream)
+    torch.cuda.synchronize()
+    tms = hip.elapsed_ms(ev[0], ev[1]) / args.steps
+    hip.destroy(ev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle.conv_norm as cn
+        t1, rows = time.perf_counter(), 0
+        while rows < B and time.perf_counter() - t1 < args.cpu_seconds:
+            sl = slice(rows, rows + 1)
+            cn.short_conv(x[sl], wc)
+            cn.short_conv_bwd(x[sl], wc, dy[sl])
+            cn.gated_rmsnorm(o[sl], z[sl], wn)
+            cn.gated_rmsnorm_bwd(o[sl], z[sl], wn, dyn[sl])
+            rows += 1
+        spent = time.perf_counter() - t1
+        cpu = {"value": round(rows * T / spent, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "cpu_model": cpu_model(),
+               "sample": f"{rows} of {B} sequences x {T} tokens, all channels, fp64 numpy ({spent:.1f} s)"}
+
+    line = {
+        "metric": metric, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "ms_per_step_p10": round(pct(per, 10), 4),
+        "ms_per_step_p50": round(pct(per, 50), 4), "ms_per_step_p90": round(pct(per, 90), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normal inputs resident in HBM)",
+        "config": {"workload": wl, "B": B, "T": T, "H": H, "d": d, "conv_channels": D, "conv_width": W, "op": op},
+        "step": {"method_bytes": int(step_bytes), "hbm_gbs": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+                 "hbm_frac": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "hbm_frac_of_copy": round(step_bytes / (ms_per_step / 1e3) / 1e9 / copy, 4)},
+        "copy_gbs": round(copy, 1), "wall_s_timed": round(wall, 4), "roofline": roof,
+        "kernels": {n: {k: round(v, 4) if isinstance(v, float) else v for k, v in dd.items()}
+                    for n, dd in kernels.items()},
+        "unfused_pipeline": {"ms_per_step": round(tms, 4), "fused_speedup": round(tms / ms_per_step, 3),
+                             "what": "torch conv1d (groups = channels) + silu and rms_norm * silu, with autograd"},
+        "cpu_baseline": cpu,
+    }
     print(json.dumps(line), flush=True)
     if args.copy_probe:
         copy_probe(torch, dev)

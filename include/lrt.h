@@ -321,6 +321,58 @@ int kda_bwd_varlen(const void* q, const void* k, const void* v, const float* log
                    int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The two steps either side of the mixer, as the single-pass fused kernels
+ * of the pretraining recipe (AMD ROCm blog "Pretraining hybrid LLMs with
+ * Primus", "Recipe", Table 4: the FLA fusion row names fused gated norm and
+ * short conv kernels; the epsilon row gives 1e-6).  The pages name the steps
+ * without defining them; the library computes:
+ *
+ * short_conv_fwd: the short convolution on the mixer's q, k or v projection,
+ *   a causal depthwise convolution of width W over the tokens of each
+ *   sequence followed by SiLU:
+ *     pre[t, c] = sum_{j<W} w[c, j] x[t - (W - 1) + j, c],  y = pre * sigmoid(pre),
+ *   tokens before the sequence start counting as zero.  x, y: [n_seq, T, D]
+ *   (dense, cu_seqlens NULL) or one packed row [1, T, D] holding n_seq
+ *   sequences at [cu_seqlens[s], cu_seqlens[s + 1]) (the mixers' varlen
+ *   convention: n_seq + 1 int32, cu[0] = 0, non-decreasing, cu[n_seq] = T;
+ *   malformed tables are clamped, results then undefined); dtype LRT_F32 or
+ *   LRT_BF16.  w: [D, W] fp32 (tap W - 1 multiplies the current token).
+ *   D a multiple of 8 below 2^24; W in {2, 3, 4}; at most 2^31 - 1 tokens.
+ *   q, k and v may go through one call as the columns of one [.., 3 D]
+ *   tensor.  y must not alias x (LRT_ERR_SHAPE).
+ * short_conv_bwd: dx [like x] and dw [D, W] fp32 (overwritten) of
+ *   L = sum(dy * y), from x, w and dy; dx aliases neither x nor dy.
+ *   Workspace: short_conv_bwd_workspace_bytes(tokens, D, W) bytes, 16-byte
+ *   aligned (tokens = n_seq * T dense, T packed); (size_t)-1 for invalid
+ *   sizes.  dw is summed in a fixed order: repeated calls are bitwise equal.
+ *
+ * gated_rmsnorm_fwd: the mixer's output gate and norm over rows of d values
+ *   (one token and head each):  y = o / sqrt(mean(o^2) + eps) * w * silu(z).
+ *   o, z, y: [rows, d] dtype (y aliases neither, LRT_ERR_SHAPE); w: [d] fp32; d in
+ *   {16, 32, 64, 128, 256}; rows <= 2^31 - 1; eps in [0, 1].
+ * gated_rmsnorm_bwd: do, dz [rows, d] dtype and dw [d] fp32 (overwritten) of
+ *   L = sum(dy * y); do and dz alias no input.  Workspace:
+ *   gated_rmsnorm_bwd_workspace_bytes(rows, d) bytes, 16-byte aligned.
+ *   Deterministic as above.
+ *
+ * All: device pointers; token tensors and workspaces 16-byte aligned, w, dw
+ * and cu_seqlens 4-byte aligned; nothing allocated or synchronised; errors
+ * (LRT_ERR_*) returned before anything is enqueued.  With no tokens or rows
+ * the forwards do nothing and the backwards write dw = 0.
+ */
+int short_conv_fwd(const void* x, const float* w, void* y, const int* cu_seqlens, int n_seq, int T, int D, int W,
+                   int dtype, void* stream);
+int short_conv_bwd(const void* x, const float* w, const void* dy, void* dx, float* dw, const int* cu_seqlens,
+                   int n_seq, int T, int D, int W, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+size_t short_conv_bwd_workspace_bytes(long long n_tokens, int D, int W);
+int gated_rmsnorm_fwd(const void* o, const void* z, const float* w, void* y, long long rows, int d, float eps,
+                      int dtype, void* stream);
+int gated_rmsnorm_bwd(const void* o, const void* z, const float* w, const void* dy, void* d_o, void* dz, float* dw,
+                      long long rows, int d, float eps, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream);
+size_t gated_rmsnorm_bwd_workspace_bytes(long long rows, int d);
+
+/*
  * Workspace bytes needed by `op` (LRT_OP_*) at these sizes.  Returns
  * (size_t)-1 for invalid arguments.  0 is never returned for valid ones.
  */

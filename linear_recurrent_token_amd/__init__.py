@@ -38,7 +38,8 @@ OP_KDA_BWD, OP_KDA_BWD_VARLEN = 8, 9
 EXPORTS = ("gdn_fwd", "gdn_bwd", "gdn_fwd_train", "gdn_bwd_saved", "gdn_fwd_noalloc", "kda_fwd", "ssd_fwd",
            "ssd_bwd", "ssd_fwd_train", "ssd_bwd_saved", "gdn_fwd_varlen", "kda_fwd_varlen", "gdn_bwd_varlen",
            "gdn_fwd_fused", "kda_fwd_fused", "kda_bwd", "kda_bwd_varlen", "kda_fwd_train", "kda_bwd_saved",
-           "kda_fwd_fused_lowrank",
+           "kda_fwd_fused_lowrank", "short_conv_fwd", "short_conv_bwd", "short_conv_bwd_workspace_bytes",
+           "gated_rmsnorm_fwd", "gated_rmsnorm_bwd", "gated_rmsnorm_bwd_workspace_bytes",
            "lrt_workspace_bytes", "lrt_status_string", "lrt_profile_attach", "lrt_profile_count",
            "lrt_kernel_name")
 NOALLOC_MAX_BYTES = 64 << 20  # LRT_NOALLOC_MAX_BYTES
@@ -81,6 +82,17 @@ def lib():
         L.kda_fwd_train.argtypes = [vp] * 8 + [ci] * 7 + [vp, sz, vp]
         L.kda_fwd_fused_lowrank.argtypes = [vp] * 5 + [ci] + [vp] * 4 + [ci] * 7 + [vp, sz, vp]
         L.kda_bwd_saved.argtypes = [vp] * 14 + [ci] * 7 + [vp, sz, vp]
+        ll, cf = ctypes.c_longlong, ctypes.c_float
+        L.short_conv_fwd.argtypes = [vp] * 4 + [ci] * 5 + [vp]
+        L.short_conv_bwd.argtypes = [vp] * 6 + [ci] * 5 + [vp, sz, vp]
+        L.short_conv_bwd_workspace_bytes.argtypes = [ll, ci, ci]
+        L.short_conv_bwd_workspace_bytes.restype = sz
+        L.gated_rmsnorm_fwd.argtypes = [vp] * 4 + [ll, ci, cf, ci, vp]
+        L.gated_rmsnorm_bwd.argtypes = [vp] * 7 + [ll, ci, cf, ci, vp, sz, vp]
+        L.gated_rmsnorm_bwd_workspace_bytes.argtypes = [ll, ci]
+        L.gated_rmsnorm_bwd_workspace_bytes.restype = sz
+        for f in ("short_conv_fwd", "short_conv_bwd", "gated_rmsnorm_fwd", "gated_rmsnorm_bwd"):
+            getattr(L, f).restype = ci
         for f in ("gdn_fwd", "kda_fwd", "ssd_fwd", "gdn_bwd", "ssd_bwd", "gdn_fwd_train", "gdn_bwd_saved",
                   "ssd_fwd_train", "ssd_bwd_saved", "gdn_fwd_noalloc", "gdn_fwd_varlen", "kda_fwd_varlen",
                   "gdn_bwd_varlen", "gdn_fwd_fused", "kda_fwd_fused", "kda_bwd", "kda_bwd_varlen",
@@ -469,3 +481,87 @@ def _bwd(delta, q, k, v, log_a, beta, h0, do, dht, chunk, want_dh0, workspace, o
     if rc != 0:
         raise LrtError(fn, rc)
     return gq, gk, gv, gla, gb, gh0
+
+
+# ------------------------------------------------------------------------
+# The steps either side of the mixer: short convolution (+ SiLU) on its
+# q/k/v projections and gated RMSNorm on its output (lrt.h documents them).
+
+def _conv_args(x, w, cu_seqlens):
+    if x.device.type != "cuda" or x.dim() != 3 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, T, D] tensor on a GPU device")
+    B, T, D = x.shape
+    if w.dtype != torch.float32 or w.device != x.device or w.dim() != 2 or w.shape[0] != D or not w.is_contiguous():
+        raise ValueError("w must be a contiguous float32 [D, W] tensor on x's device")
+    if cu_seqlens is None:
+        return B, T, D, int(w.shape[1]), None
+    if B != 1:
+        raise ValueError("packed sequences take x as [1, T, D]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != x.device or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be an int32 vector on x's device")
+    return int(cu_seqlens.numel()) - 1, T, D, int(w.shape[1]), cu_seqlens
+
+
+def short_conv(x, w, cu_seqlens=None, out=None):
+    """silu(causal depthwise conv(x, w)) per sequence: x [B, T, D] (or packed
+    [1, T, D] with cu_seqlens), w [D, W] float32.  Returns y like x."""
+    n, T, D, W, cu = _conv_args(x, w, cu_seqlens)
+    y = torch.empty_like(x) if out is None else out
+    _check(x.device, x.dtype, "out", y, tuple(x.shape), x.dtype)
+    rc = lib().short_conv_fwd(_p(x), _p(w), _p(y), _p(cu), n, T, D, W, _dtype_code(x), _stream(x.device))
+    if rc != 0:
+        raise LrtError("short_conv_fwd", rc)
+    return y
+
+
+def short_conv_bwd(x, w, dy, cu_seqlens=None, workspace=None):
+    """(dx, dw) of sum(dy * short_conv(x, w)); dw float32 [D, W]."""
+    n, T, D, W, cu = _conv_args(x, w, cu_seqlens)
+    _check(x.device, x.dtype, "dy", dy, tuple(x.shape), x.dtype)
+    need = int(lib().short_conv_bwd_workspace_bytes(x.shape[0] * T, D, W))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    dx = torch.empty_like(x)
+    dw = torch.empty((D, W), dtype=torch.float32, device=x.device)
+    rc = lib().short_conv_bwd(_p(x), _p(w), _p(dy), _p(dx), _p(dw), _p(cu), n, T, D, W, _dtype_code(x),
+                              _p(workspace), workspace.numel() * workspace.element_size(), _stream(x.device))
+    if rc != 0:
+        raise LrtError("short_conv_bwd", rc)
+    return dx, dw
+
+
+def _norm_args(o, z, w):
+    if o.device.type != "cuda" or not o.is_contiguous():
+        raise ValueError("o must be a contiguous tensor on a GPU device")
+    d = int(o.shape[-1])
+    _check(o.device, o.dtype, "z", z, tuple(o.shape), o.dtype)
+    _check(o.device, o.dtype, "w", w, (d,), torch.float32)
+    return o.numel() // d if d else 0, d
+
+
+def gated_rmsnorm(o, z, w, eps=1e-6):
+    """o / sqrt(mean(o^2) + eps) * w * silu(z) over the last axis; w float32 [d]."""
+    rows, d = _norm_args(o, z, w)
+    y = torch.empty_like(o)
+    rc = lib().gated_rmsnorm_fwd(_p(o), _p(z), _p(w), _p(y), rows, d, float(eps), _dtype_code(o),
+                                 _stream(o.device))
+    if rc != 0:
+        raise LrtError("gated_rmsnorm_fwd", rc)
+    return y
+
+
+def gated_rmsnorm_bwd(o, z, w, dy, eps=1e-6, workspace=None):
+    """(do, dz, dw) of sum(dy * gated_rmsnorm(o, z, w)); dw float32 [d]."""
+    rows, d = _norm_args(o, z, w)
+    _check(o.device, o.dtype, "dy", dy, tuple(o.shape), o.dtype)
+    need = int(lib().gated_rmsnorm_bwd_workspace_bytes(rows, d))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=o.device)
+    do, dz = torch.empty_like(o), torch.empty_like(o)
+    dw = torch.empty((d,), dtype=torch.float32, device=o.device)
+    rc = lib().gated_rmsnorm_bwd(_p(o), _p(z), _p(w), _p(dy), _p(do), _p(dz), _p(dw), rows, d, float(eps),
+                                 _dtype_code(o), _p(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(o.device))
+    if rc != 0:
+        raise LrtError("gated_rmsnorm_bwd", rc)
+    return do, dz, dw

@@ -62,7 +62,8 @@ void prof_after(void* stream) {
 static const char* const kKernelNames[kKNumKinds] = {
     "k_bwd_local", "k_dstate",   "k_grad",       "k_kda_prep", "k_state_copy", "k_wy",     "k_scan",
     "k_wy_bwd",    "k_scan_bwd", "k_scan_local", "k_carry",    "k_ssd_prep",   "k_ssd_fwd",
-    "k_varlen_plan", "k_kda_prep_bwd", "k_grad_kda", "k_kda_prep_fast", "k_kda_prep_fast_bwd", "k_list_reset"};
+    "k_varlen_plan", "k_kda_prep_bwd", "k_grad_kda", "k_kda_prep_fast", "k_kda_prep_fast_bwd", "k_list_reset",
+    "k_conv_fwd", "k_conv_bwd", "k_rows_reduce(conv dw)", "k_gnorm_fwd", "k_gnorm_bwd", "k_rows_reduce(norm dw)"};
 
 // Queried on every call (a device attribute read; nothing is cached between
 // calls).

@@ -201,6 +201,12 @@ enum KernelKind {
   kKKdaPrepFast,
   kKKdaPrepFastBwd,
   kKListReset,
+  kKConvFwd,
+  kKConvBwd,
+  kKConvDw,
+  kKNormFwd,
+  kKNormBwd,
+  kKNormDw,
   kKNumKinds
 };
 // Bracket one launch with the timing hook's events (no-ops unless attached).

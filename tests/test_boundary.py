@@ -317,3 +317,79 @@ def test_kda_backward_and_training_pair_validation(L):
     a = list(lr)
     a[18] = need - 1
     assert lib.kda_fwd_fused_lowrank(*a) == c["LRT_ERR_WORKSPACE"]
+
+
+def test_conv_and_gated_norm_validation(L):
+    """short_conv_* and gated_rmsnorm_*: every invalid argument is rejected
+    before a launch (each call below fails validation, so nothing runs)."""
+    c = codes()
+    lib = L.lib()
+    F = FAKE
+    SZ = ctypes.c_size_t(-1).value
+    # short_conv_fwd(x, w, y, cu, n_seq, T, D, W, dtype, stream)
+    conv = lambda x=F, w=F, y=F + 4096, cu=None, n=2, T=8, D=64, W=4, dt=1: lib.short_conv_fwd(
+        x, w, y, cu, n, T, D, W, dt, None)
+    assert conv(dt=7) == c["LRT_ERR_DTYPE"]
+    assert conv(D=12) == c["LRT_ERR_SHAPE"]
+    assert conv(D=0) == c["LRT_ERR_SHAPE"]
+    assert conv(W=5) == c["LRT_ERR_SHAPE"]
+    assert conv(W=1) == c["LRT_ERR_SHAPE"]
+    assert conv(n=0) == c["LRT_ERR_SHAPE"]
+    assert conv(T=-1) == c["LRT_ERR_SHAPE"]
+    assert conv(x=None) == c["LRT_ERR_NULL"]
+    assert conv(w=None) == c["LRT_ERR_NULL"]
+    assert conv(y=None) == c["LRT_ERR_NULL"]
+    assert conv(x=F + 8) == c["LRT_ERR_ALIGN"]
+    assert conv(y=F + 8) == c["LRT_ERR_ALIGN"]
+    assert conv(w=F + 2) == c["LRT_ERR_ALIGN"]
+    assert conv(cu=F + 2) == c["LRT_ERR_ALIGN"]
+    assert conv(y=F) == c["LRT_ERR_SHAPE"]  # in place
+    assert conv(T=0) == c["LRT_OK"]  # no tokens: nothing to do, nothing launched
+    # short_conv_bwd(x, w, dy, dx, dw, cu, n_seq, T, D, W, dtype, ws, ws_bytes, stream)
+    need = lib.short_conv_bwd_workspace_bytes(16, 64, 4)
+    assert need != SZ and need >= 256
+    cb = lambda x=F, w=F, dy=F + 4096, dx=F + 8192, dw=F, cu=None, n=2, T=8, D=64, W=4, dt=1, ws=F, wsb=need: \
+        lib.short_conv_bwd(x, w, dy, dx, dw, cu, n, T, D, W, dt, ws, wsb, None)
+    assert cb(wsb=need - 1) == c["LRT_ERR_WORKSPACE"]
+    assert cb(ws=None) == c["LRT_ERR_WORKSPACE"]
+    assert cb(ws=F + 8) == c["LRT_ERR_WORKSPACE"]
+    assert cb(dw=None) == c["LRT_ERR_NULL"]
+    assert cb(dx=None) == c["LRT_ERR_NULL"]
+    assert cb(dy=None) == c["LRT_ERR_NULL"]
+    assert cb(dw=F + 2) == c["LRT_ERR_ALIGN"]
+    assert cb(dx=F + 8) == c["LRT_ERR_ALIGN"]
+    assert cb(dx=F + 4096) == c["LRT_ERR_SHAPE"]  # dx aliases dy
+    assert cb(D=20) == c["LRT_ERR_SHAPE"]
+    for bad in ((-1, 64, 4), (16, 12, 4), (16, 64, 5), (1 << 31, 64, 4)):
+        assert lib.short_conv_bwd_workspace_bytes(*bad) == SZ, bad
+    # gated_rmsnorm_fwd(o, z, w, y, rows, d, eps, dtype, stream)
+    gn = lambda o=F, z=F + 4096, w=F, y=F + 8192, rows=10, d=128, eps=1e-6, dt=1: lib.gated_rmsnorm_fwd(
+        o, z, w, y, rows, d, eps, dt, None)
+    assert gn(dt=3) == c["LRT_ERR_DTYPE"]
+    assert gn(d=48) == c["LRT_ERR_SHAPE"]
+    assert gn(d=512) == c["LRT_ERR_SHAPE"]
+    assert gn(rows=-1) == c["LRT_ERR_SHAPE"]
+    assert gn(eps=-1.0) == c["LRT_ERR_SHAPE"]
+    assert gn(eps=float("nan")) == c["LRT_ERR_SHAPE"]
+    assert gn(o=None) == c["LRT_ERR_NULL"]
+    assert gn(z=None) == c["LRT_ERR_NULL"]
+    assert gn(w=None) == c["LRT_ERR_NULL"]
+    assert gn(y=None) == c["LRT_ERR_NULL"]
+    assert gn(o=F + 8) == c["LRT_ERR_ALIGN"]
+    assert gn(w=F + 2) == c["LRT_ERR_ALIGN"]
+    assert gn(y=F) == c["LRT_ERR_SHAPE"]  # y aliases o
+    assert gn(rows=0) == c["LRT_OK"]
+    # gated_rmsnorm_bwd(o, z, w, dy, do, dz, dw, rows, d, eps, dtype, ws, ws_bytes, stream)
+    nneed = lib.gated_rmsnorm_bwd_workspace_bytes(10, 128)
+    assert nneed != SZ and nneed > 0
+    gb = lambda o=F, z=F + 4096, w=F, dy=F + 8192, do=F + 12288, dz=F + 16384, dw=F, rows=10, d=128, ws=F, \
+        wsb=nneed: lib.gated_rmsnorm_bwd(o, z, w, dy, do, dz, dw, rows, d, 1e-6, 1, ws, wsb, None)
+    assert gb(wsb=nneed - 1) == c["LRT_ERR_WORKSPACE"]
+    assert gb(ws=None) == c["LRT_ERR_WORKSPACE"]
+    assert gb(dw=None) == c["LRT_ERR_NULL"]
+    assert gb(do=None) == c["LRT_ERR_NULL"]
+    assert gb(dz=F + 12288) == c["LRT_ERR_SHAPE"]  # dz aliases do
+    assert gb(do=F) == c["LRT_ERR_SHAPE"]  # do aliases o
+    assert gb(dz=F + 8) == c["LRT_ERR_ALIGN"]
+    assert lib.gated_rmsnorm_bwd_workspace_bytes(10, 100) == SZ
+    assert lib.gated_rmsnorm_bwd_workspace_bytes(-5, 128) == SZ
