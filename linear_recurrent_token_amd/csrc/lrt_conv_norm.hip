@@ -24,8 +24,7 @@ namespace lrt {
 
 namespace {
 
-constexpr int kConvTB = 16;     // tokens per block of one wave
-constexpr int kConvGroups = 64; // token-block groups of the backward (its dw partials)
+constexpr int kConvGroups = 64; // range groups (workgroups per piece group; the backward's dw partials)
 constexpr int kNormBlocks = 1024;  // workgroups of the norm backward (its dw partials)
 
 __device__ __forceinline__ float silu_f(float p) { return p * sigmoid_f(p); }
@@ -77,49 +76,61 @@ __device__ __forceinline__ void seq_bounds(const int* cu, int n, int T, int ntok
   s1 = max(min(cu[lo + 1], ntok), t + 1);
 }
 
+// Both convolution kernels: four channels per lane (8-byte bf16 / 16-byte
+// fp32 pieces: a wave covers 256 consecutive channels of a row); grid (piece
+// groups of 64, range groups); wave w of workgroup (gx, gy) walks the tokens
+// [r0, r1) of range q = gy * 4 + w in order, kConvCB rows at a time (issued
+// together, clamped addresses, zero selected outside the range), carrying
+// the last W - 1 rows of x (and, backward, the last W values of g) from one
+// chunk to the next, so only a range's first W - 1 rows (and, backward, the
+// W - 1 after it) are read twice.  A chunk whose window holds a sequence
+// boundary takes each token's own sequence bounds and masks (edge path).
+constexpr int kConvCB = 8;  // rows per chunk
+
+// tokens per range: the ranges of one piece group cover ntok
+__device__ __forceinline__ int conv_range(int ntok, int nranges) {
+  const int r = (ntok + nranges - 1) / nranges;
+  return (r + kConvCB - 1) / kConvCB * kConvCB;
+}
+
 // ------------------------------------------------------------ k_conv_fwd
-// Four channels per lane (8-byte bf16 / 16-byte fp32 pieces: a wave covers 256
-// consecutive channels of a row).  grid (piece groups of 64, token-block
-// groups); wave w of workgroup (gx, gy) takes token blocks
-// gy * 4 + w + i * 4 * gridDim.y.  A block's rows and the W - 1 before it load
-// up front (clamped addresses, zero selected outside the block's window);
-// each output row is then W fused multiply-adds of rows in registers.
-// edge: a sequence boundary lies inside the block's window, so each token
-// masks the taps before its own sequence start.
 template <typename E, int W>
 __global__ __launch_bounds__(256) void k_conv_fwd(const E* __restrict__ x, const float* __restrict__ w,
                                                   E* __restrict__ y, const int* __restrict__ cu, int n, int T,
                                                   int ntok, int D) {
   typedef typename Vec4<E>::T Raw;
-  constexpr int R = kConvTB + W - 1;
   const int P = D / 4, p = blockIdx.x * 64 + lane_id();
-  if (p >= P) return;
-  const int ntb = (ntok + kConvTB - 1) / kConvTB;
-  f32x4 wv[W];
+  const int RL = conv_range(ntok, 4 * gridDim.y);
+  const int r0 = (blockIdx.y * 4 + wave_id()) * RL, r1 = min(r0 + RL, ntok);
+  if (p >= P || r0 >= ntok) return;
+  f32x4 wv[W], xw[W];
 #pragma unroll
   for (int j = 0; j < W; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) wv[j][e] = w[(size_t)(p * 4 + e) * W + j];
-  for (int tb = blockIdx.y * 4 + wave_id(); tb < ntb; tb += 4 * gridDim.y) {
-    const int t0 = tb * kConvTB, t1 = min(t0 + kConvTB, ntok);
-    Raw raw[R];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int t = t0 - (W - 1) + i;
-      const Raw r = load4_raw<E>(x + (size_t)min(max(t, 0), ntok - 1) * D + p * 4);
-      raw[i] = (t >= 0 && t < t1) ? r : Vec4<E>::pack(zero4());
+  for (int j = 0; j < W - 1; ++j) {
+    const int t = r0 - (W - 1) + j;
+    const f32x4 r = load4<E>(x + (size_t)max(t, 0) * D + p * 4);
+    xw[j] = t >= 0 ? r : zero4();
+  }
+  auto load_chunk = [&](Raw(&raw)[kConvCB], int c0) {
+#pragma unroll
+    for (int i = 0; i < kConvCB; ++i) {
+      const int t = c0 + i;
+      const Raw r = load4_raw<E>(x + (size_t)min(t, ntok - 1) * D + p * 4);
+      raw[i] = t < r1 ? r : Vec4<E>::pack(zero4());
     }
+  };
+  auto do_chunk = [&](const Raw(&raw)[kConvCB], int c0) {
     int s0, s1;
-    seq_bounds(cu, n, T, ntok, t0, s0, s1);
-    const bool edge = s0 > t0 - (W - 1) || s1 < t1;  // wave-uniform
-    f32x4 xw[W];
+    seq_bounds(cu, n, T, ntok, c0, s0, s1);
+    const bool edge = s0 > c0 - (W - 1) || s1 < min(c0 + kConvCB, ntok);  // wave-uniform
 #pragma unroll
-    for (int j = 0; j < W - 1; ++j) xw[j] = Vec4<E>::unpack(raw[j]);
-#pragma unroll
-    for (int i = 0; i < kConvTB; ++i) {
-      const int t = t0 + i;
-      xw[W - 1] = Vec4<E>::unpack(raw[i + W - 1]);
-      if (t < t1) {
+    for (int i = 0; i < kConvCB; ++i) {
+      const int t = c0 + i;
+      xw[W - 1] = Vec4<E>::unpack(raw[i]);
+      if (t < r1) {
         int a = s0;  // first token of t's sequence
         if (edge) {
           int b_;
@@ -137,71 +148,72 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const E* __restrict__ x, const
 #pragma unroll
       for (int j = 0; j < W - 1; ++j) xw[j] = xw[j + 1];
     }
+  };
+  for (int c0 = r0; c0 < r1; c0 += kConvCB) {
+    Raw raw[kConvCB];
+    load_chunk(raw, c0);
+    do_chunk(raw, c0);
   }
 }
 
 // ------------------------------------------------------------ k_conv_bwd
-// Same walk over blocks of TBB tokens (16 bf16 / 8 fp32: the block's rows
-// stay in registers).  All rows a block needs are issued first: x rows
-// t0 - (W - 1) .. t1 + W - 2 and dy rows t0 .. t1 + W - 2 (the look-ahead its
-// dx needs).  Then, rolling over t' = t0 .. t1 + W - 2:
+// Rolling over t' = r0 .. r1 + W - 2 (the W - 1 rows after the range are the
+// look-ahead its last dx rows need):
 //   g[t'] = dy[t'] silu'(pre[t']),
-//   dx[t] = sum_m w[W - 1 - m] g[t + m]  for t = t' - (W - 1), t + m inside
-//           t's sequence (the last W values of g in registers),
-//   dw[j] += g[t'] x[t' - (W - 1) + j]   for t' in [t0, t1), taps inside t''s
+//   dx[t] = sum_m w[W - 1 - m] g[t + m]  for t = t' - (W - 1) in [r0, r1),
+//           t + m inside t's sequence,
+//   dw[j] += g[t'] x[t' - (W - 1) + j]   for t' in [r0, r1), taps inside t''s
 //           sequence,
-// dw summed in registers over a wave's blocks, then over the four waves in
-// LDS, into partial[gridDim.y][D][W] for k_rows_reduce.
-template <typename E>
-constexpr int conv_tb_bwd() {
-  return sizeof(E) == 2 ? 8 : 8;
-}
+// dw summed in registers over the range, then over the four waves in LDS,
+// into partial[gridDim.y][D][W] for k_rows_reduce.
 template <typename E, int W>
 __global__ __launch_bounds__(256) void k_conv_bwd(const E* __restrict__ x, const float* __restrict__ w,
                                                   const E* __restrict__ dy, E* __restrict__ dx,
                                                   float* __restrict__ partial, const int* __restrict__ cu, int n,
                                                   int T, int ntok, int D) {
   typedef typename Vec4<E>::T Raw;
-  constexpr int TBB = conv_tb_bwd<E>(), NX = TBB + 2 * (W - 1), NG = TBB + W - 1;
   __shared__ float sdw[4][64][4 * W];
   const int P = D / 4, p = blockIdx.x * 64 + lane_id(), wv_ = wave_id();
   const bool active = p < P;
   const int pc = active ? p : 0;  // inactive lanes read piece 0 and write nothing
-  const int ntb = (ntok + TBB - 1) / TBB;
-  f32x4 wv[W], dwa[W];
+  const int RL = conv_range(ntok, 4 * gridDim.y);
+  const int r0 = (blockIdx.y * 4 + wv_) * RL, r1 = min(r0 + RL, ntok), lim = min(r1 + W - 1, ntok);
+  f32x4 wv[W], dwa[W], xw[W], gh[W];
 #pragma unroll
   for (int j = 0; j < W; ++j) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) wv[j][e] = w[(size_t)(pc * 4 + e) * W + j];
     dwa[j] = zero4();
+    gh[j] = zero4();
   }
-  for (int tb = blockIdx.y * 4 + wv_; tb < ntb; tb += 4 * gridDim.y) {
-    const int t0 = tb * TBB, t1 = min(t0 + TBB, ntok), lim = min(t1 + W - 1, ntok);
-    Raw xr[NX], dr[NG];
+  if (r0 < ntok) {
 #pragma unroll
-    for (int i = 0; i < NX; ++i) {
-      const int t = t0 - (W - 1) + i;
-      const Raw r = load4_raw<E>(x + (size_t)min(max(t, 0), ntok - 1) * D + pc * 4);
-      xr[i] = (t >= 0 && t < lim) ? r : Vec4<E>::pack(zero4());
+    for (int j = 0; j < W - 1; ++j) {
+      const int t = r0 - (W - 1) + j;
+      const f32x4 r = load4<E>(x + (size_t)max(t, 0) * D + pc * 4);
+      xw[j] = t >= 0 ? r : zero4();
     }
+  }
+  const int end = r1 + W - 1;  // the last chunk covers the look-ahead rows
+  auto load_chunk = [&](Raw(&xr)[kConvCB], Raw(&dr)[kConvCB], int c0) {
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int t = t0 + i;
-      const Raw r = load4_raw<E>(dy + (size_t)min(t, ntok - 1) * D + pc * 4);
-      dr[i] = t < lim ? r : Vec4<E>::pack(zero4());
+    for (int i = 0; i < kConvCB; ++i) {
+      const int t = c0 + i;
+      const size_t off = (size_t)min(t, ntok - 1) * D + pc * 4;
+      const Raw a = load4_raw<E>(x + off), b = load4_raw<E>(dy + off);
+      xr[i] = t < lim ? a : Vec4<E>::pack(zero4());
+      dr[i] = t < lim ? b : Vec4<E>::pack(zero4());
     }
+  };
+  auto do_chunk = [&](const Raw(&xr)[kConvCB], const Raw(&dr)[kConvCB], int c0) {
     int s0, s1;
-    seq_bounds(cu, n, T, ntok, t0, s0, s1);
-    const bool edge = s0 > t0 - (W - 1) || s1 < lim;  // wave-uniform
-    f32x4 xw[W], gh[W];
+    seq_bounds(cu, n, T, ntok, min(c0, ntok - 1), s0, s1);
+    // wave-uniform: a boundary inside the chunk's window [c0 - (W - 1), c0 + kConvCB)
+    const bool edge = s0 > c0 - (W - 1) || s1 < min(c0 + kConvCB, ntok);
 #pragma unroll
-    for (int j = 0; j < W; ++j) gh[j] = zero4();
-#pragma unroll
-    for (int j = 0; j < W - 1; ++j) xw[j] = Vec4<E>::unpack(xr[j]);
-#pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int tp = t0 + i;
-      xw[W - 1] = Vec4<E>::unpack(xr[i + W - 1]);
+    for (int i = 0; i < kConvCB; ++i) {
+      const int tp = c0 + i;
+      xw[W - 1] = Vec4<E>::unpack(xr[i]);
       const f32x4 dv = Vec4<E>::unpack(dr[i]);
       int a = s0;
       if (edge && tp < ntok) {
@@ -215,7 +227,7 @@ __global__ __launch_bounds__(256) void k_conv_bwd(const E* __restrict__ x, const
       f32x4 g;
 #pragma unroll
       for (int e = 0; e < 4; ++e) g[e] = dv[e] * dsilu_f(pre[e]);
-      if (i < TBB && tp < t1) {
+      if (tp < r1) {
 #pragma unroll
         for (int j = 0; j < W; ++j)
           if (!edge || tp - (W - 1) + j >= a) dwa[j] += g * xw[j];
@@ -223,24 +235,27 @@ __global__ __launch_bounds__(256) void k_conv_bwd(const E* __restrict__ x, const
 #pragma unroll
       for (int m = 0; m < W - 1; ++m) gh[m] = gh[m + 1];
       gh[W - 1] = g;  // gh[m] = g[tp - (W - 1) + m]
-      if (i >= W - 1) {
-        const int t = tp - (W - 1);
-        if (t < t1 && active) {
-          int b = s1;  // end of t's sequence
-          if (edge) {
-            int a_;
-            seq_bounds(cu, n, T, ntok, t, a_, b);
-          }
-          f32x4 o = zero4();
-#pragma unroll
-          for (int m = 0; m < W; ++m)
-            if (!edge || t + m < b) o += wv[W - 1 - m] * gh[m];
-          store4<E>(dx + (size_t)t * D + p * 4, o);
+      const int t = tp - (W - 1);
+      if (t >= r0 && t < r1 && active) {
+        int b = s1;  // end of t's sequence
+        if (edge) {
+          int a_;
+          seq_bounds(cu, n, T, ntok, t, a_, b);
         }
+        f32x4 o = zero4();
+#pragma unroll
+        for (int m = 0; m < W; ++m)
+          if (!edge || t + m < b) o += wv[W - 1 - m] * gh[m];
+        store4<E>(dx + (size_t)t * D + p * 4, o);
       }
 #pragma unroll
       for (int j = 0; j < W - 1; ++j) xw[j] = xw[j + 1];
     }
+  };
+  for (int c0 = r0; r0 < ntok && c0 < end; c0 += kConvCB) {
+    Raw xr[kConvCB], dr[kConvCB];
+    load_chunk(xr, dr, c0);
+    do_chunk(xr, dr, c0);
   }
   // the four waves' dw sums of this workgroup's pieces, added in wave order
 #pragma unroll
@@ -381,12 +396,11 @@ __global__ __launch_bounds__(256) void k_gnorm_bwd(const E* __restrict__ o, cons
 }
 
 
-// launch shapes
-int conv_groups_fwd(int ntok) { return max(1, min((ntok + 4 * kConvTB - 1) / (4 * kConvTB), 65535)); }
-template <typename E>
-int conv_groups_bwd(int ntok) {
-  return max(1, min((ntok + 4 * conv_tb_bwd<E>() - 1) / (4 * conv_tb_bwd<E>()), kConvGroups));
-}
+// launch shapes (range groups of four waves): the forward takes ranges down
+// to 32 rows, up to 256 groups; the backward at most kConvGroups (its dw
+// partials), ranges of at least 16 rows
+int conv_groups_fwd(int ntok) { return max(1, min((ntok + 127) / 128, 256)); }
+int conv_groups(int ntok) { return max(1, min((ntok + 63) / 64, kConvGroups)); }
 int gnorm_blocks(long long rows, int d, int esz) {
   const int per = 256 / (d / (16 / esz));
   const long long nb = (rows + per - 1) / per;
@@ -421,7 +435,7 @@ void conv_fwd_t(const void* x, const float* w, void* y, const int* cu, int n, in
 template <typename E, int W>
 void conv_bwd_t(const void* x, const float* w, const void* dy, void* dx, float* dw, float* partial, const int* cu,
                 int n, int T, int ntok, int D, hipStream_t st) {
-  const int P = D / 4, ng = conv_groups_bwd<E>(ntok);
+  const int P = D / 4, ng = conv_groups(ntok);
   LRT_LAUNCH(kKConvBwd, (k_conv_bwd<E, W>), dim3((P + 63) / 64, ng), dim3(256), st, (const E*)x, w,
              (const E*)dy, (E*)dx, partial, cu, n, T, ntok, D);
   LRT_LAUNCH(kKConvDw, k_rows_reduce<kReduceWaves>, dim3((D * W + 63) / 64), dim3(64 * kReduceWaves), st,
@@ -439,7 +453,7 @@ extern "C" {
 size_t short_conv_bwd_workspace_bytes(long long n_tokens, int D, int W) {
   if (n_tokens < 0 || n_tokens > 0x7fffffffLL || D < 8 || D % 8 != 0 || D >= (1 << 24) || W < 2 || W > 4)
     return (size_t)-1;
-  // the partial sums of at most kConvGroups token-block groups (either dtype)
+  // the partial sums of at most kConvGroups range groups
   return (size_t)kConvGroups * D * W * sizeof(float);
 }
 
