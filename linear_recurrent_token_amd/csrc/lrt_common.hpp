@@ -85,11 +85,40 @@ __device__ __forceinline__ int xcd_group(int bid, int nblocks) {
 // *_fused entry points to the raw projections:
 //   q, k  <- x / sqrt(sum x^2 + kL2Eps) per (token, head) row over d_k;
 //   beta  <- sigmoid(z);   log a <- -softplus(z) = -(max(z, 0) + log(1 + e^-|z|))
-// (the stable form; the hardware exp / log, a few ulp in fp32).
+// (the stable form).  They run on the hardware's base-2 exponential and
+// logarithm, reciprocal and reciprocal square root (about 1 ulp each), whose
+// arguments stay in range here: 1 + e^-|z| lies in [1, 2], a reciprocal of
+// 1 + e^-z is 0 for an infinite argument, and a row's sum of squares plus
+// kL2Eps is positive.
 constexpr float kL2Eps = 1e-6f;
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + __expf(-z)); }
+constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float hw_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+__device__ __forceinline__ float sigmoid_f(float z) { return hw_rcp(1.f + hw_exp2(-z * kLog2e)); }
 __device__ __forceinline__ float neg_softplus_f(float z) {
-  return -(fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z))));
+  return -(fmaxf(z, 0.f) + kLn2 * hw_log2(1.f + hw_exp2(-fabsf(z) * kLog2e)));
+}
+
+// Sum of x over aligned groups of G consecutive lanes (G a power of two up to
+// 64), every lane of a group receiving its group's sum.  Inside a 16-lane row
+// the partner values move by DPP (quad permutations, then the half-row and
+// row mirrors), with no LDS traffic; wider groups add ds_bpermute steps.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+template <int G>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "lane groups are powers of two");
+  if constexpr (G >= 2) x += dpp_move<0xB1>(x);   // quad_perm [1, 0, 3, 2]: lane ^ 1
+  if constexpr (G >= 4) x += dpp_move<0x4E>(x);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+  if constexpr (G >= 8) x += dpp_move<0x141>(x);  // row_half_mirror: the other quad of the 8
+  if constexpr (G >= 16) x += dpp_move<0x140>(x); // row_mirror: the other half of the row
+  if constexpr (G >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (G >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
 }
 
 // ------------------------------------------------------------ sequence map
@@ -464,9 +493,8 @@ struct Tile {
       float ss = 0.f;
 #pragma unroll
       for (int i = 0; i < V; ++i) ss += to_f(e[i]) * to_f(e[i]);
-#pragma unroll
-      for (int m = 1; m < PR; m <<= 1) ss += __shfl_xor(ss, m, 64);
-      const float sc = 1.f / sqrtf(ss + eps);
+      ss = lane_group_sum<PR>(ss);
+      const float sc = hw_rsq(ss + eps);
 #pragma unroll
       for (int i = 0; i < V; ++i) e[i] = from_f<E>(to_f(e[i]) * sc);
       __builtin_memcpy(&x[s], e, 16);

@@ -308,20 +308,15 @@ __global__ __launch_bounds__(64 * NWR) void k_rows_reduce(const float* __restric
 constexpr int kReduceWaves = 16;
 
 // ------------------------------------------------------------ gated norm
-// G = d / V lanes per row (a power of two dividing 64): a row's sum of
-// squares is a butterfly over its G lanes.  A thread keeps one piece index
+// G = d / V lanes per row (a power of two dividing 64): a row's sums run over
+// its G lanes (lane_group_sum).  A thread keeps one piece index
 // (threadIdx.x % G) for every row it visits, so its w piece loads once.
-__device__ __forceinline__ float group_sum(float x, int G) {
-  for (int o = G >> 1; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
-template <typename E>
+template <typename E, int G>
 __global__ __launch_bounds__(256) void k_gnorm_fwd(const E* __restrict__ o, const E* __restrict__ z,
                                                    const float* __restrict__ w, E* __restrict__ y, int rows, int d,
                                                    float eps) {
-  constexpr int V = 16 / (int)sizeof(E);
-  const int G = d / V, pc = threadIdx.x % G, per = 256 / G;
+  constexpr int V = 16 / (int)sizeof(E), per = 256 / G;
+  const int pc = threadIdx.x % G;
   float wv[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) wv[e] = w[pc * V + e];
@@ -333,7 +328,7 @@ __global__ __launch_bounds__(256) void k_gnorm_fwd(const E* __restrict__ o, cons
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < V; ++e) ss += ov[e] * ov[e];
-    const float rstd = rsqrtf(group_sum(ss, G) / (float)d + eps);
+    const float rstd = hw_rsq(lane_group_sum<G>(ss) / (float)d + eps);
 #pragma unroll
     for (int e = 0; e < V; ++e) out[e] = ov[e] * rstd * wv[e] * silu_f(zv[e]);
     piece_store<E>(y + off, out);
@@ -343,14 +338,14 @@ __global__ __launch_bounds__(256) void k_gnorm_fwd(const E* __restrict__ o, cons
 // do = r (dn - n mean(dn n)), dn = dy w silu(z); dz = dy n w silu'(z);
 // dw partial per workgroup: sum over its rows of dy n silu(z), the row slots
 // added in slot order.
-template <typename E>
+template <typename E, int G>
 __global__ __launch_bounds__(256) void k_gnorm_bwd(const E* __restrict__ o, const E* __restrict__ z,
                                                    const float* __restrict__ w, const E* __restrict__ dy,
                                                    E* __restrict__ dout, E* __restrict__ dz,
                                                    float* __restrict__ partial, int rows, int d, float eps) {
-  constexpr int V = 16 / (int)sizeof(E);
+  constexpr int V = 16 / (int)sizeof(E), per = 256 / G;
   __shared__ float sdw[256][V];
-  const int G = d / V, pc = threadIdx.x % G, per = 256 / G;
+  const int pc = threadIdx.x % G;
   float wv[V], dwa[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) {
@@ -366,7 +361,7 @@ __global__ __launch_bounds__(256) void k_gnorm_bwd(const E* __restrict__ o, cons
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < V; ++e) ss += ov[e] * ov[e];
-    const float rstd = rsqrtf(group_sum(ss, G) / (float)d + eps);
+    const float rstd = hw_rsq(lane_group_sum<G>(ss) / (float)d + eps);
     float n[V], dn[V], dzv[V], dot = 0.f;
 #pragma unroll
     for (int e = 0; e < V; ++e) {
@@ -377,7 +372,7 @@ __global__ __launch_bounds__(256) void k_gnorm_bwd(const E* __restrict__ o, cons
       dwa[e] += gv[e] * n[e] * sz;
       dot += dn[e] * n[e];
     }
-    const float mdot = group_sum(dot, G) / (float)d;
+    const float mdot = lane_group_sum<G>(dot) / (float)d;
     float dov[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) dov[e] = rstd * (dn[e] - n[e] * mdot);
@@ -405,6 +400,30 @@ int gnorm_blocks(long long rows, int d, int esz) {
   const int per = 256 / (d / (16 / esz));
   const long long nb = (rows + per - 1) / per;
   return (int)(nb < 1 ? 1 : nb > kNormBlocks ? kNormBlocks : nb);
+}
+
+// the norm kernels at G = d / V lanes per row
+template <typename E>
+void gnorm_fwd_t(const void* o, const void* z, const float* w, void* y, int rows, int d, float eps, int nb,
+                 hipStream_t st) {
+  constexpr int V = 16 / (int)sizeof(E);
+#define LRT_GN(G_)                                                                                         \
+  if (d / V == G_)                                                                                         \
+    LRT_LAUNCH(kKNormFwd, (k_gnorm_fwd<E, G_>), dim3(nb), dim3(256), st, (const E*)o, (const E*)z, w, (E*)y, \
+               rows, d, eps);
+  LRT_GN(2) LRT_GN(4) LRT_GN(8) LRT_GN(16) LRT_GN(32) LRT_GN(64)
+#undef LRT_GN
+}
+template <typename E>
+void gnorm_bwd_t(const void* o, const void* z, const float* w, const void* dy, void* d_o, void* dz, float* partial,
+                 int rows, int d, float eps, int nb, hipStream_t st) {
+  constexpr int V = 16 / (int)sizeof(E);
+#define LRT_GN(G_)                                                                                             \
+  if (d / V == G_)                                                                                             \
+    LRT_LAUNCH(kKNormBwd, (k_gnorm_bwd<E, G_>), dim3(nb), dim3(256), st, (const E*)o, (const E*)z, w,           \
+               (const E*)dy, (E*)d_o, (E*)dz, partial, rows, d, eps);
+  LRT_GN(2) LRT_GN(4) LRT_GN(8) LRT_GN(16) LRT_GN(32) LRT_GN(64)
+#undef LRT_GN
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -541,11 +560,9 @@ int gated_rmsnorm_fwd(const void* o, const void* z, const float* w, void* y, lon
   const int nb = gnorm_blocks(rows, d, esz);
   hipStream_t st = (hipStream_t)stream;
   if (dtype == LRT_BF16)
-    LRT_LAUNCH(kKNormFwd, k_gnorm_fwd<bf16>, dim3(nb), dim3(256), st, (const bf16*)o, (const bf16*)z, w, (bf16*)y,
-               (int)rows, d, eps);
+    gnorm_fwd_t<bf16>(o, z, w, y, (int)rows, d, eps, nb, st);
   else
-    LRT_LAUNCH(kKNormFwd, k_gnorm_fwd<float>, dim3(nb), dim3(256), st, (const float*)o, (const float*)z, w,
-               (float*)y, (int)rows, d, eps);
+    gnorm_fwd_t<float>(o, z, w, y, (int)rows, d, eps, nb, st);
   return hipGetLastError() == hipSuccess ? LRT_OK : LRT_ERR_LAUNCH;
 }
 
@@ -569,11 +586,9 @@ int gated_rmsnorm_bwd(const void* o, const void* z, const float* w, const void* 
   const int nb = rows > 0 ? gnorm_blocks(rows, d, esz) : 0;
   if (rows > 0) {
     if (dtype == LRT_BF16)
-      LRT_LAUNCH(kKNormBwd, k_gnorm_bwd<bf16>, dim3(nb), dim3(256), st, (const bf16*)o, (const bf16*)z, w,
-                 (const bf16*)dy, (bf16*)d_o, (bf16*)dz, partial, (int)rows, d, eps);
+      gnorm_bwd_t<bf16>(o, z, w, dy, d_o, dz, partial, (int)rows, d, eps, nb, st);
     else
-      LRT_LAUNCH(kKNormBwd, k_gnorm_bwd<float>, dim3(nb), dim3(256), st, (const float*)o, (const float*)z, w,
-                 (const float*)dy, (float*)d_o, (float*)dz, partial, (int)rows, d, eps);
+      gnorm_bwd_t<float>(o, z, w, dy, d_o, dz, partial, (int)rows, d, eps, nb, st);
   }
   LRT_LAUNCH(kKNormDw, k_rows_reduce<kReduceWaves>, dim3((d + 63) / 64), dim3(64 * kReduceWaves), st,
              (const float*)partial, dw, nb, d);

@@ -230,15 +230,20 @@ SEG_CASES = [
     ("kda_seg8_slow_C32", "kda", 1, 4096 - 5, 2, 64, 64, 32, "perdim", -6.0, 0.1),
     ("kda_seg4_perdim_C64", "kda", 1, 4096, 2, 128, 128, 64, "perdim", 0.0, 0.1),
     ("kda_seg4_lowrank_C64", "kda", 1, 4096, 2, 128, 128, 64, "lowrank", 0.0, 0.1),
+    # fp32 through the segment carry (its MFMA in fp32), at the fp32 bar: slow
+    # gates, small beta and a unit-scale h0, so the carried state dominates
+    ("gdn_seg8_fp32_slow_C32", "gdn", 1, 4096 - 3, 2, 64, 64, 32, "scalar", -6.0, 1.0, torch.float32, -4.0),
+    ("kda_seg8_fp32_slow_C32", "kda", 1, 4096 - 3, 2, 64, 64, 32, "perdim", -6.0, 1.0, torch.float32, -4.0),
 ]
 
 
 @pytest.mark.parametrize("case", SEG_CASES, ids=[c[0] for c in SEG_CASES])
 def test_fwd_segmented_scan(case):
-    name, op, B, T, H, dk, dv, chunk, gate, shift, h0s = case
+    name, op, B, T, H, dk, dv, chunk, gate, shift, h0s = case[:11]
+    dt, bshift = case[11:] if len(case) > 11 else (torch.bfloat16, 0.0)
     say(f"[fwd] {name}")
-    inp = synth.make_inputs(f"{op}_fwd", B, T, H, dk, dv, dtype=torch.bfloat16, seed=1, device="cuda", gate=gate,
-                            gate_shift=shift, h0_std=h0s)
+    inp = synth.make_inputs(f"{op}_fwd", B, T, H, dk, dv, dtype=dt, seed=1, device="cuda", gate=gate,
+                            gate_shift=shift, h0_std=h0s, beta_shift=bshift)
     eo, eh = run_fwd(op, inp, chunk)
     say(f"  rel err o={eo:.2e} ht={eh:.2e}")
-    assert eo <= 1e-2 and eh <= 1e-2, (eo, eh)
+    assert eo <= TOL[dt] and eh <= TOL[dt], (eo, eh)
