@@ -317,6 +317,7 @@ __global__ __launch_bounds__(256) void k_gnorm_fwd(const E* __restrict__ o, cons
                                                    float eps) {
   constexpr int V = 16 / (int)sizeof(E), per = 256 / G;
   const int pc = threadIdx.x % G;
+  const float inv_d = 1.f / (float)d;
   float wv[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) wv[e] = w[pc * V + e];
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(256) void k_gnorm_fwd(const E* __restrict__ o, cons
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < V; ++e) ss += ov[e] * ov[e];
-    const float rstd = hw_rsq(lane_group_sum<G>(ss) / (float)d + eps);
+    const float rstd = hw_rsq(lane_group_sum<G>(ss) * inv_d + eps);
 #pragma unroll
     for (int e = 0; e < V; ++e) out[e] = ov[e] * rstd * wv[e] * silu_f(zv[e]);
     piece_store<E>(y + off, out);
@@ -346,6 +347,7 @@ __global__ __launch_bounds__(256) void k_gnorm_bwd(const E* __restrict__ o, cons
   constexpr int V = 16 / (int)sizeof(E), per = 256 / G;
   __shared__ float sdw[256][V];
   const int pc = threadIdx.x % G;
+  const float inv_d = 1.f / (float)d;
   float wv[V], dwa[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) {
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(256) void k_gnorm_bwd(const E* __restrict__ o, cons
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < V; ++e) ss += ov[e] * ov[e];
-    const float rstd = hw_rsq(lane_group_sum<G>(ss) / (float)d + eps);
+    const float rstd = hw_rsq(lane_group_sum<G>(ss) * inv_d + eps);
     float n[V], dn[V], dzv[V], dot = 0.f;
 #pragma unroll
     for (int e = 0; e < V; ++e) {
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(256) void k_gnorm_bwd(const E* __restrict__ o, cons
       dwa[e] += gv[e] * n[e] * sz;
       dot += dn[e] * n[e];
     }
-    const float mdot = lane_group_sum<G>(dot) / (float)d;
+    const float mdot = lane_group_sum<G>(dot) * inv_d;
     float dov[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) dov[e] = rstd * (dn[e] - n[e] * mdot);

@@ -512,6 +512,10 @@ namespace lrt {
 // the half-G area, T and T diag(b) the dead K o e^-G and Q o e^G areas.  A
 // chunk whose |G| exceeds 60 is appended to `slow` (count in slow[0], tiles
 // from slow[1]) and left to k_kda_prep's exact path.  Outputs as k_kda_prep.
+// LOWRANK (with FUSE): the gate as its rank-kGateRank factors, log_a_ = z
+// [tokens][R] and wup = W_up [H * d_k][R]; z and one half's W_up rows sit in
+// the columns [d_k/2, d_k/2 + 2R) of the K o e^G rows, free until that half
+// is staged, and the half's pre-activation W_up z is one MFMA product.
 template <typename E, int C, int DK, int DV>
 struct KdaFastLds {
   static constexpr int NT = 256;
@@ -540,15 +544,23 @@ __global__ void k_list_reset(int* slow) {
   if (threadIdx.x == 0) slow[0] = 0;
 }
 
-template <typename E, int C, int DK, int DV, bool FUSE = false>
+// Whether the low-rank gate's staging fits the fast kernel's layout.
+template <typename E, int C, int DK, int DV>
+constexpr bool kda_fast_lowrank_fits() {
+  return DK / 2 + 2 * kGateRank <= KdaFastLds<E, C, DK, DV>::LK && DK / 2 <= C;
+}
+
+template <typename E, int C, int DK, int DV, bool FUSE = false, bool LOWRANK = false>
 __global__ __launch_bounds__(256, 2) void k_kda_prep_fast(const E* __restrict__ q, const E* __restrict__ k,
                                                           const E* __restrict__ v, const void* __restrict__ log_a_,
                                                           const float* __restrict__ beta, SeqMap m,
                                                           E* __restrict__ wW, E* __restrict__ wUp,
                                                           E* __restrict__ wKt, float* __restrict__ wGC,
                                                           E* __restrict__ wQg, E* __restrict__ wP,
-                                                          E* __restrict__ wT, int* __restrict__ slow) {
+                                                          E* __restrict__ wT, int* __restrict__ slow,
+                                                          const E* __restrict__ wup) {
   typedef KdaFastLds<E, C, DK, DV> Lay;
+  static_assert(!LOWRANK || (FUSE && kda_fast_lowrank_fits<E, C, DK, DV>()), "low-rank gate staging");
   constexpr int NT = 256, NW = 4;
   constexpr int LK = Lay::LK, LV = Lay::LV, LC = Lay::LC, DH = Lay::DH, LGH = Lay::LGH, LA = Lay::LA;
   constexpr int NQ = Lay::NQ, NB = C / 16;
@@ -572,12 +584,14 @@ __global__ __launch_bounds__(256, 2) void k_kda_prep_fast(const E* __restrict__ 
   const int H = m.H, ntiles = tile_count(m);
 
   typedef typename std::conditional<FUSE, E, float>::type GE;  // element type of the gate input
-  const GE* log_a = (const GE*)log_a_;
+  const GE* log_a = (const GE*)log_a_;  // LOWRANK: z [tokens][R]
   constexpr int GV = 16 / (int)sizeof(GE), GPR = DK / GV;  // gate elements per piece, pieces per row
   static_assert(DH % GV == 0, "a gate piece lies in one half of d_k");
+  constexpr int R = kGateRank;
   Tile<E, C, DK, NT> tk, tq;
   Tile<E, C, DV, NT> tv;
-  Tile<GE, C, DK, NT> tg;
+  Tile<GE, C, LOWRANK ? R : DK, NT> tg;
+  Tile<E, LOWRANK ? DH : 16, LOWRANK ? R : 16, NT> tw0, tw1;  // LOWRANK: this head's W_up rows, by half
   float rb = 0.f;
   // the next tile's inputs in three parts, each issued once the current
   // tile's copy of it has reached LDS: 1 k, q, beta; 2 the gate; 4 v
@@ -593,7 +607,15 @@ __global__ __launch_bounds__(256, 2) void k_kda_prep_fast(const E* __restrict__ 
       tq.load_rows_clamped(q + (ltok * H + lh) * DK, (size_t)H * DK, lnv);              \
       rb = beta[(ltok + min(tid, lnv - 1)) * H + lh]; /* masked where used */           \
     }                                                                                   \
-    if ((PART_) & 2) tg.load_rows_clamped(log_a + (ltok * H + lh) * DK, (size_t)H * DK, lnv); \
+    if ((PART_) & 2) {                                                                  \
+      if constexpr (LOWRANK) {                                                          \
+        tg.load_rows_clamped(log_a + ltok * R, (size_t)R, lnv);                         \
+        tw0.load_block(wup + (size_t)lh * DK * R);                                      \
+        tw1.load_block(wup + ((size_t)lh * DK + DH) * R);                               \
+      } else {                                                                          \
+        tg.load_rows_clamped(log_a + (ltok * H + lh) * DK, (size_t)H * DK, lnv);        \
+      }                                                                                 \
+    }                                                                                   \
     if ((PART_) & 4) tv.load_rows_clamped(v + (ltok * H + lh) * DV, (size_t)H * DV, lnv); \
   }
 
@@ -609,6 +631,10 @@ __global__ __launch_bounds__(256, 2) void k_kda_prep_fast(const E* __restrict__ 
     }
     tk.store_masked(sK, LK, nv);
     tq.store_masked(sQ, LK, nv);
+    if constexpr (LOWRANK) {
+      tg.store_masked(sS + DH, LK, nv);  // z rows
+      tw0.store(sS + DH + R, LK);        // W_up rows of the first half
+    }
     asm volatile("" ::"v"(rb));  // consumed by every lane (no load into it left pending)
     if (tid < C) sb[tid] = tid < nv ? (FUSE ? sigmoid_f(rb) : rb) : 0.f;
     if (tid == 0) *sgmax = 0;
@@ -617,8 +643,24 @@ __global__ __launch_bounds__(256, 2) void k_kda_prep_fast(const E* __restrict__ 
     // the scaled rows of that half
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
+      if constexpr (LOWRANK) {
+        // this half's pre-activation W_up z (rows d, cols t) on MFMA, then
+        // log a = -softplus, rows past the end zero
+        if (hf == 1) tw1.store(sS + DH + R, LK);  // (the first half's rows are dead)
+        lds_barrier();
+        for (int tt = w; tt < (DH / 16) * NB; tt += NW) {
+          const int td = tt / NB, ti = tt % NB;
+          f32x4 acc = zero4();
+          mma<R>(acc, sS + DH + R + td * 16 * LK, LK, sS + DH + ti * 16 * LK, LK);
+          const int t = ti * 16 + (l & 15);
+          f32x4 y;
 #pragma unroll
-      for (int s2 = 0; s2 < tg.PT; ++s2) {
+          for (int r = 0; r < 4; ++r) y[r] = t < nv ? neg_softplus_f(acc[r]) : 0.f;
+          *(f32x4*)(sG + t * LGH + td * 16 + (l >> 4) * 4) = y;
+        }
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < (LOWRANK ? 0 : tg.PT); ++s2) {
         const int idx = tid + NT * s2;
         if (tg.NP % NT == 0 || idx < tg.NP) {
           const int r = idx / GPR, c0 = (idx % GPR) * GV;
@@ -787,24 +829,25 @@ __global__ __launch_bounds__(256, 2) void k_kda_prep_fast(const E* __restrict__ 
 }
 
 // The chunk-parallel pass of the KDA forward: k_kda_prep_fast (two
-// workgroups per CU) where it fits in half of a CU's LDS, with k_kda_prep
-// taking the chunks it leaves to the exact path; k_kda_prep alone otherwise
-// (and for the low-rank gate).  wT (nullable): also write Tinv.  fast_kind /
+// workgroups per CU) where it fits in half of a CU's LDS (and, for the
+// low-rank gate, where its staging fits), with k_kda_prep taking the chunks
+// it leaves to the exact path; k_kda_prep alone otherwise.  wT (nullable): also write Tinv.  fast_kind /
 // kind: the timing hook's ids of the two kernels.
 template <typename E, int C, int DK, int DV, bool FUSE, bool LOWRANK = false>
 int launch_kda_prep(const void* q, const void* k, const void* v, const void* log_a, const float* beta,
                     const SeqMap& sm, const FwdWs& ws, E* wT, const void* wup, int tiles, int fast_kind, int kind,
                     hipStream_t st) {
   typedef KdaLds<E, C, DK, DV, 64 * kWyWaves> Lay;
-  if constexpr (!LOWRANK && KdaFastLds<E, C, DK, DV>::TOTAL <= kLdsMax / 2) {
+  if constexpr (KdaFastLds<E, C, DK, DV>::TOTAL <= kLdsMax / 2 &&
+                (!LOWRANK || kda_fast_lowrank_fits<E, C, DK, DV>())) {
     LRT_LAUNCH(kKListReset, k_list_reset<>, dim3(1), dim3(64), st, ws.slow);
-    LRT_LAUNCH(fast_kind, (k_kda_prep_fast<E, C, DK, DV, FUSE>),
+    LRT_LAUNCH(fast_kind, (k_kda_prep_fast<E, C, DK, DV, FUSE, LOWRANK>),
                dim3(persistent_grid(tiles, KdaFastLds<E, C, DK, DV>::TOTAL)), dim3(256), st, (const E*)q, (const E*)k,
                (const E*)v, log_a, beta, sm, (E*)ws.W, (E*)ws.Up, (E*)ws.Kt, ws.GC, (E*)ws.Qg, (E*)ws.P, wT,
-               ws.slow);
-    LRT_LAUNCH(kind, (k_kda_prep<E, C, DK, DV, kWyWaves, FUSE, false>), dim3(persistent_grid(tiles, Lay::TOTAL)),
+               ws.slow, (const E*)wup);
+    LRT_LAUNCH(kind, (k_kda_prep<E, C, DK, DV, kWyWaves, FUSE, LOWRANK>), dim3(persistent_grid(tiles, Lay::TOTAL)),
                dim3(64 * kWyWaves), st, (const E*)q, (const E*)k, (const E*)v, log_a, beta, sm, (E*)ws.W,
-               (E*)ws.Up, (E*)ws.Kt, ws.GC, (E*)ws.Qg, (E*)ws.P, wT, (const E*)nullptr, (const int*)ws.slow);
+               (E*)ws.Up, (E*)ws.Kt, ws.GC, (E*)ws.Qg, (E*)ws.P, wT, (const E*)wup, (const int*)ws.slow);
   } else {
     LRT_LAUNCH(kind, (k_kda_prep<E, C, DK, DV, kWyWaves, FUSE, LOWRANK>), dim3(persistent_grid(tiles, Lay::TOTAL)),
                dim3(64 * kWyWaves), st, (const E*)q, (const E*)k, (const E*)v, log_a, beta, sm, (E*)ws.W,
