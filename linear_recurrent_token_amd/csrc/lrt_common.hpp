@@ -101,21 +101,24 @@ __device__ __forceinline__ float neg_softplus_f(float z) {
   return -(fmaxf(z, 0.f) + kLn2 * hw_log2(1.f + hw_exp2(-fabsf(z) * kLog2e)));
 }
 
+// x from another lane of the same 16-lane row, by a DPP control (VALU only).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
 // Sum of x over aligned groups of G consecutive lanes (G a power of two up to
 // 64), every lane of a group receiving its group's sum.  Inside a 16-lane row
-// the partner values move by DPP (quad permutations, then the half-row and
-// row mirrors), with no LDS traffic; wider groups add ds_bpermute steps.
-template <int CTRL>
-__device__ __forceinline__ float dpp_move(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
-}
+// the partner values move by DPP: pairs (quad_perm 1,0,3,2), quads (2,3,0,1),
+// the other quad of eight (mirror inside 8 lanes), the other half of the row
+// (mirror inside 16 lanes), with no LDS traffic; wider groups add
+// ds_bpermute steps.
 template <int G>
 __device__ __forceinline__ float lane_group_sum(float x) {
   static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "lane groups are powers of two");
-  if constexpr (G >= 2) x += dpp_move<0xB1>(x);   // quad_perm [1, 0, 3, 2]: lane ^ 1
-  if constexpr (G >= 4) x += dpp_move<0x4E>(x);   // quad_perm [2, 3, 0, 1]: lane ^ 2
-  if constexpr (G >= 8) x += dpp_move<0x141>(x);  // row_half_mirror: the other quad of the 8
-  if constexpr (G >= 16) x += dpp_move<0x140>(x); // row_mirror: the other half of the row
+  if constexpr (G >= 2) x += dpp_mov<0xB1>(x);
+  if constexpr (G >= 4) x += dpp_mov<0x4E>(x);
+  if constexpr (G >= 8) x += dpp_mov<0x141>(x);
+  if constexpr (G >= 16) x += dpp_mov<0x140>(x);
   if constexpr (G >= 32) x += __shfl_xor(x, 16, 64);
   if constexpr (G >= 64) x += __shfl_xor(x, 32, 64);
   return x;
@@ -652,21 +655,8 @@ __device__ __forceinline__ void block_to_lds(E* lds, int ls, const E* g) {
   t.store(lds, ls);
 }
 
-// x from another lane of the same 16-lane row, by a DPP control (VALU only).
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
-}
-// Sum over the 16 lanes of a row group (lanes with equal l / 16), all in
-// DPP: pairs (quad_perm 1,0,3,2), quads (2,3,0,1), halves of the row
-// (mirror inside 8 lanes), then the two halves (mirror inside 16 lanes).
-__device__ __forceinline__ float sum16(float x) {
-  x += dpp_mov<0xB1>(x);
-  x += dpp_mov<0x4E>(x);
-  x += dpp_mov<0x141>(x);
-  x += dpp_mov<0x140>(x);
-  return x;
-}
+// Sum over the 16 lanes of a row group (lanes with equal l / 16).
+__device__ __forceinline__ float sum16(float x) { return lane_group_sum<16>(x); }
 // Row sums of an accumulator tile: v[r] holds row 4 * (l / 16) + r of column
 // l % 16.  Returns, in every lane, the sum over the 16 columns of row
 // 4 * (l / 16) + ((l >> 2) & 3): halves of the row group trade rows (lane
