@@ -393,3 +393,16 @@ def test_conv_and_gated_norm_validation(L):
     assert gb(dz=F + 8) == c["LRT_ERR_ALIGN"]
     assert lib.gated_rmsnorm_bwd_workspace_bytes(10, 100) == SZ
     assert lib.gated_rmsnorm_bwd_workspace_bytes(-5, 128) == SZ
+
+
+def test_autograd_bindings_refuse_cpu_tensors(L):
+    """The autograd layer is marshalling only: CPU tensors are refused, never
+    computed on the host."""
+    import torch
+    from linear_recurrent_token_amd import autograd as A
+    q = torch.zeros((1, 4, 1, 16))
+    la = torch.zeros((1, 4, 1))
+    with pytest.raises(ValueError):
+        A.gated_delta_net(q, q, q, la, la)
+    with pytest.raises(ValueError):
+        A.short_conv(torch.zeros((1, 4, 8)), torch.zeros((8, 4)))
