@@ -69,7 +69,7 @@ struct KdaGradLds {
   static constexpr size_t PCOL = PDB + (size_t)NW * C * 4;   // [NB][d_k] per-block sums of k o Kt-part
   static constexpr size_t PDEC = PCOL + (size_t)NB * DK * 4; // [NW][d_k] partials of rowsum(dH' o Hn)
   static constexpr size_t STOT = PDEC + (size_t)NW * DK * 4; // [NQ][d_k] segment totals of the cumsums
-  static constexpr size_t FL = STOT + (size_t)NQ * DK * 4;    // largest decay of a 16-token block (float bits)
+  static constexpr size_t FL = STOT + (size_t)NQ * DK * 4;    // largest decay of a 16-token block, largest |G| (float bits)
   static constexpr size_t U0 = al(FL + 16);
   // phase A
   static constexpr size_t SA = U0;    // Hn^T [v][d]; then dH'^T
@@ -191,6 +191,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     float* pdec = (float*)(smz + Lay::PDEC);
     float* stot = (float*)(smz + Lay::STOT);
     int* sbmax = (int*)(smz + Lay::FL);
+    int* scmax = sbmax + 1;
     E* sS = (E*)(smz + Lay::SA);
     E* sdO = (E*)(smz + Lay::DOA);
     E* sUt = (E*)(smz + Lay::UTA);
@@ -224,21 +225,20 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     tdu.store(sdUt, LC);
     lds_barrier();
     LRT_KG_LOAD(tile, cp, n, 4)
-    // dP^T = lower(dO U^T)^T, tiles (ti, tj) with tj <= ti (the others are never read)
+    // dP^T = lower(dO U^T)^T: products for the tiles (ti, tj) with tj <= ti,
+    // zeros written for the others (phase C's whole-chunk sums read them)
 #pragma unroll
     for (int s2 = 0; s2 < ZPW; ++s2) {
       const int t2 = w + NW * s2;
       if (t2 < NZ) {
         const int ti = t2 / NB, tj = t2 % NB;
-        if (tj <= ti) {
-          f32x4 acc = zero4();
-          mma<DV, false, true>(acc, sdO + ti * 16 * LV, LV, sUt + tj * 16, LC);
-          const int j = tj * 16 + (l & 15), i0 = ti * 16 + dsub;
-          f32x4 dp;
+        f32x4 acc = zero4();
+        if (tj <= ti) mma<DV, false, true>(acc, sdO + ti * 16 * LV, LV, sUt + tj * 16, LC);
+        const int j = tj * 16 + (l & 15), i0 = ti * 16 + dsub;
+        f32x4 dp;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) dp[r] = (j <= i0 + r) ? acc[r] : 0.f;
-          store4<E>(sdPT + j * LC + i0, dp);
-        }
+        for (int r = 0; r < 4; ++r) dp[r] = (j <= i0 + r) ? acc[r] : 0.f;
+        store4<E>(sdPT + j * LC + i0, dp);
       }
       tile_fence();
     }
@@ -310,7 +310,10 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     tt.store(sT, LC);
     asm volatile("" ::"v"(rb));  // consumed by every lane (no load into it left pending)
     if (tid < C) sb[tid] = tid < nv ? rb : 0.f;
-    if (tid == 0) *sbmax = 0;
+    if (tid == 0) {
+      *sbmax = 0;
+      *scmax = 0;
+    }
     lds_barrier();
     // G = inclusive cumsum of log a over the chunk, per key dimension: thread
     // (d, segment) scans RS rows in registers, then adds the earlier segments' totals
@@ -392,14 +395,24 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     {
       // the largest decay of one 16-token block, max over (block, d) of
       // G(row before the block) - G(the block's last row)
-      float bm = 0.f;
+      // and the largest |G| of the chunk (every one within e^60: the whole
+      // chunk factorises, phase C)
+      float bm = 0.f, cm = 0.f;
       if (tid < DK) {
         for (int b2 = 0; b2 < NB; ++b2)
           bm = fmaxf(bm, (b2 > 0 ? sG[(b2 * 16 - 1) * LG + tid] : 0.f) - sG[(b2 * 16 + 15) * LG + tid]);
+#pragma unroll 8
+        for (int t = 0; t < C; ++t) cm = fmaxf(cm, fabsf(sG[t * LG + tid]));
       }
 #pragma unroll
-      for (int msk = 1; msk < 64; msk <<= 1) bm = fmaxf(bm, __shfl_xor(bm, msk, 64));
-      if (l == 0 && w * 64 < DK) atomicMax(sbmax, __float_as_int(bm));  // non-negative floats order as ints
+      for (int msk = 1; msk < 64; msk <<= 1) {
+        bm = fmaxf(bm, __shfl_xor(bm, msk, 64));
+        cm = fmaxf(cm, __shfl_xor(cm, msk, 64));
+      }
+      if (l == 0 && w * 64 < DK) {  // non-negative floats order as ints
+        atomicMax(sbmax, __float_as_int(bm));
+        atomicMax(scmax, __float_as_int(cm));
+      }
     }
     lds_barrier();
     // Z = dX (K o E)^T + dY V^T, then Z diag(b) = dX X^T + dY Y^T; tiles (ti, tk), tk <= ti
@@ -451,21 +464,20 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
       tile_fence();
     }
     lds_barrier();
-    // dA^T = -strict_lower(Z diag(b) T^T)^T, tiles (ti, tj) with tj <= ti
+    // dA^T = -strict_lower(Z diag(b) T^T)^T: products for the tiles (ti, tj)
+    // with tj <= ti, zeros written for the others
 #pragma unroll
     for (int s2 = 0; s2 < ZPW; ++s2) {
       const int t2 = w + NW * s2;
       if (t2 < NZ) {
         const int ti = t2 / NB, tj = t2 % NB;
-        if (tj <= ti) {
-          f32x4 acc = zero4();
-          mma<C, true, false>(acc, sZT + ti * 16, LC, sT + tj * 16 * LC, LC);
-          const int j = tj * 16 + (l & 15), i0 = ti * 16 + dsub;
-          f32x4 da;
+        f32x4 acc = zero4();
+        if (tj <= ti) mma<C, true, false>(acc, sZT + ti * 16, LC, sT + tj * 16 * LC, LC);
+        const int j = tj * 16 + (l & 15), i0 = ti * 16 + dsub;
+        f32x4 da;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) da[r] = (j < i0 + r) ? -acc[r] : 0.f;
-          store4<E>(sdAT + j * LC + i0, da);
-        }
+        for (int r = 0; r < 4; ++r) da[r] = (j < i0 + r) ? -acc[r] : 0.f;
+        store4<E>(sdAT + j * LC + i0, da);
       }
       tile_fence();
     }
@@ -487,8 +499,12 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     //   Kend_j = k_j e^(G_s(j) - G_j),  Qx_i = q_i e^(G_i - G_ref(i)),  bKx_i = b_i k_i e^(G_i - G_ref(i)).
     // In the fast regime both halves of a pair's dG term (row side +, column
     // side -) are formed from the same rounded staged rows, so they cancel
-    // in the reverse cumsum as they do in exact arithmetic.
+    // in the reverse cumsum as they do in exact arithmetic.  While every |G|
+    // of the chunk is within e^60 (fastc) the whole chunk is one block with
+    // its reference at the chunk start (G = 0): Kend_j = k_j e^(-G_j),
+    // Qx_i = q_i e^(G_i), and each sum is one product over all C tokens.
     const bool fastd = __int_as_float(*sbmax) <= 60.f;
+    const bool fastc = fastd && __int_as_float(*scmax) <= 60.f;
     // q rows over dU^T; Qx from this thread's own q pieces, before the
     // registers take the next chunk's q
     tq.store_masked(sQ, LK, nv);
@@ -497,7 +513,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
       const int idx = tid + NT * s2;
       if (tq.NP % NT == 0 || idx < tq.NP) {
         const int t = idx / (DK / V), d0 = (idx % (DK / V)) * V, blk = t >> 4;
-        const int ref = fastd ? blk * 16 + 15 : blk * 16 - 1;
+        const int ref = fastc ? -1 : fastd ? blk * 16 + 15 : blk * 16 - 1;
         E e[V];
         __builtin_memcpy(e, &tq.x[s2], 16);
         float g[V], gr[V], x[V];
@@ -515,11 +531,15 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     LRT_KG_LOAD(next, np, nn, 1)
     for (int p = tid; p < C * (DK / V); p += NT) {
       const int t = p / (DK / V), d0 = (p % (DK / V)) * V, blk = t >> 4;
-      const int ref = fastd ? blk * 16 + 15 : blk * 16 - 1;
+      const int ref = fastc ? -1 : fastd ? blk * 16 + 15 : blk * 16 - 1;
       float kx[V], g[V], gs[V], gr[V], a[V], b2[V];
       lds_vec_load<E>(sK + t * LK + d0, kx);
       lds_f32_load<V>(sG + t * LG + d0, g);
-      lds_f32_load<V>(sG + (blk * 16 + 15) * LG + d0, gs);
+      if (fastc)
+#pragma unroll
+        for (int i = 0; i < V; ++i) gs[i] = 0.f;
+      else
+        lds_f32_load<V>(sG + (blk * 16 + 15) * LG + d0, gs);
       if (ref >= 0)
         lds_f32_load<V>(sG + ref * LG + d0, gr);
       else
@@ -544,11 +564,15 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
       if (td < NDT) {
         const int d0 = td * 16 + dsub;
         const f32x4 gi = *(const f32x4*)(sG + tl * LG + d0);
-        const int ref = fastd ? tb * 16 + 15 : tb * 16 - 1;
+        const int ref = fastc ? -1 : fastd ? tb * 16 + 15 : tb * 16 - 1;
         const f32x4 gref = ref >= 0 ? *(const f32x4*)(sG + ref * LG + d0) : zero4();
         const f32x4 kk = load4<E>(sK + tl * LK + d0), qq = load4<E>(sQ + tl * LK + d0);
         f32x4 rp = zero4(), ra = zero4();
-        const int nsj = fastd ? tb + 1 : tb;
+        if (fastc) {
+          mma<C, true, true>(rp, sKe + td * 16, LK, sdPT + tb * 16, LC);
+          mma<C, true, true>(ra, sKe + td * 16, LK, sdAT + tb * 16, LC);
+        }
+        const int nsj = fastc ? 0 : fastd ? tb + 1 : tb;
         for (int sj = 0; sj < nsj; ++sj) {
           f32x4 xp = zero4(), xa = zero4();
           mma<16, true, true>(xp, sKe + sj * 16 * LK + td * 16, LK, sdPT + sj * 16 * LC + tb * 16, LC);
@@ -608,9 +632,13 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
       if (td < NDT) {
         const int d0 = td * 16 + dsub;
         const f32x4 gj = *(const f32x4*)(sG + tl * LG + d0);
-        const f32x4 gs = *(const f32x4*)(sG + (tb * 16 + 15) * LG + d0);
+        const f32x4 gs = fastc ? zero4() : *(const f32x4*)(sG + (tb * 16 + 15) * LG + d0);
         f32x4 cc = zero4();
-        for (int si = fastd ? tb : tb + 1; si < NB; ++si) {
+        if (fastc) {
+          mma<C, true, false>(cc, sQs + td * 16, LK, sdPT + tb * 16 * LC, LC);
+          mma<C, true, false>(cc, sKs + td * 16, LK, sdAT + tb * 16 * LC, LC);
+        }
+        for (int si = fastc ? NB : fastd ? tb : tb + 1; si < NB; ++si) {
           f32x4 x = zero4();
           mma<16, true, false>(x, sQs + si * 16 * LK + td * 16, LK, sdPT + tb * 16 * LC + si * 16, LC);
           mma<16, true, false>(x, sKs + si * 16 * LK + td * 16, LK, sdAT + tb * 16 * LC + si * 16, LC);
