@@ -189,6 +189,11 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
   constexpr int V = 16 / (int)sizeof(E);
   constexpr int NKT = (DK / 16) * NB, KPW = (NKT + NW - 1) / NW;
   static_assert(NW % NB == 0, "waves must cover whole column blocks");
+  // Every wave holds KPW tiles d = w / NB + (NW / NB) s of one column block
+  // w % NB: the products then read the fragments the tiles share (dO, dS,
+  // dU, U, T, M) once per k step for all of them (mma_nA).
+  constexpr int NWB = NW / NB;
+  constexpr bool kShared = (DK / 16) % NWB == 0 && (DV / 16) % NWB == 0;
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
 
   Tile<E, C, DK, NT> tq, tk;
@@ -380,6 +385,28 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
       const int ti = w % NB, i = ti * 16 + (l & 15);
       const float gam = __expf(sg[i]);
       float esum = 0.f;
+      if constexpr (kShared) {
+        const int td0 = w / NB;
+#pragma unroll
+        for (int s = 0; s < KPW; ++s) {
+          dqa[s] = zero4();
+          dwa[s] = zero4();
+        }
+        if constexpr (DELTA)
+          mma_nA2<DV, KPW, true, false, true>(dqa, dwa, sS + td0 * 16, NWB * 16, LK, sdO + ti * 16 * LV, LV,
+                                              sdUt + ti * 16, LC);
+        else
+          mma_nA<DV, KPW, true, false>(dqa, sS + td0 * 16, NWB * 16, LK, sdO + ti * 16 * LV, LV);
+#pragma unroll
+        for (int s = 0; s < KPW; ++s) {
+          const int d0 = (td0 + NWB * s) * 16 + (l >> 4) * 4;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) esum += to_f(sQ[i * LK + d0 + r]) * dqa[s][r];
+          dqa[s] *= gam;
+          dwa[s] = -dwa[s];
+        }
+        mma_nA<C, KPW, true, true>(dqa, sK + td0 * 16, NWB * 16, LK, sdSj + ti * 16, LC);
+      } else {
 #pragma unroll
       for (int s = 0; s < KPW; ++s) {
         const int td = w / NB + (NW / NB) * s;
@@ -401,6 +428,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
           }
         }
         tile_fence();
+      }
       }
       esum = sum4(esum * gam);
       wave_order();
@@ -432,6 +460,23 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
       const int tj = w % NB, j = tj * 16 + (l & 15);
       const float kt = __expf(gC - sg[j]);
       float ssum = 0.f;
+      if constexpr (kShared) {
+        const int td0 = w / NB;
+#pragma unroll
+        for (int s = 0; s < KPW; ++s) dka[s] = zero4();
+        if constexpr (DELTA)
+          mma_nA<DV, KPW, true, true>(dka, sS + td0 * 16, NWB * 16, LK, sUt + tj * 16, LC);
+        else
+          mma_nA<DV, KPW, true, false>(dka, sS + td0 * 16, NWB * 16, LK, sUt + tj * 16 * LV, LV);
+#pragma unroll
+        for (int s = 0; s < KPW; ++s) {
+          const int d0 = (td0 + NWB * s) * 16 + (l >> 4) * 4;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ssum += dka[s][r] * to_f(sK[j * LK + d0 + r]);
+          dka[s] *= kt;
+        }
+        mma_nA<C, KPW, true, false>(dka, sQ + td0 * 16, NWB * 16, LK, sdSj + tj * 16 * LC, LC);
+      } else {
 #pragma unroll
       for (int s = 0; s < KPW; ++s) {
         const int td = w / NB + (NW / NB) * s;
@@ -450,6 +495,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
           dka[s] = acc;
         }
         tile_fence();
+      }
       }
       ssum = sum4(ssum * kt);
       const float stot = sum16(ssum);  // over the wave's 16 columns j (lanes 0..15)
@@ -476,6 +522,19 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
       {
         const float bgj = sb[jw] * __expf(sg[jw]);
         float e = 0.f;
+        if constexpr (kShared) {
+          f32x4 xa[KPW];
+#pragma unroll
+          for (int s = 0; s < KPW; ++s) xa[s] = zero4();
+          mma_nA<C, KPW, true, true>(xa, sdW + (w / NB) * 16, NWB * 16, LK, sT + (w % NB) * 16, LC);
+#pragma unroll
+          for (int s = 0; s < KPW; ++s) {
+            const int d0 = (w / NB + NWB * s) * 16 + (l >> 4) * 4;
+            dka[s] += bgj * xa[s];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) e += xa[s][r] * to_f(sK[jw * LK + d0 + r]);
+          }
+        } else {
 #pragma unroll
         for (int s = 0; s < KPW; ++s) {
           const int kt = w + NW * s;
@@ -490,6 +549,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
           }
           tile_fence();
         }
+        }
         e = sum4(e);
         if (l < 16) mycx[jw] += e;
       }
@@ -497,6 +557,20 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
       {
         const float bj = sb[jw];
         float e = 0.f;
+        if constexpr (kShared) {
+          constexpr int VPW = (DV / 16) / NWB;
+          f32x4 ya[VPW];
+#pragma unroll
+          for (int s = 0; s < VPW; ++s) ya[s] = zero4();
+          mma_nA<C, VPW, false, true>(ya, sdUt + (w / NB) * 16 * LC, NWB * 16 * LC, LC, sT + (w % NB) * 16, LC);
+#pragma unroll
+          for (int s = 0; s < VPW; ++s) {
+            const int v0 = (w / NB + NWB * s) * 16 + (l >> 4) * 4;
+            store4<E>(sdV + jw * LV + v0, bj * ya[s]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) e += ya[s][r] * to_f(sV[jw * LV + v0 + r]);
+          }
+        } else {
 #pragma unroll
         for (int s2 = 0; s2 < ((DV / 16) * NB + NW - 1) / NW; ++s2) {
           const int tt2 = w + NW * s2;
@@ -509,6 +583,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
 #pragma unroll
           for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sV[jw * LV + v0 + r]);
           tile_fence();
+        }
         }
         e = sum4(e);
         if (l < 16) mydb[jw] += e;
@@ -585,6 +660,13 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
       if (l < 16) mydg[jw] -= ecol2;
       lds_barrier();
       // dK^T += K^T M (cols j: sum_i k_i M_ij) + K^T M^T (cols i: sum_j k_j M_ij) -> dk rows over dW
+      if constexpr (kShared) {
+        mma_nA2<C, KPW, true, false, true>(dka, dka, sK + (w / NB) * 16, NWB * 16, LK, sMt + (w % NB) * 16 * LC, LC,
+                                           sMt + (w % NB) * 16, LC);
+#pragma unroll
+        for (int s = 0; s < KPW; ++s)
+          store4<E>(sdK + ((w % NB) * 16 + (l & 15)) * LK + (w / NB + NWB * s) * 16 + (l >> 4) * 4, dka[s]);
+      } else {
 #pragma unroll
       for (int s = 0; s < KPW; ++s) {
         const int kt = w + NW * s;
@@ -595,6 +677,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
           store4<E>(sdK + (tj * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, dka[s]);
         }
         tile_fence();
+      }
       }
       // dg (+ the X = diag(b gamma) K term), reverse cumsum -> dlog_a; dbeta
       if (threadIdx.x < 64) {

@@ -347,6 +347,46 @@ __device__ __forceinline__ void mma_nA(f32x4 (&acc)[NA], const float* a, int ast
 #pragma unroll
   for (int s = 0; s < NA; ++s) mma<K, AK, BK>(acc[s], a + s * astep, lda, b, ldb);
 }
+// NA tiles, each A_s times two B operands: acc1[s] += A_s B1 and
+// acc2[s] += A_s B2, every fragment read once per k step (acc1 and acc2 may
+// be the same array: the two products then interleave by k step).
+template <int K, int NA, bool AK, bool B1K, bool B2K>
+__device__ __forceinline__ void mma_nA2(f32x4 (&acc1)[NA], f32x4 (&acc2)[NA], const bf16* a, int astep, int lda,
+                                        const bf16* b1, int ldb1, const bf16* b2, int ldb2) {
+  const int l = lane_id();
+#pragma unroll
+  for (int k = 0; k + 32 <= K; k += 32) {
+    const bf16x8 f1 = B1K ? frag_k8_outer(b1, ldb1, k, 0) : *(const bf16x8*)(b1 + (l & 15) * ldb1 + k + (l >> 4) * 8);
+    const bf16x8 f2 = B2K ? frag_k8_outer(b2, ldb2, k, 0) : *(const bf16x8*)(b2 + (l & 15) * ldb2 + k + (l >> 4) * 8);
+#pragma unroll
+    for (int s = 0; s < NA; ++s) {
+      const bf16* as = a + s * astep;
+      const bf16x8 fa = AK ? frag_k8_outer(as, lda, k, 0) : *(const bf16x8*)(as + (l & 15) * lda + k + (l >> 4) * 8);
+      acc1[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f1, acc1[s], 0, 0, 0);
+      acc2[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f2, acc2[s], 0, 0, 0);
+    }
+  }
+  if constexpr (K % 32 == 16) {
+    constexpr int k = K - 16;
+    const bf16x8 f1 = B1K ? frag_k16_outer(b1, ldb1, k) : frag_k16_inner(b1, ldb1, k);
+    const bf16x8 f2 = B2K ? frag_k16_outer(b2, ldb2, k) : frag_k16_inner(b2, ldb2, k);
+#pragma unroll
+    for (int s = 0; s < NA; ++s) {
+      const bf16x8 fa = AK ? frag_k16_outer(a + s * astep, lda, k) : frag_k16_inner(a + s * astep, lda, k);
+      acc1[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f1, acc1[s], 0, 0, 0);
+      acc2[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f2, acc2[s], 0, 0, 0);
+    }
+  }
+}
+template <int K, int NA, bool AK, bool B1K, bool B2K>
+__device__ __forceinline__ void mma_nA2(f32x4 (&acc1)[NA], f32x4 (&acc2)[NA], const float* a, int astep, int lda,
+                                        const float* b1, int ldb1, const float* b2, int ldb2) {
+#pragma unroll
+  for (int s = 0; s < NA; ++s) {
+    mma<K, AK, B1K>(acc1[s], a + s * astep, lda, b1, ldb1);
+    mma<K, AK, B2K>(acc2[s], a + s * astep, lda, b2, ldb2);
+  }
+}
 
 // ------------------------------------------------------------- vector moves
 // Four consecutive elements of E packed for one store / load.
