@@ -71,6 +71,10 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
   constexpr int NH = (DK / 16) * NTV, HPW = (NH + NW - 1) / NW;
   constexpr int NU = (C / 16) * NTV, UPW = (NU + NW - 1) / NW;
   static_assert(!KDA || (READ_P && DELTA && !PT), "the KDA reverse scan reads the stored P");
+  // When every wave holds the same number of tiles of one column block, a
+  // wave's products read the fragment its tiles share once per k step.
+  constexpr bool kShU = NU % NW == 0 && NW % NTV == 0;
+  constexpr bool kShH = NH % NW == 0 && NW % NTV == 0;
   __shared__ __attribute__((aligned(16))) E sQ[C * LK];    // q rows (KDA: Q o e^G rows)
   __shared__ __attribute__((aligned(16))) E sW[C * LK];    // W rows
   __shared__ __attribute__((aligned(16))) E sKt[dstate_kt_elems<C, DK, LK, LC, KDA>()];  // Ktil rows (KDA: Ktil^T)
@@ -198,8 +202,26 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
     lds_barrier();
     LRT_DSTATE_FETCH(nprev, 2)
     // dU = dU_local + Ktil dH'  (rows t, cols v) -> dU^T
+    if constexpr (kShU) {
+      const int ti0 = w / NTV, tv = w % NTV;
+      constexpr int AS = (NW / NTV) * 16;
+      f32x4 acc[UPW];
 #pragma unroll
-    for (int s = 0; s < UPW; ++s) {
+      for (int s = 0; s < UPW; ++s) acc[s] = READ_P ? zero4() : du[s];
+      if constexpr (READ_P && PT)
+        mma_nA<C, UPW, false, true>(acc, sP + ti0 * 16 * LC, AS * LC, LC, sO + tv * 16, LB);
+      else if constexpr (READ_P)
+        mma_nA<C, UPW, true, true>(acc, sP + ti0 * 16, AS, LC, sO + tv * 16, LB);
+      if constexpr (KDA)
+        mma_nA<DK, UPW, true, false>(acc, sKt + ti0 * 16, AS, LC, sdS + tv * 16 * LK, LK);
+      else
+        mma_nA<DK, UPW>(acc, sKt + ti0 * 16 * LK, AS * LK, LK, sdS + tv * 16 * LK, LK);
+#pragma unroll
+      for (int s = 0; s < UPW; ++s)
+        store4<E>(sdU + (tv * 16 + (l & 15)) * LC + (ti0 + (NW / NTV) * s) * 16 + (l >> 4) * 4, acc[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < (kShU ? 0 : UPW); ++s) {
       const int tt = w + NW * s;
       if (tt < NU) {
         const int ti = tt / NTV, tv = tt % NTV;
@@ -223,8 +245,28 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
     lds_barrier();
     lds_to_block<E, BV, C, NT>(wdU + (tile * DV + v0) * C, sdU, LC);
     // dH <- gamma_C dH' + Q^T diag(gamma) dO - W^T dU
+    if constexpr (kShH) {
+      const int td0 = w / NTV, tv = w % NTV;
+      constexpr int AS = (NW / NTV) * 16;
 #pragma unroll
-    for (int s = 0; s < HPW; ++s) {
+      for (int s = 0; s < HPW; ++s) {
+        if constexpr (KDA)
+          hacc[s] *= *(const f32x4*)(sg + (td0 + (NW / NTV) * s) * 16 + (l >> 4) * 4);
+        else
+          hacc[s] *= dec;
+      }
+      mma_nA<C, HPW, true, true>(hacc, sQ + td0 * 16, AS, LK, og + tv * 16, LB);
+      if constexpr (DELTA) {
+        f32x4 wdu[HPW];
+#pragma unroll
+        for (int s = 0; s < HPW; ++s) wdu[s] = zero4();
+        mma_nA<C, HPW, true, false>(wdu, sW + td0 * 16, AS, LK, sdU + tv * 16 * LC, LC);
+#pragma unroll
+        for (int s = 0; s < HPW; ++s) hacc[s] -= wdu[s];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < (kShH ? 0 : HPW); ++s) {
       const int tt = w + NW * s;
       if (tt < NH) {
         const int td = tt / NTV, tv = tt % NTV;

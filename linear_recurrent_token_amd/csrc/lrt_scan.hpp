@@ -267,6 +267,11 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
   constexpr int NH = (DK / 16) * NTV, HPW = (NH + NW - 1) / NW;  // state tiles (rows d, cols v)
   constexpr int NU = NB * NTV, UPW = (NU + NW - 1) / NW;         // U tiles (rows t, cols v)
   constexpr int NO = NTV * NB;                                   // O^T tiles (rows v, cols t)
+  // When every wave holds the same number of tiles of one column block, a
+  // wave's products read the fragment its tiles share once per k step.
+  constexpr bool kShU = NU % NW == 0 && NW % NTV == 0;
+  constexpr bool kShH = NH % NW == 0 && NW % NTV == 0;
+  constexpr bool kShO = NO % NW == 0 && NW % NB == 0;
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
   E* sW = (E*)(smem + Lay::W);
   E* sK = (E*)(smem + Lay::K);  // GDN: k rows; KDA: Ktil^T
@@ -397,13 +402,18 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
     lds_barrier();
     if constexpr (MODE == kScanBwd || SAVE) lds_to_block<E, BV, DK, NT>(a.S + (tile * DV + v0) * DK, sS, LK);
     // ---- U = U' - W Hn -> U^T (GDN: and (e^(g_C - g) U)^T)
+    f32x4 wh[UPW];
+#pragma unroll
+    for (int s = 0; s < UPW; ++s) wh[s] = zero4();
+    if constexpr (DELTA && kShU)
+      mma_nA<DK, UPW>(wh, sW + (w / NTV) * 16 * LK, (NW / NTV) * 16 * LK, LK, sS + (w % NTV) * 16 * LK, LK);
 #pragma unroll
     for (int s = 0; s < UPW; ++s) {
       const int tt = w + NW * s;
       if (tt < NU) {
         const int ti = tt / NTV, tv = tt % NTV;
-        f32x4 acc = zero4();
-        if constexpr (DELTA) mma<DK>(acc, sW + ti * 16 * LK, LK, sS + tv * 16 * LK, LK);
+        f32x4 acc = wh[s];
+        if constexpr (DELTA && !kShU) mma<DK>(acc, sW + ti * 16 * LK, LK, sS + tv * 16 * LK, LK);
         const f32x4 u = up[s] - acc;
         const int vv = tv * 16 + (l & 15), t = ti * 16 + (l >> 4) * 4;
         store4<E>(sU + vv * LC + t, u);
@@ -415,7 +425,22 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
     // U^T rows out from their LDS copy (16 bytes per access)
     if constexpr ((MODE == kScanBwd || SAVE) && DELTA) lds_to_block<E, BV, C, NT>(a.U + (tile * DV + v0) * C, sU, LC);
     // ---- O^T = Hn^T (Q diag(gamma))^T + U^T P^T -> o rows; state update
-    if constexpr (FWD) {
+    if constexpr (FWD && kShO) {
+      constexpr int OPW = NO / NW;
+      const int ti = w % NB, i = ti * 16 + (l & 15);
+      f32x4 oa[OPW];
+#pragma unroll
+      for (int s = 0; s < OPW; ++s) oa[s] = zero4();
+      mma_nA<DK, OPW>(oa, sS + (w / NB) * 16 * LK, (NW / NB) * 16 * LK, LK, sQ + ti * 16 * LK, LK);
+      if constexpr (!KDA) {
+        const float gm = sgam[i];
+#pragma unroll
+        for (int s = 0; s < OPW; ++s) oa[s] *= gm;
+      }
+      mma_nA<C, OPW>(oa, sU + (w / NB) * 16 * LC, (NW / NB) * 16 * LC, LC, sP + ti * 16 * LC, LC);
+#pragma unroll
+      for (int s = 0; s < OPW; ++s) store4<E>(sO + i * LB + (w / NB + (NW / NB) * s) * 16 + (l >> 4) * 4, oa[s]);
+    } else if constexpr (FWD) {
       for (int tt = w; tt < NO; tt += NW) {
         const int tv = tt / NB, ti = tt % NB;
         f32x4 acc = zero4();
@@ -427,8 +452,21 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
       }
     }
     const float gdec = KDA ? 0.f : __expf(sg[C - 1]);
+    if constexpr (kShH) {
 #pragma unroll
-    for (int s = 0; s < HPW; ++s) {
+      for (int s = 0; s < HPW; ++s) {
+        if constexpr (KDA)
+          hacc[s] *= *(const f32x4*)(sg + (w / NTV + (NW / NTV) * s) * 16 + (l >> 4) * 4);
+        else
+          hacc[s] *= gdec;
+      }
+      if constexpr (KDA)
+        mma_nA<C, HPW>(hacc, sK + (w / NTV) * 16 * LC, (NW / NTV) * 16 * LC, LC, sU + (w % NTV) * 16 * LC, LC);
+      else
+        mma_nA<C, HPW, true, false>(hacc, sK + (w / NTV) * 16, (NW / NTV) * 16, LK, sUk + (w % NTV) * 16 * LC, LC);
+    }
+#pragma unroll
+    for (int s = 0; s < (kShH ? 0 : HPW); ++s) {
       const int tt = w + NW * s;
       if (tt < NH) {
         const int td = tt / NTV, tv = tt % NTV;
