@@ -191,9 +191,10 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
   static_assert(NW % NB == 0, "waves must cover whole column blocks");
   // Every wave holds KPW tiles d = w / NB + (NW / NB) s of one column block
   // w % NB: the products then read the fragments the tiles share (dO, dS,
-  // dU, U, T, M) once per k step for all of them (mma_nA).
+  // dU, U, T, M) once per k step for all of them (mma_nA; bf16 operands).
   constexpr int NWB = NW / NB;
-  constexpr bool kShared = (DK / 16) % NWB == 0 && (DV / 16) % NWB == 0;
+  constexpr bool kShared = sizeof(E) == 2 && (DK / 16) % NWB == 0 && (DV / 16) % NWB == 0;
+  constexpr bool kSharedT = sizeof(E) == 2 && (NB * NB) % NW == 0;  // the (i, j) tile products: NB * NB / NW per wave
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
 
   Tile<E, C, DK, NT> tq, tk;
@@ -593,8 +594,24 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
       lds_barrier();
       LRT_G_LOAD(next, np, nn, 8)
       // dT = (dW K^T) diag(b gamma) + (dU V^T) diag(b)   (rows i, cols j) -> dT^T [j][i]
+      if constexpr (kSharedT) {
+        constexpr int TPW = NB * NB / NW;
+        f32x4 z1[TPW], z2[TPW];
 #pragma unroll
-      for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
+        for (int s = 0; s < TPW; ++s) {
+          z1[s] = zero4();
+          z2[s] = zero4();
+        }
+        mma_nA<DK, TPW>(z1, sdW + (w / NB) * 16 * LK, NWB * 16 * LK, LK, sK + (w % NB) * 16 * LK, LK);
+        mma_nA<DV, TPW, true, false>(z2, sdUt + (w / NB) * 16, NWB * 16, LC, sV + (w % NB) * 16 * LV, LV);
+        const int j = (w % NB) * 16 + (l & 15);
+        const float bj = sb[j], bgj = bj * __expf(sg[j]);
+#pragma unroll
+        for (int s = 0; s < TPW; ++s)
+          store4<E>(sdTt + j * LC + (w / NB + NWB * s) * 16 + (l >> 4) * 4, bgj * z1[s] + bj * z2[s]);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < (kSharedT ? 0 : (NB * NB + NW - 1) / NW); ++s2) {
         const int t2 = w + NW * s2;
         if (t2 >= NB * NB) break;
         const int ti = t2 / NB, tj = t2 % NB;
@@ -607,8 +624,18 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
       }
       lds_barrier();
       // R = dT Tinv^T (rows i, cols k) -> R^T [k][i]
+      if constexpr (kSharedT) {
+        constexpr int TPW = NB * NB / NW;
+        f32x4 ra[TPW];
 #pragma unroll
-      for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
+        for (int s = 0; s < TPW; ++s) ra[s] = zero4();
+        mma_nA<C, TPW, true, false>(ra, sdTt + (w / NB) * 16, NWB * 16, LC, sT + (w % NB) * 16 * LC, LC);
+#pragma unroll
+        for (int s = 0; s < TPW; ++s)
+          store4<E>(sRt + ((w % NB) * 16 + (l & 15)) * LC + (w / NB + NWB * s) * 16 + (l >> 4) * 4, ra[s]);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < (kSharedT ? 0 : (NB * NB + NW - 1) / NW); ++s2) {
         const int t2 = w + NW * s2;
         if (t2 >= NB * NB) break;
         const int ti = t2 / NB, tk2 = t2 % NB;

@@ -72,9 +72,10 @@ __global__ __launch_bounds__(64 * NW) void k_dstate(const E* __restrict__ q, con
   constexpr int NU = (C / 16) * NTV, UPW = (NU + NW - 1) / NW;
   static_assert(!KDA || (READ_P && DELTA && !PT), "the KDA reverse scan reads the stored P");
   // When every wave holds the same number of tiles of one column block, a
-  // wave's products read the fragment its tiles share once per k step.
-  constexpr bool kShU = NU % NW == 0 && NW % NTV == 0;
-  constexpr bool kShH = NH % NW == 0 && NW % NTV == 0;
+  // wave's bf16 products read the fragment its tiles share once per k step
+  // (fp32 operands are read per 16-long k step either way).
+  constexpr bool kShU = sizeof(E) == 2 && NU % NW == 0 && NW % NTV == 0;
+  constexpr bool kShH = sizeof(E) == 2 && NH % NW == 0 && NW % NTV == 0;
   __shared__ __attribute__((aligned(16))) E sQ[C * LK];    // q rows (KDA: Q o e^G rows)
   __shared__ __attribute__((aligned(16))) E sW[C * LK];    // W rows
   __shared__ __attribute__((aligned(16))) E sKt[dstate_kt_elems<C, DK, LK, LC, KDA>()];  // Ktil rows (KDA: Ktil^T)

@@ -118,6 +118,9 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
   constexpr int YPW = (NVT + WPB - 1) / WPB;  // dY^T tiles per wave
   constexpr int NZ = NB * NB, ZPW = (NZ + NW - 1) / NW;
   static_assert(NW % NB == 0, "waves must cover whole token blocks");
+  // When every wave holds KPW (YPW) tiles of its token block, a wave's
+  // bf16 products read the fragments its tiles share once per k step (mma_nA).
+  constexpr bool kSh = sizeof(E) == 2 && NDT % WPB == 0 && NVT % WPB == 0;
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
   const int H = m.H, ntiles = tile_count(m);
   int tid = threadIdx.x;  // (re-derived per chunk below, opaque to the compiler)
@@ -244,8 +247,20 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     }
     // (dO Hn^T)^T (rows d, cols t) kept in registers; dW = -dU Hn^T rows into X
     f32x4 dqa[KPW];
+    if constexpr (kSh) {
+      f32x4 xw[KPW];
 #pragma unroll
-    for (int s = 0; s < KPW; ++s) {
+      for (int s = 0; s < KPW; ++s) {
+        dqa[s] = zero4();
+        xw[s] = zero4();
+      }
+      mma_nA2<DV, KPW, true, false, true>(dqa, xw, sS + (w / NB) * 16, WPB * 16, LK, sdO + tb * 16 * LV, LV,
+                                          sdUt + tb * 16, LC);
+#pragma unroll
+      for (int s = 0; s < KPW; ++s) store4<E>(sX + tl * LK + (w / NB + WPB * s) * 16 + dsub, -xw[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < (kSh ? 0 : KPW); ++s) {
       const int td = w / NB + WPB * s;
       dqa[s] = zero4();
       if (td < NDT) {
@@ -292,8 +307,16 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     LRT_KG_LOAD(tile, cp, n, 24)
     lds_barrier();
     // dKt = U dH'^T rows into H
+    if constexpr (kSh) {
+      f32x4 xk[KPW];
 #pragma unroll
-    for (int s = 0; s < KPW; ++s) {
+      for (int s = 0; s < KPW; ++s) xk[s] = zero4();
+      mma_nA<DV, KPW, true, true>(xk, sS + (w / NB) * 16, WPB * 16, LK, sUt + tb * 16, LC);
+#pragma unroll
+      for (int s = 0; s < KPW; ++s) store4<E>(sH + tl * LK + (w / NB + WPB * s) * 16 + dsub, xk[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < (kSh ? 0 : KPW); ++s) {
       const int td = w / NB + WPB * s;
       if (td < NDT) {
         f32x4 x = zero4();
@@ -347,14 +370,16 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     float dbp = 0.f;  // this lane's dbeta terms (token tl)
     f32x4 dka[KPW], dga[KPW], dxa[KPW];
 #pragma unroll
+    for (int s = 0; s < KPW; ++s) dxa[s] = zero4();
+    if constexpr (kSh) mma_nA<C, KPW, true, true>(dxa, sX + (w / NB) * 16, WPB * 16, LK, sT + tb * 16, LC);
+#pragma unroll
     for (int s = 0; s < KPW; ++s) {
       const int td = w / NB + WPB * s;
       dka[s] = zero4();
       dga[s] = zero4();
-      dxa[s] = zero4();
       if (td < NDT) {
         const int d0 = td * 16 + dsub;
-        mma<C, true, true>(dxa[s], sX + td * 16, LK, sT + tb * 16, LC);
+        if constexpr (!kSh) mma<C, true, true>(dxa[s], sX + td * 16, LK, sT + tb * 16, LC);
         const f32x4 g = *(const f32x4*)(sG + tl * LG + d0);
         const f32x4 gc = *(const f32x4*)(sG + (C - 1) * LG + d0);
         const f32x4 kk = load4<E>(sK + tl * LK + d0);
@@ -430,11 +455,16 @@ __global__ __launch_bounds__(64 * NW) void k_grad_kda(
     // dY^T = (T^T dU)^T, rows v, cols j -> dY rows over dX
     f32x4 ya[YPW];
 #pragma unroll
-    for (int s = 0; s < YPW; ++s) {
-      const int tvb = w / NB + WPB * s;
-      ya[s] = zero4();
-      if (tvb < NVT) mma<C, false, true>(ya[s], sdUt + tvb * 16 * LC, LC, sT + tb * 16, LC);
-      tile_fence();
+    for (int s = 0; s < YPW; ++s) ya[s] = zero4();
+    if constexpr (kSh) {
+      mma_nA<C, YPW, false, true>(ya, sdUt + (w / NB) * 16 * LC, WPB * 16 * LC, LC, sT + tb * 16, LC);
+    } else {
+#pragma unroll
+      for (int s = 0; s < YPW; ++s) {
+        const int tvb = w / NB + WPB * s;
+        if (tvb < NVT) mma<C, false, true>(ya[s], sdUt + tvb * 16 * LC, LC, sT + tb * 16, LC);
+        tile_fence();
+      }
     }
 #pragma unroll
     for (int s = 0; s < YPW; ++s) {

@@ -268,10 +268,11 @@ __global__ __launch_bounds__(64 * NW) void k_scan(ScanArgs<E> a) {
   constexpr int NU = NB * NTV, UPW = (NU + NW - 1) / NW;         // U tiles (rows t, cols v)
   constexpr int NO = NTV * NB;                                   // O^T tiles (rows v, cols t)
   // When every wave holds the same number of tiles of one column block, a
-  // wave's products read the fragment its tiles share once per k step.
-  constexpr bool kShU = NU % NW == 0 && NW % NTV == 0;
-  constexpr bool kShH = NH % NW == 0 && NW % NTV == 0;
-  constexpr bool kShO = NO % NW == 0 && NW % NB == 0;
+  // wave's bf16 products read the fragment its tiles share once per k step
+  // (fp32 operands are read per 16-long k step either way).
+  constexpr bool kShU = sizeof(E) == 2 && NU % NW == 0 && NW % NTV == 0;
+  constexpr bool kShH = sizeof(E) == 2 && NH % NW == 0 && NW % NTV == 0;
+  constexpr bool kShO = sizeof(E) == 2 && NO % NW == 0 && NW % NB == 0;
   __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
   E* sW = (E*)(smem + Lay::W);
   E* sK = (E*)(smem + Lay::K);  // GDN: k rows; KDA: Ktil^T
