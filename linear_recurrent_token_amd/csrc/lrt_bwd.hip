@@ -166,10 +166,20 @@ struct GradLds {
   // phase 2, over phase 1's buffers
   static constexpr size_t VV = U0;                                        // v rows [t][v]
   static constexpr size_t TT = VV + (size_t)C * LV * es;                  // Tinv [i][j]
-  static constexpr size_t DW = TT + (size_t)C * LC * es;                  // dW rows [i][d]; later dk rows
-  static constexpr size_t F = DW + (size_t)C * LK * es;                   // dv rows; later dT^T, R^T, M^T
-  static constexpr size_t END2 = F + mx((size_t)C * LV, 3 * (size_t)C * LC) * es;
-  static constexpr size_t TOTAL = DELTA ? mx(END1, END2) : END1;
+  static constexpr size_t DW = TT + (size_t)C * LC * es;                  // dW rows [i][d]
+  static constexpr size_t F = DW + (size_t)C * LK * es;                   // dv rows
+  static constexpr size_t TOTAL = DELTA ? mx(END1, F + mx((size_t)C * LV, 3 * (size_t)C * LC) * es) : END1;
+  // dT^T, R^T, M^T: past the dv rows where that needs no more LDS (then the dT
+  // products need not wait for the dv rows' copy-out), else over them
+  static constexpr bool SEPT = F + ((size_t)C * LV + 3 * (size_t)C * LC) * es <= TOTAL;
+  static constexpr size_t TR = SEPT ? F + (size_t)C * LV * es : F;
+  static constexpr size_t MT = TR + 2 * (size_t)C * LC * es;
+  // dk rows: over S^T where they miss M^T (the next chunk stores its S^T only
+  // after its first barrier, so no barrier is needed after their copy into
+  // registers), else over dW
+  static constexpr bool LATE_S = DELTA && (ST + (size_t)C * LK * es <= MT || ST >= MT + (size_t)C * LC * es) &&
+                                 ST + (size_t)C * LK * es <= TOTAL;
+  static constexpr size_t DKR = LATE_S ? ST : DW;
 };
 
 template <typename E, int C, int DK, int DV, int NW = 8, bool DELTA = true>
@@ -272,9 +282,9 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
     E* sV = (E*)(smz + Lay::VV);
     E* sT = (E*)(smz + Lay::TT);
     E* sdW = (E*)(smz + Lay::DW);
-    E* sdK = (E*)(smz + Lay::DW);
+    E* sdK = (E*)(smz + Lay::DKR);
     E* sdV = (E*)(smz + Lay::F);
-    E* sdTt = (E*)(smz + Lay::F);
+    E* sdTt = (E*)(smz + Lay::TR);
     E* sRt = sdTt + C * LC;
     E* sMt = sRt + C * LC;
     int tidv = threadIdx.x;
@@ -301,7 +311,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
     else
       tu.store_masked(sUt, LV, nv);
     tdu.store(sdUt, LC);
-    tS.store(sS, LK);
+    if constexpr (!Lay::LATE_S) tS.store(sS, LK);
     asm volatile("" ::"v"(rg));  // consumed by every lane (no load into it left pending)
     if (threadIdx.x < C) sg[threadIdx.x] = rg;
     slot_zero<NW, C>(pdgs);
@@ -318,6 +328,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
     }
     tdS.load_block(wdS + (size_t)tile * DV * DK);  // dH' of this chunk, needed after dS
     lds_barrier();
+    if constexpr (Lay::LATE_S) tS.store(sS, LK);  // over the previous chunk's dk rows
     LRT_G_LOAD(next, np, nn, 1)
 
     // dS = (dO U^T) o Gamma (inclusive); E = dS o (Q K^T) -> dg rows +, cols -
@@ -591,7 +602,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
       }
       lds_barrier();
       lds_to_rows<E, C, DV, NT>(dv_out + (tok0 * H + h) * DV, (size_t)H * DV, sdV, LV, nv);
-      lds_barrier();
+      if constexpr (!Lay::SEPT) lds_barrier();
       LRT_G_LOAD(next, np, nn, 8)
       // dT = (dW K^T) diag(b gamma) + (dU V^T) diag(b)   (rows i, cols j) -> dT^T [j][i]
       if constexpr (kSharedT) {
@@ -733,7 +744,7 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
       ptok = tok0;
       ph = h;
       pnv = nv;
-      lds_barrier();
+      if constexpr (!Lay::LATE_S) lds_barrier();
     } else {
       // dg, reverse cumsum -> dlog_a (wave 0, one token per lane)
       if (threadIdx.x < 64) {
