@@ -600,40 +600,47 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
         e = sum4(e);
         if (l < 16) mydb[jw] += e;
       }
+      // dT = (dW K^T) diag(b gamma) + (dU V^T) diag(b)   (rows i, cols j) -> dT^T [j][i]
+      // (in the dY phase when dT^T is not over the dv rows, else after their copy-out)
+      auto dt_products = [&]() {
+        if constexpr (kSharedT) {
+          constexpr int TPW = NB * NB / NW;
+          f32x4 z1[TPW], z2[TPW];
+#pragma unroll
+          for (int s = 0; s < TPW; ++s) {
+            z1[s] = zero4();
+            z2[s] = zero4();
+          }
+          mma_nA<DK, TPW>(z1, sdW + (w / NB) * 16 * LK, NWB * 16 * LK, LK, sK + (w % NB) * 16 * LK, LK);
+          mma_nA<DV, TPW, true, false>(z2, sdUt + (w / NB) * 16, NWB * 16, LC, sV + (w % NB) * 16 * LV, LV);
+          const int j = (w % NB) * 16 + (l & 15);
+          const float bj = sb[j], bgj = bj * __expf(sg[j]);
+#pragma unroll
+          for (int s = 0; s < TPW; ++s)
+            store4<E>(sdTt + j * LC + (w / NB + NWB * s) * 16 + (l >> 4) * 4, bgj * z1[s] + bj * z2[s]);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < (kSharedT ? 0 : (NB * NB + NW - 1) / NW); ++s2) {
+          const int t2 = w + NW * s2;
+          if (t2 >= NB * NB) break;
+          const int ti = t2 / NB, tj = t2 % NB;
+          const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
+          f32x4 z1 = zero4(), z2 = zero4();
+          mma<DK>(z1, sdW + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
+          mma<DV, true, false>(z2, sdUt + ti * 16, LC, sV + tj * 16 * LV, LV);
+          store4<E>(sdTt + j * LC + i0, sb[j] * (__expf(sg[j]) * z1 + z2));
+          tile_fence();
+        }
+      };
+      if constexpr (Lay::SEPT) dt_products();
       lds_barrier();
       lds_to_rows<E, C, DV, NT>(dv_out + (tok0 * H + h) * DV, (size_t)H * DV, sdV, LV, nv);
       if constexpr (!Lay::SEPT) lds_barrier();
       LRT_G_LOAD(next, np, nn, 8)
-      // dT = (dW K^T) diag(b gamma) + (dU V^T) diag(b)   (rows i, cols j) -> dT^T [j][i]
-      if constexpr (kSharedT) {
-        constexpr int TPW = NB * NB / NW;
-        f32x4 z1[TPW], z2[TPW];
-#pragma unroll
-        for (int s = 0; s < TPW; ++s) {
-          z1[s] = zero4();
-          z2[s] = zero4();
-        }
-        mma_nA<DK, TPW>(z1, sdW + (w / NB) * 16 * LK, NWB * 16 * LK, LK, sK + (w % NB) * 16 * LK, LK);
-        mma_nA<DV, TPW, true, false>(z2, sdUt + (w / NB) * 16, NWB * 16, LC, sV + (w % NB) * 16 * LV, LV);
-        const int j = (w % NB) * 16 + (l & 15);
-        const float bj = sb[j], bgj = bj * __expf(sg[j]);
-#pragma unroll
-        for (int s = 0; s < TPW; ++s)
-          store4<E>(sdTt + j * LC + (w / NB + NWB * s) * 16 + (l >> 4) * 4, bgj * z1[s] + bj * z2[s]);
+      if constexpr (!Lay::SEPT) {
+        dt_products();
+        lds_barrier();
       }
-#pragma unroll
-      for (int s2 = 0; s2 < (kSharedT ? 0 : (NB * NB + NW - 1) / NW); ++s2) {
-        const int t2 = w + NW * s2;
-        if (t2 >= NB * NB) break;
-        const int ti = t2 / NB, tj = t2 % NB;
-        const int j = tj * 16 + (l & 15), i0 = ti * 16 + (l >> 4) * 4;
-        f32x4 z1 = zero4(), z2 = zero4();
-        mma<DK>(z1, sdW + ti * 16 * LK, LK, sK + tj * 16 * LK, LK);
-        mma<DV, true, false>(z2, sdUt + ti * 16, LC, sV + tj * 16 * LV, LV);
-        store4<E>(sdTt + j * LC + i0, sb[j] * (__expf(sg[j]) * z1 + z2));
-        tile_fence();
-      }
-      lds_barrier();
       // R = dT Tinv^T (rows i, cols k) -> R^T [k][i]
       if constexpr (kSharedT) {
         constexpr int TPW = NB * NB / NW;
