@@ -420,27 +420,27 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
         mma_nA<C, KPW, true, true>(dqa, sK + td0 * 16, NWB * 16, LK, sdSj + ti * 16, LC);
       } else {
 #pragma unroll
-      for (int s = 0; s < KPW; ++s) {
-        const int td = w / NB + (NW / NB) * s;
-        dqa[s] = zero4();
-        dwa[s] = zero4();
-        if (td < DK / 16) {
-          const int d0 = td * 16 + (l >> 4) * 4;
-          f32x4 acc = zero4();
-          mma<DV, true, false>(acc, sS + td * 16, LK, sdO + ti * 16 * LV, LV);
+        for (int s = 0; s < KPW; ++s) {
+          const int td = w / NB + (NW / NB) * s;
+          dqa[s] = zero4();
+          dwa[s] = zero4();
+          if (td < DK / 16) {
+            const int d0 = td * 16 + (l >> 4) * 4;
+            f32x4 acc = zero4();
+            mma<DV, true, false>(acc, sS + td * 16, LK, sdO + ti * 16 * LV, LV);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) esum += to_f(sQ[i * LK + d0 + r]) * acc[r];
-          acc *= gam;
-          mma<C, true, true>(acc, sK + td * 16, LK, sdSj + ti * 16, LC);
-          dqa[s] = acc;
-          if constexpr (DELTA) {
-            f32x4 dw = zero4();
-            mma<DV, true, true>(dw, sS + td * 16, LK, sdUt + ti * 16, LC);
-            dwa[s] = -dw;
+            for (int r = 0; r < 4; ++r) esum += to_f(sQ[i * LK + d0 + r]) * acc[r];
+            acc *= gam;
+            mma<C, true, true>(acc, sK + td * 16, LK, sdSj + ti * 16, LC);
+            dqa[s] = acc;
+            if constexpr (DELTA) {
+              f32x4 dw = zero4();
+              mma<DV, true, true>(dw, sS + td * 16, LK, sdUt + ti * 16, LC);
+              dwa[s] = -dw;
+            }
           }
+          tile_fence();
         }
-        tile_fence();
-      }
       }
       esum = sum4(esum * gam);
       wave_order();
@@ -490,24 +490,24 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
         mma_nA<C, KPW, true, false>(dka, sQ + td0 * 16, NWB * 16, LK, sdSj + tj * 16 * LC, LC);
       } else {
 #pragma unroll
-      for (int s = 0; s < KPW; ++s) {
-        const int td = w / NB + (NW / NB) * s;
-        dka[s] = zero4();
-        if (td < DK / 16) {
-          const int d0 = td * 16 + (l >> 4) * 4;
-          f32x4 acc = zero4();
-          if constexpr (DELTA)
-            mma<DV, true, true>(acc, sS + td * 16, LK, sUt + tj * 16, LC);
-          else
-            mma<DV, true, false>(acc, sS + td * 16, LK, sUt + tj * 16 * LV, LV);
+        for (int s = 0; s < KPW; ++s) {
+          const int td = w / NB + (NW / NB) * s;
+          dka[s] = zero4();
+          if (td < DK / 16) {
+            const int d0 = td * 16 + (l >> 4) * 4;
+            f32x4 acc = zero4();
+            if constexpr (DELTA)
+              mma<DV, true, true>(acc, sS + td * 16, LK, sUt + tj * 16, LC);
+            else
+              mma<DV, true, false>(acc, sS + td * 16, LK, sUt + tj * 16 * LV, LV);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ssum += acc[r] * to_f(sK[j * LK + d0 + r]);
-          acc *= kt;
-          mma<C, true, false>(acc, sQ + td * 16, LK, sdSj + tj * 16 * LC, LC);
-          dka[s] = acc;
+            for (int r = 0; r < 4; ++r) ssum += acc[r] * to_f(sK[j * LK + d0 + r]);
+            acc *= kt;
+            mma<C, true, false>(acc, sQ + td * 16, LK, sdSj + tj * 16 * LC, LC);
+            dka[s] = acc;
+          }
+          tile_fence();
         }
-        tile_fence();
-      }
       }
       ssum = sum4(ssum * kt);
       const float stot = sum16(ssum);  // over the wave's 16 columns j (lanes 0..15)
@@ -548,19 +548,19 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
           }
         } else {
 #pragma unroll
-        for (int s = 0; s < KPW; ++s) {
-          const int kt = w + NW * s;
-          if (kt < NKT) {
-            const int td = kt / NB, tj = kt % NB;
-            const int d0 = td * 16 + (l >> 4) * 4;
-            f32x4 acc = zero4();
-            mma<C, true, true>(acc, sdW + td * 16, LK, sT + tj * 16, LC);
-            dka[s] += bgj * acc;
+          for (int s = 0; s < KPW; ++s) {
+            const int kt = w + NW * s;
+            if (kt < NKT) {
+              const int td = kt / NB, tj = kt % NB;
+              const int d0 = td * 16 + (l >> 4) * 4;
+              f32x4 acc = zero4();
+              mma<C, true, true>(acc, sdW + td * 16, LK, sT + tj * 16, LC);
+              dka[s] += bgj * acc;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sK[jw * LK + d0 + r]);
+              for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sK[jw * LK + d0 + r]);
+            }
+            tile_fence();
           }
-          tile_fence();
-        }
         }
         e = sum4(e);
         if (l < 16) mycx[jw] += e;
@@ -584,18 +584,18 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
           }
         } else {
 #pragma unroll
-        for (int s2 = 0; s2 < ((DV / 16) * NB + NW - 1) / NW; ++s2) {
-          const int tt2 = w + NW * s2;
-          if (tt2 >= (DV / 16) * NB) break;
-          const int tvv = tt2 / NB, tj = tt2 % NB;
-          const int v0 = tvv * 16 + (l >> 4) * 4;
-          f32x4 acc = zero4();
-          mma<C, false, true>(acc, sdUt + tvv * 16 * LC, LC, sT + tj * 16, LC);
-          store4<E>(sdV + jw * LV + v0, bj * acc);
+          for (int s2 = 0; s2 < ((DV / 16) * NB + NW - 1) / NW; ++s2) {
+            const int tt2 = w + NW * s2;
+            if (tt2 >= (DV / 16) * NB) break;
+            const int tvv = tt2 / NB, tj = tt2 % NB;
+            const int v0 = tvv * 16 + (l >> 4) * 4;
+            f32x4 acc = zero4();
+            mma<C, false, true>(acc, sdUt + tvv * 16 * LC, LC, sT + tj * 16, LC);
+            store4<E>(sdV + jw * LV + v0, bj * acc);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sV[jw * LV + v0 + r]);
-          tile_fence();
-        }
+            for (int r = 0; r < 4; ++r) e += acc[r] * to_f(sV[jw * LV + v0 + r]);
+            tile_fence();
+          }
         }
         e = sum4(e);
         if (l < 16) mydb[jw] += e;
@@ -713,16 +713,16 @@ __global__ __launch_bounds__(64 * NW) void k_grad(const E* __restrict__ q, const
           store4<E>(sdK + ((w % NB) * 16 + (l & 15)) * LK + (w / NB + NWB * s) * 16 + (l >> 4) * 4, dka[s]);
       } else {
 #pragma unroll
-      for (int s = 0; s < KPW; ++s) {
-        const int kt = w + NW * s;
-        if (kt < NKT) {
-          const int td = kt / NB, tj = kt % NB;
-          mma<C, true, false>(dka[s], sK + td * 16, LK, sMt + tj * 16 * LC, LC);
-          mma<C, true, true>(dka[s], sK + td * 16, LK, sMt + tj * 16, LC);
-          store4<E>(sdK + (tj * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, dka[s]);
+        for (int s = 0; s < KPW; ++s) {
+          const int kt = w + NW * s;
+          if (kt < NKT) {
+            const int td = kt / NB, tj = kt % NB;
+            mma<C, true, false>(dka[s], sK + td * 16, LK, sMt + tj * 16 * LC, LC);
+            mma<C, true, true>(dka[s], sK + td * 16, LK, sMt + tj * 16, LC);
+            store4<E>(sdK + (tj * 16 + (l & 15)) * LK + td * 16 + (l >> 4) * 4, dka[s]);
+          }
+          tile_fence();
         }
-        tile_fence();
-      }
       }
       // dg (+ the X = diag(b gamma) K term), reverse cumsum -> dlog_a; dbeta
       if (threadIdx.x < 64) {
