@@ -75,6 +75,13 @@ CASES = [
     ("fp32_d128_C64", 1, 150, 2, 128, 128, 64, torch.float32, -6.0, 0.1, 0.1),
     ("fp32_dk128_dv64_C64", 1, 100, 2, 128, 64, 64, torch.float32, -2.0, 0.1, 0.1),
     ("fp32_d64_C64", 2, 130, 2, 64, 64, 64, torch.float32, -6.0, 0.1, 0.1),
+    # bf16 layouts of the gradient kernel: one d_k tile per wave at chunk 16
+    # (the shared-fragment products), the dk rows over S^T with dT^T over the
+    # dv rows (d = 64), neither (d_k 128, d_v 64), and a one-tile d_k
+    ("bf16_d128_C16", 1, 90, 2, 128, 128, 16, torch.bfloat16, -6.0, 0.1, 0.1),
+    ("bf16_d64_C64", 2, 130, 2, 64, 64, 64, torch.bfloat16, -6.0, 0.1, 0.1),
+    ("bf16_dk128_dv64_C64", 1, 100, 2, 128, 64, 64, torch.bfloat16, -2.0, 0.1, 0.1),
+    ("bf16_dk16_dv128_C64", 1, 100, 2, 16, 128, 64, torch.bfloat16, -6.0, 0.1, 0.1),
 ]
 
 
@@ -167,6 +174,8 @@ SSD_CASES = [
     ("bf16_dk32_dv128", 1, 100, 2, 32, 128, 32, torch.bfloat16, -6.0, 0.1, 0.1),
     ("bf16_long_slow_C64", 1, 4096 - 7, 2, 128, 128, 64, torch.bfloat16, -6.0, 0.1, 0.1),
     ("fp32_d128_C64", 1, 150, 2, 128, 128, 64, torch.float32, -6.0, 0.1, 0.1),
+    ("bf16_d128_C16", 1, 90, 2, 128, 128, 16, torch.bfloat16, -6.0, 0.1, 0.1),
+    ("bf16_d64_C64", 2, 130, 2, 64, 64, 64, torch.bfloat16, -6.0, 0.1, 0.1),
 ]
 
 

@@ -85,6 +85,7 @@ CASES = [
     # chunk whose fp32 operands fit in LDS
     ("fp32_d128_C64", 1, 100, 2, 128, 128, 64, torch.float32, "perdim", 0.0, 0.1, 0.1),
     ("bf16_T61_C16", 2, 61, 3, 64, 64, 16, torch.bfloat16, "perdim", 0.0, 0.1, 0.1),
+    ("bf16_d128_C16", 1, 90, 2, 128, 128, 16, torch.bfloat16, "perdim", 0.0, 0.1, 0.1),
     ("bf16_C32", 1, 200, 2, 128, 128, 32, torch.bfloat16, "perdim", 0.0, 0.1, 0.1),
     ("bf16_C64_T300", 2, 300, 2, 128, 128, 64, torch.bfloat16, "perdim", 0.0, 0.1, 0.1),
     ("bf16_C64_strong", 1, 256, 2, 128, 128, 64, torch.bfloat16, "perdim", 3.0, 0.1, 0.1),
