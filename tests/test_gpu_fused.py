@@ -51,6 +51,7 @@ CASES = [
     ("gdn", 2, 300, 2, 128, 128, 64, torch.bfloat16, 2.0),
     ("gdn", 1, 130, 2, 64, 32, 32, torch.float32, -6.0),
     ("gdn", 1, 2560 - 3, 1, 128, 128, 64, torch.bfloat16, -6.0),  # segment-parallel scan
+    ("gdn", 16, 2048, 8, 128, 128, 64, torch.bfloat16, 2.0),  # the 2048-token shape, every element
     ("kda", 2, 300, 2, 128, 128, 64, torch.bfloat16, 0.0),
     ("kda", 1, 130, 2, 64, 64, 32, torch.float32, -2.0),
     ("kda", 1, 4096, 2, 128, 128, 64, torch.bfloat16, -4.0),  # segment-parallel scan

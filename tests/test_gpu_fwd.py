@@ -100,13 +100,12 @@ def test_fwd_small(case):
 
 @pytest.mark.parametrize("name,op", [("gdn_fp32_tiny", "gdn"), ("ssd_bf16_2k", "ssd"), ("gdn_bf16_2k", "gdn")])
 def test_fwd_named_workloads(name, op):
-    """The named workloads at full size; outputs sampled on value-column blocks
-    the oracle computes exactly (columns of the state never mix)."""
+    """The named workloads at full size, every element of o and ht against the
+    oracle (about 3 s of fp64 work on 8 cores at the 2048-token shapes)."""
     say(f"[fwd] workload {name}")
     c = synth.CONFIGS[name]
     inp = synth.config_inputs(name, device="cuda")
-    cols = None if c["dv"] <= 16 else (c["dv"] - 8, 8)
-    eo, eh = run_fwd(op, inp, c["chunk"], cols=cols)
+    eo, eh = run_fwd(op, inp, c["chunk"])
     say(f"  rel err o={eo:.2e} ht={eh:.2e}")
     assert eo <= TOL[c["dtype"]] and eh <= TOL[c["dtype"]], (eo, eh)
 
