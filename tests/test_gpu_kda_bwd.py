@@ -162,7 +162,20 @@ VARLEN = [
     # lengths, H, d_k, d_v, chunk, dtype, gate_shift
     ([130, 7, 64, 1, 300, 0, 65], 2, 128, 128, 64, torch.bfloat16, 0.0),
     ([50, 16, 3, 97], 2, 64, 32, 16, torch.float32, 1.0),
+    # the three regimes of the gradient kernel's decayed sums side by side in
+    # the packed sequences' chunks: whole-chunk, 16-token blocks, exact
+    ([200, 33, 64, 150, 17], 2, 128, 128, 64, torch.bfloat16, "regimes"),
 ]
+
+
+def regime_shift(T, H, device):
+    """A gate shift per (token, head) cycling every 64 packed tokens through
+    -2 (every |G| of a 64-token chunk within e^60), +1 (16-token blocks within
+    e^60, the chunk past it) and +3 (a block past e^60: the exact path)."""
+    n = torch.arange(T, device=device).view(T, 1) // 64
+    h = torch.arange(H, device=device).view(1, H)
+    r = (n + h) % 3
+    return torch.where(r == 0, -2.0, torch.where(r == 1, 1.0, 3.0)).view(1, T, H, 1)
 
 
 @pytest.mark.parametrize("case", VARLEN, ids=[f"{len(c[0])}seq_C{c[4]}_{str(c[5])[6:]}" for c in VARLEN])
@@ -174,6 +187,8 @@ def test_kda_bwd_varlen(case):
     say(f"[kda_bwd_varlen] {case}")
     T = int(sum(lens))
     n = len(lens)
+    if shift == "regimes":
+        shift = regime_shift(T, H, "cuda")
     inp = synth.make_inputs("kda_fwd_bwd", 1, T, H, dk, dv, dtype=dt, seed=6, device="cuda", gate="perdim",
                             gate_shift=shift)
     h0 = synth.randn((n, H, dk, dv), 6, "h0", "cuda", std=0.1)
