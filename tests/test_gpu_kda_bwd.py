@@ -165,6 +165,7 @@ VARLEN = [
     # the three regimes of the gradient kernel's decayed sums side by side in
     # the packed sequences' chunks: whole-chunk, 16-token blocks, exact
     ([200, 33, 64, 150, 17], 2, 128, 128, 64, torch.bfloat16, "regimes"),
+    ([200, 33, 64, 150, 17], 2, 64, 64, 64, torch.float32, "regimes"),
 ]
 
 
