@@ -51,6 +51,15 @@ struct SsdFwdLds {
   static constexpr size_t PT = S + (size_t)BV * LK * es;  // P^T [j][i]
   static constexpr size_t O = PT + (size_t)C * LC * es;   // o rows [t][v]
   static constexpr size_t TOTAL = O + (size_t)C * LB * es;
+  // second copies of q, v and Hn^T for odd chunks where they fit: the chunk
+  // step then needs no barrier between its output products and the next
+  // chunk's staging
+  static constexpr size_t Q2 = TOTAL;
+  static constexpr size_t V2 = Q2 + (size_t)C * LK * es;
+  static constexpr size_t S2 = V2 + (size_t)C * LB * es;
+  static constexpr size_t TOTAL_DB = S2 + (size_t)BV * LK * es;
+  static constexpr bool DB = TOTAL_DB <= 160 * 1024;
+  static constexpr size_t ALLOC = DB ? TOTAL_DB : TOTAL;
 };
 
 template <typename E, int C, int DK, int BV, int NW = 8, int PF = 1, int OCC = 2, bool SAVE = false>
@@ -66,12 +75,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_ssd_fwd(const E* __restrict__ 
   constexpr int NH = (DK / 16) * NTV, HPW = (NH + NW - 1) / NW;  // state tiles (rows d, cols v)
   constexpr int NO = NTV * NB;                                   // O^T tiles (rows v, cols t)
   static_assert(C <= 64, "one token per lane in the gate scan");
-  __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
+  constexpr bool DB = Lay::DB;
+  __shared__ __attribute__((aligned(16))) char smem[Lay::ALLOC];
   E* sK = (E*)(smem + Lay::K);
-  E* sQ = (E*)(smem + Lay::Q);
-  E* sV = (E*)(smem + Lay::V);
+  E* sQ0 = (E*)(smem + Lay::Q);
+  E* sV0 = (E*)(smem + Lay::V);
   E* sVk = (E*)(smem + Lay::VK);
-  E* sS = (E*)(smem + Lay::S);
+  E* sS0 = (E*)(smem + Lay::S);
   E* sPt = (E*)(smem + Lay::PT);
   E* sO = (E*)(smem + Lay::O);
 
@@ -113,6 +123,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_ssd_fwd(const E* __restrict__ 
   auto step = [&](Ops& x, int n) {
     const int nv = min(C, T - n * C);
     const size_t tok0 = (size_t)b * T + (size_t)n * C;
+    // this chunk's copies of q, v and Hn^T (odd chunks: the second set)
+    E* const sQ = DB && (n & 1) ? (E*)(smem + Lay::Q2) : sQ0;
+    E* const sV = DB && (n & 1) ? (E*)(smem + Lay::V2) : sV0;
+    E* const sS = DB && (n & 1) ? (E*)(smem + Lay::S2) : sS0;
     // ---- gates, in every wave: lane t holds token t's g, gamma, e^(g_C - g)
     asm volatile("" ::"v"(x.la));
     const float g = wave_incl_scan(l < nv ? x.la : 0.f);
@@ -154,6 +168,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_ssd_fwd(const E* __restrict__ 
       lds_to_block<E, BV, DK, NT>(wS + (tile * DV + v0) * DK, sS, LK);
       wG[tile * C + min(l, C - 1)] = g;
     }
+    // (second copies) the previous chunk's o rows, complete since the
+    // barrier; issued after the prefetch, so the next wait for operands
+    // leaves these stores in flight
+    if (DB && n > 0)
+      lds_to_rows_clamped<E, C, BV, NT>(o + (((size_t)b * T + (size_t)(n - 1) * C) * H + h) * DV + v0,
+                                        (size_t)H * DV, sO, LB, C);
     // ---- P^T (rows j, cols i): P_ij = (q_i . k_j) e^(g_i - g_j), j <= i
 #pragma unroll
     for (int s2 = 0; s2 < (NB * NB + NW - 1) / NW; ++s2) {
@@ -172,6 +192,26 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_ssd_fwd(const E* __restrict__ 
           for (int r = 0; r < 4; ++r) p[r] = (j <= i0 + r) ? p[r] * __expf(gi[r] - gj) : 0.f;
         }
         store4<E>(sPt + j * LC + i0, p);
+      }
+    }
+    // ---- Hn <- gamma_C Hn + K^T (e^(g_C - g) V) (reads only K and e^(g_C - g) V; the
+    // output products below read the LDS copy of the chunk-start Hn)
+    const float dec = __shfl(gam, C - 1, 64);
+#pragma unroll
+    for (int s = 0; s < HPW; ++s) hacc[s] *= dec;
+    if constexpr (NH % NW == 0 && NW % NTV == 0) {
+      // a wave's tiles share their column block v: one e^(g_C - g) V
+      // fragment per k step for all of them (tile s is rows td = w / NTV +
+      // (NW / NTV) s, as everywhere hacc is indexed)
+      mma_nA<C, HPW, true, true>(hacc, sK + (w / NTV) * 16, (NW / NTV) * 16, LK, sVk + (w % NTV) * 16, LB);
+    } else {
+#pragma unroll
+      for (int s = 0; s < HPW; ++s) {
+        const int tt = w + NW * s;
+        if (tt < NH) {
+          const int td = tt / NTV, tv2 = tt % NTV;
+          mma<C, true, true>(hacc[s], sK + td * 16, LK, sVk + tv2 * 16, LB);
+        }
       }
     }
     lds_barrier();
@@ -209,29 +249,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_ssd_fwd(const E* __restrict__ 
         }
       }
     }
-    // ---- Hn <- gamma_C Hn + K^T (e^(g_C - g) V)
-    const float dec = __shfl(gam, C - 1, 64);
-#pragma unroll
-    for (int s = 0; s < HPW; ++s) hacc[s] *= dec;
-    if constexpr (NH % NW == 0 && NW % NTV == 0) {
-      // a wave's tiles share their column block v: one e^(g_C - g) V
-      // fragment per k step for all of them (tile s is rows td = w / NTV +
-      // (NW / NTV) s, as everywhere hacc is indexed)
-      mma_nA<C, HPW, true, true>(hacc, sK + (w / NTV) * 16, (NW / NTV) * 16, LK, sVk + (w % NTV) * 16, LB);
-    } else {
-#pragma unroll
-      for (int s = 0; s < HPW; ++s) {
-        const int tt = w + NW * s;
-        if (tt < NH) {
-          const int td = tt / NTV, tv2 = tt % NTV;
-          mma<C, true, true>(hacc[s], sK + td * 16, LK, sVk + tv2 * 16, LB);
-        }
-      }
+    if constexpr (!DB) {
+      lds_barrier();
+      // o rows out; issued after the prefetch, so the next chunk's wait for
+      // its operands leaves these stores in flight
+      lds_to_rows_clamped<E, C, BV, NT>(o + (tok0 * H + h) * DV + v0, (size_t)H * DV, sO, LB, nv);
     }
-    lds_barrier();
-    // o rows out; issued after the prefetch, so the next chunk's wait for
-    // its operands leaves these stores in flight
-    lds_to_rows_clamped<E, C, BV, NT>(o + (tok0 * H + h) * DV + v0, (size_t)H * DV, sO, LB, nv);
   };
 
   Ops x0, x1;
@@ -240,6 +263,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_ssd_fwd(const E* __restrict__ 
   for (int n = 0; n < N; n += PF) {
     step(x0, n);
     if (PF > 1 && n + 1 < N) step(x1, n + 1);
+  }
+  if (DB && N > 0) {  // the last chunk's o rows
+    lds_barrier();
+    lds_to_rows_clamped<E, C, BV, NT>(o + (((size_t)b * T + (size_t)(N - 1) * C) * H + h) * DV + v0, (size_t)H * DV,
+                                      sO, LB, T - (N - 1) * C);
   }
   if (ht != nullptr) {
 #pragma unroll
