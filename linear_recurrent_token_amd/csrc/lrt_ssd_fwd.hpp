@@ -24,7 +24,11 @@
 //    rows and chunk index), so the compiler's wait for a chunk's operands
 //    counts exactly and leaves later loads and the stores in flight;
 //  * a wave's output and state tiles share one operand fragment per k step;
-//  * three barriers per chunk.
+//  * two barriers per chunk where second copies of q, v and Hn^T fit in LDS
+//    (odd chunks use them): the state update runs before the P^T barrier,
+//    and a chunk's o rows leave after the next chunk's first barrier, so no
+//    barrier separates the output products from the next chunk's staging;
+//    otherwise three.
 // SAVE (the training forward) also writes each chunk's start state S_n
 // ([d_v][d_k] per chunk, as the backward reads it), the gate cumsums g and
 // P^T ([j][i] per chunk; the column blocks of one (b, h) write identical
